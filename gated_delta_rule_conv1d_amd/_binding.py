@@ -1,0 +1,294 @@
+"""ctypes binding of libgdn.so (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+F32, BF16 = 0, 1
+_STATUS = {0: "GDN_OK", -1: "GDN_ERR_INVALID_ARG", -2: "GDN_ERR_UNSUPPORTED", -3: "GDN_ERR_WORKSPACE",
+           -4: "GDN_ERR_HIP"}
+
+#: every symbol include/gdn.h declares
+SYMBOLS = ("gdn_status_string", "gdn_max_chunks", "gdn_chunk_index", "gdn_conv1d", "gdn_conv1d_bwd_workspace",
+           "gdn_conv1d_bwd", "gdn_chunk_fwd_workspace", "gdn_chunk_fwd", "gdn_chunk_bwd_workspace",
+           "gdn_chunk_bwd", "gdn_norm_gate", "gdn_norm_gate_bwd_workspace", "gdn_norm_gate_bwd")
+
+
+class GdnError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} returned {code} ({_STATUS.get(code, 'unknown')})")
+        self.code = code
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [("n_seqs", ctypes.c_int32), ("total_tokens", ctypes.c_int32), ("h_qk", ctypes.c_int32),
+                ("h_v", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+@dataclass(frozen=True)
+class Shape:
+    n_seqs: int
+    total_tokens: int
+    h_qk: int
+    h_v: int
+    d_k: int
+    d_v: int
+    chunk: int = 64
+    dtype: int = BF16
+    scale: float = 1.0
+
+    @property
+    def channels(self) -> int:
+        return 2 * self.h_qk * self.d_k + self.h_v * self.d_v
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == BF16 else torch.float32
+
+    def c(self) -> _Shape:
+        return _Shape(self.n_seqs, self.total_tokens, self.h_qk, self.h_v, self.d_k, self.d_v, self.chunk,
+                      self.dtype, self.scale)
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libgdn.so")
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libgdn.so (built by gated_delta_rule_conv1d_amd.build)."""
+    global _lib
+    if _lib is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m gated_delta_rule_conv1d_amd.build` "
+                               "(there is no CPU fallback)")
+        lib = ctypes.CDLL(path)
+        P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+        S = ctypes.POINTER(_Shape)
+        sig = {
+            "gdn_status_string": (ctypes.c_char_p, [I32]),
+            "gdn_max_chunks": (I64, [S]),
+            "gdn_chunk_index": (I32, [S, P, P, P, P]),
+            "gdn_conv1d": (I32, [S, P, P, I32, F, P, P, P]),
+            "gdn_conv1d_bwd_workspace": (SZ, [S, I32]),
+            "gdn_conv1d_bwd": (I32, [S, P, P, P, I32, F, P, P, P, P, SZ, P]),
+            "gdn_chunk_fwd_workspace": (SZ, [S]),
+            "gdn_chunk_fwd": (I32, [S, P, P, P, I64, I64, P, P, P, P, P, P, P, SZ, P]),
+            "gdn_chunk_bwd_workspace": (SZ, [S]),
+            "gdn_chunk_bwd": (I32, [S, P, P, P, I64, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+            "gdn_norm_gate": (I32, [S, P, P, P, F, P, P]),
+            "gdn_norm_gate_bwd_workspace": (SZ, [S]),
+            "gdn_norm_gate_bwd": (I32, [S, P, P, P, P, F, P, P, P, P, SZ, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(fn: str, code: int):
+    if code != 0:
+        raise GdnError(fn, code)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None, inner_contig=True):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if inner_contig and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _tok_view(t: torch.Tensor, name: str, rows: int, width: int) -> int:
+    """Token stride of a [T, width] (possibly strided-row) view with unit inner stride."""
+    if t.dim() != 2 or t.shape[0] != rows or t.shape[1] != width or (width > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be a [{rows}, {width}] view with unit inner stride")
+    return t.stride(0)
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is not None and ws.numel() >= nbytes:
+        return ws
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------------------- chunk index
+def max_chunks(shape: Shape) -> int:
+    return int(load().gdn_max_chunks(ctypes.byref(shape.c())))
+
+
+def chunk_index(cu_seqlens: torch.Tensor, shape: Shape) -> Tuple[torch.Tensor, torch.Tensor]:
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (shape.n_seqs + 1,))
+    M = max_chunks(shape)
+    table = torch.empty((M, 4), dtype=torch.int32, device=cu_seqlens.device)
+    first = torch.empty((shape.n_seqs + 1,), dtype=torch.int32, device=cu_seqlens.device)
+    _check("gdn_chunk_index", load().gdn_chunk_index(ctypes.byref(shape.c()), _ptr(cu_seqlens), _ptr(table),
+                                                     _ptr(first), _stream(cu_seqlens.device)))
+    return table, first
+
+
+# ----------------------------------------------------------------------------- conv
+def conv1d(x: torch.Tensor, w_conv: torch.Tensor, cu_seqlens: torch.Tensor, shape: Shape, l2_eps: float = 1e-6,
+           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    dt = shape.torch_dtype
+    T, Cch = shape.total_tokens, shape.channels
+    _need(x, "x", dt, (T, Cch))
+    _need(w_conv, "w_conv", dt)
+    if w_conv.dim() != 2 or w_conv.shape[0] != Cch:
+        raise ValueError("w_conv must be [Cch, width]")
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (shape.n_seqs + 1,))
+    y = torch.empty_like(x) if out is None else out
+    _need(y, "out", dt, (T, Cch))
+    _check("gdn_conv1d", load().gdn_conv1d(ctypes.byref(shape.c()), _ptr(x), _ptr(w_conv), int(w_conv.shape[1]),
+                                           float(l2_eps), _ptr(cu_seqlens), _ptr(y), _stream(x.device)))
+    return y
+
+
+def conv1d_bwd_workspace(shape: Shape, width: int) -> int:
+    return int(load().gdn_conv1d_bwd_workspace(ctypes.byref(shape.c()), int(width)))
+
+
+def conv1d_bwd(dy: torch.Tensor, x: torch.Tensor, w_conv: torch.Tensor, cu_seqlens: torch.Tensor, shape: Shape,
+               l2_eps: float = 1e-6, ws: Optional[torch.Tensor] = None):
+    dt = shape.torch_dtype
+    T, Cch = shape.total_tokens, shape.channels
+    _need(dy, "dy", dt, (T, Cch))
+    _need(x, "x", dt, (T, Cch))
+    _need(w_conv, "w_conv", dt)
+    width = int(w_conv.shape[1])
+    dx = torch.empty_like(x)
+    dw = torch.empty((Cch, width), dtype=torch.float32, device=x.device)
+    nb = conv1d_bwd_workspace(shape, width)
+    ws = _workspace(nb, x.device, ws)
+    _check("gdn_conv1d_bwd", load().gdn_conv1d_bwd(ctypes.byref(shape.c()), _ptr(dy), _ptr(x), _ptr(w_conv), width,
+                                                   float(l2_eps), _ptr(cu_seqlens), _ptr(dx), _ptr(dw), _ptr(ws),
+                                                   ws.numel(), _stream(x.device)))
+    return dx, dw
+
+
+# ----------------------------------------------------------------------------- chunked recurrence
+def chunk_fwd_workspace(shape: Shape) -> int:
+    return int(load().gdn_chunk_fwd_workspace(ctypes.byref(shape.c())))
+
+
+def chunk_bwd_workspace(shape: Shape) -> int:
+    return int(load().gdn_chunk_bwd_workspace(ctypes.byref(shape.c())))
+
+
+def _qkv_strides(q, k, v, shape: Shape):
+    T = shape.total_tokens
+    sq = _tok_view(q, "q", T, shape.h_qk * shape.d_k)
+    sk = _tok_view(k, "k", T, shape.h_qk * shape.d_k)
+    sv = _tok_view(v, "v", T, shape.h_v * shape.d_v)
+    if sq != sk:
+        raise ValueError("q and k must share one token stride")
+    return sq, sv
+
+
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+              cu_seqlens: torch.Tensor, shape: Shape, h0: Optional[torch.Tensor] = None, want_ht: bool = True,
+              ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """q, k: [T, Hk*dk] views; v: [T, Hv*dv] view; g, beta: fp32 [T, Hv].
+    Returns (o [T, Hv, dv], ht [N, Hv, dk, dv] fp32 or None)."""
+    dt = shape.torch_dtype
+    T, N, Hv, dk, dv = shape.total_tokens, shape.n_seqs, shape.h_v, shape.d_k, shape.d_v
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, dt, inner_contig=False)
+    sqk, sv = _qkv_strides(q, k, v, shape)
+    _need(g, "g", torch.float32, (T, Hv))
+    _need(beta, "beta", torch.float32, (T, Hv))
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (N, Hv, dk, dv))
+    o = torch.empty((T, Hv, dv), dtype=dt, device=q.device) if out is None else out
+    ht = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=q.device) if want_ht else None
+    ws = _workspace(chunk_fwd_workspace(shape), q.device, ws)
+    _check("gdn_chunk_fwd", load().gdn_chunk_fwd(ctypes.byref(shape.c()), _ptr(q), _ptr(k), _ptr(v), sqk, sv,
+                                                 _ptr(g), _ptr(beta), _ptr(cu_seqlens), _ptr(h0), _ptr(o), _ptr(ht),
+                                                 _ptr(ws), ws.numel(), _stream(q.device)))
+    return o, ht
+
+
+def chunk_bwd(q, k, v, g, beta, cu_seqlens, shape: Shape, d_o, h0=None, dht=None, dq=None, dk=None, dv=None,
+              want_dh0: bool = True, ws: Optional[torch.Tensor] = None):
+    """Returns dict dq, dk, dv (like q, k, v: [T, H*d]), dg, dbeta [T, Hv] fp32, dh0 (or None)."""
+    dt = shape.torch_dtype
+    T, N, Hk, Hv, dkk, dvv = shape.total_tokens, shape.n_seqs, shape.h_qk, shape.h_v, shape.d_k, shape.d_v
+    sqk, sv = _qkv_strides(q, k, v, shape)
+    _need(d_o, "d_o", dt, (T, Hv, dvv))
+    if dq is None:
+        dq = torch.empty((T, Hk * dkk), dtype=dt, device=q.device)
+    if dk is None:
+        dk = torch.empty((T, Hk * dkk), dtype=dt, device=q.device)
+    if dv is None:
+        dv = torch.empty((T, Hv * dvv), dtype=dt, device=q.device)
+    if _tok_view(dq, "dq", T, Hk * dkk) != sqk or _tok_view(dk, "dk", T, Hk * dkk) != sqk \
+            or _tok_view(dv, "dv", T, Hv * dvv) != sv:
+        raise ValueError("dq/dk/dv must use the token strides of q/k/v")
+    if dht is not None:
+        _need(dht, "dht", torch.float32, (N, Hv, dkk, dvv))
+    dg = torch.empty((T, Hv), dtype=torch.float32, device=q.device)
+    db = torch.empty((T, Hv), dtype=torch.float32, device=q.device)
+    dh0 = torch.empty((N, Hv, dkk, dvv), dtype=torch.float32, device=q.device) if want_dh0 else None
+    ws = _workspace(chunk_bwd_workspace(shape), q.device, ws)
+    _check("gdn_chunk_bwd", load().gdn_chunk_bwd(
+        ctypes.byref(shape.c()), _ptr(q), _ptr(k), _ptr(v), sqk, sv, _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+        _ptr(h0), _ptr(d_o), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(dh0), _ptr(ws),
+        ws.numel(), _stream(q.device)))
+    return dict(dq=dq, dk=dk, dv=dv, dg=dg, dbeta=db, dh0=dh0)
+
+
+# ----------------------------------------------------------------------------- norm gate
+def norm_gate(o: torch.Tensor, z: torch.Tensor, w_norm: torch.Tensor, shape: Shape, eps: float = 1e-6,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    dt = shape.torch_dtype
+    sh = (shape.total_tokens, shape.h_v, shape.d_v)
+    _need(o, "o", dt, sh)
+    _need(z, "z", dt, sh)
+    _need(w_norm, "w_norm", dt, (shape.d_v,))
+    y = torch.empty_like(o) if out is None else out
+    _check("gdn_norm_gate", load().gdn_norm_gate(ctypes.byref(shape.c()), _ptr(o), _ptr(z), _ptr(w_norm), float(eps),
+                                                 _ptr(y), _stream(o.device)))
+    return y
+
+
+def norm_gate_bwd_workspace(shape: Shape) -> int:
+    return int(load().gdn_norm_gate_bwd_workspace(ctypes.byref(shape.c())))
+
+
+def norm_gate_bwd(dy, o, z, w_norm, shape: Shape, eps: float = 1e-6, ws: Optional[torch.Tensor] = None):
+    dt = shape.torch_dtype
+    sh = (shape.total_tokens, shape.h_v, shape.d_v)
+    for t, nm in ((dy, "dy"), (o, "o"), (z, "z")):
+        _need(t, nm, dt, sh)
+    _need(w_norm, "w_norm", dt, (shape.d_v,))
+    d_o = torch.empty_like(o)
+    dz = torch.empty_like(z)
+    dw = torch.empty((shape.d_v,), dtype=torch.float32, device=o.device)
+    ws = _workspace(norm_gate_bwd_workspace(shape), o.device, ws)
+    _check("gdn_norm_gate_bwd", load().gdn_norm_gate_bwd(ctypes.byref(shape.c()), _ptr(dy), _ptr(o), _ptr(z),
+                                                         _ptr(w_norm), float(eps), _ptr(d_o), _ptr(dz), _ptr(dw),
+                                                         _ptr(ws), ws.numel(), _stream(o.device)))
+    return d_o, dz, dw

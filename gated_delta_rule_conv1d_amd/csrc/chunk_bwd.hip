@@ -1,0 +1,647 @@
+// Chunked gated delta rule, reverse mode, and the forward/backward dispatch.
+//
+// Pages: "[Qwen3.5 MoE] Add hybrid decoder model", Summary (GatedDeltaNet);
+// "Support Qwen35 SFT", feature list (training with the layer).
+//
+// With H the state entering a chunk, dHn the gradient w.r.t. the state
+// leaving it, dO' = scale * dO, K~ = diag(e) K (e_s = e^{gamma_last - gamma_s}):
+//   dW  = P^T dO' + K~ dHn                      (state pass, reversed)
+//   dH  = Gam_last dHn + (diag(Gam) Q)^T dO' - Wk^T dW
+//   dWk = -dW H^T,  dT = dW (diag(beta) V)^T + dWk (diag(beta Gam) K)^T
+//   dXu = T^T dW,  dXw = T^T dWk,  dA = strict_lower(-T^T dT T^T)
+//   dV  = diag(beta) dXu
+//   dS  = lower_incl(dO' W^T) * D
+//   dQ  = diag(Gam) dO' H^T + dS K
+//   dK  = diag(e) W dHn^T + diag(beta Gam) dXw + dS^T Q + A~ K + A~^T K,
+//         A~ = dA * beta_r D_rs
+//   dbeta_r = <dXu_r, v_r> + Gam_r <dXw_r, k_r> + sum_s dA_rs D_rs k_r.k_s
+//   dgamma_r = <dQs_r, q_r> - <dKhn_r, k_r> + beta_r Gam_r <dXw_r, k_r>
+//            + rows(dP*P) - cols(dP*P) + rows(dA*A) - cols(dA*A)
+//   dgamma_last += Gam_last <H, dHn> + sum_r <dKhn_r, k_r>
+//   dg_s = sum_{r >= s} dgamma_r   (within the chunk)
+// Every sum has a fixed order; no floating-point atomics.
+#include "chunk_common.cuh"
+
+namespace gdn {
+
+template <typename E, int D, int C>
+void launch_chunk_fwd_core(const ChunkArgs& a, hipStream_t st, bool out_mode);
+
+// ---------------------------------------------------------------------------
+// Reverse state pass, one workgroup per (sequence, v-head, dv tile).
+// ---------------------------------------------------------------------------
+template <typename E, int D, int C, int DVT>
+struct StateBwdSmem {
+  static constexpr int LDQ = D + Pad<E>::E16;
+  static constexpr int LDCE = C + Pad<E>::E16;
+  static constexpr int LD2C = 2 * C + Pad<E>::E16;
+  E Pt[C][LDCE];
+  E Ktil[C][LDQ];
+  E QW[D][LD2C];
+  E OW[DVT][LD2C];
+  E dHt[DVT][LDQ];
+  float gam[C];
+  float Gm[C];
+};
+
+template <typename E, int D, int C, int DVT>
+__global__ __launch_bounds__(kChunkThreads) void state_bwd_kernel(ChunkArgs a) {
+  using S = StateBwdSmem<E, D, C, DVT>;
+  __shared__ S sm;
+  constexpr int NVT = D / DVT;
+  constexpr int NCT = DVT / 16;
+  constexpr int NHT = (D / 16) * NCT;
+  constexpr int NHW = (NHT + kChunkWaves - 1) / kChunkWaves;
+  constexpr int NWT = (C / 16) * NCT;
+  const int bid = blockIdx.x;
+  const int vt = bid % NVT, h = (bid / NVT) % a.Hv, n = bid / (NVT * a.Hv);
+  const int j = h / a.G;
+  const int w = wave_id();
+  const int col0 = vt * DVT;
+
+  f32x4 dH[NHW];
+#pragma unroll
+  for (int i = 0; i < NHW; ++i) {
+    const int t = w + kChunkWaves * i;
+    dH[i] = zero4();
+    if (t < NHT && a.dht) {
+      const int rt = t / NCT, ct = t % NCT;
+      const float* src = a.dht + ((int64_t)n * a.Hv + h) * D * D;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dH[i][e] = src[(rt * 16 + acc_row(e)) * D + col0 + ct * 16 + acc_col()];
+    }
+  }
+  auto write_dHt = [&]() {
+#pragma unroll
+    for (int i = 0; i < NHW; ++i) {
+      const int t = w + kChunkWaves * i;
+      if (t < NHT) {
+        const int rt = t / NCT, ct = t % NCT;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.dHt[ct * 16 + acc_col()][rt * 16 + acc_row(e)] = from_f<E>(dH[i][e]);
+      }
+    }
+  };
+  write_dHt();
+
+  const int c0 = a.seq_chunk0[n], c1 = a.seq_chunk0[n + 1];
+  for (int ci = c1 - 1; ci >= c0; --ci) {
+    const int4 ent = chunk_entry(a.table, ci);
+    const int tok0 = ent.y, len = ent.z;
+    const int64_t slot = (int64_t)ci * a.Hv + h;
+    {  // gradient w.r.t. the state leaving this chunk
+      E* dst = (E*)a.dHn + slot * D * D;
+#pragma unroll
+      for (int i = 0; i < NHW; ++i) {
+        const int t = w + kChunkWaves * i;
+        if (t < NHT) store_tile<E>(dst, D, (t / NCT) * 16, col0 + (t % NCT) * 16, dH[i], D);
+      }
+    }
+    for (int e = threadIdx.x; e < C; e += kChunkThreads) {
+      const float gm = a.gam[slot * C + e];
+      sm.gam[e] = gm;
+      sm.Gm[e] = __expf(gm);
+    }
+    __syncthreads();
+    rows2s_t<E, C, C>(&sm.Pt[0][0], S::LDCE, (const E*)a.P + slot * C * C, C, C, nullptr, 1.f);
+    rows2s_t<E, D, C>(&sm.Ktil[0][0], S::LDQ, (const E*)a.Kt + slot * D * C, C, D, nullptr, 1.f);
+    rows2s_t<E, C, D>(&sm.QW[0][0], S::LD2C, (const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D, a.sqk, len,
+                      sm.Gm, 1.f);
+    rows2s_t<E, C, D>(&sm.QW[0][C], S::LD2C, (const E*)a.Wk + slot * C * D, D, C, nullptr, -1.f);
+    rows2s_t<E, C, DVT>(&sm.OW[0][0], S::LD2C, (const E*)a.d_o + (int64_t)tok0 * a.Hv * D + (int64_t)h * D + col0,
+                        (int64_t)a.Hv * D, len, nullptr, a.scale);
+    __syncthreads();
+
+    E* dWg = (E*)a.dW + slot * C * D;
+    for (int t = w; t < NWT; t += kChunkWaves) {
+      const int rt = t / NCT, ct = t % NCT;
+      f32x4 acc = mm_tile<E, C>(zero4(), &sm.Pt[rt * 16][0], S::LDCE, &sm.OW[ct * 16][0], S::LD2C);
+      acc = mm_tile<E, D>(acc, &sm.Ktil[rt * 16][0], S::LDQ, &sm.dHt[ct * 16][0], S::LDQ);
+      store_tile<E>(dWg, D, rt * 16, col0 + ct * 16, acc, C);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.OW[ct * 16 + acc_col()][C + rt * 16 + acc_row(e)] = from_f<E>(acc[e]);
+    }
+    __syncthreads();
+    const float gl = sm.Gm[len - 1];
+#pragma unroll
+    for (int i = 0; i < NHW; ++i) {
+      const int t = w + kChunkWaves * i;
+      if (t < NHT) {
+        const int rt = t / NCT, ct = t % NCT;
+        const f32x4 y = mm_tile<E, 2 * C>(zero4(), &sm.QW[rt * 16][0], S::LD2C, &sm.OW[ct * 16][0], S::LD2C);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dH[i][e] = gl * dH[i][e] + y[e];
+      }
+    }
+    __syncthreads();
+    write_dHt();
+  }
+  if (a.dh0) {
+    float* dst = a.dh0 + ((int64_t)n * a.Hv + h) * D * D;
+#pragma unroll
+    for (int i = 0; i < NHW; ++i) {
+      const int t = w + kChunkWaves * i;
+      if (t < NHT) {
+        const int rt = t / NCT, ct = t % NCT;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(rt * 16 + acc_row(e)) * D + col0 + ct * 16 + acc_col()] = dH[i][e];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Contractions over d_v, one workgroup per (chunk, v-head):
+//   dWk = -dW Hc^T  (kept in LDS and written to workspace)
+//   dT  = beta_s (dW V^T)_rs + beta_s Gam_s (dWk K^T)_rs
+//   hdot = <Hc, dHn>
+// ---------------------------------------------------------------------------
+template <typename E, int D, int C>
+struct GradASmem {
+  static constexpr int LDQ = D + Pad<E>::E16;
+  E dWk[C][LDQ];
+  E Vs[C][LDQ];
+  E Ks[C][LDQ];
+  float bs[C];
+  float red[kChunkThreads];
+};
+
+template <typename E, int D, int C>
+__global__ __launch_bounds__(kChunkThreads) void grad_a_kernel(ChunkArgs a) {
+  using S = GradASmem<E, D, C>;
+  __shared__ S sm;
+  constexpr int NT = C / 16, ND = D / 16;
+  const int ci = blockIdx.x, h = blockIdx.y;
+  const int4 ent = chunk_entry(a.table, ci);
+  if (ent.x < 0) return;
+  const int tok0 = ent.y, len = ent.z;
+  const int j = h / a.G;
+  const int w = wave_id(), tid = threadIdx.x;
+  const int64_t slot = (int64_t)ci * a.Hv + h;
+  const E* Hc = (const E*)a.Hc + slot * D * D;
+  const E* dW = (const E*)a.dW + slot * C * D;
+
+  rows2s<E, C, D>(&sm.Vs[0][0], S::LDQ, (const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)h * D, a.sv, len);
+  rows2s<E, C, D>(&sm.Ks[0][0], S::LDQ, (const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D, a.sqk, len);
+  for (int e = tid; e < C; e += kChunkThreads) sm.bs[e] = e < len ? a.beta[(int64_t)(tok0 + e) * a.Hv + h] : 0.f;
+  E* dWkg = (E*)a.dWk + slot * C * D;
+  for (int t = w; t < NT * ND; t += kChunkWaves) {
+    const int rt = t / ND, ct = t % ND;
+    const f32x4 acc = mm_tile<E, D>(zero4(), dW + rt * 16 * D, D, Hc + ct * 16 * D, D);
+    f32x4 neg;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      neg[e] = -acc[e];
+      sm.dWk[rt * 16 + acc_row(e)][ct * 16 + acc_col()] = from_f<E>(neg[e]);
+    }
+    store_tile<E>(dWkg, D, rt * 16, ct * 16, neg, C);
+  }
+  // <Hc, dHn>
+  {
+    const E* dHn = (const E*)a.dHn + slot * D * D;
+    float s = 0.f;
+    for (int e = tid; e < D * D; e += kChunkThreads) s += to_f<E>(Hc[e]) * to_f<E>(dHn[e]);
+    sm.red[tid] = s;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float s = 0.f;
+    for (int i = 0; i < kChunkThreads; ++i) s += sm.red[i];
+    a.hdot[slot] = s;
+  }
+  const float* gam = a.gam + slot * C;
+  float* dTg = a.dT + slot * C * C;
+  for (int t = w; t < NT * NT; t += kChunkWaves) {
+    const int rt = t / NT, ct = t % NT;
+    const f32x4 xu = mm_tile<E, D>(zero4(), dW + rt * 16 * D, D, &sm.Vs[ct * 16][0], S::LDQ);
+    const f32x4 xw = mm_tile<E, D>(zero4(), &sm.dWk[rt * 16][0], S::LDQ, &sm.Ks[ct * 16][0], S::LDQ);
+    const int s = ct * 16 + acc_col();
+    const float bsv = sm.bs[s], bg = bsv * __expf(gam[s]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dTg[(rt * 16 + acc_row(e)) * C + s] = bsv * xu[e] + bg * xw[e];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// WY-representation gradients, one workgroup per (chunk, k-head), looping
+// over the k-head's v-heads; dq and dk accumulate in registers across them.
+// ---------------------------------------------------------------------------
+template <typename E, int D, int C>
+struct GradBSmem {
+  static constexpr int LDQ = D + Pad<E>::E16;
+  static constexpr int LDCE = C + Pad<E>::E16;
+  static constexpr int LD2C = 2 * C + Pad<E>::E16;
+  static constexpr int LDCF = C + 4;
+  static constexpr int NT = C / 16, ND = D / 16;
+  E QKt[D][LD2C];   // [Q^T | K^T]
+  float Am[C][LDCF];  // A, then dA
+  float Tm[C][LDCF];
+  float Tt[C][LDCF];
+  float dT[C][LDCF];
+  union U {
+    struct { E dUt[D][LDCE]; E dWkt[D][LDCE]; } x;
+    float M1t[C][LDCF];
+    struct { E dS[C][LDCE]; E dSA[C][LD2C]; E Att[C][LDCE]; } s;
+    float Xs[kChunkWaves][16][20];
+  } r;
+  float gam[C], beta[C], Gm[C], em[C];
+  float pCD[4][ND][C];   // row partials of C x D tiles: dXu.v, dXw.k, dQs.q, dKhn.k
+  float pCC[5][NT][C];   // dA D Skk rows, dA*A rows, dA*A cols, dP*P rows, dP*P cols
+};
+
+template <typename E, int D, int C>
+__global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
+  using S = GradBSmem<E, D, C>;
+  __shared__ S sm;
+  constexpr int NT = S::NT, ND = S::ND;
+  constexpr int NQT = NT * ND;
+  constexpr int NQW = (NQT + kChunkWaves - 1) / kChunkWaves;
+  const int ci = blockIdx.x, j = blockIdx.y;
+  const int4 ent = chunk_entry(a.table, ci);
+  if (ent.x < 0) return;
+  const int tok0 = ent.y, len = ent.z;
+  const int w = wave_id(), lane = lane_id(), tid = threadIdx.x;
+  const E* qg = (const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D;
+  const E* kg = (const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D;
+
+  rows2s_t<E, C, D>(&sm.QKt[0][0], S::LD2C, qg, a.sqk, len, nullptr, 1.f);
+  rows2s_t<E, C, D>(&sm.QKt[0][C], S::LD2C, kg, a.sqk, len, nullptr, 1.f);
+
+  f32x4 dQ[NQW], dK[NQW];
+#pragma unroll
+  for (int i = 0; i < NQW; ++i) dQ[i] = dK[i] = zero4();
+
+  for (int gi = 0; gi < a.G; ++gi) {
+    const int h = j * a.G + gi;
+    const int64_t slot = (int64_t)ci * a.Hv + h;
+    const E* vg = (const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)h * D;
+    const E* dog = (const E*)a.d_o + (int64_t)tok0 * a.Hv * D + (int64_t)h * D;
+    const int64_t ldo = (int64_t)a.Hv * D;
+    for (int e = tid; e < C; e += kChunkThreads) {
+      const float gm = a.gam[slot * C + e];
+      sm.gam[e] = gm;
+      sm.Gm[e] = __expf(gm);
+      sm.beta[e] = e < len ? a.beta[(int64_t)(tok0 + e) * a.Hv + h] : 0.f;
+    }
+    __syncthreads();
+    for (int e = tid; e < C; e += kChunkThreads) sm.em[e] = e < len ? __expf(sm.gam[len - 1] - sm.gam[e]) : 0.f;
+    // A = strict_lower(beta_r D_rs k_r.k_s)
+    for (int t = w; t < NT * NT; t += kChunkWaves) {
+      const int rt = t / NT, ct = t % NT;
+      f32x4 skk = zero4();
+      if (rt * 16 < len && ct * 16 < len)
+        skk = mm_tile_rows<E, D>(zero4(), kg + (int64_t)rt * 16 * a.sqk, a.sqk, len - rt * 16,
+                                 kg + (int64_t)ct * 16 * a.sqk, a.sqk, len - ct * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = rt * 16 + acc_row(e), s = ct * 16 + acc_col();
+        sm.Am[r][s] = (s < r) ? sm.beta[r] * __expf(sm.gam[r] - sm.gam[s]) * skk[e] : 0.f;
+      }
+    }
+    __syncthreads();
+    unit_lower_inverse<C, S::LDCF>(sm.Am, sm.Tm, sm.Tt, sm.r.Xs);
+    // dU (= dW) and dWk transposed into LDS, dT
+    rows2s_t<E, C, D>(&sm.r.x.dUt[0][0], S::LDCE, (const E*)a.dW + slot * C * D, D, C, nullptr, 1.f);
+    rows2s_t<E, C, D>(&sm.r.x.dWkt[0][0], S::LDCE, (const E*)a.dWk + slot * C * D, D, C, nullptr, 1.f);
+    for (int e = tid; e < C * C; e += kChunkThreads) sm.dT[e / C][e % C] = a.dT[slot * C * C + e];
+    __syncthreads();
+    // dXu = T^T dU -> dv, <dXu, v>;  dXw = T^T dWk -> dK, <dXw, k>
+    E* dvg = (E*)a.dv + (int64_t)tok0 * a.sv + (int64_t)h * D;
+#pragma unroll
+    for (int i = 0; i < NQW; ++i) {
+      const int t = w + kChunkWaves * i;
+      if (t < NQT) {
+        const int rt = t / ND, ct = t % ND;
+        const f32x4 xu = mm_tile_fa<E, C>(zero4(), &sm.Tt[rt * 16][0], S::LDCF, &sm.r.x.dUt[ct * 16][0], S::LDCE);
+        const f32x4 xw = mm_tile_fa<E, C>(zero4(), &sm.Tt[rt * 16][0], S::LDCF, &sm.r.x.dWkt[ct * 16][0], S::LDCE);
+        f32x4 dvv;
+        float pu[4], pw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = rt * 16 + acc_row(e), c = ct * 16 + acc_col();
+          const float br = sm.beta[r];
+          dvv[e] = br * xu[e];
+          const float vv = r < len ? to_f<E>(vg[(int64_t)r * a.sv + c]) : 0.f;
+          pu[e] = xu[e] * vv;
+          pw[e] = xw[e] * to_f<E>(sm.QKt[c][C + r]);
+          dK[i][e] += br * sm.Gm[r] * xw[e];
+        }
+        store_tile<E>(dvg, a.sv, rt * 16, ct * 16, dvv, len);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pu[e] = group_sum<16>(pu[e]);
+          pw[e] = group_sum<16>(pw[e]);
+        }
+        if ((lane & 15) == 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sm.pCD[0][ct][rt * 16 + acc_row(e)] = pu[e];
+            sm.pCD[1][ct][rt * 16 + acc_row(e)] = pw[e];
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // M1 = dT T^T  (stored transposed)
+    for (int t = w; t < NT * NT; t += kChunkWaves) {
+      const int rt = t / NT, ct = t % NT;
+      const f32x4 m = mm_tile<float, C>(zero4(), &sm.dT[rt * 16][0], S::LDCF, &sm.Tm[ct * 16][0], S::LDCF);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.r.M1t[ct * 16 + acc_col()][rt * 16 + acc_row(e)] = m[e];
+    }
+    __syncthreads();
+    // dA = strict_lower(-T^T M1)
+    for (int t = w; t < NT * NT; t += kChunkWaves) {
+      const int rt = t / NT, ct = t % NT;
+      const f32x4 m = mm_tile<float, C>(zero4(), &sm.Tt[rt * 16][0], S::LDCF, &sm.r.M1t[ct * 16][0], S::LDCF);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = rt * 16 + acc_row(e), s = ct * 16 + acc_col();
+        sm.Am[r][s] = (s < r && r < len) ? -m[e] : 0.f;
+      }
+    }
+    __syncthreads();
+    // C x C pass: A~, dS, and the dgamma / dbeta terms of A and P
+    const E* Wg = (const E*)a.W + slot * C * D;
+    const E* Pg = (const E*)a.P + slot * C * C;
+    for (int t = w; t < NT * NT; t += kChunkWaves) {
+      const int rt = t / NT, ct = t % NT;
+      f32x4 skk = zero4(), dp = zero4();
+      if (rt * 16 < len && ct * 16 < len) {
+        skk = mm_tile_rows<E, D>(zero4(), kg + (int64_t)rt * 16 * a.sqk, a.sqk, len - rt * 16,
+                                 kg + (int64_t)ct * 16 * a.sqk, a.sqk, len - ct * 16);
+        dp = mm_tile_rows<E, D>(zero4(), dog + (int64_t)rt * 16 * ldo, ldo, len - rt * 16, Wg + ct * 16 * D, D, 16);
+      }
+      float rb[4], ra[4], rp[4], ca = 0.f, cp = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = rt * 16 + acc_row(e), s = ct * 16 + acc_col();
+        const float dd = (s <= r) ? __expf(sm.gam[r] - sm.gam[s]) : 0.f;
+        const float dA = sm.Am[r][s];
+        const float At = dA * sm.beta[r] * dd;
+        const float AdA = At * skk[e];
+        const float dP = (s <= r && r < len) ? a.scale * dp[e] : 0.f;
+        const float PdP = dP * to_f<E>(Pg[r * C + s]);
+        const float dS = dP * dd;
+        rb[e] = dA * dd * skk[e];
+        ra[e] = AdA;
+        rp[e] = PdP;
+        ca += AdA;
+        cp += PdP;
+        sm.r.s.dS[r][s] = from_f<E>(dS);
+        sm.r.s.dSA[s][r] = from_f<E>(dS);
+        sm.r.s.dSA[r][C + s] = from_f<E>(At);
+        sm.r.s.Att[s][r] = from_f<E>(At);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        rb[e] = group_sum<16>(rb[e]);
+        ra[e] = group_sum<16>(ra[e]);
+        rp[e] = group_sum<16>(rp[e]);
+      }
+      ca += __shfl_xor(ca, 16, kWave);
+      ca += __shfl_xor(ca, 32, kWave);
+      cp += __shfl_xor(cp, 16, kWave);
+      cp += __shfl_xor(cp, 32, kWave);
+      if ((lane & 15) == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = rt * 16 + acc_row(e);
+          sm.pCC[0][ct][r] = rb[e];
+          sm.pCC[1][ct][r] = ra[e];
+          sm.pCC[3][ct][r] = rp[e];
+        }
+      }
+      if (lane < 16) {
+        sm.pCC[2][rt][ct * 16 + lane] = ca;
+        sm.pCC[4][rt][ct * 16 + lane] = cp;
+      }
+    }
+    __syncthreads();
+    // dQ += Gam dO' Hc^T + dS K;   dK += e W dHn^T + [dS^T | A~][Q; K] + A~^T K
+    const E* Hc = (const E*)a.Hc + slot * D * D;
+    const E* dHn = (const E*)a.dHn + slot * D * D;
+#pragma unroll
+    for (int i = 0; i < NQW; ++i) {
+      const int t = w + kChunkWaves * i;
+      if (t < NQT) {
+        const int rt = t / ND, ct = t % ND;
+        f32x4 qs = zero4(), kh = zero4();
+        if (rt * 16 < len) {
+          qs = mm_tile_rows<E, D>(zero4(), dog + (int64_t)rt * 16 * ldo, ldo, len - rt * 16, Hc + ct * 16 * D, D, 16);
+          kh = mm_tile<E, D>(zero4(), Wg + rt * 16 * D, D, dHn + ct * 16 * D, D);
+        }
+        f32x4 sq = mm_tile<E, C>(zero4(), &sm.r.s.dS[rt * 16][0], S::LDCE, &sm.QKt[ct * 16][C], S::LD2C);
+        f32x4 sk = mm_tile<E, 2 * C>(zero4(), &sm.r.s.dSA[rt * 16][0], S::LD2C, &sm.QKt[ct * 16][0], S::LD2C);
+        sk = mm_tile<E, C>(sk, &sm.r.s.Att[rt * 16][0], S::LDCE, &sm.QKt[ct * 16][C], S::LD2C);
+        float pq[4], pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = rt * 16 + acc_row(e), c = ct * 16 + acc_col();
+          const float qsv = a.scale * sm.Gm[r] * qs[e];
+          const float khv = sm.em[r] * kh[e];
+          dQ[i][e] += qsv + sq[e];
+          dK[i][e] += khv + sk[e];
+          pq[e] = qsv * to_f<E>(sm.QKt[c][r]);
+          pk[e] = khv * to_f<E>(sm.QKt[c][C + r]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pq[e] = group_sum<16>(pq[e]);
+          pk[e] = group_sum<16>(pk[e]);
+        }
+        if ((lane & 15) == 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sm.pCD[2][ct][rt * 16 + acc_row(e)] = pq[e];
+            sm.pCD[3][ct][rt * 16 + acc_row(e)] = pk[e];
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // per-row totals, then dg = reverse cumulative sum within the chunk
+    if (w == 0) {
+      const int r = lane;
+      float dbeta = 0.f, dgam = 0.f, tk = 0.f;
+      if (r < C) {
+        float su = 0.f, sw = 0.f, sq = 0.f;
+        for (int c = 0; c < ND; ++c) {
+          su += sm.pCD[0][c][r];
+          sw += sm.pCD[1][c][r];
+          sq += sm.pCD[2][c][r];
+          tk += sm.pCD[3][c][r];
+        }
+        float rb = 0.f, ar = 0.f, ac = 0.f, pr = 0.f, pc = 0.f;
+        for (int c = 0; c < NT; ++c) {
+          rb += sm.pCC[0][c][r];
+          ar += sm.pCC[1][c][r];
+          ac += sm.pCC[2][c][r];
+          pr += sm.pCC[3][c][r];
+          pc += sm.pCC[4][c][r];
+        }
+        dbeta = su + sm.Gm[r] * sw + rb;
+        dgam = sq - tk + sm.beta[r] * sm.Gm[r] * sw + (ar - ac) + (pr - pc);
+        if (r >= len) dgam = tk = 0.f;
+      }
+      float tks = tk;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) tks += __shfl_xor(tks, off, kWave);
+      if (r == len - 1) dgam += sm.Gm[len - 1] * a.hdot[slot] + tks;
+      // reverse inclusive scan: dg_r = sum_{r' >= r} dgam_{r'}
+      float x = dgam;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const float y = __shfl_down(x, off, kWave);
+        if (r + off < kWave) x += y;
+      }
+      if (r < len) {
+        a.dg[(int64_t)(tok0 + r) * a.Hv + h] = x;
+        a.dbeta[(int64_t)(tok0 + r) * a.Hv + h] = dbeta;
+      }
+    }
+    __syncthreads();
+  }
+  E* dqg = (E*)a.dq + (int64_t)tok0 * a.sqk + (int64_t)j * D;
+  E* dkg = (E*)a.dk + (int64_t)tok0 * a.sqk + (int64_t)j * D;
+#pragma unroll
+  for (int i = 0; i < NQW; ++i) {
+    const int t = w + kChunkWaves * i;
+    if (t < NQT) {
+      const int rt = t / ND, ct = t % ND;
+      store_tile<E>(dqg, a.sqk, rt * 16, ct * 16, dQ[i], len);
+      store_tile<E>(dkg, a.sqk, rt * 16, ct * 16, dK[i], len);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side: workspace plan and dispatch
+// ---------------------------------------------------------------------------
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsPlan {
+  size_t table, seq0, Wk, U, P, Kt, gam, end_fwd;
+  size_t Hc, W, dHn, dW, dT, dWk, hdot, end_bwd;
+};
+
+static WsPlan plan(const gdn_shape* s) {
+  const size_t M = (size_t)max_chunks(s), Hv = s->h_v, C = s->chunk, D = s->d_k;
+  const size_t es = s->dtype == GDN_BF16 ? 2 : 4;
+  WsPlan p;
+  size_t o = 0;
+  p.table = o; o = align256(o + M * 16);
+  p.seq0 = o; o = align256(o + ((size_t)s->n_seqs + 1) * 4);
+  p.Wk = o; o = align256(o + M * Hv * C * D * es);
+  p.U = o; o = align256(o + M * Hv * C * D * es);
+  p.P = o; o = align256(o + M * Hv * C * C * es);
+  p.Kt = o; o = align256(o + M * Hv * D * C * es);
+  p.gam = o; o = align256(o + M * Hv * C * 4);
+  p.end_fwd = o;
+  p.Hc = o; o = align256(o + M * Hv * D * D * es);
+  p.W = o; o = align256(o + M * Hv * C * D * es);
+  p.dHn = o; o = align256(o + M * Hv * D * D * es);
+  p.dW = o; o = align256(o + M * Hv * C * D * es);
+  p.dT = o; o = align256(o + M * Hv * C * C * 4);
+  p.dWk = o; o = align256(o + M * Hv * C * D * es);
+  p.hdot = o; o = align256(o + M * Hv * 4);
+  p.end_bwd = o;
+  return p;
+}
+
+size_t chunk_fwd_ws_bytes(const gdn_shape* s) { return plan(s).end_fwd; }
+size_t chunk_bwd_ws_bytes(const gdn_shape* s) { return plan(s).end_bwd; }
+
+static void fill_ws(ChunkArgs& a, const gdn_shape* s, void* ws) {
+  const WsPlan p = plan(s);
+  char* b = (char*)ws;
+  a.table = (const int32_t*)(b + p.table);
+  a.seq_chunk0 = (const int32_t*)(b + p.seq0);
+  a.Wk = b + p.Wk;
+  a.U = b + p.U;
+  a.P = b + p.P;
+  a.Kt = b + p.Kt;
+  a.gam = (float*)(b + p.gam);
+  a.Hc = b + p.Hc;
+  a.W = b + p.W;
+  a.dHn = b + p.dHn;
+  a.dW = b + p.dW;
+  a.dT = (float*)(b + p.dT);
+  a.dWk = b + p.dWk;
+  a.hdot = (float*)(b + p.hdot);
+}
+
+template <typename E, int D, int C>
+constexpr bool fits() {
+  constexpr size_t lim = 160 * 1024;
+  return sizeof(PrepSmem<E, D, C>) <= lim && sizeof(StateSmem<E, D, C, (D >= 32 ? 32 : D), true>) <= lim &&
+         sizeof(StateBwdSmem<E, D, C, (D >= 32 ? 32 : D)>) <= lim && sizeof(GradASmem<E, D, C>) <= lim &&
+         sizeof(GradBSmem<E, D, C>) <= lim;
+}
+
+template <typename E, int D, int C>
+static void launch_chunk_bwd_core(const ChunkArgs& a, hipStream_t st) {
+  constexpr int DVT = D >= 32 ? 32 : D;
+  launch_chunk_fwd_core<E, D, C>(a, st, false);  // Hc, W per chunk
+  state_bwd_kernel<E, D, C, DVT><<<dim3(a.N * a.Hv * (D / DVT)), kChunkThreads, 0, st>>>(a);
+  grad_a_kernel<E, D, C><<<dim3(a.max_chunks, a.Hv), kChunkThreads, 0, st>>>(a);
+  grad_b_kernel<E, D, C><<<dim3(a.max_chunks, a.Hk), kChunkThreads, 0, st>>>(a);
+}
+
+// Calls f.template operator()<E, D, C>() for the runtime (dtype, d, chunk)
+// when that combination fits in LDS; returns false otherwise.
+template <typename F>
+static bool dispatch(const gdn_shape* s, F&& f) {
+#define GDN_CASE(E, D, C)                                       \
+  if (s->d_k == D && s->chunk == C) {                           \
+    if constexpr (fits<E, D, C>()) { f.template operator()<E, D, C>(); return true; } \
+    return false;                                               \
+  }
+  if (s->dtype == GDN_BF16) {
+    GDN_CASE(bf16, 16, 16) GDN_CASE(bf16, 16, 32) GDN_CASE(bf16, 16, 64)
+    GDN_CASE(bf16, 32, 16) GDN_CASE(bf16, 32, 32) GDN_CASE(bf16, 32, 64)
+    GDN_CASE(bf16, 64, 16) GDN_CASE(bf16, 64, 32) GDN_CASE(bf16, 64, 64)
+    GDN_CASE(bf16, 128, 16) GDN_CASE(bf16, 128, 32) GDN_CASE(bf16, 128, 64)
+  } else if (s->dtype == GDN_F32) {
+    GDN_CASE(float, 16, 16) GDN_CASE(float, 16, 32) GDN_CASE(float, 16, 64)
+    GDN_CASE(float, 32, 16) GDN_CASE(float, 32, 32) GDN_CASE(float, 32, 64)
+    GDN_CASE(float, 64, 16) GDN_CASE(float, 64, 32) GDN_CASE(float, 64, 64)
+    GDN_CASE(float, 128, 16) GDN_CASE(float, 128, 32)
+  }
+#undef GDN_CASE
+  return false;
+}
+
+bool chunk_supported(const gdn_shape* s) {
+  return dispatch(s, [&]<typename E, int D, int C>() {});
+}
+
+bool run_chunk_fwd(const gdn_shape* s, const void* q, const void* k, const void* v, int64_t sqk, int64_t sv,
+                   const float* g, const float* beta, const int32_t* cu, const float* h0, void* o, float* ht,
+                   void* ws, hipStream_t st) {
+  ChunkArgs a = {};
+  a.q = q; a.k = k; a.v = v; a.sqk = sqk; a.sv = sv; a.g = g; a.beta = beta; a.cu = cu; a.h0 = h0;
+  a.o = o; a.ht = ht;
+  a.N = s->n_seqs; a.T = s->total_tokens; a.Hk = s->h_qk; a.Hv = s->h_v; a.G = s->h_v / s->h_qk;
+  a.max_chunks = (int)max_chunks(s); a.scale = s->scale;
+  fill_ws(a, s, ws);
+  run_chunk_index(s, cu, (int32_t*)a.table, (int32_t*)a.seq_chunk0, st);
+  return dispatch(s, [&]<typename E, int D, int C>() { launch_chunk_fwd_core<E, D, C>(a, st, true); });
+}
+
+bool run_chunk_bwd(const gdn_shape* s, const void* q, const void* k, const void* v, int64_t sqk, int64_t sv,
+                   const float* g, const float* beta, const int32_t* cu, const float* h0, const void* d_o,
+                   const float* dht, void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0,
+                   void* ws, hipStream_t st) {
+  ChunkArgs a = {};
+  a.q = q; a.k = k; a.v = v; a.sqk = sqk; a.sv = sv; a.g = g; a.beta = beta; a.cu = cu; a.h0 = h0;
+  a.o = nullptr; a.ht = nullptr;
+  a.d_o = d_o; a.dht = dht; a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
+  a.N = s->n_seqs; a.T = s->total_tokens; a.Hk = s->h_qk; a.Hv = s->h_v; a.G = s->h_v / s->h_qk;
+  a.max_chunks = (int)max_chunks(s); a.scale = s->scale;
+  fill_ws(a, s, ws);
+  run_chunk_index(s, cu, (int32_t*)a.table, (int32_t*)a.seq_chunk0, st);
+  return dispatch(s, [&]<typename E, int D, int C>() { launch_chunk_bwd_core<E, D, C>(a, st); });
+}
+
+}  // namespace gdn

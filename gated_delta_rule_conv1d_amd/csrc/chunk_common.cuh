@@ -1,0 +1,205 @@
+// Shared pieces of the chunked gated-delta-rule kernels (forward and backward).
+#pragma once
+
+#include "gdn_common.cuh"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+constexpr int kChunkThreads = 256;  // 4 waves per workgroup
+constexpr int kChunkWaves = kChunkThreads / kWave;
+
+struct ChunkArgs {
+  // inputs
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t sqk, sv;
+  const float* g;
+  const float* beta;
+  const int32_t* cu;
+  const float* h0;
+  // forward outputs
+  void* o;
+  float* ht;
+  // backward inputs / outputs
+  const void* d_o;
+  const float* dht;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dg;
+  float* dbeta;
+  float* dh0;
+  // sizes
+  int N, T, Hk, Hv, G, max_chunks;
+  float scale;
+  // workspace
+  const int32_t* table;       // [max_chunks][4]
+  const int32_t* seq_chunk0;  // [N+1]
+  void* Wk;                   // [slot][C][D]
+  void* U;                    // [slot][C][D]
+  void* P;                    // [slot][C][C]
+  void* Kt;                   // [slot][D][C]
+  float* gam;                 // [slot][C]
+  void* Hc;                   // [slot][D][D]  state entering the chunk
+  void* W;                    // [slot][C][D]  W = U - Wk Hc
+  void* dHn;                  // [slot][D][D]  gradient w.r.t. the state leaving the chunk
+  void* dW;                   // [slot][C][D]
+  float* dT;                  // [slot][C][C]
+  void* dWk;                  // [slot][C][D]
+  float* hdot;                // [slot]        <Hc, dHn>
+};
+
+template <typename E> struct Pad {
+  static constexpr int E16 = 16 / (int)sizeof(E);  // elements per 16 bytes
+};
+
+// Element load/store of one accumulator tile straight to/from global memory.
+template <typename E>
+__device__ __forceinline__ void store_tile(E* base, int64_t ld, int r0, int c0, f32x4 v, int rows_valid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = r0 + acc_row(i);
+    if (r < rows_valid) base[(int64_t)r * ld + c0 + acc_col()] = from_f<E>(v[i]);
+  }
+}
+
+// copy a [R][Ccols] row-major E tile between global (dense, ld = Ccols) and LDS
+// (row stride lds), 16 bytes per thread step
+template <typename E, int R, int Ccols>
+__device__ __forceinline__ void g2s(E* s, int lds, const E* g) {
+  constexpr int V = Vec<E>::N;
+  constexpr int PER_ROW = Ccols / V;
+  for (int e = threadIdx.x; e < R * PER_ROW; e += kChunkThreads) {
+    const int r = e / PER_ROW, c = (e % PER_ROW) * V;
+    *reinterpret_cast<uint4*>(s + r * lds + c) = *reinterpret_cast<const uint4*>(g + (int64_t)r * Ccols + c);
+  }
+}
+
+// rows [0, len) of a token-major input (row stride ld elements) into LDS; zero rows past len
+template <typename E, int R, int Ccols>
+__device__ __forceinline__ void rows2s(E* s, int lds, const E* g, int64_t ld, int len) {
+  constexpr int V = Vec<E>::N;
+  constexpr int PER_ROW = Ccols / V;
+  for (int e = threadIdx.x; e < R * PER_ROW; e += kChunkThreads) {
+    const int r = e / PER_ROW, c = (e % PER_ROW) * V;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (r < len) val = *reinterpret_cast<const uint4*>(g + (int64_t)r * ld + c);
+    *reinterpret_cast<uint4*>(s + r * lds + c) = val;
+  }
+}
+
+// rows [0, len) of a token-major input written transposed into LDS:
+// s[c * lds + r] = g[r * ld + c]; zero past len.  Optional per-row scale.
+template <typename E, int R, int Ccols>
+__device__ __forceinline__ void rows2s_t(E* s, int lds, const E* g, int64_t ld, int len, const float* rscale,
+                                         float mult) {
+  constexpr int V = Vec<E>::N;
+  constexpr int PER_ROW = Ccols / V;
+  for (int e = threadIdx.x; e < R * PER_ROW; e += kChunkThreads) {
+    const int r = e / PER_ROW, c = (e % PER_ROW) * V;
+    float val[V];
+    if (r < len) {
+      Vec<E>::load(g + (int64_t)r * ld + c, val);
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; ++i) val[i] = 0.f;
+    }
+    const float f = (rscale ? rscale[r] : 1.f) * mult;
+#pragma unroll
+    for (int i = 0; i < V; ++i) s[(c + i) * lds + r] = from_f<E>(val[i] * f);
+  }
+}
+
+__device__ __forceinline__ int4 chunk_entry(const int32_t* table, int ci) {
+  return reinterpret_cast<const int4*>(table)[ci];
+}
+
+template <typename E, int D, int C>
+struct PrepSmem {
+  static constexpr int LDQ = D + Pad<E>::E16;   // [C][LDQ]  E
+  static constexpr int LDCE = C + Pad<E>::E16;  // [*][LDCE] E
+  static constexpr int LDCF = C + 4;            // [C][LDCF] f32
+  E Qs[C][LDQ];
+  E Ks[C][LDQ];
+  E Kt[D][LDCE];
+  E Vt[D][LDCE];
+  float Sk[C][LDCF];
+  float Am[C][LDCF];
+  float Tm[C][LDCF];
+  float Tt[C][LDCF];
+  E TB[C][LDCE];
+  float gam[C];
+  float beta[C];
+  float Xs[kChunkWaves][16][20];
+};
+
+// (I + A)^-1 for strictly lower A [C][C] (fp32 in LDS) into Tm and Tt = Tm^T.
+template <int C, int LDCF>
+__device__ __forceinline__ void unit_lower_inverse(const float (*Am)[LDCF], float (*Tm)[LDCF], float (*Tt)[LDCF],
+                                                   float (*Xs)[16][20]) {
+  const int tid = threadIdx.x, w = wave_id();
+  for (int e = tid; e < C * C; e += kChunkThreads) {
+    Tm[e / C][e % C] = 0.f;
+    Tt[e / C][e % C] = 0.f;
+  }
+  __syncthreads();
+  if (tid < C) {  // diagonal 16x16 blocks, one column per lane
+    const int o = (tid >> 4) * 16, c = tid & 15;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = (r == c) ? 1.f : 0.f;
+#pragma unroll
+      for (int s = 0; s < r; ++s) acc -= Am[o + r][o + s] * x[s];
+      x[r] = acc;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      Tm[o + r][o + c] = x[r];
+      Tt[o + c][o + r] = x[r];
+    }
+  }
+  __syncthreads();
+  constexpr int NB = C / 16;
+#pragma unroll
+  for (int i = 1; i < NB; ++i) {
+    // T_{i,jb} = -T_ii sum_{k=jb}^{i-1} A_{i,k} T_{k,jb}; wave jb handles one block
+    if (w < i) {
+      const int jb = w;
+      f32x4 acc = zero4();
+      for (int kb = jb; kb < i; ++kb)
+        acc = mm_tile<float, 16>(acc, &Am[i * 16][kb * 16], LDCF, &Tt[jb * 16][kb * 16], LDCF);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Xs[w][acc_col()][acc_row(e)] = acc[e];
+    }
+    __syncthreads();
+    if (w < i) {
+      const int jb = w;
+      f32x4 acc = mm_tile<float, 16>(zero4(), &Tm[i * 16][i * 16], LDCF, &Xs[w][0][0], 20);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = i * 16 + acc_row(e), c = jb * 16 + acc_col();
+        Tm[r][c] = -acc[e];
+        Tt[c][r] = -acc[e];
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <typename E, int D, int C, int DVT, bool OUT>
+struct StateSmem {
+  static constexpr int LDQ = D + Pad<E>::E16;
+  static constexpr int LDCE = C + Pad<E>::E16;
+  E Wk[C][LDQ];
+  E Q[OUT ? C : 1][LDQ];
+  E Kt[D][LDCE];
+  E P[OUT ? C : 1][LDCE];
+  E Ht[DVT][LDQ];
+  E Wt[DVT][LDCE];
+  float gam[C];
+};
+
+}  // namespace gdn

@@ -1,0 +1,375 @@
+// Chunked gated delta rule: chunk index, per-chunk WY preparation, and the
+// serial inter-chunk state pass (forward).
+//
+// Pages: "[Qwen3.5 MoE] Add hybrid decoder model", Summary (GatedDeltaNet
+// linear attention; FLA kernels optional); "Support Qwen35 SFT", XTuner changes
+// (GatedDeltaNet varlen mode); "feat(models): dense Qwen3.5 custom attention",
+// Summary (cu_seqlens from position_ids; one packed row).
+//
+// Per chunk (rows r, s; gamma = within-chunk cumulative gate, Gam = e^gamma,
+// D_rs = e^{gamma_r - gamma_s} for r >= s, H = S^T entering the chunk):
+//   A  = strict_lower(diag(beta) (D * K K^T)),   T = (I + A)^-1
+//   U  = T diag(beta) V,   Wk = T diag(beta Gam) K,   W = U - Wk H
+//   O  = scale (diag(Gam) Q H + lower_incl(D * Q K^T) W)
+//   H' = Gam_last H + K^T diag(e^{gamma_last - gamma}) W
+// which is the token recurrence re-associated exactly.  Only non-positive
+// differences gamma_r - gamma_s (r >= s) are ever exponentiated; the mask is
+// applied before the exponential.
+#include "chunk_common.cuh"
+
+namespace gdn {
+
+// ---------------------------------------------------------------------------
+// Chunk index: one workgroup scans the per-sequence chunk counts, then fills
+// the table for every slot below the max_chunks bound.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void chunk_index_kernel(const int32_t* __restrict__ cu, int N, int C,
+                                                           int max_chunks, int32_t* __restrict__ table,
+                                                           int32_t* __restrict__ seq_chunk0) {
+  __shared__ int scan[1024];
+  __shared__ int base_s;
+  const int tid = threadIdx.x;
+  if (tid == 0) base_s = 0;
+  __syncthreads();
+  for (int n0 = 0; n0 < N; n0 += 1024) {
+    const int n = n0 + tid;
+    const int cnt = n < N ? (cu[n + 1] - cu[n] + C - 1) / C : 0;
+    scan[tid] = cnt;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int add = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += add;
+      __syncthreads();
+    }
+    const int base = base_s;
+    if (n < N) seq_chunk0[n] = base + scan[tid] - cnt;
+    __syncthreads();
+    if (tid == 0) base_s = base + scan[1023];
+    __syncthreads();
+  }
+  const int n_chunks = base_s;
+  if (tid == 0) seq_chunk0[N] = n_chunks;
+  __syncthreads();
+  for (int c = tid; c < max_chunks; c += 1024) {
+    int4 ent = make_int4(-1, 0, 0, 0);
+    if (c < n_chunks) {
+      int lo = 0, hi = N - 1;  // last n with seq_chunk0[n] <= c
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (seq_chunk0[mid] <= c) lo = mid; else hi = mid - 1;
+      }
+      const int tok0 = cu[lo] + (c - seq_chunk0[lo]) * C;
+      ent = make_int4(lo, tok0, min(C, cu[lo + 1] - tok0), 0);
+    }
+    reinterpret_cast<int4*>(table)[c] = ent;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// WY preparation, one workgroup per (chunk, k-head), looping over the k-head's
+// v-heads.  K K^T and Q K^T on MFMA (operand type E), the unit-lower
+// triangular inverse in fp32 (16x16 diagonal blocks by per-lane forward
+// substitution, off-diagonal blocks by block substitution on fp32 MFMA),
+// U and Wk on MFMA.
+// ---------------------------------------------------------------------------
+template <typename E, int D, int C>
+__global__ __launch_bounds__(kChunkThreads) void prep_kernel(ChunkArgs a) {
+  using S = PrepSmem<E, D, C>;
+  __shared__ S sm;
+  constexpr int V = Vec<E>::N;
+  constexpr int NT = C / 16, ND = D / 16;
+  const int ci = blockIdx.x, j = blockIdx.y;
+  const int4 ent = chunk_entry(a.table, ci);
+  if (ent.x < 0) return;
+  const int tok0 = ent.y, len = ent.z;
+  const int tid = threadIdx.x, w = wave_id(), lane = lane_id();
+  const E* qg = (const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D;
+  const E* kg = (const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D;
+
+  rows2s<E, C, D>(&sm.Qs[0][0], S::LDQ, qg, a.sqk, len);
+  rows2s<E, C, D>(&sm.Ks[0][0], S::LDQ, kg, a.sqk, len);
+  rows2s_t<E, C, D>(&sm.Kt[0][0], S::LDCE, kg, a.sqk, len, nullptr, 1.f);
+  __syncthreads();
+  for (int t = w; t < NT * NT; t += kChunkWaves) {
+    const int rt = t / NT, ct = t % NT;
+    const f32x4 acc = mm_tile<E, D>(zero4(), &sm.Ks[rt * 16][0], S::LDQ, &sm.Ks[ct * 16][0], S::LDQ);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.Sk[rt * 16 + acc_row(e)][ct * 16 + acc_col()] = acc[e];
+  }
+  __syncthreads();
+
+  for (int gi = 0; gi < a.G; ++gi) {
+    const int h = j * a.G + gi;
+    const int64_t slot = (int64_t)ci * a.Hv + h;
+    if (w == 0) {  // within-chunk cumulative gate
+      float gv = 0.f, bv = 0.f;
+      if (lane < len) {
+        gv = a.g[(int64_t)(tok0 + lane) * a.Hv + h];
+        bv = a.beta[(int64_t)(tok0 + lane) * a.Hv + h];
+      }
+      float x = gv;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const float y = __shfl_up(x, off, kWave);
+        if (lane >= off) x += y;
+      }
+      if (lane < C) {
+        sm.gam[lane] = x;
+        sm.beta[lane] = bv;
+        a.gam[slot * C + lane] = x;
+      }
+    }
+    const E* vg = (const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)h * D;
+    rows2s_t<E, C, D>(&sm.Vt[0][0], S::LDCE, vg, a.sv, len, nullptr, 1.f);
+    __syncthreads();
+
+    // P = lower_incl(D * Q K^T) (staged in TB), A = strict_lower(beta_r D * K K^T)
+    for (int t = w; t < NT * NT; t += kChunkWaves) {
+      const int rt = t / NT, ct = t % NT;
+      const f32x4 acc = mm_tile<E, D>(zero4(), &sm.Qs[rt * 16][0], S::LDQ, &sm.Ks[ct * 16][0], S::LDQ);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = rt * 16 + acc_row(e), s = ct * 16 + acc_col();
+        const float dd = (s <= r) ? __expf(sm.gam[r] - sm.gam[s]) : 0.f;
+        sm.TB[r][s] = from_f<E>((r < len) ? dd * acc[e] : 0.f);
+        sm.Am[r][s] = (s < r) ? sm.beta[r] * dd * sm.Sk[r][s] : 0.f;
+      }
+    }
+    __syncthreads();
+    {
+      E* Pg = (E*)a.P + slot * C * C;
+      for (int e = tid; e < C * (C / V); e += kChunkThreads) {
+        const int r = e / (C / V), c = (e % (C / V)) * V;
+        *reinterpret_cast<uint4*>(Pg + r * C + c) = *reinterpret_cast<const uint4*>(&sm.TB[r][c]);
+      }
+    }
+    unit_lower_inverse<C, S::LDCF>(sm.Am, sm.Tm, sm.Tt, sm.Xs);  // starts and ends with a barrier
+
+    // U = (T diag(beta)) V
+    for (int e = tid; e < C * C; e += kChunkThreads) {
+      const int r = e / C, s = e % C;
+      sm.TB[r][s] = from_f<E>(sm.Tm[r][s] * sm.beta[s]);
+    }
+    __syncthreads();
+    {
+      E* Ug = (E*)a.U + slot * C * D;
+      for (int t = w; t < NT * ND; t += kChunkWaves) {
+        const int rt = t / ND, ct = t % ND;
+        const f32x4 acc = mm_tile<E, C>(zero4(), &sm.TB[rt * 16][0], S::LDCE, &sm.Vt[ct * 16][0], S::LDCE);
+        store_tile<E>(Ug, D, rt * 16, ct * 16, acc, C);
+      }
+    }
+    __syncthreads();
+    // Wk = (T diag(beta Gam)) K
+    for (int e = tid; e < C * C; e += kChunkThreads) {
+      const int r = e / C, s = e % C;
+      sm.TB[r][s] = from_f<E>(sm.Tm[r][s] * sm.beta[s] * __expf(sm.gam[s]));
+    }
+    __syncthreads();
+    {
+      E* Wg = (E*)a.Wk + slot * C * D;
+      for (int t = w; t < NT * ND; t += kChunkWaves) {
+        const int rt = t / ND, ct = t % ND;
+        const f32x4 acc = mm_tile<E, C>(zero4(), &sm.TB[rt * 16][0], S::LDCE, &sm.Kt[ct * 16][0], S::LDCE);
+        store_tile<E>(Wg, D, rt * 16, ct * 16, acc, C);
+      }
+    }
+    // Kt_e[d][s] = e^{gamma_last - gamma_s} k_s[d]  (s < len), 0 past len
+    {
+      E* Kg = (E*)a.Kt + slot * D * C;
+      const float glast = sm.gam[len - 1];
+      for (int e = tid; e < D * (C / V); e += kChunkThreads) {
+        const int d = e / (C / V), s0 = (e % (C / V)) * V;
+        float val[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          const int s = s0 + i;
+          val[i] = (s < len) ? to_f<E>(sm.Kt[d][s]) * __expf(glast - sm.gam[s]) : 0.f;
+        }
+        Vec<E>::store(Kg + d * C + s0, val);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Inter-chunk state pass, one workgroup per (sequence, v-head, dv tile of DVT
+// columns).  The state tile H [D][DVT] stays in registers (fp32) for the whole
+// sequence; each chunk stages Wk, Kt_e (and Q, P for the output) in LDS, and
+// H^T / W^T as bf16 MFMA operands.  Dv tiles are independent: the update acts
+// on the state by left multiplication only.
+//   OUT   = true : writes o and the final state ht
+//   OUT   = false: writes, per chunk, the entering state Hc and W (for the
+//                  backward pass), and the final state if asked
+// ---------------------------------------------------------------------------
+template <typename E, int D, int C, int DVT, bool OUT>
+__global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
+  using S = StateSmem<E, D, C, DVT, OUT>;
+  __shared__ S sm;
+  constexpr int NVT = D / DVT;
+  constexpr int NCT = DVT / 16;                 // column tiles
+  constexpr int NHT = (D / 16) * NCT;           // state tiles
+  constexpr int NHW = (NHT + kChunkWaves - 1) / kChunkWaves;
+  constexpr int NWT = (C / 16) * NCT;           // W / O tiles
+  constexpr int NWW = (NWT + kChunkWaves - 1) / kChunkWaves;
+  const int bid = blockIdx.x;
+  const int vt = bid % NVT, h = (bid / NVT) % a.Hv, n = bid / (NVT * a.Hv);
+  const int j = h / a.G;
+  const int w = wave_id();
+  const int col0 = vt * DVT;
+
+  f32x4 Hr[NHW];
+#pragma unroll
+  for (int i = 0; i < NHW; ++i) {
+    const int t = w + kChunkWaves * i;
+    Hr[i] = zero4();
+    if (t < NHT && a.h0) {
+      const int rt = t / NCT, ct = t % NCT;
+      const float* src = a.h0 + ((int64_t)n * a.Hv + h) * D * D;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Hr[i][e] = src[(rt * 16 + acc_row(e)) * D + col0 + ct * 16 + acc_col()];
+    }
+  }
+  auto write_Ht = [&]() {
+#pragma unroll
+    for (int i = 0; i < NHW; ++i) {
+      const int t = w + kChunkWaves * i;
+      if (t < NHT) {
+        const int rt = t / NCT, ct = t % NCT;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm.Ht[ct * 16 + acc_col()][rt * 16 + acc_row(e)] = from_f<E>(Hr[i][e]);
+      }
+    }
+  };
+  write_Ht();
+
+  const int c0 = a.seq_chunk0[n], c1 = a.seq_chunk0[n + 1];
+  for (int ci = c0; ci < c1; ++ci) {
+    const int4 ent = chunk_entry(a.table, ci);
+    const int tok0 = ent.y, len = ent.z;
+    const int64_t slot = (int64_t)ci * a.Hv + h;
+    g2s<E, C, D>(&sm.Wk[0][0], S::LDQ, (const E*)a.Wk + slot * C * D);
+    g2s<E, D, C>(&sm.Kt[0][0], S::LDCE, (const E*)a.Kt + slot * D * C);
+    if (OUT) {
+      rows2s<E, C, D>(&sm.Q[0][0], S::LDQ, (const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D, a.sqk, len);
+      g2s<E, C, C>(&sm.P[0][0], S::LDCE, (const E*)a.P + slot * C * C);
+    } else {
+      // state entering this chunk, for the backward pass
+      E* Hg = (E*)a.Hc + slot * D * D;
+#pragma unroll
+      for (int i = 0; i < NHW; ++i) {
+        const int t = w + kChunkWaves * i;
+        if (t < NHT) store_tile<E>(Hg, D, (t / NCT) * 16, col0 + (t % NCT) * 16, Hr[i], D);
+      }
+    }
+    for (int e = threadIdx.x; e < C; e += kChunkThreads) sm.gam[e] = a.gam[slot * C + e];
+    __syncthreads();
+
+    const E* Ug = (const E*)a.U + slot * C * D;
+    f32x4 Or[NWW];
+#pragma unroll
+    for (int i = 0; i < NWW; ++i) {
+      const int t = w + kChunkWaves * i;
+      Or[i] = zero4();
+      if (t < NWT) {
+        const int rt = t / NCT, ct = t % NCT;
+        const f32x4 x = mm_tile<E, D>(zero4(), &sm.Wk[rt * 16][0], S::LDQ, &sm.Ht[ct * 16][0], S::LDQ);
+        f32x4 wv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = rt * 16 + acc_row(e), c = ct * 16 + acc_col();
+          wv[e] = to_f<E>(Ug[r * D + col0 + c]) - x[e];
+          sm.Wt[c][r] = from_f<E>(wv[e]);
+        }
+        if (!OUT) store_tile<E>((E*)a.W + slot * C * D, D, rt * 16, col0 + ct * 16, wv, C);
+        if (OUT) {
+          const f32x4 xo = mm_tile<E, D>(zero4(), &sm.Q[rt * 16][0], S::LDQ, &sm.Ht[ct * 16][0], S::LDQ);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Or[i][e] = __expf(sm.gam[rt * 16 + acc_row(e)]) * xo[e];
+        }
+      }
+    }
+    __syncthreads();
+
+    const float gl = __expf(sm.gam[len - 1]);
+#pragma unroll
+    for (int i = 0; i < NHW; ++i) {
+      const int t = w + kChunkWaves * i;
+      if (t < NHT) {
+        const int rt = t / NCT, ct = t % NCT;
+        const f32x4 y = mm_tile<E, C>(zero4(), &sm.Kt[rt * 16][0], S::LDCE, &sm.Wt[ct * 16][0], S::LDCE);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Hr[i][e] = gl * Hr[i][e] + y[e];
+      }
+    }
+    if (OUT) {
+      E* og = (E*)a.o + (int64_t)tok0 * a.Hv * D + (int64_t)h * D + col0;
+#pragma unroll
+      for (int i = 0; i < NWW; ++i) {
+        const int t = w + kChunkWaves * i;
+        if (t < NWT) {
+          const int rt = t / NCT, ct = t % NCT;
+          const f32x4 y = mm_tile<E, C>(zero4(), &sm.P[rt * 16][0], S::LDCE, &sm.Wt[ct * 16][0], S::LDCE);
+          f32x4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = a.scale * (Or[i][e] + y[e]);
+          store_tile<E>(og, (int64_t)a.Hv * D, rt * 16, ct * 16, ov, len);
+        }
+      }
+    }
+    __syncthreads();
+    write_Ht();
+  }
+  if (a.ht) {
+    float* dst = a.ht + ((int64_t)n * a.Hv + h) * D * D;
+#pragma unroll
+    for (int i = 0; i < NHW; ++i) {
+      const int t = w + kChunkWaves * i;
+      if (t < NHT) {
+        const int rt = t / NCT, ct = t % NCT;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(rt * 16 + acc_row(e)) * D + col0 + ct * 16 + acc_col()] = Hr[i][e];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+int64_t max_chunks(const gdn_shape* s) {
+  return ((int64_t)s->total_tokens + s->chunk - 1) / s->chunk + s->n_seqs;
+}
+
+void run_chunk_index(const gdn_shape* s, const int32_t* cu, int32_t* table, int32_t* seq_chunk0, hipStream_t st) {
+  chunk_index_kernel<<<1, 1024, 0, st>>>(cu, s->n_seqs, s->chunk, (int)max_chunks(s), table, seq_chunk0);
+}
+
+template <typename E, int D>
+constexpr int state_dvt() { return D >= 32 ? 32 : D; }
+
+template <typename E, int D, int C>
+void launch_chunk_fwd_core(const ChunkArgs& a, hipStream_t st, bool out_mode) {
+  constexpr int DVT = state_dvt<E, D>();
+  dim3 gprep(a.max_chunks, a.Hk);
+  prep_kernel<E, D, C><<<gprep, kChunkThreads, 0, st>>>(a);
+  dim3 gstate(a.N * a.Hv * (D / DVT));
+  if (out_mode) state_fwd_kernel<E, D, C, DVT, true><<<gstate, kChunkThreads, 0, st>>>(a);
+  else state_fwd_kernel<E, D, C, DVT, false><<<gstate, kChunkThreads, 0, st>>>(a);
+}
+
+// explicit instantiation helpers used by the dispatcher in chunk_bwd.hip
+#define GDN_INST_FWD(E, D, C) template void launch_chunk_fwd_core<E, D, C>(const ChunkArgs&, hipStream_t, bool);
+GDN_INST_FWD(bf16, 16, 16) GDN_INST_FWD(bf16, 16, 32) GDN_INST_FWD(bf16, 16, 64)
+GDN_INST_FWD(bf16, 32, 16) GDN_INST_FWD(bf16, 32, 32) GDN_INST_FWD(bf16, 32, 64)
+GDN_INST_FWD(bf16, 64, 16) GDN_INST_FWD(bf16, 64, 32) GDN_INST_FWD(bf16, 64, 64)
+GDN_INST_FWD(bf16, 128, 16) GDN_INST_FWD(bf16, 128, 32) GDN_INST_FWD(bf16, 128, 64)
+GDN_INST_FWD(float, 16, 16) GDN_INST_FWD(float, 16, 32) GDN_INST_FWD(float, 16, 64)
+GDN_INST_FWD(float, 32, 16) GDN_INST_FWD(float, 32, 32) GDN_INST_FWD(float, 32, 64)
+GDN_INST_FWD(float, 64, 16) GDN_INST_FWD(float, 64, 32) GDN_INST_FWD(float, 64, 64)
+GDN_INST_FWD(float, 128, 16) GDN_INST_FWD(float, 128, 32)
+#undef GDN_INST_FWD
+
+}  // namespace gdn

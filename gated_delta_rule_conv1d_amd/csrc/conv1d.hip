@@ -1,0 +1,382 @@
+// Causal depthwise conv1d + SiLU + per-head L2 normalisation, forward and
+// backward, over one packed varlen row.
+//
+// Pages: "[Qwen3.5 MoE] Add hybrid decoder model", Summary (depthwise conv1d
+// inside GatedDeltaNet); "Support Qwen35 SFT", Notes and XTuner changes
+// (causal_conv1d dependency, varlen mode).
+//
+// Layout: x, y [T][Cch] channel-last.  A lane owns 16 bytes of consecutive
+// channels (8 bf16 or 4 float), so a wave reads/writes 1 KiB (bf16) of one
+// token per instruction, fully coalesced.  Each wave walks TB consecutive
+// tokens of its channel block, keeping the width-1 previous inputs in
+// registers; the sequence containing the wave's first token is found by
+// binary search in cu_seqlens and the history is cleared at every sequence
+// start.  L2 groups (one q/k head = d channels) are aligned lane groups and
+// reduce with xor shuffles.
+#include "gdn_common.cuh"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+constexpr int kConvTB = 64;       // tokens per wave
+constexpr int kConvWaves = 4;     // waves (token blocks) per workgroup
+
+__device__ __forceinline__ int find_seq(const int32_t* cu, int N, int t) {
+  // largest n with cu[n] <= t (so cu[n] <= t < cu[n+1] when t < T)
+  int lo = 0, hi = N;  // answer in [0, N-1]
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo < N ? lo : N - 1;
+}
+
+template <typename E, int D, int W>
+__global__ __launch_bounds__(256) void conv_fwd_kernel(const E* __restrict__ x, const E* __restrict__ w,
+                                                       const int32_t* __restrict__ cu, int N, int T,
+                                                       int Cch, int n_qk, float eps, E* __restrict__ y) {
+  constexpr int V = Vec<E>::N;      // channels per lane
+  constexpr int LPH = D / V;        // lanes per L2 group
+  const int lane = lane_id();
+  const int tb = blockIdx.x * kConvWaves + wave_id();
+  const int t0 = tb * kConvTB;
+  if (t0 >= T) return;
+  const int t1 = min(t0 + kConvTB, T);
+  const int ch = (blockIdx.y * kWave + lane) * V;
+  const bool active = ch < Cch;
+  const bool is_qk = ch < n_qk;
+
+  float wr[V][W];
+  float hist[W - 1][V];
+#pragma unroll
+  for (int c = 0; c < V; ++c)
+#pragma unroll
+    for (int i = 0; i < W; ++i) wr[c][i] = active ? to_f<E>(w[(size_t)(ch + c) * W + i]) : 0.f;
+
+  int n = find_seq(cu, N, t0);
+  int seq_start = cu[n], seq_end = cu[n + 1];
+#pragma unroll
+  for (int i = 0; i < W - 1; ++i) {
+    const int s = t0 - (W - 1) + i;
+    if (active && s >= seq_start) Vec<E>::load(x + (size_t)s * Cch + ch, hist[i]);
+    else
+#pragma unroll
+      for (int c = 0; c < V; ++c) hist[i][c] = 0.f;
+  }
+
+  for (int t = t0; t < t1; ++t) {
+    if (t >= seq_end) {  // entering a new sequence (skip empty ones)
+      while (cu[n + 1] <= t) ++n;
+      seq_start = cu[n];
+      seq_end = cu[n + 1];
+#pragma unroll
+      for (int i = 0; i < W - 1; ++i)
+#pragma unroll
+        for (int c = 0; c < V; ++c) hist[i][c] = 0.f;
+    }
+    float cur[V];
+    if (active) Vec<E>::load(x + (size_t)t * Cch + ch, cur);
+    else
+#pragma unroll
+      for (int c = 0; c < V; ++c) cur[c] = 0.f;
+    float a[V];
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < V; ++c) {
+      float acc = wr[c][W - 1] * cur[c];
+#pragma unroll
+      for (int i = 0; i < W - 1; ++i) acc += wr[c][i] * hist[i][c];
+      a[c] = acc * sigmoidf_(acc);
+      ss += a[c] * a[c];
+    }
+    ss = group_sum<LPH>(ss);
+    if (is_qk) {
+      const float inv = rsqrtf(ss + eps);
+#pragma unroll
+      for (int c = 0; c < V; ++c) a[c] *= inv;
+    }
+    if (active) Vec<E>::store(y + (size_t)t * Cch + ch, a);
+#pragma unroll
+    for (int i = 0; i < W - 2; ++i)
+#pragma unroll
+      for (int c = 0; c < V; ++c) hist[i][c] = hist[i + 1][c];
+#pragma unroll
+    for (int c = 0; c < V; ++c) hist[W - 2][c] = cur[c];
+  }
+}
+
+// Backward.  For token t: recompute c, a = SiLU(c), the L2 norm; then
+// da = dy/n - a (a.dy)/n^3 (q/k) or dy (v); dc = da * s (1 + c (1 - s)).
+// dx[s] = sum_i w_i dc[s + W-1 - i] over terms in s's sequence; each wave
+// computes dc for its TB tokens plus W-1 look-ahead tokens.  dw partial sums
+// per (workgroup, channel, tap) go to workspace in a fixed order.
+template <typename E, int D, int W>
+__global__ __launch_bounds__(256) void conv_bwd_kernel(const E* __restrict__ dy, const E* __restrict__ x,
+                                                       const E* __restrict__ w, const int32_t* __restrict__ cu,
+                                                       int N, int T, int Cch, int n_qk, float eps,
+                                                       E* __restrict__ dx, float* __restrict__ dw_part) {
+  constexpr int V = Vec<E>::N;
+  constexpr int LPH = D / V;
+  __shared__ float red[kConvWaves][kWave * V * W];
+  const int lane = lane_id();
+  const int wv = wave_id();
+  const int tb = blockIdx.x * kConvWaves + wv;
+  const int t0 = tb * kConvTB;
+  const int ch = (blockIdx.y * kWave + lane) * V;
+  const bool active = ch < Cch;
+  const bool is_qk = ch < n_qk;
+
+  float dwacc[V][W];
+#pragma unroll
+  for (int c = 0; c < V; ++c)
+#pragma unroll
+    for (int i = 0; i < W; ++i) dwacc[c][i] = 0.f;
+
+  if (t0 < T) {
+    const int t1 = min(t0 + kConvTB, T);
+    const int tend = min(t1 + W - 1, T);
+    float wr[V][W];
+#pragma unroll
+    for (int c = 0; c < V; ++c)
+#pragma unroll
+      for (int i = 0; i < W; ++i) wr[c][i] = active ? to_f<E>(w[(size_t)(ch + c) * W + i]) : 0.f;
+
+    int n = find_seq(cu, N, t0);
+    int seq_start = cu[n], seq_end = cu[n + 1];
+    float hist[W - 1][V];
+#pragma unroll
+    for (int i = 0; i < W - 1; ++i) {
+      const int s = t0 - (W - 1) + i;
+      if (active && s >= seq_start) Vec<E>::load(x + (size_t)s * Cch + ch, hist[i]);
+      else
+#pragma unroll
+        for (int c = 0; c < V; ++c) hist[i][c] = 0.f;
+    }
+    // window of the last W dc values and their sequence starts: slot W-1 newest
+    float dcw[W][V];
+    int dcs[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      dcs[i] = 0x7fffffff;
+#pragma unroll
+      for (int c = 0; c < V; ++c) dcw[i][c] = 0.f;
+    }
+    for (int t = t0; t < tend; ++t) {
+      if (t >= seq_end) {
+        while (cu[n + 1] <= t) ++n;
+        seq_start = cu[n];
+        seq_end = cu[n + 1];
+#pragma unroll
+        for (int i = 0; i < W - 1; ++i)
+#pragma unroll
+          for (int c = 0; c < V; ++c) hist[i][c] = 0.f;
+      }
+      float cur[V], g[V];
+      if (active) {
+        Vec<E>::load(x + (size_t)t * Cch + ch, cur);
+        Vec<E>::load(dy + (size_t)t * Cch + ch, g);
+      } else {
+#pragma unroll
+        for (int c = 0; c < V; ++c) cur[c] = g[c] = 0.f;
+      }
+      float cc[V], sg[V], a[V];
+      float ss = 0.f, dot = 0.f;
+#pragma unroll
+      for (int c = 0; c < V; ++c) {
+        float acc = wr[c][W - 1] * cur[c];
+#pragma unroll
+        for (int i = 0; i < W - 1; ++i) acc += wr[c][i] * hist[i][c];
+        cc[c] = acc;
+        sg[c] = sigmoidf_(acc);
+        a[c] = acc * sg[c];
+        ss += a[c] * a[c];
+        dot += a[c] * g[c];
+      }
+      ss = group_sum<LPH>(ss);
+      dot = group_sum<LPH>(dot);
+      float dcv[V];
+      const float inv = rsqrtf(ss + eps);
+      const float inv3 = inv * inv * inv;
+#pragma unroll
+      for (int c = 0; c < V; ++c) {
+        const float da = is_qk ? (g[c] * inv - a[c] * dot * inv3) : g[c];
+        dcv[c] = da * sg[c] * (1.f + cc[c] * (1.f - sg[c]));
+      }
+      if (t < t1) {  // own token: weight gradient
+#pragma unroll
+        for (int c = 0; c < V; ++c) {
+#pragma unroll
+          for (int i = 0; i < W - 1; ++i) dwacc[c][i] += dcv[c] * hist[i][c];
+          dwacc[c][W - 1] += dcv[c] * cur[c];
+        }
+      }
+      // shift windows
+#pragma unroll
+      for (int i = 0; i < W - 2; ++i)
+#pragma unroll
+        for (int c = 0; c < V; ++c) hist[i][c] = hist[i + 1][c];
+#pragma unroll
+      for (int c = 0; c < V; ++c) hist[W - 2][c] = cur[c];
+#pragma unroll
+      for (int i = 0; i < W - 1; ++i) {
+        dcs[i] = dcs[i + 1];
+#pragma unroll
+        for (int c = 0; c < V; ++c) dcw[i][c] = dcw[i + 1][c];
+      }
+      dcs[W - 1] = seq_start;
+#pragma unroll
+      for (int c = 0; c < V; ++c) dcw[W - 1][c] = dcv[c];
+      // dx for token s = t - (W-1): slot m holds dc[s + m], which the tap
+      // W-1-m multiplies; only terms inside s's sequence count.
+      const int s = t - (W - 1);
+      if (s >= t0 && active) {
+        float o[V];
+#pragma unroll
+        for (int c = 0; c < V; ++c) o[c] = 0.f;
+#pragma unroll
+        for (int m = 0; m < W; ++m) {
+          if (dcs[m] <= s) {
+#pragma unroll
+            for (int c = 0; c < V; ++c) o[c] += wr[c][W - 1 - m] * dcw[m][c];
+          }
+        }
+        Vec<E>::store(dx + (size_t)s * Cch + ch, o);
+      }
+    }
+    // tokens whose W-1 successors run past the end of the row: after the last
+    // iteration slot k holds dc[tend - W + k]
+    if (active) {
+      for (int s = max(t0, tend - (W - 1)); s < t1; ++s) {
+        float o[V];
+#pragma unroll
+        for (int c = 0; c < V; ++c) o[c] = 0.f;
+#pragma unroll
+        for (int m = 0; m < W; ++m) {
+          const int slot = s + m - (tend - W);
+          if (s + m < tend && dcs[slot] <= s) {
+#pragma unroll
+            for (int c = 0; c < V; ++c) o[c] += wr[c][W - 1 - m] * dcw[slot][c];
+          }
+        }
+        Vec<E>::store(dx + (size_t)s * Cch + ch, o);
+      }
+    }
+  }
+  // reduce dw over the workgroup's waves in a fixed order
+#pragma unroll
+  for (int c = 0; c < V; ++c)
+#pragma unroll
+    for (int i = 0; i < W; ++i) red[wv][(lane * V + c) * W + i] = dwacc[c][i];
+  __syncthreads();
+  for (int e = threadIdx.x; e < kWave * V * W; e += blockDim.x) {
+    const int chl = e / W;  // channel within the block
+    const int gch = blockIdx.y * kWave * V + chl;
+    if (gch < Cch) {
+      float s = 0.f;
+#pragma unroll
+      for (int k = 0; k < kConvWaves; ++k) s += red[k][e];
+      dw_part[((size_t)blockIdx.x * Cch + gch) * W + (e % W)] = s;
+    }
+  }
+}
+
+__global__ void sum_parts_kernel(const float* __restrict__ part, int nparts, int n, float* __restrict__ out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int p = 0; p < nparts; ++p) s += part[(size_t)p * n + i];
+  out[i] = s;
+}
+
+// --------------------------------------------------------------------------
+// host side
+// --------------------------------------------------------------------------
+static int conv_grid_x(int T) {
+  const int ntb = (T + kConvTB - 1) / kConvTB;
+  return (ntb + kConvWaves - 1) / kConvWaves;
+}
+
+size_t conv_bwd_ws_bytes(const gdn_shape* s, int width) {
+  const int Cch = 2 * s->h_qk * s->d_k + s->h_v * s->d_v;
+  const int gx = conv_grid_x(s->total_tokens) > 0 ? conv_grid_x(s->total_tokens) : 1;
+  return (size_t)gx * Cch * width * sizeof(float);
+}
+
+template <typename E, int D, int W>
+static void launch_conv_fwd(const gdn_shape* s, const void* x, const void* w, const int32_t* cu, float eps,
+                            void* y, hipStream_t st) {
+  constexpr int V = Vec<E>::N;
+  const int Cch = 2 * s->h_qk * s->d_k + s->h_v * s->d_v;
+  dim3 grid(conv_grid_x(s->total_tokens), (Cch + kWave * V - 1) / (kWave * V));
+  conv_fwd_kernel<E, D, W><<<grid, 256, 0, st>>>((const E*)x, (const E*)w, cu, s->n_seqs, s->total_tokens, Cch,
+                                                 2 * s->h_qk * s->d_k, eps, (E*)y);
+}
+
+template <typename E, int D, int W>
+static void launch_conv_bwd(const gdn_shape* s, const void* dy, const void* x, const void* w, const int32_t* cu,
+                            float eps, void* dx, float* dw, void* ws, hipStream_t st) {
+  constexpr int V = Vec<E>::N;
+  const int Cch = 2 * s->h_qk * s->d_k + s->h_v * s->d_v;
+  dim3 grid(conv_grid_x(s->total_tokens), (Cch + kWave * V - 1) / (kWave * V));
+  float* part = (float*)ws;
+  conv_bwd_kernel<E, D, W><<<grid, 256, 0, st>>>((const E*)dy, (const E*)x, (const E*)w, cu, s->n_seqs,
+                                                 s->total_tokens, Cch, 2 * s->h_qk * s->d_k, eps, (E*)dx, part);
+  const int n = Cch * W;
+  sum_parts_kernel<<<(n + 255) / 256, 256, 0, st>>>(part, (int)grid.x, n, dw);
+}
+
+template <typename E, int D>
+static bool conv_fwd_w(const gdn_shape* s, const void* x, const void* w, int width, const int32_t* cu, float eps,
+                       void* y, hipStream_t st) {
+  switch (width) {
+    case 2: launch_conv_fwd<E, D, 2>(s, x, w, cu, eps, y, st); return true;
+    case 3: launch_conv_fwd<E, D, 3>(s, x, w, cu, eps, y, st); return true;
+    case 4: launch_conv_fwd<E, D, 4>(s, x, w, cu, eps, y, st); return true;
+  }
+  return false;
+}
+
+template <typename E, int D>
+static bool conv_bwd_w(const gdn_shape* s, const void* dy, const void* x, const void* w, int width,
+                       const int32_t* cu, float eps, void* dx, float* dw, void* ws, hipStream_t st) {
+  switch (width) {
+    case 2: launch_conv_bwd<E, D, 2>(s, dy, x, w, cu, eps, dx, dw, ws, st); return true;
+    case 3: launch_conv_bwd<E, D, 3>(s, dy, x, w, cu, eps, dx, dw, ws, st); return true;
+    case 4: launch_conv_bwd<E, D, 4>(s, dy, x, w, cu, eps, dx, dw, ws, st); return true;
+  }
+  return false;
+}
+
+bool run_conv_fwd(const gdn_shape* s, const void* x, const void* w, int width, const int32_t* cu, float eps,
+                  void* y, hipStream_t st) {
+  if (s->total_tokens == 0) return true;
+#define GDN_CONV_D(E, D) \
+  if (s->d_k == D) return conv_fwd_w<E, D>(s, x, w, width, cu, eps, y, st);
+  if (s->dtype == GDN_BF16) {
+    GDN_CONV_D(bf16, 16) GDN_CONV_D(bf16, 32) GDN_CONV_D(bf16, 64) GDN_CONV_D(bf16, 128)
+  } else {
+    GDN_CONV_D(float, 16) GDN_CONV_D(float, 32) GDN_CONV_D(float, 64) GDN_CONV_D(float, 128)
+  }
+#undef GDN_CONV_D
+  return false;
+}
+
+bool run_conv_bwd(const gdn_shape* s, const void* dy, const void* x, const void* w, int width, const int32_t* cu,
+                  float eps, void* dx, float* dw, void* ws, hipStream_t st) {
+  if (s->total_tokens == 0) {
+    const int n = (2 * s->h_qk * s->d_k + s->h_v * s->d_v) * width;
+    sum_parts_kernel<<<(n + 255) / 256, 256, 0, st>>>((const float*)ws, 0, n, dw);
+    return true;
+  }
+#define GDN_CONV_D(E, D) \
+  if (s->d_k == D) return conv_bwd_w<E, D>(s, dy, x, w, width, cu, eps, dx, dw, ws, st);
+  if (s->dtype == GDN_BF16) {
+    GDN_CONV_D(bf16, 16) GDN_CONV_D(bf16, 32) GDN_CONV_D(bf16, 64) GDN_CONV_D(bf16, 128)
+  } else {
+    GDN_CONV_D(float, 16) GDN_CONV_D(float, 32) GDN_CONV_D(float, 64) GDN_CONV_D(float, 128)
+  }
+#undef GDN_CONV_D
+  return false;
+}
+
+}  // namespace gdn

@@ -1,0 +1,186 @@
+// C ABI of the library: host-side argument checks, workspace sizing, and
+// launches on the caller's stream.  Every check runs before anything is
+// enqueued.
+#include <hip/hip_runtime.h>
+
+#include "gdn_internal.h"
+
+using namespace gdn;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// shape checks shared by every entry point
+gdn_status check_shape(const gdn_shape* s) {
+  if (!s) return GDN_ERR_INVALID_ARG;
+  if (s->n_seqs < 1 || s->total_tokens < 0 || s->h_qk < 1 || s->h_v < 1) return GDN_ERR_INVALID_ARG;
+  if (s->h_v % s->h_qk != 0) return GDN_ERR_INVALID_ARG;
+  if (s->dtype != GDN_F32 && s->dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+  if (!dim_ok(s->d_k) || s->d_v != s->d_k) return GDN_ERR_UNSUPPORTED;
+  if ((int64_t)s->total_tokens * (2 * s->h_qk * s->d_k + s->h_v * s->d_v) > ((int64_t)1 << 40))
+    return GDN_ERR_INVALID_ARG;
+  return GDN_OK;
+}
+
+gdn_status check_chunk(const gdn_shape* s) {
+  if (s->chunk != 16 && s->chunk != 32 && s->chunk != 64) return GDN_ERR_UNSUPPORTED;
+  if (!chunk_supported(s)) return GDN_ERR_UNSUPPORTED;
+  if (max_chunks(s) > (int64_t)1 << 30) return GDN_ERR_INVALID_ARG;
+  return GDN_OK;
+}
+
+size_t esize(const gdn_shape* s) { return s->dtype == GDN_BF16 ? 2 : 4; }
+
+bool stride_ok(const gdn_shape* s, int64_t stride, int64_t min_elems) {
+  return stride >= min_elems && (stride * (int64_t)esize(s)) % 16 == 0;
+}
+
+gdn_status launched() { return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(gdn_status status) {
+  switch (status) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_INVALID_ARG: return "GDN_ERR_INVALID_ARG: invalid argument";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: unsupported shape or dtype";
+    case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP: kernel launch failed";
+  }
+  return "unknown gdn_status";
+}
+
+int64_t gdn_max_chunks(const gdn_shape* shape) {
+  if (check_shape(shape) != GDN_OK || shape->chunk < 1) return -1;
+  return max_chunks(shape);
+}
+
+gdn_status gdn_chunk_index(const gdn_shape* shape, const int32_t* cu_seqlens, int32_t* table, int32_t* seq_chunk0,
+                           gdn_stream stream) {
+  gdn_status st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  if (shape->chunk != 16 && shape->chunk != 32 && shape->chunk != 64) return GDN_ERR_UNSUPPORTED;
+  if (!cu_seqlens || !table || !seq_chunk0 || !aligned16(table)) return GDN_ERR_INVALID_ARG;
+  run_chunk_index(shape, cu_seqlens, table, seq_chunk0, (hipStream_t)stream);
+  return launched();
+}
+
+gdn_status gdn_conv1d(const gdn_shape* shape, const void* x, const void* w_conv, int32_t width, float l2_eps,
+                      const int32_t* cu_seqlens, void* y, gdn_stream stream) {
+  gdn_status st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  if (width < 2 || width > 4) return GDN_ERR_UNSUPPORTED;
+  if (!x || !w_conv || !cu_seqlens || !y || x == y) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(y)) return GDN_ERR_INVALID_ARG;
+  if (!(l2_eps >= 0.f)) return GDN_ERR_INVALID_ARG;
+  if (!run_conv_fwd(shape, x, w_conv, width, cu_seqlens, l2_eps, y, (hipStream_t)stream)) return GDN_ERR_UNSUPPORTED;
+  return launched();
+}
+
+size_t gdn_conv1d_bwd_workspace(const gdn_shape* shape, int32_t width) {
+  if (check_shape(shape) != GDN_OK || width < 2 || width > 4) return 0;
+  return conv_bwd_ws_bytes(shape, width);
+}
+
+gdn_status gdn_conv1d_bwd(const gdn_shape* shape, const void* dy, const void* x, const void* w_conv, int32_t width,
+                          float l2_eps, const int32_t* cu_seqlens, void* dx, float* dw_conv, void* ws,
+                          size_t ws_bytes, gdn_stream stream) {
+  gdn_status st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  if (width < 2 || width > 4) return GDN_ERR_UNSUPPORTED;
+  if (!dy || !x || !w_conv || !cu_seqlens || !dx || !dw_conv) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(dy) || !aligned16(x) || !aligned16(dx) || dx == x || dx == dy) return GDN_ERR_INVALID_ARG;
+  if (!(l2_eps >= 0.f)) return GDN_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws) || ws_bytes < conv_bwd_ws_bytes(shape, width)) return GDN_ERR_WORKSPACE;
+  if (!run_conv_bwd(shape, dy, x, w_conv, width, cu_seqlens, l2_eps, dx, dw_conv, ws, (hipStream_t)stream))
+    return GDN_ERR_UNSUPPORTED;
+  return launched();
+}
+
+size_t gdn_chunk_fwd_workspace(const gdn_shape* shape) {
+  if (check_shape(shape) != GDN_OK || check_chunk(shape) != GDN_OK) return 0;
+  return chunk_fwd_ws_bytes(shape);
+}
+
+gdn_status gdn_chunk_fwd(const gdn_shape* shape, const void* q, const void* k, const void* v, int64_t tok_stride_qk,
+                         int64_t tok_stride_v, const float* g, const float* beta, const int32_t* cu_seqlens,
+                         const float* h0, void* o, float* ht, void* ws, size_t ws_bytes, gdn_stream stream) {
+  gdn_status st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  if ((st = check_chunk(shape)) != GDN_OK) return st;
+  if (!q || !k || !v || !g || !beta || !cu_seqlens || !o) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return GDN_ERR_INVALID_ARG;
+  if (!stride_ok(shape, tok_stride_qk, (int64_t)shape->h_qk * shape->d_k) ||
+      !stride_ok(shape, tok_stride_v, (int64_t)shape->h_v * shape->d_v))
+    return GDN_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws) || ws_bytes < chunk_fwd_ws_bytes(shape)) return GDN_ERR_WORKSPACE;
+  if (!run_chunk_fwd(shape, q, k, v, tok_stride_qk, tok_stride_v, g, beta, cu_seqlens, h0, o, ht, ws,
+                     (hipStream_t)stream))
+    return GDN_ERR_UNSUPPORTED;
+  return launched();
+}
+
+size_t gdn_chunk_bwd_workspace(const gdn_shape* shape) {
+  if (check_shape(shape) != GDN_OK || check_chunk(shape) != GDN_OK) return 0;
+  return chunk_bwd_ws_bytes(shape);
+}
+
+gdn_status gdn_chunk_bwd(const gdn_shape* shape, const void* q, const void* k, const void* v, int64_t tok_stride_qk,
+                         int64_t tok_stride_v, const float* g, const float* beta, const int32_t* cu_seqlens,
+                         const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, float* dg,
+                         float* dbeta, float* dh0, void* ws, size_t ws_bytes, gdn_stream stream) {
+  gdn_status st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  if ((st = check_chunk(shape)) != GDN_OK) return st;
+  if (!q || !k || !v || !g || !beta || !cu_seqlens || !d_o || !dq || !dk || !dv || !dg || !dbeta)
+    return GDN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_o) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv))
+    return GDN_ERR_INVALID_ARG;
+  if (!stride_ok(shape, tok_stride_qk, (int64_t)shape->h_qk * shape->d_k) ||
+      !stride_ok(shape, tok_stride_v, (int64_t)shape->h_v * shape->d_v))
+    return GDN_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws) || ws_bytes < chunk_bwd_ws_bytes(shape)) return GDN_ERR_WORKSPACE;
+  if (!run_chunk_bwd(shape, q, k, v, tok_stride_qk, tok_stride_v, g, beta, cu_seqlens, h0, d_o, dht, dq, dk, dv, dg,
+                     dbeta, dh0, ws, (hipStream_t)stream))
+    return GDN_ERR_UNSUPPORTED;
+  return launched();
+}
+
+gdn_status gdn_norm_gate(const gdn_shape* shape, const void* o, const void* z, const void* w_norm, float eps, void* y,
+                         gdn_stream stream) {
+  gdn_status st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  if (!o || !z || !w_norm || !y) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(o) || !aligned16(z) || !aligned16(w_norm) || !aligned16(y)) return GDN_ERR_INVALID_ARG;
+  if (!(eps >= 0.f)) return GDN_ERR_INVALID_ARG;
+  if (!run_norm_fwd(shape, o, z, w_norm, eps, y, (hipStream_t)stream)) return GDN_ERR_UNSUPPORTED;
+  return launched();
+}
+
+size_t gdn_norm_gate_bwd_workspace(const gdn_shape* shape) {
+  if (check_shape(shape) != GDN_OK) return 0;
+  return norm_bwd_ws_bytes(shape);
+}
+
+gdn_status gdn_norm_gate_bwd(const gdn_shape* shape, const void* dy, const void* o, const void* z, const void* w_norm,
+                             float eps, void* d_o, void* dz, float* dw_norm, void* ws, size_t ws_bytes,
+                             gdn_stream stream) {
+  gdn_status st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  if (!dy || !o || !z || !w_norm || !d_o || !dz || !dw_norm) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(dy) || !aligned16(o) || !aligned16(z) || !aligned16(w_norm) || !aligned16(d_o) || !aligned16(dz))
+    return GDN_ERR_INVALID_ARG;
+  if (!(eps >= 0.f)) return GDN_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws) || ws_bytes < norm_bwd_ws_bytes(shape)) return GDN_ERR_WORKSPACE;
+  if (!run_norm_bwd(shape, dy, o, z, w_norm, eps, d_o, dz, dw_norm, ws, (hipStream_t)stream))
+    return GDN_ERR_UNSUPPORTED;
+  return launched();
+}
+
+}  // extern "C"

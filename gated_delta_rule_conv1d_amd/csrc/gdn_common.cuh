@@ -1,0 +1,206 @@
+// Device helpers shared by the gfx950 kernels: bf16 conversion, the 16x16
+// MFMA tile primitive, wave reductions, and the per-chunk workspace layout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef uint16_t bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf2f(bf16 b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// float -> bf16, round to nearest even; NaN stays NaN, infinities pass.
+__device__ __forceinline__ bf16 f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (bf16)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16)(u >> 16);
+}
+
+template <typename E> __device__ __forceinline__ float to_f(E v);
+template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f<bf16>(bf16 v) { return bf2f(v); }
+
+template <typename E> __device__ __forceinline__ E from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float v) { return f2bf(v); }
+
+// 16-byte vector of elements: 8 bf16 or 4 float.
+template <typename E> struct Vec {
+  static constexpr int N = 16 / (int)sizeof(E);
+  __device__ static void load(const E* p, float* out) {
+    uint4 raw = *reinterpret_cast<const uint4*>(p);
+    const E* e = reinterpret_cast<const E*>(&raw);
+#pragma unroll
+    for (int i = 0; i < N; ++i) out[i] = to_f<E>(e[i]);
+  }
+  __device__ static void store(E* p, const float* in) {
+    uint4 raw;
+    E* e = reinterpret_cast<E*>(&raw);
+#pragma unroll
+    for (int i = 0; i < N; ++i) e[i] = from_f<E>(in[i]);
+    *reinterpret_cast<uint4*>(p) = raw;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// MFMA 16x16 tiles.  One wave computes D[16x16] += A[16xK] * B[Kx16] with
+// A stored row-major (K contiguous, row stride lda) and B stored column by
+// column (K contiguous, column stride ldb).  Both may live in LDS or global
+// memory.  Accumulator layout: lane l holds rows 4*(l>>4)+i (i<4), column l&15.
+// bf16 operands use v_mfma_f32_16x16x32_bf16 (8 k-values per lane), float
+// operands v_mfma_f32_16x16x4_f32 (1 k-value per lane).  The k-values each
+// lane supplies only have to agree between A and B, so any consistent k order
+// gives the same contraction.
+// ---------------------------------------------------------------------------
+template <typename E> struct Mma;
+
+template <> struct Mma<bf16> {
+  static constexpr int KS = 32, KPL = 8;
+  typedef bf16x8 frag;
+  __device__ static frag load(const bf16* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+  }
+  __device__ static frag from_floats(const float* v) {
+    uint4 raw;
+    bf16* e = reinterpret_cast<bf16*>(&raw);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = f2bf(v[i]);
+    return __builtin_bit_cast(bf16x8, raw);
+  }
+  __device__ static frag zero() { return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0)); }
+  __device__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mma<float> {
+  static constexpr int KS = 4, KPL = 1;
+  typedef float frag;
+  __device__ static frag load(const float* p) { return *p; }
+  __device__ static frag from_floats(const float* v) { return v[0]; }
+  __device__ static frag zero() { return 0.f; }
+  __device__ static f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+// accumulator coordinates
+__device__ __forceinline__ int acc_row(int i) { return 4 * (lane_id() >> 4) + i; }
+__device__ __forceinline__ int acc_col() { return lane_id() & 15; }
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+template <typename E, int K>
+__device__ __forceinline__ f32x4 mm_tile(f32x4 acc, const E* A, int lda, const E* B, int ldb) {
+  const int lane = lane_id();
+  const int r = lane & 15, kq = (lane >> 4) * Mma<E>::KPL;
+  const E* a = A + r * lda + kq;
+  const E* b = B + r * ldb + kq;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += Mma<E>::KS)
+    acc = Mma<E>::mma(Mma<E>::load(a + k0), Mma<E>::load(b + k0), acc);
+  return acc;
+}
+
+// Same contraction with float operands fed to the MFMA of type E: for E=bf16
+// each lane converts its 8 float k-values to bf16 on the fly.
+template <typename E, int K>
+__device__ __forceinline__ f32x4 mm_tile_f(f32x4 acc, const float* A, int lda, const float* B, int ldb) {
+  const int lane = lane_id();
+  const int r = lane & 15, kq = (lane >> 4) * Mma<E>::KPL;
+  const float* a = A + r * lda + kq;
+  const float* b = B + r * ldb + kq;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += Mma<E>::KS) {
+    float av[Mma<E>::KPL], bv[Mma<E>::KPL];
+#pragma unroll
+    for (int i = 0; i < Mma<E>::KPL; ++i) {
+      av[i] = a[k0 + i];
+      bv[i] = b[k0 + i];
+    }
+    acc = Mma<E>::mma(Mma<E>::from_floats(av), Mma<E>::from_floats(bv), acc);
+  }
+  return acc;
+}
+
+// A from float storage (converted to the MFMA type of E on the fly), B from E.
+template <typename E, int K>
+__device__ __forceinline__ f32x4 mm_tile_fa(f32x4 acc, const float* A, int lda, const E* B, int ldb) {
+  const int lane = lane_id();
+  const int r = lane & 15, kq = (lane >> 4) * Mma<E>::KPL;
+  const float* a = A + r * lda + kq;
+  const E* b = B + r * ldb + kq;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += Mma<E>::KS) {
+    float av[Mma<E>::KPL];
+#pragma unroll
+    for (int i = 0; i < Mma<E>::KPL; ++i) av[i] = a[k0 + i];
+    acc = Mma<E>::mma(Mma<E>::from_floats(av), Mma<E>::load(b + k0), acc);
+  }
+  return acc;
+}
+
+// Both operands from (global) row-major storage with row validity: A row r
+// (0..15 of the tile) is read only if r < a_rows, B "row" (output column) n
+// only if n < b_rows; others contribute zero.  Row strides are 64-bit.
+template <typename E, int K>
+__device__ __forceinline__ f32x4 mm_tile_rows(f32x4 acc, const E* A, int64_t lda, int a_rows, const E* B,
+                                              int64_t ldb, int b_rows) {
+  const int lane = lane_id();
+  const int r = lane & 15, kq = (lane >> 4) * Mma<E>::KPL;
+  const bool va = r < a_rows, vb = r < b_rows;
+  const E* a = A + (va ? r : 0) * lda + kq;
+  const E* b = B + (vb ? r : 0) * ldb + kq;
+  const typename Mma<E>::frag zf = Mma<E>::zero();
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += Mma<E>::KS) {
+    const typename Mma<E>::frag fa = va ? Mma<E>::load(a + k0) : zf;
+    const typename Mma<E>::frag fb = vb ? Mma<E>::load(b + k0) : zf;
+    acc = Mma<E>::mma(fa, fb, acc);
+  }
+  return acc;
+}
+
+// ---------------------------------------------------------------------------
+// Reductions
+// ---------------------------------------------------------------------------
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float v) {  // sum over aligned groups of WIDTH lanes
+#pragma unroll
+  for (int off = 1; off < WIDTH; off <<= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + __expf(-x)); }
+
+// ---------------------------------------------------------------------------
+// Workspace layout of the chunked recurrence.  Per chunk slot c and v-head h
+// (slot = index in the chunk table, tiles are zero-padded past the chunk's
+// length):
+//   Wk  [C][D]   E   T diag(beta*Gamma) K
+//   U   [C][D]   E   T diag(beta) V
+//   P   [C][C]   E   lower-inclusive (D_rs * q_r.k_s)
+//   Kt  [D][C]   E   (e^{gamma_last - gamma_s} k_s)^T
+//   gam [C]      f32 within-chunk cumulative gate (padding repeats the last)
+// ---------------------------------------------------------------------------
+struct ChunkWs {
+  int32_t* table;      // [max_chunks][4]
+  int32_t* seq_chunk0; // [N+1]
+  void* Wk;
+  void* U;
+  void* P;
+  void* Kt;
+  float* gam;
+};
+
+}  // namespace gdn

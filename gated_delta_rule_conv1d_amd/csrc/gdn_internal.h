@@ -1,0 +1,40 @@
+// Host-side declarations shared by the kernel translation units and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/gdn.h"
+
+namespace gdn {
+
+// conv1d.hip
+size_t conv_bwd_ws_bytes(const gdn_shape* s, int width);
+bool run_conv_fwd(const gdn_shape* s, const void* x, const void* w, int width, const int32_t* cu, float eps,
+                  void* y, hipStream_t st);
+bool run_conv_bwd(const gdn_shape* s, const void* dy, const void* x, const void* w, int width, const int32_t* cu,
+                  float eps, void* dx, float* dw, void* ws, hipStream_t st);
+
+// norm_gate.hip
+size_t norm_bwd_ws_bytes(const gdn_shape* s);
+bool run_norm_fwd(const gdn_shape* s, const void* o, const void* z, const void* w, float eps, void* y,
+                  hipStream_t st);
+bool run_norm_bwd(const gdn_shape* s, const void* dy, const void* o, const void* z, const void* w, float eps,
+                  void* d_o, void* dz, float* dw, void* ws, hipStream_t st);
+
+// chunk_fwd.hip / chunk_bwd.hip
+int64_t max_chunks(const gdn_shape* s);
+bool chunk_supported(const gdn_shape* s);
+void run_chunk_index(const gdn_shape* s, const int32_t* cu, int32_t* table, int32_t* seq_chunk0, hipStream_t st);
+size_t chunk_fwd_ws_bytes(const gdn_shape* s);
+size_t chunk_bwd_ws_bytes(const gdn_shape* s);
+bool run_chunk_fwd(const gdn_shape* s, const void* q, const void* k, const void* v, int64_t sqk, int64_t sv,
+                   const float* g, const float* beta, const int32_t* cu, const float* h0, void* o, float* ht,
+                   void* ws, hipStream_t st);
+bool run_chunk_bwd(const gdn_shape* s, const void* q, const void* k, const void* v, int64_t sqk, int64_t sv,
+                   const float* g, const float* beta, const int32_t* cu, const float* h0, const void* d_o,
+                   const float* dht, void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0,
+                   void* ws, hipStream_t st);
+
+}  // namespace gdn

@@ -1,0 +1,182 @@
+/*
+ * gdn.h -- C ABI of the GatedDeltaNet layer library for AMD MI355X (gfx950).
+ *
+ * The layer, over one packed row of N variable-length sequences:
+ *
+ *   conv:   y = SiLU(causal depthwise conv1d(x)), then each q and k head is
+ *           L2-normalised:  y <- y / sqrt(|y|^2 + eps)
+ *   chunk:  the gated delta rule per sequence and v-head,
+ *           S_t = e^{g_t} S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,
+ *           o_t = scale * S_t q_t,
+ *           evaluated chunk by chunk in the WY form
+ *   norm:   RMSNormGated:  y = o * rsqrt(mean(o^2) + eps) * w * SiLU(z)
+ *
+ * and the reverse mode of each step.  Where the pages name these pieces:
+ *  - "[Qwen3.5 MoE] Add hybrid decoder model (GatedDeltaNet + full attention +
+ *    MoE)", Summary: GatedDeltaNet linear attention, RMSNormGated, depthwise
+ *    conv1d, softplus gate.
+ *  - "Support Qwen35 SFT", XTuner changes: GatedDeltaNet with varlen support
+ *    on causal_conv1d and flash-linear-attention; per-token sequence ids.
+ *  - "feat(models): dense Qwen3.5 custom attention", Summary and review fix:
+ *    cu_seqlens derived from position_ids; the path receives one packed row.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers.  The caller allocates every
+ *    buffer, including workspace (sized by the *_workspace queries).  The
+ *    library allocates nothing, keeps no mutable global state, never
+ *    synchronises and never reads device memory from the host.  All work is
+ *    enqueued on `stream` (a hipStream_t; NULL means the default stream).
+ *  - Arguments are validated on the host before anything is enqueued; on any
+ *    error nothing is launched.  Device-side contents that break a documented
+ *    precondition (for example a cu_seqlens that is not non-decreasing or
+ *    does not end at total_tokens) give undefined results.
+ *  - cu_seqlens: int32 [N+1] on the device, cu[0] = 0, cu[N] = T,
+ *    non-decreasing; sequence n owns tokens [cu[n], cu[n+1]).  Zero-length
+ *    sequences are allowed.
+ *  - Element type of x, y, q, k, v, o, z, w_conv, w_norm and their gradients
+ *    is shape->dtype (GDN_F32 = float, GDN_BF16 = bfloat16).  g, beta,
+ *    states, dg, dbeta, dw_conv, dw_norm and state gradients are always
+ *    float32.  All arithmetic is float32 (bf16 values are MFMA operands).
+ *  - Layouts are token-major:  x, y [T][Cch] with Cch = 2*Hk*dk + Hv*dv and
+ *    channel blocks [q (Hk*dk) | k (Hk*dk) | v (Hv*dv)];  o, z, norm output
+ *    [T][Hv][dv];  g, beta [T][Hv];  states [N][Hv][dk][dv] holding H = S^T
+ *    (row i = key dimension, column c = value dimension).
+ *  - V-head h reads q/k head h / (Hv/Hk).
+ *  - Pointers must be 16-byte aligned; token strides (in elements) must keep
+ *    every row 16-byte aligned.
+ *  - Outputs are overwritten, never accumulated into.  Every result is
+ *    deterministic: the same inputs give the same bits on every run.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_INVALID_ARG = -1,  /* null required pointer, bad size, misaligned pointer/stride */
+  GDN_ERR_UNSUPPORTED = -2,  /* valid but unsupported shape (head dim, chunk, dtype, width) */
+  GDN_ERR_WORKSPACE = -3,    /* workspace pointer null or smaller than the query returns */
+  GDN_ERR_HIP = -4           /* a kernel launch failed (hipGetLastError) */
+} gdn_status;
+
+enum { GDN_F32 = 0, GDN_BF16 = 1 };
+
+typedef struct gdn_shape {
+  int32_t n_seqs;       /* N >= 1 */
+  int32_t total_tokens; /* T >= 0, equals cu_seqlens[N] */
+  int32_t h_qk;         /* Hk >= 1 */
+  int32_t h_v;          /* Hv >= 1, Hv % Hk == 0 */
+  int32_t d_k;          /* 16, 32, 64 or 128 */
+  int32_t d_v;          /* must equal d_k */
+  int32_t chunk;        /* 16, 32 or 64 (chunk <= 64; GDN_F32 with d=128 needs chunk <= 32) */
+  int32_t dtype;        /* GDN_F32 or GDN_BF16 */
+  float scale;          /* query scale (o_t = scale * S_t q_t) */
+} gdn_shape;
+
+typedef void* gdn_stream; /* hipStream_t */
+
+/* Human-readable name of a status code (static string). */
+const char* gdn_status_string(gdn_status status);
+
+/* --------------------------------------------------------------------------
+ * Chunk index (varlen bookkeeping).  Chunks of `chunk` tokens restart at each
+ * sequence start and never straddle two sequences; the last chunk of a
+ * sequence may be shorter.  Pages: "feat(models): dense Qwen3.5 custom
+ * attention" (cu_seqlens; seq_lens as the packed-sample boundary contract),
+ * "Support Qwen35 SFT" (review: per-token seq_idx needed by GatedDeltaNet).
+ *
+ * gdn_max_chunks: upper bound ceil(T/chunk) + N used to size every grid and
+ *   buffer without reading cu_seqlens on the host.
+ * gdn_chunk_index writes
+ *   table      int32 [max_chunks][4]: (sequence, first token, length, 0) for
+ *              chunk c < n_chunks, and (-1, 0, 0, 0) after the last chunk;
+ *   seq_chunk0 int32 [N+1]: index of the first chunk of each sequence,
+ *              seq_chunk0[N] = n_chunks.
+ * -------------------------------------------------------------------------- */
+int64_t gdn_max_chunks(const gdn_shape* shape);
+gdn_status gdn_chunk_index(const gdn_shape* shape, const int32_t* cu_seqlens,
+                           int32_t* table, int32_t* seq_chunk0, gdn_stream stream);
+
+/* --------------------------------------------------------------------------
+ * Causal depthwise conv1d + SiLU + L2 normalisation of q and k heads.
+ * Pages: "[Qwen3.5 MoE] Add hybrid decoder model", Summary (depthwise conv1d
+ * in GatedDeltaNet); "Support Qwen35 SFT", Notes and XTuner changes
+ * (causal_conv1d, varlen mode).
+ *   c[t, ch] = sum_{i < width} w_conv[ch][i] * x[t - width + 1 + i][ch], terms
+ *              before the first token of t's sequence are zero (no history is
+ *              carried into a sequence);
+ *   y = c * sigmoid(c);  q/k heads (channels < 2*Hk*dk, groups of dk):
+ *   y <- y / sqrt(sum(y^2) + l2_eps).
+ * x, y: [T][Cch] (y must not alias x); w_conv: [Cch][width]; width in 2..4.
+ * -------------------------------------------------------------------------- */
+gdn_status gdn_conv1d(const gdn_shape* shape, const void* x, const void* w_conv, int32_t width,
+                      float l2_eps, const int32_t* cu_seqlens, void* y, gdn_stream stream);
+
+/* Reverse mode of gdn_conv1d.  dy: gradient w.r.t. y [T][Cch]; writes dx
+ * [T][Cch] (dtype) and dw_conv [Cch][width] (float32, summed over all tokens
+ * in a fixed order).  Workspace: gdn_conv1d_bwd_workspace bytes. */
+size_t gdn_conv1d_bwd_workspace(const gdn_shape* shape, int32_t width);
+gdn_status gdn_conv1d_bwd(const gdn_shape* shape, const void* dy, const void* x, const void* w_conv,
+                          int32_t width, float l2_eps, const int32_t* cu_seqlens, void* dx,
+                          float* dw_conv, void* ws, size_t ws_bytes, gdn_stream stream);
+
+/* --------------------------------------------------------------------------
+ * Gated delta rule, chunked.  Pages: "[Qwen3.5 MoE] Add hybrid decoder
+ * model", Summary (GatedDeltaNet linear attention, FLA kernels optional with a
+ * naive fallback); "Support Qwen35 SFT", XTuner changes (varlen mode).
+ *   q, k: element (t, j, i) at q[t*tok_stride_qk + j*dk + i] (k likewise);
+ *   v:    element (t, h, c) at v[t*tok_stride_v + h*dv + c];
+ *   q and k are used as given (the caller normalises them: gdn_conv1d does);
+ *   g, beta: float32 [T][Hv]; g <= 0 is assumed for the stated accuracy;
+ *   h0: float32 [N][Hv][dk][dv] initial states, or NULL for zero states;
+ *   o:  [T][Hv][dv] output;  ht: float32 [N][Hv][dk][dv] final states or NULL.
+ * A zero-length sequence leaves its state unchanged (ht = h0 or 0).
+ * -------------------------------------------------------------------------- */
+size_t gdn_chunk_fwd_workspace(const gdn_shape* shape);
+gdn_status gdn_chunk_fwd(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                         int64_t tok_stride_qk, int64_t tok_stride_v, const float* g,
+                         const float* beta, const int32_t* cu_seqlens, const float* h0, void* o,
+                         float* ht, void* ws, size_t ws_bytes, gdn_stream stream);
+
+/* Reverse mode of gdn_chunk_fwd (recomputes the forward internally).
+ *   d_o: [T][Hv][dv] gradient w.r.t. o;  dht: float32 gradient w.r.t. ht, or NULL;
+ *   dq, dk: written with tok_stride_qk like q and k (may point into a
+ *           [T][Cch] buffer next to dv);  dv: written with tok_stride_v;
+ *   dg, dbeta: float32 [T][Hv];  dh0: float32 [N][Hv][dk][dv] or NULL. */
+size_t gdn_chunk_bwd_workspace(const gdn_shape* shape);
+gdn_status gdn_chunk_bwd(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                         int64_t tok_stride_qk, int64_t tok_stride_v, const float* g,
+                         const float* beta, const int32_t* cu_seqlens, const float* h0,
+                         const void* d_o, const float* dht, void* dq, void* dk, void* dv,
+                         float* dg, float* dbeta, float* dh0, void* ws, size_t ws_bytes,
+                         gdn_stream stream);
+
+/* --------------------------------------------------------------------------
+ * RMSNormGated epilogue.  Page: "[Qwen3.5 MoE] Add hybrid decoder model",
+ * Summary (RMSNormGated).
+ *   per row (token, v-head) of dv values:
+ *   y = o * rsqrt(mean(o^2) + eps) * w_norm * z * sigmoid(z)
+ * o, z, y: [T][Hv][dv]; w_norm: [dv] (dtype).  y may alias o.
+ * -------------------------------------------------------------------------- */
+gdn_status gdn_norm_gate(const gdn_shape* shape, const void* o, const void* z, const void* w_norm,
+                         float eps, void* y, gdn_stream stream);
+
+/* Reverse mode of gdn_norm_gate.  Writes d_o, dz [T][Hv][dv] (dtype) and
+ * dw_norm [dv] (float32, fixed-order sum over rows). */
+size_t gdn_norm_gate_bwd_workspace(const gdn_shape* shape);
+gdn_status gdn_norm_gate_bwd(const gdn_shape* shape, const void* dy, const void* o, const void* z,
+                             const void* w_norm, float eps, void* d_o, void* dz, float* dw_norm,
+                             void* ws, size_t ws_bytes, gdn_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,76 @@
+"""Helpers for the GPU parity tests: move seeded inputs to the device and
+compare with the oracle by max|diff| / RMS(oracle)."""
+import numpy as np
+import torch
+
+import gated_delta_rule_conv1d_amd as gdn
+import synth
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def to_dev(a: np.ndarray, dtype: str) -> torch.Tensor:
+    """float32 numpy values -> device tensor of the workload's element type
+    (bf16 values are exact: the arrays hold bf16-representable numbers)."""
+    if dtype == "bf16":
+        bits = synth.bf16_bits(np.asarray(a, dtype=np.float32))
+        return torch.from_numpy(bits.view(np.int16)).to(dev()).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev())
+
+
+def f32(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev())
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy()
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    ref = np.asarray(ref, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    if ref.size == 0:
+        return 0.0
+    err = float(np.max(np.abs(got - ref)))
+    return err / rms if rms > 0 else err
+
+
+def assert_close(got, ref, tol, name):
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    e = rel_err(got, ref)
+    assert e <= tol, f"{name}: max|diff|/rms = {e:.3e} > {tol:.0e}"
+    return e
+
+
+def shape_of(cfg: synth.Config, T=None, N=None, chunk=None, scale=1.0) -> gdn.Shape:
+    return gdn.Shape(n_seqs=N if N is not None else cfg.N, total_tokens=T if T is not None else cfg.T,
+                     h_qk=cfg.h_qk, h_v=cfg.h_v, d_k=cfg.d_k, d_v=cfg.d_v,
+                     chunk=chunk if chunk is not None else cfg.chunk,
+                     dtype=gdn.BF16 if cfg.dtype == "bf16" else gdn.F32, scale=scale)
+
+
+def small_cfg(dtype="bf16", lengths=(70, 1, 33, 64, 5), Hk=2, Hv=4, d=32, chunk=16, norm=True, h0=True,
+              bwd=True, seed=7, weak=False):
+    return synth.Config(name="case", lengths=tuple(lengths), h_qk=Hk, h_v=Hv, d_k=d, d_v=d, chunk=chunk,
+                        dtype=dtype, norm=norm, h0=h0, bwd=bwd, seed=seed, weak_decay=weak)
+
+
+def qkv_inputs(cfg: synth.Config, seed=11):
+    """Synthetic unit-norm q, k and N(0,1) v in the storage precision (used by
+    the per-call chunk tests so both sides start from identical values)."""
+    rng = np.random.default_rng(seed)
+    T = cfg.T
+    q = rng.standard_normal((T, cfg.h_qk, cfg.d_k))
+    k = rng.standard_normal((T, cfg.h_qk, cfg.d_k))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, cfg.h_v, cfg.d_v))
+    q, k, v = (a.astype(np.float32) for a in (q, k, v))
+    if cfg.dtype == "bf16":
+        q, k, v = (synth.round_bf16(a) for a in (q, k, v))
+    return q, k, v

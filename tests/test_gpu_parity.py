@@ -1,0 +1,193 @@
+"""GPU parity: every C-ABI call and the whole layer against the CPU oracle,
+element by element, on seeded inputs spanning several chunks and ragged
+tails.  Tolerance: max|gpu - oracle| <= tol * RMS(oracle), tol = 1e-4 (fp32
+storage) or 2e-2 (bf16 storage, fp32 accumulation)."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_conv1d_amd as gdn
+import oracle
+import synth
+from gpu_util import (TOL, assert_close, f32, host, qkv_inputs, shape_of, small_cfg, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _print_case(name, **kw):
+    print(f"[case] {name} " + " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+# ----------------------------------------------------------------------------- A0 chunk index
+@pytest.mark.parametrize("lengths,chunk", [((64,), 16), ((5, 0, 16, 17, 1), 16), ((2048,) * 4, 64),
+                                           ((0, 0, 3), 32), ((1,) * 300, 64), ((4097, 0, 63, 65, 64), 64)])
+def test_chunk_index_bit_exact(lengths, chunk):
+    _print_case("chunk_index", lengths=len(lengths), chunk=chunk)
+    cfg = small_cfg(lengths=lengths, chunk=chunk)
+    s = shape_of(cfg)
+    cu = synth.cu_from_lengths(lengths)
+    table, first = gdn.chunk_index(torch.from_numpy(cu).cuda(), s)
+    torch.cuda.synchronize()
+    ref_tab, ref_first = oracle.chunk_table(cu, chunk)
+    tab = table.cpu().numpy()
+    n = len(ref_tab)
+    np.testing.assert_array_equal(first.cpu().numpy(), ref_first)
+    np.testing.assert_array_equal(tab[:n, :3], ref_tab)
+    assert np.all(tab[n:, 0] == -1)
+
+
+# ----------------------------------------------------------------------------- A1 conv
+@pytest.mark.parametrize("dtype,d,lengths", [("f32", 16, (64,)), ("f32", 32, (1, 2, 3, 70, 9)),
+                                             ("bf16", 128, (1, 3, 64, 130, 2, 77)), ("bf16", 64, (200,)),
+                                             ("bf16", 16, (5, 0, 40))])
+@pytest.mark.parametrize("width", [4, 3])
+def test_conv1d_fwd_bwd(dtype, d, lengths, width):
+    _print_case("conv1d", dtype=dtype, d=d, lengths=lengths, width=width)
+    cfg = small_cfg(dtype=dtype, lengths=lengths, d=d).replace(width=width)
+    inp = synth.make_inputs(cfg)
+    s = shape_of(cfg)
+    nqk = 2 * cfg.h_qk * cfg.d_k
+    x, w, cu = to_dev(inp["x"], dtype), to_dev(inp["w_conv"], dtype), torch.from_numpy(inp["cu"]).cuda()
+    y = gdn.conv1d(x, w, cu, s)
+    ref = oracle.conv1d(inp["x"], inp["w_conv"], inp["cu"], nqk, cfg.d_k)
+    assert_close(host(y), ref, TOL[dtype], "y")
+    rng = np.random.default_rng(3)
+    dy = rng.standard_normal(inp["x"].shape).astype(np.float32)
+    if dtype == "bf16":
+        dy = synth.round_bf16(dy)
+    dx, dw = gdn.conv1d_bwd(to_dev(dy, dtype), x, w, cu, s)
+    rdx, rdw = oracle.conv1d_bwd(inp["x"], inp["w_conv"], inp["cu"], nqk, cfg.d_k, dy)
+    assert_close(host(dx), rdx, TOL[dtype], "dx")
+    assert_close(host(dw), rdw, TOL[dtype], "dw_conv")
+
+
+# ----------------------------------------------------------------------------- A6 norm gate
+@pytest.mark.parametrize("dtype,d", [("f32", 16), ("bf16", 128), ("bf16", 32)])
+def test_norm_gate_fwd_bwd(dtype, d):
+    _print_case("norm_gate", dtype=dtype, d=d)
+    cfg = small_cfg(dtype=dtype, d=d, lengths=(37, 100))
+    inp = synth.make_inputs(cfg)
+    s = shape_of(cfg)
+    rng = np.random.default_rng(5)
+    o = rng.standard_normal((cfg.T, cfg.h_v, d)).astype(np.float32)
+    dy = rng.standard_normal((cfg.T, cfg.h_v, d)).astype(np.float32)
+    if dtype == "bf16":
+        o, dy = synth.round_bf16(o), synth.round_bf16(dy)
+    z, wn = inp["z"], inp["w_norm"]
+    y = gdn.norm_gate(to_dev(o, dtype), to_dev(z, dtype), to_dev(wn, dtype), s)
+    assert_close(host(y), oracle.norm_gate(o, z, wn), TOL[dtype], "y")
+    d_o, dz, dw = gdn.norm_gate_bwd(to_dev(dy, dtype), to_dev(o, dtype), to_dev(z, dtype), to_dev(wn, dtype), s)
+    rdo, rdz, rdw = oracle.norm_gate_bwd(o, z, wn, dy)
+    assert_close(host(d_o), rdo, TOL[dtype], "d_o")
+    assert_close(host(dz), rdz, TOL[dtype], "dz")
+    assert_close(host(dw), rdw, TOL[dtype], "dw_norm")
+
+
+# ----------------------------------------------------------------------------- A3-A5, A7 chunk
+CHUNK_CASES = [
+    ("f32", 16, 16, 2, 2, (64,)),
+    ("f32", 16, 16, 1, 2, (40, 1, 23)),
+    ("f32", 32, 32, 2, 4, (70, 1, 33, 64, 5)),
+    ("f32", 64, 64, 1, 2, (130, 7)),
+    ("bf16", 128, 64, 2, 4, (200, 1, 64, 63, 65)),
+    ("bf16", 128, 32, 1, 2, (100, 33)),
+    ("bf16", 64, 16, 2, 2, (50, 17)),
+    ("bf16", 32, 64, 1, 1, (129,)),
+]
+
+
+@pytest.mark.parametrize("dtype,d,chunk,Hk,Hv,lengths", CHUNK_CASES)
+def test_chunk_fwd_bwd(dtype, d, chunk, Hk, Hv, lengths):
+    _print_case("chunk", dtype=dtype, d=d, chunk=chunk, Hk=Hk, Hv=Hv, lengths=lengths)
+    cfg = small_cfg(dtype=dtype, d=d, chunk=chunk, Hk=Hk, Hv=Hv, lengths=lengths)
+    inp = synth.make_inputs(cfg)
+    q, k, v = qkv_inputs(cfg)
+    s = shape_of(cfg, scale=0.75)
+    cu = torch.from_numpy(inp["cu"]).cuda()
+    T = cfg.T
+    qd, kd, vd = to_dev(q.reshape(T, -1), dtype), to_dev(k.reshape(T, -1), dtype), to_dev(v.reshape(T, -1), dtype)
+    g, beta, h0 = f32(inp["g"]), f32(inp["beta"]), f32(inp["h0"])
+    o, ht = gdn.chunk_fwd(qd, kd, vd, g, beta, cu, s, h0=h0)
+    ro, rht = oracle.recurrence(q, k, v, inp["g"], inp["beta"], inp["cu"], h0=inp["h0"], scale=0.75)
+    tol = TOL[dtype]
+    assert_close(host(o), ro, tol, "o")
+    assert_close(host(ht), rht, tol, "ht")
+    rng = np.random.default_rng(9)
+    d_o = rng.standard_normal(ro.shape).astype(np.float32)
+    dht = rng.standard_normal(rht.shape).astype(np.float32)
+    if dtype == "bf16":
+        d_o = synth.round_bf16(d_o)
+    r = gdn.chunk_bwd(qd, kd, vd, g, beta, cu, s, to_dev(d_o, dtype), h0=h0, dht=f32(dht))
+    ref = oracle.recurrence_bwd(q, k, v, inp["g"], inp["beta"], inp["cu"], d_o, h0=inp["h0"], dht=dht, scale=0.75)
+    assert_close(host(r["dq"]).reshape(ref["dq"].shape), ref["dq"], tol, "dq")
+    assert_close(host(r["dk"]).reshape(ref["dk"].shape), ref["dk"], tol, "dk")
+    assert_close(host(r["dv"]).reshape(ref["dv"].shape), ref["dv"], tol, "dv")
+    assert_close(host(r["dg"]), ref["dg"], tol, "dg")
+    assert_close(host(r["dbeta"]), ref["dbeta"], tol, "dbeta")
+    assert_close(host(r["dh0"]), ref["dh0"], tol, "dh0")
+
+
+def test_chunk_weak_decay_long_range():
+    """A_log = -6: the state is carried across many chunks (long-range path)."""
+    cfg = small_cfg(dtype="bf16", d=64, chunk=64, Hk=1, Hv=2, lengths=(1000, 300), weak=True)
+    _print_case("weak_decay", lengths=cfg.lengths)
+    inp = synth.make_inputs(cfg)
+    q, k, v = qkv_inputs(cfg)
+    s = shape_of(cfg)
+    T = cfg.T
+    o, ht = gdn.chunk_fwd(to_dev(q.reshape(T, -1), "bf16"), to_dev(k.reshape(T, -1), "bf16"),
+                          to_dev(v.reshape(T, -1), "bf16"), f32(inp["g"]), f32(inp["beta"]),
+                          torch.from_numpy(inp["cu"]).cuda(), s, h0=f32(inp["h0"]))
+    ro, rht = oracle.recurrence(q, k, v, inp["g"], inp["beta"], inp["cu"], h0=inp["h0"])
+    assert_close(host(o), ro, TOL["bf16"], "o")
+    assert_close(host(ht), rht, TOL["bf16"], "ht")
+
+
+# ----------------------------------------------------------------------------- whole layer
+def _layer_gpu(cfg, inp):
+    s = shape_of(cfg)
+    dt = cfg.dtype
+    L = gdn.GatedDeltaNetLayer(s, cfg.width, norm=cfg.norm)
+    t = dict(x=to_dev(inp["x"], dt), w=to_dev(inp["w_conv"], dt), g=f32(inp["g"]), beta=f32(inp["beta"]),
+             cu=torch.from_numpy(inp["cu"]).cuda(),
+             z=to_dev(inp["z"], dt) if "z" in inp else None, wn=to_dev(inp["w_norm"], dt) if "w_norm" in inp else None,
+             h0=f32(inp["h0"]) if "h0" in inp else None)
+    fwd = L.forward(t["x"], t["w"], t["g"], t["beta"], t["cu"], t["z"], t["wn"], t["h0"])
+    bwd = None
+    if cfg.bwd:
+        dy = to_dev(inp["dy"], dt) if cfg.norm else to_dev(inp["dy"], dt)
+        bwd = L.backward(dy, t["x"], t["w"], t["g"], t["beta"], t["cu"], fwd, t["z"], t["wn"], t["h0"])
+    torch.cuda.synchronize()
+    return fwd, bwd
+
+
+@pytest.mark.parametrize("norm,h0", [(False, False), (True, True)])
+def test_layer_tiny_full(norm, h0):
+    cfg = synth.config("tiny").replace(norm=norm, h0=h0, bwd=True)
+    _print_case("layer_tiny", norm=norm, h0=h0)
+    inp = synth.make_inputs(cfg)
+    fwd, bwd = _layer_gpu(cfg, inp)
+    ref = oracle.layer_fwd(cfg, inp)
+    tol = TOL["f32"]
+    assert_close(host(fwd["o"]), ref["o"], tol, "o")
+    assert_close(host(fwd["ht"]), ref["ht"], tol, "ht")
+    if norm:
+        assert_close(host(fwd["y"]), ref["y"], tol, "y")
+    dy = inp["dy"]
+    rb = oracle.layer_bwd(cfg, inp, ref, dy)
+    for key in ("dx", "dw_conv", "dg", "dbeta") + (("dz", "dw_norm", "dh0") if norm else ()):
+        assert_close(host(bwd[key]), rb[key], tol, key)
+
+
+def test_layer_small_bf16_full():
+    cfg = small_cfg(dtype="bf16", d=128, chunk=64, Hk=2, Hv=4, lengths=(300, 1, 64, 65, 130))
+    _print_case("layer_small_bf16", lengths=cfg.lengths)
+    inp = synth.make_inputs(cfg)
+    fwd, bwd = _layer_gpu(cfg, inp)
+    ref = oracle.layer_fwd(cfg, inp)
+    rb = oracle.layer_bwd(cfg, inp, ref, inp["dy"])
+    tol = TOL["bf16"]
+    assert_close(host(fwd["y"]), ref["y"], tol, "y")
+    assert_close(host(fwd["ht"]), ref["ht"], tol, "ht")
+    for key in ("dx", "dw_conv", "dg", "dbeta", "dz", "dw_norm", "dh0"):
+        assert_close(host(bwd[key]), rb[key], tol, key)
