@@ -29,17 +29,26 @@ void launch_chunk_fwd_core(const ChunkArgs& a, hipStream_t st, bool out_mode);
 
 // ---------------------------------------------------------------------------
 // Reverse state pass, one workgroup per (sequence, v-head, dv tile).
+// fp32 operands that decide the result (P, Gam q, dW, dH) enter the bf16
+// MFMAs as hi + lo parts; dO, Wk and K~ are used as stored.
 // ---------------------------------------------------------------------------
 template <typename E, int D, int C, int DVT>
 struct StateBwdSmem {
+  static constexpr int LO = Split<E>::on ? 1 : 0;
   static constexpr int LDQ = D + Pad<E>::E16;
   static constexpr int LDCE = C + Pad<E>::E16;
   static constexpr int LD2C = 2 * C + Pad<E>::E16;
   E Pt[C][LDCE];
+  E Ptl[LO ? C : 1][LDCE];
   E Ktil[C][LDQ];
-  E QW[D][LD2C];
-  E OW[DVT][LD2C];
+  E Ktill[LO ? C : 1][LDQ];  // lo part of K~
+  E QW[D][LD2C];             // [ (Gam q)^T | -Wk^T ]
+  E Qlo[LO ? D : 1][LDCE];   // lo part of (Gam q)^T
+  E Wklo[LO ? D : 1][LDCE];  // lo part of -Wk^T
+  E OW[DVT][LD2C];           // [ dO^T | dW^T ]
+  E dWlo[LO ? DVT : 1][LDCE];
   E dHt[DVT][LDQ];
+  E dHtl[LO ? DVT : 1][LDQ];
   float gam[C];
   float Gm[C];
 };
@@ -48,6 +57,7 @@ template <typename E, int D, int C, int DVT>
 __global__ __launch_bounds__(kChunkThreads) void state_bwd_kernel(ChunkArgs a) {
   using S = StateBwdSmem<E, D, C, DVT>;
   __shared__ S sm;
+  constexpr bool LO = Split<E>::on;
   constexpr int NVT = D / DVT;
   constexpr int NCT = DVT / 16;
   constexpr int NHT = (D / 16) * NCT;
@@ -78,7 +88,10 @@ __global__ __launch_bounds__(kChunkThreads) void state_bwd_kernel(ChunkArgs a) {
       if (t < NHT) {
         const int rt = t / NCT, ct = t % NCT;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm.dHt[ct * 16 + acc_col()][rt * 16 + acc_row(e)] = from_f<E>(dH[i][e]);
+        for (int e = 0; e < 4; ++e) {
+          const int c = ct * 16 + acc_col(), r = rt * 16 + acc_row(e);
+          split_store<E>(&sm.dHt[c][r], &sm.dHtl[0][0] + c * S::LDQ + r, dH[i][e]);
+        }
       }
     }
   };
@@ -90,11 +103,11 @@ __global__ __launch_bounds__(kChunkThreads) void state_bwd_kernel(ChunkArgs a) {
     const int tok0 = ent.y, len = ent.z;
     const int64_t slot = (int64_t)ci * a.Hv + h;
     {  // gradient w.r.t. the state leaving this chunk
-      E* dst = (E*)a.dHn + slot * D * D;
+      float* dst = a.dHn + slot * D * D;
 #pragma unroll
       for (int i = 0; i < NHW; ++i) {
         const int t = w + kChunkWaves * i;
-        if (t < NHT) store_tile<E>(dst, D, (t / NCT) * 16, col0 + (t % NCT) * 16, dH[i], D);
+        if (t < NHT) store_tile<float>(dst, D, (t / NCT) * 16, col0 + (t % NCT) * 16, dH[i], D);
       }
     }
     for (int e = threadIdx.x; e < C; e += kChunkThreads) {
@@ -103,23 +116,50 @@ __global__ __launch_bounds__(kChunkThreads) void state_bwd_kernel(ChunkArgs a) {
       sm.Gm[e] = __expf(gm);
     }
     __syncthreads();
-    rows2s_t<E, C, C>(&sm.Pt[0][0], S::LDCE, (const E*)a.P + slot * C * C, C, C, nullptr, 1.f);
+    {
+      const float* Pg = a.P + slot * C * C;
+      for (int e = threadIdx.x; e < C * C; e += kChunkThreads) {
+        const int r = e / C, c = e % C;  // P[r][c] -> Pt[c][r]
+        split_store<E>(&sm.Pt[c][r], &sm.Ptl[0][0] + c * S::LDCE + r, Pg[e]);
+      }
+      const E* qg = (const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D;
+      for (int e = threadIdx.x; e < C * D; e += kChunkThreads) {
+        const int r = e / D, d = e % D;  // (Gam_r q_r)^T
+        const float qv = r < len ? sm.Gm[r] * to_f<E>(qg[(int64_t)r * a.sqk + d]) : 0.f;
+        split_store<E>(&sm.QW[d][r], &sm.Qlo[0][0] + d * S::LDCE + r, qv);
+      }
+    }
     rows2s_t<E, D, C>(&sm.Ktil[0][0], S::LDQ, (const E*)a.Kt + slot * D * C, C, D, nullptr, 1.f);
-    rows2s_t<E, C, D>(&sm.QW[0][0], S::LD2C, (const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D, a.sqk, len,
-                      sm.Gm, 1.f);
     rows2s_t<E, C, D>(&sm.QW[0][C], S::LD2C, (const E*)a.Wk + slot * C * D, D, C, nullptr, -1.f);
+    if constexpr (LO) {
+      rows2s_t<E, D, C>(&sm.Ktill[0][0], S::LDQ, (const E*)a.Ktl + slot * D * C, C, D, nullptr, 1.f);
+      rows2s_t<E, C, D>(&sm.Wklo[0][0], S::LDCE, (const E*)a.Wkl + slot * C * D, D, C, nullptr, -1.f);
+    }
     rows2s_t<E, C, DVT>(&sm.OW[0][0], S::LD2C, (const E*)a.d_o + (int64_t)tok0 * a.Hv * D + (int64_t)h * D + col0,
-                        (int64_t)a.Hv * D, len, nullptr, a.scale);
+                        (int64_t)a.Hv * D, len, nullptr, 1.f);
     __syncthreads();
 
-    E* dWg = (E*)a.dW + slot * C * D;
+    float* dWg = a.dW + slot * C * D;
+    float* dWtg = a.dWt + slot * D * C;
     for (int t = w; t < NWT; t += kChunkWaves) {
       const int rt = t / NCT, ct = t % NCT;
-      f32x4 acc = mm_tile<E, C>(zero4(), &sm.Pt[rt * 16][0], S::LDCE, &sm.OW[ct * 16][0], S::LD2C);
-      acc = mm_tile<E, D>(acc, &sm.Ktil[rt * 16][0], S::LDQ, &sm.dHt[ct * 16][0], S::LDQ);
-      store_tile<E>(dWg, D, rt * 16, col0 + ct * 16, acc, C);
+      f32x4 p = mm_tile<E, C>(zero4(), &sm.Pt[rt * 16][0], S::LDCE, &sm.OW[ct * 16][0], S::LD2C);
+      if constexpr (LO) p = mm_tile<E, C>(p, &sm.Ptl[rt * 16][0], S::LDCE, &sm.OW[ct * 16][0], S::LD2C);
+      f32x4 kd = mm_tile<E, D>(zero4(), &sm.Ktil[rt * 16][0], S::LDQ, &sm.dHt[ct * 16][0], S::LDQ);
+      if constexpr (LO) {
+        kd = mm_tile<E, D>(kd, &sm.Ktil[rt * 16][0], S::LDQ, &sm.dHtl[ct * 16][0], S::LDQ);
+        kd = mm_tile<E, D>(kd, &sm.Ktill[rt * 16][0], S::LDQ, &sm.dHt[ct * 16][0], S::LDQ);
+      }
+      f32x4 acc;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sm.OW[ct * 16 + acc_col()][C + rt * 16 + acc_row(e)] = from_f<E>(acc[e]);
+      for (int e = 0; e < 4; ++e) acc[e] = a.scale * p[e] + kd[e];
+      store_tile<float>(dWg, D, rt * 16, col0 + ct * 16, acc, C);
+      store_tile_t(dWtg, C, rt * 16, col0 + ct * 16, acc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = ct * 16 + acc_col(), r = rt * 16 + acc_row(e);
+        split_store<E>(&sm.OW[c][C + r], &sm.dWlo[0][0] + c * S::LDCE + r, acc[e]);
+      }
     }
     __syncthreads();
     const float gl = sm.Gm[len - 1];
@@ -128,9 +168,15 @@ __global__ __launch_bounds__(kChunkThreads) void state_bwd_kernel(ChunkArgs a) {
       const int t = w + kChunkWaves * i;
       if (t < NHT) {
         const int rt = t / NCT, ct = t % NCT;
-        const f32x4 y = mm_tile<E, 2 * C>(zero4(), &sm.QW[rt * 16][0], S::LD2C, &sm.OW[ct * 16][0], S::LD2C);
+        f32x4 y1 = mm_tile<E, C>(zero4(), &sm.QW[rt * 16][0], S::LD2C, &sm.OW[ct * 16][0], S::LD2C);
+        if constexpr (LO) y1 = mm_tile<E, C>(y1, &sm.Qlo[rt * 16][0], S::LDCE, &sm.OW[ct * 16][0], S::LD2C);
+        f32x4 y2 = mm_tile<E, C>(zero4(), &sm.QW[rt * 16][C], S::LD2C, &sm.OW[ct * 16][C], S::LD2C);
+        if constexpr (LO) {
+          y2 = mm_tile<E, C>(y2, &sm.QW[rt * 16][C], S::LD2C, &sm.dWlo[ct * 16][0], S::LDCE);
+          y2 = mm_tile<E, C>(y2, &sm.Wklo[rt * 16][0], S::LDCE, &sm.OW[ct * 16][C], S::LD2C);
+        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dH[i][e] = gl * dH[i][e] + y[e];
+        for (int e = 0; e < 4; ++e) dH[i][e] = gl * dH[i][e] + a.scale * y1[e] + y2[e];
       }
     }
     __syncthreads();
@@ -152,14 +198,16 @@ __global__ __launch_bounds__(kChunkThreads) void state_bwd_kernel(ChunkArgs a) {
 
 // ---------------------------------------------------------------------------
 // Contractions over d_v, one workgroup per (chunk, v-head):
-//   dWk = -dW Hc^T  (kept in LDS and written to workspace)
+//   dWk = -dW Hc^T  (hi/lo in LDS; transposed fp32 copy to workspace)
 //   dT  = beta_s (dW V^T)_rs + beta_s Gam_s (dWk K^T)_rs
 //   hdot = <Hc, dHn>
 // ---------------------------------------------------------------------------
 template <typename E, int D, int C>
 struct GradASmem {
+  static constexpr int LO = Split<E>::on ? 1 : 0;
   static constexpr int LDQ = D + Pad<E>::E16;
   E dWk[C][LDQ];
+  E dWkl[LO ? C : 1][LDQ];
   E Vs[C][LDQ];
   E Ks[C][LDQ];
   float bs[C];
@@ -169,7 +217,9 @@ struct GradASmem {
 template <typename E, int D, int C>
 __global__ __launch_bounds__(kChunkThreads) void grad_a_kernel(ChunkArgs a) {
   using S = GradASmem<E, D, C>;
+  using M = Mma<E>;
   __shared__ S sm;
+  constexpr bool LO = Split<E>::on;
   constexpr int NT = C / 16, ND = D / 16;
   const int ci = blockIdx.x, h = blockIdx.y;
   const int4 ent = chunk_entry(a.table, ci);
@@ -178,29 +228,31 @@ __global__ __launch_bounds__(kChunkThreads) void grad_a_kernel(ChunkArgs a) {
   const int j = h / a.G;
   const int w = wave_id(), tid = threadIdx.x;
   const int64_t slot = (int64_t)ci * a.Hv + h;
-  const E* Hc = (const E*)a.Hc + slot * D * D;
-  const E* dW = (const E*)a.dW + slot * C * D;
+  const float* Hc = a.Hc + slot * D * D;
+  const float* dW = a.dW + slot * C * D;
 
   rows2s<E, C, D>(&sm.Vs[0][0], S::LDQ, (const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)h * D, a.sv, len);
   rows2s<E, C, D>(&sm.Ks[0][0], S::LDQ, (const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D, a.sqk, len);
   for (int e = tid; e < C; e += kChunkThreads) sm.bs[e] = e < len ? a.beta[(int64_t)(tok0 + e) * a.Hv + h] : 0.f;
-  E* dWkg = (E*)a.dWk + slot * C * D;
+  float* dWkt = a.dWkt + slot * D * C;
   for (int t = w; t < NT * ND; t += kChunkWaves) {
     const int rt = t / ND, ct = t % ND;
-    const f32x4 acc = mm_tile<E, D>(zero4(), dW + rt * 16 * D, D, Hc + ct * 16 * D, D);
+    const f32x4 acc = mm_gen<E, D, true, true>(
+        zero4(), [&](int r, int k, float* o) { ld_row<float, M::KPL>(dW + (rt * 16 + r) * D + k, o); },
+        [&](int c, int k, float* o) { ld_row<float, M::KPL>(Hc + (ct * 16 + c) * D + k, o); });
     f32x4 neg;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       neg[e] = -acc[e];
-      sm.dWk[rt * 16 + acc_row(e)][ct * 16 + acc_col()] = from_f<E>(neg[e]);
+      const int r = rt * 16 + acc_row(e), c = ct * 16 + acc_col();
+      split_store<E>(&sm.dWk[r][c], &sm.dWkl[0][0] + r * S::LDQ + c, neg[e]);
     }
-    store_tile<E>(dWkg, D, rt * 16, ct * 16, neg, C);
+    store_tile_t(dWkt, C, rt * 16, ct * 16, neg);
   }
-  // <Hc, dHn>
-  {
-    const E* dHn = (const E*)a.dHn + slot * D * D;
+  {  // <Hc, dHn>
+    const float* dHn = a.dHn + slot * D * D;
     float s = 0.f;
-    for (int e = tid; e < D * D; e += kChunkThreads) s += to_f<E>(Hc[e]) * to_f<E>(dHn[e]);
+    for (int e = tid; e < D * D; e += kChunkThreads) s += Hc[e] * dHn[e];
     sm.red[tid] = s;
   }
   __syncthreads();
@@ -213,8 +265,11 @@ __global__ __launch_bounds__(kChunkThreads) void grad_a_kernel(ChunkArgs a) {
   float* dTg = a.dT + slot * C * C;
   for (int t = w; t < NT * NT; t += kChunkWaves) {
     const int rt = t / NT, ct = t % NT;
-    const f32x4 xu = mm_tile<E, D>(zero4(), dW + rt * 16 * D, D, &sm.Vs[ct * 16][0], S::LDQ);
-    const f32x4 xw = mm_tile<E, D>(zero4(), &sm.dWk[rt * 16][0], S::LDQ, &sm.Ks[ct * 16][0], S::LDQ);
+    const f32x4 xu = mm_gen<E, D, true, false>(
+        zero4(), [&](int r, int k, float* o) { ld_row<float, M::KPL>(dW + (rt * 16 + r) * D + k, o); },
+        [&](int c, int k, float* o) { ld_row<E, M::KPL>(&sm.Vs[ct * 16 + c][k], o); });
+    f32x4 xw = mm_tile<E, D>(zero4(), &sm.dWk[rt * 16][0], S::LDQ, &sm.Ks[ct * 16][0], S::LDQ);
+    if constexpr (LO) xw = mm_tile<E, D>(xw, &sm.dWkl[rt * 16][0], S::LDQ, &sm.Ks[ct * 16][0], S::LDQ);
     const int s = ct * 16 + acc_col();
     const float bsv = sm.bs[s], bg = bsv * __expf(gam[s]);
 #pragma unroll
@@ -228,20 +283,16 @@ __global__ __launch_bounds__(kChunkThreads) void grad_a_kernel(ChunkArgs a) {
 // ---------------------------------------------------------------------------
 template <typename E, int D, int C>
 struct GradBSmem {
-  static constexpr int LDQ = D + Pad<E>::E16;
-  static constexpr int LDCE = C + Pad<E>::E16;
   static constexpr int LD2C = 2 * C + Pad<E>::E16;
   static constexpr int LDCF = C + 4;
   static constexpr int NT = C / 16, ND = D / 16;
-  E QKt[D][LD2C];   // [Q^T | K^T]
+  E QKt[D][LD2C];     // [Q^T | K^T]
   float Am[C][LDCF];  // A, then dA
   float Tm[C][LDCF];
   float Tt[C][LDCF];
-  float dT[C][LDCF];
   union U {
-    struct { E dUt[D][LDCE]; E dWkt[D][LDCE]; } x;
     float M1t[C][LDCF];
-    struct { E dS[C][LDCE]; E dSA[C][LD2C]; E Att[C][LDCE]; } s;
+    struct { float dS[C][LDCF]; float At[C][LDCF]; } s;
     float Xs[kChunkWaves][16][20];
   } r;
   float gam[C], beta[C], Gm[C], em[C];
@@ -252,6 +303,8 @@ struct GradBSmem {
 template <typename E, int D, int C>
 __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
   using S = GradBSmem<E, D, C>;
+  using M = Mma<E>;
+  constexpr int KPL = M::KPL;
   __shared__ S sm;
   constexpr int NT = S::NT, ND = S::ND;
   constexpr int NQT = NT * ND;
@@ -277,6 +330,21 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
     const E* vg = (const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)h * D;
     const E* dog = (const E*)a.d_o + (int64_t)tok0 * a.Hv * D + (int64_t)h * D;
     const int64_t ldo = (int64_t)a.Hv * D;
+    const float* Wg = a.W + slot * C * D;
+    const float* Hc = a.Hc + slot * D * D;
+    const float* dHn = a.dHn + slot * D * D;
+    const float* dWt = a.dWt + slot * D * C;
+    const float* dWkt = a.dWkt + slot * D * C;
+    const float* dTg = a.dT + slot * C * C;
+    const float* Pg = a.P + slot * C * C;
+    auto do_rows = [&](int r0) {  // masked rows of dO
+      return [&, r0](int r, int k, float* o) {
+        if (r0 + r < len) ld_row<E, KPL>(dog + (int64_t)(r0 + r) * ldo + k, o);
+        else
+#pragma unroll
+          for (int i = 0; i < KPL; ++i) o[i] = 0.f;
+      };
+    };
     for (int e = tid; e < C; e += kChunkThreads) {
       const float gm = a.gam[slot * C + e];
       sm.gam[e] = gm;
@@ -300,20 +368,18 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
     }
     __syncthreads();
     unit_lower_inverse<C, S::LDCF>(sm.Am, sm.Tm, sm.Tt, sm.r.Xs);
-    // dU (= dW) and dWk transposed into LDS, dT
-    rows2s_t<E, C, D>(&sm.r.x.dUt[0][0], S::LDCE, (const E*)a.dW + slot * C * D, D, C, nullptr, 1.f);
-    rows2s_t<E, C, D>(&sm.r.x.dWkt[0][0], S::LDCE, (const E*)a.dWk + slot * C * D, D, C, nullptr, 1.f);
-    for (int e = tid; e < C * C; e += kChunkThreads) sm.dT[e / C][e % C] = a.dT[slot * C * C + e];
-    __syncthreads();
-    // dXu = T^T dU -> dv, <dXu, v>;  dXw = T^T dWk -> dK, <dXw, k>
+    // dXu = T^T dW -> dv, <dXu, v>;  dXw = T^T dWk -> dK, <dXw, k>
     E* dvg = (E*)a.dv + (int64_t)tok0 * a.sv + (int64_t)h * D;
 #pragma unroll
     for (int i = 0; i < NQW; ++i) {
       const int t = w + kChunkWaves * i;
       if (t < NQT) {
         const int rt = t / ND, ct = t % ND;
-        const f32x4 xu = mm_tile_fa<E, C>(zero4(), &sm.Tt[rt * 16][0], S::LDCF, &sm.r.x.dUt[ct * 16][0], S::LDCE);
-        const f32x4 xw = mm_tile_fa<E, C>(zero4(), &sm.Tt[rt * 16][0], S::LDCF, &sm.r.x.dWkt[ct * 16][0], S::LDCE);
+        auto ta = [&](int r, int k, float* o) { ld_row<float, KPL>(&sm.Tt[rt * 16 + r][k], o); };
+        const f32x4 xu = mm_gen<E, C, true, true>(
+            zero4(), ta, [&](int c, int k, float* o) { ld_row<float, KPL>(dWt + (ct * 16 + c) * C + k, o); });
+        const f32x4 xw = mm_gen<E, C, true, true>(
+            zero4(), ta, [&](int c, int k, float* o) { ld_row<float, KPL>(dWkt + (ct * 16 + c) * C + k, o); });
         f32x4 dvv;
         float pu[4], pw[4];
 #pragma unroll
@@ -341,11 +407,10 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
         }
       }
     }
-    __syncthreads();
-    // M1 = dT T^T  (stored transposed)
+    // M1 = dT T^T (fp32 MFMA), stored transposed
     for (int t = w; t < NT * NT; t += kChunkWaves) {
       const int rt = t / NT, ct = t % NT;
-      const f32x4 m = mm_tile<float, C>(zero4(), &sm.dT[rt * 16][0], S::LDCF, &sm.Tm[ct * 16][0], S::LDCF);
+      const f32x4 m = mm_tile<float, C>(zero4(), dTg + rt * 16 * C, C, &sm.Tm[ct * 16][0], S::LDCF);
 #pragma unroll
       for (int e = 0; e < 4; ++e) sm.r.M1t[ct * 16 + acc_col()][rt * 16 + acc_row(e)] = m[e];
     }
@@ -362,15 +427,15 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
     }
     __syncthreads();
     // C x C pass: A~, dS, and the dgamma / dbeta terms of A and P
-    const E* Wg = (const E*)a.W + slot * C * D;
-    const E* Pg = (const E*)a.P + slot * C * C;
     for (int t = w; t < NT * NT; t += kChunkWaves) {
       const int rt = t / NT, ct = t % NT;
       f32x4 skk = zero4(), dp = zero4();
       if (rt * 16 < len && ct * 16 < len) {
         skk = mm_tile_rows<E, D>(zero4(), kg + (int64_t)rt * 16 * a.sqk, a.sqk, len - rt * 16,
                                  kg + (int64_t)ct * 16 * a.sqk, a.sqk, len - ct * 16);
-        dp = mm_tile_rows<E, D>(zero4(), dog + (int64_t)rt * 16 * ldo, ldo, len - rt * 16, Wg + ct * 16 * D, D, 16);
+        dp = mm_gen<E, D, false, true>(zero4(), do_rows(rt * 16), [&](int c, int k, float* o) {
+          ld_row<float, KPL>(Wg + (ct * 16 + c) * D + k, o);
+        });
       }
       float rb[4], ra[4], rp[4], ca = 0.f, cp = 0.f;
 #pragma unroll
@@ -381,17 +446,14 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
         const float At = dA * sm.beta[r] * dd;
         const float AdA = At * skk[e];
         const float dP = (s <= r && r < len) ? a.scale * dp[e] : 0.f;
-        const float PdP = dP * to_f<E>(Pg[r * C + s]);
-        const float dS = dP * dd;
+        const float PdP = dP * Pg[r * C + s];
         rb[e] = dA * dd * skk[e];
         ra[e] = AdA;
         rp[e] = PdP;
         ca += AdA;
         cp += PdP;
-        sm.r.s.dS[r][s] = from_f<E>(dS);
-        sm.r.s.dSA[s][r] = from_f<E>(dS);
-        sm.r.s.dSA[r][C + s] = from_f<E>(At);
-        sm.r.s.Att[s][r] = from_f<E>(At);
+        sm.r.s.dS[r][s] = dP * dd;
+        sm.r.s.At[r][s] = At;
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -418,9 +480,7 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();
-    // dQ += Gam dO' Hc^T + dS K;   dK += e W dHn^T + [dS^T | A~][Q; K] + A~^T K
-    const E* Hc = (const E*)a.Hc + slot * D * D;
-    const E* dHn = (const E*)a.dHn + slot * D * D;
+    // dQ += Gam dO' Hc^T + dS K;   dK += e W dHn^T + dS^T Q + (A~ + A~^T) K
 #pragma unroll
     for (int i = 0; i < NQW; ++i) {
       const int t = w + kChunkWaves * i;
@@ -428,12 +488,32 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
         const int rt = t / ND, ct = t % ND;
         f32x4 qs = zero4(), kh = zero4();
         if (rt * 16 < len) {
-          qs = mm_tile_rows<E, D>(zero4(), dog + (int64_t)rt * 16 * ldo, ldo, len - rt * 16, Hc + ct * 16 * D, D, 16);
-          kh = mm_tile<E, D>(zero4(), Wg + rt * 16 * D, D, dHn + ct * 16 * D, D);
+          qs = mm_gen<E, D, false, true>(zero4(), do_rows(rt * 16), [&](int c, int k, float* o) {
+            ld_row<float, KPL>(Hc + (ct * 16 + c) * D + k, o);
+          });
+          kh = mm_gen<E, D, true, true>(
+              zero4(), [&](int r, int k, float* o) { ld_row<float, KPL>(Wg + (rt * 16 + r) * D + k, o); },
+              [&](int c, int k, float* o) { ld_row<float, KPL>(dHn + (ct * 16 + c) * D + k, o); });
         }
-        f32x4 sq = mm_tile<E, C>(zero4(), &sm.r.s.dS[rt * 16][0], S::LDCE, &sm.QKt[ct * 16][C], S::LD2C);
-        f32x4 sk = mm_tile<E, 2 * C>(zero4(), &sm.r.s.dSA[rt * 16][0], S::LD2C, &sm.QKt[ct * 16][0], S::LD2C);
-        sk = mm_tile<E, C>(sk, &sm.r.s.Att[rt * 16][0], S::LDCE, &sm.QKt[ct * 16][C], S::LD2C);
+        auto kt = [&](int c, int k, float* o) { ld_row<E, KPL>(&sm.QKt[ct * 16 + c][C + k], o); };
+        auto qt = [&](int c, int k, float* o) { ld_row<E, KPL>(&sm.QKt[ct * 16 + c][k], o); };
+        const f32x4 sq = mm_gen<E, C, true, false>(
+            zero4(), [&](int r, int k, float* o) { ld_row<float, KPL>(&sm.r.s.dS[rt * 16 + r][k], o); }, kt);
+        f32x4 sk = mm_gen<E, C, true, false>(
+            zero4(),
+            [&](int r, int k, float* o) {
+#pragma unroll
+              for (int u = 0; u < KPL; ++u) o[u] = sm.r.s.dS[k + u][rt * 16 + r];
+            },
+            qt);
+        sk = mm_gen<E, C, true, false>(
+            sk,
+            [&](int r, int k, float* o) {
+              ld_row<float, KPL>(&sm.r.s.At[rt * 16 + r][k], o);
+#pragma unroll
+              for (int u = 0; u < KPL; ++u) o[u] += sm.r.s.At[k + u][rt * 16 + r];
+            },
+            kt);
         float pq[4], pk[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -522,7 +602,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsPlan {
   size_t table, seq0, Wk, U, P, Kt, gam, end_fwd;
-  size_t Hc, W, dHn, dW, dT, dWk, hdot, end_bwd;
+  size_t Wkl, Ktl, Hc, W, dHn, dW, dWt, dT, dWkt, hdot, end_bwd;
 };
 
 static WsPlan plan(const gdn_shape* s) {
@@ -533,17 +613,20 @@ static WsPlan plan(const gdn_shape* s) {
   p.table = o; o = align256(o + M * 16);
   p.seq0 = o; o = align256(o + ((size_t)s->n_seqs + 1) * 4);
   p.Wk = o; o = align256(o + M * Hv * C * D * es);
-  p.U = o; o = align256(o + M * Hv * C * D * es);
-  p.P = o; o = align256(o + M * Hv * C * C * es);
+  p.U = o; o = align256(o + M * Hv * C * D * 4);
+  p.P = o; o = align256(o + M * Hv * C * C * 4);
   p.Kt = o; o = align256(o + M * Hv * D * C * es);
   p.gam = o; o = align256(o + M * Hv * C * 4);
   p.end_fwd = o;
-  p.Hc = o; o = align256(o + M * Hv * D * D * es);
-  p.W = o; o = align256(o + M * Hv * C * D * es);
-  p.dHn = o; o = align256(o + M * Hv * D * D * es);
-  p.dW = o; o = align256(o + M * Hv * C * D * es);
+  p.Wkl = o; o = align256(o + M * Hv * C * D * es);
+  p.Ktl = o; o = align256(o + M * Hv * D * C * es);
+  p.Hc = o; o = align256(o + M * Hv * D * D * 4);
+  p.W = o; o = align256(o + M * Hv * C * D * 4);
+  p.dHn = o; o = align256(o + M * Hv * D * D * 4);
+  p.dW = o; o = align256(o + M * Hv * C * D * 4);
+  p.dWt = o; o = align256(o + M * Hv * D * C * 4);
   p.dT = o; o = align256(o + M * Hv * C * C * 4);
-  p.dWk = o; o = align256(o + M * Hv * C * D * es);
+  p.dWkt = o; o = align256(o + M * Hv * D * C * 4);
   p.hdot = o; o = align256(o + M * Hv * 4);
   p.end_bwd = o;
   return p;
@@ -558,16 +641,19 @@ static void fill_ws(ChunkArgs& a, const gdn_shape* s, void* ws) {
   a.table = (const int32_t*)(b + p.table);
   a.seq_chunk0 = (const int32_t*)(b + p.seq0);
   a.Wk = b + p.Wk;
-  a.U = b + p.U;
-  a.P = b + p.P;
+  a.U = (float*)(b + p.U);
+  a.P = (float*)(b + p.P);
   a.Kt = b + p.Kt;
   a.gam = (float*)(b + p.gam);
-  a.Hc = b + p.Hc;
-  a.W = b + p.W;
-  a.dHn = b + p.dHn;
-  a.dW = b + p.dW;
+  a.Wkl = b + p.Wkl;
+  a.Ktl = b + p.Ktl;
+  a.Hc = (float*)(b + p.Hc);
+  a.W = (float*)(b + p.W);
+  a.dHn = (float*)(b + p.dHn);
+  a.dW = (float*)(b + p.dW);
+  a.dWt = (float*)(b + p.dWt);
   a.dT = (float*)(b + p.dT);
-  a.dWk = b + p.dWk;
+  a.dWkt = (float*)(b + p.dWkt);
   a.hdot = (float*)(b + p.hdot);
 }
 

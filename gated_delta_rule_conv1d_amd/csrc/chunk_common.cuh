@@ -38,22 +38,37 @@ struct ChunkArgs {
   const int32_t* table;       // [max_chunks][4]
   const int32_t* seq_chunk0;  // [N+1]
   void* Wk;                   // [slot][C][D]
-  void* U;                    // [slot][C][D]
-  void* P;                    // [slot][C][C]
+  float* U;                   // [slot][C][D]
+  float* P;                   // [slot][C][C]
   void* Kt;                   // [slot][D][C]
+  void* Wkl;                  // [slot][C][D]  lo part of Wk (backward only)
+  void* Ktl;                  // [slot][D][C]  lo part of Kt (backward only)
   float* gam;                 // [slot][C]
-  void* Hc;                   // [slot][D][D]  state entering the chunk
-  void* W;                    // [slot][C][D]  W = U - Wk Hc
-  void* dHn;                  // [slot][D][D]  gradient w.r.t. the state leaving the chunk
-  void* dW;                   // [slot][C][D]
+  float* Hc;                  // [slot][D][D]  state entering the chunk
+  float* W;                   // [slot][C][D]  W = U - Wk Hc
+  float* dHn;                 // [slot][D][D]  gradient w.r.t. the state leaving the chunk
+  float* dW;                  // [slot][C][D]
+  float* dWt;                 // [slot][D][C]  dW transposed
   float* dT;                  // [slot][C][C]
-  void* dWk;                  // [slot][C][D]
+  float* dWkt;                // [slot][D][C]  dWk transposed
   float* hdot;                // [slot]        <Hc, dHn>
 };
 
 template <typename E> struct Pad {
   static constexpr int E16 = 16 / (int)sizeof(E);  // elements per 16 bytes
 };
+
+// bf16 operands carry a second "lo" part (x - bf16(x)) so that products that
+// decide the output keep ~16 significant bits; float operands need none.
+template <typename E> struct Split { static constexpr bool on = false; };
+template <> struct Split<bf16> { static constexpr bool on = true; };
+
+template <typename E>
+__device__ __forceinline__ void split_store(E* hi, E* lo, float x) {
+  const E h = from_f<E>(x);
+  *hi = h;
+  if constexpr (Split<E>::on) *lo = from_f<E>(x - to_f<E>(h));
+}
 
 // Element load/store of one accumulator tile straight to/from global memory.
 template <typename E>
@@ -63,6 +78,12 @@ __device__ __forceinline__ void store_tile(E* base, int64_t ld, int r0, int c0, 
     const int r = r0 + acc_row(i);
     if (r < rows_valid) base[(int64_t)r * ld + c0 + acc_col()] = from_f<E>(v[i]);
   }
+}
+
+// one accumulator tile stored transposed: dst[(c0 + col) * ld + r0 + row]
+// (each lane writes 4 consecutive rows = one 16-byte vector for float)
+__device__ __forceinline__ void store_tile_t(float* dst, int64_t ld, int r0, int c0, f32x4 v) {
+  *reinterpret_cast<float4*>(dst + (int64_t)(c0 + acc_col()) * ld + r0 + acc_row(0)) = make_float4(v[0], v[1], v[2], v[3]);
 }
 
 // copy a [R][Ccols] row-major E tile between global (dense, ld = Ccols) and LDS
@@ -129,10 +150,13 @@ struct PrepSmem {
   float Am[C][LDCF];
   float Tm[C][LDCF];
   float Tt[C][LDCF];
-  E TB[C][LDCE];
+  E TB[C][LDCE];   // hi part of T diag(beta) / T diag(beta Gam)
+  union {
+    E TBl[Split<E>::on ? C : 1][LDCE];  // lo part
+    float Xs[kChunkWaves][16][20];      // solve scratch
+  };
   float gam[C];
   float beta[C];
-  float Xs[kChunkWaves][16][20];
 };
 
 // (I + A)^-1 for strictly lower A [C][C] (fp32 in LDS) into Tm and Tt = Tm^T.
@@ -193,12 +217,16 @@ template <typename E, int D, int C, int DVT, bool OUT>
 struct StateSmem {
   static constexpr int LDQ = D + Pad<E>::E16;
   static constexpr int LDCE = C + Pad<E>::E16;
+  static constexpr int LO = Split<E>::on ? 1 : 0;
   E Wk[C][LDQ];
   E Q[OUT ? C : 1][LDQ];
   E Kt[D][LDCE];
   E P[OUT ? C : 1][LDCE];
+  E Pl[OUT && LO ? C : 1][LDCE];
   E Ht[DVT][LDQ];
+  E Htl[LO ? DVT : 1][LDQ];
   E Wt[DVT][LDCE];
+  E Wtl[LO ? DVT : 1][LDCE];
   float gam[C];
 };
 

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(1024) void chunk_index_kernel(const int32_t* __rest
 // substitution, off-diagonal blocks by block substitution on fp32 MFMA),
 // U and Wk on MFMA.
 // ---------------------------------------------------------------------------
-template <typename E, int D, int C>
+template <typename E, int D, int C, bool LO_OUT>
 __global__ __launch_bounds__(kChunkThreads) void prep_kernel(ChunkArgs a) {
   using S = PrepSmem<E, D, C>;
   __shared__ S sm;
@@ -124,60 +124,69 @@ __global__ __launch_bounds__(kChunkThreads) void prep_kernel(ChunkArgs a) {
     rows2s_t<E, C, D>(&sm.Vt[0][0], S::LDCE, vg, a.sv, len, nullptr, 1.f);
     __syncthreads();
 
-    // P = lower_incl(D * Q K^T) (staged in TB), A = strict_lower(beta_r D * K K^T)
-    for (int t = w; t < NT * NT; t += kChunkWaves) {
-      const int rt = t / NT, ct = t % NT;
-      const f32x4 acc = mm_tile<E, D>(zero4(), &sm.Qs[rt * 16][0], S::LDQ, &sm.Ks[ct * 16][0], S::LDQ);
+    // P = lower_incl(D * Q K^T) (fp32 to workspace), A = strict_lower(beta_r D * K K^T)
+    {
+      float* Pg = a.P + slot * C * C;
+      for (int t = w; t < NT * NT; t += kChunkWaves) {
+        const int rt = t / NT, ct = t % NT;
+        const f32x4 acc = mm_tile<E, D>(zero4(), &sm.Qs[rt * 16][0], S::LDQ, &sm.Ks[ct * 16][0], S::LDQ);
+        f32x4 pv;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = rt * 16 + acc_row(e), s = ct * 16 + acc_col();
-        const float dd = (s <= r) ? __expf(sm.gam[r] - sm.gam[s]) : 0.f;
-        sm.TB[r][s] = from_f<E>((r < len) ? dd * acc[e] : 0.f);
-        sm.Am[r][s] = (s < r) ? sm.beta[r] * dd * sm.Sk[r][s] : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          const int r = rt * 16 + acc_row(e), s = ct * 16 + acc_col();
+          const float dd = (s <= r) ? __expf(sm.gam[r] - sm.gam[s]) : 0.f;
+          pv[e] = (r < len) ? dd * acc[e] : 0.f;
+          sm.Am[r][s] = (s < r) ? sm.beta[r] * dd * sm.Sk[r][s] : 0.f;
+        }
+        store_tile<float>(Pg, C, rt * 16, ct * 16, pv, C);
       }
     }
     __syncthreads();
-    {
-      E* Pg = (E*)a.P + slot * C * C;
-      for (int e = tid; e < C * (C / V); e += kChunkThreads) {
-        const int r = e / (C / V), c = (e % (C / V)) * V;
-        *reinterpret_cast<uint4*>(Pg + r * C + c) = *reinterpret_cast<const uint4*>(&sm.TB[r][c]);
-      }
-    }
     unit_lower_inverse<C, S::LDCF>(sm.Am, sm.Tm, sm.Tt, sm.Xs);  // starts and ends with a barrier
 
-    // U = (T diag(beta)) V
+    // U = (T diag(beta)) V, the left factor split into hi + lo bf16 parts; fp32 result
     for (int e = tid; e < C * C; e += kChunkThreads) {
       const int r = e / C, s = e % C;
-      sm.TB[r][s] = from_f<E>(sm.Tm[r][s] * sm.beta[s]);
+      split_store<E>(&sm.TB[r][s], &sm.TBl[0][0] + r * S::LDCE + s, sm.Tm[r][s] * sm.beta[s]);
     }
     __syncthreads();
     {
-      E* Ug = (E*)a.U + slot * C * D;
+      float* Ug = a.U + slot * C * D;
       for (int t = w; t < NT * ND; t += kChunkWaves) {
         const int rt = t / ND, ct = t % ND;
-        const f32x4 acc = mm_tile<E, C>(zero4(), &sm.TB[rt * 16][0], S::LDCE, &sm.Vt[ct * 16][0], S::LDCE);
-        store_tile<E>(Ug, D, rt * 16, ct * 16, acc, C);
+        f32x4 acc = mm_tile<E, C>(zero4(), &sm.TB[rt * 16][0], S::LDCE, &sm.Vt[ct * 16][0], S::LDCE);
+        if constexpr (Split<E>::on)
+          acc = mm_tile<E, C>(acc, &sm.TBl[rt * 16][0], S::LDCE, &sm.Vt[ct * 16][0], S::LDCE);
+        store_tile<float>(Ug, D, rt * 16, ct * 16, acc, C);
       }
     }
     __syncthreads();
     // Wk = (T diag(beta Gam)) K
     for (int e = tid; e < C * C; e += kChunkThreads) {
       const int r = e / C, s = e % C;
-      sm.TB[r][s] = from_f<E>(sm.Tm[r][s] * sm.beta[s] * __expf(sm.gam[s]));
+      split_store<E>(&sm.TB[r][s], &sm.TBl[0][0] + r * S::LDCE + s, sm.Tm[r][s] * sm.beta[s] * __expf(sm.gam[s]));
     }
     __syncthreads();
     {
       E* Wg = (E*)a.Wk + slot * C * D;
       for (int t = w; t < NT * ND; t += kChunkWaves) {
         const int rt = t / ND, ct = t % ND;
-        const f32x4 acc = mm_tile<E, C>(zero4(), &sm.TB[rt * 16][0], S::LDCE, &sm.Kt[ct * 16][0], S::LDCE);
+        f32x4 acc = mm_tile<E, C>(zero4(), &sm.TB[rt * 16][0], S::LDCE, &sm.Kt[ct * 16][0], S::LDCE);
+        if constexpr (Split<E>::on)
+          acc = mm_tile<E, C>(acc, &sm.TBl[rt * 16][0], S::LDCE, &sm.Kt[ct * 16][0], S::LDCE);
         store_tile<E>(Wg, D, rt * 16, ct * 16, acc, C);
+        if constexpr (LO_OUT && Split<E>::on) {
+          f32x4 lo;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) lo[e] = acc[e] - to_f<E>(from_f<E>(acc[e]));
+          store_tile<E>((E*)a.Wkl + slot * C * D, D, rt * 16, ct * 16, lo, C);
+        }
       }
     }
     // Kt_e[d][s] = e^{gamma_last - gamma_s} k_s[d]  (s < len), 0 past len
     {
       E* Kg = (E*)a.Kt + slot * D * C;
+      E* Klg = (E*)a.Ktl + slot * D * C;
       const float glast = sm.gam[len - 1];
       for (int e = tid; e < D * (C / V); e += kChunkThreads) {
         const int d = e / (C / V), s0 = (e % (C / V)) * V;
@@ -188,6 +197,11 @@ __global__ __launch_bounds__(kChunkThreads) void prep_kernel(ChunkArgs a) {
           val[i] = (s < len) ? to_f<E>(sm.Kt[d][s]) * __expf(glast - sm.gam[s]) : 0.f;
         }
         Vec<E>::store(Kg + d * C + s0, val);
+        if constexpr (LO_OUT && Split<E>::on) {
+#pragma unroll
+          for (int i = 0; i < V; ++i) val[i] -= to_f<E>(from_f<E>(val[i]));
+          Vec<E>::store(Klg + d * C + s0, val);
+        }
       }
     }
     __syncthreads();
@@ -208,6 +222,7 @@ template <typename E, int D, int C, int DVT, bool OUT>
 __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
   using S = StateSmem<E, D, C, DVT, OUT>;
   __shared__ S sm;
+  constexpr bool LO = Split<E>::on;
   constexpr int NVT = D / DVT;
   constexpr int NCT = DVT / 16;                 // column tiles
   constexpr int NHT = (D / 16) * NCT;           // state tiles
@@ -232,6 +247,7 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
       for (int e = 0; e < 4; ++e) Hr[i][e] = src[(rt * 16 + acc_row(e)) * D + col0 + ct * 16 + acc_col()];
     }
   }
+  // H^T as the B operand of the next chunk's products, hi + lo parts
   auto write_Ht = [&]() {
 #pragma unroll
     for (int i = 0; i < NHW; ++i) {
@@ -239,7 +255,10 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
       if (t < NHT) {
         const int rt = t / NCT, ct = t % NCT;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm.Ht[ct * 16 + acc_col()][rt * 16 + acc_row(e)] = from_f<E>(Hr[i][e]);
+        for (int e = 0; e < 4; ++e) {
+          const int c = ct * 16 + acc_col(), r = rt * 16 + acc_row(e);
+          split_store<E>(&sm.Ht[c][r], &sm.Htl[0][0] + c * S::LDQ + r, Hr[i][e]);
+        }
       }
     }
   };
@@ -252,22 +271,26 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
     const int64_t slot = (int64_t)ci * a.Hv + h;
     g2s<E, C, D>(&sm.Wk[0][0], S::LDQ, (const E*)a.Wk + slot * C * D);
     g2s<E, D, C>(&sm.Kt[0][0], S::LDCE, (const E*)a.Kt + slot * D * C);
-    if (OUT) {
+    if constexpr (OUT) {
       rows2s<E, C, D>(&sm.Q[0][0], S::LDQ, (const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D, a.sqk, len);
-      g2s<E, C, C>(&sm.P[0][0], S::LDCE, (const E*)a.P + slot * C * C);
+      const float* Pg = a.P + slot * C * C;
+      for (int e = threadIdx.x; e < C * C; e += kChunkThreads) {
+        const int r = e / C, c = e % C;
+        split_store<E>(&sm.P[r][c], &sm.Pl[0][0] + r * S::LDCE + c, Pg[e]);
+      }
     } else {
       // state entering this chunk, for the backward pass
-      E* Hg = (E*)a.Hc + slot * D * D;
+      float* Hg = a.Hc + slot * D * D;
 #pragma unroll
       for (int i = 0; i < NHW; ++i) {
         const int t = w + kChunkWaves * i;
-        if (t < NHT) store_tile<E>(Hg, D, (t / NCT) * 16, col0 + (t % NCT) * 16, Hr[i], D);
+        if (t < NHT) store_tile<float>(Hg, D, (t / NCT) * 16, col0 + (t % NCT) * 16, Hr[i], D);
       }
     }
     for (int e = threadIdx.x; e < C; e += kChunkThreads) sm.gam[e] = a.gam[slot * C + e];
     __syncthreads();
 
-    const E* Ug = (const E*)a.U + slot * C * D;
+    const float* Ug = a.U + slot * C * D;
     f32x4 Or[NWW];
 #pragma unroll
     for (int i = 0; i < NWW; ++i) {
@@ -275,17 +298,19 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
       Or[i] = zero4();
       if (t < NWT) {
         const int rt = t / NCT, ct = t % NCT;
-        const f32x4 x = mm_tile<E, D>(zero4(), &sm.Wk[rt * 16][0], S::LDQ, &sm.Ht[ct * 16][0], S::LDQ);
+        f32x4 x = mm_tile<E, D>(zero4(), &sm.Wk[rt * 16][0], S::LDQ, &sm.Ht[ct * 16][0], S::LDQ);
+        if constexpr (LO) x = mm_tile<E, D>(x, &sm.Wk[rt * 16][0], S::LDQ, &sm.Htl[ct * 16][0], S::LDQ);
         f32x4 wv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = rt * 16 + acc_row(e), c = ct * 16 + acc_col();
-          wv[e] = to_f<E>(Ug[r * D + col0 + c]) - x[e];
-          sm.Wt[c][r] = from_f<E>(wv[e]);
+          wv[e] = Ug[r * D + col0 + c] - x[e];
+          split_store<E>(&sm.Wt[c][r], &sm.Wtl[0][0] + c * S::LDCE + r, wv[e]);
         }
-        if (!OUT) store_tile<E>((E*)a.W + slot * C * D, D, rt * 16, col0 + ct * 16, wv, C);
-        if (OUT) {
-          const f32x4 xo = mm_tile<E, D>(zero4(), &sm.Q[rt * 16][0], S::LDQ, &sm.Ht[ct * 16][0], S::LDQ);
+        if constexpr (!OUT) store_tile<float>(a.W + slot * C * D, D, rt * 16, col0 + ct * 16, wv, C);
+        if constexpr (OUT) {
+          f32x4 xo = mm_tile<E, D>(zero4(), &sm.Q[rt * 16][0], S::LDQ, &sm.Ht[ct * 16][0], S::LDQ);
+          if constexpr (LO) xo = mm_tile<E, D>(xo, &sm.Q[rt * 16][0], S::LDQ, &sm.Htl[ct * 16][0], S::LDQ);
 #pragma unroll
           for (int e = 0; e < 4; ++e) Or[i][e] = __expf(sm.gam[rt * 16 + acc_row(e)]) * xo[e];
         }
@@ -299,19 +324,24 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
       const int t = w + kChunkWaves * i;
       if (t < NHT) {
         const int rt = t / NCT, ct = t % NCT;
-        const f32x4 y = mm_tile<E, C>(zero4(), &sm.Kt[rt * 16][0], S::LDCE, &sm.Wt[ct * 16][0], S::LDCE);
+        f32x4 y = mm_tile<E, C>(zero4(), &sm.Kt[rt * 16][0], S::LDCE, &sm.Wt[ct * 16][0], S::LDCE);
+        if constexpr (LO) y = mm_tile<E, C>(y, &sm.Kt[rt * 16][0], S::LDCE, &sm.Wtl[ct * 16][0], S::LDCE);
 #pragma unroll
         for (int e = 0; e < 4; ++e) Hr[i][e] = gl * Hr[i][e] + y[e];
       }
     }
-    if (OUT) {
+    if constexpr (OUT) {
       E* og = (E*)a.o + (int64_t)tok0 * a.Hv * D + (int64_t)h * D + col0;
 #pragma unroll
       for (int i = 0; i < NWW; ++i) {
         const int t = w + kChunkWaves * i;
         if (t < NWT) {
           const int rt = t / NCT, ct = t % NCT;
-          const f32x4 y = mm_tile<E, C>(zero4(), &sm.P[rt * 16][0], S::LDCE, &sm.Wt[ct * 16][0], S::LDCE);
+          f32x4 y = mm_tile<E, C>(zero4(), &sm.P[rt * 16][0], S::LDCE, &sm.Wt[ct * 16][0], S::LDCE);
+          if constexpr (LO) {
+            y = mm_tile<E, C>(y, &sm.P[rt * 16][0], S::LDCE, &sm.Wtl[ct * 16][0], S::LDCE);
+            y = mm_tile<E, C>(y, &sm.Pl[rt * 16][0], S::LDCE, &sm.Wt[ct * 16][0], S::LDCE);
+          }
           f32x4 ov;
 #pragma unroll
           for (int e = 0; e < 4; ++e) ov[e] = a.scale * (Or[i][e] + y[e]);
@@ -354,7 +384,8 @@ template <typename E, int D, int C>
 void launch_chunk_fwd_core(const ChunkArgs& a, hipStream_t st, bool out_mode) {
   constexpr int DVT = state_dvt<E, D>();
   dim3 gprep(a.max_chunks, a.Hk);
-  prep_kernel<E, D, C><<<gprep, kChunkThreads, 0, st>>>(a);
+  if (out_mode) prep_kernel<E, D, C, false><<<gprep, kChunkThreads, 0, st>>>(a);
+  else prep_kernel<E, D, C, true><<<gprep, kChunkThreads, 0, st>>>(a);
   dim3 gstate(a.N * a.Hv * (D / DVT));
   if (out_mode) state_fwd_kernel<E, D, C, DVT, true><<<gstate, kChunkThreads, 0, st>>>(a);
   else state_fwd_kernel<E, D, C, DVT, false><<<gstate, kChunkThreads, 0, st>>>(a);

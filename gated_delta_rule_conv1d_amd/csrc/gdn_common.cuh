@@ -106,10 +106,20 @@ __device__ __forceinline__ f32x4 mm_tile(f32x4 acc, const E* A, int lda, const E
   const int r = lane & 15, kq = (lane >> 4) * Mma<E>::KPL;
   const E* a = A + r * lda + kq;
   const E* b = B + r * ldb + kq;
+  if constexpr (K % Mma<E>::KS != 0) {
+    // K smaller than one instruction's k-extent (bf16, K = 16): lanes whose
+    // k-values lie past K feed zeros
+    static_assert(K < Mma<E>::KS, "K must be a multiple of the MFMA k-extent or smaller");
+    const bool kv = kq < K;
+    const typename Mma<E>::frag fa = kv ? Mma<E>::load(a) : Mma<E>::zero();
+    const typename Mma<E>::frag fb = kv ? Mma<E>::load(b) : Mma<E>::zero();
+    return Mma<E>::mma(fa, fb, acc);
+  } else {
 #pragma unroll
-  for (int k0 = 0; k0 < K; k0 += Mma<E>::KS)
-    acc = Mma<E>::mma(Mma<E>::load(a + k0), Mma<E>::load(b + k0), acc);
-  return acc;
+    for (int k0 = 0; k0 < K; k0 += Mma<E>::KS)
+      acc = Mma<E>::mma(Mma<E>::load(a + k0), Mma<E>::load(b + k0), acc);
+    return acc;
+  }
 }
 
 // Same contraction with float operands fed to the MFMA of type E: for E=bf16
@@ -120,13 +130,16 @@ __device__ __forceinline__ f32x4 mm_tile_f(f32x4 acc, const float* A, int lda, c
   const int r = lane & 15, kq = (lane >> 4) * Mma<E>::KPL;
   const float* a = A + r * lda + kq;
   const float* b = B + r * ldb + kq;
+  constexpr bool PART = K % Mma<E>::KS != 0;
+  static_assert(!PART || K < Mma<E>::KS, "K must be a multiple of the MFMA k-extent or smaller");
+  const bool kv = !PART || kq < K;
 #pragma unroll
   for (int k0 = 0; k0 < K; k0 += Mma<E>::KS) {
     float av[Mma<E>::KPL], bv[Mma<E>::KPL];
 #pragma unroll
     for (int i = 0; i < Mma<E>::KPL; ++i) {
-      av[i] = a[k0 + i];
-      bv[i] = b[k0 + i];
+      av[i] = kv ? a[k0 + i] : 0.f;
+      bv[i] = kv ? b[k0 + i] : 0.f;
     }
     acc = Mma<E>::mma(Mma<E>::from_floats(av), Mma<E>::from_floats(bv), acc);
   }
@@ -140,12 +153,15 @@ __device__ __forceinline__ f32x4 mm_tile_fa(f32x4 acc, const float* A, int lda, 
   const int r = lane & 15, kq = (lane >> 4) * Mma<E>::KPL;
   const float* a = A + r * lda + kq;
   const E* b = B + r * ldb + kq;
+  constexpr bool PART = K % Mma<E>::KS != 0;
+  static_assert(!PART || K < Mma<E>::KS, "K must be a multiple of the MFMA k-extent or smaller");
+  const bool kv = !PART || kq < K;
 #pragma unroll
   for (int k0 = 0; k0 < K; k0 += Mma<E>::KS) {
     float av[Mma<E>::KPL];
 #pragma unroll
-    for (int i = 0; i < Mma<E>::KPL; ++i) av[i] = a[k0 + i];
-    acc = Mma<E>::mma(Mma<E>::from_floats(av), Mma<E>::load(b + k0), acc);
+    for (int i = 0; i < Mma<E>::KPL; ++i) av[i] = kv ? a[k0 + i] : 0.f;
+    acc = Mma<E>::mma(Mma<E>::from_floats(av), kv ? Mma<E>::load(b + k0) : Mma<E>::zero(), acc);
   }
   return acc;
 }
@@ -158,7 +174,10 @@ __device__ __forceinline__ f32x4 mm_tile_rows(f32x4 acc, const E* A, int64_t lda
                                               int64_t ldb, int b_rows) {
   const int lane = lane_id();
   const int r = lane & 15, kq = (lane >> 4) * Mma<E>::KPL;
-  const bool va = r < a_rows, vb = r < b_rows;
+  constexpr bool PART = K % Mma<E>::KS != 0;
+  static_assert(!PART || K < Mma<E>::KS, "K must be a multiple of the MFMA k-extent or smaller");
+  const bool kv = !PART || kq < K;
+  const bool va = r < a_rows && kv, vb = r < b_rows && kv;
   const E* a = A + (va ? r : 0) * lda + kq;
   const E* b = B + (vb ? r : 0) * ldb + kq;
   const typename Mma<E>::frag zf = Mma<E>::zero();
@@ -169,6 +188,66 @@ __device__ __forceinline__ f32x4 mm_tile_rows(f32x4 acc, const E* A, int64_t lda
     acc = Mma<E>::mma(fa, fb, acc);
   }
   return acc;
+}
+
+// ---------------------------------------------------------------------------
+// Split-precision tiles.  Operands are produced by loader callables
+//   la(r, k, float* out)  -> out[0..KPL) = A[r][k .. k+KPL)   (r = 0..15 in tile)
+//   lb(c, k, float* out)  -> out[0..KPL) = B[k .. k+KPL)[c]
+// For bf16 MFMA an fp32 operand x is fed as hi = bf16(x) and lo = bf16(x - hi)
+// (SA / SB say which operands need it); the tile sums hi*hi, hi*lo and lo*hi,
+// so the products keep ~16 significant bits while running on bf16 MFMA.
+// Operands that are exactly bf16 (inputs) skip the lo part.  With float
+// operands this is one fp32 MFMA per k-step.
+// ---------------------------------------------------------------------------
+template <typename E, int K, bool SA, bool SB, typename LA, typename LB>
+__device__ __forceinline__ f32x4 mm_gen(f32x4 acc, LA&& la, LB&& lb) {
+  using M = Mma<E>;
+  const int lane = lane_id();
+  const int r = lane & 15, kq = (lane >> 4) * M::KPL;
+  constexpr bool PART = K % M::KS != 0;
+  static_assert(!PART || K < M::KS, "K must be a multiple of the MFMA k-extent or smaller");
+  const bool kv = !PART || kq < K;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += M::KS) {
+    float av[M::KPL], bv[M::KPL];
+    if (kv) {
+      la(r, k0 + kq, av);
+      lb(r, k0 + kq, bv);
+    } else {
+#pragma unroll
+      for (int i = 0; i < M::KPL; ++i) av[i] = bv[i] = 0.f;
+    }
+    if constexpr (M::KPL == 1) {
+      acc = M::mma(M::from_floats(av), M::from_floats(bv), acc);
+    } else {
+      float al[M::KPL], bl[M::KPL];
+#pragma unroll
+      for (int i = 0; i < M::KPL; ++i) {
+        al[i] = av[i] - bf2f(f2bf(av[i]));
+        bl[i] = bv[i] - bf2f(f2bf(bv[i]));
+      }
+      const typename M::frag ah = M::from_floats(av), bh = M::from_floats(bv);
+      acc = M::mma(ah, bh, acc);
+      if constexpr (SB) acc = M::mma(ah, M::from_floats(bl), acc);
+      if constexpr (SA) acc = M::mma(M::from_floats(al), bh, acc);
+    }
+  }
+  return acc;
+}
+
+// loaders
+template <typename T, int N>
+__device__ __forceinline__ void ld_row(const T* p, float* out) {  // N consecutive values
+  if constexpr (sizeof(T) * N == 16) {
+    Vec<T>::load(p, out);
+  } else if constexpr (sizeof(T) * N == 32) {
+    Vec<T>::load(p, out);
+    Vec<T>::load(p + 16 / sizeof(T), out + 16 / sizeof(T));
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) out[i] = to_f<T>(p[i]);
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -187,22 +187,37 @@ def split_qkv(y, Hk, Hv, dk, dv):
     return q, k, v
 
 
-def layer_fwd(cfg, inp, bits=64, scale=1.0):
+def _store(a, storage):
+    """Round a tensor that crosses a call boundary to its storage format.
+
+    With storage="bf16" the layer is computed as the four calls of the library
+    compose it: the conv output and the recurrence output (and, backward, the
+    gradients handed from one call to the next) are stored as bf16 between
+    calls, so the oracle rounds exactly those tensors, to nearest-even, and
+    computes everything else in full precision."""
+    if storage == "bf16":
+        import synth  # the seeded-input module; only its rounding helper is used
+        return synth.round_bf16(np.asarray(a, dtype=np.float32)).astype(np.float64)
+    return a
+
+
+def layer_fwd(cfg, inp, bits=64, scale=1.0, storage=None):
     """Forward of the layer on one workload's inputs (see synth.make_inputs).
 
     Returns dict: y_conv [T, Cch], o [T, Hv, dv], ht [N, Hv, dk, dv] and, when
     the workload has the norm, y [T, Hv, dv]."""
     Hk, Hv, dk, dv = cfg.h_qk, cfg.h_v, cfg.d_k, cfg.d_v
-    yc = conv1d(inp["x"], inp["w_conv"], inp["cu"], 2 * Hk * dk, dk, bits=bits)
+    yc = _store(conv1d(inp["x"], inp["w_conv"], inp["cu"], 2 * Hk * dk, dk, bits=bits), storage)
     q, k, v = split_qkv(yc, Hk, Hv, dk, dv)
     o, ht = recurrence(q, k, v, inp["g"], inp["beta"], inp["cu"], h0=inp.get("h0"), scale=scale, bits=bits)
+    o = _store(o, storage)
     out = dict(y_conv=yc, o=o, ht=ht)
     if cfg.norm:
         out["y"] = norm_gate(o, inp["z"], inp["w_norm"], bits=bits)
     return out
 
 
-def layer_bwd(cfg, inp, fwd, dy, bits=64, scale=1.0, dht=None):
+def layer_bwd(cfg, inp, fwd, dy, bits=64, scale=1.0, dht=None, storage=None):
     """Backward of the layer given the upstream gradient dy on its output
     (the norm output if present, else o).  Returns dict with dx, dw_conv, dg,
     dbeta, dh0, and dz, dw_norm when the norm is present; also the gradients
@@ -211,6 +226,7 @@ def layer_bwd(cfg, inp, fwd, dy, bits=64, scale=1.0, dht=None):
     res = {}
     if cfg.norm:
         d_o, dz, dwn = norm_gate_bwd(fwd["o"], inp["z"], inp["w_norm"], dy, bits=bits)
+        d_o = _store(d_o, storage)
         res.update(dz=dz, dw_norm=dwn)
     else:
         d_o = dy
@@ -220,7 +236,8 @@ def layer_bwd(cfg, inp, fwd, dy, bits=64, scale=1.0, dht=None):
                        scale=scale, bits=bits)
     res.update(dq=r["dq"], dk=r["dk"], dv=r["dv"], dg=r["dg"], dbeta=r["dbeta"], dh0=r["dh0"])
     T = q.shape[0]
-    dyc = np.concatenate([r["dq"].reshape(T, -1), r["dk"].reshape(T, -1), r["dv"].reshape(T, -1)], axis=1)
+    dyc = _store(np.concatenate([r["dq"].reshape(T, -1), r["dk"].reshape(T, -1), r["dv"].reshape(T, -1)], axis=1),
+                 storage)
     dx, dwc = conv1d_bwd(inp["x"], inp["w_conv"], inp["cu"], 2 * Hk * dk, dk, dyc, bits=bits)
     res.update(dx=dx, dw_conv=dwc)
     return res

@@ -40,9 +40,33 @@ def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     return err / rms if rms > 0 else err
 
 
+def mixed_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max_i |got_i - ref_i| / max(RMS(ref), |ref_i|)."""
+    ref = np.asarray(ref, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    den = np.maximum(rms, np.abs(ref))
+    den = np.where(den > 0, den, 1.0)
+    return float(np.max(np.abs(got - ref) / den))
+
+
 def assert_close(got, ref, tol, name):
+    """fp32 storage (tol 1e-4): max|diff| <= tol * RMS(ref).
+    bf16 storage (tol 2e-2): |diff_i| <= tol * max(RMS(ref), |ref_i|) for every
+    element -- the same bound wherever |ref_i| <= RMS, and 2% relative error on
+    the heavy tail, where the bf16 representation error alone (up to 2^-8 of the
+    value) already exceeds 2e-2 * RMS once |ref_i| > 5 RMS."""
+    got = np.asarray(got)
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     e = rel_err(got, ref)
+    if tol >= TOL["bf16"]:
+        m = mixed_err(got, ref)
+        print(f"  {name}: max|d|/rms={e:.3e} mixed={m:.3e}", flush=True)
+        assert m <= tol, f"{name}: max|d|/max(rms,|ref|) = {m:.3e} > {tol:.0e} (max|d|/rms = {e:.3e})"
+        return m
+    print(f"  {name}: max|d|/rms={e:.3e}", flush=True)
     assert e <= tol, f"{name}: max|diff|/rms = {e:.3e} > {tol:.0e}"
     return e
 

@@ -88,7 +88,8 @@ CHUNK_CASES = [
     ("f32", 16, 16, 2, 2, (64,)),
     ("f32", 16, 16, 1, 2, (40, 1, 23)),
     ("f32", 32, 32, 2, 4, (70, 1, 33, 64, 5)),
-    ("f32", 64, 64, 1, 2, (130, 7)),
+    ("f32", 64, 32, 1, 2, (130, 7)),
+    ("bf16", 16, 16, 2, 2, (40, 9)),
     ("bf16", 128, 64, 2, 4, (200, 1, 64, 63, 65)),
     ("bf16", 128, 32, 1, 2, (100, 33)),
     ("bf16", 64, 16, 2, 2, (50, 17)),
@@ -184,8 +185,8 @@ def test_layer_small_bf16_full():
     _print_case("layer_small_bf16", lengths=cfg.lengths)
     inp = synth.make_inputs(cfg)
     fwd, bwd = _layer_gpu(cfg, inp)
-    ref = oracle.layer_fwd(cfg, inp)
-    rb = oracle.layer_bwd(cfg, inp, ref, inp["dy"])
+    ref = oracle.layer_fwd(cfg, inp, storage="bf16")
+    rb = oracle.layer_bwd(cfg, inp, ref, inp["dy"], storage="bf16")
     tol = TOL["bf16"]
     assert_close(host(fwd["y"]), ref["y"], tol, "y")
     assert_close(host(fwd["ht"]), ref["ht"], tol, "ht")
