@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark the GatedDeltaNet layer on one MI355X.
+
+One step = the whole layer path over one packed row: conv1d+SiLU+L2, the
+chunked gated delta rule, RMSNormGated, and (for the training workload) the
+backward of all three.  Default workload: the training step, 8 sequences x
+8192 tokens packed in one row, 16 q/k heads, 32 v heads, d = 128, bf16.
+
+Prints ONE JSON line with the throughput (tokens/s), the roofline of the
+dominant kernel (per-kernel durations from HIP events on the library's stream,
+taken in a second pass over the same number of steps), and the CPU oracle timed
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+WORKLOADS = {
+    "train": "training step: fwd+bwd, 8 x 8192 packed varlen row, 16 qk / 32 v heads, d=128, bf16",
+    "dense": "forward: 4 x 2048 dense batch as one packed row, 16 qk / 32 v heads, d=128, bf16",
+    "varlen": "forward: 20 log-uniform lengths packed into 32768 tokens, h0 in / ht out, d=128, bf16",
+    "long": "forward: one 65536-token sequence, 16 qk / 32 v heads, d=128, bf16",
+    "tiny": "forward: 64 tokens, 2 heads, d=16, chunk 16, fp32",
+}
+
+
+def csrc_hash() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(HERE, "gated_delta_rule_conv1d_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_bytes(cfg, n_chunks: int, has_h0: bool) -> dict:
+    """Algorithmic bytes per launch of each kernel: every input it must read
+    once and every output it must write once (workspace tensors included, at
+    the precision they are stored in)."""
+    T, N, Hk, Hv, D, C = cfg.T, cfg.N, cfg.h_qk, cfg.h_v, cfg.d_k, cfg.chunk
+    es = 2 if cfg.dtype == "bf16" else 4
+    Cch = 2 * Hk * D + Hv * D
+    W = cfg.width
+    S = n_chunks * Hv          # (chunk, v-head) slots
+    qk = 2 * T * Hk * D * es
+    v = T * Hv * D * es
+    gb = 2 * T * Hv * 4
+    o = T * Hv * D * es
+    st = N * Hv * D * D * 4
+    wk, kt, u, p, gm = C * D * es, D * C * es, C * D * 4, C * C * 4, C * 4
+    hc, wf = D * D * 4, C * D * 4
+    b = {
+        "conv_fwd": 2 * T * Cch * es + Cch * W * es,
+        "conv_bwd": 3 * T * Cch * es + Cch * W * es,
+        "norm_fwd": 3 * o + D * es,
+        "norm_bwd": 5 * o + D * es,
+        "chunk_prep": qk + v + gb + S * (wk + u + p + kt + gm),
+        "chunk_prep_bwd": qk + v + gb + S * (2 * wk + u + p + 2 * kt + gm),
+        "chunk_state_fwd": qk // 2 + S * (wk + kt + u + p + gm) + o + (st if has_h0 else 0) + st,
+        "chunk_state_store": S * (wk + kt + u + gm + hc + wf) + (st if has_h0 else 0),
+        "chunk_state_bwd": qk // 2 + o + S * (p + 2 * kt + 2 * wk + gm + hc + 2 * wf),
+        "chunk_grad_a": qk // 2 + v + T * Hv * 4 + S * (2 * hc + wf + gm + wf + p + 4),
+        "chunk_grad_b": 2 * qk + 2 * v + o + 3 * T * Hv * 4 + S * (2 * wf + p + wf + 2 * hc + p + gm + 4),
+    }
+    return b
+
+
+def kernel_flops(cfg, n_chunks: int) -> dict:
+    """Algorithmic flops (the contractions of the method, triangular-aware)."""
+    Hv, Hk, D, C = cfg.h_v, cfg.h_qk, cfg.d_k, cfg.chunk
+    S = n_chunks * Hv
+    return {
+        "chunk_prep": n_chunks * Hk * 2 * (C * C // 2) * D * 2 + S * (2 * C * C * C / 3 + 2 * 2 * (C * C // 2) * D),
+        "chunk_state_fwd": S * (2 * 2 * C * D * D + 2 * D * C * D + 2 * (C * C // 2) * D),
+        "chunk_state_store": S * (2 * C * D * D + 2 * D * C * D),
+        "chunk_state_bwd": S * (2 * (C * C // 2) * D + 2 * C * D * D + 2 * 2 * D * C * D),
+        "chunk_grad_a": S * (2 * C * D * D + 2 * 2 * C * C * D),
+        "chunk_grad_b": S * (2 * 2 * C * C * C + 2 * 2 * (C * C // 2) * D + 3 * 2 * C * D * D + 5 * 2 * (C * C // 2) * D),
+    }
+
+
+def load_traffic(kernel: str, workload: str, n_launch_units: float):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
+    were taken on the current kernel sources; else None."""
+    path = os.path.join(HERE, "profiles", f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for ln in f:
+            if ln.startswith("#") or "=" not in ln:
+                continue
+            k, v = ln.split("=", 1)
+            rec[k.strip()] = v.strip()
+    if rec.get("csrc_hash") != csrc_hash():
+        return None
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(cfg, inp, kheads: int):
+    """The CPU oracle, as it stands, on all sequences of the workload restricted
+    to `kheads` q/k heads (with their v-heads); scaled to whole-layer tokens/s."""
+    import oracle
+    sub_cfg, sub, _, _ = oracle.subset(cfg, inp, list(range(cfg.N)), list(range(kheads)))
+    sub = {k: (v.astype("float64") if v.dtype.kind == "f" else v) for k, v in sub.items()}
+    t0 = time.perf_counter()
+    fwd = oracle.layer_fwd(sub_cfg, sub)
+    if cfg.bwd:
+        oracle.layer_bwd(sub_cfg, sub, fwd, sub["dy"])
+    dt = time.perf_counter() - t0
+    tokens_equiv = cfg.T * kheads / cfg.h_qk
+    return {"value": tokens_equiv / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"all {cfg.N} sequences ({cfg.T} tokens) x {kheads} of {cfg.h_qk} q/k heads "
+                      f"({kheads * cfg.h_v // cfg.h_qk} v-heads), fp64 {'fwd+bwd' if cfg.bwd else 'fwd'}; "
+                      f"{dt:.1f} s scaled to whole-layer tokens/s",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="train", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-heads", type=int, default=2, help="q/k heads in the CPU-oracle sample (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_conv1d_amd as gdn
+    import synth
+
+    cfg = synth.config(args.workload)
+    t_gen = time.perf_counter()
+    inp = synth.make_inputs(cfg)
+    t_gen = time.perf_counter() - t_gen
+    dev = torch.device("cuda:0")
+    bf = cfg.dtype == "bf16"
+
+    def to_dev(key):
+        if bf and key + "_bits" in inp:
+            return torch.from_numpy(inp[key + "_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(inp[key], dtype=np.float32)).to(dev)
+
+    x, w = to_dev("x"), to_dev("w_conv")
+    g, beta = to_dev("g"), to_dev("beta")
+    cu = torch.from_numpy(inp["cu"]).to(dev)
+    z = to_dev("z") if cfg.norm else None
+    wn = to_dev("w_norm") if cfg.norm else None
+    h0 = to_dev("h0") if cfg.h0 else None
+    dy = to_dev("dy") if cfg.bwd else None
+    shape = gdn.Shape(cfg.N, cfg.T, cfg.h_qk, cfg.h_v, cfg.d_k, cfg.d_v, cfg.chunk,
+                      gdn.BF16 if bf else gdn.F32, 1.0)
+    layer = gdn.GatedDeltaNetLayer(shape, cfg.width, dev, norm=cfg.norm)
+
+    def step():
+        f = layer.forward(x, w, g, beta, cu, z, wn, h0)
+        if cfg.bwd:
+            layer.backward(dy, x, w, g, beta, cu, f, z, wn, h0)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = cfg.T * args.steps / elapsed
+
+    # per-kernel durations: HIP events recorded by the library on its stream
+    gdn.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    rep = gdn.profile_report()
+    gdn.profile_enable(False)
+
+    import oracle
+    n_chunks = len(oracle.chunk_table(inp["cu"], cfg.chunk)[0])
+    kb = kernel_bytes(cfg, n_chunks, cfg.h0)
+    kf = kernel_flops(cfg, n_chunks)
+    kernels = {}
+    for name, (cnt, tot) in rep.items():
+        avg_ms = tot / cnt
+        kernels[name] = {"launches": cnt, "avg_us": round(avg_ms * 1e3, 2),
+                         "share": round(tot / sum(t for _, t in rep.values()), 4)}
+        if name in kb:
+            kernels[name]["GBps"] = round(kb[name] / (avg_ms * 1e-3) / 1e9, 1)
+        if name in kf:
+            kernels[name]["TFLOPs"] = round(kf[name] / (avg_ms * 1e-3) / 1e12, 2)
+    dom = max(rep, key=lambda k: rep[k][1])
+    cnt, tot = rep[dom]
+    avg_s = tot / cnt * 1e-3
+    t_hbm = kb.get(dom, 0) / (HBM_PEAK_GBS * 1e9)
+    t_mfma = kf.get(dom, 0) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    if t_mfma > t_hbm:
+        achieved = kf[dom] / avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
+    else:
+        achieved = kb.get(dom, 0) / avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof["kernel"] = dom
+    roof["avg_us"] = round(avg_s * 1e6, 2)
+    roof["algorithmic_bytes"] = kb.get(dom)
+    roof["traffic"] = load_traffic(dom, args.workload, 1)
+
+    # whole-step roofline of the path (fused algorithmic minimum)
+    step_bytes = (33024 + (57856 if cfg.bwd else 0)) * cfg.T if args.workload != "tiny" else None
+
+    cpu = None
+    if args.cpu_heads > 0:
+        cpu = cpu_baseline(cfg, inp, min(args.cpu_heads, cfg.h_qk))
+
+    out = {
+        "metric": "GatedDeltaNet fwd+bwd tokens/s, packed varlen H=32 d=128 bf16; % roofline"
+        if cfg.bwd else "GatedDeltaNet fwd tokens/s, packed varlen; % roofline",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}", "tokens": cfg.T,
+                   "n_seqs": cfg.N, "h_qk": cfg.h_qk, "h_v": cfg.h_v, "d": cfg.d_k, "chunk": cfg.chunk,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "step_fraction_of_fused_minimum": (round(step_bytes / (HBM_PEAK_GBS * 1e9) / (ms_per_step * 1e-3), 4)
+                                           if step_bytes else None),
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+        "input_generation_s": round(t_gen, 2),
+        "csrc_hash": csrc_hash(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

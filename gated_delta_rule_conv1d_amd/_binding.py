@@ -16,7 +16,8 @@ _STATUS = {0: "GDN_OK", -1: "GDN_ERR_INVALID_ARG", -2: "GDN_ERR_UNSUPPORTED", -3
 #: every symbol include/gdn.h declares
 SYMBOLS = ("gdn_status_string", "gdn_max_chunks", "gdn_chunk_index", "gdn_conv1d", "gdn_conv1d_bwd_workspace",
            "gdn_conv1d_bwd", "gdn_chunk_fwd_workspace", "gdn_chunk_fwd", "gdn_chunk_bwd_workspace",
-           "gdn_chunk_bwd", "gdn_norm_gate", "gdn_norm_gate_bwd_workspace", "gdn_norm_gate_bwd")
+           "gdn_chunk_bwd", "gdn_norm_gate", "gdn_norm_gate_bwd_workspace", "gdn_norm_gate_bwd",
+           "gdn_profile_enable", "gdn_profile_report")
 
 
 class GdnError(RuntimeError):
@@ -88,6 +89,8 @@ def load() -> ctypes.CDLL:
             "gdn_norm_gate": (I32, [S, P, P, P, F, P, P]),
             "gdn_norm_gate_bwd_workspace": (SZ, [S]),
             "gdn_norm_gate_bwd": (I32, [S, P, P, P, P, F, P, P, P, P, SZ, P]),
+            "gdn_profile_enable": (None, [ctypes.c_int]),
+            "gdn_profile_report": (SZ, [ctypes.c_char_p, SZ]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -292,3 +295,22 @@ def norm_gate_bwd(dy, o, z, w_norm, shape: Shape, eps: float = 1e-6, ws: Optiona
                                                          _ptr(w_norm), float(eps), _ptr(d_o), _ptr(dz), _ptr(dw),
                                                          _ptr(ws), ws.numel(), _stream(o.device)))
     return d_o, dz, dw
+
+
+# ----------------------------------------------------------------------------- diagnostics
+def profile_enable(on: bool) -> None:
+    """Bracket every later kernel launch with HIP events (True) or stop (False)."""
+    load().gdn_profile_enable(1 if on else 0)
+
+
+def profile_report() -> dict:
+    """{kernel name: (launches, total ms)} for the launches since profile_enable(True)."""
+    lib = load()
+    n = int(lib.gdn_profile_report(None, 0))
+    buf = ctypes.create_string_buffer(n + 1)
+    lib.gdn_profile_report(buf, n + 1)
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, cnt, ms = line.split()
+        out[name] = (int(cnt), float(ms))
+    return out

@@ -21,6 +21,7 @@
 //   dg_s = sum_{r >= s} dgamma_r   (within the chunk)
 // Every sum has a fixed order; no floating-point atomics.
 #include "chunk_common.cuh"
+#include "profile.h"
 
 namespace gdn {
 
@@ -669,8 +670,15 @@ template <typename E, int D, int C>
 static void launch_chunk_bwd_core(const ChunkArgs& a, hipStream_t st) {
   constexpr int DVT = D >= 32 ? 32 : D;
   launch_chunk_fwd_core<E, D, C>(a, st, false);  // Hc, W per chunk
-  state_bwd_kernel<E, D, C, DVT><<<dim3(a.N * a.Hv * (D / DVT)), kChunkThreads, 0, st>>>(a);
-  grad_a_kernel<E, D, C><<<dim3(a.max_chunks, a.Hv), kChunkThreads, 0, st>>>(a);
+  {
+    GDN_PROF("chunk_state_bwd", st);
+    state_bwd_kernel<E, D, C, DVT><<<dim3(a.N * a.Hv * (D / DVT)), kChunkThreads, 0, st>>>(a);
+  }
+  {
+    GDN_PROF("chunk_grad_a", st);
+    grad_a_kernel<E, D, C><<<dim3(a.max_chunks, a.Hv), kChunkThreads, 0, st>>>(a);
+  }
+  GDN_PROF("chunk_grad_b", st);
   grad_b_kernel<E, D, C><<<dim3(a.max_chunks, a.Hk), kChunkThreads, 0, st>>>(a);
 }
 

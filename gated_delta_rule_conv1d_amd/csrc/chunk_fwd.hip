@@ -16,6 +16,7 @@
 // differences gamma_r - gamma_s (r >= s) are ever exponentiated; the mask is
 // applied before the exponential.
 #include "chunk_common.cuh"
+#include "profile.h"
 
 namespace gdn {
 
@@ -374,6 +375,7 @@ int64_t max_chunks(const gdn_shape* s) {
 }
 
 void run_chunk_index(const gdn_shape* s, const int32_t* cu, int32_t* table, int32_t* seq_chunk0, hipStream_t st) {
+  GDN_PROF("chunk_index", st);
   chunk_index_kernel<<<1, 1024, 0, st>>>(cu, s->n_seqs, s->chunk, (int)max_chunks(s), table, seq_chunk0);
 }
 
@@ -384,9 +386,13 @@ template <typename E, int D, int C>
 void launch_chunk_fwd_core(const ChunkArgs& a, hipStream_t st, bool out_mode) {
   constexpr int DVT = state_dvt<E, D>();
   dim3 gprep(a.max_chunks, a.Hk);
-  if (out_mode) prep_kernel<E, D, C, false><<<gprep, kChunkThreads, 0, st>>>(a);
-  else prep_kernel<E, D, C, true><<<gprep, kChunkThreads, 0, st>>>(a);
+  {
+    GDN_PROF(out_mode ? "chunk_prep" : "chunk_prep_bwd", st);
+    if (out_mode) prep_kernel<E, D, C, false><<<gprep, kChunkThreads, 0, st>>>(a);
+    else prep_kernel<E, D, C, true><<<gprep, kChunkThreads, 0, st>>>(a);
+  }
   dim3 gstate(a.N * a.Hv * (D / DVT));
+  GDN_PROF(out_mode ? "chunk_state_fwd" : "chunk_state_store", st);
   if (out_mode) state_fwd_kernel<E, D, C, DVT, true><<<gstate, kChunkThreads, 0, st>>>(a);
   else state_fwd_kernel<E, D, C, DVT, false><<<gstate, kChunkThreads, 0, st>>>(a);
 }

@@ -15,6 +15,7 @@
 // reduce with xor shuffles.
 #include "gdn_common.cuh"
 #include "gdn_internal.h"
+#include "profile.h"
 
 namespace gdn {
 
@@ -308,6 +309,7 @@ static void launch_conv_fwd(const gdn_shape* s, const void* x, const void* w, co
   constexpr int V = Vec<E>::N;
   const int Cch = 2 * s->h_qk * s->d_k + s->h_v * s->d_v;
   dim3 grid(conv_grid_x(s->total_tokens), (Cch + kWave * V - 1) / (kWave * V));
+  GDN_PROF("conv_fwd", st);
   conv_fwd_kernel<E, D, W><<<grid, 256, 0, st>>>((const E*)x, (const E*)w, cu, s->n_seqs, s->total_tokens, Cch,
                                                  2 * s->h_qk * s->d_k, eps, (E*)y);
 }
@@ -319,9 +321,13 @@ static void launch_conv_bwd(const gdn_shape* s, const void* dy, const void* x, c
   const int Cch = 2 * s->h_qk * s->d_k + s->h_v * s->d_v;
   dim3 grid(conv_grid_x(s->total_tokens), (Cch + kWave * V - 1) / (kWave * V));
   float* part = (float*)ws;
-  conv_bwd_kernel<E, D, W><<<grid, 256, 0, st>>>((const E*)dy, (const E*)x, (const E*)w, cu, s->n_seqs,
-                                                 s->total_tokens, Cch, 2 * s->h_qk * s->d_k, eps, (E*)dx, part);
+  {
+    GDN_PROF("conv_bwd", st);
+    conv_bwd_kernel<E, D, W><<<grid, 256, 0, st>>>((const E*)dy, (const E*)x, (const E*)w, cu, s->n_seqs,
+                                                   s->total_tokens, Cch, 2 * s->h_qk * s->d_k, eps, (E*)dx, part);
+  }
   const int n = Cch * W;
+  GDN_PROF("conv_dw_sum", st);
   sum_parts_kernel<<<(n + 255) / 256, 256, 0, st>>>(part, (int)grid.x, n, dw);
 }
 

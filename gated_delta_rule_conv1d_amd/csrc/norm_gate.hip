@@ -11,6 +11,7 @@
 // a row group that reduces with xor shuffles.  Pure HBM streaming.
 #include "gdn_common.cuh"
 #include "gdn_internal.h"
+#include "profile.h"
 
 namespace gdn {
 
@@ -126,6 +127,7 @@ static void launch_norm_fwd(const gdn_shape* s, const void* o, const void* z, co
   constexpr int RPB = kNormThreads / (DV / Vec<E>::N);
   const long rows = (long)s->total_tokens * s->h_v;
   const long blocks = (rows + RPB - 1) / RPB;
+  GDN_PROF("norm_fwd", st);
   norm_fwd_kernel<E, DV><<<dim3((unsigned)blocks), kNormThreads, 0, st>>>((const E*)o, (const E*)z,
                                                                           (const E*)w, eps, rows, (E*)y);
 }
@@ -135,8 +137,12 @@ static void launch_norm_bwd(const gdn_shape* s, const void* dy, const void* o, c
                             float eps, void* d_o, void* dz, float* dw, void* ws, hipStream_t st) {
   const long rows = (long)s->total_tokens * s->h_v;
   float* part = (float*)ws;
-  norm_bwd_kernel<E, DV><<<kNormBwdBlocks, kNormThreads, 0, st>>>((const E*)dy, (const E*)o, (const E*)z,
-                                                                  (const E*)w, eps, rows, (E*)d_o, (E*)dz, part);
+  {
+    GDN_PROF("norm_bwd", st);
+    norm_bwd_kernel<E, DV><<<kNormBwdBlocks, kNormThreads, 0, st>>>((const E*)dy, (const E*)o, (const E*)z,
+                                                                    (const E*)w, eps, rows, (E*)d_o, (E*)dz, part);
+  }
+  GDN_PROF("norm_dw_sum", st);
   norm_sum_kernel<<<(DV + 255) / 256, 256, 0, st>>>(part, kNormBwdBlocks, DV, dw);
 }
 

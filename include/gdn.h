@@ -24,9 +24,10 @@
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers.  The caller allocates every
  *    buffer, including workspace (sized by the *_workspace queries).  The
- *    library allocates nothing, keeps no mutable global state, never
- *    synchronises and never reads device memory from the host.  All work is
- *    enqueued on `stream` (a hipStream_t; NULL means the default stream).
+ *    library allocates no device memory, never synchronises and never reads
+ *    device memory from the host; its only mutable global state is the opt-in
+ *    timing record of gdn_profile_enable.  All work is enqueued on `stream`
+ *    (a hipStream_t; NULL means the default stream).
  *  - Arguments are validated on the host before anything is enqueued; on any
  *    error nothing is launched.  Device-side contents that break a documented
  *    precondition (for example a cu_seqlens that is not non-decreasing or
@@ -174,6 +175,19 @@ size_t gdn_norm_gate_bwd_workspace(const gdn_shape* shape);
 gdn_status gdn_norm_gate_bwd(const gdn_shape* shape, const void* dy, const void* o, const void* z,
                              const void* w_norm, float eps, void* d_o, void* dz, float* dw_norm,
                              void* ws, size_t ws_bytes, gdn_stream stream);
+
+/* --------------------------------------------------------------------------
+ * Diagnostics: per-kernel timing with HIP events.  For benchmarks and
+ * profiling only (not part of the layer's computation).
+ * gdn_profile_enable(1) clears earlier records and brackets every later kernel
+ * launch of the library with hipEventRecord on its stream; (0) stops.
+ * gdn_profile_report writes "kernel_name launches total_ms" lines into buf
+ * (at most cap bytes including the terminating zero), waiting for the
+ * recorded events, and returns the full length.  Not thread-safe; the event
+ * objects are created once and reused.
+ * -------------------------------------------------------------------------- */
+void gdn_profile_enable(int on);
+size_t gdn_profile_report(char* buf, size_t cap);
 
 #ifdef __cplusplus
 }
