@@ -76,7 +76,7 @@ typedef struct gdn_shape {
   int32_t h_v;          /* Hv >= 1, Hv % Hk == 0 */
   int32_t d_k;          /* 16, 32, 64 or 128 */
   int32_t d_v;          /* must equal d_k */
-  int32_t chunk;        /* 16, 32 or 64 (chunk <= 64; GDN_F32 with d=128 needs chunk <= 32) */
+  int32_t chunk;        /* 16, 32 or 64 (GDN_F32 with d=128 needs chunk <= 32) */
   int32_t dtype;        /* GDN_F32 or GDN_BF16 */
   float scale;          /* query scale (o_t = scale * S_t q_t) */
 } gdn_shape;

@@ -1,0 +1,130 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/gdn.h declares, and rejects bad arguments on the host before anything
+is enqueued (only failing argument sets are passed here, so nothing launches)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_conv1d_amd as gdn
+from gated_delta_rule_conv1d_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced: calls below fail validation first
+FAKE_ODD = ctypes.c_void_p(0x10008)    # not 16-byte aligned
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "gdn.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = gdn.load()
+    names = header_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B.SYMBOLS)
+
+
+def shape(**kw):
+    d = dict(n_seqs=2, total_tokens=100, h_qk=2, h_v=4, d_k=32, d_v=32, chunk=16, dtype=gdn.BF16, scale=1.0)
+    d.update(kw)
+    return B._Shape(*[d[f] for f, _ in B._Shape._fields_])
+
+
+def test_status_strings():
+    lib = gdn.load()
+    for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, -4):
+        assert lib.gdn_status_string(code).startswith(b"GDN_")
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(n_seqs=0), INVALID), (dict(total_tokens=-1), INVALID), (dict(h_qk=0), INVALID),
+    (dict(h_v=3), INVALID), (dict(d_k=48, d_v=48), UNSUPPORTED), (dict(d_v=64), UNSUPPORTED),
+    (dict(dtype=7), UNSUPPORTED), (dict(chunk=8), UNSUPPORTED), (dict(chunk=128), UNSUPPORTED),
+    (dict(dtype=gdn.F32, d_k=128, d_v=128, chunk=64), UNSUPPORTED),
+])
+def test_chunk_fwd_rejects_shape(bad, code):
+    lib = gdn.load()
+    s = shape(**bad)
+    rc = lib.gdn_chunk_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, 64, 128, FAKE, FAKE, FAKE, None, FAKE, None,
+                           FAKE, 1 << 40, None)
+    assert rc == code
+    assert lib.gdn_chunk_fwd_workspace(ctypes.byref(s)) == 0
+
+
+def test_chunk_fwd_rejects_pointers_strides_workspace():
+    lib = gdn.load()
+    s = shape()
+    ws = lib.gdn_chunk_fwd_workspace(ctypes.byref(s))
+    assert ws > 0
+
+    def call(q=FAKE, k=FAKE, v=FAKE, sqk=64, sv=128, g=FAKE, b=FAKE, cu=FAKE, o=FAKE, w=FAKE, nb=ws):
+        return lib.gdn_chunk_fwd(ctypes.byref(s), q, k, v, sqk, sv, g, b, cu, None, o, None, w, nb, None)
+
+    assert call(q=None) == INVALID
+    assert call(v=None) == INVALID
+    assert call(g=None) == INVALID
+    assert call(cu=None) == INVALID
+    assert call(o=None) == INVALID
+    assert call(q=FAKE_ODD) == INVALID
+    assert call(sqk=63) == INVALID          # shorter than one token of q
+    assert call(sqk=68) == INVALID          # rows not 16-byte aligned (bf16)
+    assert call(sv=100) == INVALID
+    assert call(w=None) == WORKSPACE
+    assert call(nb=ws - 1) == WORKSPACE
+
+
+def test_chunk_bwd_rejects():
+    lib = gdn.load()
+    s = shape()
+    ws = lib.gdn_chunk_bwd_workspace(ctypes.byref(s))
+    assert ws > lib.gdn_chunk_fwd_workspace(ctypes.byref(s))
+
+    def call(d_o=FAKE, dq=FAKE, w=FAKE, nb=ws):
+        return lib.gdn_chunk_bwd(ctypes.byref(s), FAKE, FAKE, FAKE, 64, 128, FAKE, FAKE, FAKE, None, d_o, None,
+                                 dq, FAKE, FAKE, FAKE, FAKE, None, w, nb, None)
+
+    assert call(d_o=None) == INVALID
+    assert call(dq=None) == INVALID
+    assert call(dq=FAKE_ODD) == INVALID
+    assert call(nb=ws - 256) == WORKSPACE
+
+
+def test_conv_and_norm_reject():
+    lib = gdn.load()
+    s = shape()
+    assert lib.gdn_conv1d(ctypes.byref(s), FAKE, FAKE, 5, 1e-6, FAKE, ctypes.c_void_p(0x20000), None) == UNSUPPORTED
+    assert lib.gdn_conv1d(ctypes.byref(s), FAKE, FAKE, 1, 1e-6, FAKE, ctypes.c_void_p(0x20000), None) == UNSUPPORTED
+    assert lib.gdn_conv1d(ctypes.byref(s), FAKE, FAKE, 4, 1e-6, FAKE, FAKE, None) == INVALID   # y aliases x
+    assert lib.gdn_conv1d(ctypes.byref(s), FAKE, FAKE, 4, -1.0, FAKE, ctypes.c_void_p(0x20000), None) == INVALID
+    assert lib.gdn_conv1d(ctypes.byref(s), None, FAKE, 4, 1e-6, FAKE, ctypes.c_void_p(0x20000), None) == INVALID
+    nb = lib.gdn_conv1d_bwd_workspace(ctypes.byref(s), 4)
+    assert nb > 0 and lib.gdn_conv1d_bwd_workspace(ctypes.byref(s), 9) == 0
+    assert lib.gdn_conv1d_bwd(ctypes.byref(s), FAKE, FAKE, FAKE, 4, 1e-6, FAKE, ctypes.c_void_p(0x20000), FAKE,
+                              None, nb, None) == WORKSPACE
+    assert lib.gdn_norm_gate(ctypes.byref(s), FAKE, FAKE, FAKE, 1e-6, None, None) == INVALID
+    assert lib.gdn_norm_gate(ctypes.byref(s), FAKE, FAKE, FAKE_ODD, 1e-6, FAKE, None) == INVALID
+    nb = lib.gdn_norm_gate_bwd_workspace(ctypes.byref(s))
+    assert lib.gdn_norm_gate_bwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 1e-6, FAKE, FAKE, FAKE, FAKE, nb - 4,
+                                 None) == WORKSPACE
+    assert lib.gdn_chunk_index(ctypes.byref(shape(chunk=24)), FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert lib.gdn_chunk_index(ctypes.byref(s), None, FAKE, FAKE, None) == INVALID
+
+
+def test_workspace_sizes_grow_with_tokens_and_max_chunks_bound():
+    lib = gdn.load()
+    prev_f = prev_b = 0
+    for T in (0, 1, 64, 65, 1000, 65536):
+        s = shape(total_tokens=T, n_seqs=3, d_k=128, d_v=128, h_qk=16, h_v=32, chunk=64)
+        f = lib.gdn_chunk_fwd_workspace(ctypes.byref(s))
+        b = lib.gdn_chunk_bwd_workspace(ctypes.byref(s))
+        assert f >= prev_f and b >= prev_b and b > f
+        prev_f, prev_b = f, b
+        assert lib.gdn_max_chunks(ctypes.byref(s)) == -(-T // 64) + 3
