@@ -64,8 +64,8 @@ __global__ __launch_bounds__(kChunkThreads) void state_bwd_kernel(ChunkArgs a) {
   constexpr int NHT = (D / 16) * NCT;
   constexpr int NHW = (NHT + kChunkWaves - 1) / kChunkWaves;
   constexpr int NWT = (C / 16) * NCT;
-  const int bid = blockIdx.x;
-  const int vt = bid % NVT, h = (bid / NVT) % a.Hv, n = bid / (NVT * a.Hv);
+  int n, h, vt;
+  if (!state_block(blockIdx.x, a.N, a.Hk, a.G, NVT, n, h, vt)) return;
   const int j = h / a.G;
   const int w = wave_id();
   const int col0 = vt * DVT;
@@ -96,13 +96,56 @@ __global__ __launch_bounds__(kChunkThreads) void state_bwd_kernel(ChunkArgs a) {
       }
     }
   };
-  write_dHt();
+
+  // next chunk's tiles, staged in registers
+  TileRegs<float, C, C> pP;
+  TileRegs<E, D, C> pKt, pKtl;
+  TileRegs<E, C, D> pQ, pWk, pWkl;
+  TileRegs<E, C, DVT> pO;
+  TileRegs<float, 1, C> pG;
+  float qsc[TileRegs<E, C, D>::N];
+  int ptok = 0, plen = 0;
+  auto prefetch = [&](int ci) {
+    const int4 ent = chunk_entry(a.table, ci);
+    ptok = ent.y;
+    plen = ent.z;
+    const int64_t slot = (int64_t)ci * a.Hv + h;
+    pP.load(a.P + slot * C * C, C, C);
+    pKt.load((const E*)a.Kt + slot * D * C, C, D);
+    pWk.load((const E*)a.Wk + slot * C * D, D, C);
+    if constexpr (LO) {
+      pKtl.load((const E*)a.Ktl + slot * D * C, C, D);
+      pWkl.load((const E*)a.Wkl + slot * C * D, D, C);
+    }
+    pQ.load((const E*)a.q + (int64_t)ptok * a.sqk + (int64_t)j * D, a.sqk, plen);
+    pO.load((const E*)a.d_o + (int64_t)ptok * a.Hv * D + (int64_t)h * D + col0, (int64_t)a.Hv * D, plen);
+    pG.load(a.gam + slot * C, C, 1);
+#pragma unroll
+    for (int i = 0; i < TileRegs<E, C, D>::N; ++i) {  // raw gamma of each q row; exponentiated at commit
+      const int r = pQ.row_of(i);
+      qsc[i] = r < C ? a.gam[slot * C + r] : 0.f;
+    }
+  };
 
   const int c0 = a.seq_chunk0[n], c1 = a.seq_chunk0[n + 1];
+  if (c0 < c1) prefetch(c1 - 1);
+  write_dHt();
   for (int ci = c1 - 1; ci >= c0; --ci) {
-    const int4 ent = chunk_entry(a.table, ci);
-    const int tok0 = ent.y, len = ent.z;
+    const int len = plen;
     const int64_t slot = (int64_t)ci * a.Hv + h;
+    __syncthreads();  // the previous chunk is done with the LDS tiles
+    pP.template store_t<E>(&sm.Pt[0][0], S::LDCE, LO ? &sm.Ptl[0][0] : nullptr, S::LDCE);
+    pKt.template store_t<E>(&sm.Ktil[0][0], S::LDQ);
+    pWk.template store_t<E>(&sm.QW[0][C], S::LD2C, nullptr, 0, nullptr, -1.f);
+    if constexpr (LO) {
+      pKtl.template store_t<E>(&sm.Ktill[0][0], S::LDQ);
+      pWkl.template store_t<E>(&sm.Wklo[0][0], S::LDCE, nullptr, 0, nullptr, -1.f);
+    }
+#pragma unroll
+    for (int i = 0; i < TileRegs<E, C, D>::N; ++i) qsc[i] = __expf(qsc[i]);
+    pQ.template store_t<E>(&sm.QW[0][0], S::LD2C, LO ? &sm.Qlo[0][0] : nullptr, S::LDCE, qsc);
+    pO.template store_t<E>(&sm.OW[0][0], S::LD2C);
+    pG.store(&sm.gam[0], C);
     {  // gradient w.r.t. the state leaving this chunk
       float* dst = a.dHn + slot * D * D;
 #pragma unroll
@@ -111,34 +154,8 @@ __global__ __launch_bounds__(kChunkThreads) void state_bwd_kernel(ChunkArgs a) {
         if (t < NHT) store_tile<float>(dst, D, (t / NCT) * 16, col0 + (t % NCT) * 16, dH[i], D);
       }
     }
-    for (int e = threadIdx.x; e < C; e += kChunkThreads) {
-      const float gm = a.gam[slot * C + e];
-      sm.gam[e] = gm;
-      sm.Gm[e] = __expf(gm);
-    }
     __syncthreads();
-    {
-      const float* Pg = a.P + slot * C * C;
-      for (int e = threadIdx.x; e < C * C; e += kChunkThreads) {
-        const int r = e / C, c = e % C;  // P[r][c] -> Pt[c][r]
-        split_store<E>(&sm.Pt[c][r], &sm.Ptl[0][0] + c * S::LDCE + r, Pg[e]);
-      }
-      const E* qg = (const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D;
-      for (int e = threadIdx.x; e < C * D; e += kChunkThreads) {
-        const int r = e / D, d = e % D;  // (Gam_r q_r)^T
-        const float qv = r < len ? sm.Gm[r] * to_f<E>(qg[(int64_t)r * a.sqk + d]) : 0.f;
-        split_store<E>(&sm.QW[d][r], &sm.Qlo[0][0] + d * S::LDCE + r, qv);
-      }
-    }
-    rows2s_t<E, D, C>(&sm.Ktil[0][0], S::LDQ, (const E*)a.Kt + slot * D * C, C, D, nullptr, 1.f);
-    rows2s_t<E, C, D>(&sm.QW[0][C], S::LD2C, (const E*)a.Wk + slot * C * D, D, C, nullptr, -1.f);
-    if constexpr (LO) {
-      rows2s_t<E, D, C>(&sm.Ktill[0][0], S::LDQ, (const E*)a.Ktl + slot * D * C, C, D, nullptr, 1.f);
-      rows2s_t<E, C, D>(&sm.Wklo[0][0], S::LDCE, (const E*)a.Wkl + slot * C * D, D, C, nullptr, -1.f);
-    }
-    rows2s_t<E, C, DVT>(&sm.OW[0][0], S::LD2C, (const E*)a.d_o + (int64_t)tok0 * a.Hv * D + (int64_t)h * D + col0,
-                        (int64_t)a.Hv * D, len, nullptr, 1.f);
-    __syncthreads();
+    if (ci > c0) prefetch(ci - 1);  // in flight during this chunk's compute
 
     float* dWg = a.dW + slot * C * D;
     float* dWtg = a.dWt + slot * D * C;
@@ -163,7 +180,7 @@ __global__ __launch_bounds__(kChunkThreads) void state_bwd_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();
-    const float gl = sm.Gm[len - 1];
+    const float gl = __expf(sm.gam[len - 1]);
 #pragma unroll
     for (int i = 0; i < NHW; ++i) {
       const int t = w + kChunkWaves * i;
@@ -180,8 +197,7 @@ __global__ __launch_bounds__(kChunkThreads) void state_bwd_kernel(ChunkArgs a) {
         for (int e = 0; e < 4; ++e) dH[i][e] = gl * dH[i][e] + a.scale * y1[e] + y2[e];
       }
     }
-    __syncthreads();
-    write_dHt();
+    write_dHt();  // the dW pass (the only reader of dHt) is over for every wave
   }
   if (a.dh0) {
     float* dst = a.dh0 + ((int64_t)n * a.Hv + h) * D * D;
@@ -672,7 +688,7 @@ static void launch_chunk_bwd_core(const ChunkArgs& a, hipStream_t st) {
   launch_chunk_fwd_core<E, D, C>(a, st, false);  // Hc, W per chunk
   {
     GDN_PROF("chunk_state_bwd", st);
-    state_bwd_kernel<E, D, C, DVT><<<dim3(a.N * a.Hv * (D / DVT)), kChunkThreads, 0, st>>>(a);
+    state_bwd_kernel<E, D, C, DVT><<<dim3(state_grid(a.N, a.Hk, a.G, D / DVT)), kChunkThreads, 0, st>>>(a);
   }
   {
     GDN_PROF("chunk_grad_a", st);

@@ -217,6 +217,7 @@ template <typename E, int D, int C, int DVT, bool OUT>
 struct StateSmem {
   static constexpr int LDQ = D + Pad<E>::E16;
   static constexpr int LDCE = C + Pad<E>::E16;
+  static constexpr int LDU = DVT + 4;
   static constexpr int LO = Split<E>::on ? 1 : 0;
   E Wk[C][LDQ];
   E Q[OUT ? C : 1][LDQ];
@@ -227,7 +228,98 @@ struct StateSmem {
   E Htl[LO ? DVT : 1][LDQ];
   E Wt[DVT][LDCE];
   E Wtl[LO ? DVT : 1][LDCE];
+  float U[C][LDU];
   float gam[C];
 };
+
+// Register staging of one [R][COLS] tile of T read from global memory (row
+// stride ld elements, rows past rows_valid read as zero) by all threads of a
+// workgroup with 16-byte loads; store() writes it to LDS afterwards.  Used to
+// issue the next chunk's loads before the current chunk's compute.
+template <typename T, int R, int COLS>
+struct TileRegs {
+  static constexpr int V = 16 / (int)sizeof(T);
+  static constexpr int PER_ROW = COLS / V;
+  static constexpr int TOTAL = R * PER_ROW;
+  static constexpr int N = (TOTAL + kChunkThreads - 1) / kChunkThreads;
+  uint4 r[N];
+  __device__ __forceinline__ void load(const T* g, int64_t ld, int rows_valid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int e = threadIdx.x + i * kChunkThreads;
+      r[i] = make_uint4(0, 0, 0, 0);
+      if (e < TOTAL) {
+        const int row = e / PER_ROW, c = (e % PER_ROW) * V;
+        if (row < rows_valid) r[i] = *reinterpret_cast<const uint4*>(g + (int64_t)row * ld + c);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(T* s, int lds) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int e = threadIdx.x + i * kChunkThreads;
+      if (e < TOTAL) {
+        const int row = e / PER_ROW, c = (e % PER_ROW) * V;
+        *reinterpret_cast<uint4*>(s + row * lds + c) = r[i];
+      }
+    }
+  }
+  // tile written transposed: hi[c * lds + row] (optionally scaled per row by
+  // rs[i] for the i-th register slot, and split into hi / lo[c * lds_lo + row]
+  // when lo != null)
+  template <typename E>
+  __device__ __forceinline__ void store_t(E* hi, int lds, E* lo = nullptr, int lds_lo = 0, const float* rs = nullptr,
+                                          float mult = 1.f) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int e = threadIdx.x + i * kChunkThreads;
+      if (e < TOTAL) {
+        const int row = e / PER_ROW, c = (e % PER_ROW) * V;
+        const T* f = reinterpret_cast<const T*>(&r[i]);
+        const float sc = (rs ? rs[i] : 1.f) * mult;
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+          const float x = to_f<T>(f[u]) * sc;
+          if (lo) split_store<E>(hi + (c + u) * lds + row, lo + (c + u) * lds_lo + row, x);
+          else hi[(c + u) * lds + row] = from_f<E>(x);
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ int row_of(int i) const { return (threadIdx.x + i * kChunkThreads) / PER_ROW; }
+  // float tile written as E hi (and lo) parts
+  template <typename E>
+  __device__ __forceinline__ void store_split(E* hi, E* lo, int lds) const {
+    static_assert(sizeof(T) == 4, "split store takes a float tile");
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int e = threadIdx.x + i * kChunkThreads;
+      if (e < TOTAL) {
+        const int row = e / PER_ROW, c = (e % PER_ROW) * V;
+        const float* f = reinterpret_cast<const float*>(&r[i]);
+#pragma unroll
+        for (int u = 0; u < V; ++u) split_store<E>(hi + row * lds + c + u, lo + row * lds + c + u, f[u]);
+      }
+    }
+  }
+};
+
+// Workgroup -> (sequence, v-head, dv tile) so that the G * NVT workgroups that
+// read one (sequence, k-head)'s chunk tiles share an XCD (blocks are dealt to
+// the 8 XCDs round-robin) and hence its L2.  Returns false for padding blocks.
+__device__ __forceinline__ bool state_block(int bid, int N, int Hk, int G, int NVT, int& n, int& h, int& vt) {
+  const int per = G * NVT;
+  const int xcd = bid & 7, q = bid >> 3;
+  const int m = q % per;
+  const int gidx = (q / per) * 8 + xcd;
+  if (gidx >= N * Hk) return false;
+  n = gidx / Hk;
+  h = (gidx % Hk) * G + m / NVT;
+  vt = m % NVT;
+  return true;
+}
+
+
+inline int state_grid(int N, int Hk, int G, int NVT) { return ((N * Hk + 7) / 8) * 8 * G * NVT; }
 
 }  // namespace gdn

@@ -230,8 +230,8 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
   constexpr int NHW = (NHT + kChunkWaves - 1) / kChunkWaves;
   constexpr int NWT = (C / 16) * NCT;           // W / O tiles
   constexpr int NWW = (NWT + kChunkWaves - 1) / kChunkWaves;
-  const int bid = blockIdx.x;
-  const int vt = bid % NVT, h = (bid / NVT) % a.Hv, n = bid / (NVT * a.Hv);
+  int n, h, vt;
+  if (!state_block(blockIdx.x, a.N, a.Hk, a.G, NVT, n, h, vt)) return;
   const int j = h / a.G;
   const int w = wave_id();
   const int col0 = vt * DVT;
@@ -263,23 +263,46 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
       }
     }
   };
-  write_Ht();
+
+  // next chunk's tiles, staged in registers
+  TileRegs<E, C, D> pWk;
+  TileRegs<E, D, C> pKt;
+  TileRegs<E, OUT ? C : 16, OUT ? D : 16 / (int)sizeof(E)> pQ;
+  TileRegs<float, OUT ? C : 1, OUT ? C : 4> pP;
+  TileRegs<float, C, DVT> pU;
+  TileRegs<float, 1, C> pG;
+  int ptok = 0, plen = 0;
+  auto prefetch = [&](int ci) {
+    const int4 ent = chunk_entry(a.table, ci);
+    ptok = ent.y;
+    plen = ent.z;
+    const int64_t slot = (int64_t)ci * a.Hv + h;
+    pWk.load((const E*)a.Wk + slot * C * D, D, C);
+    pKt.load((const E*)a.Kt + slot * D * C, C, D);
+    if constexpr (OUT) {
+      pQ.load((const E*)a.q + (int64_t)ptok * a.sqk + (int64_t)j * D, a.sqk, plen);
+      pP.load(a.P + slot * C * C, C, C);
+    }
+    pU.load(a.U + slot * C * D + col0, D, C);
+    pG.load(a.gam + slot * C, C, 1);
+  };
 
   const int c0 = a.seq_chunk0[n], c1 = a.seq_chunk0[n + 1];
+  if (c0 < c1) prefetch(c0);
+  write_Ht();
   for (int ci = c0; ci < c1; ++ci) {
-    const int4 ent = chunk_entry(a.table, ci);
-    const int tok0 = ent.y, len = ent.z;
+    const int tok0 = ptok, len = plen;
     const int64_t slot = (int64_t)ci * a.Hv + h;
-    g2s<E, C, D>(&sm.Wk[0][0], S::LDQ, (const E*)a.Wk + slot * C * D);
-    g2s<E, D, C>(&sm.Kt[0][0], S::LDCE, (const E*)a.Kt + slot * D * C);
+    __syncthreads();  // the previous chunk is done with the LDS tiles
+    pWk.store(&sm.Wk[0][0], S::LDQ);
+    pKt.store(&sm.Kt[0][0], S::LDCE);
     if constexpr (OUT) {
-      rows2s<E, C, D>(&sm.Q[0][0], S::LDQ, (const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D, a.sqk, len);
-      const float* Pg = a.P + slot * C * C;
-      for (int e = threadIdx.x; e < C * C; e += kChunkThreads) {
-        const int r = e / C, c = e % C;
-        split_store<E>(&sm.P[r][c], &sm.Pl[0][0] + r * S::LDCE + c, Pg[e]);
-      }
-    } else {
+      pQ.store(&sm.Q[0][0], S::LDQ);
+      pP.template store_split<E>(&sm.P[0][0], &sm.Pl[0][0], S::LDCE);
+    }
+    pU.store(&sm.U[0][0], S::LDU);
+    pG.store(&sm.gam[0], C);
+    if constexpr (!OUT) {
       // state entering this chunk, for the backward pass
       float* Hg = a.Hc + slot * D * D;
 #pragma unroll
@@ -288,10 +311,9 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
         if (t < NHT) store_tile<float>(Hg, D, (t / NCT) * 16, col0 + (t % NCT) * 16, Hr[i], D);
       }
     }
-    for (int e = threadIdx.x; e < C; e += kChunkThreads) sm.gam[e] = a.gam[slot * C + e];
     __syncthreads();
+    if (ci + 1 < c1) prefetch(ci + 1);  // in flight during this chunk's compute
 
-    const float* Ug = a.U + slot * C * D;
     f32x4 Or[NWW];
 #pragma unroll
     for (int i = 0; i < NWW; ++i) {
@@ -305,7 +327,7 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = rt * 16 + acc_row(e), c = ct * 16 + acc_col();
-          wv[e] = Ug[r * D + col0 + c] - x[e];
+          wv[e] = sm.U[r][c] - x[e];
           split_store<E>(&sm.Wt[c][r], &sm.Wtl[0][0] + c * S::LDCE + r, wv[e]);
         }
         if constexpr (!OUT) store_tile<float>(a.W + slot * C * D, D, rt * 16, col0 + ct * 16, wv, C);
@@ -350,8 +372,7 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
         }
       }
     }
-    __syncthreads();
-    write_Ht();
+    write_Ht();  // phase 1 (the only reader of Ht) is over for every wave
   }
   if (a.ht) {
     float* dst = a.ht + ((int64_t)n * a.Hv + h) * D * D;
@@ -391,7 +412,7 @@ void launch_chunk_fwd_core(const ChunkArgs& a, hipStream_t st, bool out_mode) {
     if (out_mode) prep_kernel<E, D, C, false><<<gprep, kChunkThreads, 0, st>>>(a);
     else prep_kernel<E, D, C, true><<<gprep, kChunkThreads, 0, st>>>(a);
   }
-  dim3 gstate(a.N * a.Hv * (D / DVT));
+  dim3 gstate(state_grid(a.N, a.Hk, a.G, D / DVT));
   GDN_PROF(out_mode ? "chunk_state_fwd" : "chunk_state_store", st);
   if (out_mode) state_fwd_kernel<E, D, C, DVT, true><<<gstate, kChunkThreads, 0, st>>>(a);
   else state_fwd_kernel<E, D, C, DVT, false><<<gstate, kChunkThreads, 0, st>>>(a);
