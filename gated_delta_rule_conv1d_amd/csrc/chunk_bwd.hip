@@ -214,63 +214,176 @@ __global__ __launch_bounds__(kChunkThreads) void state_bwd_kernel(ChunkArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Contractions over d_v, one workgroup per (chunk, v-head):
-//   dWk = -dW Hc^T  (hi/lo in LDS; transposed fp32 copy to workspace)
-//   dT  = beta_s (dW V^T)_rs + beta_s Gam_s (dWk K^T)_rs
+// Every contraction over d_v, one workgroup per (chunk, v-head), from operands
+// staged in LDS (fp32 ones as hi + lo bf16):
+//   dQs = scale diag(Gam) dO Hc^T        dWk = -dW Hc^T  (stored transposed)
+//   dT  = dW (diag(beta) V)^T + dWk (diag(beta Gam) K)^T
+//   dKh = diag(e) W dHn^T                dP  = scale dO W^T (lower-incl., rows < len)
 //   hdot = <Hc, dHn>
 // ---------------------------------------------------------------------------
 template <typename E, int D, int C>
 struct GradASmem {
   static constexpr int LO = Split<E>::on ? 1 : 0;
   static constexpr int LDQ = D + Pad<E>::E16;
-  E dWk[C][LDQ];
-  E dWkl[LO ? C : 1][LDQ];
-  E Vs[C][LDQ];
-  E Ks[C][LDQ];
-  float bs[C];
+  E Hh[D][LDQ];                 // Hc, then dHn (hi)
+  E Hl[LO ? D : 1][LDQ];        // lo parts; K while the H region is between uses
+  E Os[C][LDQ];                 // dO, then dWk hi, then dO again
+  E Xh[C][LDQ];                 // dW, then W (hi)
+  E Xl[LO ? C : 1][LDQ];        // lo parts
+  E Vs[C][LDQ];                 // V, then dWk lo
+  E Ks[LO ? 1 : C][LDQ];        // K (float operands only)
+  float bs[C], gm[C], em[C];
   float red[kChunkThreads];
 };
 
 template <typename E, int D, int C>
 __global__ __launch_bounds__(kChunkThreads) void grad_a_kernel(ChunkArgs a) {
   using S = GradASmem<E, D, C>;
-  using M = Mma<E>;
   __shared__ S sm;
   constexpr bool LO = Split<E>::on;
   constexpr int NT = C / 16, ND = D / 16;
+  constexpr int RT = NT >= 2 ? 2 : 1;      // block rows (C side)
+  constexpr int CD = ND >= 4 ? 4 : ND;     // block cols on the D side
+  constexpr int CC = NT >= 2 ? 2 : 1;      // block cols on the C side
   const int ci = blockIdx.x, h = blockIdx.y;
   const int4 ent = chunk_entry(a.table, ci);
   if (ent.x < 0) return;
   const int tok0 = ent.y, len = ent.z;
   const int j = h / a.G;
-  const int w = wave_id(), tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const int64_t slot = (int64_t)ci * a.Hv + h;
   const float* Hc = a.Hc + slot * D * D;
-  const float* dW = a.dW + slot * C * D;
+  const float* dHn = a.dHn + slot * D * D;
+  const E* dog = (const E*)a.d_o + (int64_t)tok0 * a.Hv * D + (int64_t)h * D;
+  const int64_t ldo = (int64_t)a.Hv * D;
+  E* Hlo = LO ? &sm.Hl[0][0] : nullptr;
+  E* Xlo = LO ? &sm.Xl[0][0] : nullptr;
+  E* Kst = LO ? &sm.Hl[0][0] : &sm.Ks[0][0];  // K reuses the lo half of the H region
 
-  rows2s<E, C, D>(&sm.Vs[0][0], S::LDQ, (const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)h * D, a.sv, len);
-  rows2s<E, C, D>(&sm.Ks[0][0], S::LDQ, (const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D, a.sqk, len);
-  for (int e = tid; e < C; e += kChunkThreads) sm.bs[e] = e < len ? a.beta[(int64_t)(tok0 + e) * a.Hv + h] : 0.f;
-  float* dWkt = a.dWkt + slot * D * C;
-  for (int t = w; t < NT * ND; t += kChunkWaves) {
-    const int rt = t / ND, ct = t % ND;
-    const f32x4 acc = mm_gen<E, D, true, true>(
-        zero4(), [&](int r, int k, float* o) { ld_row<float, M::KPL>(dW + (rt * 16 + r) * D + k, o); },
-        [&](int c, int k, float* o) { ld_row<float, M::KPL>(Hc + (ct * 16 + c) * D + k, o); });
-    f32x4 neg;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      neg[e] = -acc[e];
-      const int r = rt * 16 + acc_row(e), c = ct * 16 + acc_col();
-      split_store<E>(&sm.dWk[r][c], &sm.dWkl[0][0] + r * S::LDQ + c, neg[e]);
-    }
-    store_tile_t(dWkt, C, rt * 16, ct * 16, neg);
+  {  // stage Hc, dO, dW, V
+    TileRegs<float, D, D> rH;
+    TileRegs<E, C, D> rO, rV;
+    TileRegs<float, C, D> rW;
+    rH.load(Hc, D, D);
+    rO.load(dog, ldo, len);
+    rW.load(a.dW + slot * C * D, D, C);
+    rV.load((const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)h * D, a.sv, len);
+    rH.template store_split<E>(&sm.Hh[0][0], Hlo, S::LDQ);
+    rO.store(&sm.Os[0][0], S::LDQ);
+    rW.template store_split<E>(&sm.Xh[0][0], Xlo, S::LDQ);
+    rV.store(&sm.Vs[0][0], S::LDQ);
   }
-  {  // <Hc, dHn>
-    const float* dHn = a.dHn + slot * D * D;
-    float s = 0.f;
-    for (int e = tid; e < D * D; e += kChunkThreads) s += Hc[e] * dHn[e];
-    sm.red[tid] = s;
+  for (int e = tid; e < C; e += kChunkThreads) {
+    const float g = a.gam[slot * C + e];
+    sm.bs[e] = e < len ? a.beta[(int64_t)(tok0 + e) * a.Hv + h] : 0.f;
+    sm.gm[e] = __expf(g);
+    sm.em[e] = e < len ? __expf(a.gam[slot * C + len - 1] - g) : 0.f;
+  }
+  __syncthreads();
+
+  // (a) dQs = scale Gam dO Hc^T (to workspace); dT1 = dW V^T kept for (c)
+  for_blocks<NT, ND, RT, CD>([&](int r0, int c0) {
+    f32x4 acc[RT][CD];
+    zero_blk(acc);
+    mm_blk<E, D, RT, CD, false, LO>(acc, &sm.Os[r0 * 16][0], nullptr, S::LDQ, &sm.Hh[c0 * 16][0],
+                                    LO ? &sm.Hl[c0 * 16][0] : nullptr, S::LDQ);
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int jj = 0; jj < CD; ++jj) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = a.scale * sm.gm[(r0 + i) * 16 + acc_row(e)] * acc[i][jj][e];
+        store_tile<float>(a.dQs + slot * C * D, D, (r0 + i) * 16, (c0 + jj) * 16, v, C);
+      }
+  });
+  constexpr int NBT = (NT / RT) * (NT / CC);
+  constexpr int NBW = (NBT + kChunkWaves - 1) / kChunkWaves;
+  f32x4 dT1[NBW][RT][CC];
+#pragma unroll
+  for (int bi = 0; bi < NBW; ++bi) {
+    zero_blk(dT1[bi]);
+    const int b = wave_id() + bi * kChunkWaves;
+    if (b < NBT) {
+      const int r0 = (b / (NT / CC)) * RT, c0 = (b % (NT / CC)) * CC;
+      mm_blk<E, D, RT, CC, LO, false>(dT1[bi], &sm.Xh[r0 * 16][0], LO ? &sm.Xl[r0 * 16][0] : nullptr, S::LDQ,
+                                      &sm.Vs[c0 * 16][0], nullptr, S::LDQ);
+    }
+  }
+  __syncthreads();  // dO and V are no longer read
+
+  // (b) dWk = -dW Hc^T: hi -> Os, lo -> Vs; transposed fp32 copy to workspace
+  for_blocks<NT, ND, RT, CD>([&](int r0, int c0) {
+    f32x4 acc[RT][CD];
+    zero_blk(acc);
+    mm_blk<E, D, RT, CD, LO, LO>(acc, &sm.Xh[r0 * 16][0], LO ? &sm.Xl[r0 * 16][0] : nullptr, S::LDQ,
+                                 &sm.Hh[c0 * 16][0], LO ? &sm.Hl[c0 * 16][0] : nullptr, S::LDQ);
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int jj = 0; jj < CD; ++jj) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = -acc[i][jj][e];
+          const int r = (r0 + i) * 16 + acc_row(e), c = (c0 + jj) * 16 + acc_col();
+          split_store<E>(&sm.Os[r][c], &sm.Vs[r][c], v[e]);
+        }
+        store_tile_t(a.dWkt + slot * D * C, C, (r0 + i) * 16, (c0 + jj) * 16, v);
+      }
+  });
+  __syncthreads();  // Hc is no longer read
+  {
+    TileRegs<E, C, D> rK;
+    rK.load((const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D, a.sqk, len);
+    rK.store(Kst, S::LDQ);
+  }
+  __syncthreads();
+
+  // (c) dT = beta_s dT1 + beta_s Gam_s dWk K^T
+#pragma unroll
+  for (int bi = 0; bi < NBW; ++bi) {
+    const int b = wave_id() + bi * kChunkWaves;
+    if (b < NBT) {
+      const int r0 = (b / (NT / CC)) * RT, c0 = (b % (NT / CC)) * CC;
+      f32x4 acc[RT][CC];
+      zero_blk(acc);
+      mm_blk<E, D, RT, CC, LO, false>(acc, &sm.Os[r0 * 16][0], LO ? &sm.Vs[r0 * 16][0] : nullptr, S::LDQ,
+                                      Kst + c0 * 16 * S::LDQ, nullptr, S::LDQ);
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int jj = 0; jj < CC; ++jj) {
+          const int s = (c0 + jj) * 16 + acc_col();
+          const float bsv = sm.bs[s], bg = bsv * sm.gm[s];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            a.dT[slot * C * C + ((r0 + i) * 16 + acc_row(e)) * C + s] = bsv * dT1[bi][i][jj][e] + bg * acc[i][jj][e];
+        }
+    }
+  }
+  __syncthreads();  // dWk and K are no longer read
+
+  {  // stage dHn (and <Hc, dHn>), W, dO again
+    TileRegs<float, D, D> rD, rH;
+    TileRegs<float, C, D> rW;
+    TileRegs<E, C, D> rO;
+    rD.load(dHn, D, D);
+    rH.load(Hc, D, D);
+    rW.load(a.W + slot * C * D, D, C);
+    rO.load(dog, ldo, len);
+    float hs = 0.f;
+#pragma unroll
+    for (int i = 0; i < TileRegs<float, D, D>::N; ++i) {
+      const float* x = reinterpret_cast<const float*>(&rD.r[i]);
+      const float* y = reinterpret_cast<const float*>(&rH.r[i]);
+      if (threadIdx.x + i * kChunkThreads < TileRegs<float, D, D>::TOTAL)
+        hs += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+    }
+    sm.red[tid] = hs;
+    rD.template store_split<E>(&sm.Hh[0][0], Hlo, S::LDQ);
+    rW.template store_split<E>(&sm.Xh[0][0], Xlo, S::LDQ);
+    rO.store(&sm.Os[0][0], S::LDQ);
   }
   __syncthreads();
   if (tid == 0) {
@@ -278,42 +391,66 @@ __global__ __launch_bounds__(kChunkThreads) void grad_a_kernel(ChunkArgs a) {
     for (int i = 0; i < kChunkThreads; ++i) s += sm.red[i];
     a.hdot[slot] = s;
   }
-  const float* gam = a.gam + slot * C;
-  float* dTg = a.dT + slot * C * C;
-  for (int t = w; t < NT * NT; t += kChunkWaves) {
-    const int rt = t / NT, ct = t % NT;
-    const f32x4 xu = mm_gen<E, D, true, false>(
-        zero4(), [&](int r, int k, float* o) { ld_row<float, M::KPL>(dW + (rt * 16 + r) * D + k, o); },
-        [&](int c, int k, float* o) { ld_row<E, M::KPL>(&sm.Vs[ct * 16 + c][k], o); });
-    f32x4 xw = mm_tile<E, D>(zero4(), &sm.dWk[rt * 16][0], S::LDQ, &sm.Ks[ct * 16][0], S::LDQ);
-    if constexpr (LO) xw = mm_tile<E, D>(xw, &sm.dWkl[rt * 16][0], S::LDQ, &sm.Ks[ct * 16][0], S::LDQ);
-    const int s = ct * 16 + acc_col();
-    const float bsv = sm.bs[s], bg = bsv * __expf(gam[s]);
+  // (d) dKh = e W dHn^T;  dP = scale dO W^T
+  for_blocks<NT, ND, RT, CD>([&](int r0, int c0) {
+    f32x4 acc[RT][CD];
+    zero_blk(acc);
+    mm_blk<E, D, RT, CD, LO, LO>(acc, &sm.Xh[r0 * 16][0], LO ? &sm.Xl[r0 * 16][0] : nullptr, S::LDQ,
+                                 &sm.Hh[c0 * 16][0], LO ? &sm.Hl[c0 * 16][0] : nullptr, S::LDQ);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) dTg[(rt * 16 + acc_row(e)) * C + s] = bsv * xu[e] + bg * xw[e];
-  }
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int jj = 0; jj < CD; ++jj) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = sm.em[(r0 + i) * 16 + acc_row(e)] * acc[i][jj][e];
+        store_tile<float>(a.dKh + slot * C * D, D, (r0 + i) * 16, (c0 + jj) * 16, v, C);
+      }
+  });
+  for_blocks<NT, NT, RT, CC>([&](int r0, int c0) {
+    f32x4 acc[RT][CC];
+    zero_blk(acc);
+    mm_blk<E, D, RT, CC, false, LO>(acc, &sm.Os[r0 * 16][0], nullptr, S::LDQ, &sm.Xh[c0 * 16][0],
+                                    LO ? &sm.Xl[c0 * 16][0] : nullptr, S::LDQ);
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int jj = 0; jj < CC; ++jj) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = (r0 + i) * 16 + acc_row(e), c = (c0 + jj) * 16 + acc_col();
+          v[e] = (c <= r && r < len) ? a.scale * acc[i][jj][e] : 0.f;
+        }
+        store_tile<float>(a.dP + slot * C * C, C, (r0 + i) * 16, (c0 + jj) * 16, v, C);
+      }
+  });
 }
 
 // ---------------------------------------------------------------------------
 // WY-representation gradients, one workgroup per (chunk, k-head), looping
 // over the k-head's v-heads; dq and dk accumulate in registers across them.
+// Every operand is staged in LDS first (fp32 ones split on the fly into bf16
+// hi + lo MFMA parts); K K^T is formed once per k-head.
 // ---------------------------------------------------------------------------
 template <typename E, int D, int C>
 struct GradBSmem {
   static constexpr int LD2C = 2 * C + Pad<E>::E16;
   static constexpr int LDCF = C + 4;
   static constexpr int NT = C / 16, ND = D / 16;
-  E QKt[D][LD2C];     // [Q^T | K^T]
-  float Am[C][LDCF];  // A, then dA
+  E QKt[D][LD2C];      // [Q^T | K^T]
+  float Skk[C][LDCF];  // K K^T
+  float Am[C][LDCF];   // A, then dA
   float Tm[C][LDCF];
   float Tt[C][LDCF];
   union U {
-    float M1t[C][LDCF];
+    float Xf[D][LDCF];                            // dW^T or dWk^T
+    struct { float dT[C][LDCF]; float M1t[C][LDCF]; } m;
     struct { float dS[C][LDCF]; float At[C][LDCF]; } s;
     float Xs[kChunkWaves][16][20];
   } r;
   float gam[C], beta[C], Gm[C], em[C];
-  float pCD[4][ND][C];   // row partials of C x D tiles: dXu.v, dXw.k, dQs.q, dKhn.k
+  float pCD[4][ND][C];   // row partials of C x D tiles: dXu.v, dXw.k, dQs.q, dKh.k
   float pCC[5][NT][C];   // dA D Skk rows, dA*A rows, dA*A cols, dP*P rows, dP*P cols
 };
 
@@ -322,6 +459,7 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
   using S = GradBSmem<E, D, C>;
   using M = Mma<E>;
   constexpr int KPL = M::KPL;
+  constexpr bool LO = Split<E>::on;
   __shared__ S sm;
   constexpr int NT = S::NT, ND = S::ND;
   constexpr int NQT = NT * ND;
@@ -336,6 +474,23 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
 
   rows2s_t<E, C, D>(&sm.QKt[0][0], S::LD2C, qg, a.sqk, len, nullptr, 1.f);
   rows2s_t<E, C, D>(&sm.QKt[0][C], S::LD2C, kg, a.sqk, len, nullptr, 1.f);
+  __syncthreads();
+  // K K^T (exact bf16 products, fp32 sums), shared by the k-head's v-heads
+  for (int t = w; t < NT * NT; t += kChunkWaves) {
+    const int rt = t / NT, ct = t % NT;
+    const f32x4 skk = mm_gen<E, D, false, false>(
+        zero4(),
+        [&](int r, int k, float* o) {
+#pragma unroll
+          for (int u = 0; u < KPL; ++u) o[u] = to_f<E>(sm.QKt[k + u][C + rt * 16 + r]);
+        },
+        [&](int c, int k, float* o) {
+#pragma unroll
+          for (int u = 0; u < KPL; ++u) o[u] = to_f<E>(sm.QKt[k + u][C + ct * 16 + c]);
+        });
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.Skk[rt * 16 + acc_row(e)][ct * 16 + acc_col()] = skk[e];
+  }
 
   f32x4 dQ[NQW], dK[NQW];
 #pragma unroll
@@ -345,97 +500,106 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
     const int h = j * a.G + gi;
     const int64_t slot = (int64_t)ci * a.Hv + h;
     const E* vg = (const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)h * D;
-    const E* dog = (const E*)a.d_o + (int64_t)tok0 * a.Hv * D + (int64_t)h * D;
-    const int64_t ldo = (int64_t)a.Hv * D;
-    const float* Wg = a.W + slot * C * D;
-    const float* Hc = a.Hc + slot * D * D;
-    const float* dHn = a.dHn + slot * D * D;
-    const float* dWt = a.dWt + slot * D * C;
-    const float* dWkt = a.dWkt + slot * D * C;
-    const float* dTg = a.dT + slot * C * C;
-    const float* Pg = a.P + slot * C * C;
-    auto do_rows = [&](int r0) {  // masked rows of dO
-      return [&, r0](int r, int k, float* o) {
-        if (r0 + r < len) ld_row<E, KPL>(dog + (int64_t)(r0 + r) * ldo + k, o);
-        else
-#pragma unroll
-          for (int i = 0; i < KPL; ++i) o[i] = 0.f;
-      };
-    };
     for (int e = tid; e < C; e += kChunkThreads) {
       const float gm = a.gam[slot * C + e];
       sm.gam[e] = gm;
       sm.Gm[e] = __expf(gm);
       sm.beta[e] = e < len ? a.beta[(int64_t)(tok0 + e) * a.Hv + h] : 0.f;
+      sm.em[e] = e < len ? __expf(a.gam[slot * C + len - 1] - gm) : 0.f;
     }
     __syncthreads();
-    for (int e = tid; e < C; e += kChunkThreads) sm.em[e] = e < len ? __expf(sm.gam[len - 1] - sm.gam[e]) : 0.f;
     // A = strict_lower(beta_r D_rs k_r.k_s)
-    for (int t = w; t < NT * NT; t += kChunkWaves) {
-      const int rt = t / NT, ct = t % NT;
-      f32x4 skk = zero4();
-      if (rt * 16 < len && ct * 16 < len)
-        skk = mm_tile_rows<E, D>(zero4(), kg + (int64_t)rt * 16 * a.sqk, a.sqk, len - rt * 16,
-                                 kg + (int64_t)ct * 16 * a.sqk, a.sqk, len - ct * 16);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = rt * 16 + acc_row(e), s = ct * 16 + acc_col();
-        sm.Am[r][s] = (s < r) ? sm.beta[r] * __expf(sm.gam[r] - sm.gam[s]) * skk[e] : 0.f;
-      }
+    for (int e = tid; e < C * C; e += kChunkThreads) {
+      const int r = e / C, s = e % C;
+      sm.Am[r][s] = (s < r) ? sm.beta[r] * __expf(sm.gam[r] - sm.gam[s]) * sm.Skk[r][s] : 0.f;
     }
     __syncthreads();
     unit_lower_inverse<C, S::LDCF>(sm.Am, sm.Tm, sm.Tt, sm.r.Xs);
-    // dXu = T^T dW -> dv, <dXu, v>;  dXw = T^T dWk -> dK, <dXw, k>
+
+    auto ta = [&](int rt) {
+      return [&, rt](int r, int k, float* o) { ld_row<float, KPL>(&sm.Tt[rt * 16 + r][k], o); };
+    };
+    auto xb = [&](int ct) {
+      return [&, ct](int c, int k, float* o) { ld_row<float, KPL>(&sm.r.Xf[ct * 16 + c][k], o); };
+    };
+    // dXu = T^T dW -> dv and <dXu, v>
+    {
+      TileRegs<float, D, C> rX;
+      rX.load(a.dWt + slot * D * C, C, D);
+      rX.store(&sm.r.Xf[0][0], S::LDCF);
+    }
+    __syncthreads();
     E* dvg = (E*)a.dv + (int64_t)tok0 * a.sv + (int64_t)h * D;
 #pragma unroll
     for (int i = 0; i < NQW; ++i) {
       const int t = w + kChunkWaves * i;
       if (t < NQT) {
         const int rt = t / ND, ct = t % ND;
-        auto ta = [&](int r, int k, float* o) { ld_row<float, KPL>(&sm.Tt[rt * 16 + r][k], o); };
-        const f32x4 xu = mm_gen<E, C, true, true>(
-            zero4(), ta, [&](int c, int k, float* o) { ld_row<float, KPL>(dWt + (ct * 16 + c) * C + k, o); });
-        const f32x4 xw = mm_gen<E, C, true, true>(
-            zero4(), ta, [&](int c, int k, float* o) { ld_row<float, KPL>(dWkt + (ct * 16 + c) * C + k, o); });
+        const f32x4 xu = mm_gen<E, C, LO, LO>(zero4(), ta(rt), xb(ct));
         f32x4 dvv;
-        float pu[4], pw[4];
+        float pu[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = rt * 16 + acc_row(e), c = ct * 16 + acc_col();
-          const float br = sm.beta[r];
-          dvv[e] = br * xu[e];
-          const float vv = r < len ? to_f<E>(vg[(int64_t)r * a.sv + c]) : 0.f;
-          pu[e] = xu[e] * vv;
-          pw[e] = xw[e] * to_f<E>(sm.QKt[c][C + r]);
-          dK[i][e] += br * sm.Gm[r] * xw[e];
+          dvv[e] = sm.beta[r] * xu[e];
+          pu[e] = xu[e] * (r < len ? to_f<E>(vg[(int64_t)r * a.sv + c]) : 0.f);
         }
         store_tile<E>(dvg, a.sv, rt * 16, ct * 16, dvv, len);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pu[e] = group_sum<16>(pu[e]);
-          pw[e] = group_sum<16>(pw[e]);
-        }
+        for (int e = 0; e < 4; ++e) pu[e] = group_sum<16>(pu[e]);
         if ((lane & 15) == 0) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sm.pCD[0][ct][rt * 16 + acc_row(e)] = pu[e];
-            sm.pCD[1][ct][rt * 16 + acc_row(e)] = pw[e];
-          }
+          for (int e = 0; e < 4; ++e) sm.pCD[0][ct][rt * 16 + acc_row(e)] = pu[e];
         }
       }
     }
-    // M1 = dT T^T (fp32 MFMA), stored transposed
-    for (int t = w; t < NT * NT; t += kChunkWaves) {
-      const int rt = t / NT, ct = t % NT;
-      const f32x4 m = mm_tile<float, C>(zero4(), dTg + rt * 16 * C, C, &sm.Tm[ct * 16][0], S::LDCF);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sm.r.M1t[ct * 16 + acc_col()][rt * 16 + acc_row(e)] = m[e];
+    __syncthreads();
+    // dXw = T^T dWk -> dK and <dXw, k>
+    {
+      TileRegs<float, D, C> rX;
+      rX.load(a.dWkt + slot * D * C, C, D);
+      rX.store(&sm.r.Xf[0][0], S::LDCF);
     }
     __syncthreads();
-    // dA = strict_lower(-T^T M1)
+#pragma unroll
+    for (int i = 0; i < NQW; ++i) {
+      const int t = w + kChunkWaves * i;
+      if (t < NQT) {
+        const int rt = t / ND, ct = t % ND;
+        const f32x4 xw = mm_gen<E, C, LO, LO>(zero4(), ta(rt), xb(ct));
+        float pw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = rt * 16 + acc_row(e), c = ct * 16 + acc_col();
+          pw[e] = xw[e] * to_f<E>(sm.QKt[c][C + r]);
+          dK[i][e] += sm.beta[r] * sm.Gm[r] * xw[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pw[e] = group_sum<16>(pw[e]);
+        if ((lane & 15) == 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sm.pCD[1][ct][rt * 16 + acc_row(e)] = pw[e];
+        }
+      }
+    }
+    __syncthreads();
+    // M1 = dT T^T (fp32 MFMA), stored transposed; dA = strict_lower(-T^T M1)
+    {
+      TileRegs<float, C, C> rT;
+      rT.load(a.dT + slot * C * C, C, C);
+      rT.store(&sm.r.m.dT[0][0], S::LDCF);
+    }
+    __syncthreads();
     for (int t = w; t < NT * NT; t += kChunkWaves) {
       const int rt = t / NT, ct = t % NT;
-      const f32x4 m = mm_tile<float, C>(zero4(), &sm.Tt[rt * 16][0], S::LDCF, &sm.r.M1t[ct * 16][0], S::LDCF);
+      const f32x4 m = mm_tile<float, C>(zero4(), &sm.r.m.dT[rt * 16][0], S::LDCF, &sm.Tm[ct * 16][0], S::LDCF);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.r.m.M1t[ct * 16 + acc_col()][rt * 16 + acc_row(e)] = m[e];
+    }
+    __syncthreads();
+    for (int t = w; t < NT * NT; t += kChunkWaves) {
+      const int rt = t / NT, ct = t % NT;
+      const f32x4 m = mm_tile<float, C>(zero4(), &sm.Tt[rt * 16][0], S::LDCF, &sm.r.m.M1t[ct * 16][0], S::LDCF);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = rt * 16 + acc_row(e), s = ct * 16 + acc_col();
@@ -444,27 +608,22 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
     }
     __syncthreads();
     // C x C pass: A~, dS, and the dgamma / dbeta terms of A and P
+    const float* Pg = a.P + slot * C * C;
+    const float* dPg = a.dP + slot * C * C;
     for (int t = w; t < NT * NT; t += kChunkWaves) {
       const int rt = t / NT, ct = t % NT;
-      f32x4 skk = zero4(), dp = zero4();
-      if (rt * 16 < len && ct * 16 < len) {
-        skk = mm_tile_rows<E, D>(zero4(), kg + (int64_t)rt * 16 * a.sqk, a.sqk, len - rt * 16,
-                                 kg + (int64_t)ct * 16 * a.sqk, a.sqk, len - ct * 16);
-        dp = mm_gen<E, D, false, true>(zero4(), do_rows(rt * 16), [&](int c, int k, float* o) {
-          ld_row<float, KPL>(Wg + (ct * 16 + c) * D + k, o);
-        });
-      }
       float rb[4], ra[4], rp[4], ca = 0.f, cp = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = rt * 16 + acc_row(e), s = ct * 16 + acc_col();
+        const float skk = sm.Skk[r][s];
         const float dd = (s <= r) ? __expf(sm.gam[r] - sm.gam[s]) : 0.f;
         const float dA = sm.Am[r][s];
         const float At = dA * sm.beta[r] * dd;
-        const float AdA = At * skk[e];
-        const float dP = (s <= r && r < len) ? a.scale * dp[e] : 0.f;
+        const float AdA = At * skk;
+        const float dP = dPg[r * C + s];
         const float PdP = dP * Pg[r * C + s];
-        rb[e] = dA * dd * skk[e];
+        rb[e] = dA * dd * skk;
         ra[e] = AdA;
         rp[e] = PdP;
         ca += AdA;
@@ -497,33 +656,26 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();
-    // dQ += Gam dO' Hc^T + dS K;   dK += e W dHn^T + dS^T Q + (A~ + A~^T) K
+    // dQ += dQs + dS K;   dK += dKh + dS^T Q + (A~ + A~^T) K
+    const float* dQsg = a.dQs + slot * C * D;
+    const float* dKhg = a.dKh + slot * C * D;
 #pragma unroll
     for (int i = 0; i < NQW; ++i) {
       const int t = w + kChunkWaves * i;
       if (t < NQT) {
         const int rt = t / ND, ct = t % ND;
-        f32x4 qs = zero4(), kh = zero4();
-        if (rt * 16 < len) {
-          qs = mm_gen<E, D, false, true>(zero4(), do_rows(rt * 16), [&](int c, int k, float* o) {
-            ld_row<float, KPL>(Hc + (ct * 16 + c) * D + k, o);
-          });
-          kh = mm_gen<E, D, true, true>(
-              zero4(), [&](int r, int k, float* o) { ld_row<float, KPL>(Wg + (rt * 16 + r) * D + k, o); },
-              [&](int c, int k, float* o) { ld_row<float, KPL>(dHn + (ct * 16 + c) * D + k, o); });
-        }
         auto kt = [&](int c, int k, float* o) { ld_row<E, KPL>(&sm.QKt[ct * 16 + c][C + k], o); };
         auto qt = [&](int c, int k, float* o) { ld_row<E, KPL>(&sm.QKt[ct * 16 + c][k], o); };
-        const f32x4 sq = mm_gen<E, C, true, false>(
+        const f32x4 sq = mm_gen<E, C, LO, false>(
             zero4(), [&](int r, int k, float* o) { ld_row<float, KPL>(&sm.r.s.dS[rt * 16 + r][k], o); }, kt);
-        f32x4 sk = mm_gen<E, C, true, false>(
+        f32x4 sk = mm_gen<E, C, LO, false>(
             zero4(),
             [&](int r, int k, float* o) {
 #pragma unroll
               for (int u = 0; u < KPL; ++u) o[u] = sm.r.s.dS[k + u][rt * 16 + r];
             },
             qt);
-        sk = mm_gen<E, C, true, false>(
+        sk = mm_gen<E, C, LO, false>(
             sk,
             [&](int r, int k, float* o) {
               ld_row<float, KPL>(&sm.r.s.At[rt * 16 + r][k], o);
@@ -535,8 +687,8 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = rt * 16 + acc_row(e), c = ct * 16 + acc_col();
-          const float qsv = a.scale * sm.Gm[r] * qs[e];
-          const float khv = sm.em[r] * kh[e];
+          const float qsv = dQsg[r * D + c];
+          const float khv = dKhg[r * D + c];
           dQ[i][e] += qsv + sq[e];
           dK[i][e] += khv + sk[e];
           pq[e] = qsv * to_f<E>(sm.QKt[c][r]);
@@ -619,7 +771,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsPlan {
   size_t table, seq0, Wk, U, P, Kt, gam, end_fwd;
-  size_t Wkl, Ktl, Hc, W, dHn, dW, dWt, dT, dWkt, hdot, end_bwd;
+  size_t Wkl, Ktl, Hc, W, dHn, dW, dWt, dT, dWkt, dQs, dKh, dP, hdot, end_bwd;
 };
 
 static WsPlan plan(const gdn_shape* s) {
@@ -644,6 +796,9 @@ static WsPlan plan(const gdn_shape* s) {
   p.dWt = o; o = align256(o + M * Hv * D * C * 4);
   p.dT = o; o = align256(o + M * Hv * C * C * 4);
   p.dWkt = o; o = align256(o + M * Hv * D * C * 4);
+  p.dQs = o; o = align256(o + M * Hv * C * D * 4);
+  p.dKh = o; o = align256(o + M * Hv * C * D * 4);
+  p.dP = o; o = align256(o + M * Hv * C * C * 4);
   p.hdot = o; o = align256(o + M * Hv * 4);
   p.end_bwd = o;
   return p;
@@ -671,6 +826,9 @@ static void fill_ws(ChunkArgs& a, const gdn_shape* s, void* ws) {
   a.dWt = (float*)(b + p.dWt);
   a.dT = (float*)(b + p.dT);
   a.dWkt = (float*)(b + p.dWkt);
+  a.dQs = (float*)(b + p.dQs);
+  a.dKh = (float*)(b + p.dKh);
+  a.dP = (float*)(b + p.dP);
   a.hdot = (float*)(b + p.hdot);
 }
 

@@ -51,6 +51,9 @@ struct ChunkArgs {
   float* dWt;                 // [slot][D][C]  dW transposed
   float* dT;                  // [slot][C][C]
   float* dWkt;                // [slot][D][C]  dWk transposed
+  float* dQs;                 // [slot][C][D]  scale diag(Gam) dO Hc^T
+  float* dKh;                 // [slot][C][D]  diag(e) W dHn^T
+  float* dP;                  // [slot][C][C]  scale dO W^T (lower-inclusive, rows < len)
   float* hdot;                // [slot]        <Hc, dHn>
 };
 
@@ -319,6 +322,14 @@ __device__ __forceinline__ bool state_block(int bid, int N, int Hk, int G, int N
   return true;
 }
 
+
+// visit the RT x CT blocks of an NR x NC tile grid owned by this wave
+template <int NR, int NC, int RT, int CT, typename F>
+__device__ __forceinline__ void for_blocks(F&& f) {
+  static_assert(NR % RT == 0 && NC % CT == 0, "block shape must divide the tile grid");
+  constexpr int NBC = NC / CT, NB = (NR / RT) * NBC;
+  for (int b = wave_id(); b < NB; b += kChunkWaves) f((b / NBC) * RT, (b % NBC) * CT);
+}
 
 inline int state_grid(int N, int Hk, int G, int NVT) { return ((N * Hk + 7) / 8) * 8 * G * NVT; }
 

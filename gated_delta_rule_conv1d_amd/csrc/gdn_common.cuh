@@ -16,13 +16,9 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ float bf2f(bf16 b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// float -> bf16, round to nearest even; NaN stays NaN, infinities pass.
-__device__ __forceinline__ bf16 f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return (bf16)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16)(u >> 16);
-}
+// float -> bf16, round to nearest even (gfx950 converts natively:
+// v_cvt_pk_bf16_f32); NaN stays NaN, infinities pass.
+__device__ __forceinline__ bf16 f2bf(float f) { return __builtin_bit_cast(bf16, static_cast<__bf16>(f)); }
 
 template <typename E> __device__ __forceinline__ float to_f(E v);
 template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
@@ -234,6 +230,54 @@ __device__ __forceinline__ f32x4 mm_gen(f32x4 acc, LA&& la, LB&& lb) {
     }
   }
   return acc;
+}
+
+// ---------------------------------------------------------------------------
+// Register-blocked tiles: one wave computes RT x CT output tiles of 16x16,
+// loading each A fragment once per k-step for CT tiles and each B fragment once
+// for RT tiles (LDS / L1 traffic per MFMA drops by ~RT*CT/(RT+CT)).  A: RT*16
+// rows, K contiguous, row stride lda; B: CT*16 output columns, K contiguous,
+// stride ldb.  Optional lo parts (same layout) add hi*lo and lo*hi products.
+// ---------------------------------------------------------------------------
+template <typename E, int K, int RT, int CT, bool ALO, bool BLO>
+__device__ __forceinline__ void mm_blk(f32x4 (&acc)[RT][CT], const E* A, const E* Al, int lda, const E* B,
+                                       const E* Bl, int ldb) {
+  using M = Mma<E>;
+  const int lane = lane_id();
+  const int r = lane & 15, kq = (lane >> 4) * M::KPL;
+  constexpr bool PART = K % M::KS != 0;
+  static_assert(!PART || K < M::KS, "K must be a multiple of the MFMA k-extent or smaller");
+  const bool kv = !PART || kq < K;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += M::KS) {
+    typename M::frag fa[RT], fal[RT], fb[CT], fbl[CT];
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      fa[i] = kv ? M::load(A + (i * 16 + r) * lda + kq + k0) : M::zero();
+      if constexpr (ALO) fal[i] = kv ? M::load(Al + (i * 16 + r) * lda + kq + k0) : M::zero();
+    }
+#pragma unroll
+    for (int j = 0; j < CT; ++j) {
+      fb[j] = kv ? M::load(B + (j * 16 + r) * ldb + kq + k0) : M::zero();
+      if constexpr (BLO) fbl[j] = kv ? M::load(Bl + (j * 16 + r) * ldb + kq + k0) : M::zero();
+    }
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int j = 0; j < CT; ++j) {
+        acc[i][j] = M::mma(fa[i], fb[j], acc[i][j]);
+        if constexpr (BLO) acc[i][j] = M::mma(fa[i], fbl[j], acc[i][j]);
+        if constexpr (ALO) acc[i][j] = M::mma(fal[i], fb[j], acc[i][j]);
+      }
+  }
+}
+
+template <int RT, int CT>
+__device__ __forceinline__ void zero_blk(f32x4 (&acc)[RT][CT]) {
+#pragma unroll
+  for (int i = 0; i < RT; ++i)
+#pragma unroll
+    for (int j = 0; j < CT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // loaders
