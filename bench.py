@@ -138,6 +138,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="train", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-heads", type=int, default=2, help="q/k heads in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times (the reference for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters of rocprofv3) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -146,6 +149,15 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calib:
+        src = torch.empty(args.copy_calib << 20, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_calib << 20, "repeats": 3}))
+        return
 
     import gated_delta_rule_conv1d_amd as gdn
     import synth

@@ -43,9 +43,9 @@ struct StateBwdSmem {
   E Ptl[LO ? C : 1][LDCE];
   E Ktil[C][LDQ];
   E Ktill[LO ? C : 1][LDQ];  // lo part of K~
-  E QW[D][LD2C];             // [ (Gam q)^T | -Wk^T ]
+  E QW[D][LD2C];             // [ (Gam q)^T | Wk^T ]
   E Qlo[LO ? D : 1][LDCE];   // lo part of (Gam q)^T
-  E Wklo[LO ? D : 1][LDCE];  // lo part of -Wk^T
+  E Wklo[LO ? D : 1][LDCE];  // lo part of Wk^T
   E OW[DVT][LD2C];           // [ dO^T | dW^T ]
   E dWlo[LO ? DVT : 1][LDCE];
   E dHt[DVT][LDQ];
@@ -88,43 +88,35 @@ __global__ __launch_bounds__(kChunkThreads) void state_bwd_kernel(ChunkArgs a) {
       const int t = w + kChunkWaves * i;
       if (t < NHT) {
         const int rt = t / NCT, ct = t % NCT;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int c = ct * 16 + acc_col(), r = rt * 16 + acc_row(e);
-          split_store<E>(&sm.dHt[c][r], &sm.dHtl[0][0] + c * S::LDQ + r, dH[i][e]);
-        }
+        const int c = ct * 16 + acc_col(), r = rt * 16 + acc_row(0);
+        st4_split<E>(&sm.dHt[c][r], &sm.dHtl[0][0] + c * S::LDQ + r, dH[i]);
       }
     }
   };
 
-  // next chunk's tiles, staged in registers
+  // next chunk's tiles, staged in registers (all pre-transposed by the
+  // preparation pass except dO, which is gathered column-wise)
   TileRegs<float, C, C> pP;
-  TileRegs<E, D, C> pKt, pKtl;
-  TileRegs<E, C, D> pQ, pWk, pWkl;
-  TileRegs<E, C, DVT> pO;
+  TileRegs<E, C, D> pKh, pKl;
+  TileRegs<E, D, C> pWh, pWl, pQh, pQl;
+  ColRegs<E, C, DVT> pO;
   TileRegs<float, 1, C> pG;
-  float qsc[TileRegs<E, C, D>::N];
-  int ptok = 0, plen = 0;
+  int plen = 0;
   auto prefetch = [&](int ci) {
     const int4 ent = chunk_entry(a.table, ci);
-    ptok = ent.y;
     plen = ent.z;
     const int64_t slot = (int64_t)ci * a.Hv + h;
-    pP.load(a.P + slot * C * C, C, C);
-    pKt.load((const E*)a.Kt + slot * D * C, C, D);
-    pWk.load((const E*)a.Wk + slot * C * D, D, C);
+    pP.load(a.Ptr + slot * C * C, C, C);
+    pKh.load((const E*)a.Krh + slot * C * D, D, C);
+    pWh.load((const E*)a.Wth + slot * D * C, C, D);
+    pQh.load((const E*)a.Qth + slot * D * C, C, D);
     if constexpr (LO) {
-      pKtl.load((const E*)a.Ktl + slot * D * C, C, D);
-      pWkl.load((const E*)a.Wkl + slot * C * D, D, C);
+      pKl.load((const E*)a.Krl + slot * C * D, D, C);
+      pWl.load((const E*)a.Wtl + slot * D * C, C, D);
+      pQl.load((const E*)a.Qtl + slot * D * C, C, D);
     }
-    pQ.load((const E*)a.q + (int64_t)ptok * a.sqk + (int64_t)j * D, a.sqk, plen);
-    pO.load((const E*)a.d_o + (int64_t)ptok * a.Hv * D + (int64_t)h * D + col0, (int64_t)a.Hv * D, plen);
+    pO.load((const E*)a.d_o + (int64_t)ent.y * a.Hv * D + (int64_t)h * D + col0, (int64_t)a.Hv * D, plen);
     pG.load(a.gam + slot * C, C, 1);
-#pragma unroll
-    for (int i = 0; i < TileRegs<E, C, D>::N; ++i) {  // raw gamma of each q row; exponentiated at commit
-      const int r = pQ.row_of(i);
-      qsc[i] = r < C ? a.gam[slot * C + r] : 0.f;
-    }
   };
 
   const int c0 = a.seq_chunk0[n], c1 = a.seq_chunk0[n + 1];
@@ -134,17 +126,16 @@ __global__ __launch_bounds__(kChunkThreads) void state_bwd_kernel(ChunkArgs a) {
     const int len = plen;
     const int64_t slot = (int64_t)ci * a.Hv + h;
     __syncthreads();  // the previous chunk is done with the LDS tiles
-    pP.template store_t<E>(&sm.Pt[0][0], S::LDCE, LO ? &sm.Ptl[0][0] : nullptr, S::LDCE);
-    pKt.template store_t<E>(&sm.Ktil[0][0], S::LDQ);
-    pWk.template store_t<E>(&sm.QW[0][C], S::LD2C, nullptr, 0, nullptr, -1.f);
+    pP.template store_split<E>(&sm.Pt[0][0], LO ? &sm.Ptl[0][0] : nullptr, S::LDCE);
+    pKh.store(&sm.Ktil[0][0], S::LDQ);
+    pWh.store(&sm.QW[0][C], S::LD2C);
+    pQh.store(&sm.QW[0][0], S::LD2C);
     if constexpr (LO) {
-      pKtl.template store_t<E>(&sm.Ktill[0][0], S::LDQ);
-      pWkl.template store_t<E>(&sm.Wklo[0][0], S::LDCE, nullptr, 0, nullptr, -1.f);
+      pKl.store(&sm.Ktill[0][0], S::LDQ);
+      pWl.store(&sm.Wklo[0][0], S::LDCE);
+      pQl.store(&sm.Qlo[0][0], S::LDCE);
     }
-#pragma unroll
-    for (int i = 0; i < TileRegs<E, C, D>::N; ++i) qsc[i] = __expf(qsc[i]);
-    pQ.template store_t<E>(&sm.QW[0][0], S::LD2C, LO ? &sm.Qlo[0][0] : nullptr, S::LDCE, qsc);
-    pO.template store_t<E>(&sm.OW[0][0], S::LD2C);
+    pO.store(&sm.OW[0][0], S::LD2C);
     pG.store(&sm.gam[0], C);
     {  // gradient w.r.t. the state leaving this chunk
       float* dst = a.dHn + slot * D * D;
@@ -173,10 +164,9 @@ __global__ __launch_bounds__(kChunkThreads) void state_bwd_kernel(ChunkArgs a) {
       for (int e = 0; e < 4; ++e) acc[e] = a.scale * p[e] + kd[e];
       store_tile<float>(dWg, D, rt * 16, col0 + ct * 16, acc, C);
       store_tile_t(dWtg, C, rt * 16, col0 + ct * 16, acc);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = ct * 16 + acc_col(), r = rt * 16 + acc_row(e);
-        split_store<E>(&sm.OW[c][C + r], &sm.dWlo[0][0] + c * S::LDCE + r, acc[e]);
+      {
+        const int c = ct * 16 + acc_col(), r = rt * 16 + acc_row(0);
+        st4_split<E>(&sm.OW[c][C + r], &sm.dWlo[0][0] + c * S::LDCE + r, acc);
       }
     }
     __syncthreads();
@@ -194,7 +184,7 @@ __global__ __launch_bounds__(kChunkThreads) void state_bwd_kernel(ChunkArgs a) {
           y2 = mm_tile<E, C>(y2, &sm.Wklo[rt * 16][0], S::LDCE, &sm.OW[ct * 16][C], S::LD2C);
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dH[i][e] = gl * dH[i][e] + a.scale * y1[e] + y2[e];
+        for (int e = 0; e < 4; ++e) dH[i][e] = gl * dH[i][e] + a.scale * y1[e] - y2[e];
       }
     }
     write_dHt();  // the dW pass (the only reader of dHt) is over for every wave
@@ -771,7 +761,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsPlan {
   size_t table, seq0, Wk, U, P, Kt, gam, end_fwd;
-  size_t Wkl, Ktl, Hc, W, dHn, dW, dWt, dT, dWkt, dQs, dKh, dP, hdot, end_bwd;
+  size_t Ptr, Krh, Krl, Wth, Wtl, Qth, Qtl, Hc, W, dHn, dW, dWt, dT, dWkt, dQs, dKh, dP, hdot, end_bwd;
 };
 
 static WsPlan plan(const gdn_shape* s) {
@@ -787,8 +777,13 @@ static WsPlan plan(const gdn_shape* s) {
   p.Kt = o; o = align256(o + M * Hv * D * C * es);
   p.gam = o; o = align256(o + M * Hv * C * 4);
   p.end_fwd = o;
-  p.Wkl = o; o = align256(o + M * Hv * C * D * es);
-  p.Ktl = o; o = align256(o + M * Hv * D * C * es);
+  p.Ptr = o; o = align256(o + M * Hv * C * C * 4);
+  p.Krh = o; o = align256(o + M * Hv * C * D * es);
+  p.Krl = o; o = align256(o + M * Hv * C * D * es);
+  p.Wth = o; o = align256(o + M * Hv * D * C * es);
+  p.Wtl = o; o = align256(o + M * Hv * D * C * es);
+  p.Qth = o; o = align256(o + M * Hv * D * C * es);
+  p.Qtl = o; o = align256(o + M * Hv * D * C * es);
   p.Hc = o; o = align256(o + M * Hv * D * D * 4);
   p.W = o; o = align256(o + M * Hv * C * D * 4);
   p.dHn = o; o = align256(o + M * Hv * D * D * 4);
@@ -817,8 +812,13 @@ static void fill_ws(ChunkArgs& a, const gdn_shape* s, void* ws) {
   a.P = (float*)(b + p.P);
   a.Kt = b + p.Kt;
   a.gam = (float*)(b + p.gam);
-  a.Wkl = b + p.Wkl;
-  a.Ktl = b + p.Ktl;
+  a.Ptr = (float*)(b + p.Ptr);
+  a.Krh = b + p.Krh;
+  a.Krl = b + p.Krl;
+  a.Wth = b + p.Wth;
+  a.Wtl = b + p.Wtl;
+  a.Qth = b + p.Qth;
+  a.Qtl = b + p.Qtl;
   a.Hc = (float*)(b + p.Hc);
   a.W = (float*)(b + p.W);
   a.dHn = (float*)(b + p.dHn);

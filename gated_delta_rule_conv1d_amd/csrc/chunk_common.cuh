@@ -41,8 +41,14 @@ struct ChunkArgs {
   float* U;                   // [slot][C][D]
   float* P;                   // [slot][C][C]
   void* Kt;                   // [slot][D][C]
-  void* Wkl;                  // [slot][C][D]  lo part of Wk (backward only)
-  void* Ktl;                  // [slot][D][C]  lo part of Kt (backward only)
+  // backward only: operands of the reverse state pass, transposed once per chunk
+  float* Ptr;                 // [slot][C][C]  P^T
+  void* Krh;                  // [slot][C][D]  rows e_s k_s (hi)
+  void* Krl;                  //               (lo)
+  void* Wth;                  // [slot][D][C]  Wk^T (hi)
+  void* Wtl;                  //               (lo)
+  void* Qth;                  // [slot][D][C]  (Gam_r q_r)^T (hi)
+  void* Qtl;                  //               (lo)
   float* gam;                 // [slot][C]
   float* Hc;                  // [slot][D][D]  state entering the chunk
   float* W;                   // [slot][C][D]  W = U - Wk Hc
@@ -87,6 +93,27 @@ __device__ __forceinline__ void store_tile(E* base, int64_t ld, int r0, int c0, 
 // (each lane writes 4 consecutive rows = one 16-byte vector for float)
 __device__ __forceinline__ void store_tile_t(float* dst, int64_t ld, int r0, int c0, f32x4 v) {
   *reinterpret_cast<float4*>(dst + (int64_t)(c0 + acc_col()) * ld + r0 + acc_row(0)) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// the 4 accumulator values of a lane (consecutive rows r..r+3 of one column)
+// written to hi[0..3] (and lo[0..3]) -- one 8-byte (bf16) or 16-byte store each
+template <typename E>
+__device__ __forceinline__ void st4_split(E* hi, E* lo, f32x4 v) {
+  if constexpr (sizeof(E) == 2) {
+    uint2 h, l;
+    uint16_t* hh = reinterpret_cast<uint16_t*>(&h);
+    uint16_t* ll = reinterpret_cast<uint16_t*>(&l);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16 b = f2bf(v[i]);
+      hh[i] = b;
+      ll[i] = f2bf(v[i] - bf2f(b));
+    }
+    *reinterpret_cast<uint2*>(hi) = h;
+    if constexpr (Split<E>::on) *reinterpret_cast<uint2*>(lo) = l;
+  } else {
+    *reinterpret_cast<float4*>(hi) = make_float4(v[0], v[1], v[2], v[3]);
+  }
 }
 
 // copy a [R][Ccols] row-major E tile between global (dense, ld = Ccols) and LDS
@@ -300,8 +327,44 @@ struct TileRegs {
       if (e < TOTAL) {
         const int row = e / PER_ROW, c = (e % PER_ROW) * V;
         const float* f = reinterpret_cast<const float*>(&r[i]);
+        st4_split<E>(hi + row * lds + c, lo + row * lds + c, f32x4{f[0], f[1], f[2], f[3]});
+      }
+    }
+  }
+};
+
+// Register staging of a [R][COLS] tile read column-wise: each slot holds V
+// consecutive rows of one column, so store() writes the transposed tile
+// (dst[c * lds + r]) with one 16-byte store per slot, and the loads of a wave
+// walk along rows (coalesced for COLS >= 32).
+template <typename T, int R, int COLS>
+struct ColRegs {
+  static constexpr int V = 16 / (int)sizeof(T);
+  static constexpr int TOTAL = COLS * (R / V);
+  static constexpr int N = (TOTAL + kChunkThreads - 1) / kChunkThreads;
+  uint4 r[N];
+  __device__ __forceinline__ void load(const T* g, int64_t ld, int rows_valid) {
 #pragma unroll
-        for (int u = 0; u < V; ++u) split_store<E>(hi + row * lds + c + u, lo + row * lds + c + u, f[u]);
+    for (int i = 0; i < N; ++i) {
+      const int e = threadIdx.x + i * kChunkThreads;
+      T* v = reinterpret_cast<T*>(&r[i]);
+#pragma unroll
+      for (int u = 0; u < V; ++u) v[u] = from_f<T>(0.f);
+      if (e < TOTAL) {
+        const int c = e % COLS, r0 = (e / COLS) * V;
+#pragma unroll
+        for (int u = 0; u < V; ++u)
+          if (r0 + u < rows_valid) v[u] = g[(int64_t)(r0 + u) * ld + c];
+      }
+    }
+  }
+  __device__ __forceinline__ void store(T* s, int lds) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int e = threadIdx.x + i * kChunkThreads;
+      if (e < TOTAL) {
+        const int c = e % COLS, r0 = (e / COLS) * V;
+        *reinterpret_cast<uint4*>(s + c * lds + r0) = r[i];
       }
     }
   }

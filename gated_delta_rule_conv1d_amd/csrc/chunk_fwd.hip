@@ -140,6 +140,7 @@ __global__ __launch_bounds__(kChunkThreads) void prep_kernel(ChunkArgs a) {
           sm.Am[r][s] = (s < r) ? sm.beta[r] * dd * sm.Sk[r][s] : 0.f;
         }
         store_tile<float>(Pg, C, rt * 16, ct * 16, pv, C);
+        if constexpr (LO_OUT) store_tile_t(a.Ptr + slot * C * C, C, rt * 16, ct * 16, pv);
       }
     }
     __syncthreads();
@@ -176,18 +177,15 @@ __global__ __launch_bounds__(kChunkThreads) void prep_kernel(ChunkArgs a) {
         if constexpr (Split<E>::on)
           acc = mm_tile<E, C>(acc, &sm.TBl[rt * 16][0], S::LDCE, &sm.Kt[ct * 16][0], S::LDCE);
         store_tile<E>(Wg, D, rt * 16, ct * 16, acc, C);
-        if constexpr (LO_OUT && Split<E>::on) {
-          f32x4 lo;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) lo[e] = acc[e] - to_f<E>(from_f<E>(acc[e]));
-          store_tile<E>((E*)a.Wkl + slot * C * D, D, rt * 16, ct * 16, lo, C);
+        if constexpr (LO_OUT) {  // Wk^T [D][C], hi / lo
+          const int64_t o = slot * D * C + (int64_t)(ct * 16 + acc_col()) * C + rt * 16 + acc_row(0);
+          st4_split<E>((E*)a.Wth + o, (E*)a.Wtl + o, acc);
         }
       }
     }
     // Kt_e[d][s] = e^{gamma_last - gamma_s} k_s[d]  (s < len), 0 past len
     {
       E* Kg = (E*)a.Kt + slot * D * C;
-      E* Klg = (E*)a.Ktl + slot * D * C;
       const float glast = sm.gam[len - 1];
       for (int e = tid; e < D * (C / V); e += kChunkThreads) {
         const int d = e / (C / V), s0 = (e % (C / V)) * V;
@@ -198,10 +196,33 @@ __global__ __launch_bounds__(kChunkThreads) void prep_kernel(ChunkArgs a) {
           val[i] = (s < len) ? to_f<E>(sm.Kt[d][s]) * __expf(glast - sm.gam[s]) : 0.f;
         }
         Vec<E>::store(Kg + d * C + s0, val);
-        if constexpr (LO_OUT && Split<E>::on) {
+      }
+      if constexpr (LO_OUT) {
+        // rows e_s k_s [C][D] and (Gam_r q_r)^T [D][C], hi / lo, for the reverse state pass
+        for (int e = tid; e < C * (D / V); e += kChunkThreads) {
+          const int s = e / (D / V), c0 = (e % (D / V)) * V;
+          const float es = (s < len) ? __expf(glast - sm.gam[s]) : 0.f;
+          float val[V], lo[V];
 #pragma unroll
-          for (int i = 0; i < V; ++i) val[i] -= to_f<E>(from_f<E>(val[i]));
-          Vec<E>::store(Klg + d * C + s0, val);
+          for (int i = 0; i < V; ++i) {
+            val[i] = es * to_f<E>(sm.Ks[s][c0 + i]);
+            lo[i] = val[i] - to_f<E>(from_f<E>(val[i]));
+          }
+          const int64_t o = slot * C * D + (int64_t)s * D + c0;
+          Vec<E>::store((E*)a.Krh + o, val);
+          if constexpr (Split<E>::on) Vec<E>::store((E*)a.Krl + o, lo);
+        }
+        for (int e = tid; e < D * (C / V); e += kChunkThreads) {
+          const int d = e % D, s0 = (e / D) * V;
+          float val[V], lo[V];
+#pragma unroll
+          for (int i = 0; i < V; ++i) {
+            val[i] = __expf(sm.gam[s0 + i]) * to_f<E>(sm.Qs[s0 + i][d]);
+            lo[i] = val[i] - to_f<E>(from_f<E>(val[i]));
+          }
+          const int64_t o = slot * D * C + (int64_t)d * C + s0;
+          Vec<E>::store((E*)a.Qth + o, val);
+          if constexpr (Split<E>::on) Vec<E>::store((E*)a.Qtl + o, lo);
         }
       }
     }
@@ -255,11 +276,8 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
       const int t = w + kChunkWaves * i;
       if (t < NHT) {
         const int rt = t / NCT, ct = t % NCT;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int c = ct * 16 + acc_col(), r = rt * 16 + acc_row(e);
-          split_store<E>(&sm.Ht[c][r], &sm.Htl[0][0] + c * S::LDQ + r, Hr[i][e]);
-        }
+        const int c = ct * 16 + acc_col(), r = rt * 16 + acc_row(0);
+        st4_split<E>(&sm.Ht[c][r], &sm.Htl[0][0] + c * S::LDQ + r, Hr[i]);
       }
     }
   };
@@ -325,10 +343,10 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
         if constexpr (LO) x = mm_tile<E, D>(x, &sm.Wk[rt * 16][0], S::LDQ, &sm.Htl[ct * 16][0], S::LDQ);
         f32x4 wv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = rt * 16 + acc_row(e), c = ct * 16 + acc_col();
-          wv[e] = sm.U[r][c] - x[e];
-          split_store<E>(&sm.Wt[c][r], &sm.Wtl[0][0] + c * S::LDCE + r, wv[e]);
+        for (int e = 0; e < 4; ++e) wv[e] = sm.U[rt * 16 + acc_row(e)][ct * 16 + acc_col()] - x[e];
+        {
+          const int c = ct * 16 + acc_col(), r = rt * 16 + acc_row(0);
+          st4_split<E>(&sm.Wt[c][r], &sm.Wtl[0][0] + c * S::LDCE + r, wv);
         }
         if constexpr (!OUT) store_tile<float>(a.W + slot * C * D, D, rt * 16, col0 + ct * 16, wv, C);
         if constexpr (OUT) {
