@@ -428,11 +428,15 @@ struct GradBSmem {
   static constexpr int LD2C = 2 * C + Pad<E>::E16;
   static constexpr int LDCF = C + 4;
   static constexpr int NT = C / 16, ND = D / 16;
+  static constexpr int LDV = D + Pad<E>::E16;
   E QKt[D][LD2C];      // [Q^T | K^T]
   float Skk[C][LDCF];  // K K^T
-  float Am[C][LDCF];   // A, then dA
-  float Tm[C][LDCF];
-  float Tt[C][LDCF];
+  union {
+    float Am[C][LDCF];  // A (solve), later dA
+    E Vs[C][LDV];       // v rows, between the two
+  } av;
+  float Tm[C][LDCF];   // T, later P
+  float Tt[C][LDCF];   // T^T, later dP
   union U {
     float Xf[D][LDCF];                            // dW^T or dWk^T
     struct { float dT[C][LDCF]; float M1t[C][LDCF]; } m;
@@ -490,6 +494,8 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
     const int h = j * a.G + gi;
     const int64_t slot = (int64_t)ci * a.Hv + h;
     const E* vg = (const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)h * D;
+    TileRegs<E, C, D> pV;  // in flight during the solve
+    pV.load(vg, a.sv, len);
     for (int e = tid; e < C; e += kChunkThreads) {
       const float gm = a.gam[slot * C + e];
       sm.gam[e] = gm;
@@ -501,10 +507,10 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
     // A = strict_lower(beta_r D_rs k_r.k_s)
     for (int e = tid; e < C * C; e += kChunkThreads) {
       const int r = e / C, s = e % C;
-      sm.Am[r][s] = (s < r) ? sm.beta[r] * __expf(sm.gam[r] - sm.gam[s]) * sm.Skk[r][s] : 0.f;
+      sm.av.Am[r][s] = (s < r) ? sm.beta[r] * __expf(sm.gam[r] - sm.gam[s]) * sm.Skk[r][s] : 0.f;
     }
     __syncthreads();
-    unit_lower_inverse<C, S::LDCF>(sm.Am, sm.Tm, sm.Tt, sm.r.Xs);
+    unit_lower_inverse<C, S::LDCF>(sm.av.Am, sm.Tm, sm.Tt, sm.r.Xs);
 
     auto ta = [&](int rt) {
       return [&, rt](int r, int k, float* o) { ld_row<float, KPL>(&sm.Tt[rt * 16 + r][k], o); };
@@ -516,6 +522,7 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
     {
       TileRegs<float, D, C> rX;
       rX.load(a.dWt + slot * D * C, C, D);
+      pV.store(&sm.av.Vs[0][0], S::LDV);
       rX.store(&sm.r.Xf[0][0], S::LDCF);
     }
     __syncthreads();
@@ -532,7 +539,7 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
         for (int e = 0; e < 4; ++e) {
           const int r = rt * 16 + acc_row(e), c = ct * 16 + acc_col();
           dvv[e] = sm.beta[r] * xu[e];
-          pu[e] = xu[e] * (r < len ? to_f<E>(vg[(int64_t)r * a.sv + c]) : 0.f);
+          pu[e] = xu[e] * to_f<E>(sm.av.Vs[r][c]);
         }
         store_tile<E>(dvg, a.sv, rt * 16, ct * 16, dvv, len);
 #pragma unroll
@@ -574,9 +581,12 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
     }
     __syncthreads();
     // M1 = dT T^T (fp32 MFMA), stored transposed; dA = strict_lower(-T^T M1)
+    TileRegs<float, C, C> pP, pdP;  // in flight during dA
     {
       TileRegs<float, C, C> rT;
       rT.load(a.dT + slot * C * C, C, C);
+      pP.load(a.P + slot * C * C, C, C);
+      pdP.load(a.dP + slot * C * C, C, C);
       rT.store(&sm.r.m.dT[0][0], S::LDCF);
     }
     __syncthreads();
@@ -593,13 +603,14 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = rt * 16 + acc_row(e), s = ct * 16 + acc_col();
-        sm.Am[r][s] = (s < r && r < len) ? -m[e] : 0.f;
+        sm.av.Am[r][s] = (s < r && r < len) ? -m[e] : 0.f;
       }
     }
     __syncthreads();
+    pP.store(&sm.Tm[0][0], S::LDCF);  // T is no longer needed
+    pdP.store(&sm.Tt[0][0], S::LDCF);
+    __syncthreads();
     // C x C pass: A~, dS, and the dgamma / dbeta terms of A and P
-    const float* Pg = a.P + slot * C * C;
-    const float* dPg = a.dP + slot * C * C;
     for (int t = w; t < NT * NT; t += kChunkWaves) {
       const int rt = t / NT, ct = t % NT;
       float rb[4], ra[4], rp[4], ca = 0.f, cp = 0.f;
@@ -608,11 +619,11 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
         const int r = rt * 16 + acc_row(e), s = ct * 16 + acc_col();
         const float skk = sm.Skk[r][s];
         const float dd = (s <= r) ? __expf(sm.gam[r] - sm.gam[s]) : 0.f;
-        const float dA = sm.Am[r][s];
+        const float dA = sm.av.Am[r][s];
         const float At = dA * sm.beta[r] * dd;
         const float AdA = At * skk;
-        const float dP = dPg[r * C + s];
-        const float PdP = dP * Pg[r * C + s];
+        const float dP = sm.Tt[r][s];
+        const float PdP = dP * sm.Tm[r][s];
         rb[e] = dA * dd * skk;
         ra[e] = AdA;
         rp[e] = PdP;
