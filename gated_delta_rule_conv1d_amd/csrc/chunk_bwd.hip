@@ -771,7 +771,7 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsPlan {
-  size_t table, seq0, Wk, U, P, Kt, gam, end_fwd;
+  size_t table, seq0, Wk, U, P, Kt, Ktl, gam, end_fwd;
   size_t Ptr, Krh, Krl, Wth, Wtl, Qth, Qtl, Hc, W, dHn, dW, dWt, dT, dWkt, dQs, dKh, dP, hdot, end_bwd;
 };
 
@@ -786,6 +786,7 @@ static WsPlan plan(const gdn_shape* s) {
   p.U = o; o = align256(o + M * Hv * C * D * 4);
   p.P = o; o = align256(o + M * Hv * C * C * 4);
   p.Kt = o; o = align256(o + M * Hv * D * C * es);
+  p.Ktl = o; o = align256(o + (es == 2 ? M * Hv * D * C * es : 0));
   p.gam = o; o = align256(o + M * Hv * C * 4);
   p.end_fwd = o;
   p.Ptr = o; o = align256(o + M * Hv * C * C * 4);
@@ -822,6 +823,7 @@ static void fill_ws(ChunkArgs& a, const gdn_shape* s, void* ws) {
   a.U = (float*)(b + p.U);
   a.P = (float*)(b + p.P);
   a.Kt = b + p.Kt;
+  a.Ktl = b + p.Ktl;
   a.gam = (float*)(b + p.gam);
   a.Ptr = (float*)(b + p.Ptr);
   a.Krh = b + p.Krh;

@@ -40,7 +40,8 @@ struct ChunkArgs {
   void* Wk;                   // [slot][C][D]
   float* U;                   // [slot][C][D]
   float* P;                   // [slot][C][C]
-  void* Kt;                   // [slot][D][C]
+  void* Kt;                   // [slot][D][C]  (e_s k_s)^T, e_s = e^{gamma_last - gamma_s}
+  void* Ktl;                  //               its lo part (bf16 only)
   // backward only: operands of the reverse state pass, transposed once per chunk
   float* Ptr;                 // [slot][C][C]  P^T
   void* Krh;                  // [slot][C][D]  rows e_s k_s (hi)
@@ -252,6 +253,7 @@ struct StateSmem {
   E Wk[C][LDQ];
   E Q[OUT ? C : 1][LDQ];
   E Kt[D][LDCE];
+  E Ktl[LO ? D : 1][LDCE];
   E P[OUT ? C : 1][LDCE];
   E Pl[OUT && LO ? C : 1][LDCE];
   E Ht[DVT][LDQ];

@@ -189,13 +189,15 @@ __global__ __launch_bounds__(kChunkThreads) void prep_kernel(ChunkArgs a) {
       const float glast = sm.gam[len - 1];
       for (int e = tid; e < D * (C / V); e += kChunkThreads) {
         const int d = e / (C / V), s0 = (e % (C / V)) * V;
-        float val[V];
+        float val[V], lo[V];
 #pragma unroll
         for (int i = 0; i < V; ++i) {
           const int s = s0 + i;
           val[i] = (s < len) ? to_f<E>(sm.Kt[d][s]) * __expf(glast - sm.gam[s]) : 0.f;
+          lo[i] = val[i] - to_f<E>(from_f<E>(val[i]));
         }
         Vec<E>::store(Kg + d * C + s0, val);
+        if constexpr (Split<E>::on) Vec<E>::store((E*)a.Ktl + slot * D * C + d * C + s0, lo);
       }
       if constexpr (LO_OUT) {
         // rows e_s k_s [C][D] and (Gam_r q_r)^T [D][C], hi / lo, for the reverse state pass
@@ -285,6 +287,7 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
   // next chunk's tiles, staged in registers
   TileRegs<E, C, D> pWk;
   TileRegs<E, D, C> pKt;
+  TileRegs<E, LO ? D : 1, LO ? C : 16 / (int)sizeof(E)> pKtl;
   TileRegs<E, OUT ? C : 16, OUT ? D : 16 / (int)sizeof(E)> pQ;
   TileRegs<float, OUT ? C : 1, OUT ? C : 4> pP;
   TileRegs<float, C, DVT> pU;
@@ -297,6 +300,7 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
     const int64_t slot = (int64_t)ci * a.Hv + h;
     pWk.load((const E*)a.Wk + slot * C * D, D, C);
     pKt.load((const E*)a.Kt + slot * D * C, C, D);
+    if constexpr (LO) pKtl.load((const E*)a.Ktl + slot * D * C, C, D);
     if constexpr (OUT) {
       pQ.load((const E*)a.q + (int64_t)ptok * a.sqk + (int64_t)j * D, a.sqk, plen);
       pP.load(a.P + slot * C * C, C, C);
@@ -314,6 +318,7 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
     __syncthreads();  // the previous chunk is done with the LDS tiles
     pWk.store(&sm.Wk[0][0], S::LDQ);
     pKt.store(&sm.Kt[0][0], S::LDCE);
+    if constexpr (LO) pKtl.store(&sm.Ktl[0][0], S::LDCE);
     if constexpr (OUT) {
       pQ.store(&sm.Q[0][0], S::LDQ);
       pP.template store_split<E>(&sm.P[0][0], &sm.Pl[0][0], S::LDCE);
@@ -366,7 +371,10 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
       if (t < NHT) {
         const int rt = t / NCT, ct = t % NCT;
         f32x4 y = mm_tile<E, C>(zero4(), &sm.Kt[rt * 16][0], S::LDCE, &sm.Wt[ct * 16][0], S::LDCE);
-        if constexpr (LO) y = mm_tile<E, C>(y, &sm.Kt[rt * 16][0], S::LDCE, &sm.Wtl[ct * 16][0], S::LDCE);
+        if constexpr (LO) {
+          y = mm_tile<E, C>(y, &sm.Kt[rt * 16][0], S::LDCE, &sm.Wtl[ct * 16][0], S::LDCE);
+          y = mm_tile<E, C>(y, &sm.Ktl[rt * 16][0], S::LDCE, &sm.Wt[ct * 16][0], S::LDCE);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) Hr[i][e] = gl * Hr[i][e] + y[e];
       }

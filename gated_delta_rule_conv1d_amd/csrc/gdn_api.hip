@@ -75,7 +75,8 @@ gdn_status gdn_conv1d(const gdn_shape* shape, const void* x, const void* w_conv,
   gdn_status st = check_shape(shape);
   if (st != GDN_OK) return st;
   if (width < 2 || width > 4) return GDN_ERR_UNSUPPORTED;
-  if (!x || !w_conv || !cu_seqlens || !y || x == y) return GDN_ERR_INVALID_ARG;
+  const bool any = shape->total_tokens > 0;  // token-indexed pointers may be null for an empty row
+  if (!w_conv || !cu_seqlens || (any && (!x || !y || x == y))) return GDN_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(y)) return GDN_ERR_INVALID_ARG;
   if (!(l2_eps >= 0.f)) return GDN_ERR_INVALID_ARG;
   if (!run_conv_fwd(shape, x, w_conv, width, cu_seqlens, l2_eps, y, (hipStream_t)stream)) return GDN_ERR_UNSUPPORTED;
@@ -93,8 +94,9 @@ gdn_status gdn_conv1d_bwd(const gdn_shape* shape, const void* dy, const void* x,
   gdn_status st = check_shape(shape);
   if (st != GDN_OK) return st;
   if (width < 2 || width > 4) return GDN_ERR_UNSUPPORTED;
-  if (!dy || !x || !w_conv || !cu_seqlens || !dx || !dw_conv) return GDN_ERR_INVALID_ARG;
-  if (!aligned16(dy) || !aligned16(x) || !aligned16(dx) || dx == x || dx == dy) return GDN_ERR_INVALID_ARG;
+  const bool any = shape->total_tokens > 0;
+  if (!w_conv || !cu_seqlens || !dw_conv || (any && (!dy || !x || !dx))) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(dy) || !aligned16(x) || !aligned16(dx) || (any && (dx == x || dx == dy))) return GDN_ERR_INVALID_ARG;
   if (!(l2_eps >= 0.f)) return GDN_ERR_INVALID_ARG;
   if (!ws || !aligned16(ws) || ws_bytes < conv_bwd_ws_bytes(shape, width)) return GDN_ERR_WORKSPACE;
   if (!run_conv_bwd(shape, dy, x, w_conv, width, cu_seqlens, l2_eps, dx, dw_conv, ws, (hipStream_t)stream))
@@ -113,7 +115,8 @@ gdn_status gdn_chunk_fwd(const gdn_shape* shape, const void* q, const void* k, c
   gdn_status st = check_shape(shape);
   if (st != GDN_OK) return st;
   if ((st = check_chunk(shape)) != GDN_OK) return st;
-  if (!q || !k || !v || !g || !beta || !cu_seqlens || !o) return GDN_ERR_INVALID_ARG;
+  const bool any = shape->total_tokens > 0;
+  if (!cu_seqlens || (any && (!q || !k || !v || !g || !beta || !o))) return GDN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return GDN_ERR_INVALID_ARG;
   if (!stride_ok(shape, tok_stride_qk, (int64_t)shape->h_qk * shape->d_k) ||
       !stride_ok(shape, tok_stride_v, (int64_t)shape->h_v * shape->d_v))
@@ -137,7 +140,8 @@ gdn_status gdn_chunk_bwd(const gdn_shape* shape, const void* q, const void* k, c
   gdn_status st = check_shape(shape);
   if (st != GDN_OK) return st;
   if ((st = check_chunk(shape)) != GDN_OK) return st;
-  if (!q || !k || !v || !g || !beta || !cu_seqlens || !d_o || !dq || !dk || !dv || !dg || !dbeta)
+  const bool any = shape->total_tokens > 0;
+  if (!cu_seqlens || (any && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta)))
     return GDN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_o) || !aligned16(dq) || !aligned16(dk) ||
       !aligned16(dv))
@@ -156,7 +160,8 @@ gdn_status gdn_norm_gate(const gdn_shape* shape, const void* o, const void* z, c
                          gdn_stream stream) {
   gdn_status st = check_shape(shape);
   if (st != GDN_OK) return st;
-  if (!o || !z || !w_norm || !y) return GDN_ERR_INVALID_ARG;
+  const bool any = shape->total_tokens > 0;
+  if (!w_norm || (any && (!o || !z || !y))) return GDN_ERR_INVALID_ARG;
   if (!aligned16(o) || !aligned16(z) || !aligned16(w_norm) || !aligned16(y)) return GDN_ERR_INVALID_ARG;
   if (!(eps >= 0.f)) return GDN_ERR_INVALID_ARG;
   if (!run_norm_fwd(shape, o, z, w_norm, eps, y, (hipStream_t)stream)) return GDN_ERR_UNSUPPORTED;
@@ -173,7 +178,8 @@ gdn_status gdn_norm_gate_bwd(const gdn_shape* shape, const void* dy, const void*
                              gdn_stream stream) {
   gdn_status st = check_shape(shape);
   if (st != GDN_OK) return st;
-  if (!dy || !o || !z || !w_norm || !d_o || !dz || !dw_norm) return GDN_ERR_INVALID_ARG;
+  const bool any = shape->total_tokens > 0;
+  if (!w_norm || !dw_norm || (any && (!dy || !o || !z || !d_o || !dz))) return GDN_ERR_INVALID_ARG;
   if (!aligned16(dy) || !aligned16(o) || !aligned16(z) || !aligned16(w_norm) || !aligned16(d_o) || !aligned16(dz))
     return GDN_ERR_INVALID_ARG;
   if (!(eps >= 0.f)) return GDN_ERR_INVALID_ARG;

@@ -306,24 +306,5 @@ __device__ __forceinline__ float group_sum(float v) {  // sum over aligned group
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + __expf(-x)); }
 
-// ---------------------------------------------------------------------------
-// Workspace layout of the chunked recurrence.  Per chunk slot c and v-head h
-// (slot = index in the chunk table, tiles are zero-padded past the chunk's
-// length):
-//   Wk  [C][D]   E   T diag(beta*Gamma) K
-//   U   [C][D]   E   T diag(beta) V
-//   P   [C][C]   E   lower-inclusive (D_rs * q_r.k_s)
-//   Kt  [D][C]   E   (e^{gamma_last - gamma_s} k_s)^T
-//   gam [C]      f32 within-chunk cumulative gate (padding repeats the last)
-// ---------------------------------------------------------------------------
-struct ChunkWs {
-  int32_t* table;      // [max_chunks][4]
-  int32_t* seq_chunk0; // [N+1]
-  void* Wk;
-  void* U;
-  void* P;
-  void* Kt;
-  float* gam;
-};
 
 }  // namespace gdn

@@ -34,7 +34,10 @@
  *    does not end at total_tokens) give undefined results.
  *  - cu_seqlens: int32 [N+1] on the device, cu[0] = 0, cu[N] = T,
  *    non-decreasing; sequence n owns tokens [cu[n], cu[n+1]).  Zero-length
- *    sequences are allowed.
+ *    sequences are allowed, and so is an empty row (T = 0): then the
+ *    token-indexed pointers (x, y, q, k, v, g, beta, o, z and their
+ *    gradients) may be NULL, states are still written (ht = h0 or 0,
+ *    dh0 = dht or 0) and weight gradients are zero.
  *  - Element type of x, y, q, k, v, o, z, w_conv, w_norm and their gradients
  *    is shape->dtype (GDN_F32 = float, GDN_BF16 = bfloat16).  g, beta,
  *    states, dg, dbeta, dw_conv, dw_norm and state gradients are always

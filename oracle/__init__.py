@@ -236,8 +236,8 @@ def layer_bwd(cfg, inp, fwd, dy, bits=64, scale=1.0, dht=None, storage=None):
                        scale=scale, bits=bits)
     res.update(dq=r["dq"], dk=r["dk"], dv=r["dv"], dg=r["dg"], dbeta=r["dbeta"], dh0=r["dh0"])
     T = q.shape[0]
-    dyc = _store(np.concatenate([r["dq"].reshape(T, -1), r["dk"].reshape(T, -1), r["dv"].reshape(T, -1)], axis=1),
-                 storage)
+    dyc = _store(np.concatenate([r["dq"].reshape(T, Hk * dk), r["dk"].reshape(T, Hk * dk),
+                                 r["dv"].reshape(T, Hv * dv)], axis=1), storage)
     dx, dwc = conv1d_bwd(inp["x"], inp["w_conv"], inp["cu"], 2 * Hk * dk, dk, dyc, bits=bits)
     res.update(dx=dx, dw_conv=dwc)
     return res

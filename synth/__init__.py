@@ -128,9 +128,17 @@ def cu_from_lengths(lengths) -> np.ndarray:
 def bf16_bits(a: np.ndarray) -> np.ndarray:
     """float32 -> bf16 bit patterns, round-to-nearest-even (finite inputs)."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32)
-    rounded = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
-    return (rounded >> np.uint32(16)).astype(np.uint16)
+    u = a.reshape(-1).view(np.uint32)
+    out = np.empty(u.shape, dtype=np.uint16)
+    step = 1 << 20  # blocks that stay in cache
+    for i in range(0, u.size, step):
+        ub = u[i:i + step]
+        r = (ub >> np.uint32(16)) & np.uint32(1)
+        r += np.uint32(0x7FFF)
+        r += ub
+        r >>= np.uint32(16)
+        out[i:i + step] = r
+    return out.reshape(a.shape)
 
 
 def bf16_value(bits: np.ndarray) -> np.ndarray:

@@ -98,3 +98,32 @@ def qkv_inputs(cfg: synth.Config, seed=11):
     if cfg.dtype == "bf16":
         q, k, v = (synth.round_bf16(a) for a in (q, k, v))
     return q, k, v
+
+
+def layer_gpu(cfg, inp, layer=None):
+    """The whole layer through GatedDeltaNetLayer (the path bench.py times):
+    forward, and backward when the workload has one."""
+    s = shape_of(cfg)
+    dt = cfg.dtype
+    L = layer or gdn.GatedDeltaNetLayer(s, cfg.width, norm=cfg.norm)
+    t = dict(x=to_dev(inp["x"], dt), w=to_dev(inp["w_conv"], dt), g=f32(inp["g"]), beta=f32(inp["beta"]),
+             cu=torch.from_numpy(inp["cu"]).cuda(),
+             z=to_dev(inp["z"], dt) if "z" in inp else None, wn=to_dev(inp["w_norm"], dt) if "w_norm" in inp else None,
+             h0=f32(inp["h0"]) if "h0" in inp else None)
+    fwd = L.forward(t["x"], t["w"], t["g"], t["beta"], t["cu"], t["z"], t["wn"], t["h0"])
+    bwd = None
+    if cfg.bwd:
+        bwd = L.backward(to_dev(inp["dy"], dt), t["x"], t["w"], t["g"], t["beta"], t["cu"], fwd, t["z"], t["wn"],
+                         t["h0"])
+    torch.cuda.synchronize()
+    return fwd, bwd
+
+
+def channels(cfg, kheads):
+    """Columns of the [T, Cch] conv input that belong to some q/k heads and
+    their v-heads (channel blocks [q | k | v])."""
+    G = cfg.h_v // cfg.h_qk
+    dk, dv, Hk = cfg.d_k, cfg.d_v, cfg.h_qk
+    q = np.concatenate([np.arange(j * dk, (j + 1) * dk) for j in kheads])
+    v = np.concatenate([2 * Hk * dk + np.arange(h * dv, (h + 1) * dv) for j in kheads for h in range(j * G, j * G + G)])
+    return np.concatenate([q, q + Hk * dk, v])

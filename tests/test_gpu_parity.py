@@ -9,7 +9,7 @@ import torch
 import gated_delta_rule_conv1d_amd as gdn
 import oracle
 import synth
-from gpu_util import (TOL, assert_close, f32, host, qkv_inputs, shape_of, small_cfg, to_dev)
+from gpu_util import (TOL, assert_close, f32, host, layer_gpu, qkv_inputs, shape_of, small_cfg, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -145,29 +145,12 @@ def test_chunk_weak_decay_long_range():
 
 
 # ----------------------------------------------------------------------------- whole layer
-def _layer_gpu(cfg, inp):
-    s = shape_of(cfg)
-    dt = cfg.dtype
-    L = gdn.GatedDeltaNetLayer(s, cfg.width, norm=cfg.norm)
-    t = dict(x=to_dev(inp["x"], dt), w=to_dev(inp["w_conv"], dt), g=f32(inp["g"]), beta=f32(inp["beta"]),
-             cu=torch.from_numpy(inp["cu"]).cuda(),
-             z=to_dev(inp["z"], dt) if "z" in inp else None, wn=to_dev(inp["w_norm"], dt) if "w_norm" in inp else None,
-             h0=f32(inp["h0"]) if "h0" in inp else None)
-    fwd = L.forward(t["x"], t["w"], t["g"], t["beta"], t["cu"], t["z"], t["wn"], t["h0"])
-    bwd = None
-    if cfg.bwd:
-        dy = to_dev(inp["dy"], dt) if cfg.norm else to_dev(inp["dy"], dt)
-        bwd = L.backward(dy, t["x"], t["w"], t["g"], t["beta"], t["cu"], fwd, t["z"], t["wn"], t["h0"])
-    torch.cuda.synchronize()
-    return fwd, bwd
-
-
 @pytest.mark.parametrize("norm,h0", [(False, False), (True, True)])
 def test_layer_tiny_full(norm, h0):
     cfg = synth.config("tiny").replace(norm=norm, h0=h0, bwd=True)
     _print_case("layer_tiny", norm=norm, h0=h0)
     inp = synth.make_inputs(cfg)
-    fwd, bwd = _layer_gpu(cfg, inp)
+    fwd, bwd = layer_gpu(cfg, inp)
     ref = oracle.layer_fwd(cfg, inp)
     tol = TOL["f32"]
     assert_close(host(fwd["o"]), ref["o"], tol, "o")
@@ -184,7 +167,7 @@ def test_layer_small_bf16_full():
     cfg = small_cfg(dtype="bf16", d=128, chunk=64, Hk=2, Hv=4, lengths=(300, 1, 64, 65, 130))
     _print_case("layer_small_bf16", lengths=cfg.lengths)
     inp = synth.make_inputs(cfg)
-    fwd, bwd = _layer_gpu(cfg, inp)
+    fwd, bwd = layer_gpu(cfg, inp)
     ref = oracle.layer_fwd(cfg, inp, storage="bf16")
     rb = oracle.layer_bwd(cfg, inp, ref, inp["dy"], storage="bf16")
     tol = TOL["bf16"]

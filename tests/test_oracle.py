@@ -238,6 +238,21 @@ def test_zero_length_sequence_passes_state_through():
     np.testing.assert_array_equal(ht[1], H0[1])
 
 
+def test_empty_row_layer():
+    """T = 0: states pass through (ht = h0), their gradient is dht (here 0
+    when none is given), and the weight gradients are zero sums."""
+    cfg = synth.config("varlen").replace(lengths=(0, 0), varlen_rule=None, h_qk=1, h_v=2, d_k=16, d_v=16,
+                                         chunk=16, bwd=True)
+    inp = synth.make_inputs(cfg)
+    fwd = oracle.layer_fwd(cfg, inp)
+    np.testing.assert_array_equal(fwd["ht"], inp["h0"])
+    dht = np.random.default_rng(5).standard_normal(inp["h0"].shape)
+    b = oracle.layer_bwd(cfg, inp, fwd, inp["dy"], dht=dht)
+    np.testing.assert_array_equal(b["dh0"], dht)
+    assert b["dx"].shape == (0, inp["x"].shape[1])
+    assert not np.any(b["dw_conv"]) and not np.any(b["dw_norm"])
+
+
 @pytest.mark.parametrize("C", [1, 2, 4, 16, 64, 100])
 def test_chunk_size_invariance(C):
     q, k, v, g, beta, cu, H0 = rnd_problem(17, [70, 1, 33, 64], Hk=2, Hv=4, dk=8, dv=6, g_scale=0.3)
