@@ -7,9 +7,9 @@ backward of all three.  Default workload: the training step, 8 sequences x
 8192 tokens packed in one row, 16 q/k heads, 32 v heads, d = 128, bf16.
 
 Prints ONE JSON line with the throughput (tokens/s), the roofline of the
-dominant kernel (per-kernel durations from HIP events on the library's stream,
-taken in a second pass over the same number of steps), and the CPU oracle timed
-on a bounded sample of the same workload.
+dominant kernel (per-kernel durations from HIP events that the library records
+on its stream during the timed steps), and the CPU oracle timed on a bounded
+sample of the same workload (all sequences, --cpu-heads of the q/k heads).
 """
 from __future__ import annotations
 
@@ -47,47 +47,59 @@ def csrc_hash() -> str:
 
 def kernel_bytes(cfg, n_chunks: int, has_h0: bool) -> dict:
     """Algorithmic bytes per launch of each kernel: every input it must read
-    once and every output it must write once (workspace tensors included, at
-    the precision they are stored in)."""
+    once and every output it must write once, workspace tensors included at
+    the precision they are stored in (a q/k tile shared by the G v-heads of a
+    k-head counts once).  Slot = (chunk, v-head); k-slot = (chunk, k-head)."""
     T, N, Hk, Hv, D, C = cfg.T, cfg.N, cfg.h_qk, cfg.h_v, cfg.d_k, cfg.chunk
     es = 2 if cfg.dtype == "bf16" else 4
+    lo = 2 if cfg.dtype == "bf16" else 1        # hi + lo parts of split bf16 operands
     Cch = 2 * Hk * D + Hv * D
     W = cfg.width
-    S = n_chunks * Hv          # (chunk, v-head) slots
-    qk = 2 * T * Hk * D * es
-    v = T * Hv * D * es
-    gb = 2 * T * Hv * 4
-    o = T * Hv * D * es
-    st = N * Hv * D * D * 4
-    wk, kt, u, p, gm = C * D * es, D * C * es, C * D * 4, C * C * 4, C * 4
-    hc, wf = D * D * 4, C * D * 4
-    b = {
+    S, SK = n_chunks * Hv, n_chunks * Hk
+    tile_e, tile_f = C * D * es, C * D * 4    # [C][D] tile in the element type / in fp32
+    cc_f, row_f = C * C * 4, C * 4            # [C][C] fp32 tile / one fp32 row of C
+    dd_f = D * D * 4                          # [D][D] fp32 state
+    qk_in = SK * 2 * tile_e                   # q and k of each k-slot
+    v_in = S * tile_e
+    gb_in = 2 * T * Hv * 4                    # g and beta
+    st = N * Hv * dd_f                        # one state per (sequence, v-head)
+    prep_out = S * (tile_e + tile_f + cc_f + lo * tile_e + row_f)   # Wk, U, P, K~^T (hi, lo), gamma
+    return {
         "conv_fwd": 2 * T * Cch * es + Cch * W * es,
         "conv_bwd": 3 * T * Cch * es + Cch * W * es,
-        "norm_fwd": 3 * o + D * es,
-        "norm_bwd": 5 * o + D * es,
-        "chunk_prep": qk + v + gb + S * (wk + u + p + kt + gm),
-        "chunk_prep_bwd": qk + v + gb + S * (2 * wk + u + p + 2 * kt + gm),
-        "chunk_state_fwd": qk // 2 + S * (wk + kt + u + p + gm) + o + (st if has_h0 else 0) + st,
-        "chunk_state_store": S * (wk + kt + u + gm + hc + wf) + (st if has_h0 else 0),
-        "chunk_state_bwd": qk // 2 + o + S * (p + 2 * kt + 2 * wk + gm + hc + 2 * wf),
-        "chunk_grad_a": qk // 2 + v + T * Hv * 4 + S * (2 * hc + wf + gm + wf + p + 4),
-        "chunk_grad_b": 2 * qk + 2 * v + o + 3 * T * Hv * 4 + S * (2 * wf + p + wf + 2 * hc + p + gm + 4),
+        "norm_fwd": 3 * T * Hv * D * es + D * es,
+        "norm_bwd": 5 * T * Hv * D * es + D * es,
+        "chunk_prep": qk_in + v_in + gb_in + prep_out,
+        # + P^T, K~ rows, Wk^T and (Gamma q)^T for the reverse pass
+        "chunk_prep_bwd": qk_in + v_in + gb_in + prep_out + S * (cc_f + 3 * lo * tile_e),
+        "chunk_state_fwd": SK * tile_e + S * (tile_e + lo * tile_e + tile_f + cc_f + row_f)
+                           + S * tile_e + (st if has_h0 else 0) + st,
+        "chunk_state_store": S * (tile_e + lo * tile_e + tile_f + row_f) + (st if has_h0 else 0)
+                             + S * (dd_f + tile_f),
+        "chunk_state_bwd": S * (cc_f + 3 * lo * tile_e + row_f + tile_e) + S * (dd_f + 2 * tile_f),
+        "chunk_grad_a": SK * tile_e + S * (2 * dd_f + 2 * tile_f + 2 * tile_e + 2 * row_f)
+                        + S * (3 * tile_f + 2 * cc_f + 4),
+        "chunk_grad_b": qk_in + S * (4 * tile_f + 3 * cc_f + tile_e + 2 * row_f + 4)
+                        + S * (tile_e + 2 * row_f) + SK * 2 * tile_e,
     }
-    return b
 
 
 def kernel_flops(cfg, n_chunks: int) -> dict:
-    """Algorithmic flops (the contractions of the method, triangular-aware)."""
+    """Algorithmic flops per launch: the method's contractions, triangular
+    factors counted once (no split-precision extra products)."""
     Hv, Hk, D, C = cfg.h_v, cfg.h_qk, cfg.d_k, cfg.chunk
-    S = n_chunks * Hv
+    S, SK = n_chunks * Hv, n_chunks * Hk
+    tri = C * (C + 1) // 2                     # entries of a lower-inclusive C x C factor
+    cd2 = 2 * C * D * D                        # one [C][D] x [D][D] product
     return {
-        "chunk_prep": n_chunks * Hk * 2 * (C * C // 2) * D * 2 + S * (2 * C * C * C / 3 + 2 * 2 * (C * C // 2) * D),
-        "chunk_state_fwd": S * (2 * 2 * C * D * D + 2 * D * C * D + 2 * (C * C // 2) * D),
-        "chunk_state_store": S * (2 * C * D * D + 2 * D * C * D),
-        "chunk_state_bwd": S * (2 * (C * C // 2) * D + 2 * C * D * D + 2 * 2 * D * C * D),
-        "chunk_grad_a": S * (2 * C * D * D + 2 * 2 * C * C * D),
-        "chunk_grad_b": S * (2 * 2 * C * C * C + 2 * 2 * (C * C // 2) * D + 3 * 2 * C * D * D + 5 * 2 * (C * C // 2) * D),
+        "chunk_prep": SK * 2 * 2 * tri * D + S * (C ** 3 // 3 + 2 * 2 * tri * D),
+        "chunk_prep_bwd": SK * 2 * 2 * tri * D + S * (C ** 3 // 3 + 2 * 2 * tri * D),
+        "chunk_state_fwd": S * (3 * cd2 + 2 * tri * D),
+        "chunk_state_store": S * 2 * cd2,
+        "chunk_state_bwd": S * (3 * cd2 + 2 * tri * D),
+        "chunk_grad_a": S * (3 * cd2 + 2 * 2 * C * C * D + 2 * tri * D),
+        "chunk_grad_b": SK * 2 * tri * D + S * (C ** 3 // 3 + 2 * 2 * tri * D + 2 * C ** 3 + 3 * 2 * tri * D
+                                                + 2 * C * C * D),
     }
 
 
@@ -137,7 +149,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="train", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-heads", type=int, default=2, help="q/k heads in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--cpu-heads", type=int, default=8, help="q/k heads in the CPU-oracle sample (0: skip)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the reference for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters of rocprofv3) and exit")
@@ -190,24 +202,24 @@ def main():
         if cfg.bwd:
             layer.backward(dy, x, w, g, beta, cu, f, z, wn, h0)
 
+    # Per-kernel durations come from HIP events that the library records around
+    # each launch on the stream it launches on, during the timed steps
+    # themselves.  Warm-up runs with recording on too, so that the timed steps
+    # reuse pooled events instead of creating them.
+    gdn.profile_enable(True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    gdn.profile_enable(True)  # clears the warm-up records
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
-    value = cfg.T * args.steps / elapsed
-
-    # per-kernel durations: HIP events recorded by the library on its stream
-    gdn.profile_enable(True)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
     rep = gdn.profile_report()
     gdn.profile_enable(False)
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = cfg.T * args.steps / elapsed
 
     import oracle
     n_chunks = len(oracle.chunk_table(inp["cu"], cfg.chunk)[0])
