@@ -859,7 +859,8 @@ static void launch_chunk_bwd_core(const ChunkArgs& a, hipStream_t st) {
   launch_chunk_fwd_core<E, D, C>(a, st, false);  // Hc, W per chunk
   {
     GDN_PROF("chunk_state_bwd", st);
-    state_bwd_kernel<E, D, C, DVT><<<dim3(state_grid(a.N, a.Hk, a.G, D / DVT)), kChunkThreads, 0, st>>>(a);
+    if constexpr (use_wide_state<E, D, C>()) launch_state_bwd_wide(a, st);
+    else state_bwd_kernel<E, D, C, DVT><<<dim3(state_grid(a.N, a.Hk, a.G, D / DVT)), kChunkThreads, 0, st>>>(a);
   }
   {
     GDN_PROF("chunk_grad_a", st);

@@ -268,17 +268,17 @@ struct StateSmem {
 // stride ld elements, rows past rows_valid read as zero) by all threads of a
 // workgroup with 16-byte loads; store() writes it to LDS afterwards.  Used to
 // issue the next chunk's loads before the current chunk's compute.
-template <typename T, int R, int COLS>
+template <typename T, int R, int COLS, int NTH = kChunkThreads>
 struct TileRegs {
   static constexpr int V = 16 / (int)sizeof(T);
   static constexpr int PER_ROW = COLS / V;
   static constexpr int TOTAL = R * PER_ROW;
-  static constexpr int N = (TOTAL + kChunkThreads - 1) / kChunkThreads;
+  static constexpr int N = (TOTAL + NTH - 1) / NTH;
   uint4 r[N];
   __device__ __forceinline__ void load(const T* g, int64_t ld, int rows_valid) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int e = threadIdx.x + i * kChunkThreads;
+      const int e = threadIdx.x + i * NTH;
       r[i] = make_uint4(0, 0, 0, 0);
       if (e < TOTAL) {
         const int row = e / PER_ROW, c = (e % PER_ROW) * V;
@@ -289,7 +289,7 @@ struct TileRegs {
   __device__ __forceinline__ void store(T* s, int lds) const {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int e = threadIdx.x + i * kChunkThreads;
+      const int e = threadIdx.x + i * NTH;
       if (e < TOTAL) {
         const int row = e / PER_ROW, c = (e % PER_ROW) * V;
         *reinterpret_cast<uint4*>(s + row * lds + c) = r[i];
@@ -304,7 +304,7 @@ struct TileRegs {
                                           float mult = 1.f) const {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int e = threadIdx.x + i * kChunkThreads;
+      const int e = threadIdx.x + i * NTH;
       if (e < TOTAL) {
         const int row = e / PER_ROW, c = (e % PER_ROW) * V;
         const T* f = reinterpret_cast<const T*>(&r[i]);
@@ -318,14 +318,14 @@ struct TileRegs {
       }
     }
   }
-  __device__ __forceinline__ int row_of(int i) const { return (threadIdx.x + i * kChunkThreads) / PER_ROW; }
+  __device__ __forceinline__ int row_of(int i) const { return (threadIdx.x + i * NTH) / PER_ROW; }
   // float tile written as E hi (and lo) parts
   template <typename E>
   __device__ __forceinline__ void store_split(E* hi, E* lo, int lds) const {
     static_assert(sizeof(T) == 4, "split store takes a float tile");
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int e = threadIdx.x + i * kChunkThreads;
+      const int e = threadIdx.x + i * NTH;
       if (e < TOTAL) {
         const int row = e / PER_ROW, c = (e % PER_ROW) * V;
         const float* f = reinterpret_cast<const float*>(&r[i]);
@@ -339,16 +339,16 @@ struct TileRegs {
 // consecutive rows of one column, so store() writes the transposed tile
 // (dst[c * lds + r]) with one 16-byte store per slot, and the loads of a wave
 // walk along rows (coalesced for COLS >= 32).
-template <typename T, int R, int COLS>
+template <typename T, int R, int COLS, int NTH = kChunkThreads>
 struct ColRegs {
   static constexpr int V = 16 / (int)sizeof(T);
   static constexpr int TOTAL = COLS * (R / V);
-  static constexpr int N = (TOTAL + kChunkThreads - 1) / kChunkThreads;
+  static constexpr int N = (TOTAL + NTH - 1) / NTH;
   uint4 r[N];
   __device__ __forceinline__ void load(const T* g, int64_t ld, int rows_valid) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int e = threadIdx.x + i * kChunkThreads;
+      const int e = threadIdx.x + i * NTH;
       T* v = reinterpret_cast<T*>(&r[i]);
 #pragma unroll
       for (int u = 0; u < V; ++u) v[u] = from_f<T>(0.f);
@@ -363,7 +363,7 @@ struct ColRegs {
   __device__ __forceinline__ void store(T* s, int lds) const {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const int e = threadIdx.x + i * kChunkThreads;
+      const int e = threadIdx.x + i * NTH;
       if (e < TOTAL) {
         const int c = e % COLS, r0 = (e / COLS) * V;
         *reinterpret_cast<uint4*>(s + c * lds + r0) = r[i];
@@ -397,5 +397,12 @@ __device__ __forceinline__ void for_blocks(F&& f) {
 }
 
 inline int state_grid(int N, int Hk, int G, int NVT) { return ((N * Hk + 7) / 8) * 8 * G * NVT; }
+
+// State passes with one 1024-thread workgroup per (sequence, v-head), for
+// bf16, d = 128, chunk 64 (state_wide.hip).
+void launch_state_fwd_wide(const ChunkArgs& a, hipStream_t st, bool out_mode);
+void launch_state_bwd_wide(const ChunkArgs& a, hipStream_t st);
+template <typename E, int D, int C>
+constexpr bool use_wide_state() { return sizeof(E) == 2 && D == 128 && C == 64; }
 
 }  // namespace gdn

@@ -440,6 +440,10 @@ void launch_chunk_fwd_core(const ChunkArgs& a, hipStream_t st, bool out_mode) {
   }
   dim3 gstate(state_grid(a.N, a.Hk, a.G, D / DVT));
   GDN_PROF(out_mode ? "chunk_state_fwd" : "chunk_state_store", st);
+  if constexpr (use_wide_state<E, D, C>()) {
+    launch_state_fwd_wide(a, st, out_mode);
+    return;
+  }
   if (out_mode) state_fwd_kernel<E, D, C, DVT, true><<<gstate, kChunkThreads, 0, st>>>(a);
   else state_fwd_kernel<E, D, C, DVT, false><<<gstate, kChunkThreads, 0, st>>>(a);
 }
