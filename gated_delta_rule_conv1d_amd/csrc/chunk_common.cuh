@@ -119,22 +119,22 @@ __device__ __forceinline__ void st4_split(E* hi, E* lo, f32x4 v) {
 
 // copy a [R][Ccols] row-major E tile between global (dense, ld = Ccols) and LDS
 // (row stride lds), 16 bytes per thread step
-template <typename E, int R, int Ccols>
+template <typename E, int R, int Ccols, int NTH = kChunkThreads>
 __device__ __forceinline__ void g2s(E* s, int lds, const E* g) {
   constexpr int V = Vec<E>::N;
   constexpr int PER_ROW = Ccols / V;
-  for (int e = threadIdx.x; e < R * PER_ROW; e += kChunkThreads) {
+  for (int e = threadIdx.x; e < R * PER_ROW; e += NTH) {
     const int r = e / PER_ROW, c = (e % PER_ROW) * V;
     *reinterpret_cast<uint4*>(s + r * lds + c) = *reinterpret_cast<const uint4*>(g + (int64_t)r * Ccols + c);
   }
 }
 
 // rows [0, len) of a token-major input (row stride ld elements) into LDS; zero rows past len
-template <typename E, int R, int Ccols>
+template <typename E, int R, int Ccols, int NTH = kChunkThreads>
 __device__ __forceinline__ void rows2s(E* s, int lds, const E* g, int64_t ld, int len) {
   constexpr int V = Vec<E>::N;
   constexpr int PER_ROW = Ccols / V;
-  for (int e = threadIdx.x; e < R * PER_ROW; e += kChunkThreads) {
+  for (int e = threadIdx.x; e < R * PER_ROW; e += NTH) {
     const int r = e / PER_ROW, c = (e % PER_ROW) * V;
     uint4 val = make_uint4(0, 0, 0, 0);
     if (r < len) val = *reinterpret_cast<const uint4*>(g + (int64_t)r * ld + c);
@@ -144,12 +144,12 @@ __device__ __forceinline__ void rows2s(E* s, int lds, const E* g, int64_t ld, in
 
 // rows [0, len) of a token-major input written transposed into LDS:
 // s[c * lds + r] = g[r * ld + c]; zero past len.  Optional per-row scale.
-template <typename E, int R, int Ccols>
+template <typename E, int R, int Ccols, int NTH = kChunkThreads>
 __device__ __forceinline__ void rows2s_t(E* s, int lds, const E* g, int64_t ld, int len, const float* rscale,
                                          float mult) {
   constexpr int V = Vec<E>::N;
   constexpr int PER_ROW = Ccols / V;
-  for (int e = threadIdx.x; e < R * PER_ROW; e += kChunkThreads) {
+  for (int e = threadIdx.x; e < R * PER_ROW; e += NTH) {
     const int r = e / PER_ROW, c = (e % PER_ROW) * V;
     float val[V];
     if (r < len) {
@@ -191,11 +191,11 @@ struct PrepSmem {
 };
 
 // (I + A)^-1 for strictly lower A [C][C] (fp32 in LDS) into Tm and Tt = Tm^T.
-template <int C, int LDCF>
+template <int C, int LDCF, int NTH = kChunkThreads>
 __device__ __forceinline__ void unit_lower_inverse(const float (*Am)[LDCF], float (*Tm)[LDCF], float (*Tt)[LDCF],
                                                    float (*Xs)[16][20]) {
   const int tid = threadIdx.x, w = wave_id();
-  for (int e = tid; e < C * C; e += kChunkThreads) {
+  for (int e = tid; e < C * C; e += NTH) {
     Tm[e / C][e % C] = 0.f;
     Tt[e / C][e % C] = 0.f;
   }

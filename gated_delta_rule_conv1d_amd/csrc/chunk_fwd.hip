@@ -74,8 +74,9 @@ __global__ __launch_bounds__(1024) void chunk_index_kernel(const int32_t* __rest
 // substitution, off-diagonal blocks by block substitution on fp32 MFMA),
 // U and Wk on MFMA.
 // ---------------------------------------------------------------------------
-template <typename E, int D, int C, bool LO_OUT>
-__global__ __launch_bounds__(kChunkThreads) void prep_kernel(ChunkArgs a) {
+template <typename E, int D, int C, bool LO_OUT, int NTH>
+__global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
+  constexpr int NW = NTH / kWave;
   using S = PrepSmem<E, D, C>;
   __shared__ S sm;
   constexpr int V = Vec<E>::N;
@@ -88,11 +89,11 @@ __global__ __launch_bounds__(kChunkThreads) void prep_kernel(ChunkArgs a) {
   const E* qg = (const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D;
   const E* kg = (const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D;
 
-  rows2s<E, C, D>(&sm.Qs[0][0], S::LDQ, qg, a.sqk, len);
-  rows2s<E, C, D>(&sm.Ks[0][0], S::LDQ, kg, a.sqk, len);
-  rows2s_t<E, C, D>(&sm.Kt[0][0], S::LDCE, kg, a.sqk, len, nullptr, 1.f);
+  rows2s<E, C, D, NTH>(&sm.Qs[0][0], S::LDQ, qg, a.sqk, len);
+  rows2s<E, C, D, NTH>(&sm.Ks[0][0], S::LDQ, kg, a.sqk, len);
+  rows2s_t<E, C, D, NTH>(&sm.Kt[0][0], S::LDCE, kg, a.sqk, len, nullptr, 1.f);
   __syncthreads();
-  for (int t = w; t < NT * NT; t += kChunkWaves) {
+  for (int t = w; t < NT * NT; t += NW) {
     const int rt = t / NT, ct = t % NT;
     const f32x4 acc = mm_tile<E, D>(zero4(), &sm.Ks[rt * 16][0], S::LDQ, &sm.Ks[ct * 16][0], S::LDQ);
 #pragma unroll
@@ -122,13 +123,13 @@ __global__ __launch_bounds__(kChunkThreads) void prep_kernel(ChunkArgs a) {
       }
     }
     const E* vg = (const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)h * D;
-    rows2s_t<E, C, D>(&sm.Vt[0][0], S::LDCE, vg, a.sv, len, nullptr, 1.f);
+    rows2s_t<E, C, D, NTH>(&sm.Vt[0][0], S::LDCE, vg, a.sv, len, nullptr, 1.f);
     __syncthreads();
 
     // P = lower_incl(D * Q K^T) (fp32 to workspace), A = strict_lower(beta_r D * K K^T)
     {
       float* Pg = a.P + slot * C * C;
-      for (int t = w; t < NT * NT; t += kChunkWaves) {
+      for (int t = w; t < NT * NT; t += NW) {
         const int rt = t / NT, ct = t % NT;
         const f32x4 acc = mm_tile<E, D>(zero4(), &sm.Qs[rt * 16][0], S::LDQ, &sm.Ks[ct * 16][0], S::LDQ);
         f32x4 pv;
@@ -144,17 +145,17 @@ __global__ __launch_bounds__(kChunkThreads) void prep_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();
-    unit_lower_inverse<C, S::LDCF>(sm.Am, sm.Tm, sm.Tt, sm.Xs);  // starts and ends with a barrier
+    unit_lower_inverse<C, S::LDCF, NTH>(sm.Am, sm.Tm, sm.Tt, sm.Xs);  // starts and ends with a barrier
 
     // U = (T diag(beta)) V, the left factor split into hi + lo bf16 parts; fp32 result
-    for (int e = tid; e < C * C; e += kChunkThreads) {
+    for (int e = tid; e < C * C; e += NTH) {
       const int r = e / C, s = e % C;
       split_store<E>(&sm.TB[r][s], &sm.TBl[0][0] + r * S::LDCE + s, sm.Tm[r][s] * sm.beta[s]);
     }
     __syncthreads();
     {
       float* Ug = a.U + slot * C * D;
-      for (int t = w; t < NT * ND; t += kChunkWaves) {
+      for (int t = w; t < NT * ND; t += NW) {
         const int rt = t / ND, ct = t % ND;
         f32x4 acc = mm_tile<E, C>(zero4(), &sm.TB[rt * 16][0], S::LDCE, &sm.Vt[ct * 16][0], S::LDCE);
         if constexpr (Split<E>::on)
@@ -164,14 +165,14 @@ __global__ __launch_bounds__(kChunkThreads) void prep_kernel(ChunkArgs a) {
     }
     __syncthreads();
     // Wk = (T diag(beta Gam)) K
-    for (int e = tid; e < C * C; e += kChunkThreads) {
+    for (int e = tid; e < C * C; e += NTH) {
       const int r = e / C, s = e % C;
       split_store<E>(&sm.TB[r][s], &sm.TBl[0][0] + r * S::LDCE + s, sm.Tm[r][s] * sm.beta[s] * __expf(sm.gam[s]));
     }
     __syncthreads();
     {
       E* Wg = (E*)a.Wk + slot * C * D;
-      for (int t = w; t < NT * ND; t += kChunkWaves) {
+      for (int t = w; t < NT * ND; t += NW) {
         const int rt = t / ND, ct = t % ND;
         f32x4 acc = mm_tile<E, C>(zero4(), &sm.TB[rt * 16][0], S::LDCE, &sm.Kt[ct * 16][0], S::LDCE);
         if constexpr (Split<E>::on)
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(kChunkThreads) void prep_kernel(ChunkArgs a) {
     {
       E* Kg = (E*)a.Kt + slot * D * C;
       const float glast = sm.gam[len - 1];
-      for (int e = tid; e < D * (C / V); e += kChunkThreads) {
+      for (int e = tid; e < D * (C / V); e += NTH) {
         const int d = e / (C / V), s0 = (e % (C / V)) * V;
         float val[V], lo[V];
 #pragma unroll
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(kChunkThreads) void prep_kernel(ChunkArgs a) {
       }
       if constexpr (LO_OUT) {
         // rows e_s k_s [C][D] and (Gam_r q_r)^T [D][C], hi / lo, for the reverse state pass
-        for (int e = tid; e < C * (D / V); e += kChunkThreads) {
+        for (int e = tid; e < C * (D / V); e += NTH) {
           const int s = e / (D / V), c0 = (e % (D / V)) * V;
           const float es = (s < len) ? __expf(glast - sm.gam[s]) : 0.f;
           float val[V], lo[V];
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(kChunkThreads) void prep_kernel(ChunkArgs a) {
           Vec<E>::store((E*)a.Krh + o, val);
           if constexpr (Split<E>::on) Vec<E>::store((E*)a.Krl + o, lo);
         }
-        for (int e = tid; e < D * (C / V); e += kChunkThreads) {
+        for (int e = tid; e < D * (C / V); e += NTH) {
           const int d = e % D, s0 = (e / D) * V;
           float val[V], lo[V];
 #pragma unroll
@@ -435,8 +436,9 @@ void launch_chunk_fwd_core(const ChunkArgs& a, hipStream_t st, bool out_mode) {
   dim3 gprep(a.max_chunks, a.Hk);
   {
     GDN_PROF(out_mode ? "chunk_prep" : "chunk_prep_bwd", st);
-    if (out_mode) prep_kernel<E, D, C, false><<<gprep, kChunkThreads, 0, st>>>(a);
-    else prep_kernel<E, D, C, true><<<gprep, kChunkThreads, 0, st>>>(a);
+    constexpr int NTH = D >= 64 ? 512 : kChunkThreads;  // 8 waves for the wide heads
+    if (out_mode) prep_kernel<E, D, C, false, NTH><<<gprep, NTH, 0, st>>>(a);
+    else prep_kernel<E, D, C, true, NTH><<<gprep, NTH, 0, st>>>(a);
   }
   dim3 gstate(state_grid(a.N, a.Hk, a.G, D / DVT));
   GDN_PROF(out_mode ? "chunk_state_fwd" : "chunk_state_store", st);

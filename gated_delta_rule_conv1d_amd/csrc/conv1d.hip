@@ -281,14 +281,6 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(const E* __restrict__ dy,
   }
 }
 
-__global__ void sum_parts_kernel(const float* __restrict__ part, int nparts, int n, float* __restrict__ out) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  float s = 0.f;
-  for (int p = 0; p < nparts; ++p) s += part[(size_t)p * n + i];
-  out[i] = s;
-}
-
 // --------------------------------------------------------------------------
 // host side
 // --------------------------------------------------------------------------
@@ -328,7 +320,7 @@ static void launch_conv_bwd(const gdn_shape* s, const void* dy, const void* x, c
   }
   const int n = Cch * W;
   GDN_PROF("conv_dw_sum", st);
-  sum_parts_kernel<<<(n + 255) / 256, 256, 0, st>>>(part, (int)grid.x, n, dw);
+  launch_colsum(part, (int)grid.x, n, dw, st);
 }
 
 template <typename E, int D>
@@ -371,7 +363,7 @@ bool run_conv_bwd(const gdn_shape* s, const void* dy, const void* x, const void*
                   float eps, void* dx, float* dw, void* ws, hipStream_t st) {
   if (s->total_tokens == 0) {
     const int n = (2 * s->h_qk * s->d_k + s->h_v * s->d_v) * width;
-    sum_parts_kernel<<<(n + 255) / 256, 256, 0, st>>>((const float*)ws, 0, n, dw);
+    launch_colsum((const float*)ws, 0, n, dw, st);
     return true;
   }
 #define GDN_CONV_D(E, D) \

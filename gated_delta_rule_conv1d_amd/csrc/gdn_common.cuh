@@ -307,4 +307,34 @@ __device__ __forceinline__ float group_sum(float v) {  // sum over aligned group
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + __expf(-x)); }
 
 
+// ---------------------------------------------------------------------------
+// Deterministic column sums of per-block partials: out[c] = sum_p part[p*n + c].
+// Thread (g, cc) of a block adds parts g, g + PG, g + 2 PG, ... of column
+// blockIdx.x * CW + cc; one thread per column then adds the PG group sums in
+// order.  The order of every addition is fixed, so results are bit-identical
+// run to run.
+// ---------------------------------------------------------------------------
+template <int CW, int PG>
+__global__ __launch_bounds__(CW * PG) void colsum_kernel(const float* __restrict__ part, int nparts, int n,
+                                                         float* __restrict__ out) {
+  __shared__ float s[PG][CW + 1];
+  const int cc = threadIdx.x % CW, g = threadIdx.x / CW;
+  const int c = blockIdx.x * CW + cc;
+  float acc = 0.f;
+  if (c < n)
+    for (int p = g; p < nparts; p += PG) acc += part[(size_t)p * n + c];
+  s[g][cc] = acc;
+  __syncthreads();
+  if (g == 0 && c < n) {
+    float t = 0.f;
+    for (int i = 0; i < PG; ++i) t += s[i][cc];
+    out[c] = t;
+  }
+}
+
+inline void launch_colsum(const float* part, int nparts, int n, float* out, hipStream_t st) {
+  if (n < 4096) colsum_kernel<4, 64><<<(n + 3) / 4, 256, 0, st>>>(part, nparts, n, out);
+  else colsum_kernel<16, 16><<<(n + 15) / 16, 256, 0, st>>>(part, nparts, n, out);
+}
+
 }  // namespace gdn

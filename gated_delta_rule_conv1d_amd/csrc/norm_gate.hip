@@ -111,13 +111,6 @@ __global__ __launch_bounds__(kNormThreads) void norm_bwd_kernel(const E* __restr
   }
 }
 
-__global__ void norm_sum_kernel(const float* __restrict__ part, int nparts, int dv, float* __restrict__ out) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= dv) return;
-  float s = 0.f;
-  for (int p = 0; p < nparts; ++p) s += part[(size_t)p * dv + c];
-  out[c] = s;
-}
 
 size_t norm_bwd_ws_bytes(const gdn_shape* s) { return (size_t)kNormBwdBlocks * s->d_v * sizeof(float); }
 
@@ -143,7 +136,7 @@ static void launch_norm_bwd(const gdn_shape* s, const void* dy, const void* o, c
                                                                     (const E*)w, eps, rows, (E*)d_o, (E*)dz, part);
   }
   GDN_PROF("norm_dw_sum", st);
-  norm_sum_kernel<<<(DV + 255) / 256, 256, 0, st>>>(part, kNormBwdBlocks, DV, dw);
+  launch_colsum(part, kNormBwdBlocks, DV, dw, st);
 }
 
 bool run_norm_fwd(const gdn_shape* s, const void* o, const void* z, const void* w, float eps, void* y,
