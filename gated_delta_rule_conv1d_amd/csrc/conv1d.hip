@@ -65,7 +65,12 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(const E* __restrict__ x, 
       for (int c = 0; c < V; ++c) hist[i][c] = 0.f;
   }
 
+  // the next token's x is loaded one iteration ahead
+  uint4 nx = make_uint4(0, 0, 0, 0);
+  if (active) nx = *reinterpret_cast<const uint4*>(x + (size_t)t0 * Cch + ch);
   for (int t = t0; t < t1; ++t) {
+    const uint4 rx = nx;
+    if (active && t + 1 < t1) nx = *reinterpret_cast<const uint4*>(x + (size_t)(t + 1) * Cch + ch);
     if (t >= seq_end) {  // entering a new sequence (skip empty ones)
       while (cu[n + 1] <= t) ++n;
       seq_start = cu[n];
@@ -76,10 +81,11 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(const E* __restrict__ x, 
         for (int c = 0; c < V; ++c) hist[i][c] = 0.f;
     }
     float cur[V];
-    if (active) Vec<E>::load(x + (size_t)t * Cch + ch, cur);
-    else
+    {
+      const E* ex = reinterpret_cast<const E*>(&rx);
 #pragma unroll
-      for (int c = 0; c < V; ++c) cur[c] = 0.f;
+      for (int c = 0; c < V; ++c) cur[c] = to_f<E>(ex[c]);
+    }
     float a[V];
     float ss = 0.f;
 #pragma unroll
@@ -162,7 +168,18 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(const E* __restrict__ dy,
 #pragma unroll
       for (int c = 0; c < V; ++c) dcw[i][c] = 0.f;
     }
+    // the next token's x and dy are loaded one iteration ahead
+    uint4 nx = make_uint4(0, 0, 0, 0), ng = make_uint4(0, 0, 0, 0);
+    if (active) {
+      nx = *reinterpret_cast<const uint4*>(x + (size_t)t0 * Cch + ch);
+      ng = *reinterpret_cast<const uint4*>(dy + (size_t)t0 * Cch + ch);
+    }
     for (int t = t0; t < tend; ++t) {
+      const uint4 rx = nx, rg = ng;
+      if (active && t + 1 < tend) {
+        nx = *reinterpret_cast<const uint4*>(x + (size_t)(t + 1) * Cch + ch);
+        ng = *reinterpret_cast<const uint4*>(dy + (size_t)(t + 1) * Cch + ch);
+      }
       if (t >= seq_end) {
         while (cu[n + 1] <= t) ++n;
         seq_start = cu[n];
@@ -173,12 +190,14 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(const E* __restrict__ dy,
           for (int c = 0; c < V; ++c) hist[i][c] = 0.f;
       }
       float cur[V], g[V];
-      if (active) {
-        Vec<E>::load(x + (size_t)t * Cch + ch, cur);
-        Vec<E>::load(dy + (size_t)t * Cch + ch, g);
-      } else {
+      {
+        const E* ex = reinterpret_cast<const E*>(&rx);
+        const E* eg = reinterpret_cast<const E*>(&rg);
 #pragma unroll
-        for (int c = 0; c < V; ++c) cur[c] = g[c] = 0.f;
+        for (int c = 0; c < V; ++c) {
+          cur[c] = to_f<E>(ex[c]);
+          g[c] = to_f<E>(eg[c]);
+        }
       }
       float cc[V], sg[V], a[V];
       float ss = 0.f, dot = 0.f;
