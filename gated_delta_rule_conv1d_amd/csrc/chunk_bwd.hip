@@ -426,6 +426,7 @@ __global__ __launch_bounds__(kChunkThreads) void grad_a_kernel(ChunkArgs a) {
 template <typename E, int D, int C>
 struct GradBSmem {
   static constexpr int LD2C = 2 * C + Pad<E>::E16;
+  static constexpr int LDCE = C + Pad<E>::E16;
   static constexpr int LDCF = C + 4;
   static constexpr int NT = C / 16, ND = D / 16;
   static constexpr int LDV = D + Pad<E>::E16;
@@ -435,12 +436,20 @@ struct GradBSmem {
     float Am[C][LDCF];  // A (solve), later dA
     E Vs[C][LDV];       // v rows, between the two
   } av;
-  float Tm[C][LDCF];   // T, later P
-  float Tt[C][LDCF];   // T^T, later dP
+  union {
+    struct {
+      float Tm[C][LDCF];  // T, later P
+      float Tt[C][LDCF];  // T^T, later dP'
+    };
+    struct {
+      E h[C][LD2C];
+      E l[Split<E>::on ? C : 1][LD2C];
+    } TS;  // [dS^T | A~ + A~^T] rows, hi + lo, after the C x C pass
+  };
   union U {
     float Xf[D][LDCF];                            // dW^T or dWk^T
     struct { float dT[C][LDCF]; float M1t[C][LDCF]; } m;
-    struct { float dS[C][LDCF]; float At[C][LDCF]; } s;
+    struct { E dSh[C][LDCE]; E dSl[Split<E>::on ? C : 1][LDCE]; float At[C][LDCF]; } s;  // dS (hi, lo), A~
     float Xs[kChunkWaves][16][20];
   } r;
   float gam[C], beta[C], Gm[C], em[C];
@@ -456,13 +465,17 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
   constexpr bool LO = Split<E>::on;
   __shared__ S sm;
   constexpr int NT = S::NT, ND = S::ND;
-  constexpr int NQT = NT * ND;
-  constexpr int NQW = (NQT + kChunkWaves - 1) / kChunkWaves;
+  // [C][D] output tiles per wave: a block of RT row tiles x CT adjacent column
+  // tiles (waves past the row tiles idle)
+  constexpr int NWC = ND >= kChunkWaves ? kChunkWaves : ND, NWR = kChunkWaves / NWC;
+  constexpr int RT = NT >= NWR ? NT / NWR : 1, CT = ND / NWC;
   const int ci = blockIdx.x, j = blockIdx.y;
   const int4 ent = chunk_entry(a.table, ci);
   if (ent.x < 0) return;
   const int tok0 = ent.y, len = ent.z;
   const int w = wave_id(), lane = lane_id(), tid = threadIdx.x;
+  const bool act = (w / NWC) * RT < NT;
+  const int rt0 = (w / NWC) * RT, ct0 = (w % NWC) * CT;
   const E* qg = (const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D;
   const E* kg = (const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D;
 
@@ -486,9 +499,9 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
     for (int e = 0; e < 4; ++e) sm.Skk[rt * 16 + acc_row(e)][ct * 16 + acc_col()] = skk[e];
   }
 
-  f32x4 dQ[NQW], dK[NQW];
-#pragma unroll
-  for (int i = 0; i < NQW; ++i) dQ[i] = dK[i] = zero4();
+  f32x4 dQ[RT][CT], dK[RT][CT];
+  zero_blk(dQ);
+  zero_blk(dK);
 
   for (int gi = 0; gi < a.G; ++gi) {
     const int h = j * a.G + gi;
@@ -528,10 +541,9 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
     __syncthreads();
     E* dvg = (E*)a.dv + (int64_t)tok0 * a.sv + (int64_t)h * D;
 #pragma unroll
-    for (int i = 0; i < NQW; ++i) {
-      const int t = w + kChunkWaves * i;
-      if (t < NQT) {
-        const int rt = t / ND, ct = t % ND;
+    for (int i = 0; i < RT * CT; ++i) {
+      if (act) {
+        const int rt = rt0 + i / CT, ct = ct0 + i % CT;
         const f32x4 xu = mm_gen<E, C, LO, LO>(zero4(), ta(rt), xb(ct));
         f32x4 dvv;
         float pu[4];
@@ -559,17 +571,16 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < NQW; ++i) {
-      const int t = w + kChunkWaves * i;
-      if (t < NQT) {
-        const int rt = t / ND, ct = t % ND;
+    for (int i = 0; i < RT * CT; ++i) {
+      if (act) {
+        const int rt = rt0 + i / CT, ct = ct0 + i % CT;
         const f32x4 xw = mm_gen<E, C, LO, LO>(zero4(), ta(rt), xb(ct));
         float pw[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = rt * 16 + acc_row(e), c = ct * 16 + acc_col();
           pw[e] = xw[e] * to_f<E>(sm.QKt[c][C + r]);
-          dK[i][e] += sm.beta[r] * sm.Gm[r] * xw[e];
+          dK[i / CT][i % CT][e] += sm.beta[r] * sm.Gm[r] * xw[e];
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) pw[e] = group_sum<16>(pw[e]);
@@ -629,7 +640,7 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
         rp[e] = PdP;
         ca += AdA;
         cp += PdP;
-        sm.r.s.dS[r][s] = dP * dd;
+        split_store<E>(&sm.r.s.dSh[r][s], &sm.r.s.dSl[0][0] + r * S::LDCE + s, dP * dd);
         sm.r.s.At[r][s] = At;
       }
 #pragma unroll
@@ -657,57 +668,48 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();
-    // dQ += dQs + dS K;   dK += dKh + dS^T Q + (A~ + A~^T) K
-    const float* dQsg = a.dQs + slot * C * D;
-    const float* dKhg = a.dKh + slot * C * D;
+    // [dS^T | A~ + A~^T] as rows (P and dP' are consumed)
+    for (int e = tid; e < C * C; e += kChunkThreads) {
+      const int sr = e / C, r = e % C;
+      sm.TS.h[sr][r] = sm.r.s.dSh[r][sr];
+      if constexpr (LO) sm.TS.l[sr][r] = sm.r.s.dSl[r][sr];
+      split_store<E>(&sm.TS.h[sr][C + r], &sm.TS.l[0][0] + sr * S::LD2C + C + r,
+                     sm.r.s.At[sr][r] + sm.r.s.At[r][sr]);
+    }
+    __syncthreads();
+    // dQ += dQs + dS K;   dK += dKh + [dS^T | A~ + A~^T] [Q ; K]
+    if (act) {
+      const float* dQsg = a.dQs + slot * C * D;
+      const float* dKhg = a.dKh + slot * C * D;
 #pragma unroll
-    for (int i = 0; i < NQW; ++i) {
-      const int t = w + kChunkWaves * i;
-      if (t < NQT) {
-        const int rt = t / ND, ct = t % ND;
-        auto kt = [&](int c, int k, float* o) { ld_row<E, KPL>(&sm.QKt[ct * 16 + c][C + k], o); };
-        auto qt = [&](int c, int k, float* o) { ld_row<E, KPL>(&sm.QKt[ct * 16 + c][k], o); };
-        const f32x4 sq = mm_gen<E, C, LO, false>(
-            zero4(), [&](int r, int k, float* o) { ld_row<float, KPL>(&sm.r.s.dS[rt * 16 + r][k], o); }, kt);
-        f32x4 sk = mm_gen<E, C, LO, false>(
-            zero4(),
-            [&](int r, int k, float* o) {
+      for (int ri = 0; ri < RT; ++ri)
 #pragma unroll
-              for (int u = 0; u < KPL; ++u) o[u] = sm.r.s.dS[k + u][rt * 16 + r];
-            },
-            qt);
-        sk = mm_gen<E, C, LO, false>(
-            sk,
-            [&](int r, int k, float* o) {
-              ld_row<float, KPL>(&sm.r.s.At[rt * 16 + r][k], o);
-#pragma unroll
-              for (int u = 0; u < KPL; ++u) o[u] += sm.r.s.At[k + u][rt * 16 + r];
-            },
-            kt);
-        float pq[4], pk[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = rt * 16 + acc_row(e), c = ct * 16 + acc_col();
-          const float qsv = dQsg[r * D + c];
-          const float khv = dKhg[r * D + c];
-          dQ[i][e] += qsv + sq[e];
-          dK[i][e] += khv + sk[e];
-          pq[e] = qsv * to_f<E>(sm.QKt[c][r]);
-          pk[e] = khv * to_f<E>(sm.QKt[c][C + r]);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pq[e] = group_sum<16>(pq[e]);
-          pk[e] = group_sum<16>(pk[e]);
-        }
-        if ((lane & 15) == 0) {
+        for (int cj = 0; cj < CT; ++cj) {
+          const int rt = rt0 + ri, ct = ct0 + cj;
+          float pq[4], pk[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            sm.pCD[2][ct][rt * 16 + acc_row(e)] = pq[e];
-            sm.pCD[3][ct][rt * 16 + acc_row(e)] = pk[e];
+            const int r = rt * 16 + acc_row(e), c = ct * 16 + acc_col();
+            const float qsv = dQsg[r * D + c];
+            const float khv = dKhg[r * D + c];
+            dQ[ri][cj][e] += qsv;
+            dK[ri][cj][e] += khv;
+            pq[e] = group_sum<16>(qsv * to_f<E>(sm.QKt[c][r]));
+            pk[e] = group_sum<16>(khv * to_f<E>(sm.QKt[c][C + r]));
+          }
+          if ((lane & 15) == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              sm.pCD[2][ct][rt * 16 + acc_row(e)] = pq[e];
+              sm.pCD[3][ct][rt * 16 + acc_row(e)] = pk[e];
+            }
           }
         }
-      }
+      const int r0 = rt0 * 16, c0 = ct0 * 16;
+      mm_blk<E, C, RT, CT, LO, false>(dQ, &sm.r.s.dSh[r0][0], LO ? &sm.r.s.dSl[0][0] + r0 * S::LDCE : nullptr,
+                                      S::LDCE, &sm.QKt[c0][C], nullptr, S::LD2C);
+      mm_blk<E, 2 * C, RT, CT, LO, false>(dK, &sm.TS.h[r0][0], LO ? &sm.TS.l[0][0] + r0 * S::LD2C : nullptr,
+                                          S::LD2C, &sm.QKt[c0][0], nullptr, S::LD2C);
     }
     __syncthreads();
     // per-row totals, then dg = reverse cumulative sum within the chunk
@@ -754,14 +756,14 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
   }
   E* dqg = (E*)a.dq + (int64_t)tok0 * a.sqk + (int64_t)j * D;
   E* dkg = (E*)a.dk + (int64_t)tok0 * a.sqk + (int64_t)j * D;
+  if (act) {
 #pragma unroll
-  for (int i = 0; i < NQW; ++i) {
-    const int t = w + kChunkWaves * i;
-    if (t < NQT) {
-      const int rt = t / ND, ct = t % ND;
-      store_tile<E>(dqg, a.sqk, rt * 16, ct * 16, dQ[i], len);
-      store_tile<E>(dkg, a.sqk, rt * 16, ct * 16, dK[i], len);
-    }
+    for (int ri = 0; ri < RT; ++ri)
+#pragma unroll
+      for (int cj = 0; cj < CT; ++cj) {
+        store_tile<E>(dqg, a.sqk, (rt0 + ri) * 16, (ct0 + cj) * 16, dQ[ri][cj], len);
+        store_tile<E>(dkg, a.sqk, (rt0 + ri) * 16, (ct0 + cj) * 16, dK[ri][cj], len);
+      }
   }
 }
 
