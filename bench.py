@@ -74,6 +74,10 @@ def kernel_bytes(cfg, n_chunks: int, has_h0: bool) -> dict:
         "chunk_prep_bwd": qk_in + v_in + gb_in + prep_out + S * (cc_f + 3 * lo * tile_e),
         "chunk_state_fwd": SK * tile_e + S * (tile_e + lo * tile_e + tile_f + cc_f + row_f)
                            + S * tile_e + (st if has_h0 else 0) + st,
+        # forward that also keeps the backward's products: prep_bwd's outputs, and H_c, W per slot
+        "chunk_prep_save": qk_in + v_in + gb_in + prep_out + S * (cc_f + 3 * lo * tile_e),
+        "chunk_state_save": SK * tile_e + S * (tile_e + lo * tile_e + tile_f + cc_f + row_f)
+                            + S * tile_e + (st if has_h0 else 0) + st + S * (dd_f + tile_f),
         "chunk_state_store": S * (tile_e + lo * tile_e + tile_f + row_f) + (st if has_h0 else 0)
                              + S * (dd_f + tile_f),
         "chunk_state_bwd": S * (cc_f + 3 * lo * tile_e + row_f + tile_e) + S * (dd_f + 2 * tile_f),
@@ -93,6 +97,8 @@ def kernel_flops(cfg, n_chunks: int) -> dict:
     cd2 = 2 * C * D * D                        # one [C][D] x [D][D] product
     return {
         "chunk_prep": SK * 2 * 2 * tri * D + S * (C ** 3 // 3 + 2 * 2 * tri * D),
+        "chunk_prep_save": SK * 2 * 2 * tri * D + S * (C ** 3 // 3 + 2 * 2 * tri * D),
+        "chunk_state_save": S * (3 * cd2 + 2 * tri * D),
         "chunk_prep_bwd": SK * 2 * 2 * tri * D + S * (C ** 3 // 3 + 2 * 2 * tri * D),
         "chunk_state_fwd": S * (3 * cd2 + 2 * tri * D),
         "chunk_state_store": S * 2 * cd2,
@@ -198,7 +204,8 @@ def main():
     layer = gdn.GatedDeltaNetLayer(shape, cfg.width, dev, norm=cfg.norm)
 
     def step():
-        f = layer.forward(x, w, g, beta, cu, z, wn, h0)
+        # a training step keeps the forward's chunk products for the backward
+        f = layer.forward(x, w, g, beta, cu, z, wn, h0, for_backward=cfg.bwd)
         if cfg.bwd:
             layer.backward(dy, x, w, g, beta, cu, f, z, wn, h0)
 

@@ -16,8 +16,8 @@ _STATUS = {0: "GDN_OK", -1: "GDN_ERR_INVALID_ARG", -2: "GDN_ERR_UNSUPPORTED", -3
 #: every symbol include/gdn.h declares
 SYMBOLS = ("gdn_status_string", "gdn_max_chunks", "gdn_chunk_index", "gdn_conv1d", "gdn_conv1d_bwd_workspace",
            "gdn_conv1d_bwd", "gdn_chunk_fwd_workspace", "gdn_chunk_fwd", "gdn_chunk_bwd_workspace",
-           "gdn_chunk_bwd", "gdn_norm_gate", "gdn_norm_gate_bwd_workspace", "gdn_norm_gate_bwd",
-           "gdn_profile_enable", "gdn_profile_report")
+           "gdn_chunk_bwd", "gdn_chunk_fwd_save", "gdn_chunk_bwd_saved", "gdn_norm_gate",
+           "gdn_norm_gate_bwd_workspace", "gdn_norm_gate_bwd", "gdn_profile_enable", "gdn_profile_report")
 
 
 class GdnError(RuntimeError):
@@ -86,6 +86,8 @@ def load() -> ctypes.CDLL:
             "gdn_chunk_fwd": (I32, [S, P, P, P, I64, I64, P, P, P, P, P, P, P, SZ, P]),
             "gdn_chunk_bwd_workspace": (SZ, [S]),
             "gdn_chunk_bwd": (I32, [S, P, P, P, I64, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+            "gdn_chunk_fwd_save": (I32, [S, P, P, P, I64, I64, P, P, P, P, P, P, P, SZ, P]),
+            "gdn_chunk_bwd_saved": (I32, [S, P, P, P, I64, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
             "gdn_norm_gate": (I32, [S, P, P, P, F, P, P]),
             "gdn_norm_gate_bwd_workspace": (SZ, [S]),
             "gdn_norm_gate_bwd": (I32, [S, P, P, P, P, F, P, P, P, P, SZ, P]),
@@ -212,9 +214,11 @@ def _qkv_strides(q, k, v, shape: Shape):
 
 def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
               cu_seqlens: torch.Tensor, shape: Shape, h0: Optional[torch.Tensor] = None, want_ht: bool = True,
-              ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+              ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None, save: bool = False):
     """q, k: [T, Hk*dk] views; v: [T, Hv*dv] view; g, beta: fp32 [T, Hv].
-    Returns (o [T, Hv, dv], ht [N, Hv, dk, dv] fp32 or None)."""
+    Returns (o [T, Hv, dv], ht [N, Hv, dk, dv] fp32 or None).  With save=True
+    (gdn_chunk_fwd_save) ws must be a backward-sized workspace, which then
+    holds what chunk_bwd(..., saved=True) reads."""
     dt = shape.torch_dtype
     T, N, Hv, dk, dv = shape.total_tokens, shape.n_seqs, shape.h_v, shape.d_k, shape.d_v
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
@@ -227,16 +231,21 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
         _need(h0, "h0", torch.float32, (N, Hv, dk, dv))
     o = torch.empty((T, Hv, dv), dtype=dt, device=q.device) if out is None else out
     ht = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=q.device) if want_ht else None
-    ws = _workspace(chunk_fwd_workspace(shape), q.device, ws)
-    _check("gdn_chunk_fwd", load().gdn_chunk_fwd(ctypes.byref(shape.c()), _ptr(q), _ptr(k), _ptr(v), sqk, sv,
-                                                 _ptr(g), _ptr(beta), _ptr(cu_seqlens), _ptr(h0), _ptr(o), _ptr(ht),
-                                                 _ptr(ws), ws.numel(), _stream(q.device)))
+    if save and ws is None:
+        raise ValueError("save=True needs the caller's backward workspace (it carries state to chunk_bwd)")
+    ws = _workspace(chunk_bwd_workspace(shape) if save else chunk_fwd_workspace(shape), q.device, ws)
+    name = "gdn_chunk_fwd_save" if save else "gdn_chunk_fwd"
+    _check(name, getattr(load(), name)(ctypes.byref(shape.c()), _ptr(q), _ptr(k), _ptr(v), sqk, sv,
+                                       _ptr(g), _ptr(beta), _ptr(cu_seqlens), _ptr(h0), _ptr(o), _ptr(ht),
+                                       _ptr(ws), ws.numel(), _stream(q.device)))
     return o, ht
 
 
 def chunk_bwd(q, k, v, g, beta, cu_seqlens, shape: Shape, d_o, h0=None, dht=None, dq=None, dk=None, dv=None,
-              want_dh0: bool = True, ws: Optional[torch.Tensor] = None):
-    """Returns dict dq, dk, dv (like q, k, v: [T, H*d]), dg, dbeta [T, Hv] fp32, dh0 (or None)."""
+              want_dh0: bool = True, ws: Optional[torch.Tensor] = None, saved: bool = False):
+    """Returns dict dq, dk, dv (like q, k, v: [T, H*d]), dg, dbeta [T, Hv] fp32, dh0 (or None).
+    saved=True (gdn_chunk_bwd_saved): ws is the workspace a chunk_fwd(..., save=True)
+    with the same inputs just filled."""
     dt = shape.torch_dtype
     T, N, Hk, Hv, dkk, dvv = shape.total_tokens, shape.n_seqs, shape.h_qk, shape.h_v, shape.d_k, shape.d_v
     sqk, sv = _qkv_strides(q, k, v, shape)
@@ -255,8 +264,11 @@ def chunk_bwd(q, k, v, g, beta, cu_seqlens, shape: Shape, d_o, h0=None, dht=None
     dg = torch.empty((T, Hv), dtype=torch.float32, device=q.device)
     db = torch.empty((T, Hv), dtype=torch.float32, device=q.device)
     dh0 = torch.empty((N, Hv, dkk, dvv), dtype=torch.float32, device=q.device) if want_dh0 else None
+    if saved and ws is None:
+        raise ValueError("saved=True needs the workspace filled by chunk_fwd(..., save=True)")
     ws = _workspace(chunk_bwd_workspace(shape), q.device, ws)
-    _check("gdn_chunk_bwd", load().gdn_chunk_bwd(
+    name = "gdn_chunk_bwd_saved" if saved else "gdn_chunk_bwd"
+    _check(name, getattr(load(), name)(
         ctypes.byref(shape.c()), _ptr(q), _ptr(k), _ptr(v), sqk, sv, _ptr(g), _ptr(beta), _ptr(cu_seqlens),
         _ptr(h0), _ptr(d_o), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(dh0), _ptr(ws),
         ws.numel(), _stream(q.device)))

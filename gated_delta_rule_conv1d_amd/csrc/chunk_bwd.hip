@@ -26,7 +26,7 @@
 namespace gdn {
 
 template <typename E, int D, int C>
-void launch_chunk_fwd_core(const ChunkArgs& a, hipStream_t st, bool out_mode);
+void launch_chunk_fwd_core(const ChunkArgs& a, hipStream_t st, int mode);
 
 // ---------------------------------------------------------------------------
 // Reverse state pass, one workgroup per (sequence, v-head, dv tile).
@@ -856,9 +856,9 @@ constexpr bool fits() {
 }
 
 template <typename E, int D, int C>
-static void launch_chunk_bwd_core(const ChunkArgs& a, hipStream_t st) {
+static void launch_chunk_bwd_core(const ChunkArgs& a, hipStream_t st, bool recompute) {
   constexpr int DVT = D >= 32 ? 32 : D;
-  launch_chunk_fwd_core<E, D, C>(a, st, false);  // Hc, W per chunk
+  if (recompute) launch_chunk_fwd_core<E, D, C>(a, st, kFwdStore);  // operands, Hc, W per chunk
   {
     GDN_PROF("chunk_state_bwd", st);
     if constexpr (use_wide_state<E, D, C>()) launch_state_bwd_wide(a, st);
@@ -902,7 +902,7 @@ bool chunk_supported(const gdn_shape* s) {
 
 bool run_chunk_fwd(const gdn_shape* s, const void* q, const void* k, const void* v, int64_t sqk, int64_t sv,
                    const float* g, const float* beta, const int32_t* cu, const float* h0, void* o, float* ht,
-                   void* ws, hipStream_t st) {
+                   void* ws, bool save, hipStream_t st) {
   ChunkArgs a = {};
   a.q = q; a.k = k; a.v = v; a.sqk = sqk; a.sv = sv; a.g = g; a.beta = beta; a.cu = cu; a.h0 = h0;
   a.o = o; a.ht = ht;
@@ -910,13 +910,15 @@ bool run_chunk_fwd(const gdn_shape* s, const void* q, const void* k, const void*
   a.max_chunks = (int)max_chunks(s); a.scale = s->scale;
   fill_ws(a, s, ws);
   run_chunk_index(s, cu, (int32_t*)a.table, (int32_t*)a.seq_chunk0, st);
-  return dispatch(s, [&]<typename E, int D, int C>() { launch_chunk_fwd_core<E, D, C>(a, st, true); });
+  return dispatch(s, [&]<typename E, int D, int C>() {
+    launch_chunk_fwd_core<E, D, C>(a, st, save ? kFwdBoth : kFwdOut);
+  });
 }
 
 bool run_chunk_bwd(const gdn_shape* s, const void* q, const void* k, const void* v, int64_t sqk, int64_t sv,
                    const float* g, const float* beta, const int32_t* cu, const float* h0, const void* d_o,
                    const float* dht, void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0,
-                   void* ws, hipStream_t st) {
+                   void* ws, bool saved, hipStream_t st) {
   ChunkArgs a = {};
   a.q = q; a.k = k; a.v = v; a.sqk = sqk; a.sv = sv; a.g = g; a.beta = beta; a.cu = cu; a.h0 = h0;
   a.o = nullptr; a.ht = nullptr;
@@ -924,8 +926,8 @@ bool run_chunk_bwd(const gdn_shape* s, const void* q, const void* k, const void*
   a.N = s->n_seqs; a.T = s->total_tokens; a.Hk = s->h_qk; a.Hv = s->h_v; a.G = s->h_v / s->h_qk;
   a.max_chunks = (int)max_chunks(s); a.scale = s->scale;
   fill_ws(a, s, ws);
-  run_chunk_index(s, cu, (int32_t*)a.table, (int32_t*)a.seq_chunk0, st);
-  return dispatch(s, [&]<typename E, int D, int C>() { launch_chunk_bwd_core<E, D, C>(a, st); });
+  if (!saved) run_chunk_index(s, cu, (int32_t*)a.table, (int32_t*)a.seq_chunk0, st);
+  return dispatch(s, [&]<typename E, int D, int C>() { launch_chunk_bwd_core<E, D, C>(a, st, !saved); });
 }
 
 }  // namespace gdn

@@ -9,6 +9,11 @@ namespace gdn {
 constexpr int kChunkThreads = 256;  // 4 waves per workgroup
 constexpr int kChunkWaves = kChunkThreads / kWave;
 
+// What a forward pass over the chunks produces: the output (o and the final
+// states), the per-chunk products the backward reads (the preparation pass's
+// pre-transposed operands, the entering states H_c and W), or both at once.
+enum FwdMode { kFwdOut = 1, kFwdStore = 2, kFwdBoth = 3 };
+
 struct ChunkArgs {
   // inputs
   const void* q;
@@ -400,7 +405,7 @@ inline int state_grid(int N, int Hk, int G, int NVT) { return ((N * Hk + 7) / 8)
 
 // State passes with one 1024-thread workgroup per (sequence, v-head), for
 // bf16, d = 128, chunk 64 (state_wide.hip).
-void launch_state_fwd_wide(const ChunkArgs& a, hipStream_t st, bool out_mode);
+void launch_state_fwd_wide(const ChunkArgs& a, hipStream_t st, int mode);
 void launch_state_bwd_wide(const ChunkArgs& a, hipStream_t st);
 template <typename E, int D, int C>
 constexpr bool use_wide_state() { return sizeof(E) == 2 && D == 128 && C == 64; }

@@ -243,8 +243,9 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
 //   OUT   = false: writes, per chunk, the entering state Hc and W (for the
 //                  backward pass), and the final state if asked
 // ---------------------------------------------------------------------------
-template <typename E, int D, int C, int DVT, bool OUT>
+template <typename E, int D, int C, int DVT, int MODE>
 __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
+  constexpr bool OUT = MODE & kFwdOut, STORE = MODE & kFwdStore;
   using S = StateSmem<E, D, C, DVT, OUT>;
   __shared__ S sm;
   constexpr bool LO = Split<E>::on;
@@ -326,7 +327,7 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
     }
     pU.store(&sm.U[0][0], S::LDU);
     pG.store(&sm.gam[0], C);
-    if constexpr (!OUT) {
+    if constexpr (STORE) {
       // state entering this chunk, for the backward pass
       float* Hg = a.Hc + slot * D * D;
 #pragma unroll
@@ -354,7 +355,7 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
           const int c = ct * 16 + acc_col(), r = rt * 16 + acc_row(0);
           st4_split<E>(&sm.Wt[c][r], &sm.Wtl[0][0] + c * S::LDCE + r, wv);
         }
-        if constexpr (!OUT) store_tile<float>(a.W + slot * C * D, D, rt * 16, col0 + ct * 16, wv, C);
+        if constexpr (STORE) store_tile<float>(a.W + slot * C * D, D, rt * 16, col0 + ct * 16, wv, C);
         if constexpr (OUT) {
           f32x4 xo = mm_tile<E, D>(zero4(), &sm.Q[rt * 16][0], S::LDQ, &sm.Ht[ct * 16][0], S::LDQ);
           if constexpr (LO) xo = mm_tile<E, D>(xo, &sm.Q[rt * 16][0], S::LDQ, &sm.Htl[ct * 16][0], S::LDQ);
@@ -431,27 +432,30 @@ template <typename E, int D>
 constexpr int state_dvt() { return D >= 32 ? 32 : D; }
 
 template <typename E, int D, int C>
-void launch_chunk_fwd_core(const ChunkArgs& a, hipStream_t st, bool out_mode) {
+void launch_chunk_fwd_core(const ChunkArgs& a, hipStream_t st, int mode) {
   constexpr int DVT = state_dvt<E, D>();
+  static const char* prep_name[4] = {"", "chunk_prep", "chunk_prep_bwd", "chunk_prep_save"};
+  static const char* state_name[4] = {"", "chunk_state_fwd", "chunk_state_store", "chunk_state_save"};
   dim3 gprep(a.max_chunks, a.Hk);
   {
-    GDN_PROF(out_mode ? "chunk_prep" : "chunk_prep_bwd", st);
+    GDN_PROF(prep_name[mode], st);
     constexpr int NTH = D >= 64 ? 512 : kChunkThreads;  // 8 waves for the wide heads
-    if (out_mode) prep_kernel<E, D, C, false, NTH><<<gprep, NTH, 0, st>>>(a);
+    if (mode == kFwdOut) prep_kernel<E, D, C, false, NTH><<<gprep, NTH, 0, st>>>(a);
     else prep_kernel<E, D, C, true, NTH><<<gprep, NTH, 0, st>>>(a);
   }
   dim3 gstate(state_grid(a.N, a.Hk, a.G, D / DVT));
-  GDN_PROF(out_mode ? "chunk_state_fwd" : "chunk_state_store", st);
+  GDN_PROF(state_name[mode], st);
   if constexpr (use_wide_state<E, D, C>()) {
-    launch_state_fwd_wide(a, st, out_mode);
+    launch_state_fwd_wide(a, st, mode);
     return;
   }
-  if (out_mode) state_fwd_kernel<E, D, C, DVT, true><<<gstate, kChunkThreads, 0, st>>>(a);
-  else state_fwd_kernel<E, D, C, DVT, false><<<gstate, kChunkThreads, 0, st>>>(a);
+  if (mode == kFwdOut) state_fwd_kernel<E, D, C, DVT, kFwdOut><<<gstate, kChunkThreads, 0, st>>>(a);
+  else if (mode == kFwdStore) state_fwd_kernel<E, D, C, DVT, kFwdStore><<<gstate, kChunkThreads, 0, st>>>(a);
+  else state_fwd_kernel<E, D, C, DVT, kFwdBoth><<<gstate, kChunkThreads, 0, st>>>(a);
 }
 
 // explicit instantiation helpers used by the dispatcher in chunk_bwd.hip
-#define GDN_INST_FWD(E, D, C) template void launch_chunk_fwd_core<E, D, C>(const ChunkArgs&, hipStream_t, bool);
+#define GDN_INST_FWD(E, D, C) template void launch_chunk_fwd_core<E, D, C>(const ChunkArgs&, hipStream_t, int);
 GDN_INST_FWD(bf16, 16, 16) GDN_INST_FWD(bf16, 16, 32) GDN_INST_FWD(bf16, 16, 64)
 GDN_INST_FWD(bf16, 32, 16) GDN_INST_FWD(bf16, 32, 32) GDN_INST_FWD(bf16, 32, 64)
 GDN_INST_FWD(bf16, 64, 16) GDN_INST_FWD(bf16, 64, 32) GDN_INST_FWD(bf16, 64, 64)

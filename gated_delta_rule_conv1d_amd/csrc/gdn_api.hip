@@ -40,6 +40,52 @@ bool stride_ok(const gdn_shape* s, int64_t stride, int64_t min_elems) {
 
 gdn_status launched() { return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
 
+// forward; with save, the workspace (backward-sized) keeps what the backward reads
+gdn_status chunk_fwd_call(const gdn_shape* shape, const void* q, const void* k, const void* v, int64_t tok_stride_qk,
+                          int64_t tok_stride_v, const float* g, const float* beta, const int32_t* cu_seqlens,
+                          const float* h0, void* o, float* ht, void* ws, size_t ws_bytes, bool save,
+                          gdn_stream stream) {
+  gdn_status st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  if ((st = check_chunk(shape)) != GDN_OK) return st;
+  const bool any = shape->total_tokens > 0;
+  if (!cu_seqlens || (any && (!q || !k || !v || !g || !beta || !o))) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return GDN_ERR_INVALID_ARG;
+  if (!stride_ok(shape, tok_stride_qk, (int64_t)shape->h_qk * shape->d_k) ||
+      !stride_ok(shape, tok_stride_v, (int64_t)shape->h_v * shape->d_v))
+    return GDN_ERR_INVALID_ARG;
+  const size_t need = save ? chunk_bwd_ws_bytes(shape) : chunk_fwd_ws_bytes(shape);
+  if (!ws || !aligned16(ws) || ws_bytes < need) return GDN_ERR_WORKSPACE;
+  if (!run_chunk_fwd(shape, q, k, v, tok_stride_qk, tok_stride_v, g, beta, cu_seqlens, h0, o, ht, ws, save,
+                     (hipStream_t)stream))
+    return GDN_ERR_UNSUPPORTED;
+  return launched();
+}
+
+// backward; with saved, the workspace holds what gdn_chunk_fwd_save left there
+gdn_status chunk_bwd_call(const gdn_shape* shape, const void* q, const void* k, const void* v, int64_t tok_stride_qk,
+                          int64_t tok_stride_v, const float* g, const float* beta, const int32_t* cu_seqlens,
+                          const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, float* dg,
+                          float* dbeta, float* dh0, void* ws, size_t ws_bytes, bool saved, gdn_stream stream) {
+  gdn_status st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  if ((st = check_chunk(shape)) != GDN_OK) return st;
+  const bool any = shape->total_tokens > 0;
+  if (!cu_seqlens || (any && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta)))
+    return GDN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_o) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv))
+    return GDN_ERR_INVALID_ARG;
+  if (!stride_ok(shape, tok_stride_qk, (int64_t)shape->h_qk * shape->d_k) ||
+      !stride_ok(shape, tok_stride_v, (int64_t)shape->h_v * shape->d_v))
+    return GDN_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws) || ws_bytes < chunk_bwd_ws_bytes(shape)) return GDN_ERR_WORKSPACE;
+  if (!run_chunk_bwd(shape, q, k, v, tok_stride_qk, tok_stride_v, g, beta, cu_seqlens, h0, d_o, dht, dq, dk, dv, dg,
+                     dbeta, dh0, ws, saved, (hipStream_t)stream))
+    return GDN_ERR_UNSUPPORTED;
+  return launched();
+}
+
 }  // namespace
 
 extern "C" {
@@ -112,20 +158,16 @@ size_t gdn_chunk_fwd_workspace(const gdn_shape* shape) {
 gdn_status gdn_chunk_fwd(const gdn_shape* shape, const void* q, const void* k, const void* v, int64_t tok_stride_qk,
                          int64_t tok_stride_v, const float* g, const float* beta, const int32_t* cu_seqlens,
                          const float* h0, void* o, float* ht, void* ws, size_t ws_bytes, gdn_stream stream) {
-  gdn_status st = check_shape(shape);
-  if (st != GDN_OK) return st;
-  if ((st = check_chunk(shape)) != GDN_OK) return st;
-  const bool any = shape->total_tokens > 0;
-  if (!cu_seqlens || (any && (!q || !k || !v || !g || !beta || !o))) return GDN_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return GDN_ERR_INVALID_ARG;
-  if (!stride_ok(shape, tok_stride_qk, (int64_t)shape->h_qk * shape->d_k) ||
-      !stride_ok(shape, tok_stride_v, (int64_t)shape->h_v * shape->d_v))
-    return GDN_ERR_INVALID_ARG;
-  if (!ws || !aligned16(ws) || ws_bytes < chunk_fwd_ws_bytes(shape)) return GDN_ERR_WORKSPACE;
-  if (!run_chunk_fwd(shape, q, k, v, tok_stride_qk, tok_stride_v, g, beta, cu_seqlens, h0, o, ht, ws,
-                     (hipStream_t)stream))
-    return GDN_ERR_UNSUPPORTED;
-  return launched();
+  return chunk_fwd_call(shape, q, k, v, tok_stride_qk, tok_stride_v, g, beta, cu_seqlens, h0, o, ht, ws, ws_bytes,
+                        false, stream);
+}
+
+gdn_status gdn_chunk_fwd_save(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                              int64_t tok_stride_qk, int64_t tok_stride_v, const float* g, const float* beta,
+                              const int32_t* cu_seqlens, const float* h0, void* o, float* ht, void* ws,
+                              size_t ws_bytes, gdn_stream stream) {
+  return chunk_fwd_call(shape, q, k, v, tok_stride_qk, tok_stride_v, g, beta, cu_seqlens, h0, o, ht, ws, ws_bytes,
+                        true, stream);
 }
 
 size_t gdn_chunk_bwd_workspace(const gdn_shape* shape) {
@@ -137,23 +179,17 @@ gdn_status gdn_chunk_bwd(const gdn_shape* shape, const void* q, const void* k, c
                          int64_t tok_stride_v, const float* g, const float* beta, const int32_t* cu_seqlens,
                          const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, float* dg,
                          float* dbeta, float* dh0, void* ws, size_t ws_bytes, gdn_stream stream) {
-  gdn_status st = check_shape(shape);
-  if (st != GDN_OK) return st;
-  if ((st = check_chunk(shape)) != GDN_OK) return st;
-  const bool any = shape->total_tokens > 0;
-  if (!cu_seqlens || (any && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta)))
-    return GDN_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_o) || !aligned16(dq) || !aligned16(dk) ||
-      !aligned16(dv))
-    return GDN_ERR_INVALID_ARG;
-  if (!stride_ok(shape, tok_stride_qk, (int64_t)shape->h_qk * shape->d_k) ||
-      !stride_ok(shape, tok_stride_v, (int64_t)shape->h_v * shape->d_v))
-    return GDN_ERR_INVALID_ARG;
-  if (!ws || !aligned16(ws) || ws_bytes < chunk_bwd_ws_bytes(shape)) return GDN_ERR_WORKSPACE;
-  if (!run_chunk_bwd(shape, q, k, v, tok_stride_qk, tok_stride_v, g, beta, cu_seqlens, h0, d_o, dht, dq, dk, dv, dg,
-                     dbeta, dh0, ws, (hipStream_t)stream))
-    return GDN_ERR_UNSUPPORTED;
-  return launched();
+  return chunk_bwd_call(shape, q, k, v, tok_stride_qk, tok_stride_v, g, beta, cu_seqlens, h0, d_o, dht, dq, dk, dv,
+                        dg, dbeta, dh0, ws, ws_bytes, false, stream);
+}
+
+gdn_status gdn_chunk_bwd_saved(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                               int64_t tok_stride_qk, int64_t tok_stride_v, const float* g, const float* beta,
+                               const int32_t* cu_seqlens, const float* h0, const void* d_o, const float* dht,
+                               void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0, void* ws,
+                               size_t ws_bytes, gdn_stream stream) {
+  return chunk_bwd_call(shape, q, k, v, tok_stride_qk, tok_stride_v, g, beta, cu_seqlens, h0, d_o, dht, dq, dk, dv,
+                        dg, dbeta, dh0, ws, ws_bytes, true, stream);
 }
 
 gdn_status gdn_norm_gate(const gdn_shape* shape, const void* o, const void* z, const void* w_norm, float eps, void* y,

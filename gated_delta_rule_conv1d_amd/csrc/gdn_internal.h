@@ -31,10 +31,10 @@ size_t chunk_fwd_ws_bytes(const gdn_shape* s);
 size_t chunk_bwd_ws_bytes(const gdn_shape* s);
 bool run_chunk_fwd(const gdn_shape* s, const void* q, const void* k, const void* v, int64_t sqk, int64_t sv,
                    const float* g, const float* beta, const int32_t* cu, const float* h0, void* o, float* ht,
-                   void* ws, hipStream_t st);
+                   void* ws, bool save, hipStream_t st);
 bool run_chunk_bwd(const gdn_shape* s, const void* q, const void* k, const void* v, int64_t sqk, int64_t sv,
                    const float* g, const float* beta, const int32_t* cu, const float* h0, const void* d_o,
                    const float* dht, void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0,
-                   void* ws, hipStream_t st);
+                   void* ws, bool saved, hipStream_t st);
 
 }  // namespace gdn

@@ -70,8 +70,9 @@ __device__ __forceinline__ void split8(const float4& a, const float4& b, M::frag
 
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
-template <bool OUT>
+template <int MODE>
 __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
+  constexpr bool OUT = MODE & kFwdOut, STORE = MODE & kFwdStore;
   constexpr int D = kD, C = kC;
   __shared__ FwdSmem sm;
   int n, h, vt;
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
       *reinterpret_cast<uint4*>(&sm.Ktl[e >> 3][(e & 7) * 8]) = kt_l[i];
     }
     if (tid < C) sm.gam[tid] = g_r;
-    if constexpr (!OUT) {  // state entering this chunk, for the backward pass
+    if constexpr (STORE) {  // state entering this chunk, for the backward pass
       float* Hg = a.Hc + slot * D * D;
 #pragma unroll
       for (int i = 0; i < kP2; ++i) store_tile<float>(Hg, D, rt2 * 16, i * 16, Hr[i], D);
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
     for (int i = 0; i < kP1; ++i) {
       const int c = (cb + i) * 16 + acc_col(), r = rt1 * 16 + acc_row(0);
       st4_split<E>(&sm.Wt[c][r], &sm.Wtl[c][r], x[i]);
-      if constexpr (!OUT) store_tile<float>(a.W + slot * C * D, D, rt1 * 16, (cb + i) * 16, x[i], C);
+      if constexpr (STORE) store_tile<float>(a.W + slot * C * D, D, rt1 * 16, (cb + i) * 16, x[i], C);
     }
     __syncthreads();
 
@@ -443,10 +444,11 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
 
 }  // namespace
 
-void launch_state_fwd_wide(const ChunkArgs& a, hipStream_t st, bool out_mode) {
+void launch_state_fwd_wide(const ChunkArgs& a, hipStream_t st, int mode) {
   const dim3 grid(state_grid(a.N, a.Hk, a.G, 1));
-  if (out_mode) state_fwd_wide_kernel<true><<<grid, kThreads, 0, st>>>(a);
-  else state_fwd_wide_kernel<false><<<grid, kThreads, 0, st>>>(a);
+  if (mode == kFwdOut) state_fwd_wide_kernel<kFwdOut><<<grid, kThreads, 0, st>>>(a);
+  else if (mode == kFwdStore) state_fwd_wide_kernel<kFwdStore><<<grid, kThreads, 0, st>>>(a);
+  else state_fwd_wide_kernel<kFwdBoth><<<grid, kThreads, 0, st>>>(a);
 }
 
 void launch_state_bwd_wide(const ChunkArgs& a, hipStream_t st) {

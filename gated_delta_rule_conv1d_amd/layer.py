@@ -24,6 +24,7 @@ class GatedDeltaNetLayer:
         self.l2_eps, self.norm_eps = l2_eps, norm_eps
         self.device = torch.device(device)
         self._ws: Dict[str, torch.Tensor] = {}
+        self._saved = False  # the backward workspace holds a forward's products
 
     def _buf(self, name: str, nbytes: int) -> torch.Tensor:
         t = self._ws.get(name)
@@ -37,12 +38,22 @@ class GatedDeltaNetLayer:
         nq = s.h_qk * s.d_k
         return y[:, :nq], y[:, nq:2 * nq], y[:, 2 * nq:]
 
-    def forward(self, x, w_conv, g, beta, cu_seqlens, z=None, w_norm=None, h0=None, want_ht=True):
+    def forward(self, x, w_conv, g, beta, cu_seqlens, z=None, w_norm=None, h0=None, want_ht=True,
+                for_backward=False):
+        """With for_backward=True the chunked recurrence keeps its per-chunk
+        products in this layer's backward workspace (gdn_chunk_fwd_save), and
+        the next backward() with the same inputs reads them instead of
+        recomputing them."""
         s = self.shape
         yc = B.conv1d(x, w_conv, cu_seqlens, s, self.l2_eps)
         q, k, v = self.split(yc)
-        o, ht = B.chunk_fwd(q, k, v, g, beta, cu_seqlens, s, h0=h0, want_ht=want_ht,
-                            ws=self._buf("fwd", B.chunk_fwd_workspace(s)))
+        if for_backward:
+            o, ht = B.chunk_fwd(q, k, v, g, beta, cu_seqlens, s, h0=h0, want_ht=want_ht,
+                                ws=self._buf("bwd", B.chunk_bwd_workspace(s)), save=True)
+        else:
+            o, ht = B.chunk_fwd(q, k, v, g, beta, cu_seqlens, s, h0=h0, want_ht=want_ht,
+                                ws=self._buf("fwd", B.chunk_fwd_workspace(s)))
+        self._saved = for_backward
         out = dict(y_conv=yc, o=o, ht=ht)
         if self.norm:
             out["y"] = B.norm_gate(o, z, w_norm, s, self.norm_eps)
@@ -63,7 +74,9 @@ class GatedDeltaNetLayer:
         dyc = torch.empty_like(fwd["y_conv"])
         dq, dk, dv = self.split(dyc)
         r = B.chunk_bwd(q, k, v, g, beta, cu_seqlens, s, d_o, h0=h0, dht=dht, dq=dq, dk=dk, dv=dv,
-                        want_dh0=h0 is not None, ws=self._buf("bwd", B.chunk_bwd_workspace(s)))
+                        want_dh0=h0 is not None, ws=self._buf("bwd", B.chunk_bwd_workspace(s)),
+                        saved=self._saved)
+        self._saved = False  # the saved products are consumed
         dx, dwc = B.conv1d_bwd(dyc, x, w_conv, cu_seqlens, s, self.l2_eps,
                                ws=self._buf("conv", B.conv1d_bwd_workspace(s, self.width)))
         res.update(d_o=d_o, dy_conv=dyc, dg=r["dg"], dbeta=r["dbeta"], dh0=r["dh0"], dx=dx, dw_conv=dwc)

@@ -162,6 +162,30 @@ gdn_status gdn_chunk_bwd(const gdn_shape* shape, const void* q, const void* k, c
                          float* dg, float* dbeta, float* dh0, void* ws, size_t ws_bytes,
                          gdn_stream stream);
 
+/* Training pair: the forward keeps, in a backward-sized workspace, the
+ * per-chunk products that gdn_chunk_bwd would otherwise recompute (the WY
+ * factors and their transposes, the state entering every chunk, W), and the
+ * backward reads them instead.  Same computation and same results, bit for
+ * bit, as gdn_chunk_fwd followed by gdn_chunk_bwd.  Pages: "Support Qwen35
+ * SFT", feature list (training the layer).
+ *   gdn_chunk_fwd_save: arguments as gdn_chunk_fwd; ws_bytes >=
+ *     gdn_chunk_bwd_workspace(shape).
+ *   gdn_chunk_bwd_saved: arguments as gdn_chunk_bwd, with the same ws and the
+ *     same shape, q, k, v, strides, g, beta, cu_seqlens and h0 (contents
+ *     unchanged) as the gdn_chunk_fwd_save call it follows; the workspace must
+ *     not be used by any other call in between.  The caller owns that pairing:
+ *     a mismatch is not detected and gives undefined results. */
+gdn_status gdn_chunk_fwd_save(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                              int64_t tok_stride_qk, int64_t tok_stride_v, const float* g,
+                              const float* beta, const int32_t* cu_seqlens, const float* h0, void* o,
+                              float* ht, void* ws, size_t ws_bytes, gdn_stream stream);
+gdn_status gdn_chunk_bwd_saved(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                               int64_t tok_stride_qk, int64_t tok_stride_v, const float* g,
+                               const float* beta, const int32_t* cu_seqlens, const float* h0,
+                               const void* d_o, const float* dht, void* dq, void* dk, void* dv,
+                               float* dg, float* dbeta, float* dh0, void* ws, size_t ws_bytes,
+                               gdn_stream stream);
+
 /* --------------------------------------------------------------------------
  * RMSNormGated epilogue.  Page: "[Qwen3.5 MoE] Add hybrid decoder model",
  * Summary (RMSNormGated).

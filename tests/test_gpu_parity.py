@@ -128,6 +128,34 @@ def test_chunk_fwd_bwd(dtype, d, chunk, Hk, Hv, lengths):
     assert_close(host(r["dh0"]), ref["dh0"], tol, "dh0")
 
 
+@pytest.mark.parametrize("dtype,d,chunk,Hk,Hv,lengths", CHUNK_CASES)
+def test_chunk_saved_pair_bit_identical(dtype, d, chunk, Hk, Hv, lengths):
+    """gdn_chunk_fwd_save + gdn_chunk_bwd_saved give the same bytes as
+    gdn_chunk_fwd + gdn_chunk_bwd (which recomputes the forward's products)."""
+    _print_case("chunk_saved", dtype=dtype, d=d, chunk=chunk, Hk=Hk, Hv=Hv, lengths=lengths)
+    cfg = small_cfg(dtype=dtype, d=d, chunk=chunk, Hk=Hk, Hv=Hv, lengths=lengths)
+    inp = synth.make_inputs(cfg)
+    q, k, v = qkv_inputs(cfg)
+    s = shape_of(cfg, scale=0.75)
+    cu = torch.from_numpy(inp["cu"]).cuda()
+    T = cfg.T
+    qd, kd, vd = to_dev(q.reshape(T, -1), dtype), to_dev(k.reshape(T, -1), dtype), to_dev(v.reshape(T, -1), dtype)
+    g, beta, h0 = f32(inp["g"]), f32(inp["beta"]), f32(inp["h0"])
+    d_o = to_dev(np.random.default_rng(9).standard_normal((T, cfg.h_v, d)).astype(np.float32), dtype)
+    dht = f32(np.random.default_rng(10).standard_normal((cfg.N, cfg.h_v, d, d)))
+    o1, ht1 = gdn.chunk_fwd(qd, kd, vd, g, beta, cu, s, h0=h0)
+    r1 = gdn.chunk_bwd(qd, kd, vd, g, beta, cu, s, d_o, h0=h0, dht=dht)
+    ws = torch.empty(gdn.chunk_bwd_workspace(s), dtype=torch.uint8, device="cuda")
+    o2, ht2 = gdn.chunk_fwd(qd, kd, vd, g, beta, cu, s, h0=h0, ws=ws, save=True)
+    r2 = gdn.chunk_bwd(qd, kd, vd, g, beta, cu, s, d_o, h0=h0, dht=dht, ws=ws, saved=True)
+    torch.cuda.synchronize()
+    same = lambda x, y: torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x.contiguous().view(torch.uint8),
+                                    y.view(torch.uint8) if y.dtype == torch.bfloat16 else y.contiguous().view(torch.uint8))
+    assert same(o1, o2) and same(ht1, ht2)
+    for key in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        assert same(r1[key], r2[key]), key
+
+
 def test_chunk_weak_decay_long_range():
     """A_log = -6: the state is carried across many chunks (long-range path)."""
     cfg = small_cfg(dtype="bf16", d=64, chunk=64, Hk=1, Hv=2, lengths=(1000, 300), weak=True)
