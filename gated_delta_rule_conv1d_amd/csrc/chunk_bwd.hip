@@ -507,8 +507,11 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
     const int h = j * a.G + gi;
     const int64_t slot = (int64_t)ci * a.Hv + h;
     const E* vg = (const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)h * D;
-    TileRegs<E, C, D> pV;  // in flight during the solve
+    TileRegs<E, C, D> pV;  // v rows, T and T^T (from the preparation pass)
+    TileRegs<float, C, C> pTm, pTt;
     pV.load(vg, a.sv, len);
+    pTm.load(a.Tw + slot * C * C, C, C);
+    pTt.load(a.Ttw + slot * C * C, C, C);
     for (int e = tid; e < C; e += kChunkThreads) {
       const float gm = a.gam[slot * C + e];
       sm.gam[e] = gm;
@@ -516,14 +519,9 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
       sm.beta[e] = e < len ? a.beta[(int64_t)(tok0 + e) * a.Hv + h] : 0.f;
       sm.em[e] = e < len ? __expf(a.gam[slot * C + len - 1] - gm) : 0.f;
     }
+    pTm.store(&sm.Tm[0][0], S::LDCF);
+    pTt.store(&sm.Tt[0][0], S::LDCF);
     __syncthreads();
-    // A = strict_lower(beta_r D_rs k_r.k_s)
-    for (int e = tid; e < C * C; e += kChunkThreads) {
-      const int r = e / C, s = e % C;
-      sm.av.Am[r][s] = (s < r) ? sm.beta[r] * __expf(sm.gam[r] - sm.gam[s]) * sm.Skk[r][s] : 0.f;
-    }
-    __syncthreads();
-    unit_lower_inverse<C, S::LDCF>(sm.av.Am, sm.Tm, sm.Tt, sm.r.Xs);
 
     auto ta = [&](int rt) {
       return [&, rt](int r, int k, float* o) { ld_row<float, KPL>(&sm.Tt[rt * 16 + r][k], o); };
@@ -774,7 +772,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsPlan {
   size_t table, seq0, Wk, U, P, Kt, Ktl, gam, end_fwd;
-  size_t Ptr, Krh, Krl, Wth, Wtl, Qth, Qtl, Hc, W, dHn, dW, dWt, dT, dWkt, dQs, dKh, dP, hdot, end_bwd;
+  size_t Ptr, Tw, Ttw, Krh, Krl, Wth, Wtl, Qth, Qtl, Hc, W, dHn, dW, dWt, dT, dWkt, dQs, dKh, dP, hdot, end_bwd;
 };
 
 static WsPlan plan(const gdn_shape* s) {
@@ -792,6 +790,8 @@ static WsPlan plan(const gdn_shape* s) {
   p.gam = o; o = align256(o + M * Hv * C * 4);
   p.end_fwd = o;
   p.Ptr = o; o = align256(o + M * Hv * C * C * 4);
+  p.Tw = o; o = align256(o + M * Hv * C * C * 4);
+  p.Ttw = o; o = align256(o + M * Hv * C * C * 4);
   p.Krh = o; o = align256(o + M * Hv * C * D * es);
   p.Krl = o; o = align256(o + M * Hv * C * D * es);
   p.Wth = o; o = align256(o + M * Hv * D * C * es);
@@ -828,6 +828,8 @@ static void fill_ws(ChunkArgs& a, const gdn_shape* s, void* ws) {
   a.Ktl = b + p.Ktl;
   a.gam = (float*)(b + p.gam);
   a.Ptr = (float*)(b + p.Ptr);
+  a.Tw = (float*)(b + p.Tw);
+  a.Ttw = (float*)(b + p.Ttw);
   a.Krh = b + p.Krh;
   a.Krl = b + p.Krl;
   a.Wth = b + p.Wth;
