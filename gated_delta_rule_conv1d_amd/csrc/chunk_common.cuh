@@ -351,19 +351,29 @@ struct ColRegs {
   static constexpr int V = 16 / (int)sizeof(T);
   static constexpr int TOTAL = COLS * (R / V);
   static constexpr int N = (TOTAL + NTH - 1) / NTH;
+  static_assert(sizeof(T) == 2 || sizeof(T) == 4, "16- or 32-bit elements");
   uint4 r[N];
+  // Buffer loads through a resource that covers rows [0, rows_valid): rows
+  // past it read as zero in hardware, so every load issues at once, with no
+  // branch and no per-load address.
   __device__ __forceinline__ void load(const T* g, int64_t ld, int rows_valid) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(g), 0, (int)((int64_t)rows_valid * ld * (int64_t)sizeof(T)), 0x00020000);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int e = threadIdx.x + i * NTH;
       T* v = reinterpret_cast<T*>(&r[i]);
+      const int c = e % COLS, r0 = (e / COLS) * V;
+      // one per-lane offset; the row step (uniform) goes in the scalar offset
+      const int off = (int)(((int64_t)r0 * ld + c) * (int64_t)sizeof(T));
+      const int step = (int)(ld * (int64_t)sizeof(T));
 #pragma unroll
-      for (int u = 0; u < V; ++u) v[u] = from_f<T>(0.f);
-      if (e < TOTAL) {
-        const int c = e % COLS, r0 = (e / COLS) * V;
-#pragma unroll
-        for (int u = 0; u < V; ++u)
-          if (r0 + u < rows_valid) v[u] = g[(int64_t)(r0 + u) * ld + c];
+      for (int u = 0; u < V; ++u) {
+        if constexpr (sizeof(T) == 2) {
+          v[u] = __builtin_bit_cast(T, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs, off, u * step, 0));
+        } else {
+          v[u] = __builtin_bit_cast(T, (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, off, u * step, 0));
+        }
       }
     }
   }

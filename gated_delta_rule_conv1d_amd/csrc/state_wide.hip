@@ -70,6 +70,25 @@ __device__ __forceinline__ void split8(const float4& a, const float4& b, M::frag
 
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
+// A buffer resource over [base, base + bytes): loads take a 32-bit offset
+// (out-of-range offsets read zero), so the per-lane operand is a small
+// loop-invariant offset instead of a 64-bit address the compiler may spill.
+struct Buf {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ Buf(const void* base, int64_t bytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000)) {}
+  __device__ __forceinline__ uint4 u4(int off) const {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+  __device__ __forceinline__ float4 f4(int off) const {
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  }
+  __device__ __forceinline__ float f1(int off) const {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  }
+  __device__ __forceinline__ M::frag fr(int off) const { return __builtin_bit_cast(M::frag, u4(off)); }
+};
+
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
   constexpr bool OUT = MODE & kFwdOut, STORE = MODE & kFwdStore;
@@ -102,50 +121,60 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
   };
 
   // staged operands of the next chunk
-  uint4 kt_h[kKR], kt_l[kKR];   // this thread's pieces of K~^T (hi, lo)
+  static_assert(kKR == 2, "two 16-byte pieces of each [D][C] tile per thread");
+  uint4 kt_h0, kt_h1, kt_l0, kt_l1;  // this thread's pieces of K~^T (hi, lo); named, so they stay in registers
   float g_r = 0.f;
   M::frag wkf[4], qf[4];
   f32x4 uf[kP1];
   float4 pf[2][2];
   auto load_shared = [&](int ci) {
     const int64_t slot = (int64_t)ci * a.Hv + h;
-#pragma unroll
-    for (int i = 0; i < kKR; ++i) {
-      kt_h[i] = reinterpret_cast<const uint4*>((const E*)a.Kt + slot * D * C)[tid + i * kThreads];
-      kt_l[i] = reinterpret_cast<const uint4*>((const E*)a.Ktl + slot * D * C)[tid + i * kThreads];
-    }
-    if (tid < C) g_r = a.gam[slot * C + tid];
+    const Buf kh((const E*)a.Kt + slot * D * C, D * C * 2), kl((const E*)a.Ktl + slot * D * C, D * C * 2);
+    kt_h0 = kh.u4(tid * 16);
+    kt_h1 = kh.u4((tid + kThreads) * 16);
+    kt_l0 = kl.u4(tid * 16);
+    kt_l1 = kl.u4((tid + kThreads) * 16);
+    g_r = Buf(a.gam + slot * C, C * 4).f1((tid & (C - 1)) * 4);  // every thread loads; threads < C use it
   };
+  const int a_off = ((rt1 * 16 + r16) * D + kq) * 2;   // lane's A-fragment offset in a [C][D] bf16 tile
   auto load_p1 = [&](int ci, int tok0, int len) {
     const int64_t slot = (int64_t)ci * a.Hv + h;
-    const E* wk = (const E*)a.Wk + slot * C * D + (rt1 * 16 + r16) * D + kq;
+    const Buf wk((const E*)a.Wk + slot * C * D, C * D * 2);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) wkf[ks] = fr(wk + ks * 32);
-    if constexpr (OUT) {
-      const int row = rt1 * 16 + r16;
-      const E* qp = (const E*)a.q + (int64_t)(tok0 + (row < len ? row : 0)) * a.sqk + (int64_t)j * D + kq;
+    for (int ks = 0; ks < 4; ++ks) wkf[ks] = wk.fr(a_off + ks * 64);
+    if constexpr (OUT) {  // q rows of the chunk; rows past len fall outside the buffer and read zero
+      const Buf qb((const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D, (int64_t)len * a.sqk * 2);
+      const int q_off = (int)(((int64_t)(rt1 * 16 + r16) * a.sqk + kq) * 2);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qf[ks] = row < len ? fr(qp + ks * 32) : M::zero();
+      for (int ks = 0; ks < 4; ++ks) qf[ks] = qb.fr(q_off + ks * 64);
     }
-    const float* up = a.U + slot * C * D;
+    const Buf ub(a.U + slot * C * D, C * D * 4);
 #pragma unroll
     for (int i = 0; i < kP1; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) uf[i][e] = up[(rt1 * 16 + acc_row(e)) * D + (cb + i) * 16 + acc_col()];
+      for (int e = 0; e < 4; ++e) uf[i][e] = ub.f1(((rt1 * 16 + acc_row(e)) * D + (cb + i) * 16 + acc_col()) * 4);
   };
   auto load_p2 = [&](int ci) {
-    const float* pp = a.P + ((int64_t)ci * a.Hv + h) * C * C + (rt1 * 16 + r16) * C + kq;
+    const Buf pb(a.P + ((int64_t)ci * a.Hv + h) * C * C, C * C * 4);
+    const int p_off = ((rt1 * 16 + r16) * C + kq) * 4;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      pf[ks][0] = ld4(pp + ks * 32);
-      pf[ks][1] = ld4(pp + ks * 32 + 4);
+      pf[ks][0] = pb.f4(p_off + ks * 128);
+      pf[ks][1] = pb.f4(p_off + ks * 128 + 16);
     }
   };
 
+  // the sequence's chunks are consecutive table entries: (first token, length)
+  // follow from cu_seqlens, with no table load inside the serial loop
   const int c0 = a.seq_chunk0[n], c1 = a.seq_chunk0[n + 1];
+  const int s0 = a.cu[n], s1 = a.cu[n + 1];
+  auto entry = [&](int ci) {
+    const int t = s0 + (ci - c0) * C;
+    return make_int4(n, t, min(C, s1 - t), 0);
+  };
   int4 ent = make_int4(0, 0, 0, 0);
   if (c0 < c1) {
-    ent = chunk_entry(a.table, c0);
+    ent = entry(c0);
     load_shared(c0);
     load_p1(c0, ent.y, ent.z);
     if constexpr (OUT) load_p2(c0);
@@ -155,24 +184,27 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
     const int tok0 = ent.y, len = ent.z;
     const int64_t slot = (int64_t)ci * a.Hv + h;
     __syncthreads();  // the previous chunk is done with K~^T and W^T, and H^T is written
-#pragma unroll
-    for (int i = 0; i < kKR; ++i) {
-      const int e = tid + i * kThreads;  // 16-byte piece: row e / 8, columns (e % 8) * 8 ..
-      *reinterpret_cast<uint4*>(&sm.Kt[e >> 3][(e & 7) * 8]) = kt_h[i];
-      *reinterpret_cast<uint4*>(&sm.Ktl[e >> 3][(e & 7) * 8]) = kt_l[i];
+    {  // 16-byte piece e: row e / 8, columns (e % 8) * 8 ..
+      const int e0 = tid, e1 = tid + kThreads;
+      *reinterpret_cast<uint4*>(&sm.Kt[e0 >> 3][(e0 & 7) * 8]) = kt_h0;
+      *reinterpret_cast<uint4*>(&sm.Kt[e1 >> 3][(e1 & 7) * 8]) = kt_h1;
+      *reinterpret_cast<uint4*>(&sm.Ktl[e0 >> 3][(e0 & 7) * 8]) = kt_l0;
+      *reinterpret_cast<uint4*>(&sm.Ktl[e1 >> 3][(e1 & 7) * 8]) = kt_l1;
     }
     if (tid < C) sm.gam[tid] = g_r;
-    if constexpr (STORE) {  // state entering this chunk, for the backward pass
-      float* Hg = a.Hc + slot * D * D;
-#pragma unroll
-      for (int i = 0; i < kP2; ++i) store_tile<float>(Hg, D, rt2 * 16, i * 16, Hr[i], D);
-    }
     __syncthreads();
     const bool more = ci + 1 < c1;
     int4 nent = ent;
     if (more) {
-      nent = chunk_entry(a.table, ci + 1);
+      nent = entry(ci + 1);
       load_shared(ci + 1);
+    }
+    // Stores go after the prefetch loads: the wait for a load also waits for
+    // every earlier vector-memory access of the wave.
+    if constexpr (STORE) {  // state entering this chunk, for the backward pass
+      float* Hg = a.Hc + slot * D * D;
+#pragma unroll
+      for (int i = 0; i < kP2; ++i) store_tile<float>(Hg, D, rt2 * 16, i * 16, Hr[i], D);
     }
 
     // phase 1: W = U - Wk H and diag(Gam) Q H on this wave's tiles
@@ -300,44 +332,53 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
   };
 
   // staged operands of the next chunk (reverse order)
-  uint4 kr_h[kKR], kr_l[kKR];       // this thread's pieces of the K~ rows
+  uint4 kr_h0, kr_h1, kr_l0, kr_l1;  // this thread's pieces of the K~ rows (named: registers)
   ColRegs<E, C, D, kThreads> pO;    // dO of the chunk, gathered column-wise
   float g_r = 0.f;
   float4 ptf[2][2];                 // P^T rows of this wave's dW tiles
   M::frag qth[2], qtl[2], wth[2], wtl[2];  // (Gam q)^T and Wk^T rows of its dH tiles
   auto load_shared = [&](int ci, int tok0, int len) {
     const int64_t slot = (int64_t)ci * a.Hv + h;
-#pragma unroll
-    for (int i = 0; i < kKR; ++i) {
-      kr_h[i] = reinterpret_cast<const uint4*>((const E*)a.Krh + slot * C * D)[tid + i * kThreads];
-      kr_l[i] = reinterpret_cast<const uint4*>((const E*)a.Krl + slot * C * D)[tid + i * kThreads];
-    }
+    const Buf kh((const E*)a.Krh + slot * C * D, C * D * 2), kl((const E*)a.Krl + slot * C * D, C * D * 2);
+    kr_h0 = kh.u4(tid * 16);
+    kr_h1 = kh.u4((tid + kThreads) * 16);
+    kr_l0 = kl.u4(tid * 16);
+    kr_l1 = kl.u4((tid + kThreads) * 16);
     pO.load((const E*)a.d_o + (int64_t)tok0 * a.Hv * D + (int64_t)h * D, (int64_t)a.Hv * D, len);
-    if (tid < C) g_r = a.gam[slot * C + tid];
+    g_r = Buf(a.gam + slot * C, C * 4).f1((tid & (C - 1)) * 4);  // every thread loads; threads < C use it
   };
+  const int p_off = ((rt1 * 16 + r16) * C + kq) * 4;   // lane's fragment offset in a [C][C] fp32 tile
+  const int t_off = ((rt2 * 16 + r16) * C + kq) * 2;   // and in a [D][C] bf16 tile
   auto load_p1 = [&](int ci) {
-    const float* pp = a.Ptr + ((int64_t)ci * a.Hv + h) * C * C + (rt1 * 16 + r16) * C + kq;
+    const Buf pb(a.Ptr + ((int64_t)ci * a.Hv + h) * C * C, C * C * 4);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      ptf[ks][0] = ld4(pp + ks * 32);
-      ptf[ks][1] = ld4(pp + ks * 32 + 4);
+      ptf[ks][0] = pb.f4(p_off + ks * 128);
+      ptf[ks][1] = pb.f4(p_off + ks * 128 + 16);
     }
   };
   auto load_p2 = [&](int ci) {
-    const int64_t off = ((int64_t)ci * a.Hv + h) * D * C + (rt2 * 16 + r16) * C + kq;
+    const int64_t o = ((int64_t)ci * a.Hv + h) * D * C;
+    const Buf qh((const E*)a.Qth + o, D * C * 2), ql((const E*)a.Qtl + o, D * C * 2);
+    const Buf wh((const E*)a.Wth + o, D * C * 2), wl((const E*)a.Wtl + o, D * C * 2);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      qth[ks] = fr((const E*)a.Qth + off + ks * 32);
-      qtl[ks] = fr((const E*)a.Qtl + off + ks * 32);
-      wth[ks] = fr((const E*)a.Wth + off + ks * 32);
-      wtl[ks] = fr((const E*)a.Wtl + off + ks * 32);
+      qth[ks] = qh.fr(t_off + ks * 64);
+      qtl[ks] = ql.fr(t_off + ks * 64);
+      wth[ks] = wh.fr(t_off + ks * 64);
+      wtl[ks] = wl.fr(t_off + ks * 64);
     }
   };
 
   const int c0 = a.seq_chunk0[n], c1 = a.seq_chunk0[n + 1];
+  const int s0 = a.cu[n], s1 = a.cu[n + 1];
+  auto entry = [&](int ci) {
+    const int t = s0 + (ci - c0) * C;
+    return make_int4(n, t, min(C, s1 - t), 0);
+  };
   int4 ent = make_int4(0, 0, 0, 0);
   if (c0 < c1) {
-    ent = chunk_entry(a.table, c1 - 1);
+    ent = entry(c1 - 1);
     load_shared(c1 - 1, ent.y, ent.z);
     load_p1(c1 - 1);
     load_p2(c1 - 1);
@@ -347,65 +388,62 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
     const int len = ent.z;
     const int64_t slot = (int64_t)ci * a.Hv + h;
     __syncthreads();  // the previous chunk is done with [dO^T | dW^T] and K~, and dH^T is written
-#pragma unroll
-    for (int i = 0; i < kKR; ++i) {
-      const int e = tid + i * kThreads;  // 16-byte piece: row e / 16, columns (e % 16) * 8 ..
-      *reinterpret_cast<uint4*>(&sm.Kr[e >> 4][(e & 15) * 8]) = kr_h[i];
-      *reinterpret_cast<uint4*>(&sm.Krl[e >> 4][(e & 15) * 8]) = kr_l[i];
+    {  // 16-byte piece e: row e / 16, columns (e % 16) * 8 ..
+      const int e0 = tid, e1 = tid + kThreads;
+      *reinterpret_cast<uint4*>(&sm.Kr[e0 >> 4][(e0 & 15) * 8]) = kr_h0;
+      *reinterpret_cast<uint4*>(&sm.Kr[e1 >> 4][(e1 & 15) * 8]) = kr_h1;
+      *reinterpret_cast<uint4*>(&sm.Krl[e0 >> 4][(e0 & 15) * 8]) = kr_l0;
+      *reinterpret_cast<uint4*>(&sm.Krl[e1 >> 4][(e1 & 15) * 8]) = kr_l1;
     }
     pO.store(&sm.OW[0][0], kLD2C);
     if (tid < C) sm.gam[tid] = g_r;
+    __syncthreads();
+    const bool more = ci > c0;
+    int4 nent = ent;
+    if (more) {
+      nent = entry(ci - 1);
+      load_shared(ci - 1, nent.y, nent.z);
+    }
+
+    // phase 1: dW = scale P^T dO + K~ dH on this wave's tiles, one tile at a time
+    M::frag ph[2], pl[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) split8(ptf[ks][0], ptf[ks][1], ph[ks], pl[ks]);
+    if (more) load_p1(ci - 1);  // P^T of the next chunk
+    // Stores go after this chunk's prefetch loads: the wait for a load also
+    // waits for every earlier vector-memory access of the wave.
     {  // gradient w.r.t. the state leaving this chunk
       float* dst = a.dHn + slot * D * D;
 #pragma unroll
       for (int i = 0; i < kP2; ++i) store_tile<float>(dst, D, rt2 * 16, i * 16, dH[i], D);
     }
-    __syncthreads();
-    const bool more = ci > c0;
-    int4 nent = ent;
-    if (more) {
-      nent = chunk_entry(a.table, ci - 1);
-      load_shared(ci - 1, nent.y, nent.z);
-    }
-
-    // phase 1: dW = scale P^T dO + K~ dH on this wave's tiles
-    f32x4 p[kP1], kd[kP1];
-#pragma unroll
-    for (int i = 0; i < kP1; ++i) p[i] = kd[i] = zero4();
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      M::frag ph, pl;
-      split8(ptf[ks][0], ptf[ks][1], ph, pl);
-#pragma unroll
-      for (int i = 0; i < kP1; ++i) {
-        const M::frag b = fr(&sm.OW[(cb + i) * 16 + r16][ks * 32 + kq]);
-        p[i] = M::mma(ph, b, p[i]);
-        p[i] = M::mma(pl, b, p[i]);
-      }
-    }
-    if (more) load_p1(ci - 1);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const M::frag ah = fr(&sm.Kr[rt1 * 16 + r16][ks * 32 + kq]);
-      const M::frag al = fr(&sm.Krl[rt1 * 16 + r16][ks * 32 + kq]);
-#pragma unroll
-      for (int i = 0; i < kP1; ++i) {
-        const int c = (cb + i) * 16 + r16;
-        const M::frag bh = fr(&sm.dHt[c][ks * 32 + kq]);
-        const M::frag bl = fr(&sm.dHtl[c][ks * 32 + kq]);
-        kd[i] = M::mma(ah, bh, kd[i]);
-        kd[i] = M::mma(ah, bl, kd[i]);
-        kd[i] = M::mma(al, bh, kd[i]);
-      }
-    }
 #pragma unroll
     for (int i = 0; i < kP1; ++i) {
+      const int c = (cb + i) * 16 + r16;
+      f32x4 p = zero4(), kd = zero4();
 #pragma unroll
-      for (int e = 0; e < 4; ++e) kd[i][e] += a.scale * p[i][e];  // kd <- dW
-      store_tile<float>(a.dW + slot * C * D, D, rt1 * 16, (cb + i) * 16, kd[i], C);
-      store_tile_t(a.dWt + slot * D * C, C, rt1 * 16, (cb + i) * 16, kd[i]);
-      const int c = (cb + i) * 16 + acc_col(), r = rt1 * 16 + acc_row(0);
-      st4_split<E>(&sm.OW[c][C + r], &sm.dWl[c][r], kd[i]);
+      for (int ks = 0; ks < 2; ++ks) {
+        const M::frag b = fr(&sm.OW[c][ks * 32 + kq]);
+        p = M::mma(ph[ks], b, p);
+        p = M::mma(pl[ks], b, p);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const M::frag ah = fr(&sm.Kr[rt1 * 16 + r16][ks * 32 + kq]);
+        const M::frag al = fr(&sm.Krl[rt1 * 16 + r16][ks * 32 + kq]);
+        const M::frag bh = fr(&sm.dHt[c][ks * 32 + kq]);
+        const M::frag bl = fr(&sm.dHtl[c][ks * 32 + kq]);
+        kd = M::mma(ah, bh, kd);
+        kd = M::mma(ah, bl, kd);
+        kd = M::mma(al, bh, kd);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kd[e] += a.scale * p[e];  // kd <- dW
+      store_tile<float>(a.dW + slot * C * D, D, rt1 * 16, (cb + i) * 16, kd, C);
+      store_tile_t(a.dWt + slot * D * C, C, rt1 * 16, (cb + i) * 16, kd);
+      const int cc = (cb + i) * 16 + acc_col(), r = rt1 * 16 + acc_row(0);
+      st4_split<E>(&sm.OW[cc][C + r], &sm.dWl[cc][r], kd);
+      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
 
@@ -428,6 +466,7 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) dH[i][e] = gl * dH[i][e] + a.scale * y1[e] - y2[e];
+      __builtin_amdgcn_sched_barrier(0);  // keep the next tile's fragment loads out of this one's registers
     }
     if (more) load_p2(ci - 1);
     write_dHt();  // phase 1 (the only reader of dH^T) is over for every wave
