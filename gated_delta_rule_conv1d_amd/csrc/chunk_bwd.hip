@@ -538,25 +538,32 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
     }
     __syncthreads();
     E* dvg = (E*)a.dv + (int64_t)tok0 * a.sv + (int64_t)h * D;
+    // row partials are summed in-lane over a wave's CT column tiles, then
+    // across the 16 lanes; the first column slot gets the total, the rest 0
+    float pu[4];
 #pragma unroll
     for (int i = 0; i < RT * CT; ++i) {
       if (act) {
         const int rt = rt0 + i / CT, ct = ct0 + i % CT;
         const f32x4 xu = mm_gen<E, C, LO, LO>(zero4(), ta(rt), xb(ct));
         f32x4 dvv;
-        float pu[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = rt * 16 + acc_row(e), c = ct * 16 + acc_col();
           dvv[e] = sm.beta[r] * xu[e];
-          pu[e] = xu[e] * to_f<E>(sm.av.Vs[r][c]);
+          const float t = xu[e] * to_f<E>(sm.av.Vs[r][c]);
+          pu[e] = i % CT == 0 ? t : pu[e] + t;
         }
         store_tile<E>(dvg, a.sv, rt * 16, ct * 16, dvv, len);
+        if (i % CT == CT - 1) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pu[e] = group_sum<16>(pu[e]);
-        if ((lane & 15) == 0) {
+          for (int e = 0; e < 4; ++e) pu[e] = group_sum<16>(pu[e]);
+          if ((lane & 15) == 0) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sm.pCD[0][ct][rt * 16 + acc_row(e)] = pu[e];
+            for (int cj = 0; cj < CT; ++cj)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) sm.pCD[0][ct0 + cj][rt * 16 + acc_row(e)] = cj == 0 ? pu[e] : 0.f;
+          }
         }
       }
     }
@@ -568,23 +575,28 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
       rX.store(&sm.r.Xf[0][0], S::LDCF);
     }
     __syncthreads();
+    float pw[4];
 #pragma unroll
     for (int i = 0; i < RT * CT; ++i) {
       if (act) {
         const int rt = rt0 + i / CT, ct = ct0 + i % CT;
         const f32x4 xw = mm_gen<E, C, LO, LO>(zero4(), ta(rt), xb(ct));
-        float pw[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = rt * 16 + acc_row(e), c = ct * 16 + acc_col();
-          pw[e] = xw[e] * to_f<E>(sm.QKt[c][C + r]);
+          const float t = xw[e] * to_f<E>(sm.QKt[c][C + r]);
+          pw[e] = i % CT == 0 ? t : pw[e] + t;
           dK[i / CT][i % CT][e] += sm.beta[r] * sm.Gm[r] * xw[e];
         }
+        if (i % CT == CT - 1) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pw[e] = group_sum<16>(pw[e]);
-        if ((lane & 15) == 0) {
+          for (int e = 0; e < 4; ++e) pw[e] = group_sum<16>(pw[e]);
+          if ((lane & 15) == 0) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sm.pCD[1][ct][rt * 16 + acc_row(e)] = pw[e];
+            for (int cj = 0; cj < CT; ++cj)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) sm.pCD[1][ct0 + cj][rt * 16 + acc_row(e)] = cj == 0 ? pw[e] : 0.f;
+          }
         }
       }
     }
@@ -618,6 +630,22 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
     __syncthreads();
     pP.store(&sm.Tm[0][0], S::LDCF);  // T is no longer needed
     pdP.store(&sm.Tt[0][0], S::LDCF);
+    // dQs and dKh of this wave's tiles: in flight during the next two passes
+    f32x4 qs[RT][CT], kh[RT][CT];
+    if (act) {
+      const float* dQsg = a.dQs + slot * C * D;
+      const float* dKhg = a.dKh + slot * C * D;
+#pragma unroll
+      for (int ri = 0; ri < RT; ++ri)
+#pragma unroll
+        for (int cj = 0; cj < CT; ++cj)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = (rt0 + ri) * 16 + acc_row(e), c = (ct0 + cj) * 16 + acc_col();
+            qs[ri][cj][e] = dQsg[r * D + c];
+            kh[ri][cj][e] = dKhg[r * D + c];
+          }
+    }
     __syncthreads();
     // C x C pass: A~, dS, and the dgamma / dbeta terms of A and P
     for (int t = w; t < NT * NT; t += kChunkWaves) {
@@ -677,32 +705,39 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
     __syncthreads();
     // dQ += dQs + dS K;   dK += dKh + [dS^T | A~ + A~^T] [Q ; K]
     if (act) {
-      const float* dQsg = a.dQs + slot * C * D;
-      const float* dKhg = a.dKh + slot * C * D;
 #pragma unroll
-      for (int ri = 0; ri < RT; ++ri)
+      for (int ri = 0; ri < RT; ++ri) {
+        const int rt = rt0 + ri;
+        float pq[4] = {0.f, 0.f, 0.f, 0.f}, pk[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int cj = 0; cj < CT; ++cj) {
-          const int rt = rt0 + ri, ct = ct0 + cj;
-          float pq[4], pk[4];
+        for (int cj = 0; cj < CT; ++cj)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int r = rt * 16 + acc_row(e), c = ct * 16 + acc_col();
-            const float qsv = dQsg[r * D + c];
-            const float khv = dKhg[r * D + c];
+            const int r = rt * 16 + acc_row(e), c = (ct0 + cj) * 16 + acc_col();
+            const float qsv = qs[ri][cj][e];
+            const float khv = kh[ri][cj][e];
             dQ[ri][cj][e] += qsv;
             dK[ri][cj][e] += khv;
-            pq[e] = group_sum<16>(qsv * to_f<E>(sm.QKt[c][r]));
-            pk[e] = group_sum<16>(khv * to_f<E>(sm.QKt[c][C + r]));
+            pq[e] += qsv * to_f<E>(sm.QKt[c][r]);
+            pk[e] += khv * to_f<E>(sm.QKt[c][C + r]);
           }
-          if ((lane & 15) == 0) {
+        // the wave's CT column tiles are summed in-lane; its first slot gets
+        // the total, the others zero
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pq[e] = group_sum<16>(pq[e]);
+          pk[e] = group_sum<16>(pk[e]);
+        }
+        if ((lane & 15) == 0) {
+#pragma unroll
+          for (int cj = 0; cj < CT; ++cj)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              sm.pCD[2][ct][rt * 16 + acc_row(e)] = pq[e];
-              sm.pCD[3][ct][rt * 16 + acc_row(e)] = pk[e];
+              sm.pCD[2][ct0 + cj][rt * 16 + acc_row(e)] = cj == 0 ? pq[e] : 0.f;
+              sm.pCD[3][ct0 + cj][rt * 16 + acc_row(e)] = cj == 0 ? pk[e] : 0.f;
             }
-          }
         }
+      }
       const int r0 = rt0 * 16, c0 = ct0 * 16;
       mm_blk<E, C, RT, CT, LO, false>(dQ, &sm.r.s.dSh[r0][0], LO ? &sm.r.s.dSl[0][0] + r0 * S::LDCE : nullptr,
                                       S::LDCE, &sm.QKt[c0][C], nullptr, S::LD2C);

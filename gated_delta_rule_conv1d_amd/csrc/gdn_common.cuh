@@ -297,10 +297,28 @@ __device__ __forceinline__ void ld_row(const T* p, float* out) {  // N consecuti
 // ---------------------------------------------------------------------------
 // Reductions
 // ---------------------------------------------------------------------------
+// One DPP move of v within each row of 16 lanes (CDNA3/4 DPP controls:
+// quad_perm 0x00-0xff, row_mirror 0x140, row_half_mirror 0x141).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of WIDTH lanes, the same value in every lane of a
+// group.  Inside a row the partners come from DPP: lane ^ 1 and lane ^ 2 by
+// quad permutes, then the mirrored lane of the half row and of the row, which
+// holds the sum of the partner quad / half (all its lanes agree by then), so
+// the addition tree is that of xor partners 1, 2, 4, 8.  Across rows the
+// partners come through ds_bpermute.
 template <int WIDTH>
-__device__ __forceinline__ float group_sum(float v) {  // sum over aligned groups of WIDTH lanes
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(WIDTH >= 1 && WIDTH <= kWave && (WIDTH & (WIDTH - 1)) == 0, "power-of-two group");
+  if constexpr (WIDTH >= 2) v += dpp_f<0xb1>(v);   // quad_perm [1,0,3,2]
+  if constexpr (WIDTH >= 4) v += dpp_f<0x4e>(v);   // quad_perm [2,3,0,1]
+  if constexpr (WIDTH >= 8) v += dpp_f<0x141>(v);  // row_half_mirror
+  if constexpr (WIDTH >= 16) v += dpp_f<0x140>(v); // row_mirror
 #pragma unroll
-  for (int off = 1; off < WIDTH; off <<= 1) v += __shfl_xor(v, off, kWave);
+  for (int off = 16; off < WIDTH; off <<= 1) v += __shfl_xor(v, off, kWave);
   return v;
 }
 
