@@ -450,24 +450,24 @@ struct GradBSmem {
     float Xf[D][LDCF];                            // dW^T or dWk^T
     struct { float dT[C][LDCF]; float M1t[C][LDCF]; } m;
     struct { E dSh[C][LDCE]; E dSl[Split<E>::on ? C : 1][LDCE]; float At[C][LDCF]; } s;  // dS (hi, lo), A~
-    float Xs[kChunkWaves][16][20];
   } r;
   float gam[C], beta[C], Gm[C], em[C];
   float pCD[4][ND][C];   // row partials of C x D tiles: dXu.v, dXw.k, dQs.q, dKh.k
   float pCC[5][NT][C];   // dA D Skk rows, dA*A rows, dA*A cols, dP*P rows, dP*P cols
 };
 
-template <typename E, int D, int C>
-__global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
+template <typename E, int D, int C, int NTH>
+__global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
   using S = GradBSmem<E, D, C>;
   using M = Mma<E>;
   constexpr int KPL = M::KPL;
   constexpr bool LO = Split<E>::on;
   __shared__ S sm;
   constexpr int NT = S::NT, ND = S::ND;
+  constexpr int NW = NTH / kWave;
   // [C][D] output tiles per wave: a block of RT row tiles x CT adjacent column
   // tiles (waves past the row tiles idle)
-  constexpr int NWC = ND >= kChunkWaves ? kChunkWaves : ND, NWR = kChunkWaves / NWC;
+  constexpr int NWC = ND >= NW ? NW : ND, NWR = NW / NWC;
   constexpr int RT = NT >= NWR ? NT / NWR : 1, CT = ND / NWC;
   const int ci = blockIdx.x, j = blockIdx.y;
   const int4 ent = chunk_entry(a.table, ci);
@@ -479,11 +479,11 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
   const E* qg = (const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D;
   const E* kg = (const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D;
 
-  rows2s_t<E, C, D>(&sm.QKt[0][0], S::LD2C, qg, a.sqk, len, nullptr, 1.f);
-  rows2s_t<E, C, D>(&sm.QKt[0][C], S::LD2C, kg, a.sqk, len, nullptr, 1.f);
+  rows2s_t<E, C, D, NTH>(&sm.QKt[0][0], S::LD2C, qg, a.sqk, len, nullptr, 1.f);
+  rows2s_t<E, C, D, NTH>(&sm.QKt[0][C], S::LD2C, kg, a.sqk, len, nullptr, 1.f);
   __syncthreads();
   // K K^T (exact bf16 products, fp32 sums), shared by the k-head's v-heads
-  for (int t = w; t < NT * NT; t += kChunkWaves) {
+  for (int t = w; t < NT * NT; t += NW) {
     const int rt = t / NT, ct = t % NT;
     const f32x4 skk = mm_gen<E, D, false, false>(
         zero4(),
@@ -507,12 +507,12 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
     const int h = j * a.G + gi;
     const int64_t slot = (int64_t)ci * a.Hv + h;
     const E* vg = (const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)h * D;
-    TileRegs<E, C, D> pV;  // v rows, T and T^T (from the preparation pass)
-    TileRegs<float, C, C> pTm, pTt;
+    TileRegs<E, C, D, NTH> pV;  // v rows, T and T^T (from the preparation pass)
+    TileRegs<float, C, C, NTH> pTm, pTt;
     pV.load(vg, a.sv, len);
     pTm.load(a.Tw + slot * C * C, C, C);
     pTt.load(a.Ttw + slot * C * C, C, C);
-    for (int e = tid; e < C; e += kChunkThreads) {
+    for (int e = tid; e < C; e += NTH) {
       const float gm = a.gam[slot * C + e];
       sm.gam[e] = gm;
       sm.Gm[e] = __expf(gm);
@@ -531,7 +531,7 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
     };
     // dXu = T^T dW -> dv and <dXu, v>
     {
-      TileRegs<float, D, C> rX;
+      TileRegs<float, D, C, NTH> rX;
       rX.load(a.dWt + slot * D * C, C, D);
       pV.store(&sm.av.Vs[0][0], S::LDV);
       rX.store(&sm.r.Xf[0][0], S::LDCF);
@@ -570,7 +570,7 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
     __syncthreads();
     // dXw = T^T dWk -> dK and <dXw, k>
     {
-      TileRegs<float, D, C> rX;
+      TileRegs<float, D, C, NTH> rX;
       rX.load(a.dWkt + slot * D * C, C, D);
       rX.store(&sm.r.Xf[0][0], S::LDCF);
     }
@@ -602,23 +602,23 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
     }
     __syncthreads();
     // M1 = dT T^T (fp32 MFMA), stored transposed; dA = strict_lower(-T^T M1)
-    TileRegs<float, C, C> pP, pdP;  // in flight during dA
+    TileRegs<float, C, C, NTH> pP, pdP;  // in flight during dA
     {
-      TileRegs<float, C, C> rT;
+      TileRegs<float, C, C, NTH> rT;
       rT.load(a.dT + slot * C * C, C, C);
       pP.load(a.P + slot * C * C, C, C);
       pdP.load(a.dP + slot * C * C, C, C);
       rT.store(&sm.r.m.dT[0][0], S::LDCF);
     }
     __syncthreads();
-    for (int t = w; t < NT * NT; t += kChunkWaves) {
+    for (int t = w; t < NT * NT; t += NW) {
       const int rt = t / NT, ct = t % NT;
       const f32x4 m = mm_tile<float, C>(zero4(), &sm.r.m.dT[rt * 16][0], S::LDCF, &sm.Tm[ct * 16][0], S::LDCF);
 #pragma unroll
       for (int e = 0; e < 4; ++e) sm.r.m.M1t[ct * 16 + acc_col()][rt * 16 + acc_row(e)] = m[e];
     }
     __syncthreads();
-    for (int t = w; t < NT * NT; t += kChunkWaves) {
+    for (int t = w; t < NT * NT; t += NW) {
       const int rt = t / NT, ct = t % NT;
       const f32x4 m = mm_tile<float, C>(zero4(), &sm.Tt[rt * 16][0], S::LDCF, &sm.r.m.M1t[ct * 16][0], S::LDCF);
 #pragma unroll
@@ -630,25 +630,9 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
     __syncthreads();
     pP.store(&sm.Tm[0][0], S::LDCF);  // T is no longer needed
     pdP.store(&sm.Tt[0][0], S::LDCF);
-    // dQs and dKh of this wave's tiles: in flight during the next two passes
-    f32x4 qs[RT][CT], kh[RT][CT];
-    if (act) {
-      const float* dQsg = a.dQs + slot * C * D;
-      const float* dKhg = a.dKh + slot * C * D;
-#pragma unroll
-      for (int ri = 0; ri < RT; ++ri)
-#pragma unroll
-        for (int cj = 0; cj < CT; ++cj)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = (rt0 + ri) * 16 + acc_row(e), c = (ct0 + cj) * 16 + acc_col();
-            qs[ri][cj][e] = dQsg[r * D + c];
-            kh[ri][cj][e] = dKhg[r * D + c];
-          }
-    }
     __syncthreads();
     // C x C pass: A~, dS, and the dgamma / dbeta terms of A and P
-    for (int t = w; t < NT * NT; t += kChunkWaves) {
+    for (int t = w; t < NT * NT; t += NW) {
       const int rt = t / NT, ct = t % NT;
       float rb[4], ra[4], rp[4], ca = 0.f, cp = 0.f;
 #pragma unroll
@@ -695,7 +679,7 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
     }
     __syncthreads();
     // [dS^T | A~ + A~^T] as rows (P and dP' are consumed)
-    for (int e = tid; e < C * C; e += kChunkThreads) {
+    for (int e = tid; e < C * C; e += NTH) {
       const int sr = e / C, r = e % C;
       sm.TS.h[sr][r] = sm.r.s.dSh[r][sr];
       if constexpr (LO) sm.TS.l[sr][r] = sm.r.s.dSl[r][sr];
@@ -704,6 +688,22 @@ __global__ __launch_bounds__(kChunkThreads) void grad_b_kernel(ChunkArgs a) {
     }
     __syncthreads();
     // dQ += dQs + dS K;   dK += dKh + [dS^T | A~ + A~^T] [Q ; K]
+    // dQs and dKh of this wave's tiles
+    f32x4 qs[RT][CT], kh[RT][CT];
+    if (act) {
+      const float* dQsg = a.dQs + slot * C * D;
+      const float* dKhg = a.dKh + slot * C * D;
+#pragma unroll
+      for (int ri = 0; ri < RT; ++ri)
+#pragma unroll
+        for (int cj = 0; cj < CT; ++cj)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = (rt0 + ri) * 16 + acc_row(e), c = (ct0 + cj) * 16 + acc_col();
+            qs[ri][cj][e] = dQsg[r * D + c];
+            kh[ri][cj][e] = dKhg[r * D + c];
+          }
+    }
     if (act) {
 #pragma unroll
       for (int ri = 0; ri < RT; ++ri) {
@@ -906,7 +906,9 @@ static void launch_chunk_bwd_core(const ChunkArgs& a, hipStream_t st, bool recom
     grad_a_kernel<E, D, C><<<dim3(a.max_chunks, a.Hv), kChunkThreads, 0, st>>>(a);
   }
   GDN_PROF("chunk_grad_b", st);
-  grad_b_kernel<E, D, C><<<dim3(a.max_chunks, a.Hk), kChunkThreads, 0, st>>>(a);
+  // 8 waves where the [C][D] tiles give each one a column strip of its own
+  constexpr int GB_THREADS = (D >= 64 && C >= 64) ? 2 * kChunkThreads : kChunkThreads;
+  grad_b_kernel<E, D, C, GB_THREADS><<<dim3(a.max_chunks, a.Hk), GB_THREADS, 0, st>>>(a);
 }
 
 // Calls f.template operator()<E, D, C>() for the runtime (dtype, d, chunk)
