@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kChunkThreads) void state_bwd_kernel(ChunkArgs a) {
 //   dKh = diag(e) W dHn^T                dP  = scale dO W^T (lower-incl., rows < len)
 //   hdot = <Hc, dHn>
 // ---------------------------------------------------------------------------
-template <typename E, int D, int C>
+template <typename E, int D, int C, int NTH>
 struct GradASmem {
   static constexpr int LO = Split<E>::on ? 1 : 0;
   static constexpr int LDQ = D + Pad<E>::E16;
@@ -223,18 +223,19 @@ struct GradASmem {
   E Vs[C][LDQ];                 // V, then dWk lo
   E Ks[LO ? 1 : C][LDQ];        // K (float operands only)
   float bs[C], gm[C], em[C];
-  float red[kChunkThreads];
+  float red[NTH];
 };
 
-template <typename E, int D, int C>
-__global__ __launch_bounds__(kChunkThreads) void grad_a_kernel(ChunkArgs a) {
-  using S = GradASmem<E, D, C>;
+template <typename E, int D, int C, int NTH>
+__global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
+  using S = GradASmem<E, D, C, NTH>;
   __shared__ S sm;
   constexpr bool LO = Split<E>::on;
   constexpr int NT = C / 16, ND = D / 16;
-  constexpr int RT = NT >= 2 ? 2 : 1;      // block rows (C side)
-  constexpr int CD = ND >= 4 ? 4 : ND;     // block cols on the D side
-  constexpr int CC = NT >= 2 ? 2 : 1;      // block cols on the C side
+  constexpr int NW = NTH / kWave;
+  constexpr int RT = NT >= 2 ? 2 : 1;                           // block rows (C side)
+  constexpr int CD = ND >= 4 ? (NW > kChunkWaves ? 2 : 4) : ND;  // block cols on the D side
+  constexpr int CC = NT >= 2 && NW <= kChunkWaves ? 2 : 1;      // block cols on the C side
   const int ci = blockIdx.x, h = blockIdx.y;
   const int4 ent = chunk_entry(a.table, ci);
   if (ent.x < 0) return;
@@ -251,9 +252,9 @@ __global__ __launch_bounds__(kChunkThreads) void grad_a_kernel(ChunkArgs a) {
   E* Kst = LO ? &sm.Hl[0][0] : &sm.Ks[0][0];  // K reuses the lo half of the H region
 
   {  // stage Hc, dO, dW, V
-    TileRegs<float, D, D> rH;
-    TileRegs<E, C, D> rO, rV;
-    TileRegs<float, C, D> rW;
+    TileRegs<float, D, D, NTH> rH;
+    TileRegs<E, C, D, NTH> rO, rV;
+    TileRegs<float, C, D, NTH> rW;
     rH.load(Hc, D, D);
     rO.load(dog, ldo, len);
     rW.load(a.dW + slot * C * D, D, C);
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(kChunkThreads) void grad_a_kernel(ChunkArgs a) {
     rW.template store_split<E>(&sm.Xh[0][0], Xlo, S::LDQ);
     rV.store(&sm.Vs[0][0], S::LDQ);
   }
-  for (int e = tid; e < C; e += kChunkThreads) {
+  for (int e = tid; e < C; e += NTH) {
     const float g = a.gam[slot * C + e];
     sm.bs[e] = e < len ? a.beta[(int64_t)(tok0 + e) * a.Hv + h] : 0.f;
     sm.gm[e] = __expf(g);
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(kChunkThreads) void grad_a_kernel(ChunkArgs a) {
   __syncthreads();
 
   // (a) dQs = scale Gam dO Hc^T (to workspace); dT1 = dW V^T kept for (c)
-  for_blocks<NT, ND, RT, CD>([&](int r0, int c0) {
+  for_blocks<NT, ND, RT, CD, NW>([&](int r0, int c0) {
     f32x4 acc[RT][CD];
     zero_blk(acc);
     mm_blk<E, D, RT, CD, false, LO>(acc, &sm.Os[r0 * 16][0], nullptr, S::LDQ, &sm.Hh[c0 * 16][0],
@@ -288,12 +289,12 @@ __global__ __launch_bounds__(kChunkThreads) void grad_a_kernel(ChunkArgs a) {
       }
   });
   constexpr int NBT = (NT / RT) * (NT / CC);
-  constexpr int NBW = (NBT + kChunkWaves - 1) / kChunkWaves;
+  constexpr int NBW = (NBT + NW - 1) / NW;
   f32x4 dT1[NBW][RT][CC];
 #pragma unroll
   for (int bi = 0; bi < NBW; ++bi) {
     zero_blk(dT1[bi]);
-    const int b = wave_id() + bi * kChunkWaves;
+    const int b = wave_id() + bi * NW;
     if (b < NBT) {
       const int r0 = (b / (NT / CC)) * RT, c0 = (b % (NT / CC)) * CC;
       mm_blk<E, D, RT, CC, LO, false>(dT1[bi], &sm.Xh[r0 * 16][0], LO ? &sm.Xl[r0 * 16][0] : nullptr, S::LDQ,
@@ -303,7 +304,7 @@ __global__ __launch_bounds__(kChunkThreads) void grad_a_kernel(ChunkArgs a) {
   __syncthreads();  // dO and V are no longer read
 
   // (b) dWk = -dW Hc^T: hi -> Os, lo -> Vs; transposed fp32 copy to workspace
-  for_blocks<NT, ND, RT, CD>([&](int r0, int c0) {
+  for_blocks<NT, ND, RT, CD, NW>([&](int r0, int c0) {
     f32x4 acc[RT][CD];
     zero_blk(acc);
     mm_blk<E, D, RT, CD, LO, LO>(acc, &sm.Xh[r0 * 16][0], LO ? &sm.Xl[r0 * 16][0] : nullptr, S::LDQ,
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(kChunkThreads) void grad_a_kernel(ChunkArgs a) {
   });
   __syncthreads();  // Hc is no longer read
   {
-    TileRegs<E, C, D> rK;
+    TileRegs<E, C, D, NTH> rK;
     rK.load((const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D, a.sqk, len);
     rK.store(Kst, S::LDQ);
   }
@@ -333,7 +334,7 @@ __global__ __launch_bounds__(kChunkThreads) void grad_a_kernel(ChunkArgs a) {
   // (c) dT = beta_s dT1 + beta_s Gam_s dWk K^T
 #pragma unroll
   for (int bi = 0; bi < NBW; ++bi) {
-    const int b = wave_id() + bi * kChunkWaves;
+    const int b = wave_id() + bi * NW;
     if (b < NBT) {
       const int r0 = (b / (NT / CC)) * RT, c0 = (b % (NT / CC)) * CC;
       f32x4 acc[RT][CC];
@@ -355,19 +356,19 @@ __global__ __launch_bounds__(kChunkThreads) void grad_a_kernel(ChunkArgs a) {
   __syncthreads();  // dWk and K are no longer read
 
   {  // stage dHn (and <Hc, dHn>), W, dO again
-    TileRegs<float, D, D> rD, rH;
-    TileRegs<float, C, D> rW;
-    TileRegs<E, C, D> rO;
+    TileRegs<float, D, D, NTH> rD, rH;
+    TileRegs<float, C, D, NTH> rW;
+    TileRegs<E, C, D, NTH> rO;
     rD.load(dHn, D, D);
     rH.load(Hc, D, D);
     rW.load(a.W + slot * C * D, D, C);
     rO.load(dog, ldo, len);
     float hs = 0.f;
 #pragma unroll
-    for (int i = 0; i < TileRegs<float, D, D>::N; ++i) {
+    for (int i = 0; i < TileRegs<float, D, D, NTH>::N; ++i) {
       const float* x = reinterpret_cast<const float*>(&rD.r[i]);
       const float* y = reinterpret_cast<const float*>(&rH.r[i]);
-      if (threadIdx.x + i * kChunkThreads < TileRegs<float, D, D>::TOTAL)
+      if (threadIdx.x + i * NTH < TileRegs<float, D, D, NTH>::TOTAL)
         hs += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
     }
     sm.red[tid] = hs;
@@ -378,11 +379,11 @@ __global__ __launch_bounds__(kChunkThreads) void grad_a_kernel(ChunkArgs a) {
   __syncthreads();
   if (tid == 0) {
     float s = 0.f;
-    for (int i = 0; i < kChunkThreads; ++i) s += sm.red[i];
+    for (int i = 0; i < NTH; ++i) s += sm.red[i];
     a.hdot[slot] = s;
   }
   // (d) dKh = e W dHn^T;  dP = scale dO W^T
-  for_blocks<NT, ND, RT, CD>([&](int r0, int c0) {
+  for_blocks<NT, ND, RT, CD, NW>([&](int r0, int c0) {
     f32x4 acc[RT][CD];
     zero_blk(acc);
     mm_blk<E, D, RT, CD, LO, LO>(acc, &sm.Xh[r0 * 16][0], LO ? &sm.Xl[r0 * 16][0] : nullptr, S::LDQ,
@@ -397,7 +398,7 @@ __global__ __launch_bounds__(kChunkThreads) void grad_a_kernel(ChunkArgs a) {
         store_tile<float>(a.dKh + slot * C * D, D, (r0 + i) * 16, (c0 + jj) * 16, v, C);
       }
   });
-  for_blocks<NT, NT, RT, CC>([&](int r0, int c0) {
+  for_blocks<NT, NT, RT, CC, NW>([&](int r0, int c0) {
     f32x4 acc[RT][CC];
     zero_blk(acc);
     mm_blk<E, D, RT, CC, false, LO>(acc, &sm.Os[r0 * 16][0], nullptr, S::LDQ, &sm.Xh[c0 * 16][0],
@@ -888,7 +889,7 @@ template <typename E, int D, int C>
 constexpr bool fits() {
   constexpr size_t lim = 160 * 1024;
   return sizeof(PrepSmem<E, D, C>) <= lim && sizeof(StateSmem<E, D, C, (D >= 32 ? 32 : D), true>) <= lim &&
-         sizeof(StateBwdSmem<E, D, C, (D >= 32 ? 32 : D)>) <= lim && sizeof(GradASmem<E, D, C>) <= lim &&
+         sizeof(StateBwdSmem<E, D, C, (D >= 32 ? 32 : D)>) <= lim && sizeof(GradASmem<E, D, C, 2 * kChunkThreads>) <= lim &&
          sizeof(GradBSmem<E, D, C>) <= lim;
 }
 
@@ -903,7 +904,8 @@ static void launch_chunk_bwd_core(const ChunkArgs& a, hipStream_t st, bool recom
   }
   {
     GDN_PROF("chunk_grad_a", st);
-    grad_a_kernel<E, D, C><<<dim3(a.max_chunks, a.Hv), kChunkThreads, 0, st>>>(a);
+    constexpr int GA_THREADS = (D >= 64 && C >= 64) ? 2 * kChunkThreads : kChunkThreads;
+    grad_a_kernel<E, D, C, GA_THREADS><<<dim3(a.max_chunks, a.Hv), GA_THREADS, 0, st>>>(a);
   }
   GDN_PROF("chunk_grad_b", st);
   // 8 waves where the [C][D] tiles give each one a column strip of its own

@@ -406,16 +406,16 @@ __device__ __forceinline__ bool state_block(int bid, int N, int Hk, int G, int N
 
 
 // visit the RT x CT blocks of an NR x NC tile grid owned by this wave
-template <int NR, int NC, int RT, int CT, typename F>
+template <int NR, int NC, int RT, int CT, int NW = kChunkWaves, typename F>
 __device__ __forceinline__ void for_blocks(F&& f) {
   static_assert(NR % RT == 0 && NC % CT == 0, "block shape must divide the tile grid");
   constexpr int NBC = NC / CT, NB = (NR / RT) * NBC;
-  for (int b = wave_id(); b < NB; b += kChunkWaves) f((b / NBC) * RT, (b % NBC) * CT);
+  for (int b = wave_id(); b < NB; b += NW) f((b / NBC) * RT, (b % NBC) * CT);
 }
 
 inline int state_grid(int N, int Hk, int G, int NVT) { return ((N * Hk + 7) / 8) * 8 * G * NVT; }
 
-// State passes with one 1024-thread workgroup per (sequence, v-head), for
+// State passes with one 512-thread workgroup per (sequence, v-head), for
 // bf16, d = 128, chunk 64 (state_wide.hip).
 void launch_state_fwd_wide(const ChunkArgs& a, hipStream_t st, int mode);
 void launch_state_bwd_wide(const ChunkArgs& a, hipStream_t st);
