@@ -222,17 +222,31 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
           Vec<E>::store((E*)a.Krh + o, val);
           if constexpr (Split<E>::on) Vec<E>::store((E*)a.Krl + o, lo);
         }
-        for (int e = tid; e < D * (C / V); e += NTH) {
-          const int d = e % D, s0 = (e / D) * V;
-          float val[V], lo[V];
+        // Q^T through V x V register blocks: a thread reads V rows of V
+        // consecutive d and writes V rows of Q^T; adjacent lanes take adjacent
+        // d blocks (conflict-free LDS reads), and the C / V lanes sharing a d
+        // block write whole rows of Q^T
+        constexpr int DB = D / V, SB = C / V, DF = DB >= 8 ? 8 : DB;
+        for (int e = tid; e < DB * SB; e += NTH) {
+          const int d0 = (e % DF + DF * (e / (DF * SB))) * V, s0 = ((e / DF) % SB) * V;
+          float blk[V][V], gs[V];
 #pragma unroll
           for (int i = 0; i < V; ++i) {
-            val[i] = __expf(sm.gam[s0 + i]) * to_f<E>(sm.Qs[s0 + i][d]);
-            lo[i] = val[i] - to_f<E>(from_f<E>(val[i]));
+            Vec<E>::load(&sm.Qs[s0 + i][d0], blk[i]);
+            gs[i] = __expf(sm.gam[s0 + i]);
           }
-          const int64_t o = slot * D * C + (int64_t)d * C + s0;
-          Vec<E>::store((E*)a.Qth + o, val);
-          if constexpr (Split<E>::on) Vec<E>::store((E*)a.Qtl + o, lo);
+#pragma unroll
+          for (int dd = 0; dd < V; ++dd) {
+            float val[V], lo[V];
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+              val[i] = gs[i] * blk[i][dd];
+              lo[i] = val[i] - to_f<E>(from_f<E>(val[i]));
+            }
+            const int64_t o = slot * D * C + (int64_t)(d0 + dd) * C + s0;
+            Vec<E>::store((E*)a.Qth + o, val);
+            if constexpr (Split<E>::on) Vec<E>::store((E*)a.Qtl + o, lo);
+          }
         }
       }
     }
