@@ -453,6 +453,7 @@ struct GradBSmem {
     struct { E dSh[C][LDCE]; E dSl[Split<E>::on ? C : 1][LDCE]; float At[C][LDCF]; } s;  // dS (hi, lo), A~
   } r;
   float gam[C], beta[C], Gm[C], em[C];
+  float hdot;            // <H_c, dH_n> of the current v-head
   float pCD[4][ND][C];   // row partials of C x D tiles: dXu.v, dXw.k, dQs.q, dKh.k
   float pCC[5][NT][C];   // dA D Skk rows, dA*A rows, dA*A cols, dP*P rows, dP*P cols
 };
@@ -520,6 +521,7 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
       sm.beta[e] = e < len ? a.beta[(int64_t)(tok0 + e) * a.Hv + h] : 0.f;
       sm.em[e] = e < len ? __expf(a.gam[slot * C + len - 1] - gm) : 0.f;
     }
+    if (tid == 0) sm.hdot = a.hdot[slot];  // read now, used by the row pass at the end
     pTm.store(&sm.Tm[0][0], S::LDCF);
     pTt.store(&sm.Tt[0][0], S::LDCF);
     __syncthreads();
@@ -770,17 +772,10 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
         dgam = sq - tk + sm.beta[r] * sm.Gm[r] * sw + (ar - ac) + (pr - pc);
         if (r >= len) dgam = tk = 0.f;
       }
-      float tks = tk;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) tks += __shfl_xor(tks, off, kWave);
-      if (r == len - 1) dgam += sm.Gm[len - 1] * a.hdot[slot] + tks;
+      const float tks = wave_sum(tk);
+      if (r == len - 1) dgam += sm.Gm[len - 1] * sm.hdot + tks;
       // reverse inclusive scan: dg_r = sum_{r' >= r} dgam_{r'}
-      float x = dgam;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const float y = __shfl_down(x, off, kWave);
-        if (r + off < kWave) x += y;
-      }
+      const float x = wave_suffix_sum(dgam);
       if (r < len) {
         a.dg[(int64_t)(tok0 + r) * a.Hv + h] = x;
         a.dbeta[(int64_t)(tok0 + r) * a.Hv + h] = dbeta;

@@ -322,6 +322,40 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Sum over the whole wave, the same value in every lane: row sums by DPP, then
+// the four row totals read out lane by lane and added in row order.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group_sum<16>(v);
+  const int b = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  return ((r0 + r1) + r2) + r3;
+}
+
+// Inclusive suffix sum over the wave: lane i gets the sum of lanes i..63.
+// Inside each row of 16 a Hillis-Steele scan on DPP row_shl (lane i reads lane
+// i + k of its row; past the row end the identity 0 comes in), then each lane
+// adds the totals of the rows above its own, read out lane by lane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_or_zero(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_suffix_sum(float v) {
+  v += dpp_or_zero<0x101>(v);  // row_shl:1
+  v += dpp_or_zero<0x102>(v);  // row_shl:2
+  v += dpp_or_zero<0x104>(v);  // row_shl:4
+  v += dpp_or_zero<0x108>(v);  // row_shl:8
+  const int b = __builtin_bit_cast(int, v);
+  const float t1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  const float t2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  const float t3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  const float s2 = t3, s1 = t2 + t3, s0 = t1 + s1;
+  const int row = lane_id() >> 4;
+  return v + (row == 0 ? s0 : row == 1 ? s1 : row == 2 ? s2 : 0.f);
+}
+
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + __expf(-x)); }
 
 
