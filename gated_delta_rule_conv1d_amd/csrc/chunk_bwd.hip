@@ -440,7 +440,13 @@ struct GradBSmem {
   union {
     struct {
       float Tm[C][LDCF];  // T, later P
-      float Tt[C][LDCF];  // T^T, later dP'
+      union {
+        struct {
+          E TtH[C][LDCE];  // T^T as MFMA operand parts (hi, lo)
+          E TtL[Split<E>::on ? C : 1][LDCE];
+        };
+        float dPm[C][LDCF];  // dP', after T^T
+      };
     };
     struct {
       E h[C][LD2C];
@@ -448,8 +454,8 @@ struct GradBSmem {
     } TS;  // [dS^T | A~ + A~^T] rows, hi + lo, after the C x C pass
   };
   union U {
-    float Xf[D][LDCF];                            // dW^T or dWk^T
-    struct { float dT[C][LDCF]; float M1t[C][LDCF]; } m;
+    struct { E h[D][LDCE]; E l[Split<E>::on ? D : 1][LDCE]; } x;  // dW^T or dWk^T (hi, lo)
+    struct { float dT[C][LDCF]; E M1h[C][LDCE]; E M1l[Split<E>::on ? C : 1][LDCE]; } m;  // dT, (dT T^T)^T
     struct { E dSh[C][LDCE]; E dSl[Split<E>::on ? C : 1][LDCE]; float At[C][LDCF]; } s;  // dS (hi, lo), A~
   } r;
   float gam[C], beta[C], Gm[C], em[C];
@@ -523,23 +529,27 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
     }
     if (tid == 0) sm.hdot = a.hdot[slot];  // read now, used by the row pass at the end
     pTm.store(&sm.Tm[0][0], S::LDCF);
-    pTt.store(&sm.Tt[0][0], S::LDCF);
-    __syncthreads();
-
-    auto ta = [&](int rt) {
-      return [&, rt](int r, int k, float* o) { ld_row<float, KPL>(&sm.Tt[rt * 16 + r][k], o); };
-    };
-    auto xb = [&](int ct) {
-      return [&, ct](int c, int k, float* o) { ld_row<float, KPL>(&sm.r.Xf[ct * 16 + c][k], o); };
-    };
+    // fp32 operands of the products below are split into their MFMA parts once
+    // here, not per tile
+    E* const TtL = LO ? &sm.TtL[0][0] : nullptr;
+    E* const XL = LO ? &sm.r.x.l[0][0] : nullptr;
+    pTt.template store_split<E>(&sm.TtH[0][0], TtL, S::LDCE);
     // dXu = T^T dW -> dv and <dXu, v>
     {
       TileRegs<float, D, C, NTH> rX;
       rX.load(a.dWt + slot * D * C, C, D);
       pV.store(&sm.av.Vs[0][0], S::LDV);
-      rX.store(&sm.r.Xf[0][0], S::LDCF);
+      rX.template store_split<E>(&sm.r.x.h[0][0], XL, S::LDCE);
     }
     __syncthreads();
+    // tile (rt, ct) of T^T X (X = dW^T or dWk^T staged in r.x)
+    auto txt = [&](int rt, int ct) {
+      f32x4 acc[1][1];
+      zero_blk(acc);
+      mm_blk<E, C, 1, 1, LO, LO>(acc, &sm.TtH[rt * 16][0], LO ? TtL + rt * 16 * S::LDCE : nullptr, S::LDCE,
+                                 &sm.r.x.h[ct * 16][0], LO ? XL + ct * 16 * S::LDCE : nullptr, S::LDCE);
+      return acc[0][0];
+    };
     E* dvg = (E*)a.dv + (int64_t)tok0 * a.sv + (int64_t)h * D;
     // row partials are summed in-lane over a wave's CT column tiles, then
     // across the 16 lanes; the first column slot gets the total, the rest 0
@@ -548,7 +558,7 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
     for (int i = 0; i < RT * CT; ++i) {
       if (act) {
         const int rt = rt0 + i / CT, ct = ct0 + i % CT;
-        const f32x4 xu = mm_gen<E, C, LO, LO>(zero4(), ta(rt), xb(ct));
+        const f32x4 xu = txt(rt, ct);
         f32x4 dvv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -575,7 +585,7 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
     {
       TileRegs<float, D, C, NTH> rX;
       rX.load(a.dWkt + slot * D * C, C, D);
-      rX.store(&sm.r.Xf[0][0], S::LDCF);
+      rX.template store_split<E>(&sm.r.x.h[0][0], XL, S::LDCE);
     }
     __syncthreads();
     float pw[4];
@@ -583,7 +593,7 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
     for (int i = 0; i < RT * CT; ++i) {
       if (act) {
         const int rt = rt0 + i / CT, ct = ct0 + i % CT;
-        const f32x4 xw = mm_gen<E, C, LO, LO>(zero4(), ta(rt), xb(ct));
+        const f32x4 xw = txt(rt, ct);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = rt * 16 + acc_row(e), c = ct * 16 + acc_col();
@@ -617,13 +627,21 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
     for (int t = w; t < NT * NT; t += NW) {
       const int rt = t / NT, ct = t % NT;
       const f32x4 m = mm_tile<float, C>(zero4(), &sm.r.m.dT[rt * 16][0], S::LDCF, &sm.Tm[ct * 16][0], S::LDCF);
+      E* const M1L = LO ? &sm.r.m.M1l[0][0] : nullptr;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sm.r.m.M1t[ct * 16 + acc_col()][rt * 16 + acc_row(e)] = m[e];
+      for (int e = 0; e < 4; ++e) {
+        const int c = ct * 16 + acc_col(), r = rt * 16 + acc_row(e);
+        split_store<E>(&sm.r.m.M1h[c][r], LO ? M1L + c * S::LDCE + r : nullptr, m[e]);
+      }
     }
     __syncthreads();
     for (int t = w; t < NT * NT; t += NW) {
       const int rt = t / NT, ct = t % NT;
-      const f32x4 m = mm_tile<float, C>(zero4(), &sm.Tt[rt * 16][0], S::LDCF, &sm.r.m.M1t[ct * 16][0], S::LDCF);
+      f32x4 mb[1][1];
+      zero_blk(mb);
+      mm_blk<E, C, 1, 1, LO, LO>(mb, &sm.TtH[rt * 16][0], LO ? TtL + rt * 16 * S::LDCE : nullptr, S::LDCE,
+                                 &sm.r.m.M1h[ct * 16][0], LO ? &sm.r.m.M1l[ct * 16][0] : nullptr, S::LDCE);
+      const f32x4 m = mb[0][0];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = rt * 16 + acc_row(e), s = ct * 16 + acc_col();
@@ -632,7 +650,7 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
     }
     __syncthreads();
     pP.store(&sm.Tm[0][0], S::LDCF);  // T is no longer needed
-    pdP.store(&sm.Tt[0][0], S::LDCF);
+    pdP.store(&sm.dPm[0][0], S::LDCF);  // T^T is no longer needed
     __syncthreads();
     // C x C pass: A~, dS, and the dgamma / dbeta terms of A and P
     for (int t = w; t < NT * NT; t += NW) {
@@ -646,7 +664,7 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
         const float dA = sm.av.Am[r][s];
         const float At = dA * sm.beta[r] * dd;
         const float AdA = At * skk;
-        const float dP = sm.Tt[r][s];
+        const float dP = sm.dPm[r][s];
         const float PdP = dP * sm.Tm[r][s];
         rb[e] = dA * dd * skk;
         ra[e] = AdA;
