@@ -285,7 +285,7 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
         f32x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = a.scale * sm.gm[(r0 + i) * 16 + acc_row(e)] * acc[i][jj][e];
-        store_tile<float>(a.dQs + slot * C * D, D, (r0 + i) * 16, (c0 + jj) * 16, v, C);
+        store_acc(a.dQs + slot * C * D, ND, r0 + i, c0 + jj, v);
       }
   });
   constexpr int NBT = (NT / RT) * (NT / CC);
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
         f32x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = sm.em[(r0 + i) * 16 + acc_row(e)] * acc[i][jj][e];
-        store_tile<float>(a.dKh + slot * C * D, D, (r0 + i) * 16, (c0 + jj) * 16, v, C);
+        store_acc(a.dKh + slot * C * D, ND, r0 + i, c0 + jj, v);
       }
   });
   for_blocks<NT, NT, RT, CC, NW>([&](int r0, int c0) {
@@ -614,7 +614,7 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();
-    // M1 = dT T^T (fp32 MFMA), stored transposed; dA = strict_lower(-T^T M1)
+    // M1 = dT T^T (fp32 MFMA), stored transposed and split; dA = strict_lower(-T^T M1)
     TileRegs<float, C, C, NTH> pP, pdP;  // in flight during dA
     {
       TileRegs<float, C, C, NTH> rT;
@@ -717,13 +717,10 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
 #pragma unroll
       for (int ri = 0; ri < RT; ++ri)
 #pragma unroll
-        for (int cj = 0; cj < CT; ++cj)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = (rt0 + ri) * 16 + acc_row(e), c = (ct0 + cj) * 16 + acc_col();
-            qs[ri][cj][e] = dQsg[r * D + c];
-            kh[ri][cj][e] = dKhg[r * D + c];
-          }
+        for (int cj = 0; cj < CT; ++cj) {
+          qs[ri][cj] = load_acc(dQsg, ND, rt0 + ri, ct0 + cj);
+          kh[ri][cj] = load_acc(dKhg, ND, rt0 + ri, ct0 + cj);
+        }
     }
     if (act) {
 #pragma unroll

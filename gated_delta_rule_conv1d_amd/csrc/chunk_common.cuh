@@ -87,6 +87,18 @@ __device__ __forceinline__ void split_store(E* hi, E* lo, float x) {
   if constexpr (Split<E>::on) *lo = from_f<E>(x - to_f<E>(h));
 }
 
+// Accumulator-tile layout, for fp32 tensors that one kernel writes and another
+// reads back as the same 16x16 MFMA accumulator tiles: tile (rt, ct) of a grid
+// with TPR tiles per row sits at ((rt * TPR + ct) * 64 + lane) * 4, so a lane
+// moves its four values in one 16-byte access and a wave moves 1 KiB
+// contiguous.
+__device__ __forceinline__ void store_acc(float* base, int tpr, int rt, int ct, f32x4 v) {
+  *reinterpret_cast<f32x4*>(base + ((int64_t)(rt * tpr + ct) * kWave + lane_id()) * 4) = v;
+}
+__device__ __forceinline__ f32x4 load_acc(const float* base, int tpr, int rt, int ct) {
+  return *reinterpret_cast<const f32x4*>(base + ((int64_t)(rt * tpr + ct) * kWave + lane_id()) * 4);
+}
+
 // Element load/store of one accumulator tile straight to/from global memory.
 template <typename E>
 __device__ __forceinline__ void store_tile(E* base, int64_t ld, int r0, int c0, f32x4 v, int rows_valid) {
