@@ -303,6 +303,13 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
   }
   __syncthreads();  // dO and V are no longer read
 
+  // dHn is read now, in flight during (b); <Hc, dHn> is then formed from the
+  // staged parts of Hc (hi + lo, exact in fp32 mode) before they are
+  // overwritten, so Hc is read from HBM once
+  using DRegs = TileRegs<float, D, D, NTH>;
+  DRegs rD;
+  rD.load(dHn, D, D);
+
   // (b) dWk = -dW Hc^T: hi -> Os, lo -> Vs; transposed fp32 copy to workspace
   for_blocks<NT, ND, RT, CD, NW>([&](int r0, int c0) {
     f32x4 acc[RT][CD];
@@ -323,6 +330,24 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
         store_tile_t(a.dWkt + slot * D * C, C, (r0 + i) * 16, (c0 + jj) * 16, v);
       }
   });
+  {
+    float hs = 0.f;
+#pragma unroll
+    for (int i = 0; i < DRegs::N; ++i) {
+      const int e = tid + i * NTH;
+      if (e < DRegs::TOTAL) {
+        const int row = e / DRegs::PER_ROW, c = (e % DRegs::PER_ROW) * DRegs::V;
+        const float* x = reinterpret_cast<const float*>(&rD.r[i]);
+#pragma unroll
+        for (int u = 0; u < DRegs::V; ++u) {
+          float hc = to_f<E>(sm.Hh[row][c + u]);
+          if constexpr (LO) hc += to_f<E>(sm.Hl[row][c + u]);
+          hs += x[u] * hc;
+        }
+      }
+    }
+    sm.red[tid] = hs;
+  }
   __syncthreads();  // Hc is no longer read
   {
     TileRegs<E, C, D, NTH> rK;
@@ -355,23 +380,11 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
   }
   __syncthreads();  // dWk and K are no longer read
 
-  {  // stage dHn (and <Hc, dHn>), W, dO again
-    TileRegs<float, D, D, NTH> rD, rH;
+  {  // stage dHn, W, dO again
     TileRegs<float, C, D, NTH> rW;
     TileRegs<E, C, D, NTH> rO;
-    rD.load(dHn, D, D);
-    rH.load(Hc, D, D);
     rW.load(a.W + slot * C * D, D, C);
     rO.load(dog, ldo, len);
-    float hs = 0.f;
-#pragma unroll
-    for (int i = 0; i < TileRegs<float, D, D, NTH>::N; ++i) {
-      const float* x = reinterpret_cast<const float*>(&rD.r[i]);
-      const float* y = reinterpret_cast<const float*>(&rH.r[i]);
-      if (threadIdx.x + i * NTH < TileRegs<float, D, D, NTH>::TOTAL)
-        hs += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
-    }
-    sm.red[tid] = hs;
     rD.template store_split<E>(&sm.Hh[0][0], Hlo, S::LDQ);
     rW.template store_split<E>(&sm.Xh[0][0], Xlo, S::LDQ);
     rO.store(&sm.Os[0][0], S::LDQ);
