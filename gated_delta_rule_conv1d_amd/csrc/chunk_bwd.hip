@@ -528,11 +528,10 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
     const int h = j * a.G + gi;
     const int64_t slot = (int64_t)ci * a.Hv + h;
     const E* vg = (const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)h * D;
-    TileRegs<E, C, D, NTH> pV;  // v rows, T and T^T (from the preparation pass)
-    TileRegs<float, C, C, NTH> pTm, pTt;
+    TileRegs<E, C, D, NTH> pV;  // v rows and T (from the preparation pass)
+    TileRegs<float, C, C, NTH> pTm;
     pV.load(vg, a.sv, len);
     pTm.load(a.Tw + slot * C * C, C, C);
-    pTt.load(a.Ttw + slot * C * C, C, C);
     for (int e = tid; e < C; e += NTH) {
       const float gm = a.gam[slot * C + e];
       sm.gam[e] = gm;
@@ -546,7 +545,7 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
     // here, not per tile
     E* const TtL = LO ? &sm.TtL[0][0] : nullptr;
     E* const XL = LO ? &sm.r.x.l[0][0] : nullptr;
-    pTt.template store_split<E>(&sm.TtH[0][0], TtL, S::LDCE);
+    pTm.template store_t<E>(&sm.TtH[0][0], S::LDCE, TtL, S::LDCE);  // T^T, transposed here
     // dXu = T^T dW -> dv and <dXu, v>
     {
       TileRegs<float, D, C, NTH> rX;
@@ -831,7 +830,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsPlan {
   size_t table, seq0, Wk, U, P, Kt, Ktl, gam, end_fwd;
-  size_t Ptr, Tw, Ttw, Krh, Krl, Wth, Wtl, Qth, Qtl, Hc, W, dHn, dW, dWt, dT, dWkt, dQs, dKh, dP, hdot, end_bwd;
+  size_t Ptr, Tw, Krh, Krl, Wth, Wtl, Qth, Qtl, Hc, W, dHn, dW, dWt, dT, dWkt, dQs, dKh, dP, hdot, end_bwd;
 };
 
 static WsPlan plan(const gdn_shape* s) {
@@ -850,7 +849,6 @@ static WsPlan plan(const gdn_shape* s) {
   p.end_fwd = o;
   p.Ptr = o; o = align256(o + M * Hv * C * C * 4);
   p.Tw = o; o = align256(o + M * Hv * C * C * 4);
-  p.Ttw = o; o = align256(o + M * Hv * C * C * 4);
   p.Krh = o; o = align256(o + M * Hv * C * D * es);
   p.Krl = o; o = align256(o + M * Hv * C * D * es);
   p.Wth = o; o = align256(o + M * Hv * D * C * es);
@@ -888,7 +886,6 @@ static void fill_ws(ChunkArgs& a, const gdn_shape* s, void* ws) {
   a.gam = (float*)(b + p.gam);
   a.Ptr = (float*)(b + p.Ptr);
   a.Tw = (float*)(b + p.Tw);
-  a.Ttw = (float*)(b + p.Ttw);
   a.Krh = b + p.Krh;
   a.Krl = b + p.Krl;
   a.Wth = b + p.Wth;

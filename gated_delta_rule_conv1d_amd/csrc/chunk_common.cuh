@@ -50,7 +50,6 @@ struct ChunkArgs {
   // backward only: operands of the reverse state pass, transposed once per chunk
   float* Ptr;                 // [slot][C][C]  P^T
   float* Tw;                  // [slot][C][C]  T = (I + A)^-1 (for the WY gradients)
-  float* Ttw;                 // [slot][C][C]  T^T
   void* Krh;                  // [slot][C][D]  rows e_s k_s (hi)
   void* Krl;                  //               (lo)
   void* Wth;                  // [slot][D][C]  Wk^T (hi)

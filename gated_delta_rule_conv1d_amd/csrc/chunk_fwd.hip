@@ -146,11 +146,10 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
     }
     __syncthreads();
     unit_lower_inverse<C, S::LDCF, NTH>(sm.Am, sm.Tm, sm.Tt, sm.Xs);  // starts and ends with a barrier
-    if constexpr (LO_OUT) {  // T and T^T for the WY gradients
+    if constexpr (LO_OUT) {  // T for the WY gradients
       for (int e = tid; e < C * (C / 4); e += NTH) {
         const int r = e / (C / 4), c = (e % (C / 4)) * 4;
         *reinterpret_cast<float4*>(a.Tw + slot * C * C + r * C + c) = *reinterpret_cast<const float4*>(&sm.Tm[r][c]);
-        *reinterpret_cast<float4*>(a.Ttw + slot * C * C + r * C + c) = *reinterpret_cast<const float4*>(&sm.Tt[r][c]);
       }
     }
 
