@@ -273,19 +273,21 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
   __syncthreads();
 
   // (a) dQs = scale Gam dO Hc^T (to workspace); dT1 = dW V^T kept for (c)
-  for_blocks<NT, ND, RT, CD, NW>([&](int r0, int c0) {
-    f32x4 acc[RT][CD];
+  // dQs^T tiles [D][C] (the layout the WY-gradient kernel accumulates in)
+  for_blocks<ND, NT, CD, RT, NW>([&](int d0, int r0) {
+    f32x4 acc[CD][RT];
     zero_blk(acc);
-    mm_blk<E, D, RT, CD, false, LO>(acc, &sm.Os[r0 * 16][0], nullptr, S::LDQ, &sm.Hh[c0 * 16][0],
-                                    LO ? &sm.Hl[c0 * 16][0] : nullptr, S::LDQ);
+    mm_blk<E, D, CD, RT, LO, false>(acc, &sm.Hh[d0 * 16][0], LO ? &sm.Hl[d0 * 16][0] : nullptr, S::LDQ,
+                                    &sm.Os[r0 * 16][0], nullptr, S::LDQ);
 #pragma unroll
-    for (int i = 0; i < RT; ++i)
+    for (int i = 0; i < CD; ++i)
 #pragma unroll
-      for (int jj = 0; jj < CD; ++jj) {
+      for (int jj = 0; jj < RT; ++jj) {
+        const float sc = a.scale * sm.gm[(r0 + jj) * 16 + acc_col()];
         f32x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = a.scale * sm.gm[(r0 + i) * 16 + acc_row(e)] * acc[i][jj][e];
-        store_acc(a.dQs + slot * C * D, ND, r0 + i, c0 + jj, v);
+        for (int e = 0; e < 4; ++e) v[e] = sc * acc[i][jj][e];
+        store_acc(a.dQs + slot * C * D, NT, d0 + i, r0 + jj, v);
       }
   });
   constexpr int NBT = (NT / RT) * (NT / CC);
@@ -395,20 +397,21 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
     for (int i = 0; i < NTH; ++i) s += sm.red[i];
     a.hdot[slot] = s;
   }
-  // (d) dKh = e W dHn^T;  dP = scale dO W^T
-  for_blocks<NT, ND, RT, CD, NW>([&](int r0, int c0) {
-    f32x4 acc[RT][CD];
+  // (d) dKh = e W dHn^T (as dKh^T tiles [D][C]);  dP = scale dO W^T
+  for_blocks<ND, NT, CD, RT, NW>([&](int d0, int r0) {
+    f32x4 acc[CD][RT];
     zero_blk(acc);
-    mm_blk<E, D, RT, CD, LO, LO>(acc, &sm.Xh[r0 * 16][0], LO ? &sm.Xl[r0 * 16][0] : nullptr, S::LDQ,
-                                 &sm.Hh[c0 * 16][0], LO ? &sm.Hl[c0 * 16][0] : nullptr, S::LDQ);
+    mm_blk<E, D, CD, RT, LO, LO>(acc, &sm.Hh[d0 * 16][0], LO ? &sm.Hl[d0 * 16][0] : nullptr, S::LDQ,
+                                 &sm.Xh[r0 * 16][0], LO ? &sm.Xl[r0 * 16][0] : nullptr, S::LDQ);
 #pragma unroll
-    for (int i = 0; i < RT; ++i)
+    for (int i = 0; i < CD; ++i)
 #pragma unroll
-      for (int jj = 0; jj < CD; ++jj) {
+      for (int jj = 0; jj < RT; ++jj) {
+        const float sc = sm.em[(r0 + jj) * 16 + acc_col()];
         f32x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = sm.em[(r0 + i) * 16 + acc_row(e)] * acc[i][jj][e];
-        store_acc(a.dKh + slot * C * D, ND, r0 + i, c0 + jj, v);
+        for (int e = 0; e < 4; ++e) v[e] = sc * acc[i][jj][e];
+        store_acc(a.dKh + slot * C * D, NT, d0 + i, r0 + jj, v);
       }
   });
   for_blocks<NT, NT, RT, CC, NW>([&](int r0, int c0) {
@@ -437,6 +440,17 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
 // Every operand is staged in LDS first (fp32 ones split on the fly into bf16
 // hi + lo MFMA parts); K K^T is formed once per k-head.
 // ---------------------------------------------------------------------------
+// Workgroup size of the WY-gradient kernel: 8 waves where the tiles give each
+// wave an r-tile and a d-strip of its own.
+template <int D, int C>
+constexpr int gb_threads() { return (D >= 64 && C >= 64) ? 2 * kChunkThreads : kChunkThreads; }
+// Row partial sums over d: one slot per (wave along d, lane group of 16).
+template <int D, int C>
+constexpr int gb_slots() {
+  constexpr int NWD = gb_threads<D, C>() / kWave / (C / 16), ND = D / 16;
+  return (ND >= NWD ? NWD : ND) * 4;
+}
+
 template <typename E, int D, int C>
 struct GradBSmem {
   static constexpr int LD2C = 2 * C + Pad<E>::E16;
@@ -473,7 +487,8 @@ struct GradBSmem {
   } r;
   float gam[C], beta[C], Gm[C], em[C];
   float hdot;            // <H_c, dH_n> of the current v-head
-  float pCD[4][ND][C];   // row partials of C x D tiles: dXu.v, dXw.k, dQs.q, dKh.k
+  static constexpr int NPD = gb_slots<D, C>();
+  float pCD[4][NPD][C];  // row partials over d: dXu.v, dXw.k, dQs.q, dKh.k
   float pCC[5][NT][C];   // dA D Skk rows, dA*A rows, dA*A cols, dP*P rows, dP*P cols
 };
 
@@ -486,17 +501,25 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
   __shared__ S sm;
   constexpr int NT = S::NT, ND = S::ND;
   constexpr int NW = NTH / kWave;
-  // [C][D] output tiles per wave: a block of RT row tiles x CT adjacent column
-  // tiles (waves past the row tiles idle)
-  constexpr int NWC = ND >= NW ? NW : ND, NWR = NW / NWC;
-  constexpr int RT = NT >= NWR ? NT / NWR : 1, CT = ND / NWC;
+  static_assert(NTH == gb_threads<D, C>(), "launch size");
+  // The [C][D] results (dv, dq, dk and the row sums over d) are formed as
+  // transposed [D][C] accumulator tiles, so a lane holds 4 consecutive d of
+  // one chunk row r.  Each wave owns one r-tile and DT adjacent d-tiles: row
+  // sums over d stay in-lane, one partial per (wave along d, lane group);
+  // waves past the d-tiles idle.
+  static_assert(NT <= NW, "one r-tile per wave");
+  constexpr int NWR = NT, NWD = NW / NWR;         // waves along r / along d
+  constexpr int DT = ND >= NWD ? ND / NWD : 1;   // d-tiles per wave
   const int ci = blockIdx.x, j = blockIdx.y;
   const int4 ent = chunk_entry(a.table, ci);
   if (ent.x < 0) return;
   const int tok0 = ent.y, len = ent.z;
   const int w = wave_id(), lane = lane_id(), tid = threadIdx.x;
-  const bool act = (w / NWC) * RT < NT;
-  const int rt0 = (w / NWC) * RT, ct0 = (w % NWC) * CT;
+  const int rt = w % NWR, dt0 = (w / NWR) * DT;
+  const bool act = dt0 < ND;
+  const int pslot = (w / NWR) * 4 + (lane >> 4);  // this lane's row partial slot
+  const int rrow = rt * 16 + (lane & 15);         // chunk row of this lane's accumulator column
+  const int dl = 4 * (lane >> 4);                 // first of its 4 rows within a d-tile
   const E* qg = (const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D;
   const E* kg = (const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D;
 
@@ -520,7 +543,7 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
     for (int e = 0; e < 4; ++e) sm.Skk[rt * 16 + acc_row(e)][ct * 16 + acc_col()] = skk[e];
   }
 
-  f32x4 dQ[RT][CT], dK[RT][CT];
+  f32x4 dQ[DT][1], dK[DT][1];
   zero_blk(dQ);
   zero_blk(dK);
 
@@ -554,43 +577,33 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
       rX.template store_split<E>(&sm.r.x.h[0][0], XL, S::LDCE);
     }
     __syncthreads();
-    // tile (rt, ct) of T^T X (X = dW^T or dWk^T staged in r.x)
-    auto txt = [&](int rt, int ct) {
+    // tile (dt, rt) of (T^T X)^T = X^T T (X = dW^T or dWk^T staged in r.x)
+    auto txt = [&](int dt) {
       f32x4 acc[1][1];
       zero_blk(acc);
-      mm_blk<E, C, 1, 1, LO, LO>(acc, &sm.TtH[rt * 16][0], LO ? TtL + rt * 16 * S::LDCE : nullptr, S::LDCE,
-                                 &sm.r.x.h[ct * 16][0], LO ? XL + ct * 16 * S::LDCE : nullptr, S::LDCE);
+      mm_blk<E, C, 1, 1, LO, LO>(acc, &sm.r.x.h[dt * 16][0], LO ? XL + dt * 16 * S::LDCE : nullptr, S::LDCE,
+                                 &sm.TtH[rt * 16][0], LO ? TtL + rt * 16 * S::LDCE : nullptr, S::LDCE);
       return acc[0][0];
     };
     E* dvg = (E*)a.dv + (int64_t)tok0 * a.sv + (int64_t)h * D;
-    // row partials are summed in-lane over a wave's CT column tiles, then
-    // across the 16 lanes; the first column slot gets the total, the rest 0
-    float pu[4];
+    if (act) {
+      const float br = sm.beta[rrow];
+      float pu = 0.f;
 #pragma unroll
-    for (int i = 0; i < RT * CT; ++i) {
-      if (act) {
-        const int rt = rt0 + i / CT, ct = ct0 + i % CT;
-        const f32x4 xu = txt(rt, ct);
+      for (int i = 0; i < DT; ++i) {
+        const int d = (dt0 + i) * 16 + dl;
+        const f32x4 xu = txt(dt0 + i);
+        float vv[4];
+        ld4<E>(&sm.av.Vs[rrow][d], vv);
         f32x4 dvv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = rt * 16 + acc_row(e), c = ct * 16 + acc_col();
-          dvv[e] = sm.beta[r] * xu[e];
-          const float t = xu[e] * to_f<E>(sm.av.Vs[r][c]);
-          pu[e] = i % CT == 0 ? t : pu[e] + t;
+          dvv[e] = br * xu[e];
+          pu += xu[e] * vv[e];
         }
-        store_tile<E>(dvg, a.sv, rt * 16, ct * 16, dvv, len);
-        if (i % CT == CT - 1) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) pu[e] = group_sum<16>(pu[e]);
-          if ((lane & 15) == 0) {
-#pragma unroll
-            for (int cj = 0; cj < CT; ++cj)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) sm.pCD[0][ct0 + cj][rt * 16 + acc_row(e)] = cj == 0 ? pu[e] : 0.f;
-          }
-        }
+        if (rrow < len) st4<E>(dvg + (int64_t)rrow * a.sv + d, dvv);
       }
+      sm.pCD[0][pslot][rrow] = pu;
     }
     __syncthreads();
     // dXw = T^T dWk -> dK and <dXw, k>
@@ -600,30 +613,20 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
       rX.template store_split<E>(&sm.r.x.h[0][0], XL, S::LDCE);
     }
     __syncthreads();
-    float pw[4];
+    if (act) {
+      const float bg = sm.beta[rrow] * sm.Gm[rrow];
+      float pw = 0.f;
 #pragma unroll
-    for (int i = 0; i < RT * CT; ++i) {
-      if (act) {
-        const int rt = rt0 + i / CT, ct = ct0 + i % CT;
-        const f32x4 xw = txt(rt, ct);
+      for (int i = 0; i < DT; ++i) {
+        const int d = (dt0 + i) * 16 + dl;
+        const f32x4 xw = txt(dt0 + i);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = rt * 16 + acc_row(e), c = ct * 16 + acc_col();
-          const float t = xw[e] * to_f<E>(sm.QKt[c][C + r]);
-          pw[e] = i % CT == 0 ? t : pw[e] + t;
-          dK[i / CT][i % CT][e] += sm.beta[r] * sm.Gm[r] * xw[e];
-        }
-        if (i % CT == CT - 1) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) pw[e] = group_sum<16>(pw[e]);
-          if ((lane & 15) == 0) {
-#pragma unroll
-            for (int cj = 0; cj < CT; ++cj)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) sm.pCD[1][ct0 + cj][rt * 16 + acc_row(e)] = cj == 0 ? pw[e] : 0.f;
-          }
+          pw += xw[e] * to_f<E>(sm.QKt[d + e][C + rrow]);
+          dK[i][0][e] += bg * xw[e];
         }
       }
+      sm.pCD[1][pslot][rrow] = pw;
     }
     __syncthreads();
     // M1 = dT T^T (fp32 MFMA), stored transposed and split; dA = strict_lower(-T^T M1)
@@ -720,59 +723,30 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
                      sm.r.s.At[sr][r] + sm.r.s.At[r][sr]);
     }
     __syncthreads();
-    // dQ += dQs + dS K;   dK += dKh + [dS^T | A~ + A~^T] [Q ; K]
-    // dQs and dKh of this wave's tiles
-    f32x4 qs[RT][CT], kh[RT][CT];
+    // dQ += dQs + dS K;   dK += dKh + [dS^T | A~ + A~^T] [Q ; K]   (transposed)
     if (act) {
       const float* dQsg = a.dQs + slot * C * D;
       const float* dKhg = a.dKh + slot * C * D;
+      float pq = 0.f, pk = 0.f;
 #pragma unroll
-      for (int ri = 0; ri < RT; ++ri)
-#pragma unroll
-        for (int cj = 0; cj < CT; ++cj) {
-          qs[ri][cj] = load_acc(dQsg, ND, rt0 + ri, ct0 + cj);
-          kh[ri][cj] = load_acc(dKhg, ND, rt0 + ri, ct0 + cj);
-        }
-    }
-    if (act) {
-#pragma unroll
-      for (int ri = 0; ri < RT; ++ri) {
-        const int rt = rt0 + ri;
-        float pq[4] = {0.f, 0.f, 0.f, 0.f}, pk[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int cj = 0; cj < CT; ++cj)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = rt * 16 + acc_row(e), c = (ct0 + cj) * 16 + acc_col();
-            const float qsv = qs[ri][cj][e];
-            const float khv = kh[ri][cj][e];
-            dQ[ri][cj][e] += qsv;
-            dK[ri][cj][e] += khv;
-            pq[e] += qsv * to_f<E>(sm.QKt[c][r]);
-            pk[e] += khv * to_f<E>(sm.QKt[c][C + r]);
-          }
-        // the wave's CT column tiles are summed in-lane; its first slot gets
-        // the total, the others zero
+      for (int i = 0; i < DT; ++i) {
+        const int d = (dt0 + i) * 16 + dl;
+        const f32x4 qs = load_acc(dQsg, NT, dt0 + i, rt);
+        const f32x4 kh = load_acc(dKhg, NT, dt0 + i, rt);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pq[e] = group_sum<16>(pq[e]);
-          pk[e] = group_sum<16>(pk[e]);
-        }
-        if ((lane & 15) == 0) {
-#pragma unroll
-          for (int cj = 0; cj < CT; ++cj)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              sm.pCD[2][ct0 + cj][rt * 16 + acc_row(e)] = cj == 0 ? pq[e] : 0.f;
-              sm.pCD[3][ct0 + cj][rt * 16 + acc_row(e)] = cj == 0 ? pk[e] : 0.f;
-            }
+          dQ[i][0][e] += qs[e];
+          dK[i][0][e] += kh[e];
+          pq += qs[e] * to_f<E>(sm.QKt[d + e][rrow]);
+          pk += kh[e] * to_f<E>(sm.QKt[d + e][C + rrow]);
         }
       }
-      const int r0 = rt0 * 16, c0 = ct0 * 16;
-      mm_blk<E, C, RT, CT, LO, false>(dQ, &sm.r.s.dSh[r0][0], LO ? &sm.r.s.dSl[0][0] + r0 * S::LDCE : nullptr,
-                                      S::LDCE, &sm.QKt[c0][C], nullptr, S::LD2C);
-      mm_blk<E, 2 * C, RT, CT, LO, false>(dK, &sm.TS.h[r0][0], LO ? &sm.TS.l[0][0] + r0 * S::LD2C : nullptr,
-                                          S::LD2C, &sm.QKt[c0][0], nullptr, S::LD2C);
+      sm.pCD[2][pslot][rrow] = pq;
+      sm.pCD[3][pslot][rrow] = pk;
+      mm_blk<E, C, DT, 1, false, LO>(dQ, &sm.QKt[dt0 * 16][C], nullptr, S::LD2C, &sm.r.s.dSh[rt * 16][0],
+                                     LO ? &sm.r.s.dSl[0][0] + rt * 16 * S::LDCE : nullptr, S::LDCE);
+      mm_blk<E, 2 * C, DT, 1, false, LO>(dK, &sm.QKt[dt0 * 16][0], nullptr, S::LD2C, &sm.TS.h[rt * 16][0],
+                                         LO ? &sm.TS.l[0][0] + rt * 16 * S::LD2C : nullptr, S::LD2C);
     }
     __syncthreads();
     // per-row totals, then dg = reverse cumulative sum within the chunk
@@ -781,7 +755,7 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
       float dbeta = 0.f, dgam = 0.f, tk = 0.f;
       if (r < C) {
         float su = 0.f, sw = 0.f, sq = 0.f;
-        for (int c = 0; c < ND; ++c) {
+        for (int c = 0; c < S::NPD; ++c) {
           su += sm.pCD[0][c][r];
           sw += sm.pCD[1][c][r];
           sq += sm.pCD[2][c][r];
@@ -812,14 +786,13 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
   }
   E* dqg = (E*)a.dq + (int64_t)tok0 * a.sqk + (int64_t)j * D;
   E* dkg = (E*)a.dk + (int64_t)tok0 * a.sqk + (int64_t)j * D;
-  if (act) {
+  if (act && rrow < len) {
 #pragma unroll
-    for (int ri = 0; ri < RT; ++ri)
-#pragma unroll
-      for (int cj = 0; cj < CT; ++cj) {
-        store_tile<E>(dqg, a.sqk, (rt0 + ri) * 16, (ct0 + cj) * 16, dQ[ri][cj], len);
-        store_tile<E>(dkg, a.sqk, (rt0 + ri) * 16, (ct0 + cj) * 16, dK[ri][cj], len);
-      }
+    for (int i = 0; i < DT; ++i) {
+      const int d = (dt0 + i) * 16 + dl;
+      st4<E>(dqg + (int64_t)rrow * a.sqk + d, dQ[i][0]);
+      st4<E>(dkg + (int64_t)rrow * a.sqk + d, dK[i][0]);
+    }
   }
 }
 
@@ -929,7 +902,7 @@ static void launch_chunk_bwd_core(const ChunkArgs& a, hipStream_t st, bool recom
   }
   GDN_PROF("chunk_grad_b", st);
   // 8 waves where the [C][D] tiles give each one a column strip of its own
-  constexpr int GB_THREADS = (D >= 64 && C >= 64) ? 2 * kChunkThreads : kChunkThreads;
+  constexpr int GB_THREADS = gb_threads<D, C>();
   grad_b_kernel<E, D, C, GB_THREADS><<<dim3(a.max_chunks, a.Hk), GB_THREADS, 0, st>>>(a);
 }
 

@@ -86,6 +86,32 @@ __device__ __forceinline__ void split_store(E* hi, E* lo, float x) {
   if constexpr (Split<E>::on) *lo = from_f<E>(x - to_f<E>(h));
 }
 
+// 4 consecutive elements: load as floats / store from floats.
+template <typename E>
+__device__ __forceinline__ void ld4(const E* p, float* o) {
+  if constexpr (sizeof(E) == 2) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    const E* e = reinterpret_cast<const E*>(&u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = to_f<E>(e[i]);
+  } else {
+    const float4 u = *reinterpret_cast<const float4*>(p);
+    o[0] = u.x; o[1] = u.y; o[2] = u.z; o[3] = u.w;
+  }
+}
+template <typename E>
+__device__ __forceinline__ void st4(E* p, f32x4 v) {
+  if constexpr (sizeof(E) == 2) {
+    uint2 u;
+    E* e = reinterpret_cast<E*>(&u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e[i] = from_f<E>(v[i]);
+    *reinterpret_cast<uint2*>(p) = u;
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
 // Accumulator-tile layout, for fp32 tensors that one kernel writes and another
 // reads back as the same 16x16 MFMA accumulator tiles: tile (rt, ct) of a grid
 // with TPR tiles per row sits at ((rt * TPR + ct) * 64 + lane) * 4, so a lane
