@@ -48,67 +48,69 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(const E* __restrict__ x, 
   const bool is_qk = ch < n_qk;
 
   float wr[V][W];
-  float hist[W - 1][V];
 #pragma unroll
   for (int c = 0; c < V; ++c)
 #pragma unroll
     for (int i = 0; i < W; ++i) wr[c][i] = active ? to_f<E>(w[(size_t)(ch + c) * W + i]) : 0.f;
 
+  // ring[k] holds x of the token t with (t - t0) % W == k; the token loop is
+  // unrolled by W so every slot index is a constant (no register shifting)
+  float ring[W][V];
   int n = find_seq(cu, N, t0);
   int seq_start = cu[n], seq_end = cu[n + 1];
 #pragma unroll
+  for (int c = 0; c < V; ++c) ring[0][c] = 0.f;
+#pragma unroll
   for (int i = 0; i < W - 1; ++i) {
     const int s = t0 - (W - 1) + i;
-    if (active && s >= seq_start) Vec<E>::load(x + (size_t)s * Cch + ch, hist[i]);
+    if (active && s >= seq_start) Vec<E>::load(x + (size_t)s * Cch + ch, ring[i + 1]);
     else
 #pragma unroll
-      for (int c = 0; c < V; ++c) hist[i][c] = 0.f;
+      for (int c = 0; c < V; ++c) ring[i + 1][c] = 0.f;
   }
 
   // the next token's x is loaded one iteration ahead
   uint4 nx = make_uint4(0, 0, 0, 0);
   if (active) nx = *reinterpret_cast<const uint4*>(x + (size_t)t0 * Cch + ch);
-  for (int t = t0; t < t1; ++t) {
-    const uint4 rx = nx;
-    if (active && t + 1 < t1) nx = *reinterpret_cast<const uint4*>(x + (size_t)(t + 1) * Cch + ch);
-    if (t >= seq_end) {  // entering a new sequence (skip empty ones)
-      while (cu[n + 1] <= t) ++n;
-      seq_start = cu[n];
-      seq_end = cu[n + 1];
+  for (int tb = t0; tb < t1; tb += W) {
 #pragma unroll
-      for (int i = 0; i < W - 1; ++i)
+    for (int p = 0; p < W; ++p) {
+      const int t = tb + p;
+      if (t >= t1) break;
+      const uint4 rx = nx;
+      if (active && t + 1 < t1) nx = *reinterpret_cast<const uint4*>(x + (size_t)(t + 1) * Cch + ch);
+      if (t >= seq_end) {  // entering a new sequence (skip empty ones)
+        while (cu[n + 1] <= t) ++n;
+        seq_start = cu[n];
+        seq_end = cu[n + 1];
 #pragma unroll
-        for (int c = 0; c < V; ++c) hist[i][c] = 0.f;
+        for (int i = 0; i < W; ++i)
+#pragma unroll
+          for (int c = 0; c < V; ++c) ring[i][c] = 0.f;
+      }
+      {
+        const E* ex = reinterpret_cast<const E*>(&rx);
+#pragma unroll
+        for (int c = 0; c < V; ++c) ring[p][c] = to_f<E>(ex[c]);
+      }
+      float a[V];
+      float ss = 0.f;
+#pragma unroll
+      for (int c = 0; c < V; ++c) {
+        float acc = wr[c][W - 1] * ring[p][c];
+#pragma unroll
+        for (int i = 0; i < W - 1; ++i) acc += wr[c][i] * ring[(p + 1 + i) % W][c];  // token t - (W-1) + i
+        a[c] = acc * sigmoidf_(acc);
+        ss += a[c] * a[c];
+      }
+      ss = group_sum<LPH>(ss);
+      if (is_qk) {
+        const float inv = rsqrtf(ss + eps);
+#pragma unroll
+        for (int c = 0; c < V; ++c) a[c] *= inv;
+      }
+      if (active) Vec<E>::store(y + (size_t)t * Cch + ch, a);
     }
-    float cur[V];
-    {
-      const E* ex = reinterpret_cast<const E*>(&rx);
-#pragma unroll
-      for (int c = 0; c < V; ++c) cur[c] = to_f<E>(ex[c]);
-    }
-    float a[V];
-    float ss = 0.f;
-#pragma unroll
-    for (int c = 0; c < V; ++c) {
-      float acc = wr[c][W - 1] * cur[c];
-#pragma unroll
-      for (int i = 0; i < W - 1; ++i) acc += wr[c][i] * hist[i][c];
-      a[c] = acc * sigmoidf_(acc);
-      ss += a[c] * a[c];
-    }
-    ss = group_sum<LPH>(ss);
-    if (is_qk) {
-      const float inv = rsqrtf(ss + eps);
-#pragma unroll
-      for (int c = 0; c < V; ++c) a[c] *= inv;
-    }
-    if (active) Vec<E>::store(y + (size_t)t * Cch + ch, a);
-#pragma unroll
-    for (int i = 0; i < W - 2; ++i)
-#pragma unroll
-      for (int c = 0; c < V; ++c) hist[i][c] = hist[i + 1][c];
-#pragma unroll
-    for (int c = 0; c < V; ++c) hist[W - 2][c] = cur[c];
   }
 }
 
