@@ -88,6 +88,17 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
   const int tid = threadIdx.x, w = wave_id(), lane = lane_id();
   const E* qg = (const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D;
   const E* kg = (const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D;
+  // a v-head's v rows and gates are loaded one v-head ahead
+  TileRegs<E, C, D, NTH> pV;
+  float gv = 0.f, bv = 0.f;
+  auto load_head = [&](int hh) {
+    pV.load((const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)hh * D, a.sv, len);
+    if (w == 0 && lane < len) {
+      gv = a.g[(int64_t)(tok0 + lane) * a.Hv + hh];
+      bv = a.beta[(int64_t)(tok0 + lane) * a.Hv + hh];
+    }
+  };
+  load_head(j * a.G);
 
   rows2s<E, C, D, NTH>(&sm.Qs[0][0], S::LDQ, qg, a.sqk, len);
   rows2s<E, C, D, NTH>(&sm.Ks[0][0], S::LDQ, kg, a.sqk, len);
@@ -105,11 +116,6 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
     const int h = j * a.G + gi;
     const int64_t slot = (int64_t)ci * a.Hv + h;
     if (w == 0) {  // within-chunk cumulative gate
-      float gv = 0.f, bv = 0.f;
-      if (lane < len) {
-        gv = a.g[(int64_t)(tok0 + lane) * a.Hv + h];
-        bv = a.beta[(int64_t)(tok0 + lane) * a.Hv + h];
-      }
       float x = gv;
 #pragma unroll
       for (int off = 1; off < kWave; off <<= 1) {
@@ -122,8 +128,8 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
         a.gam[slot * C + lane] = x;
       }
     }
-    const E* vg = (const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)h * D;
-    rows2s_t<E, C, D, NTH>(&sm.Vt[0][0], S::LDCE, vg, a.sv, len, nullptr, 1.f);
+    pV.template store_t<E>(&sm.Vt[0][0], S::LDCE);  // V^T
+    if (gi + 1 < a.G) load_head(h + 1);
     __syncthreads();
 
     // P = lower_incl(D * Q K^T) (fp32 to workspace), A = strict_lower(beta_r D * K K^T)
