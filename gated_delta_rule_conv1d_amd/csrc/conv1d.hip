@@ -19,7 +19,9 @@
 
 namespace gdn {
 
-constexpr int kConvTB = 64;       // tokens per wave
+constexpr int kConvTB = 64;       // tokens per wave, forward
+constexpr int kConvTBB = 128;     // tokens per wave, backward (its W-1 look-ahead
+                                  // tokens and dw partials amortise over more)
 constexpr int kConvWaves = 4;     // waves (token blocks) per workgroup
 
 __device__ __forceinline__ int find_seq(const int32_t* cu, int N, int t) {
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(const E* __restrict__ dy,
   const int lane = lane_id();
   const int wv = wave_id();
   const int tb = blockIdx.x * kConvWaves + wv;
-  const int t0 = tb * kConvTB;
+  const int t0 = tb * kConvTBB;
   const int ch = (blockIdx.y * kWave + lane) * V;
   const bool active = ch < Cch;
   const bool is_qk = ch < n_qk;
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(const E* __restrict__ dy,
     for (int i = 0; i < W; ++i) dwacc[c][i] = 0.f;
 
   if (t0 < T) {
-    const int t1 = min(t0 + kConvTB, T);
+    const int t1 = min(t0 + kConvTBB, T);
     const int tend = min(t1 + W - 1, T);
     float wr[V][W];
 #pragma unroll
@@ -305,14 +307,14 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(const E* __restrict__ dy,
 // --------------------------------------------------------------------------
 // host side
 // --------------------------------------------------------------------------
-static int conv_grid_x(int T) {
-  const int ntb = (T + kConvTB - 1) / kConvTB;
+static int conv_grid_x(int T, int tb) {
+  const int ntb = (T + tb - 1) / tb;
   return (ntb + kConvWaves - 1) / kConvWaves;
 }
 
 size_t conv_bwd_ws_bytes(const gdn_shape* s, int width) {
   const int Cch = 2 * s->h_qk * s->d_k + s->h_v * s->d_v;
-  const int gx = conv_grid_x(s->total_tokens) > 0 ? conv_grid_x(s->total_tokens) : 1;
+  const int gx = conv_grid_x(s->total_tokens, kConvTBB) > 0 ? conv_grid_x(s->total_tokens, kConvTBB) : 1;
   return (size_t)gx * Cch * width * sizeof(float);
 }
 
@@ -321,7 +323,7 @@ static void launch_conv_fwd(const gdn_shape* s, const void* x, const void* w, co
                             void* y, hipStream_t st) {
   constexpr int V = Vec<E>::N;
   const int Cch = 2 * s->h_qk * s->d_k + s->h_v * s->d_v;
-  dim3 grid(conv_grid_x(s->total_tokens), (Cch + kWave * V - 1) / (kWave * V));
+  dim3 grid(conv_grid_x(s->total_tokens, kConvTB), (Cch + kWave * V - 1) / (kWave * V));
   GDN_PROF("conv_fwd", st);
   conv_fwd_kernel<E, D, W><<<grid, 256, 0, st>>>((const E*)x, (const E*)w, cu, s->n_seqs, s->total_tokens, Cch,
                                                  2 * s->h_qk * s->d_k, eps, (E*)y);
@@ -332,7 +334,7 @@ static void launch_conv_bwd(const gdn_shape* s, const void* dy, const void* x, c
                             float eps, void* dx, float* dw, void* ws, hipStream_t st) {
   constexpr int V = Vec<E>::N;
   const int Cch = 2 * s->h_qk * s->d_k + s->h_v * s->d_v;
-  dim3 grid(conv_grid_x(s->total_tokens), (Cch + kWave * V - 1) / (kWave * V));
+  dim3 grid(conv_grid_x(s->total_tokens, kConvTBB), (Cch + kWave * V - 1) / (kWave * V));
   float* part = (float*)ws;
   {
     GDN_PROF("conv_bwd", st);
