@@ -235,16 +235,24 @@ struct PrepSmem {
 };
 
 // (I + A)^-1 for strictly lower A [C][C] (fp32 in LDS) into Tm and Tt = Tm^T.
-template <int C, int LDCF, int NTH = kChunkThreads>
+// While wave 0 solves the diagonal blocks, the other waves run
+// other(first, count) (thread tid - 64 of NTH - 64); it must not touch Am, Tm,
+// Tt, Xs nor wait at a barrier.
+struct NoWork {
+  __device__ void operator()(int, int) const {}
+};
+template <int C, int LDCF, int NTH = kChunkThreads, typename F = NoWork>
 __device__ __forceinline__ void unit_lower_inverse(const float (*Am)[LDCF], float (*Tm)[LDCF], float (*Tt)[LDCF],
-                                                   float (*Xs)[16][20]) {
+                                                   float (*Xs)[16][20], F&& other = F{}) {
+  static_assert(C <= kWave && NTH > kWave, "diagonal solve in wave 0");
   const int tid = threadIdx.x, w = wave_id();
   for (int e = tid; e < C * C; e += NTH) {
     Tm[e / C][e % C] = 0.f;
     Tt[e / C][e % C] = 0.f;
   }
   __syncthreads();
-  if (tid < C) {  // diagonal 16x16 blocks, one column per lane
+  if (tid >= kWave) other(tid - kWave, NTH - kWave);
+  else if (tid < C) {  // diagonal 16x16 blocks, one column per lane
     const int o = (tid >> 4) * 16, c = tid & 15;
     float x[16];
 #pragma unroll

@@ -151,7 +151,71 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();
-    unit_lower_inverse<C, S::LDCF, NTH>(sm.Am, sm.Tm, sm.Tt, sm.Xs);  // starts and ends with a barrier
+    // Outputs that need only gamma, K and Q (K~^T hi / lo; for the backward
+    // also the K~ rows and (Gam q)^T): written by waves 1.. while wave 0 runs
+    // the diagonal solve of the inverse
+    auto gate_outputs = [&](int t0, int nt) {
+      // Kt_e[d][s] = e^{gamma_last - gamma_s} k_s[d]  (s < len), 0 past len
+      {
+        E* Kg = (E*)a.Kt + slot * D * C;
+        const float glast = sm.gam[len - 1];
+        for (int e = t0; e < D * (C / V); e += nt) {
+          const int d = e / (C / V), s0 = (e % (C / V)) * V;
+          float val[V], lo[V];
+#pragma unroll
+          for (int i = 0; i < V; ++i) {
+            const int s = s0 + i;
+            val[i] = (s < len) ? to_f<E>(sm.Kt[d][s]) * __expf(glast - sm.gam[s]) : 0.f;
+            lo[i] = val[i] - to_f<E>(from_f<E>(val[i]));
+          }
+          Vec<E>::store(Kg + d * C + s0, val);
+          if constexpr (Split<E>::on) Vec<E>::store((E*)a.Ktl + slot * D * C + d * C + s0, lo);
+        }
+        if constexpr (LO_OUT) {
+          // rows e_s k_s [C][D] and (Gam_r q_r)^T [D][C], hi / lo, for the reverse state pass
+          for (int e = t0; e < C * (D / V); e += nt) {
+            const int s = e / (D / V), c0 = (e % (D / V)) * V;
+            const float es = (s < len) ? __expf(glast - sm.gam[s]) : 0.f;
+            float val[V], lo[V];
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+              val[i] = es * to_f<E>(sm.Ks[s][c0 + i]);
+              lo[i] = val[i] - to_f<E>(from_f<E>(val[i]));
+            }
+            const int64_t o = slot * C * D + (int64_t)s * D + c0;
+            Vec<E>::store((E*)a.Krh + o, val);
+            if constexpr (Split<E>::on) Vec<E>::store((E*)a.Krl + o, lo);
+          }
+          // Q^T through V x V register blocks: a thread reads V rows of V
+          // consecutive d and writes V rows of Q^T; adjacent lanes take adjacent
+          // d blocks (conflict-free LDS reads), and the C / V lanes sharing a d
+          // block write whole rows of Q^T
+          constexpr int DB = D / V, SB = C / V, DF = DB >= 8 ? 8 : DB;
+          for (int e = t0; e < DB * SB; e += nt) {
+            const int d0 = (e % DF + DF * (e / (DF * SB))) * V, s0 = ((e / DF) % SB) * V;
+            float blk[V][V], gs[V];
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+              Vec<E>::load(&sm.Qs[s0 + i][d0], blk[i]);
+              gs[i] = __expf(sm.gam[s0 + i]);
+            }
+#pragma unroll
+            for (int dd = 0; dd < V; ++dd) {
+              float val[V], lo[V];
+#pragma unroll
+              for (int i = 0; i < V; ++i) {
+                val[i] = gs[i] * blk[i][dd];
+                lo[i] = val[i] - to_f<E>(from_f<E>(val[i]));
+              }
+              const int64_t o = slot * D * C + (int64_t)(d0 + dd) * C + s0;
+              Vec<E>::store((E*)a.Qth + o, val);
+              if constexpr (Split<E>::on) Vec<E>::store((E*)a.Qtl + o, lo);
+            }
+          }
+        }
+      }
+    };
+    unit_lower_inverse<C, S::LDCF, NTH>(sm.Am, sm.Tm, sm.Tt, sm.Xs, gate_outputs);  // starts and ends with a barrier
     if constexpr (LO_OUT) {  // T for the WY gradients
       for (int e = tid; e < C * (C / 4); e += NTH) {
         const int r = e / (C / 4), c = (e % (C / 4)) * 4;
@@ -193,65 +257,6 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
         if constexpr (LO_OUT) {  // Wk^T [D][C], hi / lo
           const int64_t o = slot * D * C + (int64_t)(ct * 16 + acc_col()) * C + rt * 16 + acc_row(0);
           st4_split<E>((E*)a.Wth + o, (E*)a.Wtl + o, acc);
-        }
-      }
-    }
-    // Kt_e[d][s] = e^{gamma_last - gamma_s} k_s[d]  (s < len), 0 past len
-    {
-      E* Kg = (E*)a.Kt + slot * D * C;
-      const float glast = sm.gam[len - 1];
-      for (int e = tid; e < D * (C / V); e += NTH) {
-        const int d = e / (C / V), s0 = (e % (C / V)) * V;
-        float val[V], lo[V];
-#pragma unroll
-        for (int i = 0; i < V; ++i) {
-          const int s = s0 + i;
-          val[i] = (s < len) ? to_f<E>(sm.Kt[d][s]) * __expf(glast - sm.gam[s]) : 0.f;
-          lo[i] = val[i] - to_f<E>(from_f<E>(val[i]));
-        }
-        Vec<E>::store(Kg + d * C + s0, val);
-        if constexpr (Split<E>::on) Vec<E>::store((E*)a.Ktl + slot * D * C + d * C + s0, lo);
-      }
-      if constexpr (LO_OUT) {
-        // rows e_s k_s [C][D] and (Gam_r q_r)^T [D][C], hi / lo, for the reverse state pass
-        for (int e = tid; e < C * (D / V); e += NTH) {
-          const int s = e / (D / V), c0 = (e % (D / V)) * V;
-          const float es = (s < len) ? __expf(glast - sm.gam[s]) : 0.f;
-          float val[V], lo[V];
-#pragma unroll
-          for (int i = 0; i < V; ++i) {
-            val[i] = es * to_f<E>(sm.Ks[s][c0 + i]);
-            lo[i] = val[i] - to_f<E>(from_f<E>(val[i]));
-          }
-          const int64_t o = slot * C * D + (int64_t)s * D + c0;
-          Vec<E>::store((E*)a.Krh + o, val);
-          if constexpr (Split<E>::on) Vec<E>::store((E*)a.Krl + o, lo);
-        }
-        // Q^T through V x V register blocks: a thread reads V rows of V
-        // consecutive d and writes V rows of Q^T; adjacent lanes take adjacent
-        // d blocks (conflict-free LDS reads), and the C / V lanes sharing a d
-        // block write whole rows of Q^T
-        constexpr int DB = D / V, SB = C / V, DF = DB >= 8 ? 8 : DB;
-        for (int e = tid; e < DB * SB; e += NTH) {
-          const int d0 = (e % DF + DF * (e / (DF * SB))) * V, s0 = ((e / DF) % SB) * V;
-          float blk[V][V], gs[V];
-#pragma unroll
-          for (int i = 0; i < V; ++i) {
-            Vec<E>::load(&sm.Qs[s0 + i][d0], blk[i]);
-            gs[i] = __expf(sm.gam[s0 + i]);
-          }
-#pragma unroll
-          for (int dd = 0; dd < V; ++dd) {
-            float val[V], lo[V];
-#pragma unroll
-            for (int i = 0; i < V; ++i) {
-              val[i] = gs[i] * blk[i][dd];
-              lo[i] = val[i] - to_f<E>(from_f<E>(val[i]));
-            }
-            const int64_t o = slot * D * C + (int64_t)(d0 + dd) * C + s0;
-            Vec<E>::store((E*)a.Qth + o, val);
-            if constexpr (Split<E>::on) Vec<E>::store((E*)a.Qtl + o, lo);
-          }
         }
       }
     }
