@@ -215,13 +215,15 @@ template <typename E, int D, int C, int NTH>
 struct GradASmem {
   static constexpr int LO = Split<E>::on ? 1 : 0;
   static constexpr int LDQ = D + Pad<E>::E16;
+  static constexpr bool K_IN_HL = LO && D >= C;  // K's C rows fit the lo half of the H region
   E Hh[D][LDQ];                 // Hc, then dHn (hi)
-  E Hl[LO ? D : 1][LDQ];        // lo parts; K while the H region is between uses
-  E Os[C][LDQ];                 // dO, then dWk hi, then dO again
+  E Hl[LO ? D : 1][LDQ];        // lo parts; K while the H region is between uses (K_IN_HL)
+  E Od[C][LDQ];                 // dO (read in (a) and (d))
+  E Os[C][LDQ];                 // dWk hi
   E Xh[C][LDQ];                 // dW, then W (hi)
   E Xl[LO ? C : 1][LDQ];        // lo parts
   E Vs[C][LDQ];                 // V, then dWk lo
-  E Ks[LO ? 1 : C][LDQ];        // K (float operands only)
+  E Ks[K_IN_HL ? 1 : C][LDQ];   // K, where it does not fit the H region
   float bs[C], gm[C], em[C];
   float red[NTH];
 };
@@ -249,7 +251,7 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
   const int64_t ldo = (int64_t)a.Hv * D;
   E* Hlo = LO ? &sm.Hl[0][0] : nullptr;
   E* Xlo = LO ? &sm.Xl[0][0] : nullptr;
-  E* Kst = LO ? &sm.Hl[0][0] : &sm.Ks[0][0];  // K reuses the lo half of the H region
+  E* Kst = S::K_IN_HL ? &sm.Hl[0][0] : &sm.Ks[0][0];
 
   {  // stage Hc, dO, dW, V
     TileRegs<float, D, D, NTH> rH;
@@ -260,7 +262,7 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
     rW.load(a.dW + slot * C * D, D, C);
     rV.load((const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)h * D, a.sv, len);
     rH.template store_split<E>(&sm.Hh[0][0], Hlo, S::LDQ);
-    rO.store(&sm.Os[0][0], S::LDQ);
+    rO.store(&sm.Od[0][0], S::LDQ);
     rW.template store_split<E>(&sm.Xh[0][0], Xlo, S::LDQ);
     rV.store(&sm.Vs[0][0], S::LDQ);
   }
@@ -278,7 +280,7 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
     f32x4 acc[CD][RT];
     zero_blk(acc);
     mm_blk<E, D, CD, RT, LO, false>(acc, &sm.Hh[d0 * 16][0], LO ? &sm.Hl[d0 * 16][0] : nullptr, S::LDQ,
-                                    &sm.Os[r0 * 16][0], nullptr, S::LDQ);
+                                    &sm.Od[r0 * 16][0], nullptr, S::LDQ);
 #pragma unroll
     for (int i = 0; i < CD; ++i)
 #pragma unroll
@@ -382,14 +384,11 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
   }
   __syncthreads();  // dWk and K are no longer read
 
-  {  // stage dHn, W, dO again
+  {  // stage dHn, W (dO is still staged)
     TileRegs<float, C, D, NTH> rW;
-    TileRegs<E, C, D, NTH> rO;
     rW.load(a.W + slot * C * D, D, C);
-    rO.load(dog, ldo, len);
     rD.template store_split<E>(&sm.Hh[0][0], Hlo, S::LDQ);
     rW.template store_split<E>(&sm.Xh[0][0], Xlo, S::LDQ);
-    rO.store(&sm.Os[0][0], S::LDQ);
   }
   __syncthreads();
   if (tid == 0) {
@@ -417,7 +416,7 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
   for_blocks<NT, NT, RT, CC, NW>([&](int r0, int c0) {
     f32x4 acc[RT][CC];
     zero_blk(acc);
-    mm_blk<E, D, RT, CC, false, LO>(acc, &sm.Os[r0 * 16][0], nullptr, S::LDQ, &sm.Xh[c0 * 16][0],
+    mm_blk<E, D, RT, CC, false, LO>(acc, &sm.Od[r0 * 16][0], nullptr, S::LDQ, &sm.Xh[c0 * 16][0],
                                     LO ? &sm.Xl[c0 * 16][0] : nullptr, S::LDQ);
 #pragma unroll
     for (int i = 0; i < RT; ++i)

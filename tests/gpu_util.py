@@ -7,6 +7,12 @@ import gated_delta_rule_conv1d_amd as gdn
 import synth
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
+# Outputs the chunk stage stores in fp32 (ht, dh0, dg, dbeta): in bf16 mode the
+# oracle sees the same bf16-rounded inputs, so only the kernel's own arithmetic
+# (bf16 hi/lo operand splits, about 16 significant bits, fp32 sums) separates
+# them: max|diff| <= 2e-3 RMS (the worst case over the small chunk cases is
+# 8e-4, ht).
+TOL_F32_OUT = {"f32": 1e-4, "bf16": 2e-3}
 
 
 def dev():
