@@ -8,6 +8,7 @@ namespace gdn {
 
 constexpr int kChunkThreads = 256;  // 4 waves per workgroup
 constexpr int kChunkWaves = kChunkThreads / kWave;
+constexpr int kNumCUs = 256;        // MI355X: 8 XCDs x 32 compute units
 
 // What a forward pass over the chunks produces: the output (o and the final
 // states), the per-chunk products the backward reads (the preparation pass's

@@ -462,6 +462,25 @@ void run_chunk_index(const gdn_shape* s, const int32_t* cu, int32_t* table, int3
 template <typename E, int D>
 constexpr int state_dvt() { return D >= 32 ? 32 : D; }
 
+// The one-workgroup-per-(sequence, v-head) state pass runs one serial chain of
+// chunk steps per workgroup; with few chains most of the chip idles (a single
+// long sequence has only Hv of them).  Then each state is split into
+// independent 16-column dv tiles (exact: the update multiplies the state from
+// the left only), eight times the workgroups, each step re-staging the shared
+// chunk operands.  Measured at d = 128, chunk 64: 32 chains (one 65536-token
+// sequence) 8.0 -> 3.1 ms; at 128 chains the whole-state pass stays ahead
+// (0.28 ms against 0.30 with 32-column and 0.41 with 16-column tiles).
+// Returns the tile width to use, or 0 for the whole-state pass.
+inline int narrow_state_dvt(const ChunkArgs& a) { return a.N * a.Hv * 4 <= kNumCUs ? 16 : 0; }
+
+template <typename E, int D, int C, int DVT>
+static void launch_state_fwd_tiled(const ChunkArgs& a, hipStream_t st, int mode) {
+  const dim3 grid(state_grid(a.N, a.Hk, a.G, D / DVT));
+  if (mode == kFwdOut) state_fwd_kernel<E, D, C, DVT, kFwdOut><<<grid, kChunkThreads, 0, st>>>(a);
+  else if (mode == kFwdStore) state_fwd_kernel<E, D, C, DVT, kFwdStore><<<grid, kChunkThreads, 0, st>>>(a);
+  else state_fwd_kernel<E, D, C, DVT, kFwdBoth><<<grid, kChunkThreads, 0, st>>>(a);
+}
+
 template <typename E, int D, int C>
 void launch_chunk_fwd_core(const ChunkArgs& a, hipStream_t st, int mode) {
   constexpr int DVT = state_dvt<E, D>();
@@ -474,15 +493,16 @@ void launch_chunk_fwd_core(const ChunkArgs& a, hipStream_t st, int mode) {
     if (mode == kFwdOut) prep_kernel<E, D, C, false, NTH><<<gprep, NTH, 0, st>>>(a);
     else prep_kernel<E, D, C, true, NTH><<<gprep, NTH, 0, st>>>(a);
   }
-  dim3 gstate(state_grid(a.N, a.Hk, a.G, D / DVT));
   GDN_PROF(state_name[mode], st);
   if constexpr (use_wide_state<E, D, C>()) {
-    launch_state_fwd_wide(a, st, mode);
+    // every mode takes the same choice, so that the saved training pair and
+    // the recomputing backward see the same H_c and W bits
+    const int ndvt = narrow_state_dvt(a);
+    if (ndvt == 16) launch_state_fwd_tiled<E, D, C, 16>(a, st, mode);
+    else launch_state_fwd_wide(a, st, mode);
     return;
   }
-  if (mode == kFwdOut) state_fwd_kernel<E, D, C, DVT, kFwdOut><<<gstate, kChunkThreads, 0, st>>>(a);
-  else if (mode == kFwdStore) state_fwd_kernel<E, D, C, DVT, kFwdStore><<<gstate, kChunkThreads, 0, st>>>(a);
-  else state_fwd_kernel<E, D, C, DVT, kFwdBoth><<<gstate, kChunkThreads, 0, st>>>(a);
+  launch_state_fwd_tiled<E, D, C, DVT>(a, st, mode);
 }
 
 // explicit instantiation helpers used by the dispatcher in chunk_bwd.hip
