@@ -176,6 +176,28 @@ def norm_gate_bwd(o, z, w, dy, eps=NORM_EPS, bits=64):
     return d_o, dz, dw
 
 
+def gates(a, b, A_log, dt_bias, bits=64):
+    """g = -exp(A_log) * softplus(a + dt_bias), beta = sigmoid(b); a, b [T, Hv]."""
+    a = _c(a, bits); b = _c(b, bits); A_log = _c(A_log, bits); dt_bias = _c(dt_bias, bits)
+    T, Hv = a.shape
+    g = np.empty_like(a); beta = np.empty_like(b)
+    _lib(bits).oracle_gates(ctypes.c_long(T), ctypes.c_int(Hv), _p(a), _p(b), _p(A_log), _p(dt_bias),
+                            _p(g), _p(beta))
+    return g, beta
+
+
+def gates_bwd(a, b, A_log, dt_bias, dg, dbeta, bits=64):
+    """Gradients of gates(): da, db [T, Hv]; dA_log, ddt_bias [Hv]."""
+    a = _c(a, bits); b = _c(b, bits); A_log = _c(A_log, bits); dt_bias = _c(dt_bias, bits)
+    dg = _c(dg, bits); dbeta = _c(dbeta, bits)
+    T, Hv = a.shape
+    da = np.empty_like(a); db = np.empty_like(b)
+    dA = np.empty_like(A_log); ddt = np.empty_like(dt_bias)
+    _lib(bits).oracle_gates_bwd(ctypes.c_long(T), ctypes.c_int(Hv), _p(a), _p(b), _p(A_log), _p(dt_bias),
+                                _p(dg), _p(dbeta), _p(da), _p(db), _p(dA), _p(ddt))
+    return dict(da=da, db=db, dA_log=dA, ddt_bias=ddt)
+
+
 # ---------------------------------------------------------------------------
 # The whole layer.
 # ---------------------------------------------------------------------------

@@ -389,6 +389,51 @@ EXPORT void oracle_norm_gate_bwd(long rows, int dv, real eps, const real* dy, co
   free(rsv);
 }
 
+/* ---------------------------------------------------------------------------
+ * Gates of the recurrence, per token t and v-head h (page: "[Qwen3.5 MoE] Add
+ * hybrid decoder model", Summary: the softplus gate):
+ *   g[t,h]    = -exp(A_log[h]) * softplus(a[t,h] + dt_bias[h])   (decay, < 0)
+ *   beta[t,h] = sigmoid(b[t,h])                                 (write strength)
+ * softplus(x) = log(1 + e^x), written as max(x, 0) + log1p(e^-|x|) so that it
+ * neither overflows for large x nor loses the small values for negative x.
+ * a, b, g, beta: [T][Hv]; A_log, dt_bias: [Hv].
+ * ------------------------------------------------------------------------- */
+static real softplus_(real x) { return (x > 0 ? x : (real)0) + log1p(exp(-fabs(x))); }
+
+EXPORT void oracle_gates(long T, int Hv, const real* a, const real* b, const real* A_log,
+                         const real* dt_bias, real* g, real* beta) {
+  for (long t = 0; t < T; ++t)
+    for (int h = 0; h < Hv; ++h) {
+      const long e = t * Hv + h;
+      g[e] = -exp(A_log[h]) * softplus_(a[e] + dt_bias[h]);
+      beta[e] = sigm(b[e]);
+    }
+}
+
+/* Reverse mode of oracle_gates.  dg, dbeta: [T][Hv] gradients w.r.t. g, beta.
+ * d softplus(x)/dx = sigmoid(x);  dg/dA_log = g;  dbeta/db = beta (1 - beta).
+ *   da[t,h] = -exp(A_log[h]) sigmoid(a + dt_bias) dg[t,h];   db = beta (1-beta) dbeta
+ *   dA_log[h] = sum_t dg[t,h] g[t,h];   ddt_bias[h] = sum_t da[t,h]   (t in order) */
+EXPORT void oracle_gates_bwd(long T, int Hv, const real* a, const real* b, const real* A_log,
+                             const real* dt_bias, const real* dg, const real* dbeta, real* da,
+                             real* db, real* dA_log, real* ddt_bias) {
+  for (int h = 0; h < Hv; ++h) {
+    dA_log[h] = 0;
+    ddt_bias[h] = 0;
+  }
+  for (long t = 0; t < T; ++t)
+    for (int h = 0; h < Hv; ++h) {
+      const long e = t * Hv + h;
+      const real x = a[e] + dt_bias[h];
+      const real gv = -exp(A_log[h]) * softplus_(x);
+      const real bv = sigm(b[e]);
+      da[e] = -exp(A_log[h]) * sigm(x) * dg[e];
+      db[e] = bv * ((real)1 - bv) * dbeta[e];
+      dA_log[h] += dg[e] * gv;
+      ddt_bias[h] += da[e];
+    }
+}
+
 EXPORT int oracle_real_bytes(void) { return (int)sizeof(real); }
 
 EXPORT int oracle_threads(void) {

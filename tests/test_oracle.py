@@ -3,6 +3,7 @@
 finite differences, or an independent autograd transcription)."""
 import numpy as np
 import pytest
+import scipy.special
 import torch
 import torch.nn.functional as F
 
@@ -403,3 +404,57 @@ def test_chunk_table_rules():
     tab, first = oracle.chunk_table(cu, 16)
     assert tab.tolist() == [[0, 0, 5], [2, 5, 16], [3, 21, 16], [3, 37, 1], [4, 38, 1]]
     assert first.tolist() == [0, 1, 1, 2, 4, 5]
+
+
+# ---------------------------------------------------------------- gates
+def test_gates_closed_forms_and_library_softplus():
+    """softplus against numpy's logaddexp(0, x) and sigmoid against scipy's
+    expit (library routines) over the whole float range the gates meet; g(A_log = 0, a + dt_bias = 0) = -ln 2;
+    beta(0) = 1/2 and beta(b) + beta(-b) = 1; g < 0 wherever softplus > 0."""
+    x = np.concatenate([np.linspace(-60, 60, 4001), [-700.0, -300.0, 300.0, 700.0]])
+    T = x.size
+    a = x[:, None]
+    b = x[:, None]
+    g, beta = oracle.gates(a, b, np.zeros(1), np.zeros(1))
+    np.testing.assert_allclose(-g[:, 0], np.logaddexp(0.0, x), rtol=1e-14, atol=0)
+    np.testing.assert_allclose(beta[:, 0], scipy.special.expit(x), rtol=1e-14, atol=0)
+    gz, bz = oracle.gates(np.zeros((1, 3)), np.zeros((1, 3)), np.zeros(3), np.zeros(3))
+    np.testing.assert_allclose(gz, -np.log(2.0), rtol=1e-15)
+    np.testing.assert_array_equal(bz, 0.5)
+    _, bn = oracle.gates(a, -b, np.zeros(1), np.zeros(1))
+    np.testing.assert_allclose(beta + bn, 1.0, rtol=1e-15)
+    assert np.all(g[np.abs(x) < 700] < 0)
+    # the decay rate scales exactly by exp(A_log), and dt_bias shifts a
+    rng = np.random.default_rng(3)
+    a2 = rng.standard_normal((17, 4)); A = rng.uniform(0, 2, 4); dt = rng.standard_normal(4)
+    g1, _ = oracle.gates(a2, a2, A, dt)
+    g0, _ = oracle.gates(a2 + dt, a2, np.zeros(4), np.zeros(4))
+    np.testing.assert_allclose(g1, g0 * np.exp(A), rtol=1e-14)
+    assert T == g.shape[0]
+
+
+def test_gates_backward_finite_differences():
+    """Every gradient of the gates against central differences of
+    L = sum(wg * g + wb * beta)."""
+    rng = np.random.default_rng(5)
+    T, Hv = 7, 3
+    a = rng.standard_normal((T, Hv)); b = rng.standard_normal((T, Hv))
+    A = rng.uniform(0, 2, Hv); dt = rng.standard_normal(Hv)
+    wg = rng.standard_normal((T, Hv)); wb = rng.standard_normal((T, Hv))
+    r = oracle.gates_bwd(a, b, A, dt, wg, wb)
+
+    def loss(a_, b_, A_, dt_):
+        g, beta = oracle.gates(a_, b_, A_, dt_)
+        return float(np.sum(wg * g) + np.sum(wb * beta))
+
+    eps = 1e-6
+    for name, arr, key in (("a", a, "da"), ("b", b, "db"), ("A_log", A, "dA_log"), ("dt_bias", dt, "ddt_bias")):
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            args = {"a": a.copy(), "b": b.copy(), "A_log": A.copy(), "dt_bias": dt.copy()}
+            args[name][idx] += eps
+            lp = loss(args["a"], args["b"], args["A_log"], args["dt_bias"])
+            args[name][idx] -= 2 * eps
+            lm = loss(args["a"], args["b"], args["A_log"], args["dt_bias"])
+            fd[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(r[key], fd, rtol=1e-7, atol=1e-9, err_msg=name)
