@@ -1,9 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark the GatedDeltaNet layer on one MI355X.
 
-One step = the whole layer path over one packed row: conv1d+SiLU+L2, the
-chunked gated delta rule, RMSNormGated, and (for the training workload) the
-backward of all three.  Default workload: the training step, 8 sequences x
+One step = the whole layer path over one packed row: the gates (g, beta from
+a, b, A_log, dt_bias), conv1d+SiLU+L2, the chunked gated delta rule,
+RMSNormGated, and (for the training workload) the backward of all four.  Default workload: the training step, 8 sequences x
 8192 tokens packed in one row, 16 q/k heads, 32 v heads, d = 128, bf16.
 
 Prints ONE JSON line with the throughput (tokens/s), the roofline of the
@@ -32,6 +32,8 @@ WORKLOADS = {
     "varlen": "forward: 20 log-uniform lengths packed into 32768 tokens, h0 in / ht out, d=128, bf16",
     "long": "forward: one 65536-token sequence, 16 qk / 32 v heads, d=128, bf16",
     "tiny": "forward: 64 tokens, 2 heads, d=16, chunk 16, fp32",
+    "decode": "decode: 256 sequences advance one token each from their states and conv windows, "
+              "16 qk / 32 v heads, d=128, bf16",
 }
 
 
@@ -65,6 +67,11 @@ def kernel_bytes(cfg, n_chunks: int, has_h0: bool) -> dict:
     st = N * Hv * dd_f                        # one state per (sequence, v-head)
     prep_out = S * (tile_e + tile_f + cc_f + lo * tile_e + row_f)   # Wk, U, P, K~^T (hi, lo), gamma
     return {
+        # decode: the state is read and written once per (sequence, v-head)
+        "recurrent_step": 2 * N * Hv * dd_f + N * (2 * Hk * D + 2 * Hv * D) * es + 2 * N * Hv * 4,
+        "conv_step": (2 * (W - 1) + 2) * N * Cch * es + Cch * W * es,
+        "gates_fwd": 4 * T * Hv * 4 + 2 * Hv * 4,    # a, b in; g, beta out
+        "gates_bwd": 6 * T * Hv * 4 + 2 * Hv * 4,    # a, b, dg, dbeta in; da, db out
         "conv_fwd": 2 * T * Cch * es + Cch * W * es,
         "conv_bwd": 3 * T * Cch * es + Cch * W * es,
         "norm_fwd": 3 * T * Hv * D * es + D * es,
@@ -135,15 +142,20 @@ def cpu_baseline(cfg, inp, kheads: int):
     import oracle
     sub_cfg, sub, _, _ = oracle.subset(cfg, inp, list(range(cfg.N)), list(range(kheads)))
     sub = {k: (v.astype("float64") if v.dtype.kind == "f" else v) for k, v in sub.items()}
+    hv = kheads * cfg.h_v // cfg.h_qk
+    gate_in = [inp["a"][:, :hv], inp["b"][:, :hv], inp["A_log"][:hv], inp["dt_bias"][:hv]]
     t0 = time.perf_counter()
+    g, beta = oracle.gates(*gate_in)
     fwd = oracle.layer_fwd(sub_cfg, sub)
     if cfg.bwd:
-        oracle.layer_bwd(sub_cfg, sub, fwd, sub["dy"])
+        r = oracle.layer_bwd(sub_cfg, sub, fwd, sub["dy"])
+        oracle.gates_bwd(*gate_in, r["dg"], r["dbeta"])
     dt = time.perf_counter() - t0
     tokens_equiv = cfg.T * kheads / cfg.h_qk
     return {"value": tokens_equiv / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"all {cfg.N} sequences ({cfg.T} tokens) x {kheads} of {cfg.h_qk} q/k heads "
-                      f"({kheads * cfg.h_v // cfg.h_qk} v-heads), fp64 {'fwd+bwd' if cfg.bwd else 'fwd'}; "
+            "sample": ("one-token sequences from the same states, conv from zero history: " if cfg.decode else "") +
+                      f"all {cfg.N} sequences ({cfg.T} tokens) x {kheads} of {cfg.h_qk} q/k heads "
+                      f"({hv} v-heads), gates + layer, fp64 {'fwd+bwd' if cfg.bwd else 'fwd'}; "
                       f"{dt:.1f} s scaled to whole-layer tokens/s",
             "seconds": dt}
 
@@ -181,7 +193,7 @@ def main():
 
     cfg = synth.config(args.workload)
     t_gen = time.perf_counter()
-    inp = synth.make_inputs(cfg)
+    inp = synth.make_inputs(cfg, keep_raw=True)
     t_gen = time.perf_counter() - t_gen
     dev = torch.device("cuda:0")
     bf = cfg.dtype == "bf16"
@@ -192,7 +204,7 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(inp[key], dtype=np.float32)).to(dev)
 
     x, w = to_dev("x"), to_dev("w_conv")
-    g, beta = to_dev("g"), to_dev("beta")
+    ga, gb, A_log, dt_bias = (to_dev(k) for k in ("a", "b", "A_log", "dt_bias"))
     cu = torch.from_numpy(inp["cu"]).to(dev)
     z = to_dev("z") if cfg.norm else None
     wn = to_dev("w_norm") if cfg.norm else None
@@ -202,11 +214,24 @@ def main():
                       gdn.BF16 if bf else gdn.F32, 1.0)
     layer = gdn.GatedDeltaNetLayer(shape, cfg.width, dev, norm=cfg.norm)
 
-    def step():
-        # a training step keeps the forward's chunk products for the backward
-        f = layer.forward(x, w, g, beta, cu, z, wn, h0, for_backward=cfg.bwd)
-        if cfg.bwd:
-            layer.backward(dy, x, w, g, beta, cu, f, z, wn, h0)
+    if cfg.decode:
+        window = to_dev("window")
+        state = h0  # advanced in place, step after step
+
+        def step():
+            g, beta = layer.gates(ga, gb, A_log, dt_bias)
+            yc = gdn.conv1d_step(x, w, window, shape)
+            q, k, v = layer.split(yc)
+            o, _ = gdn.recurrent_step(q, k, v, g, beta, shape, state_in=state, state_out=state)
+            gdn.norm_gate(o, z, wn, shape)
+    else:
+        def step():
+            g, beta = layer.gates(ga, gb, A_log, dt_bias)
+            # a training step keeps the forward's chunk products for the backward
+            f = layer.forward(x, w, g, beta, cu, z, wn, h0, for_backward=cfg.bwd)
+            if cfg.bwd:
+                r = layer.backward(dy, x, w, g, beta, cu, f, z, wn, h0)
+                layer.gates_backward(ga, gb, A_log, dt_bias, r["dg"], r["dbeta"])
 
     # Per-kernel durations come from HIP events that the library records around
     # each launch on the stream it launches on, during the timed steps
@@ -266,8 +291,9 @@ def main():
         cpu = cpu_baseline(cfg, inp, min(args.cpu_heads, cfg.h_qk))
 
     out = {
-        "metric": "GatedDeltaNet fwd+bwd tokens/s, packed varlen H=32 d=128 bf16; % roofline"
-        if cfg.bwd else "GatedDeltaNet fwd tokens/s, packed varlen; % roofline",
+        "metric": ("GatedDeltaNet fwd+bwd tokens/s, packed varlen H=32 d=128 bf16; % roofline" if cfg.bwd else
+                   "GatedDeltaNet decode tokens/s (one token per sequence); % roofline" if cfg.decode else
+                   "GatedDeltaNet fwd tokens/s, packed varlen; % roofline"),
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -281,6 +307,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}", "tokens": cfg.T,
                    "n_seqs": cfg.N, "h_qk": cfg.h_qk, "h_v": cfg.h_v, "d": cfg.d_k, "chunk": cfg.chunk,
+                   "gates": "g, beta computed from a, b, A_log, dt_bias in the step",
                    "parallelism": "single GPU"},
         "roofline": roof,
         "step_fraction_of_fused_minimum": (round(step_bytes / (HBM_PEAK_GBS * 1e9) / (ms_per_step * 1e-3), 4)

@@ -17,7 +17,9 @@ _STATUS = {0: "GDN_OK", -1: "GDN_ERR_INVALID_ARG", -2: "GDN_ERR_UNSUPPORTED", -3
 SYMBOLS = ("gdn_status_string", "gdn_max_chunks", "gdn_chunk_index", "gdn_conv1d", "gdn_conv1d_bwd_workspace",
            "gdn_conv1d_bwd", "gdn_chunk_fwd_workspace", "gdn_chunk_fwd", "gdn_chunk_bwd_workspace",
            "gdn_chunk_bwd", "gdn_chunk_fwd_save", "gdn_chunk_bwd_saved", "gdn_norm_gate",
-           "gdn_norm_gate_bwd_workspace", "gdn_norm_gate_bwd", "gdn_profile_enable", "gdn_profile_report")
+           "gdn_norm_gate_bwd_workspace", "gdn_norm_gate_bwd", "gdn_gates", "gdn_gates_bwd_workspace",
+           "gdn_gates_bwd", "gdn_recurrent_step", "gdn_conv1d_step", "gdn_conv1d_window", "gdn_profile_enable",
+           "gdn_profile_report")
 
 
 class GdnError(RuntimeError):
@@ -91,6 +93,12 @@ def load() -> ctypes.CDLL:
             "gdn_norm_gate": (I32, [S, P, P, P, F, P, P]),
             "gdn_norm_gate_bwd_workspace": (SZ, [S]),
             "gdn_norm_gate_bwd": (I32, [S, P, P, P, P, F, P, P, P, P, SZ, P]),
+            "gdn_gates": (I32, [S, P, P, P, P, P, P, P]),
+            "gdn_gates_bwd_workspace": (SZ, [S]),
+            "gdn_gates_bwd": (I32, [S, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+            "gdn_recurrent_step": (I32, [S, P, P, P, I64, I64, P, P, P, P, P, P]),
+            "gdn_conv1d_step": (I32, [S, P, P, I32, F, P, P, P]),
+            "gdn_conv1d_window": (I32, [S, P, I32, P, P, P, P]),
             "gdn_profile_enable": (None, [ctypes.c_int]),
             "gdn_profile_report": (SZ, [ctypes.c_char_p, SZ]),
         }
@@ -307,6 +315,96 @@ def norm_gate_bwd(dy, o, z, w_norm, shape: Shape, eps: float = 1e-6, ws: Optiona
                                                          _ptr(w_norm), float(eps), _ptr(d_o), _ptr(dz), _ptr(dw),
                                                          _ptr(ws), ws.numel(), _stream(o.device)))
     return d_o, dz, dw
+
+
+# ----------------------------------------------------------------------------- gates
+def gates(a: torch.Tensor, b: torch.Tensor, A_log: torch.Tensor, dt_bias: torch.Tensor, shape: Shape):
+    """g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b); a, b float32 [T, Hv]."""
+    sh = (shape.total_tokens, shape.h_v)
+    _need(a, "a", torch.float32, sh)
+    _need(b, "b", torch.float32, sh)
+    _need(A_log, "A_log", torch.float32, (shape.h_v,))
+    _need(dt_bias, "dt_bias", torch.float32, (shape.h_v,))
+    g = torch.empty_like(a)
+    beta = torch.empty_like(b)
+    _check("gdn_gates", load().gdn_gates(ctypes.byref(shape.c()), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias),
+                                         _ptr(g), _ptr(beta), _stream(a.device)))
+    return g, beta
+
+
+def gates_bwd_workspace(shape: Shape) -> int:
+    return int(load().gdn_gates_bwd_workspace(ctypes.byref(shape.c())))
+
+
+def gates_bwd(a, b, A_log, dt_bias, dg, dbeta, shape: Shape, ws: Optional[torch.Tensor] = None):
+    """Gradients of gates(): dict(da, db [T, Hv], dA_log, ddt_bias [Hv])."""
+    sh = (shape.total_tokens, shape.h_v)
+    for t, nm in ((a, "a"), (b, "b"), (dg, "dg"), (dbeta, "dbeta")):
+        _need(t, nm, torch.float32, sh)
+    _need(A_log, "A_log", torch.float32, (shape.h_v,))
+    _need(dt_bias, "dt_bias", torch.float32, (shape.h_v,))
+    da = torch.empty_like(a)
+    db = torch.empty_like(b)
+    dA = torch.empty_like(A_log)
+    ddt = torch.empty_like(dt_bias)
+    ws = _workspace(gates_bwd_workspace(shape), a.device, ws)
+    _check("gdn_gates_bwd", load().gdn_gates_bwd(ctypes.byref(shape.c()), _ptr(a), _ptr(b), _ptr(A_log),
+                                                 _ptr(dt_bias), _ptr(dg), _ptr(dbeta), _ptr(da), _ptr(db), _ptr(dA),
+                                                 _ptr(ddt), _ptr(ws), ws.numel(), _stream(a.device)))
+    return dict(da=da, db=db, dA_log=dA, ddt_bias=ddt)
+
+
+# ----------------------------------------------------------------------------- decode
+def recurrent_step(q, k, v, g, beta, shape: Shape, state_in=None, state_out=None, o=None):
+    """One new token per sequence (shape.total_tokens == shape.n_seqs): the gated
+    delta rule step.  state_out defaults to a new tensor; pass state_out=state_in
+    to update in place.  Returns (o, state_out)."""
+    N = shape.n_seqs
+    sqk, sv = _qkv_strides(q, k, v, shape)
+    _need(g, "g", torch.float32, (N, shape.h_v))
+    _need(beta, "beta", torch.float32, (N, shape.h_v))
+    st_shape = (N, shape.h_v, shape.d_k, shape.d_v)
+    if state_in is not None:
+        _need(state_in, "state_in", torch.float32, st_shape)
+    if state_out is None:
+        state_out = torch.empty(st_shape, dtype=torch.float32, device=q.device)
+    _need(state_out, "state_out", torch.float32, st_shape)
+    if o is None:
+        o = torch.empty((N, shape.h_v, shape.d_v), dtype=shape.torch_dtype, device=q.device)
+    _check("gdn_recurrent_step", load().gdn_recurrent_step(ctypes.byref(shape.c()), _ptr(q), _ptr(k), _ptr(v), sqk,
+                                                           sv, _ptr(g), _ptr(beta), _ptr(state_in), _ptr(state_out),
+                                                           _ptr(o), _stream(q.device)))
+    return o, state_out
+
+
+def conv1d_step(x, w_conv, conv_window, shape: Shape, l2_eps: float = 1e-6):
+    """Conv1d + SiLU + L2 of one new token per sequence; advances conv_window
+    [N, width-1, Cch] in place.  Returns y [N, Cch]."""
+    dt = shape.torch_dtype
+    C = shape.channels
+    W = int(w_conv.shape[1])
+    _need(x, "x", dt, (shape.n_seqs, C))
+    _need(w_conv, "w_conv", dt, (C, W))
+    _need(conv_window, "conv_window", dt, (shape.n_seqs, W - 1, C))
+    y = torch.empty_like(x)
+    _check("gdn_conv1d_step", load().gdn_conv1d_step(ctypes.byref(shape.c()), _ptr(x), _ptr(w_conv), W,
+                                                     float(l2_eps), _ptr(conv_window), _ptr(y), _stream(x.device)))
+    return y
+
+
+def conv1d_window(x, cu_seqlens, shape: Shape, width: int, window_in=None):
+    """The conv window [N, width-1, Cch] after a prefill of x [T, Cch]."""
+    dt = shape.torch_dtype
+    C = shape.channels
+    _need(x, "x", dt, (shape.total_tokens, C))
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (shape.n_seqs + 1,))
+    if window_in is not None:
+        _need(window_in, "window_in", dt, (shape.n_seqs, width - 1, C))
+    out = torch.empty((shape.n_seqs, width - 1, C), dtype=dt, device=x.device)
+    _check("gdn_conv1d_window", load().gdn_conv1d_window(ctypes.byref(shape.c()), _ptr(x), int(width),
+                                                         _ptr(cu_seqlens), _ptr(window_in), _ptr(out),
+                                                         _stream(x.device)))
+    return out
 
 
 # ----------------------------------------------------------------------------- diagnostics

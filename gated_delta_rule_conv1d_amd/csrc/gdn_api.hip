@@ -10,6 +10,7 @@ using namespace gdn;
 namespace {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
@@ -201,6 +202,89 @@ gdn_status gdn_norm_gate(const gdn_shape* shape, const void* o, const void* z, c
   if (!aligned16(o) || !aligned16(z) || !aligned16(w_norm) || !aligned16(y)) return GDN_ERR_INVALID_ARG;
   if (!(eps >= 0.f)) return GDN_ERR_INVALID_ARG;
   if (!run_norm_fwd(shape, o, z, w_norm, eps, y, (hipStream_t)stream)) return GDN_ERR_UNSUPPORTED;
+  return launched();
+}
+
+gdn_status gdn_gates(const gdn_shape* shape, const float* a, const float* b, const float* A_log, const float* dt_bias,
+                     float* g, float* beta, gdn_stream stream) {
+  gdn_status st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  const bool any = shape->total_tokens > 0;
+  if (!A_log || !dt_bias || (any && (!a || !b || !g || !beta))) return GDN_ERR_INVALID_ARG;
+  if (!aligned4(a) || !aligned4(b) || !aligned4(A_log) || !aligned4(dt_bias) || !aligned4(g) || !aligned4(beta))
+    return GDN_ERR_INVALID_ARG;
+  if (any && (g == a || g == b || beta == a || beta == b || g == beta)) return GDN_ERR_INVALID_ARG;
+  run_gates_fwd(shape, a, b, A_log, dt_bias, g, beta, (hipStream_t)stream);
+  return launched();
+}
+
+size_t gdn_gates_bwd_workspace(const gdn_shape* shape) {
+  if (check_shape(shape) != GDN_OK) return 0;
+  return gates_bwd_ws_bytes(shape);
+}
+
+gdn_status gdn_gates_bwd(const gdn_shape* shape, const float* a, const float* b, const float* A_log,
+                         const float* dt_bias, const float* dg, const float* dbeta, float* da, float* db,
+                         float* dA_log, float* ddt_bias, void* ws, size_t ws_bytes, gdn_stream stream) {
+  gdn_status st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  const bool any = shape->total_tokens > 0;
+  if (!A_log || !dt_bias || !dA_log || !ddt_bias || (any && (!a || !b || !dg || !dbeta || !da || !db)))
+    return GDN_ERR_INVALID_ARG;
+  if (!aligned4(a) || !aligned4(b) || !aligned4(A_log) || !aligned4(dt_bias) || !aligned4(dg) || !aligned4(dbeta) ||
+      !aligned4(da) || !aligned4(db) || !aligned4(dA_log) || !aligned4(ddt_bias))
+    return GDN_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws) || ws_bytes < gates_bwd_ws_bytes(shape)) return GDN_ERR_WORKSPACE;
+  run_gates_bwd(shape, a, b, A_log, dt_bias, dg, dbeta, da, db, dA_log, ddt_bias, ws, (hipStream_t)stream);
+  return launched();
+}
+
+gdn_status gdn_recurrent_step(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                              int64_t tok_stride_qk, int64_t tok_stride_v, const float* g, const float* beta,
+                              const float* state_in, float* state_out, void* o, gdn_stream stream) {
+  gdn_status st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  if (shape->total_tokens != shape->n_seqs) return GDN_ERR_INVALID_ARG;  // one token per sequence
+  if (!q || !k || !v || !g || !beta || !state_out || !o) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(state_in) ||
+      !aligned16(state_out) || !aligned4(g) || !aligned4(beta))
+    return GDN_ERR_INVALID_ARG;
+  if (!stride_ok(shape, tok_stride_qk, (int64_t)shape->h_qk * shape->d_k) ||
+      !stride_ok(shape, tok_stride_v, (int64_t)shape->h_v * shape->d_v))
+    return GDN_ERR_INVALID_ARG;
+  if (!run_recurrent_step(shape, q, k, v, tok_stride_qk, tok_stride_v, g, beta, state_in, state_out, o,
+                          (hipStream_t)stream))
+    return GDN_ERR_UNSUPPORTED;
+  return launched();
+}
+
+gdn_status gdn_conv1d_step(const gdn_shape* shape, const void* x, const void* w_conv, int32_t width, float l2_eps,
+                           void* conv_window, void* y, gdn_stream stream) {
+  gdn_status st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  if (width < 2 || width > 4) return GDN_ERR_UNSUPPORTED;
+  if (shape->total_tokens != shape->n_seqs) return GDN_ERR_INVALID_ARG;
+  if (shape->n_seqs > 65535) return GDN_ERR_UNSUPPORTED;  // one grid row per sequence
+  if (!x || !w_conv || !conv_window || !y || y == x || y == conv_window || x == conv_window)
+    return GDN_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(conv_window)) return GDN_ERR_INVALID_ARG;
+  if (!(l2_eps >= 0.f)) return GDN_ERR_INVALID_ARG;
+  if (!run_conv_step(shape, x, w_conv, width, l2_eps, conv_window, y, (hipStream_t)stream))
+    return GDN_ERR_UNSUPPORTED;
+  return launched();
+}
+
+gdn_status gdn_conv1d_window(const gdn_shape* shape, const void* x, int32_t width, const int32_t* cu_seqlens,
+                             const void* window_in, void* window_out, gdn_stream stream) {
+  gdn_status st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  if (width < 2 || width > 4) return GDN_ERR_UNSUPPORTED;
+  if (shape->n_seqs > 65535) return GDN_ERR_UNSUPPORTED;
+  const bool any = shape->total_tokens > 0;
+  if (!cu_seqlens || !window_out || (any && !x) || window_in == window_out) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(window_in) || !aligned16(window_out)) return GDN_ERR_INVALID_ARG;
+  if (!run_conv_window(shape, x, width, cu_seqlens, window_in, window_out, (hipStream_t)stream))
+    return GDN_ERR_UNSUPPORTED;
   return launched();
 }
 

@@ -23,6 +23,23 @@ bool run_norm_fwd(const gdn_shape* s, const void* o, const void* z, const void* 
 bool run_norm_bwd(const gdn_shape* s, const void* dy, const void* o, const void* z, const void* w, float eps,
                   void* d_o, void* dz, float* dw, void* ws, hipStream_t st);
 
+// gates.hip
+size_t gates_bwd_ws_bytes(const gdn_shape* s);
+void run_gates_fwd(const gdn_shape* s, const float* a, const float* b, const float* A_log, const float* dt_bias,
+                   float* g, float* beta, hipStream_t st);
+void run_gates_bwd(const gdn_shape* s, const float* a, const float* b, const float* A_log, const float* dt_bias,
+                   const float* dg, const float* dbeta, float* da, float* db, float* dA_log, float* ddt_bias,
+                   void* ws, hipStream_t st);
+
+// recurrent.hip
+bool run_recurrent_step(const gdn_shape* s, const void* q, const void* k, const void* v, int64_t sqk, int64_t sv,
+                        const float* g, const float* beta, const float* state_in, float* state_out, void* o,
+                        hipStream_t st);
+bool run_conv_step(const gdn_shape* s, const void* x, const void* w, int width, float eps, void* window, void* y,
+                   hipStream_t st);
+bool run_conv_window(const gdn_shape* s, const void* x, int width, const int32_t* cu, const void* win_in,
+                     void* win_out, hipStream_t st);
+
 // chunk_fwd.hip / chunk_bwd.hip
 int64_t max_chunks(const gdn_shape* s);
 bool chunk_supported(const gdn_shape* s);

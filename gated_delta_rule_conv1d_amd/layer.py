@@ -38,6 +38,15 @@ class GatedDeltaNetLayer:
         nq = s.h_qk * s.d_k
         return y[:, :nq], y[:, nq:2 * nq], y[:, 2 * nq:]
 
+    def gates(self, a, b, A_log, dt_bias):
+        """g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b) (gdn_gates)."""
+        return B.gates(a, b, A_log, dt_bias, self.shape)
+
+    def gates_backward(self, a, b, A_log, dt_bias, dg, dbeta):
+        """da, db, dA_log, ddt_bias from the dg, dbeta of backward() (gdn_gates_bwd)."""
+        return B.gates_bwd(a, b, A_log, dt_bias, dg, dbeta, self.shape,
+                           ws=self._buf("gates", B.gates_bwd_workspace(self.shape)))
+
     def forward(self, x, w_conv, g, beta, cu_seqlens, z=None, w_norm=None, h0=None, want_ht=True,
                 for_backward=False):
         """With for_backward=True the chunked recurrence keeps its per-chunk

@@ -132,6 +132,28 @@ gdn_status gdn_conv1d_bwd(const gdn_shape* shape, const void* dy, const void* x,
                           float* dw_conv, void* ws, size_t ws_bytes, gdn_stream stream);
 
 /* --------------------------------------------------------------------------
+ * Gates of the recurrence.  Page: "[Qwen3.5 MoE] Add hybrid decoder model",
+ * Summary (softplus registered as a pointwise op for the GatedDeltaNet gate).
+ *   g[t,h]    = -exp(A_log[h]) * softplus(a[t,h] + dt_bias[h])   (log-decay, < 0)
+ *   beta[t,h] = sigmoid(b[t,h])
+ * a, b, g, beta: float32 [T][Hv] (g, beta as gdn_chunk_fwd takes them);
+ * A_log, dt_bias: float32 [Hv].  Only shape->total_tokens and h_v are used
+ * (the other fields must still be valid).  Pointers need 4-byte alignment;
+ * g and beta must not alias a or b.  An empty row (T = 0) launches nothing.
+ * -------------------------------------------------------------------------- */
+gdn_status gdn_gates(const gdn_shape* shape, const float* a, const float* b, const float* A_log,
+                     const float* dt_bias, float* g, float* beta, gdn_stream stream);
+
+/* Reverse mode of gdn_gates.  dg, dbeta: float32 [T][Hv] gradients w.r.t. g
+ * and beta (gdn_chunk_bwd writes them).  Writes da, db [T][Hv] and dA_log,
+ * ddt_bias [Hv] (float32, sums over all tokens in a fixed order; zero for an
+ * empty row).  Workspace: gdn_gates_bwd_workspace bytes, 16-byte aligned. */
+size_t gdn_gates_bwd_workspace(const gdn_shape* shape);
+gdn_status gdn_gates_bwd(const gdn_shape* shape, const float* a, const float* b, const float* A_log,
+                         const float* dt_bias, const float* dg, const float* dbeta, float* da, float* db,
+                         float* dA_log, float* ddt_bias, void* ws, size_t ws_bytes, gdn_stream stream);
+
+/* --------------------------------------------------------------------------
  * Gated delta rule, chunked.  Pages: "[Qwen3.5 MoE] Add hybrid decoder
  * model", Summary (GatedDeltaNet linear attention, FLA kernels optional with a
  * naive fallback); "Support Qwen35 SFT", XTuner changes (varlen mode).
@@ -202,6 +224,42 @@ size_t gdn_norm_gate_bwd_workspace(const gdn_shape* shape);
 gdn_status gdn_norm_gate_bwd(const gdn_shape* shape, const void* dy, const void* o, const void* z,
                              const void* w_norm, float eps, void* d_o, void* dz, float* dw_norm,
                              void* ws, size_t ws_bytes, gdn_stream stream);
+
+/* --------------------------------------------------------------------------
+ * Token-by-token continuation (decode).  Page: "feat(models): dense Qwen3.5
+ * custom attention", KL mismatch table (RL rollouts come from an inference
+ * engine and are scored by the trainer, so the layer also runs one token at a
+ * time) and review overview (the training path keeps no cache: a continuation
+ * carries the recurrent state and the conv window instead).  Each call takes
+ * ONE new token for each of N sequences: shape->total_tokens must equal
+ * shape->n_seqs, and token n belongs to sequence n (no cu_seqlens).
+ *
+ * gdn_recurrent_step: the gated delta rule on that token,
+ *   S' = e^{g} S (I - b k k^T) + b v k^T,  o = scale * S' q   (per v-head),
+ *   q, k, v, g, beta laid out and strided as for gdn_chunk_fwd with T = N;
+ *   state_in:  float32 [N][Hv][dk][dv] (H = S^T), or NULL for zero states;
+ *   state_out: float32 [N][Hv][dk][dv], may equal state_in (updated in place)
+ *              but must not overlap it otherwise;  o: [N][Hv][dv].
+ * gdn_conv1d_step: conv1d + SiLU + L2 (as gdn_conv1d) of that token, with
+ *   conv_window [N][width-1][Cch] (dtype) holding each sequence's previous
+ *   width-1 inputs, oldest first; it is read and then advanced by one token
+ *   in place.  x, y: [N][Cch]; y must not alias x or conv_window.  N <= 65535.
+ * gdn_conv1d_window: the conv window after a prefill call: for sequence n,
+ *   the last width-1 rows of [window_in[n] ; x rows of sequence n] (window_in
+ *   NULL means zeros, i.e. a fresh sequence), into window_out (must not alias
+ *   window_in).  x: [T][Cch] with cu_seqlens as in gdn_conv1d.  N <= 65535.
+ * A prefill with gdn_conv1d / gdn_chunk_fwd (ht) and gdn_conv1d_window,
+ * followed by these steps, continues every sequence exactly as one longer
+ * prefill would.
+ * -------------------------------------------------------------------------- */
+gdn_status gdn_recurrent_step(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                              int64_t tok_stride_qk, int64_t tok_stride_v, const float* g, const float* beta,
+                              const float* state_in, float* state_out, void* o, gdn_stream stream);
+gdn_status gdn_conv1d_step(const gdn_shape* shape, const void* x, const void* w_conv, int32_t width,
+                           float l2_eps, void* conv_window, void* y, gdn_stream stream);
+gdn_status gdn_conv1d_window(const gdn_shape* shape, const void* x, int32_t width,
+                             const int32_t* cu_seqlens, const void* window_in, void* window_out,
+                             gdn_stream stream);
 
 /* --------------------------------------------------------------------------
  * Diagnostics: per-kernel timing with HIP events.  For benchmarks and

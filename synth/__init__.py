@@ -22,6 +22,8 @@ Draw order for one workload (one ``numpy.random.default_rng(seed)`` stream):
   8. w_norm [dv] = 1 + N(0, 0.02)                     (workloads with the norm)
   9. h0 [N, Hv, dk, dv] ~ N(0, 0.1)                   (workloads with h0)
  10. dy [T, Hv, dv] ~ N(0, 1)                         (workloads with backward)
+ 11. window [N, width-1, Cch] ~ N(0, 1)               (the decode workload: the
+     previous width-1 inputs of each continuing sequence)
 Large arrays are drawn directly in float32; bf16 workloads then round every
 bf16 tensor to bf16 with round-to-nearest-even, and both sides get exactly
 those values.
@@ -57,6 +59,7 @@ class Config:
     width: int = 4            # depthwise causal conv taps
     weak_decay: bool = False  # A_log = -6: g ~ -0.0025 per token (long-range carry)
     varlen_rule: Optional[tuple] = None  # (n_seqs, total, lo, hi) when lengths are drawn
+    decode: bool = False      # one token per sequence continuing from a state and a conv window
 
     @property
     def T(self) -> int:
@@ -90,6 +93,9 @@ CONFIGS: List[Config] = [
     _base("varlen", [], seed=2, h0=True, varlen_rule=(20, 32768, 64, 8192)),
     _base("long", [65536], seed=3),
     _base("train", [8192] * 8, seed=4, bwd=True),
+    # continuation: 256 sequences advance by one token each, from states and
+    # conv windows (the previous width-1 inputs) drawn like h0 and x
+    _base("decode", [1] * 256, seed=5, h0=True, decode=True),
 ]
 
 
@@ -198,11 +204,13 @@ def make_inputs(cfg: Config, *, keep_raw: bool = False) -> Dict[str, np.ndarray]
         out["h0"] = (0.1 * rng.standard_normal((len(lengths), Hv, dk, dv))).astype(np.float32)
     if cfg.bwd:
         out["dy"] = rng.standard_normal((T, Hv, dv), dtype=np.float32)
+    if cfg.decode:
+        out["window"] = rng.standard_normal((len(lengths), W - 1, Cch), dtype=np.float32)
     out["x"] = x
     out["w_conv"] = w_conv
 
     if cfg.dtype == "bf16":
-        for key in ("x", "w_conv", "z", "w_norm", "dy"):
+        for key in ("x", "w_conv", "z", "w_norm", "dy", "window"):
             if key in out:
                 bits = bf16_bits(out[key])
                 out[key + "_bits"] = bits

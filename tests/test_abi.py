@@ -118,6 +118,50 @@ def test_conv_and_norm_reject():
     assert lib.gdn_chunk_index(ctypes.byref(s), None, FAKE, FAKE, None) == INVALID
 
 
+def test_gates_reject():
+    lib = gdn.load()
+    s = shape()
+    G, B2 = ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000)
+    odd = ctypes.c_void_p(0x10002)
+    assert lib.gdn_gates(ctypes.byref(s), FAKE, FAKE, FAKE, None, G, B2, None) == INVALID    # dt_bias missing
+    assert lib.gdn_gates(ctypes.byref(s), None, FAKE, FAKE, FAKE, G, B2, None) == INVALID
+    assert lib.gdn_gates(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, B2, None) == INVALID  # g aliases a
+    assert lib.gdn_gates(ctypes.byref(s), odd, FAKE, FAKE, FAKE, G, B2, None) == INVALID
+    assert lib.gdn_gates(ctypes.byref(shape(h_v=3)), FAKE, FAKE, FAKE, FAKE, G, B2, None) == INVALID
+    nb = lib.gdn_gates_bwd_workspace(ctypes.byref(s))
+    assert nb >= 2 * 4 * 4  # two fp32 partial rows of Hv = 4 heads at least
+    args = [FAKE] * 10
+    assert lib.gdn_gates_bwd(ctypes.byref(s), *args, FAKE, nb - 4, None) == WORKSPACE
+    assert lib.gdn_gates_bwd(ctypes.byref(s), *args, None, nb, None) == WORKSPACE
+    assert lib.gdn_gates_bwd(ctypes.byref(s), *args[:8], None, FAKE, FAKE, nb, None) == INVALID  # dA_log missing
+    assert lib.gdn_gates_bwd(ctypes.byref(s), *args[:4], None, *args[5:], FAKE, nb, None) == INVALID  # dg missing
+
+
+def test_decode_calls_reject():
+    lib = gdn.load()
+    s = shape(n_seqs=4, total_tokens=4)
+    A, B2, C3 = ctypes.c_void_p(0x20000), ctypes.c_void_p(0x30000), ctypes.c_void_p(0x40000)
+
+    def rec(sh=s, sqk=64, sv=128, st_in=FAKE, st_out=A, o=B2):
+        return lib.gdn_recurrent_step(ctypes.byref(sh), FAKE, FAKE, FAKE, sqk, sv, FAKE, FAKE, st_in, st_out, o, None)
+
+    assert rec(sh=shape(n_seqs=4, total_tokens=5)) == INVALID   # one token per sequence
+    assert rec(st_out=None) == INVALID
+    assert rec(o=None) == INVALID
+    assert rec(st_in=FAKE_ODD) == INVALID
+    assert rec(sqk=63) == INVALID
+    assert rec(sh=shape(n_seqs=4, total_tokens=4, d_k=48, d_v=48)) == UNSUPPORTED
+    assert lib.gdn_conv1d_step(ctypes.byref(s), FAKE, FAKE, 5, 1e-6, A, B2, None) == UNSUPPORTED
+    assert lib.gdn_conv1d_step(ctypes.byref(s), FAKE, FAKE, 4, 1e-6, A, FAKE, None) == INVALID  # y aliases x
+    assert lib.gdn_conv1d_step(ctypes.byref(s), FAKE, FAKE, 4, 1e-6, None, B2, None) == INVALID
+    assert lib.gdn_conv1d_step(ctypes.byref(shape(n_seqs=4, total_tokens=3)), FAKE, FAKE, 4, 1e-6, A, B2,
+                               None) == INVALID
+    assert lib.gdn_conv1d_window(ctypes.byref(s), FAKE, 4, FAKE, A, A, None) == INVALID      # in place
+    assert lib.gdn_conv1d_window(ctypes.byref(s), FAKE, 4, None, None, A, None) == INVALID   # no cu_seqlens
+    assert lib.gdn_conv1d_window(ctypes.byref(s), FAKE, 1, FAKE, None, A, None) == UNSUPPORTED
+    assert lib.gdn_conv1d_window(ctypes.byref(s), FAKE, 4, FAKE, FAKE_ODD, C3, None) == INVALID
+
+
 def test_workspace_sizes_grow_with_tokens_and_max_chunks_bound():
     lib = gdn.load()
     prev_f = prev_b = 0

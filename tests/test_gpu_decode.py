@@ -1,0 +1,137 @@
+"""GPU parity of the token-by-token continuation (decode) calls through the C
+ABI: gdn_recurrent_step, gdn_conv1d_step and gdn_conv1d_window against the
+CPU oracle.  The oracle has no decode path of its own: a decode step is the
+recurrence run over a sequence one token longer, so every expected value is
+the oracle's plain forward over the whole (prefill + decoded) sequences."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_conv1d_amd as gdn
+import oracle
+import synth
+from gpu_util import TOL, TOL_F32_OUT, assert_close, f32, host, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(name, **kw):
+    print(f"[case] {name} " + " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+def _unit_rows(a):
+    return a / np.linalg.norm(a, axis=-1, keepdims=True)
+
+
+def _cast(a, dtype):
+    a = np.asarray(a, dtype=np.float32)
+    return synth.round_bf16(a) if dtype == "bf16" else a
+
+
+@pytest.mark.parametrize("dtype,d,Hk,Hv,inplace", [("f32", 16, 2, 2, False), ("f32", 64, 1, 2, True),
+                                                   ("bf16", 32, 2, 4, False), ("bf16", 128, 16, 32, True),
+                                                   ("bf16", 128, 2, 4, False), ("f32", 128, 1, 1, True)])
+def test_recurrent_step_matches_oracle(dtype, d, Hk, Hv, inplace):
+    N = 7
+    _case("recurrent_step", dtype=dtype, d=d, Hk=Hk, Hv=Hv, N=N, inplace=inplace)
+    rng = np.random.default_rng(d + Hv)
+    q = _cast(_unit_rows(rng.standard_normal((N, Hk, d))), dtype)
+    k = _cast(_unit_rows(rng.standard_normal((N, Hk, d))), dtype)
+    v = _cast(rng.standard_normal((N, Hv, d)), dtype)
+    g = (-2.0 * rng.random((N, Hv))).astype(np.float32)
+    beta = rng.random((N, Hv)).astype(np.float32)
+    h0 = (0.3 * rng.standard_normal((N, Hv, d, d))).astype(np.float32)
+    s = gdn.Shape(N, N, Hk, Hv, d, d, 16, gdn.BF16 if dtype == "bf16" else gdn.F32, 0.75)
+    qd, kd, vd = to_dev(q.reshape(N, -1), dtype), to_dev(k.reshape(N, -1), dtype), to_dev(v.reshape(N, -1), dtype)
+    st = f32(h0)
+    o, st2 = gdn.recurrent_step(qd, kd, vd, f32(g), f32(beta), s, state_in=st, state_out=st if inplace else None)
+    ro, rht = oracle.recurrence(q, k, v, g, beta, np.arange(N + 1, dtype=np.int32), h0=h0, scale=0.75)
+    assert_close(host(o), ro, TOL[dtype], "o")
+    assert_close(host(st2), rht, TOL_F32_OUT[dtype], "state")
+    if inplace:
+        assert st2.data_ptr() == st.data_ptr()
+    # zero incoming state (state_in = NULL)
+    o0, s0 = gdn.recurrent_step(qd, kd, vd, f32(g), f32(beta), s)
+    ro0, rht0 = oracle.recurrence(q, k, v, g, beta, np.arange(N + 1, dtype=np.int32), h0=None, scale=0.75)
+    assert_close(host(o0), ro0, TOL[dtype], "o (zero state)")
+    assert_close(host(s0), rht0, TOL_F32_OUT[dtype], "state (zero state)")
+
+
+@pytest.mark.parametrize("dtype,d,Hk,Hv,width,lengths", [("f32", 16, 2, 2, 4, (9, 1, 0, 20)),
+                                                         ("bf16", 32, 1, 2, 3, (70, 2, 33)),
+                                                         ("bf16", 128, 2, 4, 4, (130, 1, 64))])
+def test_decode_continues_prefill(dtype, d, Hk, Hv, width, lengths):
+    """Prefill (gdn_conv1d, gdn_chunk_fwd with h0 -> ht, gdn_conv1d_window), then
+    three decode steps (gdn_conv1d_step, gdn_recurrent_step in place) equal the
+    oracle's forward over the sequences extended by those three tokens."""
+    _case("decode_continues_prefill", dtype=dtype, d=d, width=width, lengths=lengths)
+    steps = 3
+    N = len(lengths)
+    C = 2 * Hk * d + Hv * d
+    chunk = 16 if d < 128 else 64
+    rng = np.random.default_rng(sum(lengths) + width)
+    Ltot = [L + steps for L in lengths]
+    x_full = [_cast(rng.standard_normal((L, C)), dtype) for L in Ltot]
+    g_full = [(-np.exp(rng.uniform(0, 1, Hv)) * np.log1p(np.exp(rng.standard_normal((L, Hv))))).astype(np.float32)
+              for L in Ltot]
+    b_full = [(1 / (1 + np.exp(-rng.standard_normal((L, Hv))))).astype(np.float32) for L in Ltot]
+    w = _cast(0.25 * rng.standard_normal((C, width)), dtype)
+    h0 = (0.1 * rng.standard_normal((N, Hv, d, d))).astype(np.float32)
+    nqk = 2 * Hk * d
+
+    # oracle: the whole extended sequences at once
+    cu_full = synth.cu_from_lengths(Ltot)
+    yo = oracle.conv1d(np.concatenate(x_full), w, cu_full, nqk, d)
+    if dtype == "bf16":
+        yo = synth.round_bf16(yo.astype(np.float32)).astype(np.float64)
+    T = int(cu_full[-1])
+    q, k, v = yo[:, :Hk * d].reshape(T, Hk, d), yo[:, Hk * d:nqk].reshape(T, Hk, d), yo[:, nqk:].reshape(T, Hv, d)
+    ro, rht = oracle.recurrence(q, k, v, np.concatenate(g_full), np.concatenate(b_full), cu_full, h0=h0)
+
+    # GPU prefill
+    et = gdn.BF16 if dtype == "bf16" else gdn.F32
+    Tp = sum(lengths)
+    sp = gdn.Shape(N, Tp, Hk, Hv, d, d, chunk, et, 1.0)
+    cu_p = torch.from_numpy(synth.cu_from_lengths(lengths)).cuda()
+    xp = to_dev(np.concatenate([x[:L] for x, L in zip(x_full, lengths)]).reshape(Tp, C), dtype)
+    wd = to_dev(w, dtype)
+    yp = gdn.conv1d(xp, wd, cu_p, sp)
+    gp = f32(np.concatenate([a[:L] for a, L in zip(g_full, lengths)]).reshape(Tp, Hv))
+    bp = f32(np.concatenate([a[:L] for a, L in zip(b_full, lengths)]).reshape(Tp, Hv))
+    o_p, state = gdn.chunk_fwd(yp[:, :Hk * d], yp[:, Hk * d:nqk], yp[:, nqk:], gp, bp, cu_p, sp, h0=f32(h0))
+    window = gdn.conv1d_window(xp, cu_p, sp, width)
+    # the prefill part of the outputs
+    pre_idx = np.concatenate([np.arange(cu_full[n], cu_full[n] + lengths[n]) for n in range(N)])
+    assert_close(host(o_p), ro[pre_idx], TOL[dtype], "o (prefill)")
+
+    sd = gdn.Shape(N, N, Hk, Hv, d, d, chunk, et, 1.0)
+    for s in range(steps):
+        idx = np.array([cu_full[n] + lengths[n] + s for n in range(N)])
+        xs = to_dev(np.stack([x_full[n][lengths[n] + s] for n in range(N)]), dtype)
+        ys = gdn.conv1d_step(xs, wd, window, sd)
+        assert_close(host(ys), yo[idx], TOL[dtype], f"y_conv (step {s})")
+        gs = f32(np.stack([g_full[n][lengths[n] + s] for n in range(N)]))
+        bs = f32(np.stack([b_full[n][lengths[n] + s] for n in range(N)]))
+        o_s, state = gdn.recurrent_step(ys[:, :Hk * d], ys[:, Hk * d:nqk], ys[:, nqk:], gs, bs, sd,
+                                        state_in=state, state_out=state)
+        assert_close(host(o_s), ro[idx], TOL[dtype], f"o (step {s})")
+    assert_close(host(state), rht, TOL_F32_OUT[dtype], "final state")
+
+
+def test_conv1d_window_with_incoming_window():
+    """gdn_conv1d_window with a window_in: sequences shorter than width-1 keep
+    the older inputs, shifted (bit-exact: a pure gather)."""
+    _case("conv1d_window_in")
+    Hk, Hv, d, width = 1, 1, 16, 4
+    C = 2 * Hk * d + Hv * d
+    lengths = (0, 1, 2, 5)
+    N = len(lengths)
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((sum(lengths), C)).astype(np.float32)
+    win_in = rng.standard_normal((N, width - 1, C)).astype(np.float32)
+    s = gdn.Shape(N, sum(lengths), Hk, Hv, d, d, 16, gdn.F32, 1.0)
+    cu = synth.cu_from_lengths(lengths)
+    out = host(gdn.conv1d_window(f32(x), torch.from_numpy(cu).cuda(), s, width, window_in=f32(win_in)))
+    for n, L in enumerate(lengths):
+        hist = np.concatenate([win_in[n], x[cu[n]:cu[n + 1]]])
+        np.testing.assert_array_equal(out[n], hist[-(width - 1):])

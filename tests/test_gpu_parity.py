@@ -83,6 +83,43 @@ def test_norm_gate_fwd_bwd(dtype, d):
     assert_close(host(dw), rdw, TOL[dtype], "dw_norm")
 
 
+# ----------------------------------------------------------------------------- gates
+@pytest.mark.parametrize("T,Hk,Hv,workload", [(0, 1, 4, None), (1, 1, 3, None), (333, 2, 6, None), (700, 1, 1, None),
+                                               (65536, 16, 32, "train")])
+def test_gates_fwd_bwd(T, Hk, Hv, workload):
+    """gdn_gates / gdn_gates_bwd against the oracle's fp64 gates on the same
+    float32 inputs; the last case is the training workload's own gate draw."""
+    _print_case("gates", T=T, Hv=Hv, workload=workload)
+    if workload:
+        cfg = synth.config(workload)
+        raw = synth.make_inputs(cfg, keep_raw=True)
+        a, b, A_log, dt = raw["a"], raw["b"], raw["A_log"], raw["dt_bias"]
+    else:
+        rng = np.random.default_rng(T + Hv)
+        a, b = 3 * rng.standard_normal((T, Hv)), 3 * rng.standard_normal((T, Hv))
+        A_log, dt = rng.uniform(-1, 2, Hv), rng.standard_normal(Hv)
+    a, b, A_log, dt = (np.asarray(x, dtype=np.float32) for x in (a, b, A_log, dt))
+    rng = np.random.default_rng(7)
+    dg = rng.standard_normal((T, Hv)).astype(np.float32)
+    dbeta = rng.standard_normal((T, Hv)).astype(np.float32)
+    s = gdn.Shape(1, T, Hk, Hv, 16, 16, 16, gdn.F32, 1.0)
+    g, beta = gdn.gates(f32(a), f32(b), f32(A_log), f32(dt), s)
+    r = gdn.gates_bwd(f32(a), f32(b), f32(A_log), f32(dt), f32(dg), f32(dbeta), s)
+    rg, rbeta = oracle.gates(a, b, A_log, dt)
+    ref = oracle.gates_bwd(a, b, A_log, dt, dg, dbeta)
+    if T > 0:
+        # elementwise results: float32 arithmetic of well-conditioned functions
+        for got, want, name in ((g, rg, "g"), (beta, rbeta, "beta"), (r["da"], ref["da"], "da"),
+                                (r["db"], ref["db"], "db")):
+            got = host(got)
+            assert np.all(np.abs(got - want) <= 1e-5 * np.abs(want) + 1e-30), name
+            assert_close(got, want, 1e-4, name)
+        assert_close(host(r["dA_log"]), ref["dA_log"], 1e-4, "dA_log")
+        assert_close(host(r["ddt_bias"]), ref["ddt_bias"], 1e-4, "ddt_bias")
+    else:
+        assert not host(r["dA_log"]).any() and not host(r["ddt_bias"]).any()
+
+
 # ----------------------------------------------------------------------------- A3-A5, A7 chunk
 CHUNK_CASES = [
     ("f32", 16, 16, 2, 2, (64,)),
