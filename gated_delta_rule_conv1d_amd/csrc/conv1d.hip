@@ -71,16 +71,24 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(const E* __restrict__ x, 
       for (int c = 0; c < V; ++c) ring[i + 1][c] = 0.f;
   }
 
-  // the next token's x is loaded one iteration ahead
-  uint4 nx = make_uint4(0, 0, 0, 0);
-  if (active) nx = *reinterpret_cast<const uint4*>(x + (size_t)t0 * Cch + ch);
+  // the next W tokens' x are loaded while the current W compute (W loads in
+  // flight per wave)
+  uint4 cx[W];
+#pragma unroll
+  for (int p = 0; p < W; ++p)
+    cx[p] = (active && t0 + p < t1) ? *reinterpret_cast<const uint4*>(x + (size_t)(t0 + p) * Cch + ch)
+                                    : make_uint4(0, 0, 0, 0);
   for (int tb = t0; tb < t1; tb += W) {
+    uint4 nx[W];
+#pragma unroll
+    for (int p = 0; p < W; ++p)
+      nx[p] = (active && tb + W + p < t1) ? *reinterpret_cast<const uint4*>(x + (size_t)(tb + W + p) * Cch + ch)
+                                          : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int p = 0; p < W; ++p) {
       const int t = tb + p;
       if (t >= t1) break;
-      const uint4 rx = nx;
-      if (active && t + 1 < t1) nx = *reinterpret_cast<const uint4*>(x + (size_t)(t + 1) * Cch + ch);
+      const uint4 rx = cx[p];
       if (t >= seq_end) {  // entering a new sequence (skip empty ones)
         while (cu[n + 1] <= t) ++n;
         seq_start = cu[n];
@@ -113,6 +121,8 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(const E* __restrict__ x, 
       }
       if (active) Vec<E>::store(y + (size_t)t * Cch + ch, a);
     }
+#pragma unroll
+    for (int p = 0; p < W; ++p) cx[p] = nx[p];
   }
 }
 
@@ -122,7 +132,7 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(const E* __restrict__ x, 
 // computes dc for its TB tokens plus W-1 look-ahead tokens.  dw partial sums
 // per (workgroup, channel, tap) go to workspace in a fixed order.
 template <typename E, int D, int W>
-__global__ __launch_bounds__(256) void conv_bwd_kernel(const E* __restrict__ dy, const E* __restrict__ x,
+__global__ __launch_bounds__(256, 2) void conv_bwd_kernel(const E* __restrict__ dy, const E* __restrict__ x,
                                                        const E* __restrict__ w, const int32_t* __restrict__ cu,
                                                        int N, int T, int Cch, int n_qk, float eps,
                                                        E* __restrict__ dx, float* __restrict__ dw_part) {
@@ -154,121 +164,120 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(const E* __restrict__ dy,
 
     int n = find_seq(cu, N, t0);
     int seq_start = cu[n], seq_end = cu[n + 1];
-    float hist[W - 1][V];
-#pragma unroll
-    for (int i = 0; i < W - 1; ++i) {
-      const int s = t0 - (W - 1) + i;
-      if (active && s >= seq_start) Vec<E>::load(x + (size_t)s * Cch + ch, hist[i]);
-      else
-#pragma unroll
-        for (int c = 0; c < V; ++c) hist[i][c] = 0.f;
-    }
-    // window of the last W dc values and their sequence starts: slot W-1 newest
-    float dcw[W][V];
+    // xr[k] holds x of the token t with (t - t0) % W == k, dcr[k] / dcs[k] its
+    // dc and the start of its sequence; the token loop is unrolled by W so
+    // every slot index is a constant (no register shifting)
+    float xr[W][V], dcr[W][V];
     int dcs[W];
 #pragma unroll
     for (int i = 0; i < W; ++i) {
       dcs[i] = 0x7fffffff;
 #pragma unroll
-      for (int c = 0; c < V; ++c) dcw[i][c] = 0.f;
+      for (int c = 0; c < V; ++c) xr[i][c] = dcr[i][c] = 0.f;
     }
-    // the next token's x and dy are loaded one iteration ahead
-    uint4 nx = make_uint4(0, 0, 0, 0), ng = make_uint4(0, 0, 0, 0);
-    if (active) {
-      nx = *reinterpret_cast<const uint4*>(x + (size_t)t0 * Cch + ch);
-      ng = *reinterpret_cast<const uint4*>(dy + (size_t)t0 * Cch + ch);
+#pragma unroll
+    for (int i = 0; i < W - 1; ++i) {
+      const int s = t0 - (W - 1) + i;
+      if (active && s >= seq_start) Vec<E>::load(x + (size_t)s * Cch + ch, xr[i + 1]);
     }
-    for (int t = t0; t < tend; ++t) {
-      const uint4 rx = nx, rg = ng;
-      if (active && t + 1 < tend) {
-        nx = *reinterpret_cast<const uint4*>(x + (size_t)(t + 1) * Cch + ch);
-        ng = *reinterpret_cast<const uint4*>(dy + (size_t)(t + 1) * Cch + ch);
+    // the next W tokens' x and dy are loaded while the current W compute
+    uint4 cx[W], cg[W];
+#pragma unroll
+    for (int p = 0; p < W; ++p) {
+      const bool ok = active && t0 + p < tend;
+      cx[p] = ok ? *reinterpret_cast<const uint4*>(x + (size_t)(t0 + p) * Cch + ch) : make_uint4(0, 0, 0, 0);
+      cg[p] = ok ? *reinterpret_cast<const uint4*>(dy + (size_t)(t0 + p) * Cch + ch) : make_uint4(0, 0, 0, 0);
+    }
+    for (int tb = t0; tb < tend; tb += W) {
+      uint4 nx[W], ng[W];
+#pragma unroll
+      for (int p = 0; p < W; ++p) {
+        const int tn = tb + W + p;
+        const bool ok = active && tn < tend;
+        nx[p] = ok ? *reinterpret_cast<const uint4*>(x + (size_t)tn * Cch + ch) : make_uint4(0, 0, 0, 0);
+        ng[p] = ok ? *reinterpret_cast<const uint4*>(dy + (size_t)tn * Cch + ch) : make_uint4(0, 0, 0, 0);
       }
-      if (t >= seq_end) {
-        while (cu[n + 1] <= t) ++n;
-        seq_start = cu[n];
-        seq_end = cu[n + 1];
 #pragma unroll
-        for (int i = 0; i < W - 1; ++i)
+      for (int p = 0; p < W; ++p) {
+        const int t = tb + p;
+        if (t >= tend) break;
+        const uint4 rx = cx[p], rg = cg[p];
+        if (t >= seq_end) {  // entering a new sequence (skip empty ones): no history
+          while (cu[n + 1] <= t) ++n;
+          seq_start = cu[n];
+          seq_end = cu[n + 1];
 #pragma unroll
-          for (int c = 0; c < V; ++c) hist[i][c] = 0.f;
-      }
-      float cur[V], g[V];
-      {
-        const E* ex = reinterpret_cast<const E*>(&rx);
-        const E* eg = reinterpret_cast<const E*>(&rg);
+          for (int i = 0; i < W; ++i)
 #pragma unroll
-        for (int c = 0; c < V; ++c) {
-          cur[c] = to_f<E>(ex[c]);
-          g[c] = to_f<E>(eg[c]);
+            for (int c = 0; c < V; ++c) xr[i][c] = 0.f;
         }
-      }
-      float cc[V], sg[V], a[V];
-      float ss = 0.f, dot = 0.f;
+        float g[V];
+        {
+          const E* ex = reinterpret_cast<const E*>(&rx);
+          const E* eg = reinterpret_cast<const E*>(&rg);
 #pragma unroll
-      for (int c = 0; c < V; ++c) {
-        float acc = wr[c][W - 1] * cur[c];
-#pragma unroll
-        for (int i = 0; i < W - 1; ++i) acc += wr[c][i] * hist[i][c];
-        cc[c] = acc;
-        sg[c] = sigmoidf_(acc);
-        a[c] = acc * sg[c];
-        ss += a[c] * a[c];
-        dot += a[c] * g[c];
-      }
-      ss = group_sum<LPH>(ss);
-      dot = group_sum<LPH>(dot);
-      float dcv[V];
-      const float inv = rsqrtf(ss + eps);
-      const float inv3 = inv * inv * inv;
-#pragma unroll
-      for (int c = 0; c < V; ++c) {
-        const float da = is_qk ? (g[c] * inv - a[c] * dot * inv3) : g[c];
-        dcv[c] = da * sg[c] * (1.f + cc[c] * (1.f - sg[c]));
-      }
-      if (t < t1) {  // own token: weight gradient
-#pragma unroll
-        for (int c = 0; c < V; ++c) {
-#pragma unroll
-          for (int i = 0; i < W - 1; ++i) dwacc[c][i] += dcv[c] * hist[i][c];
-          dwacc[c][W - 1] += dcv[c] * cur[c];
-        }
-      }
-      // shift windows
-#pragma unroll
-      for (int i = 0; i < W - 2; ++i)
-#pragma unroll
-        for (int c = 0; c < V; ++c) hist[i][c] = hist[i + 1][c];
-#pragma unroll
-      for (int c = 0; c < V; ++c) hist[W - 2][c] = cur[c];
-#pragma unroll
-      for (int i = 0; i < W - 1; ++i) {
-        dcs[i] = dcs[i + 1];
-#pragma unroll
-        for (int c = 0; c < V; ++c) dcw[i][c] = dcw[i + 1][c];
-      }
-      dcs[W - 1] = seq_start;
-#pragma unroll
-      for (int c = 0; c < V; ++c) dcw[W - 1][c] = dcv[c];
-      // dx for token s = t - (W-1): slot m holds dc[s + m], which the tap
-      // W-1-m multiplies; only terms inside s's sequence count.
-      const int s = t - (W - 1);
-      if (s >= t0 && active) {
-        float o[V];
-#pragma unroll
-        for (int c = 0; c < V; ++c) o[c] = 0.f;
-#pragma unroll
-        for (int m = 0; m < W; ++m) {
-          if (dcs[m] <= s) {
-#pragma unroll
-            for (int c = 0; c < V; ++c) o[c] += wr[c][W - 1 - m] * dcw[m][c];
+          for (int c = 0; c < V; ++c) {
+            xr[p][c] = to_f<E>(ex[c]);
+            g[c] = to_f<E>(eg[c]);
           }
         }
-        Vec<E>::store(dx + (size_t)s * Cch + ch, o);
+        float cc[V], sg[V], a[V];
+        float ss = 0.f, dot = 0.f;
+#pragma unroll
+        for (int c = 0; c < V; ++c) {
+          float acc = wr[c][W - 1] * xr[p][c];
+#pragma unroll
+          for (int i = 0; i < W - 1; ++i) acc += wr[c][i] * xr[(p + 1 + i) % W][c];  // token t - (W-1) + i
+          cc[c] = acc;
+          sg[c] = sigmoidf_(acc);
+          a[c] = acc * sg[c];
+          ss += a[c] * a[c];
+          dot += a[c] * g[c];
+        }
+        ss = group_sum<LPH>(ss);
+        dot = group_sum<LPH>(dot);
+        const float inv = rsqrtf(ss + eps);
+        const float inv3 = inv * inv * inv;
+#pragma unroll
+        for (int c = 0; c < V; ++c) {
+          const float da = is_qk ? (g[c] * inv - a[c] * dot * inv3) : g[c];
+          dcr[p][c] = da * sg[c] * (1.f + cc[c] * (1.f - sg[c]));
+        }
+        dcs[p] = seq_start;
+        if (t < t1) {  // own token: weight gradient
+#pragma unroll
+          for (int c = 0; c < V; ++c) {
+#pragma unroll
+            for (int i = 0; i < W - 1; ++i) dwacc[c][i] += dcr[p][c] * xr[(p + 1 + i) % W][c];
+            dwacc[c][W - 1] += dcr[p][c] * xr[p][c];
+          }
+        }
+        // dx for token s = t - (W-1): dc[s + m] sits in slot (p + 1 + m) % W and
+        // tap W-1-m multiplies it; only terms inside s's sequence count
+        const int s = t - (W - 1);
+        if (s >= t0 && active) {
+          float o[V];
+#pragma unroll
+          for (int c = 0; c < V; ++c) o[c] = 0.f;
+#pragma unroll
+          for (int m = 0; m < W; ++m) {
+            const int k = (p + 1 + m) % W;
+            if (dcs[k] <= s) {
+#pragma unroll
+              for (int c = 0; c < V; ++c) o[c] += wr[c][W - 1 - m] * dcr[k][c];
+            }
+          }
+          Vec<E>::store(dx + (size_t)s * Cch + ch, o);
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < W; ++p) {
+        cx[p] = nx[p];
+        cg[p] = ng[p];
       }
     }
-    // tokens whose W-1 successors run past the end of the row: after the last
-    // iteration slot k holds dc[tend - W + k]
+    // tokens whose W-1 successors run past the end of the row: dc of token u
+    // (u < tend) is in slot (u - t0) % W
     if (active) {
       for (int s = max(t0, tend - (W - 1)); s < t1; ++s) {
         float o[V];
@@ -276,10 +285,10 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(const E* __restrict__ dy,
         for (int c = 0; c < V; ++c) o[c] = 0.f;
 #pragma unroll
         for (int m = 0; m < W; ++m) {
-          const int slot = s + m - (tend - W);
-          if (s + m < tend && dcs[slot] <= s) {
+          const int k = (s + m - t0) % W;
+          if (s + m < tend && dcs[k] <= s) {
 #pragma unroll
-            for (int c = 0; c < V; ++c) o[c] += wr[c][W - 1 - m] * dcw[slot][c];
+            for (int c = 0; c < V; ++c) o[c] += wr[c][W - 1 - m] * dcr[k][c];
           }
         }
         Vec<E>::store(dx + (size_t)s * Cch + ch, o);

@@ -356,7 +356,9 @@ __device__ __forceinline__ float wave_suffix_sum(float v) {
   return v + (row == 0 ? s0 : row == 1 ? s1 : row == 2 ? s2 : 0.f);
 }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + __expf(-x)); }
+// sigmoid with the hardware reciprocal (v_rcp_f32, 1 ulp) instead of an IEEE
+// division sequence; 1 + e^-x = inf gives 0, as it should.
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
 
 // ---------------------------------------------------------------------------
