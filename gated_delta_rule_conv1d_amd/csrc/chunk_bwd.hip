@@ -313,6 +313,8 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
   using DRegs = TileRegs<float, D, D, NTH>;
   DRegs rD;
   rD.load(dHn, D, D);
+  TileRegs<E, C, D, NTH> rK;  // K rows for (c), also in flight during (b)
+  rK.load((const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D, a.sqk, len);
 
   // (b) dWk = -dW Hc^T: hi -> Os, lo -> Vs; transposed fp32 copy to workspace
   for_blocks<NT, ND, RT, CD, NW>([&](int r0, int c0) {
@@ -353,12 +355,10 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
     sm.red[tid] = hs;
   }
   __syncthreads();  // Hc is no longer read
-  {
-    TileRegs<E, C, D, NTH> rK;
-    rK.load((const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D, a.sqk, len);
-    rK.store(Kst, S::LDQ);
-  }
+  rK.store(Kst, S::LDQ);
   __syncthreads();
+  TileRegs<float, C, D, NTH> rW2;  // W for (d): in flight during (c)
+  rW2.load(a.W + slot * C * D, D, C);
 
   // (c) dT = beta_s dT1 + beta_s Gam_s dWk K^T
 #pragma unroll
@@ -384,12 +384,9 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
   }
   __syncthreads();  // dWk and K are no longer read
 
-  {  // stage dHn, W (dO is still staged)
-    TileRegs<float, C, D, NTH> rW;
-    rW.load(a.W + slot * C * D, D, C);
-    rD.template store_split<E>(&sm.Hh[0][0], Hlo, S::LDQ);
-    rW.template store_split<E>(&sm.Xh[0][0], Xlo, S::LDQ);
-  }
+  // stage dHn, W (dO is still staged)
+  rD.template store_split<E>(&sm.Hh[0][0], Hlo, S::LDQ);
+  rW2.template store_split<E>(&sm.Xh[0][0], Xlo, S::LDQ);
   __syncthreads();
   if (tid == 0) {
     float s = 0.f;
@@ -552,8 +549,11 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
     const E* vg = (const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)h * D;
     TileRegs<E, C, D, NTH> pV;  // v rows and T (from the preparation pass)
     TileRegs<float, C, C, NTH> pTm;
+    TileRegs<float, D, C, NTH> rXu, rXw;  // dW^T, and dWk^T (in flight during the dXu products)
     pV.load(vg, a.sv, len);
     pTm.load(a.Tw + slot * C * C, C, C);
+    rXu.load(a.dWt + slot * D * C, C, D);
+    rXw.load(a.dWkt + slot * D * C, C, D);
     for (int e = tid; e < C; e += NTH) {
       const float gm = a.gam[slot * C + e];
       sm.gam[e] = gm;
@@ -569,12 +569,8 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
     E* const XL = LO ? &sm.r.x.l[0][0] : nullptr;
     pTm.template store_t<E>(&sm.TtH[0][0], S::LDCE, TtL, S::LDCE);  // T^T, transposed here
     // dXu = T^T dW -> dv and <dXu, v>
-    {
-      TileRegs<float, D, C, NTH> rX;
-      rX.load(a.dWt + slot * D * C, C, D);
-      pV.store(&sm.av.Vs[0][0], S::LDV);
-      rX.template store_split<E>(&sm.r.x.h[0][0], XL, S::LDCE);
-    }
+    pV.store(&sm.av.Vs[0][0], S::LDV);
+    rXu.template store_split<E>(&sm.r.x.h[0][0], XL, S::LDCE);
     __syncthreads();
     // tile (dt, rt) of (T^T X)^T = X^T T (X = dW^T or dWk^T staged in r.x)
     auto txt = [&](int dt) {
@@ -606,12 +602,13 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
     }
     __syncthreads();
     // dXw = T^T dWk -> dK and <dXw, k>
-    {
-      TileRegs<float, D, C, NTH> rX;
-      rX.load(a.dWkt + slot * D * C, C, D);
-      rX.template store_split<E>(&sm.r.x.h[0][0], XL, S::LDCE);
-    }
+    rXw.template store_split<E>(&sm.r.x.h[0][0], XL, S::LDCE);
     __syncthreads();
+    // dT, P and dP' of the C x C passes: in flight during the dXw products
+    TileRegs<float, C, C, NTH> rT, pP, pdP;
+    rT.load(a.dT + slot * C * C, C, C);
+    pP.load(a.P + slot * C * C, C, C);
+    pdP.load(a.dP + slot * C * C, C, C);
     if (act) {
       const float bg = sm.beta[rrow] * sm.Gm[rrow];
       float pw = 0.f;
@@ -629,14 +626,7 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
     }
     __syncthreads();
     // M1 = dT T^T (fp32 MFMA), stored transposed and split; dA = strict_lower(-T^T M1)
-    TileRegs<float, C, C, NTH> pP, pdP;  // in flight during dA
-    {
-      TileRegs<float, C, C, NTH> rT;
-      rT.load(a.dT + slot * C * C, C, C);
-      pP.load(a.P + slot * C * C, C, C);
-      pdP.load(a.dP + slot * C * C, C, C);
-      rT.store(&sm.r.m.dT[0][0], S::LDCF);
-    }
+    rT.store(&sm.r.m.dT[0][0], S::LDCF);
     __syncthreads();
     for (int t = w; t < NT * NT; t += NW) {
       const int rt = t / NT, ct = t % NT;
@@ -713,6 +703,12 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();
+    // this lane's dKh tiles: in flight during the transpose below
+    f32x4 khr[DT];
+    if (act) {
+#pragma unroll
+      for (int i = 0; i < DT; ++i) khr[i] = load_acc(a.dKh + slot * C * D, NT, dt0 + i, rt);
+    }
     // [dS^T | A~ + A~^T] as rows (P and dP' are consumed)
     for (int e = tid; e < C * C; e += NTH) {
       const int sr = e / C, r = e % C;
@@ -725,13 +721,12 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
     // dQ += dQs + dS K;   dK += dKh + [dS^T | A~ + A~^T] [Q ; K]   (transposed)
     if (act) {
       const float* dQsg = a.dQs + slot * C * D;
-      const float* dKhg = a.dKh + slot * C * D;
       float pq = 0.f, pk = 0.f;
 #pragma unroll
       for (int i = 0; i < DT; ++i) {
         const int d = (dt0 + i) * 16 + dl;
         const f32x4 qs = load_acc(dQsg, NT, dt0 + i, rt);
-        const f32x4 kh = load_acc(dKhg, NT, dt0 + i, rt);
+        const f32x4 kh = khr[i];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           dQ[i][0][e] += qs[e];
