@@ -519,8 +519,8 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
   const E* qg = (const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D;
   const E* kg = (const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D;
 
-  rows2s_t<E, C, D, NTH>(&sm.QKt[0][0], S::LD2C, qg, a.sqk, len, nullptr, 1.f);
-  rows2s_t<E, C, D, NTH>(&sm.QKt[0][C], S::LD2C, kg, a.sqk, len, nullptr, 1.f);
+  rows2s_t<E, C, D, NTH>(&sm.QKt[0][0], S::LD2C, qg, a.sqk, len);
+  rows2s_t<E, C, D, NTH>(&sm.QKt[0][C], S::LD2C, kg, a.sqk, len);
   __syncthreads();
   // K K^T (exact bf16 products, fp32 sums), shared by the k-head's v-heads
   for (int t = w; t < NT * NT; t += NW) {

@@ -174,24 +174,10 @@ __device__ __forceinline__ void g2s(E* s, int lds, const E* g) {
   }
 }
 
-// rows [0, len) of a token-major input (row stride ld elements) into LDS; zero rows past len
-template <typename E, int R, int Ccols, int NTH = kChunkThreads>
-__device__ __forceinline__ void rows2s(E* s, int lds, const E* g, int64_t ld, int len) {
-  constexpr int V = Vec<E>::N;
-  constexpr int PER_ROW = Ccols / V;
-  for (int e = threadIdx.x; e < R * PER_ROW; e += NTH) {
-    const int r = e / PER_ROW, c = (e % PER_ROW) * V;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (r < len) val = *reinterpret_cast<const uint4*>(g + (int64_t)r * ld + c);
-    *reinterpret_cast<uint4*>(s + r * lds + c) = val;
-  }
-}
-
 // rows [0, len) of a token-major input written transposed into LDS:
-// s[c * lds + r] = g[r * ld + c]; zero past len.  Optional per-row scale.
+// s[c * lds + r] = g[r * ld + c]; zero past len.
 template <typename E, int R, int Ccols, int NTH = kChunkThreads>
-__device__ __forceinline__ void rows2s_t(E* s, int lds, const E* g, int64_t ld, int len, const float* rscale,
-                                         float mult) {
+__device__ __forceinline__ void rows2s_t(E* s, int lds, const E* g, int64_t ld, int len) {
   constexpr int V = Vec<E>::N;
   constexpr int PER_ROW = Ccols / V;
   for (int e = threadIdx.x; e < R * PER_ROW; e += NTH) {
@@ -203,9 +189,8 @@ __device__ __forceinline__ void rows2s_t(E* s, int lds, const E* g, int64_t ld, 
 #pragma unroll
       for (int i = 0; i < V; ++i) val[i] = 0.f;
     }
-    const float f = (rscale ? rscale[r] : 1.f) * mult;
 #pragma unroll
-    for (int i = 0; i < V; ++i) s[(c + i) * lds + r] = from_f<E>(val[i] * f);
+    for (int i = 0; i < V; ++i) s[(c + i) * lds + r] = from_f<E>(val[i]);
   }
 }
 

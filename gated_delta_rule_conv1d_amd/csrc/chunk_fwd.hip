@@ -100,9 +100,14 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
   };
   load_head(j * a.G);
 
-  rows2s<E, C, D, NTH>(&sm.Qs[0][0], S::LDQ, qg, a.sqk, len);
-  rows2s<E, C, D, NTH>(&sm.Ks[0][0], S::LDQ, kg, a.sqk, len);
-  rows2s_t<E, C, D, NTH>(&sm.Kt[0][0], S::LDCE, kg, a.sqk, len, nullptr, 1.f);
+  {  // q and k rows: every load issued before the first LDS write; K^T from the same registers
+    TileRegs<E, C, D, NTH> rQ, rK;
+    rQ.load(qg, a.sqk, len);
+    rK.load(kg, a.sqk, len);
+    rQ.store(&sm.Qs[0][0], S::LDQ);
+    rK.store(&sm.Ks[0][0], S::LDQ);
+    rK.template store_t<E>(&sm.Kt[0][0], S::LDCE);
+  }
   __syncthreads();
   for (int t = w; t < NT * NT; t += NW) {
     const int rt = t / NT, ct = t % NT;
