@@ -16,7 +16,7 @@ from ._binding import (  # noqa: F401
     chunk_fwd, chunk_fwd_workspace, chunk_bwd, chunk_bwd_workspace,
     norm_gate, norm_gate_bwd, norm_gate_bwd_workspace,
     gates, gates_bwd, gates_bwd_workspace,
-    recurrent_step, conv1d_step, conv1d_window,
+    recurrent_step, conv1d_step, conv1d_window, conv1d_prefill,
     profile_enable, profile_report,
 )
 from .layer import GatedDeltaNetLayer, layer_forward, layer_backward  # noqa: F401

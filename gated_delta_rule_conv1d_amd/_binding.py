@@ -18,7 +18,8 @@ SYMBOLS = ("gdn_status_string", "gdn_max_chunks", "gdn_chunk_index", "gdn_conv1d
            "gdn_conv1d_bwd", "gdn_chunk_fwd_workspace", "gdn_chunk_fwd", "gdn_chunk_bwd_workspace",
            "gdn_chunk_bwd", "gdn_chunk_fwd_save", "gdn_chunk_bwd_saved", "gdn_norm_gate",
            "gdn_norm_gate_bwd_workspace", "gdn_norm_gate_bwd", "gdn_gates", "gdn_gates_bwd_workspace",
-           "gdn_gates_bwd", "gdn_recurrent_step", "gdn_conv1d_step", "gdn_conv1d_window", "gdn_profile_enable",
+           "gdn_gates_bwd", "gdn_recurrent_step", "gdn_conv1d_step", "gdn_conv1d_window", "gdn_conv1d_prefill",
+           "gdn_profile_enable",
            "gdn_profile_report")
 
 
@@ -99,6 +100,7 @@ def load() -> ctypes.CDLL:
             "gdn_recurrent_step": (I32, [S, P, P, P, I64, I64, P, P, P, P, P, P]),
             "gdn_conv1d_step": (I32, [S, P, P, I32, F, P, P, P]),
             "gdn_conv1d_window": (I32, [S, P, I32, P, P, P, P]),
+            "gdn_conv1d_prefill": (I32, [S, P, P, I32, F, P, P, P, P, P]),
             "gdn_profile_enable": (None, [ctypes.c_int]),
             "gdn_profile_report": (SZ, [ctypes.c_char_p, SZ]),
         }
@@ -405,6 +407,25 @@ def conv1d_window(x, cu_seqlens, shape: Shape, width: int, window_in=None):
                                                          _ptr(cu_seqlens), _ptr(window_in), _ptr(out),
                                                          _stream(x.device)))
     return out
+
+
+def conv1d_prefill(x, w_conv, cu_seqlens, shape: Shape, window_in=None, want_window=True, l2_eps: float = 1e-6):
+    """gdn_conv1d continuing from carried windows (None: fresh sequences).
+    Returns (y [T, Cch], window_out [N, width-1, Cch] or None)."""
+    dt = shape.torch_dtype
+    C = shape.channels
+    W = int(w_conv.shape[1])
+    _need(x, "x", dt, (shape.total_tokens, C))
+    _need(w_conv, "w_conv", dt, (C, W))
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (shape.n_seqs + 1,))
+    if window_in is not None:
+        _need(window_in, "window_in", dt, (shape.n_seqs, W - 1, C))
+    y = torch.empty_like(x)
+    win = torch.empty((shape.n_seqs, W - 1, C), dtype=dt, device=x.device) if want_window else None
+    _check("gdn_conv1d_prefill", load().gdn_conv1d_prefill(ctypes.byref(shape.c()), _ptr(x), _ptr(w_conv), W,
+                                                           float(l2_eps), _ptr(cu_seqlens), _ptr(window_in), _ptr(y),
+                                                           _ptr(win), _stream(x.device)))
+    return y, win
 
 
 # ----------------------------------------------------------------------------- diagnostics

@@ -36,8 +36,9 @@ __device__ __forceinline__ int find_seq(const int32_t* cu, int N, int t) {
 
 template <typename E, int D, int W>
 __global__ __launch_bounds__(256) void conv_fwd_kernel(const E* __restrict__ x, const E* __restrict__ w,
-                                                       const int32_t* __restrict__ cu, int N, int T,
-                                                       int Cch, int n_qk, float eps, E* __restrict__ y) {
+                                                       const int32_t* __restrict__ cu, const E* __restrict__ win,
+                                                       int N, int T, int Cch, int n_qk, float eps,
+                                                       E* __restrict__ y) {
   constexpr int V = Vec<E>::N;      // channels per lane
   constexpr int LPH = D / V;        // lanes per L2 group
   const int lane = lane_id();
@@ -66,6 +67,8 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(const E* __restrict__ x, 
   for (int i = 0; i < W - 1; ++i) {
     const int s = t0 - (W - 1) + i;
     if (active && s >= seq_start) Vec<E>::load(x + (size_t)s * Cch + ch, ring[i + 1]);
+    else if (active && win)  // before the sequence: its carried window, slot s - seq_start + W - 1
+      Vec<E>::load(win + ((size_t)n * (W - 1) + (s - seq_start + W - 1)) * Cch + ch, ring[i + 1]);
     else
 #pragma unroll
       for (int c = 0; c < V; ++c) ring[i + 1][c] = 0.f;
@@ -89,14 +92,19 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(const E* __restrict__ x, 
       const int t = tb + p;
       if (t >= t1) break;
       const uint4 rx = cx[p];
-      if (t >= seq_end) {  // entering a new sequence (skip empty ones)
+      if (t >= seq_end) {  // entering a new sequence (skip empty ones): t is its first token
         while (cu[n + 1] <= t) ++n;
         seq_start = cu[n];
         seq_end = cu[n + 1];
+        // history: the sequence's carried window (token t - (W-1) + i in window
+        // slot i), or zeros
 #pragma unroll
-        for (int i = 0; i < W; ++i)
+        for (int i = 0; i < W - 1; ++i) {
+          if (active && win) Vec<E>::load(win + ((size_t)n * (W - 1) + i) * Cch + ch, ring[(p + 1 + i) % W]);
+          else
 #pragma unroll
-          for (int c = 0; c < V; ++c) ring[i][c] = 0.f;
+            for (int c = 0; c < V; ++c) ring[(p + 1 + i) % W][c] = 0.f;
+        }
       }
       {
         const E* ex = reinterpret_cast<const E*>(&rx);
@@ -328,14 +336,14 @@ size_t conv_bwd_ws_bytes(const gdn_shape* s, int width) {
 }
 
 template <typename E, int D, int W>
-static void launch_conv_fwd(const gdn_shape* s, const void* x, const void* w, const int32_t* cu, float eps,
-                            void* y, hipStream_t st) {
+static void launch_conv_fwd(const gdn_shape* s, const void* x, const void* w, const int32_t* cu, const void* win,
+                            float eps, void* y, hipStream_t st) {
   constexpr int V = Vec<E>::N;
   const int Cch = 2 * s->h_qk * s->d_k + s->h_v * s->d_v;
   dim3 grid(conv_grid_x(s->total_tokens, kConvTB), (Cch + kWave * V - 1) / (kWave * V));
   GDN_PROF("conv_fwd", st);
-  conv_fwd_kernel<E, D, W><<<grid, 256, 0, st>>>((const E*)x, (const E*)w, cu, s->n_seqs, s->total_tokens, Cch,
-                                                 2 * s->h_qk * s->d_k, eps, (E*)y);
+  conv_fwd_kernel<E, D, W><<<grid, 256, 0, st>>>((const E*)x, (const E*)w, cu, (const E*)win, s->n_seqs,
+                                                 s->total_tokens, Cch, 2 * s->h_qk * s->d_k, eps, (E*)y);
 }
 
 template <typename E, int D, int W>
@@ -356,12 +364,12 @@ static void launch_conv_bwd(const gdn_shape* s, const void* dy, const void* x, c
 }
 
 template <typename E, int D>
-static bool conv_fwd_w(const gdn_shape* s, const void* x, const void* w, int width, const int32_t* cu, float eps,
-                       void* y, hipStream_t st) {
+static bool conv_fwd_w(const gdn_shape* s, const void* x, const void* w, int width, const int32_t* cu,
+                       const void* win, float eps, void* y, hipStream_t st) {
   switch (width) {
-    case 2: launch_conv_fwd<E, D, 2>(s, x, w, cu, eps, y, st); return true;
-    case 3: launch_conv_fwd<E, D, 3>(s, x, w, cu, eps, y, st); return true;
-    case 4: launch_conv_fwd<E, D, 4>(s, x, w, cu, eps, y, st); return true;
+    case 2: launch_conv_fwd<E, D, 2>(s, x, w, cu, win, eps, y, st); return true;
+    case 3: launch_conv_fwd<E, D, 3>(s, x, w, cu, win, eps, y, st); return true;
+    case 4: launch_conv_fwd<E, D, 4>(s, x, w, cu, win, eps, y, st); return true;
   }
   return false;
 }
@@ -377,11 +385,11 @@ static bool conv_bwd_w(const gdn_shape* s, const void* dy, const void* x, const 
   return false;
 }
 
-bool run_conv_fwd(const gdn_shape* s, const void* x, const void* w, int width, const int32_t* cu, float eps,
-                  void* y, hipStream_t st) {
+bool run_conv_fwd(const gdn_shape* s, const void* x, const void* w, int width, const int32_t* cu, const void* win,
+                  float eps, void* y, hipStream_t st) {
   if (s->total_tokens == 0) return true;
 #define GDN_CONV_D(E, D) \
-  if (s->d_k == D) return conv_fwd_w<E, D>(s, x, w, width, cu, eps, y, st);
+  if (s->d_k == D) return conv_fwd_w<E, D>(s, x, w, width, cu, win, eps, y, st);
   if (s->dtype == GDN_BF16) {
     GDN_CONV_D(bf16, 16) GDN_CONV_D(bf16, 32) GDN_CONV_D(bf16, 64) GDN_CONV_D(bf16, 128)
   } else {

@@ -126,7 +126,28 @@ gdn_status gdn_conv1d(const gdn_shape* shape, const void* x, const void* w_conv,
   if (!w_conv || !cu_seqlens || (any && (!x || !y || x == y))) return GDN_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(y)) return GDN_ERR_INVALID_ARG;
   if (!(l2_eps >= 0.f)) return GDN_ERR_INVALID_ARG;
-  if (!run_conv_fwd(shape, x, w_conv, width, cu_seqlens, l2_eps, y, (hipStream_t)stream)) return GDN_ERR_UNSUPPORTED;
+  if (!run_conv_fwd(shape, x, w_conv, width, cu_seqlens, nullptr, l2_eps, y, (hipStream_t)stream))
+    return GDN_ERR_UNSUPPORTED;
+  return launched();
+}
+
+gdn_status gdn_conv1d_prefill(const gdn_shape* shape, const void* x, const void* w_conv, int32_t width, float l2_eps,
+                              const int32_t* cu_seqlens, const void* window_in, void* y, void* window_out,
+                              gdn_stream stream) {
+  gdn_status st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  if (width < 2 || width > 4) return GDN_ERR_UNSUPPORTED;
+  if (window_out && shape->n_seqs > 65535) return GDN_ERR_UNSUPPORTED;
+  const bool any = shape->total_tokens > 0;
+  if (!w_conv || !cu_seqlens || (any && (!x || !y || x == y))) return GDN_ERR_INVALID_ARG;
+  if (window_in && (window_in == window_out || window_in == y)) return GDN_ERR_INVALID_ARG;
+  if (window_out && (window_out == x || window_out == y)) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(window_in) || !aligned16(window_out)) return GDN_ERR_INVALID_ARG;
+  if (!(l2_eps >= 0.f)) return GDN_ERR_INVALID_ARG;
+  if (!run_conv_fwd(shape, x, w_conv, width, cu_seqlens, window_in, l2_eps, y, (hipStream_t)stream))
+    return GDN_ERR_UNSUPPORTED;
+  if (window_out && !run_conv_window(shape, x, width, cu_seqlens, window_in, window_out, (hipStream_t)stream))
+    return GDN_ERR_UNSUPPORTED;
   return launched();
 }
 

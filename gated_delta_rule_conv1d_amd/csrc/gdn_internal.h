@@ -11,8 +11,9 @@ namespace gdn {
 
 // conv1d.hip
 size_t conv_bwd_ws_bytes(const gdn_shape* s, int width);
-bool run_conv_fwd(const gdn_shape* s, const void* x, const void* w, int width, const int32_t* cu, float eps,
-                  void* y, hipStream_t st);
+// win: NULL, or the carried window [N][width-1][Cch] of each sequence's previous inputs
+bool run_conv_fwd(const gdn_shape* s, const void* x, const void* w, int width, const int32_t* cu, const void* win,
+                  float eps, void* y, hipStream_t st);
 bool run_conv_bwd(const gdn_shape* s, const void* dy, const void* x, const void* w, int width, const int32_t* cu,
                   float eps, void* dx, float* dw, void* ws, hipStream_t st);
 

@@ -123,6 +123,20 @@ gdn_status gdn_chunk_index(const gdn_shape* shape, const int32_t* cu_seqlens,
 gdn_status gdn_conv1d(const gdn_shape* shape, const void* x, const void* w_conv, int32_t width,
                       float l2_eps, const int32_t* cu_seqlens, void* y, gdn_stream stream);
 
+/* gdn_conv1d for a prefill that continues earlier calls (chunked prefill): each
+ * sequence starts from its carried window of previous inputs instead of zero
+ * history.  Page: "feat(models): dense Qwen3.5 custom attention", KL mismatch
+ * table and review overview (continuation outside the training path).
+ *   window_in:  [N][width-1][Cch] (dtype), sequence n's previous width-1
+ *               inputs, oldest first, or NULL (zero history, as gdn_conv1d);
+ *   window_out: NULL, or [N][width-1][Cch]: the last width-1 inputs of
+ *               [window_in[n] ; x rows of sequence n] (gdn_conv1d_window);
+ *               must not alias window_in, x or y.  N <= 65535 when given.
+ * Other arguments as gdn_conv1d. */
+gdn_status gdn_conv1d_prefill(const gdn_shape* shape, const void* x, const void* w_conv, int32_t width,
+                              float l2_eps, const int32_t* cu_seqlens, const void* window_in, void* y,
+                              void* window_out, gdn_stream stream);
+
 /* Reverse mode of gdn_conv1d.  dy: gradient w.r.t. y [T][Cch]; writes dx
  * [T][Cch] (dtype) and dw_conv [Cch][width] (float32, summed over all tokens
  * in a fixed order).  Workspace: gdn_conv1d_bwd_workspace bytes. */

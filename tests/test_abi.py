@@ -160,6 +160,10 @@ def test_decode_calls_reject():
     assert lib.gdn_conv1d_window(ctypes.byref(s), FAKE, 4, None, None, A, None) == INVALID   # no cu_seqlens
     assert lib.gdn_conv1d_window(ctypes.byref(s), FAKE, 1, FAKE, None, A, None) == UNSUPPORTED
     assert lib.gdn_conv1d_window(ctypes.byref(s), FAKE, 4, FAKE, FAKE_ODD, C3, None) == INVALID
+    assert lib.gdn_conv1d_prefill(ctypes.byref(s), FAKE, FAKE, 4, 1e-6, FAKE, A, B2, A, None) == INVALID  # in place
+    assert lib.gdn_conv1d_prefill(ctypes.byref(s), FAKE, FAKE, 4, 1e-6, FAKE, A, FAKE, C3, None) == INVALID  # y = x
+    assert lib.gdn_conv1d_prefill(ctypes.byref(s), FAKE, FAKE, 4, 1e-6, FAKE, FAKE_ODD, B2, C3, None) == INVALID
+    assert lib.gdn_conv1d_prefill(ctypes.byref(s), FAKE, FAKE, 5, 1e-6, FAKE, A, B2, C3, None) == UNSUPPORTED
 
 
 def test_workspace_sizes_grow_with_tokens_and_max_chunks_bound():
