@@ -448,7 +448,8 @@ inline int state_grid(int N, int Hk, int G, int NVT) { return ((N * Hk + 7) / 8)
 
 // State passes with one 512-thread workgroup per (sequence, v-head), for
 // bf16, d = 128, chunk 64 (state_wide.hip).
-void launch_state_fwd_wide(const ChunkArgs& a, hipStream_t st, int mode);
+// half: two workgroups per (sequence, v-head), 64 state columns each
+void launch_state_fwd_wide(const ChunkArgs& a, hipStream_t st, int mode, bool half);
 void launch_state_bwd_wide(const ChunkArgs& a, hipStream_t st);
 template <typename E, int D, int C>
 constexpr bool use_wide_state() { return sizeof(E) == 2 && D == 128 && C == 64; }

@@ -468,15 +468,21 @@ template <typename E, int D>
 constexpr int state_dvt() { return D >= 32 ? 32 : D; }
 
 // The one-workgroup-per-(sequence, v-head) state pass runs one serial chain of
-// chunk steps per workgroup; with few chains most of the chip idles (a single
-// long sequence has only Hv of them).  Then each state is split into
-// independent 16-column dv tiles (exact: the update multiplies the state from
-// the left only), eight times the workgroups, each step re-staging the shared
-// chunk operands.  Measured at d = 128, chunk 64: 32 chains (one 65536-token
-// sequence) 8.0 -> 3.1 ms; at 128 chains the whole-state pass stays ahead
-// (0.28 ms against 0.30 with 32-column and 0.41 with 16-column tiles).
-// Returns the tile width to use, or 0 for the whole-state pass.
-inline int narrow_state_dvt(const ChunkArgs& a) { return a.N * a.Hv * 4 <= kNumCUs ? 16 : 0; }
+// chunk steps per workgroup; with fewer chains than compute units most of the
+// chip idles (a single long sequence has only Hv of them).  The state's dv
+// columns are independent (the update multiplies it from the left only), so
+// it can be split:
+//  - at most 64 chains: 16-column tiles, eight workgroups per chain (the
+//    general tiled pass; one 65536-token sequence at d = 128: 8.0 -> 3.1 ms);
+//  - fewer chains than CUs: two workgroups per chain with 64 columns each
+//    (the whole-state pass halved; the same arithmetic per element);
+//  - otherwise one workgroup per chain, the whole state.
+// Returns the column count per workgroup.
+inline int state_columns(const ChunkArgs& a, int D) {
+  const int chains = a.N * a.Hv;
+  if (chains * 4 <= kNumCUs) return 16;
+  return chains < kNumCUs ? D / 2 : D;
+}
 
 template <typename E, int D, int C, int DVT>
 static void launch_state_fwd_tiled(const ChunkArgs& a, hipStream_t st, int mode) {
@@ -502,9 +508,9 @@ void launch_chunk_fwd_core(const ChunkArgs& a, hipStream_t st, int mode) {
   if constexpr (use_wide_state<E, D, C>()) {
     // every mode takes the same choice, so that the saved training pair and
     // the recomputing backward see the same H_c and W bits
-    const int ndvt = narrow_state_dvt(a);
-    if (ndvt == 16) launch_state_fwd_tiled<E, D, C, 16>(a, st, mode);
-    else launch_state_fwd_wide(a, st, mode);
+    const int nc = state_columns(a, D);
+    if (nc == 16) launch_state_fwd_tiled<E, D, C, 16>(a, st, mode);
+    else launch_state_fwd_wide(a, st, mode, nc < D);
     return;
   }
   launch_state_fwd_tiled<E, D, C, DVT>(a, st, mode);

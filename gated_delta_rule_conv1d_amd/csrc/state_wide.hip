@@ -36,13 +36,14 @@ constexpr int kLD2C = 2 * kC + 8;
 typedef bf16 E;
 typedef Mma<bf16> M;
 
+template <int NC>  // state columns this workgroup carries
 struct FwdSmem {
   E Kt[kD][kLDC];    // K~^T, K~ = diag(e) K
   E Ktl[kD][kLDC];
-  E Ht[kD][kLDQ];    // H^T: Ht[c][r] = H[r][c]
-  E Htl[kD][kLDQ];
-  E Wt[kD][kLDC];    // W^T
-  E Wtl[kD][kLDC];
+  E Ht[NC][kLDQ];    // H^T: Ht[c][r] = H[r][c]
+  E Htl[NC][kLDQ];
+  E Wt[NC][kLDC];    // W^T
+  E Wtl[NC][kLDC];
   float gam[kC];
 };
 
@@ -89,32 +90,39 @@ struct Buf {
   __device__ __forceinline__ M::frag fr(int off) const { return __builtin_bit_cast(M::frag, u4(off)); }
 };
 
-template <int MODE>
+// NC = 128: the whole state; NC = 64: half of its columns (exact: the update
+// multiplies the state from the left only), two workgroups per (sequence,
+// v-head) with the same per-element arithmetic
+template <int MODE, int NC>
 __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
   constexpr bool OUT = MODE & kFwdOut, STORE = MODE & kFwdStore;
   constexpr int D = kD, C = kC;
-  __shared__ FwdSmem sm;
+  constexpr int P1 = NC / 32;  // phase-1 column tiles per wave
+  constexpr int P2 = NC / 16;  // state column tiles per wave
+  static_assert(NC == kD || NC == kD / 2, "whole or half state");
+  __shared__ FwdSmem<NC> sm;
   int n, h, vt;
-  if (!state_block(blockIdx.x, a.N, a.Hk, a.G, 1, n, h, vt)) return;
+  if (!state_block(blockIdx.x, a.N, a.Hk, a.G, kD / NC, n, h, vt)) return;
   const int j = h / a.G;
+  const int col0 = vt * NC;  // first state column of this workgroup
   const int tid = threadIdx.x, w = wave_id(), lane = lane_id();
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
-  const int rt1 = w & 3, cb = kP1 * (w >> 2);  // W / O tiles: row tile rt1, column tiles cb .. cb+3
-  const int rt2 = w;                           // state tiles: row tile rt2, every column tile
+  const int rt1 = w & 3, cb = P1 * (w >> 2);  // W / O tiles: row tile rt1, column tiles cb .. cb+P1-1
+  const int rt2 = w;                          // state tiles: row tile rt2, every column tile
 
-  f32x4 Hr[kP2];
+  f32x4 Hr[P2];
 #pragma unroll
-  for (int i = 0; i < kP2; ++i) {
+  for (int i = 0; i < P2; ++i) {
     Hr[i] = zero4();
     if (a.h0) {
       const float* src = a.h0 + ((int64_t)n * a.Hv + h) * D * D;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Hr[i][e] = src[(rt2 * 16 + acc_row(e)) * D + i * 16 + acc_col()];
+      for (int e = 0; e < 4; ++e) Hr[i][e] = src[(rt2 * 16 + acc_row(e)) * D + col0 + i * 16 + acc_col()];
     }
   }
   auto write_Ht = [&]() {
 #pragma unroll
-    for (int i = 0; i < kP2; ++i) {
+    for (int i = 0; i < P2; ++i) {
       const int c = i * 16 + acc_col(), r = rt2 * 16 + acc_row(0);
       st4_split<E>(&sm.Ht[c][r], &sm.Htl[c][r], Hr[i]);
     }
@@ -125,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
   uint4 kt_h0, kt_h1, kt_l0, kt_l1;  // this thread's pieces of K~^T (hi, lo); named, so they stay in registers
   float g_r = 0.f;
   M::frag wkf[4], qf[4];
-  f32x4 uf[kP1];
+  f32x4 uf[P1];
   float4 pf[2][2];
   auto load_shared = [&](int ci) {
     const int64_t slot = (int64_t)ci * a.Hv + h;
@@ -150,9 +158,10 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
     }
     const Buf ub(a.U + slot * C * D, C * D * 4);
 #pragma unroll
-    for (int i = 0; i < kP1; ++i)
+    for (int i = 0; i < P1; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) uf[i][e] = ub.f1(((rt1 * 16 + acc_row(e)) * D + (cb + i) * 16 + acc_col()) * 4);
+      for (int e = 0; e < 4; ++e)
+        uf[i][e] = ub.f1(((rt1 * 16 + acc_row(e)) * D + col0 + (cb + i) * 16 + acc_col()) * 4);
   };
   auto load_p2 = [&](int ci) {
     const Buf pb(a.P + ((int64_t)ci * a.Hv + h) * C * C, C * C * 4);
@@ -204,17 +213,17 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
     if constexpr (STORE) {  // state entering this chunk, for the backward pass
       float* Hg = a.Hc + slot * D * D;
 #pragma unroll
-      for (int i = 0; i < kP2; ++i) store_tile<float>(Hg, D, rt2 * 16, i * 16, Hr[i], D);
+      for (int i = 0; i < P2; ++i) store_tile<float>(Hg, D, rt2 * 16, col0 + i * 16, Hr[i], D);
     }
 
     // phase 1: W = U - Wk H and diag(Gam) Q H on this wave's tiles
-    f32x4 x[kP1], o[kP1];
+    f32x4 x[P1], o[P1];
 #pragma unroll
-    for (int i = 0; i < kP1; ++i) x[i] = o[i] = zero4();
+    for (int i = 0; i < P1; ++i) x[i] = o[i] = zero4();
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-      for (int i = 0; i < kP1; ++i) {
+      for (int i = 0; i < P1; ++i) {
         const int c = (cb + i) * 16 + r16;
         const M::frag bh = fr(&sm.Ht[c][ks * 32 + kq]);
         const M::frag bl = fr(&sm.Htl[c][ks * 32 + kq]);
@@ -227,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
       }
     }
 #pragma unroll
-    for (int i = 0; i < kP1; ++i)
+    for (int i = 0; i < P1; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[i][e] = uf[i][e] - x[i][e];  // x <- W
     if constexpr (OUT) {
@@ -235,22 +244,22 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
       for (int e = 0; e < 4; ++e) {
         const float gm = __expf(sm.gam[rt1 * 16 + acc_row(e)]);
 #pragma unroll
-        for (int i = 0; i < kP1; ++i) o[i][e] *= gm;
+        for (int i = 0; i < P1; ++i) o[i][e] *= gm;
       }
     }
     if (more) load_p1(ci + 1, nent.y, nent.z);  // Wk, q, U of the next chunk
 #pragma unroll
-    for (int i = 0; i < kP1; ++i) {
+    for (int i = 0; i < P1; ++i) {
       const int c = (cb + i) * 16 + acc_col(), r = rt1 * 16 + acc_row(0);
       st4_split<E>(&sm.Wt[c][r], &sm.Wtl[c][r], x[i]);
-      if constexpr (STORE) store_tile<float>(a.W + slot * C * D, D, rt1 * 16, (cb + i) * 16, x[i], C);
+      if constexpr (STORE) store_tile<float>(a.W + slot * C * D, D, rt1 * 16, col0 + (cb + i) * 16, x[i], C);
     }
     __syncthreads();
 
     // phase 2: H <- Gam_last H + K~^T W;  o = scale (diag(Gam) Q H + P W)
     const float gl = __expf(sm.gam[len - 1]);
 #pragma unroll
-    for (int i = 0; i < kP2; ++i)
+    for (int i = 0; i < P2; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) Hr[i][e] *= gl;
 #pragma unroll
@@ -258,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
       const M::frag ah = fr(&sm.Kt[rt2 * 16 + r16][ks * 32 + kq]);
       const M::frag al = fr(&sm.Ktl[rt2 * 16 + r16][ks * 32 + kq]);
 #pragma unroll
-      for (int i = 0; i < kP2; ++i) {
+      for (int i = 0; i < P2; ++i) {
         const int c = i * 16 + r16;
         const M::frag bh = fr(&sm.Wt[c][ks * 32 + kq]);
         const M::frag bl = fr(&sm.Wtl[c][ks * 32 + kq]);
@@ -273,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
         M::frag ph, pl;
         split8(pf[ks][0], pf[ks][1], ph, pl);
 #pragma unroll
-        for (int i = 0; i < kP1; ++i) {
+        for (int i = 0; i < P1; ++i) {
           const int c = (cb + i) * 16 + r16;
           const M::frag bh = fr(&sm.Wt[c][ks * 32 + kq]);
           const M::frag bl = fr(&sm.Wtl[c][ks * 32 + kq]);
@@ -285,10 +294,10 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
       if (more) load_p2(ci + 1);
       E* og = (E*)a.o + (int64_t)tok0 * a.Hv * D + (int64_t)h * D;
 #pragma unroll
-      for (int i = 0; i < kP1; ++i) {
+      for (int i = 0; i < P1; ++i) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[i][e] *= a.scale;
-        store_tile<E>(og, (int64_t)a.Hv * D, rt1 * 16, (cb + i) * 16, o[i], len);
+        store_tile<E>(og, (int64_t)a.Hv * D, rt1 * 16, col0 + (cb + i) * 16, o[i], len);
       }
     }
     write_Ht();  // phase 1 (the only reader of H^T) is over for every wave
@@ -297,9 +306,9 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
   if (a.ht) {
     float* dst = a.ht + ((int64_t)n * a.Hv + h) * D * D;
 #pragma unroll
-    for (int i = 0; i < kP2; ++i)
+    for (int i = 0; i < P2; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[(rt2 * 16 + acc_row(e)) * D + i * 16 + acc_col()] = Hr[i][e];
+      for (int e = 0; e < 4; ++e) dst[(rt2 * 16 + acc_row(e)) * D + col0 + i * 16 + acc_col()] = Hr[i][e];
   }
 }
 
@@ -483,11 +492,17 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
 
 }  // namespace
 
-void launch_state_fwd_wide(const ChunkArgs& a, hipStream_t st, int mode) {
-  const dim3 grid(state_grid(a.N, a.Hk, a.G, 1));
-  if (mode == kFwdOut) state_fwd_wide_kernel<kFwdOut><<<grid, kThreads, 0, st>>>(a);
-  else if (mode == kFwdStore) state_fwd_wide_kernel<kFwdStore><<<grid, kThreads, 0, st>>>(a);
-  else state_fwd_wide_kernel<kFwdBoth><<<grid, kThreads, 0, st>>>(a);
+template <int NC>
+static void launch_fwd_nc(const ChunkArgs& a, hipStream_t st, int mode) {
+  const dim3 grid(state_grid(a.N, a.Hk, a.G, kD / NC));
+  if (mode == kFwdOut) state_fwd_wide_kernel<kFwdOut, NC><<<grid, kThreads, 0, st>>>(a);
+  else if (mode == kFwdStore) state_fwd_wide_kernel<kFwdStore, NC><<<grid, kThreads, 0, st>>>(a);
+  else state_fwd_wide_kernel<kFwdBoth, NC><<<grid, kThreads, 0, st>>>(a);
+}
+
+void launch_state_fwd_wide(const ChunkArgs& a, hipStream_t st, int mode, bool half) {
+  if (half) launch_fwd_nc<kD / 2>(a, st, mode);
+  else launch_fwd_nc<kD>(a, st, mode);
 }
 
 void launch_state_bwd_wide(const ChunkArgs& a, hipStream_t st) {

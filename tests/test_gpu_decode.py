@@ -197,3 +197,45 @@ def test_chunked_prefill_continues(dtype, d, Hk, Hv, width, first, second):
     # split arithmetic that bounds a single call's fp32 outputs at 2e-3 RMS; the
     # chained state is held to half the bf16 bar.
     assert_close(host(state), rht, TOL_F32_OUT[dtype] if dtype == "f32" else 1e-2, "final state")
+
+
+def test_decode_workload_full_size():
+    """The decode workload exactly as the benchmark runs it (256 sequences, 16 q/k
+    and 32 v heads, d = 128, bf16, states and windows drawn by the generator):
+    gates, conv step, recurrent step (in place) and the norm epilogue against the
+    oracle on every sequence and head, each stage fed the oracle's own inputs."""
+    _case("decode_workload_full_size")
+    cfg = synth.config("decode")
+    inp = synth.make_inputs(cfg, keep_raw=True)
+    N, Hk, Hv, d, W = cfg.N, cfg.h_qk, cfg.h_v, cfg.d_k, cfg.width
+    C, nqk = cfg.channels, 2 * Hk * d
+    s = gdn.Shape(N, N, Hk, Hv, d, d, cfg.chunk, gdn.BF16, 1.0)
+    a, b, A_log, dt = (np.asarray(inp[k], dtype=np.float32) for k in ("a", "b", "A_log", "dt_bias"))
+    g, beta = gdn.gates(f32(a), f32(b), f32(A_log), f32(dt), s)
+    window = to_dev(inp["window"], "bf16")
+    y = gdn.conv1d_step(to_dev(inp["x"], "bf16"), to_dev(inp["w_conv"], "bf16"), window, s)
+
+    # oracle: each sequence is its window followed by the new token (4 tokens),
+    # whose conv output is the last one; the recurrence then takes that token
+    # from the drawn state
+    xs = np.concatenate([inp["window"], inp["x"][:, None, :]], axis=1).reshape(N * W, C)
+    yo = oracle.conv1d(xs, inp["w_conv"], synth.cu_from_lengths([W] * N), nqk, d).reshape(N, W, C)[:, -1]
+    assert_close(host(y), yo, TOL["bf16"], "y_conv")
+    yo = synth.round_bf16(yo.astype(np.float32)).astype(np.float64)   # crosses the ABI in bf16
+    rg, rbeta = oracle.gates(a, b, A_log, dt)
+    assert_close(host(g), rg, 1e-4, "g")
+    assert_close(host(beta), rbeta, 1e-4, "beta")
+    yd = to_dev(yo, "bf16")
+    state = f32(inp["h0"])
+    o, _ = gdn.recurrent_step(yd[:, :Hk * d], yd[:, Hk * d:nqk], yd[:, nqk:], f32(rg), f32(rbeta), s,
+                              state_in=state, state_out=state)
+    ro, rht = oracle.recurrence(yo[:, :Hk * d].reshape(N, Hk, d), yo[:, Hk * d:nqk].reshape(N, Hk, d),
+                                yo[:, nqk:].reshape(N, Hv, d), rg, rbeta, np.arange(N + 1, dtype=np.int32),
+                                h0=inp["h0"])
+    assert_close(host(o), ro, TOL["bf16"], "o")
+    assert_close(host(state), rht, TOL_F32_OUT["bf16"], "state")
+    # the epilogue, fed the oracle's own o (bf16, as it crosses the ABI)
+    o_in = synth.round_bf16(ro.astype(np.float32))
+    out = gdn.norm_gate(to_dev(o_in, "bf16"), to_dev(inp["z"], "bf16"), to_dev(inp["w_norm"], "bf16"), s)
+    ry = oracle.norm_gate(o_in, inp["z"], inp["w_norm"])
+    assert_close(host(out), ry, TOL["bf16"], "y")

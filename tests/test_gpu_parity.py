@@ -128,7 +128,8 @@ CHUNK_CASES = [
     ("f32", 64, 32, 1, 2, (130, 7)),
     ("bf16", 16, 16, 2, 2, (40, 9)),
     ("bf16", 128, 64, 2, 4, (200, 1, 64, 63, 65)),       # 20 (sequence, v-head) chains: 16-column state tiles
-    ("bf16", 128, 64, 8, 16, (100, 64, 1, 65, 20)),      # 80 chains: whole-state pass
+    ("bf16", 128, 64, 8, 16, (100, 64, 1, 65, 20)),      # 80 chains: half-state workgroups
+    ("bf16", 128, 64, 16, 32, (70, 64, 1, 65, 0, 130, 3, 40)),  # 256 chains: whole-state pass
     ("bf16", 128, 32, 1, 2, (100, 33)),
     ("bf16", 64, 16, 2, 2, (50, 17)),
     ("bf16", 32, 64, 1, 1, (129,)),
