@@ -474,14 +474,22 @@ constexpr int state_dvt() { return D >= 32 ? 32 : D; }
 // it can be split:
 //  - at most 64 chains: 16-column tiles, eight workgroups per chain (the
 //    general tiled pass; one 65536-token sequence at d = 128: 8.0 -> 3.1 ms);
-//  - fewer chains than CUs: two workgroups per chain with 64 columns each
-//    (the whole-state pass halved; the same arithmetic per element);
+//  - two workgroups per chain with 64 columns each (the whole-state pass
+//    halved, with the same arithmetic per element, so the same bits): when
+//    there are fewer chains than CUs, and for inference up to four chains per
+//    CU, where the shorter serial steps outweigh the doubled staging (dense
+//    4 x 2048: 0.28 -> 0.20 ms; varlen 32768: 0.94 -> 0.80 ms); the passes
+//    that also store H_c and W are bandwidth-bound from one chain per CU on
+//    (training 8 x 8192: 1.64 ms whole, 2.01 ms halved);
 //  - otherwise one workgroup per chain, the whole state.
-// Returns the column count per workgroup.
-inline int state_columns(const ChunkArgs& a, int D) {
+// The 16-column choice must not depend on the mode (it changes the order of
+// the sums, and the saved training pair and the recomputing backward must see
+// the same H_c and W bits); the halving may.  Returns the column count per
+// workgroup.
+inline int state_columns(const ChunkArgs& a, int D, int mode) {
   const int chains = a.N * a.Hv;
   if (chains * 4 <= kNumCUs) return 16;
-  return chains < kNumCUs ? D / 2 : D;
+  return chains < (mode == kFwdOut ? 4 * kNumCUs : kNumCUs) ? D / 2 : D;
 }
 
 template <typename E, int D, int C, int DVT>
@@ -506,9 +514,7 @@ void launch_chunk_fwd_core(const ChunkArgs& a, hipStream_t st, int mode) {
   }
   GDN_PROF(state_name[mode], st);
   if constexpr (use_wide_state<E, D, C>()) {
-    // every mode takes the same choice, so that the saved training pair and
-    // the recomputing backward see the same H_c and W bits
-    const int nc = state_columns(a, D);
+    const int nc = state_columns(a, D, mode);
     if (nc == 16) launch_state_fwd_tiled<E, D, C, 16>(a, st, mode);
     else launch_state_fwd_wide(a, st, mode, nc < D);
     return;
