@@ -548,7 +548,7 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
     const int64_t slot = (int64_t)ci * a.Hv + h;
     const E* vg = (const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)h * D;
     TileRegs<E, C, D, NTH> pV;  // v rows and T (from the preparation pass)
-    TileRegs<float, C, C, NTH> pTm;
+    TileRegs<float, C, C, NTH, true> pTm;  // rows first: also written transposed
     TileRegs<float, D, C, NTH> rXu, rXw;  // dW^T, and dWk^T (in flight during the dXu products)
     pV.load(vg, a.sv, len);
     pTm.load(a.Tw + slot * C * C, C, C);

@@ -175,13 +175,17 @@ __device__ __forceinline__ void g2s(E* s, int lds, const E* g) {
 }
 
 // rows [0, len) of a token-major input written transposed into LDS:
-// s[c * lds + r] = g[r * ld + c]; zero past len.
+// s[c * lds + r] = g[r * ld + c]; zero past len.  Rows first: 16 adjacent lanes
+// read the same columns of 16 adjacent rows, so each transposed write puts 16
+// consecutive elements of one LDS row down (no bank conflicts between them).
 template <typename E, int R, int Ccols, int NTH = kChunkThreads>
 __device__ __forceinline__ void rows2s_t(E* s, int lds, const E* g, int64_t ld, int len) {
   constexpr int V = Vec<E>::N;
   constexpr int PER_ROW = Ccols / V;
+  static_assert(R % 16 == 0, "rows in groups of 16");
   for (int e = threadIdx.x; e < R * PER_ROW; e += NTH) {
-    const int r = e / PER_ROW, c = (e % PER_ROW) * V;
+    const int grp = e >> 4;
+    const int r = (grp / PER_ROW) * 16 + (e & 15), c = (grp % PER_ROW) * V;
     float val[V];
     if (r < len) {
       Vec<E>::load(g + (int64_t)r * ld + c, val);
@@ -306,20 +310,38 @@ struct StateSmem {
 // stride ld elements, rows past rows_valid read as zero) by all threads of a
 // workgroup with 16-byte loads; store() writes it to LDS afterwards.  Used to
 // issue the next chunk's loads before the current chunk's compute.
-template <typename T, int R, int COLS, int NTH = kChunkThreads>
+// Piece e (16 bytes) is, by default, row e / PER_ROW, columns (e % PER_ROW) * V:
+// adjacent lanes take adjacent pieces of a row.  With RF (rows first), 16
+// adjacent lanes take the same columns of 16 adjacent rows: store_t then
+// writes 16 consecutive elements of a transposed row per lane group instead of
+// one element each of 16 rows a 16-byte piece apart (which fall in the same
+// LDS banks), at the price of 64-byte instead of 256-byte runs per global load.
+template <typename T, int R, int COLS, int NTH = kChunkThreads, bool RF = false>
 struct TileRegs {
   static constexpr int V = 16 / (int)sizeof(T);
   static constexpr int PER_ROW = COLS / V;
   static constexpr int TOTAL = R * PER_ROW;
   static constexpr int N = (TOTAL + NTH - 1) / NTH;
+  static_assert(!RF || R % 16 == 0, "rows-first pieces come in groups of 16 rows");
   uint4 r[N];
+  __device__ __forceinline__ static void pos(int e, int& row, int& c) {
+    if constexpr (RF) {
+      const int g = e >> 4;
+      row = (g / PER_ROW) * 16 + (e & 15);
+      c = (g % PER_ROW) * V;
+    } else {
+      row = e / PER_ROW;
+      c = (e % PER_ROW) * V;
+    }
+  }
   __device__ __forceinline__ void load(const T* g, int64_t ld, int rows_valid) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int e = threadIdx.x + i * NTH;
       r[i] = make_uint4(0, 0, 0, 0);
       if (e < TOTAL) {
-        const int row = e / PER_ROW, c = (e % PER_ROW) * V;
+        int row, c;
+        pos(e, row, c);
         if (row < rows_valid) r[i] = *reinterpret_cast<const uint4*>(g + (int64_t)row * ld + c);
       }
     }
@@ -329,7 +351,8 @@ struct TileRegs {
     for (int i = 0; i < N; ++i) {
       const int e = threadIdx.x + i * NTH;
       if (e < TOTAL) {
-        const int row = e / PER_ROW, c = (e % PER_ROW) * V;
+        int row, c;
+        pos(e, row, c);
         *reinterpret_cast<uint4*>(s + row * lds + c) = r[i];
       }
     }
@@ -344,7 +367,8 @@ struct TileRegs {
     for (int i = 0; i < N; ++i) {
       const int e = threadIdx.x + i * NTH;
       if (e < TOTAL) {
-        const int row = e / PER_ROW, c = (e % PER_ROW) * V;
+        int row, c;
+        pos(e, row, c);
         const T* f = reinterpret_cast<const T*>(&r[i]);
         const float sc = (rs ? rs[i] : 1.f) * mult;
 #pragma unroll
@@ -356,7 +380,11 @@ struct TileRegs {
       }
     }
   }
-  __device__ __forceinline__ int row_of(int i) const { return (threadIdx.x + i * NTH) / PER_ROW; }
+  __device__ __forceinline__ int row_of(int i) const {
+    int row, c;
+    pos(threadIdx.x + i * NTH, row, c);
+    return row;
+  }
   // float tile written as E hi (and lo) parts
   template <typename E>
   __device__ __forceinline__ void store_split(E* hi, E* lo, int lds) const {
@@ -365,7 +393,8 @@ struct TileRegs {
     for (int i = 0; i < N; ++i) {
       const int e = threadIdx.x + i * NTH;
       if (e < TOTAL) {
-        const int row = e / PER_ROW, c = (e % PER_ROW) * V;
+        int row, c;
+        pos(e, row, c);
         const float* f = reinterpret_cast<const float*>(&r[i]);
         st4_split<E>(hi + row * lds + c, lo + row * lds + c, f32x4{f[0], f[1], f[2], f[3]});
       }

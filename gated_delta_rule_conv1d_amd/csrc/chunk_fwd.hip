@@ -89,7 +89,7 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
   const E* qg = (const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D;
   const E* kg = (const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D;
   // a v-head's v rows and gates are loaded one v-head ahead
-  TileRegs<E, C, D, NTH> pV;
+  TileRegs<E, C, D, NTH, true> pV;  // rows first: written transposed
   float gv = 0.f, bv = 0.f;
   auto load_head = [&](int hh) {
     pV.load((const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)hh * D, a.sv, len);
@@ -101,7 +101,8 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
   load_head(j * a.G);
 
   {  // q and k rows: every load issued before the first LDS write; K^T from the same registers
-    TileRegs<E, C, D, NTH> rQ, rK;
+    TileRegs<E, C, D, NTH> rQ;
+    TileRegs<E, C, D, NTH, true> rK;  // rows first: also written transposed
     rQ.load(qg, a.sqk, len);
     rK.load(kg, a.sqk, len);
     rQ.store(&sm.Qs[0][0], S::LDQ);
