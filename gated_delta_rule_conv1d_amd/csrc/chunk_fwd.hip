@@ -81,192 +81,203 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
   __shared__ S sm;
   constexpr int V = Vec<E>::N;
   constexpr int NT = C / 16, ND = D / 16;
-  const int ci = blockIdx.x, j = blockIdx.y;
-  const int4 ent = chunk_entry(a.table, ci);
-  if (ent.x < 0) return;
-  const int tok0 = ent.y, len = ent.z;
   const int tid = threadIdx.x, w = wave_id(), lane = lane_id();
-  const E* qg = (const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D;
-  const E* kg = (const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D;
-  // a v-head's v rows and gates are loaded one v-head ahead
-  TileRegs<E, C, D, NTH, true> pV;  // rows first: written transposed
+  // Persistent: the workgroup walks items (chunk, k-head) = (it / Hk, it % Hk)
+  // from blockIdx.x in steps of gridDim.x, and requests the next item's q, k
+  // rows, first v rows and gates while the current item finishes, so that no
+  // item starts on a cold global round trip.  Padding chunks past the last
+  // one end the table, so the first of them ends the walk.
+  const int n_items = a.max_chunks * a.Hk;
+  auto item_entry = [&](int it) { return it < n_items ? chunk_entry(a.table, it / a.Hk) : make_int4(-1, 0, 0, 0); };
+  TileRegs<E, C, D, NTH, true> pV;  // a v-head's v rows; rows first: written transposed
+  TileRegs<E, C, D, NTH> rQ;
+  TileRegs<E, C, D, NTH, true> rK;  // rows first: also written transposed
   float gv = 0.f, bv = 0.f;
-  auto load_head = [&](int hh) {
-    pV.load((const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)hh * D, a.sv, len);
-    if (w == 0 && lane < len) {
-      gv = a.g[(int64_t)(tok0 + lane) * a.Hv + hh];
-      bv = a.beta[(int64_t)(tok0 + lane) * a.Hv + hh];
+  auto load_head = [&](int tok, int n, int hh) {
+    pV.load((const E*)a.v + (int64_t)tok * a.sv + (int64_t)hh * D, a.sv, n);
+    if (w == 0 && lane < n) {
+      gv = a.g[(int64_t)(tok + lane) * a.Hv + hh];
+      bv = a.beta[(int64_t)(tok + lane) * a.Hv + hh];
     }
   };
-  load_head(j * a.G);
-
-  {  // q and k rows: every load issued before the first LDS write; K^T from the same registers
-    TileRegs<E, C, D, NTH> rQ;
-    TileRegs<E, C, D, NTH, true> rK;  // rows first: also written transposed
-    rQ.load(qg, a.sqk, len);
-    rK.load(kg, a.sqk, len);
+  auto load_item = [&](int4 e, int jj) {
+    rQ.load((const E*)a.q + (int64_t)e.y * a.sqk + (int64_t)jj * D, a.sqk, e.z);
+    rK.load((const E*)a.k + (int64_t)e.y * a.sqk + (int64_t)jj * D, a.sqk, e.z);
+    load_head(e.y, e.z, jj * a.G);
+  };
+  int item = blockIdx.x;
+  int4 ent = item_entry(item);
+  if (ent.x >= 0) load_item(ent, item % a.Hk);
+  while (ent.x >= 0) {
+    const int ci = item / a.Hk, j = item % a.Hk;
+    const int tok0 = ent.y, len = ent.z;
+    const int next = item + (int)gridDim.x;
+    const int4 nent = item_entry(next);
     rQ.store(&sm.Qs[0][0], S::LDQ);
     rK.store(&sm.Ks[0][0], S::LDQ);
     rK.template store_t<E>(&sm.Kt[0][0], S::LDCE);
-  }
-  __syncthreads();
-  for (int t = w; t < NT * NT; t += NW) {
-    const int rt = t / NT, ct = t % NT;
-    const f32x4 acc = mm_tile<E, D>(zero4(), &sm.Ks[rt * 16][0], S::LDQ, &sm.Ks[ct * 16][0], S::LDQ);
+    __syncthreads();
+    for (int t = w; t < NT * NT; t += NW) {
+      const int rt = t / NT, ct = t % NT;
+      const f32x4 acc = mm_tile<E, D>(zero4(), &sm.Ks[rt * 16][0], S::LDQ, &sm.Ks[ct * 16][0], S::LDQ);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sm.Sk[rt * 16 + acc_row(e)][ct * 16 + acc_col()] = acc[e];
-  }
-  __syncthreads();
-
-  for (int gi = 0; gi < a.G; ++gi) {
-    const int h = j * a.G + gi;
-    const int64_t slot = (int64_t)ci * a.Hv + h;
-    if (w == 0) {  // within-chunk cumulative gate
-      float x = gv;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const float y = __shfl_up(x, off, kWave);
-        if (lane >= off) x += y;
-      }
-      if (lane < C) {
-        sm.gam[lane] = x;
-        sm.beta[lane] = bv;
-        a.gam[slot * C + lane] = x;
-      }
+      for (int e = 0; e < 4; ++e) sm.Sk[rt * 16 + acc_row(e)][ct * 16 + acc_col()] = acc[e];
     }
-    pV.template store_t<E>(&sm.Vt[0][0], S::LDCE);  // V^T
-    if (gi + 1 < a.G) load_head(h + 1);
     __syncthreads();
 
-    // P = lower_incl(D * Q K^T) (fp32 to workspace), A = strict_lower(beta_r D * K K^T)
-    {
-      float* Pg = a.P + slot * C * C;
-      for (int t = w; t < NT * NT; t += NW) {
-        const int rt = t / NT, ct = t % NT;
-        const f32x4 acc = mm_tile<E, D>(zero4(), &sm.Qs[rt * 16][0], S::LDQ, &sm.Ks[ct * 16][0], S::LDQ);
-        f32x4 pv;
+    for (int gi = 0; gi < a.G; ++gi) {
+      const int h = j * a.G + gi;
+      const int64_t slot = (int64_t)ci * a.Hv + h;
+      if (w == 0) {  // within-chunk cumulative gate
+        float x = gv;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = rt * 16 + acc_row(e), s = ct * 16 + acc_col();
-          const float dd = (s <= r) ? __expf(sm.gam[r] - sm.gam[s]) : 0.f;
-          pv[e] = (r < len) ? dd * acc[e] : 0.f;
-          sm.Am[r][s] = (s < r) ? sm.beta[r] * dd * sm.Sk[r][s] : 0.f;
+        for (int off = 1; off < kWave; off <<= 1) {
+          const float y = __shfl_up(x, off, kWave);
+          if (lane >= off) x += y;
         }
-        store_tile<float>(Pg, C, rt * 16, ct * 16, pv, C);
-        if constexpr (LO_OUT) store_tile_t(a.Ptr + slot * C * C, C, rt * 16, ct * 16, pv);
+        if (lane < C) {
+          sm.gam[lane] = x;
+          sm.beta[lane] = bv;
+          a.gam[slot * C + lane] = x;
+        }
       }
-    }
-    __syncthreads();
-    // Outputs that need only gamma, K and Q (K~^T hi / lo; for the backward
-    // also the K~ rows and (Gam q)^T): written by waves 1.. while wave 0 runs
-    // the diagonal solve of the inverse
-    auto gate_outputs = [&](int t0, int nt) {
-      // Kt_e[d][s] = e^{gamma_last - gamma_s} k_s[d]  (s < len), 0 past len
+      pV.template store_t<E>(&sm.Vt[0][0], S::LDCE);  // V^T
+      if (gi + 1 < a.G) load_head(tok0, len, h + 1);
+      else if (nent.x >= 0) load_item(nent, next % a.Hk);  // in flight during this v-head
+      __syncthreads();
+
+      // P = lower_incl(D * Q K^T) (fp32 to workspace), A = strict_lower(beta_r D * K K^T)
       {
-        E* Kg = (E*)a.Kt + slot * D * C;
-        const float glast = sm.gam[len - 1];
-        for (int e = t0; e < D * (C / V); e += nt) {
-          const int d = e / (C / V), s0 = (e % (C / V)) * V;
-          float val[V], lo[V];
+        float* Pg = a.P + slot * C * C;
+        for (int t = w; t < NT * NT; t += NW) {
+          const int rt = t / NT, ct = t % NT;
+          const f32x4 acc = mm_tile<E, D>(zero4(), &sm.Qs[rt * 16][0], S::LDQ, &sm.Ks[ct * 16][0], S::LDQ);
+          f32x4 pv;
 #pragma unroll
-          for (int i = 0; i < V; ++i) {
-            const int s = s0 + i;
-            val[i] = (s < len) ? to_f<E>(sm.Kt[d][s]) * __expf(glast - sm.gam[s]) : 0.f;
-            lo[i] = val[i] - to_f<E>(from_f<E>(val[i]));
+          for (int e = 0; e < 4; ++e) {
+            const int r = rt * 16 + acc_row(e), s = ct * 16 + acc_col();
+            const float dd = (s <= r) ? __expf(sm.gam[r] - sm.gam[s]) : 0.f;
+            pv[e] = (r < len) ? dd * acc[e] : 0.f;
+            sm.Am[r][s] = (s < r) ? sm.beta[r] * dd * sm.Sk[r][s] : 0.f;
           }
-          Vec<E>::store(Kg + d * C + s0, val);
-          if constexpr (Split<E>::on) Vec<E>::store((E*)a.Ktl + slot * D * C + d * C + s0, lo);
+          store_tile<float>(Pg, C, rt * 16, ct * 16, pv, C);
+          if constexpr (LO_OUT) store_tile_t(a.Ptr + slot * C * C, C, rt * 16, ct * 16, pv);
         }
-        if constexpr (LO_OUT) {
-          // rows e_s k_s [C][D] and (Gam_r q_r)^T [D][C], hi / lo, for the reverse state pass
-          for (int e = t0; e < C * (D / V); e += nt) {
-            const int s = e / (D / V), c0 = (e % (D / V)) * V;
-            const float es = (s < len) ? __expf(glast - sm.gam[s]) : 0.f;
+      }
+      __syncthreads();
+      // Outputs that need only gamma, K and Q (K~^T hi / lo; for the backward
+      // also the K~ rows and (Gam q)^T): written by waves 1.. while wave 0 runs
+      // the diagonal solve of the inverse
+      auto gate_outputs = [&](int t0, int nt) {
+        // Kt_e[d][s] = e^{gamma_last - gamma_s} k_s[d]  (s < len), 0 past len
+        {
+          E* Kg = (E*)a.Kt + slot * D * C;
+          const float glast = sm.gam[len - 1];
+          for (int e = t0; e < D * (C / V); e += nt) {
+            const int d = e / (C / V), s0 = (e % (C / V)) * V;
             float val[V], lo[V];
 #pragma unroll
             for (int i = 0; i < V; ++i) {
-              val[i] = es * to_f<E>(sm.Ks[s][c0 + i]);
+              const int s = s0 + i;
+              val[i] = (s < len) ? to_f<E>(sm.Kt[d][s]) * __expf(glast - sm.gam[s]) : 0.f;
               lo[i] = val[i] - to_f<E>(from_f<E>(val[i]));
             }
-            const int64_t o = slot * C * D + (int64_t)s * D + c0;
-            Vec<E>::store((E*)a.Krh + o, val);
-            if constexpr (Split<E>::on) Vec<E>::store((E*)a.Krl + o, lo);
+            Vec<E>::store(Kg + d * C + s0, val);
+            if constexpr (Split<E>::on) Vec<E>::store((E*)a.Ktl + slot * D * C + d * C + s0, lo);
           }
-          // Q^T through V x V register blocks: a thread reads V rows of V
-          // consecutive d and writes V rows of Q^T; adjacent lanes take adjacent
-          // d blocks (conflict-free LDS reads), and the C / V lanes sharing a d
-          // block write whole rows of Q^T
-          constexpr int DB = D / V, SB = C / V, DF = DB >= 8 ? 8 : DB;
-          for (int e = t0; e < DB * SB; e += nt) {
-            const int d0 = (e % DF + DF * (e / (DF * SB))) * V, s0 = ((e / DF) % SB) * V;
-            float blk[V][V], gs[V];
-#pragma unroll
-            for (int i = 0; i < V; ++i) {
-              Vec<E>::load(&sm.Qs[s0 + i][d0], blk[i]);
-              gs[i] = __expf(sm.gam[s0 + i]);
-            }
-#pragma unroll
-            for (int dd = 0; dd < V; ++dd) {
+          if constexpr (LO_OUT) {
+            // rows e_s k_s [C][D] and (Gam_r q_r)^T [D][C], hi / lo, for the reverse state pass
+            for (int e = t0; e < C * (D / V); e += nt) {
+              const int s = e / (D / V), c0 = (e % (D / V)) * V;
+              const float es = (s < len) ? __expf(glast - sm.gam[s]) : 0.f;
               float val[V], lo[V];
 #pragma unroll
               for (int i = 0; i < V; ++i) {
-                val[i] = gs[i] * blk[i][dd];
+                val[i] = es * to_f<E>(sm.Ks[s][c0 + i]);
                 lo[i] = val[i] - to_f<E>(from_f<E>(val[i]));
               }
-              const int64_t o = slot * D * C + (int64_t)(d0 + dd) * C + s0;
-              Vec<E>::store((E*)a.Qth + o, val);
-              if constexpr (Split<E>::on) Vec<E>::store((E*)a.Qtl + o, lo);
+              const int64_t o = slot * C * D + (int64_t)s * D + c0;
+              Vec<E>::store((E*)a.Krh + o, val);
+              if constexpr (Split<E>::on) Vec<E>::store((E*)a.Krl + o, lo);
+            }
+            // Q^T through V x V register blocks: a thread reads V rows of V
+            // consecutive d and writes V rows of Q^T; adjacent lanes take adjacent
+            // d blocks (conflict-free LDS reads), and the C / V lanes sharing a d
+            // block write whole rows of Q^T
+            constexpr int DB = D / V, SB = C / V, DF = DB >= 8 ? 8 : DB;
+            for (int e = t0; e < DB * SB; e += nt) {
+              const int d0 = (e % DF + DF * (e / (DF * SB))) * V, s0 = ((e / DF) % SB) * V;
+              float blk[V][V], gs[V];
+#pragma unroll
+              for (int i = 0; i < V; ++i) {
+                Vec<E>::load(&sm.Qs[s0 + i][d0], blk[i]);
+                gs[i] = __expf(sm.gam[s0 + i]);
+              }
+#pragma unroll
+              for (int dd = 0; dd < V; ++dd) {
+                float val[V], lo[V];
+#pragma unroll
+                for (int i = 0; i < V; ++i) {
+                  val[i] = gs[i] * blk[i][dd];
+                  lo[i] = val[i] - to_f<E>(from_f<E>(val[i]));
+                }
+                const int64_t o = slot * D * C + (int64_t)(d0 + dd) * C + s0;
+                Vec<E>::store((E*)a.Qth + o, val);
+                if constexpr (Split<E>::on) Vec<E>::store((E*)a.Qtl + o, lo);
+              }
             }
           }
         }
-      }
-    };
-    unit_lower_inverse<C, S::LDCF, NTH>(sm.Am, sm.Tm, sm.Tt, sm.Xs, gate_outputs);  // starts and ends with a barrier
-    if constexpr (LO_OUT) {  // T for the WY gradients
-      for (int e = tid; e < C * (C / 4); e += NTH) {
-        const int r = e / (C / 4), c = (e % (C / 4)) * 4;
-        *reinterpret_cast<float4*>(a.Tw + slot * C * C + r * C + c) = *reinterpret_cast<const float4*>(&sm.Tm[r][c]);
-      }
-    }
-
-    // U = (T diag(beta)) V, the left factor split into hi + lo bf16 parts; fp32 result
-    for (int e = tid; e < C * C; e += NTH) {
-      const int r = e / C, s = e % C;
-      split_store<E>(&sm.TB[r][s], &sm.TBl[0][0] + r * S::LDCE + s, sm.Tm[r][s] * sm.beta[s]);
-    }
-    __syncthreads();
-    {
-      float* Ug = a.U + slot * C * D;
-      for (int t = w; t < NT * ND; t += NW) {
-        const int rt = t / ND, ct = t % ND;
-        f32x4 acc = mm_tile<E, C>(zero4(), &sm.TB[rt * 16][0], S::LDCE, &sm.Vt[ct * 16][0], S::LDCE);
-        if constexpr (Split<E>::on)
-          acc = mm_tile<E, C>(acc, &sm.TBl[rt * 16][0], S::LDCE, &sm.Vt[ct * 16][0], S::LDCE);
-        store_tile<float>(Ug, D, rt * 16, ct * 16, acc, C);
-      }
-    }
-    __syncthreads();
-    // Wk = (T diag(beta Gam)) K
-    for (int e = tid; e < C * C; e += NTH) {
-      const int r = e / C, s = e % C;
-      split_store<E>(&sm.TB[r][s], &sm.TBl[0][0] + r * S::LDCE + s, sm.Tm[r][s] * sm.beta[s] * __expf(sm.gam[s]));
-    }
-    __syncthreads();
-    {
-      E* Wg = (E*)a.Wk + slot * C * D;
-      for (int t = w; t < NT * ND; t += NW) {
-        const int rt = t / ND, ct = t % ND;
-        f32x4 acc = mm_tile<E, C>(zero4(), &sm.TB[rt * 16][0], S::LDCE, &sm.Kt[ct * 16][0], S::LDCE);
-        if constexpr (Split<E>::on)
-          acc = mm_tile<E, C>(acc, &sm.TBl[rt * 16][0], S::LDCE, &sm.Kt[ct * 16][0], S::LDCE);
-        store_tile<E>(Wg, D, rt * 16, ct * 16, acc, C);
-        if constexpr (LO_OUT) {  // Wk^T [D][C], hi / lo
-          const int64_t o = slot * D * C + (int64_t)(ct * 16 + acc_col()) * C + rt * 16 + acc_row(0);
-          st4_split<E>((E*)a.Wth + o, (E*)a.Wtl + o, acc);
+      };
+      unit_lower_inverse<C, S::LDCF, NTH>(sm.Am, sm.Tm, sm.Tt, sm.Xs, gate_outputs);  // starts and ends with a barrier
+      if constexpr (LO_OUT) {  // T for the WY gradients
+        for (int e = tid; e < C * (C / 4); e += NTH) {
+          const int r = e / (C / 4), c = (e % (C / 4)) * 4;
+          *reinterpret_cast<float4*>(a.Tw + slot * C * C + r * C + c) = *reinterpret_cast<const float4*>(&sm.Tm[r][c]);
         }
       }
+
+      // U = (T diag(beta)) V, the left factor split into hi + lo bf16 parts; fp32 result
+      for (int e = tid; e < C * C; e += NTH) {
+        const int r = e / C, s = e % C;
+        split_store<E>(&sm.TB[r][s], &sm.TBl[0][0] + r * S::LDCE + s, sm.Tm[r][s] * sm.beta[s]);
+      }
+      __syncthreads();
+      {
+        float* Ug = a.U + slot * C * D;
+        for (int t = w; t < NT * ND; t += NW) {
+          const int rt = t / ND, ct = t % ND;
+          f32x4 acc = mm_tile<E, C>(zero4(), &sm.TB[rt * 16][0], S::LDCE, &sm.Vt[ct * 16][0], S::LDCE);
+          if constexpr (Split<E>::on)
+            acc = mm_tile<E, C>(acc, &sm.TBl[rt * 16][0], S::LDCE, &sm.Vt[ct * 16][0], S::LDCE);
+          store_tile<float>(Ug, D, rt * 16, ct * 16, acc, C);
+        }
+      }
+      __syncthreads();
+      // Wk = (T diag(beta Gam)) K
+      for (int e = tid; e < C * C; e += NTH) {
+        const int r = e / C, s = e % C;
+        split_store<E>(&sm.TB[r][s], &sm.TBl[0][0] + r * S::LDCE + s, sm.Tm[r][s] * sm.beta[s] * __expf(sm.gam[s]));
+      }
+      __syncthreads();
+      {
+        E* Wg = (E*)a.Wk + slot * C * D;
+        for (int t = w; t < NT * ND; t += NW) {
+          const int rt = t / ND, ct = t % ND;
+          f32x4 acc = mm_tile<E, C>(zero4(), &sm.TB[rt * 16][0], S::LDCE, &sm.Kt[ct * 16][0], S::LDCE);
+          if constexpr (Split<E>::on)
+            acc = mm_tile<E, C>(acc, &sm.TBl[rt * 16][0], S::LDCE, &sm.Kt[ct * 16][0], S::LDCE);
+          store_tile<E>(Wg, D, rt * 16, ct * 16, acc, C);
+          if constexpr (LO_OUT) {  // Wk^T [D][C], hi / lo
+            const int64_t o = slot * D * C + (int64_t)(ct * 16 + acc_col()) * C + rt * 16 + acc_row(0);
+            st4_split<E>((E*)a.Wth + o, (E*)a.Wtl + o, acc);
+          }
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
+    item = next;
+    ent = nent;
   }
 }
 
@@ -506,7 +517,16 @@ void launch_chunk_fwd_core(const ChunkArgs& a, hipStream_t st, int mode) {
   constexpr int DVT = state_dvt<E, D>();
   static const char* prep_name[4] = {"", "chunk_prep", "chunk_prep_bwd", "chunk_prep_save"};
   static const char* state_name[4] = {"", "chunk_state_fwd", "chunk_state_store", "chunk_state_save"};
-  dim3 gprep(a.max_chunks, a.Hk);
+  // Inference preparation runs persistent: as many workgroups as fit at once
+  // (its LDS use allows one per CU at d = 128, chunk 64), each walking its
+  // share of items with the next one's loads in flight (long 65536: 1.69 ->
+  // 1.60 ms; varlen: 0.87 -> 0.83 ms).  The variants that also write the
+  // backward's operands are write-bound and measured slower that way (2.18 ->
+  // 2.29 ms at the training workload): one item per workgroup there.
+  constexpr int per_cu = (160 * 1024) / (int)sizeof(PrepSmem<E, D, C>) >= 2 ? 2 : 1;
+  const int64_t items = (int64_t)a.max_chunks * a.Hk;
+  const int64_t resident = (int64_t)kNumCUs * per_cu;
+  dim3 gprep((unsigned)(mode == kFwdOut && items > resident ? resident : items));
   {
     GDN_PROF(prep_name[mode], st);
     constexpr int NTH = D >= 64 ? 512 : kChunkThreads;  // 8 waves for the wide heads
