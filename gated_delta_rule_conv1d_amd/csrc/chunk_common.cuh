@@ -334,16 +334,21 @@ struct TileRegs {
       c = (e % PER_ROW) * V;
     }
   }
+  // Buffer loads through a resource that covers rows [0, rows_valid): pieces
+  // past it (and past the tile) read as zero in hardware, so every load issues
+  // at once.  (Loads under a per-piece branch were each followed by a full wait
+  // for the vector-memory counter: the compiler drains it at the branch join.)
   __device__ __forceinline__ void load(const T* g, int64_t ld, int rows_valid) {
+    const int64_t bytes = (int64_t)rows_valid * ld * (int64_t)sizeof(T);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(g), 0, (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff), 0x00020000);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int e = threadIdx.x + i * NTH;
-      r[i] = make_uint4(0, 0, 0, 0);
-      if (e < TOTAL) {
-        int row, c;
-        pos(e, row, c);
-        if (row < rows_valid) r[i] = *reinterpret_cast<const uint4*>(g + (int64_t)row * ld + c);
-      }
+      int row, c;
+      pos(e, row, c);
+      const int off = e < TOTAL ? (int)(((int64_t)row * ld + c) * (int64_t)sizeof(T)) : 0x7fffffe0;
+      r[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
     }
   }
   __device__ __forceinline__ void store(T* s, int lds) const {

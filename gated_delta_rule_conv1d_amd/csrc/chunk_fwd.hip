@@ -151,17 +151,32 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
         float* Pg = a.P + slot * C * C;
         for (int t = w; t < NT * NT; t += NW) {
           const int rt = t / NT, ct = t % NT;
-          const f32x4 acc = mm_tile<E, D>(zero4(), &sm.Qs[rt * 16][0], S::LDQ, &sm.Ks[ct * 16][0], S::LDQ);
-          f32x4 pv;
+          if constexpr (LO_OUT) {  // P tiles: P^T also leaves, as 4-element runs
+            const f32x4 acc = mm_tile<E, D>(zero4(), &sm.Qs[rt * 16][0], S::LDQ, &sm.Ks[ct * 16][0], S::LDQ);
+            f32x4 pv;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = rt * 16 + acc_row(e), s = ct * 16 + acc_col();
-            const float dd = (s <= r) ? __expf(sm.gam[r] - sm.gam[s]) : 0.f;
-            pv[e] = (r < len) ? dd * acc[e] : 0.f;
-            sm.Am[r][s] = (s < r) ? sm.beta[r] * dd * sm.Sk[r][s] : 0.f;
+            for (int e = 0; e < 4; ++e) {
+              const int r = rt * 16 + acc_row(e), s = ct * 16 + acc_col();
+              const float dd = (s <= r) ? __expf(sm.gam[r] - sm.gam[s]) : 0.f;
+              pv[e] = (r < len) ? dd * acc[e] : 0.f;
+              sm.Am[r][s] = (s < r) ? sm.beta[r] * dd * sm.Sk[r][s] : 0.f;
+            }
+            store_tile<float>(Pg, C, rt * 16, ct * 16, pv, C);
+            store_tile_t(a.Ptr + slot * C * C, C, rt * 16, ct * 16, pv);
+          } else {  // P^T = K Q^T tiles: a lane holds P[r][s..s+3] (one 16-byte store) and the same piece of A
+            const f32x4 acc = mm_tile<E, D>(zero4(), &sm.Ks[ct * 16][0], S::LDQ, &sm.Qs[rt * 16][0], S::LDQ);
+            const int r = rt * 16 + acc_col(), s0 = ct * 16 + acc_row(0);
+            f32x4 pv, av;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int s = s0 + e;
+              const float dd = (s <= r) ? __expf(sm.gam[r] - sm.gam[s]) : 0.f;
+              pv[e] = (r < len) ? dd * acc[e] : 0.f;
+              av[e] = (s < r) ? sm.beta[r] * dd * sm.Sk[r][s] : 0.f;
+            }
+            *reinterpret_cast<float4*>(&sm.Am[r][s0]) = make_float4(av[0], av[1], av[2], av[3]);
+            st4<float>(Pg + (int64_t)r * C + s0, pv);
           }
-          store_tile<float>(Pg, C, rt * 16, ct * 16, pv, C);
-          if constexpr (LO_OUT) store_tile_t(a.Ptr + slot * C * C, C, rt * 16, ct * 16, pv);
         }
       }
       __syncthreads();
@@ -244,13 +259,15 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
       }
       __syncthreads();
       {
+        // formed as U^T = V^T (T diag(beta))^T tiles: a lane then holds 4
+        // consecutive d of one row of U, stored as one 16-byte write
         float* Ug = a.U + slot * C * D;
         for (int t = w; t < NT * ND; t += NW) {
-          const int rt = t / ND, ct = t % ND;
-          f32x4 acc = mm_tile<E, C>(zero4(), &sm.TB[rt * 16][0], S::LDCE, &sm.Vt[ct * 16][0], S::LDCE);
+          const int dt = t / NT, rt = t % NT;
+          f32x4 acc = mm_tile<E, C>(zero4(), &sm.Vt[dt * 16][0], S::LDCE, &sm.TB[rt * 16][0], S::LDCE);
           if constexpr (Split<E>::on)
-            acc = mm_tile<E, C>(acc, &sm.TBl[rt * 16][0], S::LDCE, &sm.Vt[ct * 16][0], S::LDCE);
-          store_tile<float>(Ug, D, rt * 16, ct * 16, acc, C);
+            acc = mm_tile<E, C>(acc, &sm.Vt[dt * 16][0], S::LDCE, &sm.TBl[rt * 16][0], S::LDCE);
+          st4<float>(Ug + (int64_t)(rt * 16 + acc_col()) * D + dt * 16 + acc_row(0), acc);
         }
       }
       __syncthreads();
@@ -263,14 +280,20 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
       {
         E* Wg = (E*)a.Wk + slot * C * D;
         for (int t = w; t < NT * ND; t += NW) {
-          const int rt = t / ND, ct = t % ND;
-          f32x4 acc = mm_tile<E, C>(zero4(), &sm.TB[rt * 16][0], S::LDCE, &sm.Kt[ct * 16][0], S::LDCE);
-          if constexpr (Split<E>::on)
-            acc = mm_tile<E, C>(acc, &sm.TBl[rt * 16][0], S::LDCE, &sm.Kt[ct * 16][0], S::LDCE);
-          store_tile<E>(Wg, D, rt * 16, ct * 16, acc, C);
-          if constexpr (LO_OUT) {  // Wk^T [D][C], hi / lo
+          if constexpr (LO_OUT) {  // Wk tiles: Wk^T [D][C] (hi / lo) leaves as 4-element runs
+            const int rt = t / ND, ct = t % ND;
+            f32x4 acc = mm_tile<E, C>(zero4(), &sm.TB[rt * 16][0], S::LDCE, &sm.Kt[ct * 16][0], S::LDCE);
+            if constexpr (Split<E>::on)
+              acc = mm_tile<E, C>(acc, &sm.TBl[rt * 16][0], S::LDCE, &sm.Kt[ct * 16][0], S::LDCE);
+            store_tile<E>(Wg, D, rt * 16, ct * 16, acc, C);
             const int64_t o = slot * D * C + (int64_t)(ct * 16 + acc_col()) * C + rt * 16 + acc_row(0);
             st4_split<E>((E*)a.Wth + o, (E*)a.Wtl + o, acc);
+          } else {  // Wk^T = K^T (T diag(beta Gam))^T tiles: 4 consecutive d of a Wk row per lane
+            const int dt = t / NT, rt = t % NT;
+            f32x4 acc = mm_tile<E, C>(zero4(), &sm.Kt[dt * 16][0], S::LDCE, &sm.TB[rt * 16][0], S::LDCE);
+            if constexpr (Split<E>::on)
+              acc = mm_tile<E, C>(acc, &sm.Kt[dt * 16][0], S::LDCE, &sm.TBl[rt * 16][0], S::LDCE);
+            st4<E>(Wg + (int64_t)(rt * 16 + acc_col()) * D + dt * 16 + acc_row(0), acc);
           }
         }
       }
