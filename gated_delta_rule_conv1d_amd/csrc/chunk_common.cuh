@@ -316,7 +316,7 @@ struct StateSmem {
 // writes 16 consecutive elements of a transposed row per lane group instead of
 // one element each of 16 rows a 16-byte piece apart (which fall in the same
 // LDS banks), at the price of 64-byte instead of 256-byte runs per global load.
-template <typename T, int R, int COLS, int NTH = kChunkThreads, bool RF = false>
+template <typename T, int R, int COLS, int NTH = kChunkThreads, bool RF = false, bool BUF = true>
 struct TileRegs {
   static constexpr int V = 16 / (int)sizeof(T);
   static constexpr int PER_ROW = COLS / V;
@@ -339,6 +339,10 @@ struct TileRegs {
   // at once.  (Loads under a per-piece branch were each followed by a full wait
   // for the vector-memory counter: the compiler drains it at the branch join.)
   __device__ __forceinline__ void load(const T* g, int64_t ld, int rows_valid) {
+    if constexpr (!BUF) {
+      load_each(g, ld, rows_valid);
+      return;
+    }
     const int64_t bytes = (int64_t)rows_valid * ld * (int64_t)sizeof(T);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<T*>(g), 0, (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff), 0x00020000);
@@ -349,6 +353,22 @@ struct TileRegs {
       pos(e, row, c);
       const int off = e < TOTAL ? (int)(((int64_t)row * ld + c) * (int64_t)sizeof(T)) : 0x7fffffe0;
       r[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    }
+  }
+  // One guarded load per piece, each completed before the next is issued.
+  // The tiled state pass (whose next-chunk prefetch competes with its own
+  // serial chunk step) measured faster this way at a single 65536-token
+  // sequence: 3.06 against 3.21 ms.
+  __device__ __forceinline__ void load_each(const T* g, int64_t ld, int rows_valid) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int e = threadIdx.x + i * NTH;
+      r[i] = make_uint4(0, 0, 0, 0);
+      if (e < TOTAL) {
+        int row, c;
+        pos(e, row, c);
+        if (row < rows_valid) r[i] = *reinterpret_cast<const uint4*>(g + (int64_t)row * ld + c);
+      }
     }
   }
   __device__ __forceinline__ void store(T* s, int lds) const {

@@ -357,14 +357,15 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
     }
   };
 
-  // next chunk's tiles, staged in registers
-  TileRegs<E, C, D> pWk;
-  TileRegs<E, D, C> pKt;
-  TileRegs<E, LO ? D : 1, LO ? C : 16 / (int)sizeof(E)> pKtl;
-  TileRegs<E, OUT ? C : 16, OUT ? D : 16 / (int)sizeof(E)> pQ;
-  TileRegs<float, OUT ? C : 1, OUT ? C : 4> pP;
-  TileRegs<float, C, DVT> pU;
-  TileRegs<float, 1, C> pG;
+  // next chunk's tiles, staged in registers (guarded loads: see TileRegs::load_each)
+  constexpr int TN = kChunkThreads;
+  TileRegs<E, C, D, TN, false, false> pWk;
+  TileRegs<E, D, C, TN, false, false> pKt;
+  TileRegs<E, LO ? D : 1, LO ? C : 16 / (int)sizeof(E), TN, false, false> pKtl;
+  TileRegs<E, OUT ? C : 16, OUT ? D : 16 / (int)sizeof(E), TN, false, false> pQ;
+  TileRegs<float, OUT ? C : 1, OUT ? C : 4, TN, false, false> pP;
+  TileRegs<float, C, DVT, TN, false, false> pU;
+  TileRegs<float, 1, C, TN, false, false> pG;
   int ptok = 0, plen = 0;
   auto prefetch = [&](int ci) {
     const int4 ent = chunk_entry(a.table, ci);
