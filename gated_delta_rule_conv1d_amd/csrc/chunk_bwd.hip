@@ -253,6 +253,10 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
   E* Xlo = LO ? &sm.Xl[0][0] : nullptr;
   E* Kst = S::K_IN_HL ? &sm.Hl[0][0] : &sm.Ks[0][0];
 
+  // dHn (read after (a)) and K (for (c)) are requested with the first tiles
+  using DRegs = TileRegs<float, D, D, NTH>;
+  DRegs rD;
+  TileRegs<E, C, D, NTH> rK;
   {  // stage Hc, dO, dW, V
     TileRegs<float, D, D, NTH> rH;
     TileRegs<E, C, D, NTH> rO, rV;
@@ -261,6 +265,8 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
     rO.load(dog, ldo, len);
     rW.load(a.dW + slot * C * D, D, C);
     rV.load((const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)h * D, a.sv, len);
+    rD.load(dHn, D, D);
+    rK.load((const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D, a.sqk, len);
     rH.template store_split<E>(&sm.Hh[0][0], Hlo, S::LDQ);
     rO.store(&sm.Od[0][0], S::LDQ);
     rW.template store_split<E>(&sm.Xh[0][0], Xlo, S::LDQ);
@@ -307,14 +313,8 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
   }
   __syncthreads();  // dO and V are no longer read
 
-  // dHn is read now, in flight during (b); <Hc, dHn> is then formed from the
-  // staged parts of Hc (hi + lo, exact in fp32 mode) before they are
-  // overwritten, so Hc is read from HBM once
-  using DRegs = TileRegs<float, D, D, NTH>;
-  DRegs rD;
-  rD.load(dHn, D, D);
-  TileRegs<E, C, D, NTH> rK;  // K rows for (c), also in flight during (b)
-  rK.load((const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D, a.sqk, len);
+  // <Hc, dHn> is formed from the staged parts of Hc (hi + lo, exact in fp32
+  // mode) before they are overwritten, so Hc is read from HBM once
 
   // (b) dWk = -dW Hc^T: hi -> Os, lo -> Vs; transposed fp32 copy to workspace
   for_blocks<NT, ND, RT, CD, NW>([&](int r0, int c0) {
@@ -388,10 +388,11 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
   rD.template store_split<E>(&sm.Hh[0][0], Hlo, S::LDQ);
   rW2.template store_split<E>(&sm.Xh[0][0], Xlo, S::LDQ);
   __syncthreads();
-  if (tid == 0) {
+  if (wave_id() == 0) {  // <Hc, dHn>: the per-thread partials summed lane-strided, then across the wave
     float s = 0.f;
-    for (int i = 0; i < NTH; ++i) s += sm.red[i];
-    a.hdot[slot] = s;
+    for (int i = lane_id(); i < NTH; i += kWave) s += sm.red[i];
+    s = wave_sum(s);
+    if (lane_id() == 0) a.hdot[slot] = s;
   }
   // (d) dKh = e W dHn^T (as dKh^T tiles [D][C]);  dP = scale dO W^T
   for_blocks<ND, NT, CD, RT, NW>([&](int d0, int r0) {
