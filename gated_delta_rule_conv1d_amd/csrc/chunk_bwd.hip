@@ -272,11 +272,14 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
     rW.template store_split<E>(&sm.Xh[0][0], Xlo, S::LDQ);
     rV.store(&sm.Vs[0][0], S::LDQ);
   }
-  for (int e = tid; e < C; e += NTH) {
+  if (tid < C) {  // per-row gates; every load unconditional (clamped rows), so they issue together
+    const int e = tid;
     const float g = a.gam[slot * C + e];
-    sm.bs[e] = e < len ? a.beta[(int64_t)(tok0 + e) * a.Hv + h] : 0.f;
+    const float gl = a.gam[slot * C + len - 1];
+    const float bt = a.beta[(int64_t)(tok0 + min(e, len - 1)) * a.Hv + h];
+    sm.bs[e] = e < len ? bt : 0.f;
     sm.gm[e] = __expf(g);
-    sm.em[e] = e < len ? __expf(a.gam[slot * C + len - 1] - g) : 0.f;
+    sm.em[e] = e < len ? __expf(gl - g) : 0.f;
   }
   __syncthreads();
 
@@ -555,14 +558,18 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
     pTm.load(a.Tw + slot * C * C, C, C);
     rXu.load(a.dWt + slot * D * C, C, D);
     rXw.load(a.dWkt + slot * D * C, C, D);
-    for (int e = tid; e < C; e += NTH) {
+    if (tid < C) {  // per-row gates; every load unconditional (clamped rows), so they issue together
+      const int e = tid;
       const float gm = a.gam[slot * C + e];
+      const float gl = a.gam[slot * C + len - 1];
+      const float bt = a.beta[(int64_t)(tok0 + min(e, len - 1)) * a.Hv + h];
+      const float hd = a.hdot[slot];  // used by the row pass at the end
       sm.gam[e] = gm;
       sm.Gm[e] = __expf(gm);
-      sm.beta[e] = e < len ? a.beta[(int64_t)(tok0 + e) * a.Hv + h] : 0.f;
-      sm.em[e] = e < len ? __expf(a.gam[slot * C + len - 1] - gm) : 0.f;
+      sm.beta[e] = e < len ? bt : 0.f;
+      sm.em[e] = e < len ? __expf(gl - gm) : 0.f;
+      if (e == 0) sm.hdot = hd;
     }
-    if (tid == 0) sm.hdot = a.hdot[slot];  // read now, used by the row pass at the end
     pTm.store(&sm.Tm[0][0], S::LDCF);
     // fp32 operands of the products below are split into their MFMA parts once
     // here, not per tile

@@ -178,23 +178,34 @@ __device__ __forceinline__ void g2s(E* s, int lds, const E* g) {
 // s[c * lds + r] = g[r * ld + c]; zero past len.  Rows first: 16 adjacent lanes
 // read the same columns of 16 adjacent rows, so each transposed write puts 16
 // consecutive elements of one LDS row down (no bank conflicts between them).
+// Buffer loads over rows [0, len) (zero past it), all issued before the
+// first write.
 template <typename E, int R, int Ccols, int NTH = kChunkThreads>
 __device__ __forceinline__ void rows2s_t(E* s, int lds, const E* g, int64_t ld, int len) {
   constexpr int V = Vec<E>::N;
   constexpr int PER_ROW = Ccols / V;
+  constexpr int NP = (R * PER_ROW + NTH - 1) / NTH;  // 16-byte pieces per thread
   static_assert(R % 16 == 0, "rows in groups of 16");
-  for (int e = threadIdx.x; e < R * PER_ROW; e += NTH) {
-    const int grp = e >> 4;
+  const int64_t bytes = (int64_t)len * ld * (int64_t)sizeof(E);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<E*>(g), 0, (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff), 0x00020000);
+  uint4 raw[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int e = threadIdx.x + i * NTH, grp = e >> 4;
     const int r = (grp / PER_ROW) * 16 + (e & 15), c = (grp % PER_ROW) * V;
-    float val[V];
-    if (r < len) {
-      Vec<E>::load(g + (int64_t)r * ld + c, val);
-    } else {
+    const int off = e < R * PER_ROW ? (int)(((int64_t)r * ld + c) * (int64_t)sizeof(E)) : 0x7fffffe0;
+    raw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+  }
 #pragma unroll
-      for (int i = 0; i < V; ++i) val[i] = 0.f;
+  for (int i = 0; i < NP; ++i) {
+    const int e = threadIdx.x + i * NTH, grp = e >> 4;
+    if (e < R * PER_ROW) {
+      const int r = (grp / PER_ROW) * 16 + (e & 15), c = (grp % PER_ROW) * V;
+      const E* v = reinterpret_cast<const E*>(&raw[i]);
+#pragma unroll
+      for (int u = 0; u < V; ++u) s[(c + u) * lds + r] = v[u];
     }
-#pragma unroll
-    for (int i = 0; i < V; ++i) s[(c + i) * lds + r] = from_f<E>(val[i]);
   }
 }
 
