@@ -101,10 +101,13 @@ __global__ __launch_bounds__(kChunkThreads) void state_bwd_kernel(ChunkArgs a) {
   TileRegs<E, D, C> pWh, pWl, pQh, pQl;
   ColRegs<E, C, DVT> pO;
   TileRegs<float, 1, C> pG;
+  // (first token, length) of chunk ci from cu_seqlens: no table load in front of the dO load
+  const int c0 = a.seq_chunk0[n], c1 = a.seq_chunk0[n + 1];
+  const int s0 = a.cu[n], s1 = a.cu[n + 1];
   int plen = 0;
   auto prefetch = [&](int ci) {
-    const int4 ent = chunk_entry(a.table, ci);
-    plen = ent.z;
+    const int tok0 = s0 + (ci - c0) * C;
+    plen = min(C, s1 - tok0);
     const int64_t slot = (int64_t)ci * a.Hv + h;
     pP.load(a.Ptr + slot * C * C, C, C);
     pKh.load((const E*)a.Krh + slot * C * D, D, C);
@@ -115,11 +118,10 @@ __global__ __launch_bounds__(kChunkThreads) void state_bwd_kernel(ChunkArgs a) {
       pWl.load((const E*)a.Wtl + slot * D * C, C, D);
       pQl.load((const E*)a.Qtl + slot * D * C, C, D);
     }
-    pO.load((const E*)a.d_o + (int64_t)ent.y * a.Hv * D + (int64_t)h * D + col0, (int64_t)a.Hv * D, plen);
+    pO.load((const E*)a.d_o + (int64_t)tok0 * a.Hv * D + (int64_t)h * D + col0, (int64_t)a.Hv * D, plen);
     pG.load(a.gam + slot * C, C, 1);
   };
 
-  const int c0 = a.seq_chunk0[n], c1 = a.seq_chunk0[n + 1];
   if (c0 < c1) prefetch(c1 - 1);
   write_dHt();
   for (int ci = c1 - 1; ci >= c0; --ci) {

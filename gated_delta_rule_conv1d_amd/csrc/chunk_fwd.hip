@@ -366,11 +366,14 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
   TileRegs<float, OUT ? C : 1, OUT ? C : 4, TN, false, false> pP;
   TileRegs<float, C, DVT, TN, false, false> pU;
   TileRegs<float, 1, C, TN, false, false> pG;
+  // the sequence's chunks are consecutive table entries: (first token, length)
+  // follow from cu_seqlens, so no table load sits in front of the Q load
+  const int c0 = a.seq_chunk0[n], c1 = a.seq_chunk0[n + 1];
+  const int s0 = a.cu[n], s1 = a.cu[n + 1];
   int ptok = 0, plen = 0;
   auto prefetch = [&](int ci) {
-    const int4 ent = chunk_entry(a.table, ci);
-    ptok = ent.y;
-    plen = ent.z;
+    ptok = s0 + (ci - c0) * C;
+    plen = min(C, s1 - ptok);
     const int64_t slot = (int64_t)ci * a.Hv + h;
     pWk.load((const E*)a.Wk + slot * C * D, D, C);
     pKt.load((const E*)a.Kt + slot * D * C, C, D);
@@ -383,7 +386,6 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
     pG.load(a.gam + slot * C, C, 1);
   };
 
-  const int c0 = a.seq_chunk0[n], c1 = a.seq_chunk0[n + 1];
   if (c0 < c1) prefetch(c0);
   write_Ht();
   for (int ci = c0; ci < c1; ++ci) {
