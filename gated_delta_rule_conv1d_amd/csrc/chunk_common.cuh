@@ -40,14 +40,15 @@ struct ChunkArgs {
   // sizes
   int N, T, Hk, Hv, G, max_chunks;
   float scale;
+  int kt_plain;  // the preparation writes Kt = k_s^T unscaled (for the 16-column state pass)
   // workspace
   const int32_t* table;       // [max_chunks][4]
   const int32_t* seq_chunk0;  // [N+1]
   void* Wk;                   // [slot][C][D]
   float* U;                   // [slot][C][D]
   float* P;                   // [slot][C][C]
-  void* Kt;                   // [slot][D][C]  (e_s k_s)^T, e_s = e^{gamma_last - gamma_s}
-  void* Ktl;                  //               its lo part (bf16 only)
+  void* Kt;                   // [slot][D][C]  (e_s k_s)^T, e_s = e^{gamma_last - gamma_s}; k_s^T with kt_plain
+  void* Ktl;                  //               its lo part (bf16 only; not written with kt_plain)
   // backward only: operands of the reverse state pass, transposed once per chunk
   float* Ptr;                 // [slot][C][C]  P^T
   float* Tw;                  // [slot][C][C]  T = (I + A)^-1 (for the WY gradients)
@@ -297,7 +298,10 @@ __device__ __forceinline__ void unit_lower_inverse(const float (*Am)[LDCF], floa
   }
 }
 
-template <typename E, int D, int C, int DVT, bool OUT>
+// KP: Kt holds the plain k_s^T (exact in bf16, no lo part) and the decay
+// e^{gamma_last - gamma_s} is applied to the rows of W instead (Ws, Wsl); with
+// OUT the unscaled W^T stays in Wt / Wtl for the output's P W.
+template <typename E, int D, int C, int DVT, bool OUT, bool KP = false>
 struct StateSmem {
   static constexpr int LDQ = D + Pad<E>::E16;
   static constexpr int LDCE = C + Pad<E>::E16;
@@ -306,13 +310,15 @@ struct StateSmem {
   E Wk[C][LDQ];
   E Q[OUT ? C : 1][LDQ];
   E Kt[D][LDCE];
-  E Ktl[LO ? D : 1][LDCE];
+  E Ktl[LO && !KP ? D : 1][LDCE];
   E P[OUT ? C : 1][LDCE];
   E Pl[OUT && LO ? C : 1][LDCE];
   E Ht[DVT][LDQ];
   E Htl[LO ? DVT : 1][LDQ];
   E Wt[DVT][LDCE];
   E Wtl[LO ? DVT : 1][LDCE];
+  E Ws[KP && OUT ? DVT : 1][LDCE];
+  E Wsl[KP && OUT && LO ? DVT : 1][LDCE];
   float U[C][LDU];
   float gam[C];
 };

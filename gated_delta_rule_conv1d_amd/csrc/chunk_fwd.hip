@@ -184,21 +184,25 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
       // also the K~ rows and (Gam q)^T): written by waves 1.. while wave 0 runs
       // the diagonal solve of the inverse
       auto gate_outputs = [&](int t0, int nt) {
-        // Kt_e[d][s] = e^{gamma_last - gamma_s} k_s[d]  (s < len), 0 past len
+        // Kt_e[d][s] = e^{gamma_last - gamma_s} k_s[d]  (s < len), 0 past len;
+        // with kt_plain the unscaled k_s[d] (exact: no lo part)
         {
           E* Kg = (E*)a.Kt + slot * D * C;
           const float glast = sm.gam[len - 1];
+          const bool plain = a.kt_plain;
           for (int e = t0; e < D * (C / V); e += nt) {
             const int d = e / (C / V), s0 = (e % (C / V)) * V;
             float val[V], lo[V];
 #pragma unroll
             for (int i = 0; i < V; ++i) {
               const int s = s0 + i;
-              val[i] = (s < len) ? to_f<E>(sm.Kt[d][s]) * __expf(glast - sm.gam[s]) : 0.f;
+              const float es = plain ? 1.f : __expf(glast - sm.gam[s]);
+              val[i] = (s < len) ? to_f<E>(sm.Kt[d][s]) * es : 0.f;
               lo[i] = val[i] - to_f<E>(from_f<E>(val[i]));
             }
             Vec<E>::store(Kg + d * C + s0, val);
-            if constexpr (Split<E>::on) Vec<E>::store((E*)a.Ktl + slot * D * C + d * C + s0, lo);
+            if constexpr (Split<E>::on)
+              if (!plain) Vec<E>::store((E*)a.Ktl + slot * D * C + d * C + s0, lo);
           }
           if constexpr (LO_OUT) {
             // rows e_s k_s [C][D] and (Gam_r q_r)^T [D][C], hi / lo, for the reverse state pass
@@ -314,12 +318,13 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
 //   OUT   = false: writes, per chunk, the entering state Hc and W (for the
 //                  backward pass), and the final state if asked
 // ---------------------------------------------------------------------------
-template <typename E, int D, int C, int DVT, int MODE>
+template <typename E, int D, int C, int DVT, int MODE, bool KP = false>
 __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
   constexpr bool OUT = MODE & kFwdOut, STORE = MODE & kFwdStore;
-  using S = StateSmem<E, D, C, DVT, OUT>;
+  using S = StateSmem<E, D, C, DVT, OUT, KP>;
   __shared__ S sm;
   constexpr bool LO = Split<E>::on;
+  constexpr bool KL = LO && !KP;  // Kt has a lo part
   constexpr int NVT = D / DVT;
   constexpr int NCT = DVT / 16;                 // column tiles
   constexpr int NHT = (D / 16) * NCT;           // state tiles
@@ -361,7 +366,7 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
   constexpr int TN = kChunkThreads;
   TileRegs<E, C, D, TN, false, false> pWk;
   TileRegs<E, D, C, TN, false, false> pKt;
-  TileRegs<E, LO ? D : 1, LO ? C : 16 / (int)sizeof(E), TN, false, false> pKtl;
+  TileRegs<E, KL ? D : 1, KL ? C : 16 / (int)sizeof(E), TN, false, false> pKtl;
   TileRegs<E, OUT ? C : 16, OUT ? D : 16 / (int)sizeof(E), TN, false, false> pQ;
   TileRegs<float, OUT ? C : 1, OUT ? C : 4, TN, false, false> pP;
   TileRegs<float, C, DVT, TN, false, false> pU;
@@ -377,7 +382,7 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
     const int64_t slot = (int64_t)ci * a.Hv + h;
     pWk.load((const E*)a.Wk + slot * C * D, D, C);
     pKt.load((const E*)a.Kt + slot * D * C, C, D);
-    if constexpr (LO) pKtl.load((const E*)a.Ktl + slot * D * C, C, D);
+    if constexpr (KL) pKtl.load((const E*)a.Ktl + slot * D * C, C, D);
     if constexpr (OUT) {
       pQ.load((const E*)a.q + (int64_t)ptok * a.sqk + (int64_t)j * D, a.sqk, plen);
       pP.load(a.P + slot * C * C, C, C);
@@ -394,7 +399,7 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
     __syncthreads();  // the previous chunk is done with the LDS tiles
     pWk.store(&sm.Wk[0][0], S::LDQ);
     pKt.store(&sm.Kt[0][0], S::LDCE);
-    if constexpr (LO) pKtl.store(&sm.Ktl[0][0], S::LDCE);
+    if constexpr (KL) pKtl.store(&sm.Ktl[0][0], S::LDCE);
     if constexpr (OUT) {
       pQ.store(&sm.Q[0][0], S::LDQ);
       pP.template store_split<E>(&sm.P[0][0], &sm.Pl[0][0], S::LDCE);
@@ -427,7 +432,22 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
         for (int e = 0; e < 4; ++e) wv[e] = sm.U[rt * 16 + acc_row(e)][ct * 16 + acc_col()] - x[e];
         {
           const int c = ct * 16 + acc_col(), r = rt * 16 + acc_row(0);
-          st4_split<E>(&sm.Wt[c][r], &sm.Wtl[0][0] + c * S::LDCE + r, wv);
+          if constexpr (KP) {
+            // rows of W scaled by e^{gamma_last - gamma_r} (0 past len) for the
+            // state update K^T (diag(e) W); the output's P W keeps W itself
+            f32x4 ws;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              ws[e] = (r + e < len) ? wv[e] * __expf(sm.gam[len - 1] - sm.gam[r + e]) : 0.f;
+            if constexpr (OUT) {
+              st4_split<E>(&sm.Wt[c][r], &sm.Wtl[0][0] + c * S::LDCE + r, wv);
+              st4_split<E>(&sm.Ws[c][r], &sm.Wsl[0][0] + c * S::LDCE + r, ws);
+            } else {
+              st4_split<E>(&sm.Wt[c][r], &sm.Wtl[0][0] + c * S::LDCE + r, ws);
+            }
+          } else {
+            st4_split<E>(&sm.Wt[c][r], &sm.Wtl[0][0] + c * S::LDCE + r, wv);
+          }
         }
         if constexpr (STORE) store_tile<float>(a.W + slot * C * D, D, rt * 16, col0 + ct * 16, wv, C);
         if constexpr (OUT) {
@@ -446,10 +466,19 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
       const int t = w + kChunkWaves * i;
       if (t < NHT) {
         const int rt = t / NCT, ct = t % NCT;
-        f32x4 y = mm_tile<E, C>(zero4(), &sm.Kt[rt * 16][0], S::LDCE, &sm.Wt[ct * 16][0], S::LDCE);
-        if constexpr (LO) {
-          y = mm_tile<E, C>(y, &sm.Kt[rt * 16][0], S::LDCE, &sm.Wtl[ct * 16][0], S::LDCE);
-          y = mm_tile<E, C>(y, &sm.Ktl[rt * 16][0], S::LDCE, &sm.Wt[ct * 16][0], S::LDCE);
+        f32x4 y;
+        if constexpr (KP) {
+          // K exact in bf16: hi and lo parts of the scaled W
+          const E* wh = OUT ? &sm.Ws[ct * 16][0] : &sm.Wt[ct * 16][0];
+          const E* wl = OUT ? &sm.Wsl[0][0] + ct * 16 * S::LDCE : &sm.Wtl[0][0] + ct * 16 * S::LDCE;
+          y = mm_tile<E, C>(zero4(), &sm.Kt[rt * 16][0], S::LDCE, wh, S::LDCE);
+          if constexpr (LO) y = mm_tile<E, C>(y, &sm.Kt[rt * 16][0], S::LDCE, wl, S::LDCE);
+        } else {
+          y = mm_tile<E, C>(zero4(), &sm.Kt[rt * 16][0], S::LDCE, &sm.Wt[ct * 16][0], S::LDCE);
+          if constexpr (LO) {
+            y = mm_tile<E, C>(y, &sm.Kt[rt * 16][0], S::LDCE, &sm.Wtl[ct * 16][0], S::LDCE);
+            y = mm_tile<E, C>(y, &sm.Ktl[rt * 16][0], S::LDCE, &sm.Wt[ct * 16][0], S::LDCE);
+          }
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) Hr[i][e] = gl * Hr[i][e] + y[e];
@@ -530,17 +559,23 @@ inline int state_columns(const ChunkArgs& a, int D, int mode) {
   return chains < (mode == kFwdOut ? 4 * kNumCUs : kNumCUs) ? D / 2 : D;
 }
 
-template <typename E, int D, int C, int DVT>
+template <typename E, int D, int C, int DVT, bool KP = false>
 static void launch_state_fwd_tiled(const ChunkArgs& a, hipStream_t st, int mode) {
   const dim3 grid(state_grid(a.N, a.Hk, a.G, D / DVT));
-  if (mode == kFwdOut) state_fwd_kernel<E, D, C, DVT, kFwdOut><<<grid, kChunkThreads, 0, st>>>(a);
-  else if (mode == kFwdStore) state_fwd_kernel<E, D, C, DVT, kFwdStore><<<grid, kChunkThreads, 0, st>>>(a);
-  else state_fwd_kernel<E, D, C, DVT, kFwdBoth><<<grid, kChunkThreads, 0, st>>>(a);
+  if (mode == kFwdOut) state_fwd_kernel<E, D, C, DVT, kFwdOut, KP><<<grid, kChunkThreads, 0, st>>>(a);
+  else if (mode == kFwdStore) state_fwd_kernel<E, D, C, DVT, kFwdStore, KP><<<grid, kChunkThreads, 0, st>>>(a);
+  else state_fwd_kernel<E, D, C, DVT, kFwdBoth, KP><<<grid, kChunkThreads, 0, st>>>(a);
 }
 
 template <typename E, int D, int C>
-void launch_chunk_fwd_core(const ChunkArgs& a, hipStream_t st, int mode) {
+void launch_chunk_fwd_core(const ChunkArgs& args, hipStream_t st, int mode) {
   constexpr int DVT = state_dvt<E, D>();
+  // The 16-column state pass reads the plain K^T (exact in bf16) and applies
+  // the decay to W's rows: no K lo part to load or multiply per chunk step
+  // (it loads the chunk's operands in every one of a chain's 8 workgroups).
+  const int nc = use_wide_state<E, D, C>() ? state_columns(args, D, mode) : DVT;
+  ChunkArgs a = args;
+  a.kt_plain = use_wide_state<E, D, C>() && nc == 16;
   static const char* prep_name[4] = {"", "chunk_prep", "chunk_prep_bwd", "chunk_prep_save"};
   static const char* state_name[4] = {"", "chunk_state_fwd", "chunk_state_store", "chunk_state_save"};
   // Inference preparation runs persistent: as many workgroups as fit at once
@@ -561,8 +596,7 @@ void launch_chunk_fwd_core(const ChunkArgs& a, hipStream_t st, int mode) {
   }
   GDN_PROF(state_name[mode], st);
   if constexpr (use_wide_state<E, D, C>()) {
-    const int nc = state_columns(a, D, mode);
-    if (nc == 16) launch_state_fwd_tiled<E, D, C, 16>(a, st, mode);
+    if (nc == 16) launch_state_fwd_tiled<E, D, C, 16, true>(a, st, mode);
     else launch_state_fwd_wide(a, st, mode, nc < D);
     return;
   }
