@@ -570,12 +570,12 @@ static void launch_state_fwd_tiled(const ChunkArgs& a, hipStream_t st, int mode)
 template <typename E, int D, int C>
 void launch_chunk_fwd_core(const ChunkArgs& args, hipStream_t st, int mode) {
   constexpr int DVT = state_dvt<E, D>();
-  // The 16-column state pass reads the plain K^T (exact in bf16) and applies
-  // the decay to W's rows: no K lo part to load or multiply per chunk step
-  // (it loads the chunk's operands in every one of a chain's 8 workgroups).
+  // The state passes at bf16, d = 128, chunk 64 read the plain K^T (exact in
+  // bf16) and apply the decay to W's rows: no K lo part to write, load or
+  // multiply per chunk step.
   const int nc = use_wide_state<E, D, C>() ? state_columns(args, D, mode) : DVT;
   ChunkArgs a = args;
-  a.kt_plain = use_wide_state<E, D, C>() && nc == 16;
+  a.kt_plain = use_wide_state<E, D, C>();
   static const char* prep_name[4] = {"", "chunk_prep", "chunk_prep_bwd", "chunk_prep_save"};
   static const char* state_name[4] = {"", "chunk_state_fwd", "chunk_state_store", "chunk_state_save"};
   // Inference preparation runs persistent: as many workgroups as fit at once

@@ -7,15 +7,17 @@
 // "Support Qwen35 SFT", XTuner changes (varlen mode: the state restarts at
 // every sequence).
 //
-// LDS holds only what several waves read: K~^T, H^T and W^T (forward);
-// [dO^T | dW^T], dH^T and K~ rows (reverse), each bf16 hi + lo.  Operands that
+// LDS holds only what several waves read: K^T, H^T and W^T (forward; H and W
+// as bf16 hi + lo); [dO^T | dW^T], dH^T and K~ rows (reverse, hi + lo).  Operands that
 // one row-tile of waves reads (Wk, q, U, P in the forward; P^T, (Gam q)^T,
 // Wk^T in the reverse) are loaded straight into MFMA fragments from global
 // memory (L2), and the next chunk's copies are requested right after the
 // current chunk's last use.
 //
 // Forward, per chunk (H = state entering it):
-//   W = U - Wk H;   o = scale (diag(Gam) Q H + P W);   H <- Gam_last H + K~^T W
+//   W = U - Wk H;   o = scale (diag(Gam) Q H + P W);   H <- Gam_last H + K^T diag(e) W
+// (K~^T W with the decay e_s = e^{gamma_last - gamma_s} moved onto W's rows,
+// so the bf16 K needs no lo part)
 // Reverse, per chunk (dH = gradient w.r.t. the state leaving it):
 //   dW = scale P^T dO + K~ dH;   dH <- Gam_last dH + scale (diag(Gam) Q)^T dO - Wk^T dW
 #include "chunk_common.cuh"
@@ -36,14 +38,15 @@ constexpr int kLD2C = 2 * kC + 8;
 typedef bf16 E;
 typedef Mma<bf16> M;
 
-template <int NC>  // state columns this workgroup carries
+template <int NC, bool OUT>  // state columns this workgroup carries; whether it forms o
 struct FwdSmem {
-  E Kt[kD][kLDC];    // K~^T, K~ = diag(e) K
-  E Ktl[kD][kLDC];
+  E Kt[kD][kLDC];    // K^T, exact in bf16
   E Ht[NC][kLDQ];    // H^T: Ht[c][r] = H[r][c]
   E Htl[NC][kLDQ];
-  E Wt[NC][kLDC];    // W^T
+  E Wt[NC][kLDC];    // W^T (with OUT, for P W), else (diag(e) W)^T
   E Wtl[NC][kLDC];
+  E Ws[OUT ? NC : 1][kLDC];   // (diag(e) W)^T, e_r = e^{gamma_last - gamma_r}, for the state update
+  E Wsl[OUT ? NC : 1][kLDC];
   float gam[kC];
 };
 
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
   constexpr int P1 = NC / 32;  // phase-1 column tiles per wave
   constexpr int P2 = NC / 16;  // state column tiles per wave
   static_assert(NC == kD || NC == kD / 2, "whole or half state");
-  __shared__ FwdSmem<NC> sm;
+  __shared__ FwdSmem<NC, OUT> sm;
   int n, h, vt;
   if (!state_block(blockIdx.x, a.N, a.Hk, a.G, kD / NC, n, h, vt)) return;
   const int j = h / a.G;
@@ -130,18 +133,16 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
 
   // staged operands of the next chunk
   static_assert(kKR == 2, "two 16-byte pieces of each [D][C] tile per thread");
-  uint4 kt_h0, kt_h1, kt_l0, kt_l1;  // this thread's pieces of K~^T (hi, lo); named, so they stay in registers
+  uint4 kt_h0, kt_h1;  // this thread's pieces of K^T; named, so they stay in registers
   float g_r = 0.f;
   M::frag wkf[4], qf[4];
   f32x4 uf[P1];
   float4 pf[2][2];
   auto load_shared = [&](int ci) {
     const int64_t slot = (int64_t)ci * a.Hv + h;
-    const Buf kh((const E*)a.Kt + slot * D * C, D * C * 2), kl((const E*)a.Ktl + slot * D * C, D * C * 2);
+    const Buf kh((const E*)a.Kt + slot * D * C, D * C * 2);
     kt_h0 = kh.u4(tid * 16);
     kt_h1 = kh.u4((tid + kThreads) * 16);
-    kt_l0 = kl.u4(tid * 16);
-    kt_l1 = kl.u4((tid + kThreads) * 16);
     g_r = Buf(a.gam + slot * C, C * 4).f1((tid & (C - 1)) * 4);  // every thread loads; threads < C use it
   };
   const int a_off = ((rt1 * 16 + r16) * D + kq) * 2;   // lane's A-fragment offset in a [C][D] bf16 tile
@@ -192,13 +193,11 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
   for (int ci = c0; ci < c1; ++ci) {
     const int tok0 = ent.y, len = ent.z;
     const int64_t slot = (int64_t)ci * a.Hv + h;
-    __syncthreads();  // the previous chunk is done with K~^T and W^T, and H^T is written
+    __syncthreads();  // the previous chunk is done with K^T and W^T, and H^T is written
     {  // 16-byte piece e: row e / 8, columns (e % 8) * 8 ..
       const int e0 = tid, e1 = tid + kThreads;
       *reinterpret_cast<uint4*>(&sm.Kt[e0 >> 3][(e0 & 7) * 8]) = kt_h0;
       *reinterpret_cast<uint4*>(&sm.Kt[e1 >> 3][(e1 & 7) * 8]) = kt_h1;
-      *reinterpret_cast<uint4*>(&sm.Ktl[e0 >> 3][(e0 & 7) * 8]) = kt_l0;
-      *reinterpret_cast<uint4*>(&sm.Ktl[e1 >> 3][(e1 & 7) * 8]) = kt_l1;
     }
     if (tid < C) sm.gam[tid] = g_r;
     __syncthreads();
@@ -248,15 +247,29 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
       }
     }
     if (more) load_p1(ci + 1, nent.y, nent.z);  // Wk, q, U of the next chunk
+    float dec[4];  // e^{gamma_last - gamma_r} of this lane's rows, 0 past len
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = rt1 * 16 + acc_row(e);
+      dec[e] = r < len ? __expf(sm.gam[len - 1] - sm.gam[r]) : 0.f;
+    }
 #pragma unroll
     for (int i = 0; i < P1; ++i) {
       const int c = (cb + i) * 16 + acc_col(), r = rt1 * 16 + acc_row(0);
-      st4_split<E>(&sm.Wt[c][r], &sm.Wtl[c][r], x[i]);
+      f32x4 xs;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xs[e] = x[i][e] * dec[e];
+      if constexpr (OUT) {
+        st4_split<E>(&sm.Wt[c][r], &sm.Wtl[c][r], x[i]);
+        st4_split<E>(&sm.Ws[c][r], &sm.Wsl[c][r], xs);
+      } else {
+        st4_split<E>(&sm.Wt[c][r], &sm.Wtl[c][r], xs);
+      }
       if constexpr (STORE) store_tile<float>(a.W + slot * C * D, D, rt1 * 16, col0 + (cb + i) * 16, x[i], C);
     }
     __syncthreads();
 
-    // phase 2: H <- Gam_last H + K~^T W;  o = scale (diag(Gam) Q H + P W)
+    // phase 2: H <- Gam_last H + K^T diag(e) W;  o = scale (diag(Gam) Q H + P W)
     const float gl = __expf(sm.gam[len - 1]);
 #pragma unroll
     for (int i = 0; i < P2; ++i)
@@ -265,15 +278,13 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const M::frag ah = fr(&sm.Kt[rt2 * 16 + r16][ks * 32 + kq]);
-      const M::frag al = fr(&sm.Ktl[rt2 * 16 + r16][ks * 32 + kq]);
 #pragma unroll
       for (int i = 0; i < P2; ++i) {
         const int c = i * 16 + r16;
-        const M::frag bh = fr(&sm.Wt[c][ks * 32 + kq]);
-        const M::frag bl = fr(&sm.Wtl[c][ks * 32 + kq]);
+        const M::frag bh = fr(OUT ? &sm.Ws[c][ks * 32 + kq] : &sm.Wt[c][ks * 32 + kq]);
+        const M::frag bl = fr(OUT ? &sm.Wsl[c][ks * 32 + kq] : &sm.Wtl[c][ks * 32 + kq]);
         Hr[i] = M::mma(ah, bh, Hr[i]);
         Hr[i] = M::mma(ah, bl, Hr[i]);
-        Hr[i] = M::mma(al, bh, Hr[i]);
       }
     }
     if constexpr (OUT) {
