@@ -65,7 +65,10 @@ def kernel_bytes(cfg, n_chunks: int, has_h0: bool) -> dict:
     v_in = S * tile_e
     gb_in = 2 * T * Hv * 4                    # g and beta
     st = N * Hv * dd_f                        # one state per (sequence, v-head)
-    prep_out = S * (tile_e + tile_f + cc_f + lo * tile_e + row_f)   # Wk, U, P, K~^T (hi, lo), gamma
+    # K^T as the state passes read it: plain bf16 K^T at d = 128, chunk 64 (the
+    # decay goes onto W's rows there), else K~^T in hi + lo parts
+    kt = 1 if (cfg.dtype == "bf16" and D == 128 and C == 64) else lo
+    prep_out = S * (tile_e + tile_f + cc_f + kt * tile_e + row_f)   # Wk, U, P, K^T, gamma
     return {
         # decode: the state is read and written once per (sequence, v-head)
         "recurrent_step": 2 * N * Hv * dd_f + N * (2 * Hk * D + 2 * Hv * D) * es + 2 * N * Hv * 4,
@@ -79,13 +82,13 @@ def kernel_bytes(cfg, n_chunks: int, has_h0: bool) -> dict:
         "chunk_prep": qk_in + v_in + gb_in + prep_out,
         # + P^T, T, K~ rows, Wk^T and (Gamma q)^T for the backward
         "chunk_prep_bwd": qk_in + v_in + gb_in + prep_out + S * (2 * cc_f + 3 * lo * tile_e),
-        "chunk_state_fwd": SK * tile_e + S * (tile_e + lo * tile_e + tile_f + cc_f + row_f)
+        "chunk_state_fwd": SK * tile_e + S * (tile_e + kt * tile_e + tile_f + cc_f + row_f)
                            + S * tile_e + (st if has_h0 else 0) + st,
         # forward that also keeps the backward's products: prep_bwd's outputs, and H_c, W per slot
         "chunk_prep_save": qk_in + v_in + gb_in + prep_out + S * (2 * cc_f + 3 * lo * tile_e),
-        "chunk_state_save": SK * tile_e + S * (tile_e + lo * tile_e + tile_f + cc_f + row_f)
+        "chunk_state_save": SK * tile_e + S * (tile_e + kt * tile_e + tile_f + cc_f + row_f)
                             + S * tile_e + (st if has_h0 else 0) + st + S * (dd_f + tile_f),
-        "chunk_state_store": S * (tile_e + lo * tile_e + tile_f + row_f) + (st if has_h0 else 0)
+        "chunk_state_store": S * (tile_e + kt * tile_e + tile_f + row_f) + (st if has_h0 else 0)
                              + S * (dd_f + tile_f),
         "chunk_state_bwd": S * (cc_f + 3 * lo * tile_e + row_f + tile_e) + S * (dd_f + 2 * tile_f),
         "chunk_grad_a": SK * tile_e + S * (2 * dd_f + 2 * tile_f + 2 * tile_e + 2 * row_f)

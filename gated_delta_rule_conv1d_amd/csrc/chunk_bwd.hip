@@ -821,7 +821,9 @@ static WsPlan plan(const gdn_shape* s) {
   p.U = o; o = align256(o + M * Hv * C * D * 4);
   p.P = o; o = align256(o + M * Hv * C * C * 4);
   p.Kt = o; o = align256(o + M * Hv * D * C * es);
-  p.Ktl = o; o = align256(o + (es == 2 ? M * Hv * D * C * es : 0));
+  // no K~ lo part where the state passes read the plain K^T (bf16, d = 128, chunk 64)
+  const bool plain_k = es == 2 && D == 128 && C == 64;
+  p.Ktl = o; o = align256(o + (es == 2 && !plain_k ? M * Hv * D * C * es : 0));
   p.gam = o; o = align256(o + M * Hv * C * 4);
   p.end_fwd = o;
   p.Ptr = o; o = align256(o + M * Hv * C * C * 4);
