@@ -65,8 +65,9 @@ def kernel_bytes(cfg, n_chunks: int, has_h0: bool) -> dict:
     v_in = S * tile_e
     gb_in = 2 * T * Hv * 4                    # g and beta
     st = N * Hv * dd_f                        # one state per (sequence, v-head)
-    # K^T as the state passes read it: plain bf16 K^T at d = 128, chunk 64 (the
-    # decay goes onto W's rows there), else K~^T in hi + lo parts
+    # K^T (and the reverse pass's K rows) as the state passes read them: plain
+    # bf16 K at d = 128, chunk 64 (the decay goes onto W's / K dH's rows
+    # there), else K~ in hi + lo parts
     kt = 1 if (cfg.dtype == "bf16" and D == 128 and C == 64) else lo
     prep_out = S * (tile_e + tile_f + cc_f + kt * tile_e + row_f)   # Wk, U, P, K^T, gamma
     return {
@@ -80,17 +81,17 @@ def kernel_bytes(cfg, n_chunks: int, has_h0: bool) -> dict:
         "norm_fwd": 3 * T * Hv * D * es + D * es,
         "norm_bwd": 5 * T * Hv * D * es + D * es,
         "chunk_prep": qk_in + v_in + gb_in + prep_out,
-        # + P^T, T, K~ rows, Wk^T and (Gamma q)^T for the backward
-        "chunk_prep_bwd": qk_in + v_in + gb_in + prep_out + S * (2 * cc_f + 3 * lo * tile_e),
+        # + P^T, T, K rows (as the K^T above), Wk^T and (Gamma q)^T for the backward
+        "chunk_prep_bwd": qk_in + v_in + gb_in + prep_out + S * (2 * cc_f + (kt + 2 * lo) * tile_e),
         "chunk_state_fwd": SK * tile_e + S * (tile_e + kt * tile_e + tile_f + cc_f + row_f)
                            + S * tile_e + (st if has_h0 else 0) + st,
         # forward that also keeps the backward's products: prep_bwd's outputs, and H_c, W per slot
-        "chunk_prep_save": qk_in + v_in + gb_in + prep_out + S * (2 * cc_f + 3 * lo * tile_e),
+        "chunk_prep_save": qk_in + v_in + gb_in + prep_out + S * (2 * cc_f + (kt + 2 * lo) * tile_e),
         "chunk_state_save": SK * tile_e + S * (tile_e + kt * tile_e + tile_f + cc_f + row_f)
                             + S * tile_e + (st if has_h0 else 0) + st + S * (dd_f + tile_f),
         "chunk_state_store": S * (tile_e + kt * tile_e + tile_f + row_f) + (st if has_h0 else 0)
                              + S * (dd_f + tile_f),
-        "chunk_state_bwd": S * (cc_f + 3 * lo * tile_e + row_f + tile_e) + S * (dd_f + 2 * tile_f),
+        "chunk_state_bwd": S * (cc_f + (kt + 2 * lo) * tile_e + row_f + tile_e) + S * (dd_f + 2 * tile_f),
         "chunk_grad_a": SK * tile_e + S * (2 * dd_f + 2 * tile_f + 2 * tile_e + 2 * row_f)
                         + S * (3 * tile_f + 2 * cc_f + 4),
         "chunk_grad_b": qk_in + S * (4 * tile_f + 4 * cc_f + tile_e + 2 * row_f + 4)

@@ -829,7 +829,7 @@ static WsPlan plan(const gdn_shape* s) {
   p.Ptr = o; o = align256(o + M * Hv * C * C * 4);
   p.Tw = o; o = align256(o + M * Hv * C * C * 4);
   p.Krh = o; o = align256(o + M * Hv * C * D * es);
-  p.Krl = o; o = align256(o + M * Hv * C * D * es);
+  p.Krl = o; o = align256(o + (plain_k ? 0 : M * Hv * C * D * es));
   p.Wth = o; o = align256(o + M * Hv * D * C * es);
   p.Wtl = o; o = align256(o + M * Hv * D * C * es);
   p.Qth = o; o = align256(o + M * Hv * D * C * es);

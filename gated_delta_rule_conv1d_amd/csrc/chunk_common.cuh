@@ -52,8 +52,8 @@ struct ChunkArgs {
   // backward only: operands of the reverse state pass, transposed once per chunk
   float* Ptr;                 // [slot][C][C]  P^T
   float* Tw;                  // [slot][C][C]  T = (I + A)^-1 (for the WY gradients)
-  void* Krh;                  // [slot][C][D]  rows e_s k_s (hi)
-  void* Krl;                  //               (lo)
+  void* Krh;                  // [slot][C][D]  rows e_s k_s (hi); rows k_s with kt_plain
+  void* Krl;                  //               (lo; not written with kt_plain)
   void* Wth;                  // [slot][D][C]  Wk^T (hi)
   void* Wtl;                  //               (lo)
   void* Qth;                  // [slot][D][C]  (Gam_r q_r)^T (hi)

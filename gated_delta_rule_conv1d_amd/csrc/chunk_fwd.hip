@@ -205,10 +205,11 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
               if (!plain) Vec<E>::store((E*)a.Ktl + slot * D * C + d * C + s0, lo);
           }
           if constexpr (LO_OUT) {
-            // rows e_s k_s [C][D] and (Gam_r q_r)^T [D][C], hi / lo, for the reverse state pass
+            // rows e_s k_s [C][D] (with kt_plain the rows k_s, exact: no lo part)
+            // and (Gam_r q_r)^T [D][C], hi / lo, for the reverse state pass
             for (int e = t0; e < C * (D / V); e += nt) {
               const int s = e / (D / V), c0 = (e % (D / V)) * V;
-              const float es = (s < len) ? __expf(glast - sm.gam[s]) : 0.f;
+              const float es = (s < len) ? (plain ? 1.f : __expf(glast - sm.gam[s])) : 0.f;
               float val[V], lo[V];
 #pragma unroll
               for (int i = 0; i < V; ++i) {
@@ -217,7 +218,8 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
               }
               const int64_t o = slot * C * D + (int64_t)s * D + c0;
               Vec<E>::store((E*)a.Krh + o, val);
-              if constexpr (Split<E>::on) Vec<E>::store((E*)a.Krl + o, lo);
+              if constexpr (Split<E>::on)
+                if (!plain) Vec<E>::store((E*)a.Krl + o, lo);
             }
             // Q^T through V x V register blocks: a thread reads V rows of V
             // consecutive d and writes V rows of Q^T; adjacent lanes take adjacent

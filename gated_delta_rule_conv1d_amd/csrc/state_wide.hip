@@ -20,6 +20,7 @@
 // so the bf16 K needs no lo part)
 // Reverse, per chunk (dH = gradient w.r.t. the state leaving it):
 //   dW = scale P^T dO + K~ dH;   dH <- Gam_last dH + scale (diag(Gam) Q)^T dO - Wk^T dW
+// (K~ dH as diag(e) (K dH): the bf16 K needs no lo part)
 #include "chunk_common.cuh"
 #include "profile.h"
 
@@ -55,8 +56,7 @@ struct BwdSmem {
   E dWl[kD][kLDC];   // lo part of dW^T
   E dHt[kD][kLDQ];   // dH^T
   E dHtl[kD][kLDQ];
-  E Kr[kC][kLDQ];    // rows of K~
-  E Krl[kC][kLDQ];
+  E Kr[kC][kLDQ];    // rows of K (exact in bf16; the decay e_s goes onto K dH's rows)
   float gam[kC];
 };
 
@@ -352,18 +352,16 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
   };
 
   // staged operands of the next chunk (reverse order)
-  uint4 kr_h0, kr_h1, kr_l0, kr_l1;  // this thread's pieces of the K~ rows (named: registers)
+  uint4 kr_h0, kr_h1;                // this thread's pieces of the K rows (named: registers)
   ColRegs<E, C, D, kThreads> pO;    // dO of the chunk, gathered column-wise
   float g_r = 0.f;
   float4 ptf[2][2];                 // P^T rows of this wave's dW tiles
   M::frag qth[2], qtl[2], wth[2], wtl[2];  // (Gam q)^T and Wk^T rows of its dH tiles
   auto load_shared = [&](int ci, int tok0, int len) {
     const int64_t slot = (int64_t)ci * a.Hv + h;
-    const Buf kh((const E*)a.Krh + slot * C * D, C * D * 2), kl((const E*)a.Krl + slot * C * D, C * D * 2);
+    const Buf kh((const E*)a.Krh + slot * C * D, C * D * 2);
     kr_h0 = kh.u4(tid * 16);
     kr_h1 = kh.u4((tid + kThreads) * 16);
-    kr_l0 = kl.u4(tid * 16);
-    kr_l1 = kl.u4((tid + kThreads) * 16);
     pO.load((const E*)a.d_o + (int64_t)tok0 * a.Hv * D + (int64_t)h * D, (int64_t)a.Hv * D, len);
     g_r = Buf(a.gam + slot * C, C * 4).f1((tid & (C - 1)) * 4);  // every thread loads; threads < C use it
   };
@@ -412,8 +410,6 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
       const int e0 = tid, e1 = tid + kThreads;
       *reinterpret_cast<uint4*>(&sm.Kr[e0 >> 4][(e0 & 15) * 8]) = kr_h0;
       *reinterpret_cast<uint4*>(&sm.Kr[e1 >> 4][(e1 & 15) * 8]) = kr_h1;
-      *reinterpret_cast<uint4*>(&sm.Krl[e0 >> 4][(e0 & 15) * 8]) = kr_l0;
-      *reinterpret_cast<uint4*>(&sm.Krl[e1 >> 4][(e1 & 15) * 8]) = kr_l1;
     }
     pO.store(&sm.OW[0][0], kLD2C);
     if (tid < C) sm.gam[tid] = g_r;
@@ -425,7 +421,7 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
       load_shared(ci - 1, nent.y, nent.z);
     }
 
-    // phase 1: dW = scale P^T dO + K~ dH on this wave's tiles, one tile at a time
+    // phase 1: dW = scale P^T dO + diag(e) K dH on this wave's tiles, one tile at a time
     M::frag ph[2], pl[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) split8(ptf[ks][0], ptf[ks][1], ph[ks], pl[ks]);
@@ -436,6 +432,12 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
       float* dst = a.dHn + slot * D * D;
 #pragma unroll
       for (int i = 0; i < kP2; ++i) store_tile<float>(dst, D, rt2 * 16, i * 16, dH[i], D);
+    }
+    float dec[4];  // e^{gamma_last - gamma_s} of this lane's rows s, 0 past len
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = rt1 * 16 + acc_row(e);
+      dec[e] = r < len ? __expf(sm.gam[len - 1] - sm.gam[r]) : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < kP1; ++i) {
@@ -450,15 +452,13 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const M::frag ah = fr(&sm.Kr[rt1 * 16 + r16][ks * 32 + kq]);
-        const M::frag al = fr(&sm.Krl[rt1 * 16 + r16][ks * 32 + kq]);
         const M::frag bh = fr(&sm.dHt[c][ks * 32 + kq]);
         const M::frag bl = fr(&sm.dHtl[c][ks * 32 + kq]);
         kd = M::mma(ah, bh, kd);
         kd = M::mma(ah, bl, kd);
-        kd = M::mma(al, bh, kd);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) kd[e] += a.scale * p[e];  // kd <- dW
+      for (int e = 0; e < 4; ++e) kd[e] = dec[e] * kd[e] + a.scale * p[e];  // kd <- dW
       store_tile<float>(a.dW + slot * C * D, D, rt1 * 16, (cb + i) * 16, kd, C);
       store_tile_t(a.dWt + slot * D * C, C, rt1 * 16, (cb + i) * 16, kd);
       const int cc = (cb + i) * 16 + acc_col(), r = rt1 * 16 + acc_row(0);
