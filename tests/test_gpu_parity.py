@@ -195,10 +195,12 @@ def test_chunk_saved_pair_bit_identical(dtype, d, chunk, Hk, Hv, lengths):
         assert same(r1[key], r2[key]), key
 
 
-def test_chunk_weak_decay_long_range():
-    """A_log = -6: the state is carried across many chunks (long-range path)."""
-    cfg = small_cfg(dtype="bf16", d=64, chunk=64, Hk=1, Hv=2, lengths=(1000, 300), weak=True)
-    _print_case("weak_decay", lengths=cfg.lengths)
+@pytest.mark.parametrize("d", [64, 128])
+def test_chunk_weak_decay_long_range(d):
+    """A_log = -6: the state is carried across many chunks (long-range path);
+    at d = 128 through the 16-column state tiles that read the plain K^T."""
+    cfg = small_cfg(dtype="bf16", d=d, chunk=64, Hk=1, Hv=2, lengths=(1000, 300), weak=True)
+    _print_case("weak_decay", d=d, lengths=cfg.lengths)
     inp = synth.make_inputs(cfg)
     q, k, v = qkv_inputs(cfg)
     s = shape_of(cfg)
