@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark the GatedDeltaNet layer on one MI355X.
 
-One step = the whole layer path over one packed row: the gates (g, beta from
-a, b, A_log, dt_bias), conv1d+SiLU+L2, the chunked gated delta rule,
-RMSNormGated, and (for the training workload) the backward of all four.  Default workload: the training step, 8 sequences x
+One step = the whole layer path over one packed row: conv1d+SiLU+L2, the
+chunked gated delta rule with its gates (g, beta computed inside the chunk
+kernels from a, b, A_log, dt_bias), RMSNormGated, and (for the training
+workload) the backward of all of them.  Default workload: the training step, 8 sequences x
 8192 tokens packed in one row, 16 q/k heads, 32 v heads, d = 128, bf16.
 
 Prints ONE JSON line with the throughput (tokens/s), the roofline of the
@@ -229,13 +230,15 @@ def main():
             o, _ = gdn.recurrent_step(q, k, v, g, beta, shape, state_in=state, state_out=state)
             gdn.norm_gate(o, z, wn, shape)
     else:
+        gates = (ga, gb, A_log, dt_bias)
+
         def step():
-            g, beta = layer.gates(ga, gb, A_log, dt_bias)
-            # a training step keeps the forward's chunk products for the backward
-            f = layer.forward(x, w, g, beta, cu, z, wn, h0, for_backward=cfg.bwd)
+            # the chunk kernels compute g and beta from the raw gate inputs (and,
+            # backward, their gradients); a training step keeps the forward's
+            # chunk products for the backward
+            f = layer.forward(x, w, None, None, cu, z, wn, h0, for_backward=cfg.bwd, gates=gates)
             if cfg.bwd:
-                r = layer.backward(dy, x, w, g, beta, cu, f, z, wn, h0)
-                layer.gates_backward(ga, gb, A_log, dt_bias, r["dg"], r["dbeta"])
+                layer.backward(dy, x, w, None, None, cu, f, z, wn, h0, gates=gates)
 
     # Per-kernel durations come from HIP events that the library records around
     # each launch on the stream it launches on, during the timed steps
@@ -261,31 +264,32 @@ def main():
     kb = kernel_bytes(cfg, n_chunks, cfg.h0)
     kf = kernel_flops(cfg, n_chunks)
     kernels = {}
+    base = lambda name: name.split(":", 1)[0]   # state-pass records carry their variant after a colon
     for name, (cnt, tot) in rep.items():
         avg_ms = tot / cnt
         kernels[name] = {"launches": cnt, "avg_us": round(avg_ms * 1e3, 2),
                          "share": round(tot / sum(t for _, t in rep.values()), 4)}
-        if name in kb:
-            kernels[name]["GBps"] = round(kb[name] / (avg_ms * 1e-3) / 1e9, 1)
-        if name in kf:
-            kernels[name]["TFLOPs"] = round(kf[name] / (avg_ms * 1e-3) / 1e12, 2)
+        if base(name) in kb:
+            kernels[name]["GBps"] = round(kb[base(name)] / (avg_ms * 1e-3) / 1e9, 1)
+        if base(name) in kf:
+            kernels[name]["TFLOPs"] = round(kf[base(name)] / (avg_ms * 1e-3) / 1e12, 2)
     dom = max(rep, key=lambda k: rep[k][1])
     cnt, tot = rep[dom]
     avg_s = tot / cnt * 1e-3
-    t_hbm = kb.get(dom, 0) / (HBM_PEAK_GBS * 1e9)
-    t_mfma = kf.get(dom, 0) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    t_hbm = kb.get(base(dom), 0) / (HBM_PEAK_GBS * 1e9)
+    t_mfma = kf.get(base(dom), 0) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
     if t_mfma > t_hbm:
-        achieved = kf[dom] / avg_s / 1e12
+        achieved = kf[base(dom)] / avg_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
     else:
-        achieved = kb.get(dom, 0) / avg_s / 1e9
+        achieved = kb.get(base(dom), 0) / avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
     roof["kernel"] = dom
     roof["avg_us"] = round(avg_s * 1e6, 2)
-    roof["algorithmic_bytes"] = kb.get(dom)
-    roof["traffic"] = load_traffic(dom, args.workload, 1)
+    roof["algorithmic_bytes"] = kb.get(base(dom))
+    roof["traffic"] = load_traffic(base(dom), args.workload, 1)
 
     # whole-step roofline of the path (fused algorithmic minimum)
     step_bytes = (33024 + (57856 if cfg.bwd else 0)) * cfg.T if args.workload != "tiny" else None
@@ -311,7 +315,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}", "tokens": cfg.T,
                    "n_seqs": cfg.N, "h_qk": cfg.h_qk, "h_v": cfg.h_v, "d": cfg.d_k, "chunk": cfg.chunk,
-                   "gates": "g, beta computed from a, b, A_log, dt_bias in the step",
+                   "gates": ("g, beta computed from a, b, A_log, dt_bias in the step" if cfg.decode else
+                             "g, beta computed from a, b, A_log, dt_bias inside the chunk kernels"),
                    "parallelism": "single GPU"},
         "roofline": roof,
         "step_fraction_of_fused_minimum": (round(step_bytes / (HBM_PEAK_GBS * 1e9) / (ms_per_step * 1e-3), 4)

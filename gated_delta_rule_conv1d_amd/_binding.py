@@ -16,7 +16,8 @@ _STATUS = {0: "GDN_OK", -1: "GDN_ERR_INVALID_ARG", -2: "GDN_ERR_UNSUPPORTED", -3
 #: every symbol include/gdn.h declares
 SYMBOLS = ("gdn_status_string", "gdn_max_chunks", "gdn_chunk_index", "gdn_conv1d", "gdn_conv1d_bwd_workspace",
            "gdn_conv1d_bwd", "gdn_chunk_fwd_workspace", "gdn_chunk_fwd", "gdn_chunk_bwd_workspace",
-           "gdn_chunk_bwd", "gdn_chunk_fwd_save", "gdn_chunk_bwd_saved", "gdn_norm_gate",
+           "gdn_chunk_bwd", "gdn_chunk_fwd_save", "gdn_chunk_bwd_saved", "gdn_chunk_fwd_fp8", "gdn_chunk_fwd_gated",
+           "gdn_chunk_fwd_save_gated", "gdn_chunk_bwd_gated", "gdn_chunk_bwd_saved_gated", "gdn_norm_gate",
            "gdn_norm_gate_bwd_workspace", "gdn_norm_gate_bwd", "gdn_gates", "gdn_gates_bwd_workspace",
            "gdn_gates_bwd", "gdn_recurrent_step", "gdn_conv1d_step", "gdn_conv1d_window", "gdn_conv1d_prefill",
            "gdn_profile_enable",
@@ -33,6 +34,16 @@ class _Shape(ctypes.Structure):
     _fields_ = [("n_seqs", ctypes.c_int32), ("total_tokens", ctypes.c_int32), ("h_qk", ctypes.c_int32),
                 ("h_v", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class _GateInputs(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("A_log", ctypes.c_void_p),
+                ("dt_bias", ctypes.c_void_p)]
+
+
+class _GateGrads(ctypes.Structure):
+    _fields_ = [("da", ctypes.c_void_p), ("db", ctypes.c_void_p), ("dA_log", ctypes.c_void_p),
+                ("ddt_bias", ctypes.c_void_p)]
 
 
 @dataclass(frozen=True)
@@ -78,6 +89,7 @@ def load() -> ctypes.CDLL:
         lib = ctypes.CDLL(path)
         P, I32, I64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
         S = ctypes.POINTER(_Shape)
+        GI, GG = ctypes.POINTER(_GateInputs), ctypes.POINTER(_GateGrads)
         sig = {
             "gdn_status_string": (ctypes.c_char_p, [I32]),
             "gdn_max_chunks": (I64, [S]),
@@ -91,6 +103,11 @@ def load() -> ctypes.CDLL:
             "gdn_chunk_bwd": (I32, [S, P, P, P, I64, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
             "gdn_chunk_fwd_save": (I32, [S, P, P, P, I64, I64, P, P, P, P, P, P, P, SZ, P]),
             "gdn_chunk_bwd_saved": (I32, [S, P, P, P, I64, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+            "gdn_chunk_fwd_fp8": (I32, [S, P, P, P, I64, I64, F, F, F, P, P, P, P, P, P, P, SZ, P]),
+            "gdn_chunk_fwd_gated": (I32, [S, P, P, P, I64, I64, GI, P, P, P, P, P, SZ, P]),
+            "gdn_chunk_fwd_save_gated": (I32, [S, P, P, P, I64, I64, GI, P, P, P, P, P, SZ, P]),
+            "gdn_chunk_bwd_gated": (I32, [S, P, P, P, I64, I64, GI, P, P, P, P, P, P, P, GG, P, P, SZ, P]),
+            "gdn_chunk_bwd_saved_gated": (I32, [S, P, P, P, I64, I64, GI, P, P, P, P, P, P, P, GG, P, P, SZ, P]),
             "gdn_norm_gate": (I32, [S, P, P, P, F, P, P]),
             "gdn_norm_gate_bwd_workspace": (SZ, [S]),
             "gdn_norm_gate_bwd": (I32, [S, P, P, P, P, F, P, P, P, P, SZ, P]),
@@ -283,6 +300,99 @@ def chunk_bwd(q, k, v, g, beta, cu_seqlens, shape: Shape, d_o, h0=None, dht=None
         _ptr(h0), _ptr(d_o), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db), _ptr(dh0), _ptr(ws),
         ws.numel(), _stream(q.device)))
     return dict(dq=dq, dk=dk, dv=dv, dg=dg, dbeta=db, dh0=dh0)
+
+
+def chunk_fwd_fp8(q8, k8, v8, scales, g, beta, cu_seqlens, shape: Shape, h0=None, want_ht: bool = True,
+                  ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """gdn_chunk_fwd_fp8: q8, k8 [T, Hk*dk] and v8 [T, Hv*dv] views of
+    torch.float8_e4m3fn (or uint8) tensors with unit inner stride; scales =
+    (scale_q, scale_k, scale_v), powers of two.  shape.dtype is BF16 (o)."""
+    T, N, Hv, dk, dv = shape.total_tokens, shape.n_seqs, shape.h_v, shape.d_k, shape.d_v
+    for t, nm in ((q8, "q"), (k8, "k"), (v8, "v")):
+        if t.dtype not in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)) or not t.is_cuda:
+            raise ValueError(f"{nm} must be a GPU float8_e4m3fn (or uint8) tensor")
+    sqk, sv = _qkv_strides(q8, k8, v8, shape)
+    _need(g, "g", torch.float32, (T, Hv))
+    _need(beta, "beta", torch.float32, (T, Hv))
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (N, Hv, dk, dv))
+    o = torch.empty((T, Hv, dv), dtype=torch.bfloat16, device=q8.device) if out is None else out
+    ht = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=q8.device) if want_ht else None
+    ws = _workspace(chunk_fwd_workspace(shape), q8.device, ws)
+    sq, sk, svs = (float(x) for x in scales)
+    _check("gdn_chunk_fwd_fp8", load().gdn_chunk_fwd_fp8(
+        ctypes.byref(shape.c()), _ptr(q8), _ptr(k8), _ptr(v8), sqk, sv, sq, sk, svs, _ptr(g), _ptr(beta),
+        _ptr(cu_seqlens), _ptr(h0), _ptr(o), _ptr(ht), _ptr(ws), ws.numel(), _stream(q8.device)))
+    return o, ht
+
+
+def _gate_inputs(gates, shape: Shape):
+    a, b, A_log, dt_bias = gates
+    _need(a, "a", torch.float32, (shape.total_tokens, shape.h_v))
+    _need(b, "b", torch.float32, (shape.total_tokens, shape.h_v))
+    _need(A_log, "A_log", torch.float32, (shape.h_v,))
+    _need(dt_bias, "dt_bias", torch.float32, (shape.h_v,))
+    return _GateInputs(_ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias))
+
+
+def chunk_fwd_gated(q, k, v, gates, cu_seqlens, shape: Shape, h0=None, want_ht: bool = True,
+                    ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None, save: bool = False):
+    """gdn_chunk_fwd_gated / gdn_chunk_fwd_save_gated: as chunk_fwd, with g and
+    beta computed inside the kernels from gates = (a, b, A_log, dt_bias)."""
+    dt = shape.torch_dtype
+    T, N, Hv, dk, dv = shape.total_tokens, shape.n_seqs, shape.h_v, shape.d_k, shape.d_v
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, dt, inner_contig=False)
+    sqk, sv = _qkv_strides(q, k, v, shape)
+    gi = _gate_inputs(gates, shape)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (N, Hv, dk, dv))
+    o = torch.empty((T, Hv, dv), dtype=dt, device=q.device) if out is None else out
+    ht = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=q.device) if want_ht else None
+    if save and ws is None:
+        raise ValueError("save=True needs the caller's backward workspace (it carries state to chunk_bwd)")
+    ws = _workspace(chunk_bwd_workspace(shape) if save else chunk_fwd_workspace(shape), q.device, ws)
+    name = "gdn_chunk_fwd_save_gated" if save else "gdn_chunk_fwd_gated"
+    _check(name, getattr(load(), name)(ctypes.byref(shape.c()), _ptr(q), _ptr(k), _ptr(v), sqk, sv,
+                                       ctypes.byref(gi), _ptr(cu_seqlens), _ptr(h0), _ptr(o), _ptr(ht),
+                                       _ptr(ws), ws.numel(), _stream(q.device)))
+    return o, ht
+
+
+def chunk_bwd_gated(q, k, v, gates, cu_seqlens, shape: Shape, d_o, h0=None, dht=None, dq=None, dk=None, dv=None,
+                    want_dh0: bool = True, ws: Optional[torch.Tensor] = None, saved: bool = False):
+    """gdn_chunk_bwd_gated / gdn_chunk_bwd_saved_gated.  Returns dict dq, dk, dv,
+    da, db [T, Hv], dA_log, ddt_bias [Hv] and dh0 (or None)."""
+    dt = shape.torch_dtype
+    T, N, Hk, Hv, dkk, dvv = shape.total_tokens, shape.n_seqs, shape.h_qk, shape.h_v, shape.d_k, shape.d_v
+    sqk, sv = _qkv_strides(q, k, v, shape)
+    gi = _gate_inputs(gates, shape)
+    _need(d_o, "d_o", dt, (T, Hv, dvv))
+    dq = torch.empty((T, Hk * dkk), dtype=dt, device=q.device) if dq is None else dq
+    dk = torch.empty((T, Hk * dkk), dtype=dt, device=q.device) if dk is None else dk
+    dv = torch.empty((T, Hv * dvv), dtype=dt, device=q.device) if dv is None else dv
+    if _tok_view(dq, "dq", T, Hk * dkk) != sqk or _tok_view(dk, "dk", T, Hk * dkk) != sqk \
+            or _tok_view(dv, "dv", T, Hv * dvv) != sv:
+        raise ValueError("dq/dk/dv must use the token strides of q/k/v")
+    if dht is not None:
+        _need(dht, "dht", torch.float32, (N, Hv, dkk, dvv))
+    da = torch.empty((T, Hv), dtype=torch.float32, device=q.device)
+    db = torch.empty((T, Hv), dtype=torch.float32, device=q.device)
+    dA = torch.empty((Hv,), dtype=torch.float32, device=q.device)
+    ddt = torch.empty((Hv,), dtype=torch.float32, device=q.device)
+    gg = _GateGrads(_ptr(da), _ptr(db), _ptr(dA), _ptr(ddt))
+    dh0 = torch.empty((N, Hv, dkk, dvv), dtype=torch.float32, device=q.device) if want_dh0 else None
+    if saved and ws is None:
+        raise ValueError("saved=True needs the workspace filled by chunk_fwd_gated(..., save=True)")
+    ws = _workspace(chunk_bwd_workspace(shape), q.device, ws)
+    name = "gdn_chunk_bwd_saved_gated" if saved else "gdn_chunk_bwd_gated"
+    _check(name, getattr(load(), name)(
+        ctypes.byref(shape.c()), _ptr(q), _ptr(k), _ptr(v), sqk, sv, ctypes.byref(gi), _ptr(cu_seqlens),
+        _ptr(h0), _ptr(d_o), _ptr(dht), _ptr(dq), _ptr(dk), _ptr(dv), ctypes.byref(gg), _ptr(dh0), _ptr(ws),
+        ws.numel(), _stream(q.device)))
+    return dict(dq=dq, dk=dk, dv=dv, da=da, db=db, dA_log=dA, ddt_bias=ddt, dh0=dh0)
 
 
 # ----------------------------------------------------------------------------- norm gate

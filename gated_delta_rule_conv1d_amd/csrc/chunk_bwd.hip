@@ -25,7 +25,7 @@
 
 namespace gdn {
 
-template <typename E, int D, int C>
+template <typename E, int D, int C, bool F8 = false>
 void launch_chunk_fwd_core(const ChunkArgs& a, hipStream_t st, int mode);
 
 // ---------------------------------------------------------------------------
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
     const int e = tid;
     const float g = a.gam[slot * C + e];
     const float gl = a.gam[slot * C + len - 1];
-    const float bt = a.beta[(int64_t)(tok0 + min(e, len - 1)) * a.Hv + h];
+    const float bt = chunk_beta(a, tok0 + min(e, len - 1), h);
     sm.bs[e] = e < len ? bt : 0.f;
     sm.gm[e] = __expf(g);
     sm.em[e] = e < len ? __expf(gl - g) : 0.f;
@@ -514,7 +514,14 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
   constexpr int DT = ND >= NWD ? ND / NWD : 1;   // d-tiles per wave
   const int ci = blockIdx.x, j = blockIdx.y;
   const int4 ent = chunk_entry(a.table, ci);
-  if (ent.x < 0) return;
+  if (ent.x < 0) {  // padding entry past the last chunk: its shares of the gate sums are zero
+    if (a.da)
+      for (int i = threadIdx.x; i < a.G; i += NTH) {
+        a.gpart[(int64_t)ci * a.Hv + j * a.G + i] = 0.f;
+        a.gpart[((int64_t)a.max_chunks + ci) * a.Hv + j * a.G + i] = 0.f;
+      }
+    return;
+  }
   const int tok0 = ent.y, len = ent.z;
   const int w = wave_id(), lane = lane_id(), tid = threadIdx.x;
   const int rt = w % NWR, dt0 = (w / NWR) * DT;
@@ -564,7 +571,7 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
       const int e = tid;
       const float gm = a.gam[slot * C + e];
       const float gl = a.gam[slot * C + len - 1];
-      const float bt = a.beta[(int64_t)(tok0 + min(e, len - 1)) * a.Hv + h];
+      const float bt = chunk_beta(a, tok0 + min(e, len - 1), h);
       const float hd = a.hdot[slot];  // used by the row pass at the end
       sm.gam[e] = gm;
       sm.Gm[e] = __expf(gm);
@@ -781,7 +788,27 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
       if (r == len - 1) dgam += sm.Gm[len - 1] * sm.hdot + tks;
       // reverse inclusive scan: dg_r = sum_{r' >= r} dgam_{r'}
       const float x = wave_suffix_sum(dgam);
-      if (r < len) {
+      if (a.da) {
+        // fused gates: da = -exp(A_log) sigmoid(a + dt_bias) dg, db = beta (1 - beta) dbeta,
+        // and this chunk's shares of dA_log = sum dg g and ddt_bias = sum da
+        float sA = 0.f, sdt = 0.f;
+        if (r < len) {
+          const int64_t e = (int64_t)(tok0 + r) * a.Hv + h;
+          const float ea = __expf(a.A_log[h]), xa = a.ga[e] + a.dt_bias[h];
+          const float dav = -ea * gate_sigmoid(xa) * x;
+          const float bb = a.gb[e];
+          a.da[e] = dav;
+          a.db[e] = gate_sigmoid(bb) * gate_sigmoid(-bb) * dbeta;
+          sA = x * (-ea * gate_softplus(xa));
+          sdt = dav;
+        }
+        sA = wave_sum(sA);
+        sdt = wave_sum(sdt);
+        if (r == 0) {
+          a.gpart[(int64_t)ci * a.Hv + h] = sA;
+          a.gpart[((int64_t)a.max_chunks + ci) * a.Hv + h] = sdt;
+        }
+      } else if (r < len) {
         a.dg[(int64_t)(tok0 + r) * a.Hv + h] = x;
         a.dbeta[(int64_t)(tok0 + r) * a.Hv + h] = dbeta;
       }
@@ -807,7 +834,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsPlan {
   size_t table, seq0, Wk, U, P, Kt, Ktl, gam, end_fwd;
-  size_t Ptr, Tw, Krh, Krl, Wth, Wtl, Qth, Qtl, Hc, W, dHn, dW, dWt, dT, dWkt, dQs, dKh, dP, hdot, end_bwd;
+  size_t Ptr, Tw, Krh, Krl, Wth, Wtl, Qth, Qtl, Hc, W, dHn, dW, dWt, dT, dWkt, dQs, dKh, dP, hdot, gpart, end_bwd;
 };
 
 static WsPlan plan(const gdn_shape* s) {
@@ -845,6 +872,7 @@ static WsPlan plan(const gdn_shape* s) {
   p.dKh = o; o = align256(o + M * Hv * C * D * 4);
   p.dP = o; o = align256(o + M * Hv * C * C * 4);
   p.hdot = o; o = align256(o + M * Hv * 4);
+  p.gpart = o; o = align256(o + 2 * M * Hv * 4);
   p.end_bwd = o;
   return p;
 }
@@ -882,6 +910,7 @@ static void fill_ws(ChunkArgs& a, const gdn_shape* s, void* ws) {
   a.dKh = (float*)(b + p.dKh);
   a.dP = (float*)(b + p.dP);
   a.hdot = (float*)(b + p.hdot);
+  a.gpart = (float*)(b + p.gpart);
 }
 
 template <typename E, int D, int C>
@@ -895,9 +924,12 @@ constexpr bool fits() {
 template <typename E, int D, int C>
 static void launch_chunk_bwd_core(const ChunkArgs& a, hipStream_t st, bool recompute) {
   constexpr int DVT = D >= 32 ? 32 : D;
-  if (recompute) launch_chunk_fwd_core<E, D, C>(a, st, kFwdStore);  // operands, Hc, W per chunk
+  if (recompute) launch_chunk_fwd_core<E, D, C, false>(a, st, kFwdStore);  // operands, Hc, W per chunk
   {
-    GDN_PROF("chunk_state_bwd", st);
+    constexpr bool wide = use_wide_state<E, D, C>();
+    const char* name = wide ? "chunk_state_bwd:wide128"
+                            : (DVT == 16 ? "chunk_state_bwd:tiled16" : "chunk_state_bwd:tiled32");
+    GDN_PROF(name, st);
     if constexpr (use_wide_state<E, D, C>()) launch_state_bwd_wide(a, st);
     else state_bwd_kernel<E, D, C, DVT><<<dim3(state_grid(a.N, a.Hk, a.G, D / DVT)), kChunkThreads, 0, st>>>(a);
   }
@@ -927,9 +959,12 @@ static bool dispatch(const gdn_shape* s, F&& f) {
     GDN_CASE(bf16, 64, 16) GDN_CASE(bf16, 64, 32) GDN_CASE(bf16, 64, 64)
     GDN_CASE(bf16, 128, 16) GDN_CASE(bf16, 128, 32) GDN_CASE(bf16, 128, 64)
   } else if (s->dtype == GDN_F32) {
-    GDN_CASE(float, 16, 16) GDN_CASE(float, 16, 32) GDN_CASE(float, 16, 64)
-    GDN_CASE(float, 32, 16) GDN_CASE(float, 32, 32) GDN_CASE(float, 32, 64)
-    GDN_CASE(float, 64, 16) GDN_CASE(float, 64, 32) GDN_CASE(float, 64, 64)
+    // float32 runs chunks of at most 32: at 64 the chunk backward's dg (a
+    // reverse sum over the chunk of terms that largely cancel) reaches the
+    // float32 bar of 1e-4 x RMS (measured 1.06e-4 at d = 32)
+    GDN_CASE(float, 16, 16) GDN_CASE(float, 16, 32)
+    GDN_CASE(float, 32, 16) GDN_CASE(float, 32, 32)
+    GDN_CASE(float, 64, 16) GDN_CASE(float, 64, 32)
     GDN_CASE(float, 128, 16) GDN_CASE(float, 128, 32)
   }
 #undef GDN_CASE
@@ -940,34 +975,69 @@ bool chunk_supported(const gdn_shape* s) {
   return dispatch(s, [&]<typename E, int D, int C>() {});
 }
 
+static void set_gates(ChunkArgs& a, const gdn_gate_inputs* gi) {
+  if (!gi) return;
+  a.g = a.beta = nullptr;
+  a.ga = gi->a; a.gb = gi->b; a.A_log = gi->A_log; a.dt_bias = gi->dt_bias;
+}
+
 bool run_chunk_fwd(const gdn_shape* s, const void* q, const void* k, const void* v, int64_t sqk, int64_t sv,
-                   const float* g, const float* beta, const int32_t* cu, const float* h0, void* o, float* ht,
-                   void* ws, bool save, hipStream_t st) {
+                   const float* g, const float* beta, const gdn_gate_inputs* gi, const int32_t* cu,
+                   const float* h0, void* o, float* ht, void* ws, bool save, hipStream_t st) {
   ChunkArgs a = {};
   a.q = q; a.k = k; a.v = v; a.sqk = sqk; a.sv = sv; a.g = g; a.beta = beta; a.cu = cu; a.h0 = h0;
+  set_gates(a, gi);
   a.o = o; a.ht = ht;
   a.N = s->n_seqs; a.T = s->total_tokens; a.Hk = s->h_qk; a.Hv = s->h_v; a.G = s->h_v / s->h_qk;
   a.max_chunks = (int)max_chunks(s); a.scale = s->scale;
   fill_ws(a, s, ws);
   run_chunk_index(s, cu, (int32_t*)a.table, (int32_t*)a.seq_chunk0, st);
   return dispatch(s, [&]<typename E, int D, int C>() {
-    launch_chunk_fwd_core<E, D, C>(a, st, save ? kFwdBoth : kFwdOut);
+    launch_chunk_fwd_core<E, D, C, false>(a, st, save ? kFwdBoth : kFwdOut);
   });
 }
 
-bool run_chunk_bwd(const gdn_shape* s, const void* q, const void* k, const void* v, int64_t sqk, int64_t sv,
-                   const float* g, const float* beta, const int32_t* cu, const float* h0, const void* d_o,
-                   const float* dht, void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0,
-                   void* ws, bool saved, hipStream_t st) {
+bool run_chunk_fwd_f8(const gdn_shape* s, const void* q, const void* k, const void* v, int64_t sqk, int64_t sv,
+                      const float scales[3], const float* g, const float* beta, const int32_t* cu, const float* h0,
+                      void* o, float* ht, void* ws, hipStream_t st) {
+  if (s->dtype != GDN_BF16 || s->d_k != 128 || s->chunk != 64) return false;
   ChunkArgs a = {};
   a.q = q; a.k = k; a.v = v; a.sqk = sqk; a.sv = sv; a.g = g; a.beta = beta; a.cu = cu; a.h0 = h0;
+  a.o = o; a.ht = ht;
+  a.N = s->n_seqs; a.T = s->total_tokens; a.Hk = s->h_qk; a.Hv = s->h_v; a.G = s->h_v / s->h_qk;
+  a.max_chunks = (int)max_chunks(s); a.scale = s->scale;
+  for (int i = 0; i < 3; ++i) a.f8_scale[i] = scales[i];
+  fill_ws(a, s, ws);
+  run_chunk_index(s, cu, (int32_t*)a.table, (int32_t*)a.seq_chunk0, st);
+  launch_chunk_fwd_core<bf16, 128, 64, true>(a, st, kFwdOut);
+  return true;
+}
+
+bool run_chunk_bwd(const gdn_shape* s, const void* q, const void* k, const void* v, int64_t sqk, int64_t sv,
+                   const float* g, const float* beta, const gdn_gate_inputs* gi, const int32_t* cu,
+                   const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, float* dg,
+                   float* dbeta, const gdn_gate_grads* gg, float* dh0, void* ws, bool saved, hipStream_t st) {
+  ChunkArgs a = {};
+  a.q = q; a.k = k; a.v = v; a.sqk = sqk; a.sv = sv; a.g = g; a.beta = beta; a.cu = cu; a.h0 = h0;
+  set_gates(a, gi);
   a.o = nullptr; a.ht = nullptr;
   a.d_o = d_o; a.dht = dht; a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = dh0;
+  if (gg) {
+    a.dg = a.dbeta = nullptr;
+    a.da = gg->da; a.db = gg->db;
+  }
   a.N = s->n_seqs; a.T = s->total_tokens; a.Hk = s->h_qk; a.Hv = s->h_v; a.G = s->h_v / s->h_qk;
   a.max_chunks = (int)max_chunks(s); a.scale = s->scale;
   fill_ws(a, s, ws);
   if (!saved) run_chunk_index(s, cu, (int32_t*)a.table, (int32_t*)a.seq_chunk0, st);
-  return dispatch(s, [&]<typename E, int D, int C>() { launch_chunk_bwd_core<E, D, C>(a, st, !saved); });
+  if (!dispatch(s, [&]<typename E, int D, int C>() { launch_chunk_bwd_core<E, D, C>(a, st, !saved); }))
+    return false;
+  if (gg) {  // dA_log, ddt_bias: the per-chunk shares summed over chunks in a fixed order
+    GDN_PROF("gates_dw_sum", st);
+    launch_colsum(a.gpart, a.max_chunks, a.Hv, gg->dA_log, st);
+    launch_colsum(a.gpart + (size_t)a.max_chunks * a.Hv, a.max_chunks, a.Hv, gg->ddt_bias, st);
+  }
+  return true;
 }
 
 }  // namespace gdn

@@ -23,6 +23,12 @@ struct ChunkArgs {
   int64_t sqk, sv;
   const float* g;
   const float* beta;
+  // raw gate inputs (the fused-gate entry points; g and beta are then NULL):
+  // g = -exp(A_log[h]) softplus(ga + dt_bias[h]), beta = sigmoid(gb)
+  const float* ga;       // [T][Hv]
+  const float* gb;       // [T][Hv]
+  const float* A_log;    // [Hv]
+  const float* dt_bias;  // [Hv]
   const int32_t* cu;
   const float* h0;
   // forward outputs
@@ -37,10 +43,15 @@ struct ChunkArgs {
   float* dg;
   float* dbeta;
   float* dh0;
+  // fused-gate backward: gradients w.r.t. the raw gate inputs (dg, dbeta NULL)
+  float* da;             // [T][Hv]
+  float* db;             // [T][Hv]
+  float* gpart;          // workspace [2][max_chunks][Hv]: per-chunk sums of dg g and da
   // sizes
   int N, T, Hk, Hv, G, max_chunks;
   float scale;
   int kt_plain;  // the preparation writes Kt = k_s^T unscaled (for the 16-column state pass)
+  float f8_scale[3];  // fp8 inputs: power-of-two scales of q, k and v (q, k, v then point to e4m3 bytes)
   // workspace
   const int32_t* table;       // [max_chunks][4]
   const int32_t* seq_chunk0;  // [N+1]
@@ -71,6 +82,18 @@ struct ChunkArgs {
   float* dP;                  // [slot][C][C]  scale dO W^T (lower-inclusive, rows < len)
   float* hdot;                // [slot]        <Hc, dHn>
 };
+
+
+// g and beta of token t, v-head h: the caller's arrays, or computed from the
+// raw gate inputs (the same functions as gdn_gates)
+__device__ __forceinline__ float chunk_g(const ChunkArgs& a, int64_t t, int h) {
+  if (a.ga) return -__expf(a.A_log[h]) * gate_softplus(a.ga[t * a.Hv + h] + a.dt_bias[h]);
+  return a.g[t * a.Hv + h];
+}
+__device__ __forceinline__ float chunk_beta(const ChunkArgs& a, int64_t t, int h) {
+  if (a.gb) return gate_sigmoid(a.gb[t * a.Hv + h]);
+  return a.beta[t * a.Hv + h];
+}
 
 template <typename E> struct Pad {
   static constexpr int E16 = 16 / (int)sizeof(E);  // elements per 16 bytes
@@ -333,6 +356,31 @@ struct StateSmem {
 // writes 16 consecutive elements of a transposed row per lane group instead of
 // one element each of 16 rows a 16-byte piece apart (which fall in the same
 // LDS banks), at the price of 64-byte instead of 256-byte runs per global load.
+// fp8 inputs (OCP e4m3: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+// exponent field 0 is subnormal, m 2^-9).  Decoded exactly: normal values are
+// (1 + m/8) 2^(e-7), i.e. float bits ((e + 120) << 23) | (m << 20).  Every
+// e4m3 value times a power-of-two scale (within bf16's range) is a bf16 value,
+// so the decoded tile is exactly the bf16 tile of the dequantised inputs.
+// (The e4m3 NaN code, 0x7f / 0xff, is outside the supported inputs.)
+__device__ __forceinline__ float fp8_e4m3_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 0xFu, m = b & 7u;
+  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+  return __uint_as_float(__float_as_uint(mag) | ((b & 0x80u) << 24));
+}
+
+// 8 fp8 values (two little-endian words) -> 8 bf16 values times `scale` (a power of two)
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi, float scale) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t src = i < 2 ? lo : hi, sh = (i & 1) * 16;
+    const float a = fp8_e4m3_to_f32((src >> sh) & 0xFFu) * scale;
+    const float b = fp8_e4m3_to_f32((src >> (sh + 8)) & 0xFFu) * scale;
+    w[i] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);  // exact: <= 4 significant bits
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 template <typename T, int R, int COLS, int NTH = kChunkThreads, bool RF = false, bool BUF = true>
 struct TileRegs {
   static constexpr int V = 16 / (int)sizeof(T);
@@ -370,6 +418,25 @@ struct TileRegs {
       pos(e, row, c);
       const int off = e < TOTAL ? (int)(((int64_t)row * ld + c) * (int64_t)sizeof(T)) : 0x7fffffe0;
       r[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+    }
+  }
+  // The same tile from an fp8 (e4m3) source with a power-of-two scale: 8-byte
+  // pieces (8 elements) through a buffer resource over rows [0, rows_valid),
+  // decoded exactly into the bf16 registers load() would hold for the
+  // dequantised tile.  ld is in elements (= bytes).
+  __device__ __forceinline__ void load_f8(const uint8_t* g, int64_t ld, int rows_valid, float scale) {
+    static_assert(sizeof(T) == 2 && V == 8, "bf16 tiles");
+    const int64_t bytes = (int64_t)rows_valid * ld;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(g), 0, (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff), 0x00020000);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int e = threadIdx.x + i * NTH;
+      int row, c;
+      pos(e, row, c);
+      const int off = e < TOTAL ? (int)((int64_t)row * ld + c) : 0x7fffffe0;
+      const uint2 raw = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0));
+      r[i] = fp8x8_to_bf16x8(raw.x, raw.y, scale);
     }
   }
   // One guarded load per piece, each completed before the next is issued.
@@ -520,7 +587,7 @@ inline int state_grid(int N, int Hk, int G, int NVT) { return ((N * Hk + 7) / 8)
 // State passes with one 512-thread workgroup per (sequence, v-head), for
 // bf16, d = 128, chunk 64 (state_wide.hip).
 // half: two workgroups per (sequence, v-head), 64 state columns each
-void launch_state_fwd_wide(const ChunkArgs& a, hipStream_t st, int mode, bool half);
+void launch_state_fwd_wide(const ChunkArgs& a, hipStream_t st, int mode, bool half, bool f8 = false);
 void launch_state_bwd_wide(const ChunkArgs& a, hipStream_t st);
 template <typename E, int D, int C>
 constexpr bool use_wide_state() { return sizeof(E) == 2 && D == 128 && C == 64; }

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(1024) void chunk_index_kernel(const int32_t* __rest
 // substitution, off-diagonal blocks by block substitution on fp32 MFMA),
 // U and Wk on MFMA.
 // ---------------------------------------------------------------------------
-template <typename E, int D, int C, bool LO_OUT, int NTH>
+template <typename E, int D, int C, bool LO_OUT, int NTH, bool F8 = false>
 __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
   constexpr int NW = NTH / kWave;
   using S = PrepSmem<E, D, C>;
@@ -93,16 +93,26 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
   TileRegs<E, C, D, NTH> rQ;
   TileRegs<E, C, D, NTH, true> rK;  // rows first: also written transposed
   float gv = 0.f, bv = 0.f;
+  // F8: q, k, v arrive as e4m3 bytes and are decoded on load (exactly: the
+  // registers then hold the bf16 tile of the dequantised inputs)
   auto load_head = [&](int tok, int n, int hh) {
-    pV.load((const E*)a.v + (int64_t)tok * a.sv + (int64_t)hh * D, a.sv, n);
+    if constexpr (F8)
+      pV.load_f8((const uint8_t*)a.v + (int64_t)tok * a.sv + (int64_t)hh * D, a.sv, n, a.f8_scale[2]);
+    else
+      pV.load((const E*)a.v + (int64_t)tok * a.sv + (int64_t)hh * D, a.sv, n);
     if (w == 0 && lane < n) {
-      gv = a.g[(int64_t)(tok + lane) * a.Hv + hh];
-      bv = a.beta[(int64_t)(tok + lane) * a.Hv + hh];
+      gv = chunk_g(a, tok + lane, hh);
+      bv = chunk_beta(a, tok + lane, hh);
     }
   };
   auto load_item = [&](int4 e, int jj) {
-    rQ.load((const E*)a.q + (int64_t)e.y * a.sqk + (int64_t)jj * D, a.sqk, e.z);
-    rK.load((const E*)a.k + (int64_t)e.y * a.sqk + (int64_t)jj * D, a.sqk, e.z);
+    if constexpr (F8) {
+      rQ.load_f8((const uint8_t*)a.q + (int64_t)e.y * a.sqk + (int64_t)jj * D, a.sqk, e.z, a.f8_scale[0]);
+      rK.load_f8((const uint8_t*)a.k + (int64_t)e.y * a.sqk + (int64_t)jj * D, a.sqk, e.z, a.f8_scale[1]);
+    } else {
+      rQ.load((const E*)a.q + (int64_t)e.y * a.sqk + (int64_t)jj * D, a.sqk, e.z);
+      rK.load((const E*)a.k + (int64_t)e.y * a.sqk + (int64_t)jj * D, a.sqk, e.z);
+    }
     load_head(e.y, e.z, jj * a.G);
   };
   int item = blockIdx.x;
@@ -320,7 +330,7 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
 //   OUT   = false: writes, per chunk, the entering state Hc and W (for the
 //                  backward pass), and the final state if asked
 // ---------------------------------------------------------------------------
-template <typename E, int D, int C, int DVT, int MODE, bool KP = false>
+template <typename E, int D, int C, int DVT, int MODE, bool KP = false, bool F8 = false>
 __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
   constexpr bool OUT = MODE & kFwdOut, STORE = MODE & kFwdStore;
   using S = StateSmem<E, D, C, DVT, OUT, KP>;
@@ -386,7 +396,10 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
     pKt.load((const E*)a.Kt + slot * D * C, C, D);
     if constexpr (KL) pKtl.load((const E*)a.Ktl + slot * D * C, C, D);
     if constexpr (OUT) {
-      pQ.load((const E*)a.q + (int64_t)ptok * a.sqk + (int64_t)j * D, a.sqk, plen);
+      if constexpr (F8)
+        pQ.load_f8((const uint8_t*)a.q + (int64_t)ptok * a.sqk + (int64_t)j * D, a.sqk, plen, a.f8_scale[0]);
+      else
+        pQ.load((const E*)a.q + (int64_t)ptok * a.sqk + (int64_t)j * D, a.sqk, plen);
       pP.load(a.P + slot * C * C, C, C);
     }
     pU.load(a.U + slot * C * D + col0, D, C);
@@ -561,16 +574,21 @@ inline int state_columns(const ChunkArgs& a, int D, int mode) {
   return chains < (mode == kFwdOut ? 4 * kNumCUs : kNumCUs) ? D / 2 : D;
 }
 
-template <typename E, int D, int C, int DVT, bool KP = false>
+template <typename E, int D, int C, int DVT, bool KP = false, bool F8 = false>
 static void launch_state_fwd_tiled(const ChunkArgs& a, hipStream_t st, int mode) {
   const dim3 grid(state_grid(a.N, a.Hk, a.G, D / DVT));
+  if constexpr (F8) {  // fp8 inputs: inference only
+    state_fwd_kernel<E, D, C, DVT, kFwdOut, KP, true><<<grid, kChunkThreads, 0, st>>>(a);
+    return;
+  }
   if (mode == kFwdOut) state_fwd_kernel<E, D, C, DVT, kFwdOut, KP><<<grid, kChunkThreads, 0, st>>>(a);
   else if (mode == kFwdStore) state_fwd_kernel<E, D, C, DVT, kFwdStore, KP><<<grid, kChunkThreads, 0, st>>>(a);
   else state_fwd_kernel<E, D, C, DVT, kFwdBoth, KP><<<grid, kChunkThreads, 0, st>>>(a);
 }
 
-template <typename E, int D, int C>
+template <typename E, int D, int C, bool F8>
 void launch_chunk_fwd_core(const ChunkArgs& args, hipStream_t st, int mode) {
+  static_assert(!F8 || use_wide_state<E, D, C>(), "fp8 inputs: bf16, d = 128, chunk 64");
   constexpr int DVT = state_dvt<E, D>();
   // The state passes at bf16, d = 128, chunk 64 read the plain K^T (exact in
   // bf16) and apply the decay to W's rows: no K lo part to write, load or
@@ -579,7 +597,16 @@ void launch_chunk_fwd_core(const ChunkArgs& args, hipStream_t st, int mode) {
   ChunkArgs a = args;
   a.kt_plain = use_wide_state<E, D, C>();
   static const char* prep_name[4] = {"", "chunk_prep", "chunk_prep_bwd", "chunk_prep_save"};
-  static const char* state_name[4] = {"", "chunk_state_fwd", "chunk_state_store", "chunk_state_save"};
+  // the timing record names the state-pass variant that ran (whole or half
+  // state per workgroup, or the column tile of the tiled pass)
+  static const char* state_name[4][4] = {
+      {"", "", "", ""},
+      {"chunk_state_fwd:wide128", "chunk_state_fwd:wide64", "chunk_state_fwd:tiled16", "chunk_state_fwd:tiled32"},
+      {"chunk_state_store:wide128", "chunk_state_store:wide64", "chunk_state_store:tiled16",
+       "chunk_state_store:tiled32"},
+      {"chunk_state_save:wide128", "chunk_state_save:wide64", "chunk_state_save:tiled16",
+       "chunk_state_save:tiled32"}};
+  const int variant = nc == 16 ? 2 : (use_wide_state<E, D, C>() ? (nc < D ? 1 : 0) : (DVT == 16 ? 2 : 3));
   // Inference preparation runs persistent: as many workgroups as fit at once
   // (its LDS use allows one per CU at d = 128, chunk 64), each walking its
   // share of items with the next one's loads in flight (long 65536: 1.69 ->
@@ -593,27 +620,29 @@ void launch_chunk_fwd_core(const ChunkArgs& args, hipStream_t st, int mode) {
   {
     GDN_PROF(prep_name[mode], st);
     constexpr int NTH = D >= 64 ? 512 : kChunkThreads;  // 8 waves for the wide heads
-    if (mode == kFwdOut) prep_kernel<E, D, C, false, NTH><<<gprep, NTH, 0, st>>>(a);
+    if constexpr (F8) prep_kernel<E, D, C, false, NTH, true><<<gprep, NTH, 0, st>>>(a);
+    else if (mode == kFwdOut) prep_kernel<E, D, C, false, NTH><<<gprep, NTH, 0, st>>>(a);
     else prep_kernel<E, D, C, true, NTH><<<gprep, NTH, 0, st>>>(a);
   }
-  GDN_PROF(state_name[mode], st);
+  GDN_PROF(state_name[mode][variant], st);
   if constexpr (use_wide_state<E, D, C>()) {
-    if (nc == 16) launch_state_fwd_tiled<E, D, C, 16, true>(a, st, mode);
-    else launch_state_fwd_wide(a, st, mode, nc < D);
+    if (nc == 16) launch_state_fwd_tiled<E, D, C, 16, true, F8>(a, st, mode);
+    else launch_state_fwd_wide(a, st, mode, nc < D, F8);
     return;
   }
   launch_state_fwd_tiled<E, D, C, DVT>(a, st, mode);
 }
 
 // explicit instantiation helpers used by the dispatcher in chunk_bwd.hip
-#define GDN_INST_FWD(E, D, C) template void launch_chunk_fwd_core<E, D, C>(const ChunkArgs&, hipStream_t, int);
+#define GDN_INST_FWD(E, D, C) template void launch_chunk_fwd_core<E, D, C, false>(const ChunkArgs&, hipStream_t, int);
+template void launch_chunk_fwd_core<bf16, 128, 64, true>(const ChunkArgs&, hipStream_t, int);
 GDN_INST_FWD(bf16, 16, 16) GDN_INST_FWD(bf16, 16, 32) GDN_INST_FWD(bf16, 16, 64)
 GDN_INST_FWD(bf16, 32, 16) GDN_INST_FWD(bf16, 32, 32) GDN_INST_FWD(bf16, 32, 64)
 GDN_INST_FWD(bf16, 64, 16) GDN_INST_FWD(bf16, 64, 32) GDN_INST_FWD(bf16, 64, 64)
 GDN_INST_FWD(bf16, 128, 16) GDN_INST_FWD(bf16, 128, 32) GDN_INST_FWD(bf16, 128, 64)
-GDN_INST_FWD(float, 16, 16) GDN_INST_FWD(float, 16, 32) GDN_INST_FWD(float, 16, 64)
-GDN_INST_FWD(float, 32, 16) GDN_INST_FWD(float, 32, 32) GDN_INST_FWD(float, 32, 64)
-GDN_INST_FWD(float, 64, 16) GDN_INST_FWD(float, 64, 32) GDN_INST_FWD(float, 64, 64)
+GDN_INST_FWD(float, 16, 16) GDN_INST_FWD(float, 16, 32)
+GDN_INST_FWD(float, 32, 16) GDN_INST_FWD(float, 32, 32)
+GDN_INST_FWD(float, 64, 16) GDN_INST_FWD(float, 64, 32)
 GDN_INST_FWD(float, 128, 16) GDN_INST_FWD(float, 128, 32)
 #undef GDN_INST_FWD
 

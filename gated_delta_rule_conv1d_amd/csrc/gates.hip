@@ -19,8 +19,8 @@ namespace gdn {
 constexpr int kGateThreads = 256;
 constexpr int kGateBwdTokens = 256;  // tokens per backward block (one partial row each)
 
-__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x))); }
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + __expf(-x)); }
+__device__ __forceinline__ float softplus_f(float x) { return gate_softplus(x); }
+__device__ __forceinline__ float sigmoid_f(float x) { return gate_sigmoid(x); }
 
 __global__ __launch_bounds__(kGateThreads) void gates_fwd_kernel(const float* __restrict__ a,
                                                                  const float* __restrict__ b,

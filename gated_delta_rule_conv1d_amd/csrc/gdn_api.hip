@@ -3,6 +3,8 @@
 // enqueued.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "gdn_internal.h"
 
 using namespace gdn;
@@ -41,39 +43,53 @@ bool stride_ok(const gdn_shape* s, int64_t stride, int64_t min_elems) {
 
 gdn_status launched() { return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
 
-// forward; with save, the workspace (backward-sized) keeps what the backward reads
+bool gates_ok(const gdn_gate_inputs* gi, bool any) {
+  if (!gi || !gi->A_log || !gi->dt_bias || (any && (!gi->a || !gi->b))) return false;
+  return aligned4(gi->a) && aligned4(gi->b) && aligned4(gi->A_log) && aligned4(gi->dt_bias);
+}
+
+bool gate_grads_ok(const gdn_gate_grads* gg, bool any) {
+  if (!gg || !gg->dA_log || !gg->ddt_bias || (any && (!gg->da || !gg->db))) return false;
+  return aligned4(gg->da) && aligned4(gg->db) && aligned4(gg->dA_log) && aligned4(gg->ddt_bias);
+}
+
+// forward; with save, the workspace (backward-sized) keeps what the backward reads;
+// with gi, g and beta come from the raw gate inputs
 gdn_status chunk_fwd_call(const gdn_shape* shape, const void* q, const void* k, const void* v, int64_t tok_stride_qk,
-                          int64_t tok_stride_v, const float* g, const float* beta, const int32_t* cu_seqlens,
-                          const float* h0, void* o, float* ht, void* ws, size_t ws_bytes, bool save,
-                          gdn_stream stream) {
+                          int64_t tok_stride_v, const float* g, const float* beta, const gdn_gate_inputs* gi,
+                          bool gated, const int32_t* cu_seqlens, const float* h0, void* o, float* ht, void* ws,
+                          size_t ws_bytes, bool save, gdn_stream stream) {
   gdn_status st = check_shape(shape);
   if (st != GDN_OK) return st;
   if ((st = check_chunk(shape)) != GDN_OK) return st;
   const bool any = shape->total_tokens > 0;
-  if (!cu_seqlens || (any && (!q || !k || !v || !g || !beta || !o))) return GDN_ERR_INVALID_ARG;
+  if (gated ? !gates_ok(gi, any) : (any && (!g || !beta))) return GDN_ERR_INVALID_ARG;
+  if (!cu_seqlens || (any && (!q || !k || !v || !o))) return GDN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return GDN_ERR_INVALID_ARG;
   if (!stride_ok(shape, tok_stride_qk, (int64_t)shape->h_qk * shape->d_k) ||
       !stride_ok(shape, tok_stride_v, (int64_t)shape->h_v * shape->d_v))
     return GDN_ERR_INVALID_ARG;
   const size_t need = save ? chunk_bwd_ws_bytes(shape) : chunk_fwd_ws_bytes(shape);
   if (!ws || !aligned16(ws) || ws_bytes < need) return GDN_ERR_WORKSPACE;
-  if (!run_chunk_fwd(shape, q, k, v, tok_stride_qk, tok_stride_v, g, beta, cu_seqlens, h0, o, ht, ws, save,
-                     (hipStream_t)stream))
+  if (!run_chunk_fwd(shape, q, k, v, tok_stride_qk, tok_stride_v, g, beta, gated ? gi : nullptr, cu_seqlens, h0,
+                     o, ht, ws, save, (hipStream_t)stream))
     return GDN_ERR_UNSUPPORTED;
   return launched();
 }
 
 // backward; with saved, the workspace holds what gdn_chunk_fwd_save left there
 gdn_status chunk_bwd_call(const gdn_shape* shape, const void* q, const void* k, const void* v, int64_t tok_stride_qk,
-                          int64_t tok_stride_v, const float* g, const float* beta, const int32_t* cu_seqlens,
-                          const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, float* dg,
-                          float* dbeta, float* dh0, void* ws, size_t ws_bytes, bool saved, gdn_stream stream) {
+                          int64_t tok_stride_v, const float* g, const float* beta, const gdn_gate_inputs* gi,
+                          bool gated, const int32_t* cu_seqlens, const float* h0, const void* d_o, const float* dht,
+                          void* dq, void* dk, void* dv, float* dg, float* dbeta, const gdn_gate_grads* gg,
+                          float* dh0, void* ws, size_t ws_bytes, bool saved, gdn_stream stream) {
   gdn_status st = check_shape(shape);
   if (st != GDN_OK) return st;
   if ((st = check_chunk(shape)) != GDN_OK) return st;
   const bool any = shape->total_tokens > 0;
-  if (!cu_seqlens || (any && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta)))
+  if (gated ? (!gates_ok(gi, any) || !gate_grads_ok(gg, any)) : (any && (!g || !beta || !dg || !dbeta)))
     return GDN_ERR_INVALID_ARG;
+  if (!cu_seqlens || (any && (!q || !k || !v || !d_o || !dq || !dk || !dv))) return GDN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_o) || !aligned16(dq) || !aligned16(dk) ||
       !aligned16(dv))
     return GDN_ERR_INVALID_ARG;
@@ -81,8 +97,8 @@ gdn_status chunk_bwd_call(const gdn_shape* shape, const void* q, const void* k, 
       !stride_ok(shape, tok_stride_v, (int64_t)shape->h_v * shape->d_v))
     return GDN_ERR_INVALID_ARG;
   if (!ws || !aligned16(ws) || ws_bytes < chunk_bwd_ws_bytes(shape)) return GDN_ERR_WORKSPACE;
-  if (!run_chunk_bwd(shape, q, k, v, tok_stride_qk, tok_stride_v, g, beta, cu_seqlens, h0, d_o, dht, dq, dk, dv, dg,
-                     dbeta, dh0, ws, saved, (hipStream_t)stream))
+  if (!run_chunk_bwd(shape, q, k, v, tok_stride_qk, tok_stride_v, g, beta, gated ? gi : nullptr, cu_seqlens, h0,
+                     d_o, dht, dq, dk, dv, dg, dbeta, gated ? gg : nullptr, dh0, ws, saved, (hipStream_t)stream))
     return GDN_ERR_UNSUPPORTED;
   return launched();
 }
@@ -180,16 +196,16 @@ size_t gdn_chunk_fwd_workspace(const gdn_shape* shape) {
 gdn_status gdn_chunk_fwd(const gdn_shape* shape, const void* q, const void* k, const void* v, int64_t tok_stride_qk,
                          int64_t tok_stride_v, const float* g, const float* beta, const int32_t* cu_seqlens,
                          const float* h0, void* o, float* ht, void* ws, size_t ws_bytes, gdn_stream stream) {
-  return chunk_fwd_call(shape, q, k, v, tok_stride_qk, tok_stride_v, g, beta, cu_seqlens, h0, o, ht, ws, ws_bytes,
-                        false, stream);
+  return chunk_fwd_call(shape, q, k, v, tok_stride_qk, tok_stride_v, g, beta, nullptr, false, cu_seqlens, h0, o, ht,
+                        ws, ws_bytes, false, stream);
 }
 
 gdn_status gdn_chunk_fwd_save(const gdn_shape* shape, const void* q, const void* k, const void* v,
                               int64_t tok_stride_qk, int64_t tok_stride_v, const float* g, const float* beta,
                               const int32_t* cu_seqlens, const float* h0, void* o, float* ht, void* ws,
                               size_t ws_bytes, gdn_stream stream) {
-  return chunk_fwd_call(shape, q, k, v, tok_stride_qk, tok_stride_v, g, beta, cu_seqlens, h0, o, ht, ws, ws_bytes,
-                        true, stream);
+  return chunk_fwd_call(shape, q, k, v, tok_stride_qk, tok_stride_v, g, beta, nullptr, false, cu_seqlens, h0, o, ht,
+                        ws, ws_bytes, true, stream);
 }
 
 size_t gdn_chunk_bwd_workspace(const gdn_shape* shape) {
@@ -201,8 +217,8 @@ gdn_status gdn_chunk_bwd(const gdn_shape* shape, const void* q, const void* k, c
                          int64_t tok_stride_v, const float* g, const float* beta, const int32_t* cu_seqlens,
                          const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, float* dg,
                          float* dbeta, float* dh0, void* ws, size_t ws_bytes, gdn_stream stream) {
-  return chunk_bwd_call(shape, q, k, v, tok_stride_qk, tok_stride_v, g, beta, cu_seqlens, h0, d_o, dht, dq, dk, dv,
-                        dg, dbeta, dh0, ws, ws_bytes, false, stream);
+  return chunk_bwd_call(shape, q, k, v, tok_stride_qk, tok_stride_v, g, beta, nullptr, false, cu_seqlens, h0, d_o,
+                        dht, dq, dk, dv, dg, dbeta, nullptr, dh0, ws, ws_bytes, false, stream);
 }
 
 gdn_status gdn_chunk_bwd_saved(const gdn_shape* shape, const void* q, const void* k, const void* v,
@@ -210,8 +226,68 @@ gdn_status gdn_chunk_bwd_saved(const gdn_shape* shape, const void* q, const void
                                const int32_t* cu_seqlens, const float* h0, const void* d_o, const float* dht,
                                void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0, void* ws,
                                size_t ws_bytes, gdn_stream stream) {
-  return chunk_bwd_call(shape, q, k, v, tok_stride_qk, tok_stride_v, g, beta, cu_seqlens, h0, d_o, dht, dq, dk, dv,
-                        dg, dbeta, dh0, ws, ws_bytes, true, stream);
+  return chunk_bwd_call(shape, q, k, v, tok_stride_qk, tok_stride_v, g, beta, nullptr, false, cu_seqlens, h0, d_o,
+                        dht, dq, dk, dv, dg, dbeta, nullptr, dh0, ws, ws_bytes, true, stream);
+}
+
+gdn_status gdn_chunk_fwd_fp8(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                             int64_t tok_stride_qk, int64_t tok_stride_v, float scale_q, float scale_k, float scale_v,
+                             const float* g, const float* beta, const int32_t* cu_seqlens, const float* h0, void* o,
+                             float* ht, void* ws, size_t ws_bytes, gdn_stream stream) {
+  gdn_status st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  if ((st = check_chunk(shape)) != GDN_OK) return st;
+  if (shape->dtype != GDN_BF16 || shape->d_k != 128 || shape->chunk != 64) return GDN_ERR_UNSUPPORTED;
+  const float scales[3] = {scale_q, scale_k, scale_v};
+  for (float x : scales) {  // powers of two: the decoded inputs are then exact bf16 values
+    int e = 0;
+    if (!(x > 0.f) || !std::isfinite(x) || std::frexp(x, &e) != 0.5f || e < -100 || e > 100)
+      return GDN_ERR_INVALID_ARG;
+  }
+  const bool any = shape->total_tokens > 0;
+  if (!cu_seqlens || (any && (!q || !k || !v || !g || !beta || !o))) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return GDN_ERR_INVALID_ARG;
+  const int64_t nqk = (int64_t)shape->h_qk * shape->d_k, nv = (int64_t)shape->h_v * shape->d_v;
+  if (tok_stride_qk < nqk || tok_stride_qk % 16 || tok_stride_v < nv || tok_stride_v % 16) return GDN_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws) || ws_bytes < chunk_fwd_ws_bytes(shape)) return GDN_ERR_WORKSPACE;
+  if (!run_chunk_fwd_f8(shape, q, k, v, tok_stride_qk, tok_stride_v, scales, g, beta, cu_seqlens, h0, o, ht, ws,
+                        (hipStream_t)stream))
+    return GDN_ERR_UNSUPPORTED;
+  return launched();
+}
+
+gdn_status gdn_chunk_fwd_gated(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                               int64_t tok_stride_qk, int64_t tok_stride_v, const gdn_gate_inputs* gates,
+                               const int32_t* cu_seqlens, const float* h0, void* o, float* ht, void* ws,
+                               size_t ws_bytes, gdn_stream stream) {
+  return chunk_fwd_call(shape, q, k, v, tok_stride_qk, tok_stride_v, nullptr, nullptr, gates, true, cu_seqlens, h0, o,
+                        ht, ws, ws_bytes, false, stream);
+}
+
+gdn_status gdn_chunk_fwd_save_gated(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                                    int64_t tok_stride_qk, int64_t tok_stride_v, const gdn_gate_inputs* gates,
+                                    const int32_t* cu_seqlens, const float* h0, void* o, float* ht, void* ws,
+                                    size_t ws_bytes, gdn_stream stream) {
+  return chunk_fwd_call(shape, q, k, v, tok_stride_qk, tok_stride_v, nullptr, nullptr, gates, true, cu_seqlens, h0, o,
+                        ht, ws, ws_bytes, true, stream);
+}
+
+gdn_status gdn_chunk_bwd_gated(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                               int64_t tok_stride_qk, int64_t tok_stride_v, const gdn_gate_inputs* gates,
+                               const int32_t* cu_seqlens, const float* h0, const void* d_o, const float* dht,
+                               void* dq, void* dk, void* dv, const gdn_gate_grads* dgates, float* dh0, void* ws,
+                               size_t ws_bytes, gdn_stream stream) {
+  return chunk_bwd_call(shape, q, k, v, tok_stride_qk, tok_stride_v, nullptr, nullptr, gates, true, cu_seqlens, h0,
+                        d_o, dht, dq, dk, dv, nullptr, nullptr, dgates, dh0, ws, ws_bytes, false, stream);
+}
+
+gdn_status gdn_chunk_bwd_saved_gated(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                                     int64_t tok_stride_qk, int64_t tok_stride_v, const gdn_gate_inputs* gates,
+                                     const int32_t* cu_seqlens, const float* h0, const void* d_o,
+                                     const float* dht, void* dq, void* dk, void* dv, const gdn_gate_grads* dgates,
+                                     float* dh0, void* ws, size_t ws_bytes, gdn_stream stream) {
+  return chunk_bwd_call(shape, q, k, v, tok_stride_qk, tok_stride_v, nullptr, nullptr, gates, true, cu_seqlens, h0,
+                        d_o, dht, dq, dk, dv, nullptr, nullptr, dgates, dh0, ws, ws_bytes, true, stream);
 }
 
 gdn_status gdn_norm_gate(const gdn_shape* shape, const void* o, const void* z, const void* w_norm, float eps, void* y,

@@ -88,6 +88,13 @@ template <> struct Mma<float> {
   }
 };
 
+// Gates of the recurrence (see gates.hip): softplus(x) = max(x, 0) +
+// log1p(e^{-|x|}) (no overflow, no loss for very negative x), and the logistic
+// sigmoid.  The gate kernels and the chunk kernels that compute g and beta
+// from their raw inputs share these, so both give the same bits.
+__device__ __forceinline__ float gate_softplus(float x) { return fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x))); }
+__device__ __forceinline__ float gate_sigmoid(float x) { return 1.f / (1.f + __expf(-x)); }
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
 // accumulator coordinates

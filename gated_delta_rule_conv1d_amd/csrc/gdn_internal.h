@@ -47,12 +47,17 @@ bool chunk_supported(const gdn_shape* s);
 void run_chunk_index(const gdn_shape* s, const int32_t* cu, int32_t* table, int32_t* seq_chunk0, hipStream_t st);
 size_t chunk_fwd_ws_bytes(const gdn_shape* s);
 size_t chunk_bwd_ws_bytes(const gdn_shape* s);
+// fp8 (e4m3) q, k, v with power-of-two scales (q, k, v scale): bf16, d = 128, chunk 64 only
+bool run_chunk_fwd_f8(const gdn_shape* s, const void* q, const void* k, const void* v, int64_t sqk, int64_t sv,
+                      const float scales[3], const float* g, const float* beta, const int32_t* cu, const float* h0,
+                      void* o, float* ht, void* ws, hipStream_t st);
+// gi / gg non-NULL: the fused-gate forms (g, beta and dg, dbeta unused)
 bool run_chunk_fwd(const gdn_shape* s, const void* q, const void* k, const void* v, int64_t sqk, int64_t sv,
-                   const float* g, const float* beta, const int32_t* cu, const float* h0, void* o, float* ht,
-                   void* ws, bool save, hipStream_t st);
+                   const float* g, const float* beta, const gdn_gate_inputs* gi, const int32_t* cu,
+                   const float* h0, void* o, float* ht, void* ws, bool save, hipStream_t st);
 bool run_chunk_bwd(const gdn_shape* s, const void* q, const void* k, const void* v, int64_t sqk, int64_t sv,
-                   const float* g, const float* beta, const int32_t* cu, const float* h0, const void* d_o,
-                   const float* dht, void* dq, void* dk, void* dv, float* dg, float* dbeta, float* dh0,
-                   void* ws, bool saved, hipStream_t st);
+                   const float* g, const float* beta, const gdn_gate_inputs* gi, const int32_t* cu,
+                   const float* h0, const void* d_o, const float* dht, void* dq, void* dk, void* dv, float* dg,
+                   float* dbeta, const gdn_gate_grads* gg, float* dh0, void* ws, bool saved, hipStream_t st);
 
 }  // namespace gdn

@@ -1,8 +1,11 @@
 // Per-kernel HIP-event timing hook (diagnostics).  The events are created once
-// and reused; reading the totals synchronises on them.
+// and reused; reading the totals synchronises on them.  One mutex guards the
+// records and the event pool, and each launch scope remembers its own record,
+// so launches from several host threads each time their own kernel.
 #include <atomic>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -18,9 +21,9 @@ struct Rec {
 };
 
 std::atomic<int> g_on{0};
-std::vector<Rec> g_recs;       // records of the current window
+std::mutex g_mu;                 // guards g_recs and g_pool
+std::vector<Rec> g_recs;         // records of the current window
 std::vector<hipEvent_t> g_pool;  // events available for reuse
-size_t g_open = (size_t)-1;
 
 hipEvent_t take() {
   if (!g_pool.empty()) {
@@ -35,23 +38,25 @@ hipEvent_t take() {
 
 }  // namespace
 
-void prof_begin(const char* name, hipStream_t st) {
+size_t prof_begin(const char* name, hipStream_t st) {
+  std::lock_guard<std::mutex> lock(g_mu);
   Rec r{name, take(), take()};
-  if (r.a) hipEventRecord(r.a, st);
+  if (r.a) (void)hipEventRecord(r.a, st);
   g_recs.push_back(r);
-  g_open = g_recs.size() - 1;
+  return g_recs.size() - 1;
 }
 
-void prof_end(hipStream_t st) {
-  if (g_open < g_recs.size() && g_recs[g_open].b) hipEventRecord(g_recs[g_open].b, st);
-  g_open = (size_t)-1;
+void prof_end(size_t rec, hipStream_t st) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (rec < g_recs.size() && g_recs[rec].b) (void)hipEventRecord(g_recs[rec].b, st);
 }
 
-ProfScope::ProfScope(const char* name, hipStream_t s) : st(s), on(g_on.load(std::memory_order_relaxed) != 0) {
-  if (on) prof_begin(name, st);
+ProfScope::ProfScope(const char* name, hipStream_t s)
+    : st(s), on(g_on.load(std::memory_order_relaxed) != 0), rec((size_t)-1) {
+  if (on) rec = prof_begin(name, st);
 }
 ProfScope::~ProfScope() {
-  if (on) prof_end(st);
+  if (on) prof_end(rec, st);
 }
 
 }  // namespace gdn
@@ -62,6 +67,7 @@ extern "C" {
 
 // Start (1) or stop (0) recording; starting clears earlier records.
 void gdn_profile_enable(int on) {
+  std::lock_guard<std::mutex> lock(g_mu);
   if (on) {
     for (auto& r : g_recs) {
       if (r.a) g_pool.push_back(r.a);
@@ -76,12 +82,13 @@ void gdn_profile_enable(int on) {
 // into buf; waits for the recorded events.  Returns the number of bytes
 // needed (excluding the terminating zero).
 size_t gdn_profile_report(char* buf, size_t cap) {
+  std::lock_guard<std::mutex> lock(g_mu);
   std::vector<std::string> names;
   std::vector<double> tot;
   std::vector<long> cnt;
   for (auto& r : g_recs) {
     if (!r.a || !r.b) continue;
-    hipEventSynchronize(r.b);
+    if (hipEventSynchronize(r.b) != hipSuccess) continue;
     float ms = 0.f;
     if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) continue;
     size_t i = 0;

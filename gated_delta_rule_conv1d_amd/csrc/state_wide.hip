@@ -91,12 +91,17 @@ struct Buf {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
   }
   __device__ __forceinline__ M::frag fr(int off) const { return __builtin_bit_cast(M::frag, u4(off)); }
+  // 8 e4m3 bytes at byte offset off, decoded exactly to a bf16 fragment
+  __device__ __forceinline__ M::frag fr_f8(int off, float scale) const {
+    const uint2 raw = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    return __builtin_bit_cast(M::frag, fp8x8_to_bf16x8(raw.x, raw.y, scale));
+  }
 };
 
 // NC = 128: the whole state; NC = 64: half of its columns (exact: the update
 // multiplies the state from the left only), two workgroups per (sequence,
 // v-head) with the same per-element arithmetic
-template <int MODE, int NC>
+template <int MODE, int NC, bool F8 = false>
 __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
   constexpr bool OUT = MODE & kFwdOut, STORE = MODE & kFwdStore;
   constexpr int D = kD, C = kC;
@@ -151,7 +156,12 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
     const Buf wk((const E*)a.Wk + slot * C * D, C * D * 2);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) wkf[ks] = wk.fr(a_off + ks * 64);
-    if constexpr (OUT) {  // q rows of the chunk; rows past len fall outside the buffer and read zero
+    if constexpr (OUT && F8) {  // e4m3 q rows, decoded exactly on load
+      const Buf qb((const uint8_t*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D, (int64_t)len * a.sqk);
+      const int q_off = (int)((int64_t)(rt1 * 16 + r16) * a.sqk + kq);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qf[ks] = qb.fr_f8(q_off + ks * 32, a.f8_scale[0]);
+    } else if constexpr (OUT) {  // q rows of the chunk; rows past len fall outside the buffer and read zero
       const Buf qb((const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D, (int64_t)len * a.sqk * 2);
       const int q_off = (int)(((int64_t)(rt1 * 16 + r16) * a.sqk + kq) * 2);
 #pragma unroll
@@ -504,16 +514,17 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
 }  // namespace
 
 template <int NC>
-static void launch_fwd_nc(const ChunkArgs& a, hipStream_t st, int mode) {
+static void launch_fwd_nc(const ChunkArgs& a, hipStream_t st, int mode, bool f8) {
   const dim3 grid(state_grid(a.N, a.Hk, a.G, kD / NC));
-  if (mode == kFwdOut) state_fwd_wide_kernel<kFwdOut, NC><<<grid, kThreads, 0, st>>>(a);
+  if (f8) state_fwd_wide_kernel<kFwdOut, NC, true><<<grid, kThreads, 0, st>>>(a);  // fp8 inputs: inference only
+  else if (mode == kFwdOut) state_fwd_wide_kernel<kFwdOut, NC><<<grid, kThreads, 0, st>>>(a);
   else if (mode == kFwdStore) state_fwd_wide_kernel<kFwdStore, NC><<<grid, kThreads, 0, st>>>(a);
   else state_fwd_wide_kernel<kFwdBoth, NC><<<grid, kThreads, 0, st>>>(a);
 }
 
-void launch_state_fwd_wide(const ChunkArgs& a, hipStream_t st, int mode, bool half) {
-  if (half) launch_fwd_nc<kD / 2>(a, st, mode);
-  else launch_fwd_nc<kD>(a, st, mode);
+void launch_state_fwd_wide(const ChunkArgs& a, hipStream_t st, int mode, bool half, bool f8) {
+  if (half) launch_fwd_nc<kD / 2>(a, st, mode, f8);
+  else launch_fwd_nc<kD>(a, st, mode, f8);
 }
 
 void launch_state_bwd_wide(const ChunkArgs& a, hipStream_t st) {

@@ -48,29 +48,37 @@ class GatedDeltaNetLayer:
                            ws=self._buf("gates", B.gates_bwd_workspace(self.shape)))
 
     def forward(self, x, w_conv, g, beta, cu_seqlens, z=None, w_norm=None, h0=None, want_ht=True,
-                for_backward=False):
+                for_backward=False, gates=None):
         """With for_backward=True the chunked recurrence keeps its per-chunk
         products in this layer's backward workspace (gdn_chunk_fwd_save), and
         the next backward() with the same inputs reads them instead of
-        recomputing them."""
+        recomputing them.  gates = (a, b, A_log, dt_bias) instead of g, beta
+        (both None): the chunk kernels compute the gates themselves
+        (gdn_chunk_fwd_gated)."""
         s = self.shape
         yc = B.conv1d(x, w_conv, cu_seqlens, s, self.l2_eps)
         q, k, v = self.split(yc)
-        if for_backward:
-            o, ht = B.chunk_fwd(q, k, v, g, beta, cu_seqlens, s, h0=h0, want_ht=want_ht,
-                                ws=self._buf("bwd", B.chunk_bwd_workspace(s)), save=True)
+        ws = (self._buf("bwd", B.chunk_bwd_workspace(s)) if for_backward
+              else self._buf("fwd", B.chunk_fwd_workspace(s)))
+        if gates is not None:
+            if g is not None or beta is not None:
+                raise ValueError("pass either g, beta or gates")
+            o, ht = B.chunk_fwd_gated(q, k, v, gates, cu_seqlens, s, h0=h0, want_ht=want_ht, ws=ws,
+                                      save=for_backward)
         else:
-            o, ht = B.chunk_fwd(q, k, v, g, beta, cu_seqlens, s, h0=h0, want_ht=want_ht,
-                                ws=self._buf("fwd", B.chunk_fwd_workspace(s)))
+            o, ht = B.chunk_fwd(q, k, v, g, beta, cu_seqlens, s, h0=h0, want_ht=want_ht, ws=ws, save=for_backward)
         self._saved = for_backward
         out = dict(y_conv=yc, o=o, ht=ht)
         if self.norm:
             out["y"] = B.norm_gate(o, z, w_norm, s, self.norm_eps)
         return out
 
-    def backward(self, dy, x, w_conv, g, beta, cu_seqlens, fwd, z=None, w_norm=None, h0=None, dht=None):
+    def backward(self, dy, x, w_conv, g, beta, cu_seqlens, fwd, z=None, w_norm=None, h0=None, dht=None,
+                 gates=None):
         """dy: gradient w.r.t. the layer output (norm output if present, else o).
-        Recomputes nothing of the conv except inside its own backward."""
+        Recomputes nothing of the conv except inside its own backward.  With
+        gates = (a, b, A_log, dt_bias) (as in forward) the result holds da, db,
+        dA_log, ddt_bias instead of dg, dbeta."""
         s = self.shape
         res = {}
         if self.norm:
@@ -82,13 +90,19 @@ class GatedDeltaNetLayer:
         q, k, v = self.split(fwd["y_conv"])
         dyc = torch.empty_like(fwd["y_conv"])
         dq, dk, dv = self.split(dyc)
-        r = B.chunk_bwd(q, k, v, g, beta, cu_seqlens, s, d_o, h0=h0, dht=dht, dq=dq, dk=dk, dv=dv,
-                        want_dh0=h0 is not None, ws=self._buf("bwd", B.chunk_bwd_workspace(s)),
-                        saved=self._saved)
+        ws = self._buf("bwd", B.chunk_bwd_workspace(s))
+        if gates is not None:
+            r = B.chunk_bwd_gated(q, k, v, gates, cu_seqlens, s, d_o, h0=h0, dht=dht, dq=dq, dk=dk, dv=dv,
+                                  want_dh0=h0 is not None, ws=ws, saved=self._saved)
+            res.update({key: r[key] for key in ("da", "db", "dA_log", "ddt_bias")})
+        else:
+            r = B.chunk_bwd(q, k, v, g, beta, cu_seqlens, s, d_o, h0=h0, dht=dht, dq=dq, dk=dk, dv=dv,
+                            want_dh0=h0 is not None, ws=ws, saved=self._saved)
+            res.update(dg=r["dg"], dbeta=r["dbeta"])
         self._saved = False  # the saved products are consumed
         dx, dwc = B.conv1d_bwd(dyc, x, w_conv, cu_seqlens, s, self.l2_eps,
                                ws=self._buf("conv", B.conv1d_bwd_workspace(s, self.width)))
-        res.update(d_o=d_o, dy_conv=dyc, dg=r["dg"], dbeta=r["dbeta"], dh0=r["dh0"], dx=dx, dw_conv=dwc)
+        res.update(d_o=d_o, dy_conv=dyc, dh0=r["dh0"], dx=dx, dw_conv=dwc)
         return res
 
 

@@ -26,7 +26,7 @@
  *    buffer, including workspace (sized by the *_workspace queries).  The
  *    library allocates no device memory, never synchronises and never reads
  *    device memory from the host; its only mutable global state is the opt-in
- *    timing record of gdn_profile_enable.  All work is enqueued on `stream`
+ *    timing record of gdn_profile_enable (mutex-guarded).  All work is enqueued on `stream`
  *    (a hipStream_t; NULL means the default stream).
  *  - Arguments are validated on the host before anything is enqueued; on any
  *    error nothing is launched.  Device-side contents that break a documented
@@ -79,7 +79,7 @@ typedef struct gdn_shape {
   int32_t h_v;          /* Hv >= 1, Hv % Hk == 0 */
   int32_t d_k;          /* 16, 32, 64 or 128 */
   int32_t d_v;          /* must equal d_k */
-  int32_t chunk;        /* 16, 32 or 64 (GDN_F32 with d=128 needs chunk <= 32) */
+  int32_t chunk;        /* 16, 32 or 64 (GDN_F32 needs chunk <= 32) */
   int32_t dtype;        /* GDN_F32 or GDN_BF16 */
   float scale;          /* query scale (o_t = scale * S_t q_t) */
 } gdn_shape;
@@ -222,6 +222,70 @@ gdn_status gdn_chunk_bwd_saved(const gdn_shape* shape, const void* q, const void
                                float* dg, float* dbeta, float* dh0, void* ws, size_t ws_bytes,
                                gdn_stream stream);
 
+/* gdn_chunk_fwd on fp8 inputs: q, k and v arrive as OCP e4m3 bytes (1 sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits) with one scale per tensor,
+ * value = e4m3 value * scale.  Pages: "Support Qwen35 SFT", feature list
+ * (fp8 training).  The scales must be powers of two (2^-100 .. 2^100;
+ * GDN_ERR_INVALID_ARG otherwise), so every dequantised input is a bf16 value:
+ * the kernels decode the bytes exactly as they load them and run the bf16
+ * path, and the results are bit-identical to gdn_chunk_fwd's on the
+ * dequantised bf16 tensors.  Token strides are in elements (bytes) and must
+ * be multiples of 16; shape->dtype is GDN_BF16 (the element type of o);
+ * supported at d = 128, chunk 64 (GDN_ERR_UNSUPPORTED otherwise).  The e4m3
+ * NaN code (0x7f, 0xff) is not a valid input.  Other arguments and the
+ * workspace (gdn_chunk_fwd_workspace) as gdn_chunk_fwd. */
+gdn_status gdn_chunk_fwd_fp8(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                             int64_t tok_stride_qk, int64_t tok_stride_v, float scale_q, float scale_k, float scale_v,
+                             const float* g, const float* beta, const int32_t* cu_seqlens, const float* h0, void* o,
+                             float* ht, void* ws, size_t ws_bytes, gdn_stream stream);
+
+/* --------------------------------------------------------------------------
+ * Fused gates: the chunked recurrence with g and beta computed inside its
+ * kernels from the gates' raw inputs, as gdn_gates would (same functions,
+ * same bits), so g and beta are never written or read as arrays; the
+ * backward returns the gradients w.r.t. those raw inputs, as gdn_gates_bwd
+ * would from dg and dbeta.  Page: "[Qwen3.5 MoE] Add hybrid decoder model",
+ * Summary (the softplus gate of GatedDeltaNet).
+ *   gates:  a, b float32 [T][Hv]; A_log, dt_bias float32 [Hv];
+ *           g = -exp(A_log[h]) softplus(a[t,h] + dt_bias[h]), beta = sigmoid(b[t,h]).
+ *   dgates: da, db float32 [T][Hv]; dA_log, ddt_bias float32 [Hv] (sums over
+ *           every token in a fixed order: deterministic; zero for an empty row).
+ * Every other argument, the workspace sizes and the pairing rules of the
+ * saved forms are those of gdn_chunk_fwd, gdn_chunk_fwd_save, gdn_chunk_bwd and
+ * gdn_chunk_bwd_saved.  Pointers need 4-byte alignment. */
+typedef struct gdn_gate_inputs {
+  const float* a;
+  const float* b;
+  const float* A_log;
+  const float* dt_bias;
+} gdn_gate_inputs;
+
+typedef struct gdn_gate_grads {
+  float* da;
+  float* db;
+  float* dA_log;
+  float* ddt_bias;
+} gdn_gate_grads;
+
+gdn_status gdn_chunk_fwd_gated(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                               int64_t tok_stride_qk, int64_t tok_stride_v, const gdn_gate_inputs* gates,
+                               const int32_t* cu_seqlens, const float* h0, void* o, float* ht, void* ws,
+                               size_t ws_bytes, gdn_stream stream);
+gdn_status gdn_chunk_fwd_save_gated(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                                    int64_t tok_stride_qk, int64_t tok_stride_v, const gdn_gate_inputs* gates,
+                                    const int32_t* cu_seqlens, const float* h0, void* o, float* ht, void* ws,
+                                    size_t ws_bytes, gdn_stream stream);
+gdn_status gdn_chunk_bwd_gated(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                               int64_t tok_stride_qk, int64_t tok_stride_v, const gdn_gate_inputs* gates,
+                               const int32_t* cu_seqlens, const float* h0, const void* d_o, const float* dht,
+                               void* dq, void* dk, void* dv, const gdn_gate_grads* dgates, float* dh0, void* ws,
+                               size_t ws_bytes, gdn_stream stream);
+gdn_status gdn_chunk_bwd_saved_gated(const gdn_shape* shape, const void* q, const void* k, const void* v,
+                                     int64_t tok_stride_qk, int64_t tok_stride_v, const gdn_gate_inputs* gates,
+                                     const int32_t* cu_seqlens, const float* h0, const void* d_o,
+                                     const float* dht, void* dq, void* dk, void* dv, const gdn_gate_grads* dgates,
+                                     float* dh0, void* ws, size_t ws_bytes, gdn_stream stream);
+
 /* --------------------------------------------------------------------------
  * RMSNormGated epilogue.  Page: "[Qwen3.5 MoE] Add hybrid decoder model",
  * Summary (RMSNormGated).
@@ -282,8 +346,11 @@ gdn_status gdn_conv1d_window(const gdn_shape* shape, const void* x, int32_t widt
  * launch of the library with hipEventRecord on its stream; (0) stops.
  * gdn_profile_report writes "kernel_name launches total_ms" lines into buf
  * (at most cap bytes including the terminating zero), waiting for the
- * recorded events, and returns the full length.  Not thread-safe; the event
- * objects are created once and reused.
+ * recorded events, and returns the full length.  State-pass records carry the
+ * variant that ran after a colon (wide128 / wide64: the whole or half state
+ * per workgroup; tiled16 / tiled32: column tiles of that width).  The records
+ * are guarded by a mutex, so launches from several host threads each time
+ * their own kernel; the event objects are created once and reused.
  * -------------------------------------------------------------------------- */
 void gdn_profile_enable(int on);
 size_t gdn_profile_report(char* buf, size_t cap);

@@ -59,6 +59,12 @@ def threads() -> int:
     return int(_lib(64).oracle_threads())
 
 
+def set_threads(n: int) -> None:
+    """Thread count of the oracle's OpenMP loops (both builds)."""
+    for bits in (64, 32):
+        _lib(bits).oracle_set_threads(ctypes.c_int(int(n)))
+
+
 def _dt(bits):
     return np.float64 if bits == 64 else np.float32
 
@@ -227,13 +233,16 @@ def layer_fwd(cfg, inp, bits=64, scale=1.0, storage=None):
     """Forward of the layer on one workload's inputs (see synth.make_inputs).
 
     Returns dict: y_conv [T, Cch], o [T, Hv, dv], ht [N, Hv, dk, dv] and, when
-    the workload has the norm, y [T, Hv, dv]."""
+    the workload has the norm, y [T, Hv, dv].  y_conv and o are the values the
+    next step consumes (rounded to the storage format); y_conv_exact and
+    o_exact are the same tensors before that rounding."""
     Hk, Hv, dk, dv = cfg.h_qk, cfg.h_v, cfg.d_k, cfg.d_v
-    yc = _store(conv1d(inp["x"], inp["w_conv"], inp["cu"], 2 * Hk * dk, dk, bits=bits), storage)
+    yc_exact = conv1d(inp["x"], inp["w_conv"], inp["cu"], 2 * Hk * dk, dk, bits=bits)
+    yc = _store(yc_exact, storage)
     q, k, v = split_qkv(yc, Hk, Hv, dk, dv)
-    o, ht = recurrence(q, k, v, inp["g"], inp["beta"], inp["cu"], h0=inp.get("h0"), scale=scale, bits=bits)
-    o = _store(o, storage)
-    out = dict(y_conv=yc, o=o, ht=ht)
+    o_exact, ht = recurrence(q, k, v, inp["g"], inp["beta"], inp["cu"], h0=inp.get("h0"), scale=scale, bits=bits)
+    o = _store(o_exact, storage)
+    out = dict(y_conv=yc, o=o, ht=ht, y_conv_exact=yc_exact, o_exact=o_exact)
     if cfg.norm:
         out["y"] = norm_gate(o, inp["z"], inp["w_norm"], bits=bits)
     return out
@@ -243,16 +252,18 @@ def layer_bwd(cfg, inp, fwd, dy, bits=64, scale=1.0, dht=None, storage=None):
     """Backward of the layer given the upstream gradient dy on its output
     (the norm output if present, else o).  Returns dict with dx, dw_conv, dg,
     dbeta, dh0, and dz, dw_norm when the norm is present; also the gradients
-    at the recurrence inputs (dq, dk, dv) and d_o."""
+    at the recurrence inputs (dq, dk, dv) and d_o (rounded to the storage
+    format, as the recurrence's backward consumes it; d_o_exact before)."""
     Hk, Hv, dk, dv = cfg.h_qk, cfg.h_v, cfg.d_k, cfg.d_v
     res = {}
     if cfg.norm:
-        d_o, dz, dwn = norm_gate_bwd(fwd["o"], inp["z"], inp["w_norm"], dy, bits=bits)
-        d_o = _store(d_o, storage)
+        d_o_exact, dz, dwn = norm_gate_bwd(fwd["o"], inp["z"], inp["w_norm"], dy, bits=bits)
+        d_o = _store(d_o_exact, storage)
         res.update(dz=dz, dw_norm=dwn)
     else:
-        d_o = dy
+        d_o = d_o_exact = dy
     res["d_o"] = d_o
+    res["d_o_exact"] = d_o_exact
     q, k, v = split_qkv(fwd["y_conv"], Hk, Hv, dk, dv)
     r = recurrence_bwd(q, k, v, inp["g"], inp["beta"], inp["cu"], d_o, h0=inp.get("h0"), dht=dht,
                        scale=scale, bits=bits)

@@ -436,6 +436,15 @@ EXPORT void oracle_gates_bwd(long T, int Hv, const real* a, const real* b, const
 
 EXPORT int oracle_real_bytes(void) { return (int)sizeof(real); }
 
+/* Thread count of the OpenMP loops (the CPU baseline also times one thread). */
+EXPORT void oracle_set_threads(int n) {
+#if defined(_OPENMP)
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 EXPORT int oracle_threads(void) {
 #if defined(_OPENMP)
   return omp_get_max_threads();

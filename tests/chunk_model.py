@@ -46,7 +46,10 @@ def _local(Q, K, V, g, b):
                 incl=incl, strict=strict)
 
 
-def chunk_fwd(q, k, v, g, beta, cu, C, h0=None, scale=1.0, return_states=False):
+def chunk_fwd(q, k, v, g, beta, cu, C, h0=None, scale=1.0, return_states=False, round_wk=None):
+    """round_wk: optional rounding applied to each chunk's Wk before it
+    multiplies the state (to model an implementation that stores Wk in a
+    narrower format)."""
     T, Hk, dk = q.shape
     _, Hv, dv = v.shape
     G = Hv // Hk
@@ -64,7 +67,8 @@ def chunk_fwd(q, k, v, g, beta, cu, C, h0=None, scale=1.0, return_states=False):
             loc = _local(Q, K, V, g[sl, h].astype(np.float64), beta[sl, h].astype(np.float64))
             H = cur[n]
             states[(h, t0)] = H
-            W = loc["U"] - loc["Wk"] @ H
+            Wk = loc["Wk"] if round_wk is None else round_wk(loc["Wk"])
+            W = loc["U"] - Wk @ H
             o[sl, h] = scale * (loc["Gam"][:, None] * (Q @ H) + loc["P"] @ W)
             cur[n] = loc["Gam"][-1] * H + K.T @ (loc["e"][:, None] * W)
         for n in range(N):
@@ -74,13 +78,15 @@ def chunk_fwd(q, k, v, g, beta, cu, C, h0=None, scale=1.0, return_states=False):
     return o, ht
 
 
-def chunk_bwd(q, k, v, g, beta, cu, C, d_o, h0=None, dht=None, scale=1.0):
-    """Gradients of <d_o, o> + <dht, ht> through the chunked form."""
+def chunk_bwd(q, k, v, g, beta, cu, C, d_o, h0=None, dht=None, scale=1.0, round_wk=None):
+    """Gradients of <d_o, o> + <dht, ht> through the chunked form.  round_wk
+    (as in chunk_fwd) models a narrower Wk in the forward state chain only:
+    the entering states and W the gradients are formed from."""
     T, Hk, dk = q.shape
     _, Hv, dv = v.shape
     G = Hv // Hk
     N = len(cu) - 1
-    _, _, states = chunk_fwd(q, k, v, g, beta, cu, C, h0=h0, scale=scale, return_states=True)
+    _, _, states = chunk_fwd(q, k, v, g, beta, cu, C, h0=h0, scale=scale, return_states=True, round_wk=round_wk)
     dq = np.zeros((T, Hk, dk)); dk_ = np.zeros((T, Hk, dk)); dv_ = np.zeros((T, Hv, dv))
     dg = np.zeros((T, Hv)); db = np.zeros((T, Hv)); dh0 = np.zeros((N, Hv, dk, dv))
     chunks = list(_chunks(cu, C))
@@ -95,7 +101,7 @@ def chunk_bwd(q, k, v, g, beta, cu, C, d_o, h0=None, dht=None, scale=1.0):
             loc = _local(Q, K, V, g[sl, h].astype(np.float64), bb)
             Gam, D, Tm, P, e, A = loc["Gam"], loc["D"], loc["Tm"], loc["P"], loc["e"], loc["A"]
             H = states[(h, t0)]
-            W = loc["U"] - loc["Wk"] @ H
+            W = loc["U"] - (loc["Wk"] if round_wk is None else round_wk(loc["Wk"])) @ H
             dOs = scale * d_o[sl, h].astype(np.float64)
             dHn = dcur[n]
             # state pass, reversed

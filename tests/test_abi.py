@@ -49,6 +49,7 @@ def test_status_strings():
     (dict(h_v=3), INVALID), (dict(d_k=48, d_v=48), UNSUPPORTED), (dict(d_v=64), UNSUPPORTED),
     (dict(dtype=7), UNSUPPORTED), (dict(chunk=8), UNSUPPORTED), (dict(chunk=128), UNSUPPORTED),
     (dict(dtype=gdn.F32, d_k=128, d_v=128, chunk=64), UNSUPPORTED),
+    (dict(dtype=gdn.F32, d_k=32, d_v=32, chunk=64), UNSUPPORTED),   # float32 runs chunks of at most 32
 ])
 def test_chunk_fwd_rejects_shape(bad, code):
     lib = gdn.load()
