@@ -14,7 +14,7 @@ from ._binding import (  # noqa: F401
     max_chunks, chunk_index,
     conv1d, conv1d_bwd, conv1d_bwd_workspace,
     chunk_fwd, chunk_fwd_workspace, chunk_bwd, chunk_bwd_workspace, chunk_fwd_gated, chunk_bwd_gated, chunk_fwd_fp8,
-    norm_gate, norm_gate_bwd, norm_gate_bwd_workspace,
+    norm_gate, norm_gate_bwd, norm_gate_bwd_workspace, norm_gate_bwd_noalloc,
     gates, gates_bwd, gates_bwd_workspace,
     recurrent_step, conv1d_step, conv1d_window, conv1d_prefill,
     profile_enable, profile_report,

@@ -18,7 +18,7 @@ SYMBOLS = ("gdn_status_string", "gdn_max_chunks", "gdn_chunk_index", "gdn_conv1d
            "gdn_conv1d_bwd", "gdn_chunk_fwd_workspace", "gdn_chunk_fwd", "gdn_chunk_bwd_workspace",
            "gdn_chunk_bwd", "gdn_chunk_fwd_save", "gdn_chunk_bwd_saved", "gdn_chunk_fwd_fp8", "gdn_chunk_fwd_gated",
            "gdn_chunk_fwd_save_gated", "gdn_chunk_bwd_gated", "gdn_chunk_bwd_saved_gated", "gdn_norm_gate",
-           "gdn_norm_gate_bwd_workspace", "gdn_norm_gate_bwd", "gdn_gates", "gdn_gates_bwd_workspace",
+           "gdn_norm_gate_bwd_workspace", "gdn_norm_gate_bwd", "gdn_norm_gate_bwd_noalloc", "gdn_gates", "gdn_gates_bwd_workspace",
            "gdn_gates_bwd", "gdn_recurrent_step", "gdn_conv1d_step", "gdn_conv1d_window", "gdn_conv1d_prefill",
            "gdn_profile_enable",
            "gdn_profile_report")
@@ -111,6 +111,7 @@ def load() -> ctypes.CDLL:
             "gdn_norm_gate": (I32, [S, P, P, P, F, P, P]),
             "gdn_norm_gate_bwd_workspace": (SZ, [S]),
             "gdn_norm_gate_bwd": (I32, [S, P, P, P, P, F, P, P, P, P, SZ, P]),
+            "gdn_norm_gate_bwd_noalloc": (I32, [S, P, P, P, P, F, P, P, P, P]),
             "gdn_gates": (I32, [S, P, P, P, P, P, P, P]),
             "gdn_gates_bwd_workspace": (SZ, [S]),
             "gdn_gates_bwd": (I32, [S, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
@@ -426,6 +427,27 @@ def norm_gate_bwd(dy, o, z, w_norm, shape: Shape, eps: float = 1e-6, ws: Optiona
     _check("gdn_norm_gate_bwd", load().gdn_norm_gate_bwd(ctypes.byref(shape.c()), _ptr(dy), _ptr(o), _ptr(z),
                                                          _ptr(w_norm), float(eps), _ptr(d_o), _ptr(dz), _ptr(dw),
                                                          _ptr(ws), ws.numel(), _stream(o.device)))
+    return d_o, dz, dw
+
+
+def norm_gate_bwd_noalloc(dy, o, z, w_norm, shape: Shape, eps: float = 1e-6, d_o=None, dz=None, dw=None):
+    """gdn_norm_gate_bwd_noalloc: the same backward with the library's own
+    device scratch instead of a workspace (outputs may be passed in, so that a
+    caller that cannot allocate can reuse them)."""
+    dt = shape.torch_dtype
+    sh = (shape.total_tokens, shape.h_v, shape.d_v)
+    for t, nm in ((dy, "dy"), (o, "o"), (z, "z")):
+        _need(t, nm, dt, sh)
+    _need(w_norm, "w_norm", dt, (shape.d_v,))
+    d_o = torch.empty_like(o) if d_o is None else d_o
+    dz = torch.empty_like(z) if dz is None else dz
+    dw = torch.empty((shape.d_v,), dtype=torch.float32, device=o.device) if dw is None else dw
+    _need(d_o, "d_o", dt, sh)
+    _need(dz, "dz", dt, sh)
+    _need(dw, "dw", torch.float32, (shape.d_v,))
+    _check("gdn_norm_gate_bwd_noalloc", load().gdn_norm_gate_bwd_noalloc(
+        ctypes.byref(shape.c()), _ptr(dy), _ptr(o), _ptr(z), _ptr(w_norm), float(eps), _ptr(d_o), _ptr(dz),
+        _ptr(dw), _stream(o.device)))
     return d_o, dz, dw
 
 

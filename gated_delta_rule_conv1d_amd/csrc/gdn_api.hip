@@ -406,4 +406,29 @@ gdn_status gdn_norm_gate_bwd(const gdn_shape* shape, const void* dy, const void*
   return launched();
 }
 
+gdn_status gdn_norm_gate_bwd_noalloc(const gdn_shape* shape, const void* dy, const void* o, const void* z,
+                                     const void* w_norm, float eps, void* d_o, void* dz, float* dw_norm,
+                                     gdn_stream stream) {
+  gdn_status st = check_shape(shape);
+  if (st != GDN_OK) return st;
+  const bool any = shape->total_tokens > 0;
+  if (!w_norm || !dw_norm || (any && (!dy || !o || !z || !d_o || !dz))) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(dy) || !aligned16(o) || !aligned16(z) || !aligned16(w_norm) || !aligned16(d_o) || !aligned16(dz))
+    return GDN_ERR_INVALID_ARG;
+  if (!(eps >= 0.f)) return GDN_ERR_INVALID_ARG;
+  if (norm_bwd_ws_bytes(shape) > norm_scratch_bytes()) return GDN_ERR_UNSUPPORTED;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return GDN_ERR_HIP;
+  if (stream) {  // the scratch used is the current device's: the stream must belong to it
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess) return GDN_ERR_HIP;
+    if ((int)sdev != cur) return GDN_ERR_INVALID_ARG;
+  }
+  void* ws = norm_scratch_ptr();
+  if (!ws) return GDN_ERR_HIP;
+  if (!run_norm_bwd(shape, dy, o, z, w_norm, eps, d_o, dz, dw_norm, ws, (hipStream_t)stream))
+    return GDN_ERR_UNSUPPORTED;
+  return launched();
+}
+
 }  // extern "C"

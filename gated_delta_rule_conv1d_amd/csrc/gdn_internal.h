@@ -19,6 +19,8 @@ bool run_conv_bwd(const gdn_shape* s, const void* dy, const void* x, const void*
 
 // norm_gate.hip
 size_t norm_bwd_ws_bytes(const gdn_shape* s);
+size_t norm_scratch_bytes();  // capacity of the allocation-free backward's device scratch
+void* norm_scratch_ptr();     // its device address on the current device, or NULL on a HIP error
 bool run_norm_fwd(const gdn_shape* s, const void* o, const void* z, const void* w, float eps, void* y,
                   hipStream_t st);
 bool run_norm_bwd(const gdn_shape* s, const void* dy, const void* o, const void* z, const void* w, float eps,

@@ -9,6 +9,8 @@
 //
 // A lane owns 16 bytes of a row (8 bf16 / 4 float); LPR = dv / that lanes form
 // a row group that reduces with xor shuffles.  Pure HBM streaming.
+#include <mutex>
+
 #include "gdn_common.cuh"
 #include "gdn_internal.h"
 #include "profile.h"
@@ -17,6 +19,14 @@ namespace gdn {
 
 constexpr int kNormThreads = 256;
 constexpr int kNormBwdBlocks = 1024;  // fixed grid of the backward (row-block stride)
+
+// Scratch of the allocation-free backward (gdn_norm_gate_bwd_noalloc): the
+// backward's per-block dw partials, kNormBwdBlocks x d_v floats for d_v <= 128
+// (512 KiB on each device the library runs on, held until the process ends).
+// Every block of the backward writes its whole row of partials before the
+// column sum reads them, so nothing needs clearing between calls.
+constexpr size_t kNormScratchFloats = (size_t)kNormBwdBlocks * 128;
+static __device__ __align__(256) float scratch[kNormScratchFloats];
 
 template <typename E, int DV>
 __global__ __launch_bounds__(kNormThreads) void norm_fwd_kernel(const E* __restrict__ o, const E* __restrict__ z,
@@ -113,6 +123,27 @@ __global__ __launch_bounds__(kNormThreads) void norm_bwd_kernel(const E* __restr
 
 
 size_t norm_bwd_ws_bytes(const gdn_shape* s) { return (size_t)kNormBwdBlocks * s->d_v * sizeof(float); }
+
+size_t norm_scratch_bytes() { return sizeof(scratch); }
+
+// Device address of `scratch` on the current device.  In host code the array's
+// name stands for a host-side shadow, not device memory, so kernels get this
+// address instead; it is looked up once per device (with that device current)
+// and kept.
+void* norm_scratch_ptr() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptr[dev] = p;
+  }
+  return ptr[dev];
+}
 
 template <typename E, int DV>
 static void launch_norm_fwd(const gdn_shape* s, const void* o, const void* z, const void* w, float eps, void* y,

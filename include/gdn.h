@@ -303,6 +303,23 @@ gdn_status gdn_norm_gate_bwd(const gdn_shape* shape, const void* dy, const void*
                              const void* w_norm, float eps, void* d_o, void* dz, float* dw_norm,
                              void* ws, size_t ws_bytes, gdn_stream stream);
 
+/* gdn_norm_gate_bwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It allocates nothing: the backward's dw
+ * partials live in a scratch array inside the library, 512 KiB per device
+ * (1024 blocks x d_v floats, d_v <= 128), created with the library's code
+ * object on each device it runs on and held until the process ends.  Every
+ * call on one device shares that device's scratch: calls that overlap in time
+ * on one device (for example on two concurrently running streams) race and
+ * give undefined results; calls ordered on one stream, or on different
+ * devices, are independent.  `stream` must belong to the current device
+ * (GDN_ERR_INVALID_ARG otherwise).  Shapes whose partials exceed the scratch
+ * return GDN_ERR_UNSUPPORTED (none among the supported d_v).  Results are
+ * bit-identical to gdn_norm_gate_bwd's; other arguments as there. */
+gdn_status gdn_norm_gate_bwd_noalloc(const gdn_shape* shape, const void* dy, const void* o, const void* z,
+                                     const void* w_norm, float eps, void* d_o, void* dz, float* dw_norm,
+                                     gdn_stream stream);
+
 /* --------------------------------------------------------------------------
  * Token-by-token continuation (decode).  Page: "feat(models): dense Qwen3.5
  * custom attention", KL mismatch table (RL rollouts come from an inference
