@@ -82,6 +82,46 @@ def test_chunk_fwd_rejects_pointers_strides_workspace():
     assert call(nb=ws - 1) == WORKSPACE
 
 
+def test_fp8_and_fused_gate_calls_reject():
+    lib = gdn.load()
+    s = shape(d_k=128, d_v=128, chunk=64, h_qk=1, h_v=2)
+    ws = lib.gdn_chunk_fwd_workspace(ctypes.byref(s))
+
+    def fp8(sc=(1.0, 0.5, 2.0), sh=s, sqk=128, w=FAKE, nb=ws):
+        return lib.gdn_chunk_fwd_fp8(ctypes.byref(sh), FAKE, FAKE, FAKE, sqk, 256, *sc, FAKE, FAKE, FAKE, None, FAKE,
+                                     None, w, nb, None)
+
+    assert fp8(sc=(0.75, 1.0, 1.0)) == INVALID      # scales must be powers of two
+    assert fp8(sc=(1.0, 0.0, 1.0)) == INVALID
+    assert fp8(sc=(1.0, 1.0, float("inf"))) == INVALID
+    assert fp8(sqk=136) == INVALID                  # byte stride not a multiple of 16
+    assert fp8(sh=shape(d_k=64, d_v=64, chunk=64)) == UNSUPPORTED
+    assert fp8(sh=shape(d_k=128, d_v=128, chunk=32)) == UNSUPPORTED
+    assert fp8(sh=shape(d_k=128, d_v=128, chunk=64, dtype=gdn.F32)) == UNSUPPORTED
+    assert fp8(nb=ws - 1) == WORKSPACE
+
+    gi = B._GateInputs(FAKE.value, FAKE.value, FAKE.value, FAKE.value)
+    gi_bad = B._GateInputs(FAKE.value, None, FAKE.value, FAKE.value)
+    gg = B._GateGrads(FAKE.value, FAKE.value, FAKE.value, FAKE.value)
+    gg_bad = B._GateGrads(FAKE.value, FAKE.value, None, FAKE.value)
+    s2 = shape()
+    ws2 = lib.gdn_chunk_bwd_workspace(ctypes.byref(s2))
+
+    def fwd(g):
+        return lib.gdn_chunk_fwd_gated(ctypes.byref(s2), FAKE, FAKE, FAKE, 64, 128, g, FAKE, None, FAKE, None, FAKE,
+                                       ws2, None)
+
+    def bwd(g, d):
+        return lib.gdn_chunk_bwd_gated(ctypes.byref(s2), FAKE, FAKE, FAKE, 64, 128, g, FAKE, None, FAKE, None,
+                                       FAKE, FAKE, FAKE, d, None, FAKE, ws2 - 256, None)
+
+    assert fwd(None) == INVALID
+    assert fwd(ctypes.byref(gi_bad)) == INVALID
+    assert bwd(ctypes.byref(gi), None) == INVALID
+    assert bwd(ctypes.byref(gi), ctypes.byref(gg_bad)) == INVALID
+    assert bwd(ctypes.byref(gi), ctypes.byref(gg)) == WORKSPACE
+
+
 def test_chunk_bwd_rejects():
     lib = gdn.load()
     s = shape()

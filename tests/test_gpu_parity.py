@@ -368,6 +368,70 @@ def test_chunk_fused_gates(dtype, d, chunk, Hk, Hv, lengths):
         assert_close(host(r2[key]), rgb[key], tol32, key)
 
 
+# ----------------------------------------------------------------------------- fp8 inputs
+FP8_CASES = [
+    (2, 4, (200, 1, 64, 63, 65), "tiled16"),                      # 20 chains: 16-column state tiles
+    (8, 16, (100, 64, 1, 65, 20), "wide64"),                      # 80 chains: half states
+    (16, 32, tuple(40 + 13 * (i % 7) for i in range(32)), "wide128"),   # 1024 chains: whole states
+]
+
+
+@pytest.mark.parametrize("Hk,Hv,lengths,variant", FP8_CASES)
+def test_chunk_fwd_fp8(Hk, Hv, lengths, variant):
+    """gdn_chunk_fwd_fp8: e4m3 q, k, v with power-of-two scales give the same
+    bytes as gdn_chunk_fwd on the dequantised bf16 tensors, and match the
+    oracle on them.  The e4m3 codes and their values come from torch's own
+    float8_e4m3fn conversion (a library routine, independent of the kernels)."""
+    _print_case("fp8", Hk=Hk, Hv=Hv, N=len(lengths), variant=variant)
+    cfg = small_cfg(dtype="bf16", d=128, chunk=64, Hk=Hk, Hv=Hv, lengths=lengths)
+    inp = synth.make_inputs(cfg)
+    q, k, v = qkv_inputs(cfg)
+    T = cfg.T
+    scales = (2.0 ** -4, 2.0 ** -3, 2.0 ** -1)
+
+    def quant(a, sc):  # e4m3 codes of a / sc (saturated to the finite range) and their exact values
+        c = torch.from_numpy(np.clip(a.reshape(T, -1) / sc, -448, 448).astype(np.float32)).to(torch.float8_e4m3fn)
+        return c, c.float().numpy().astype(np.float64) * sc
+
+    (q8, qd), (k8, kd), (v8, vd) = quant(q, scales[0]), quant(k, scales[1]), quant(v, scales[2])
+    for a in (qd, kd, vd):   # the dequantised values are bf16 values
+        assert np.array_equal(synth.round_bf16(a.astype(np.float32)), a.astype(np.float32))
+    s = shape_of(cfg)
+    cu = torch.from_numpy(inp["cu"]).cuda()
+    g, beta, h0 = f32(inp["g"]), f32(inp["beta"]), f32(inp["h0"])
+    gdn.profile_enable(True)
+    o8, ht8 = gdn.chunk_fwd_fp8(q8.cuda(), k8.cuda(), v8.cuda(), scales, g, beta, cu, s, h0=h0)
+    torch.cuda.synchronize()
+    ran = _variants(gdn.profile_report(), "chunk_state_fwd")
+    gdn.profile_enable(False)
+    ob, htb = gdn.chunk_fwd(to_dev(qd, "bf16"), to_dev(kd, "bf16"), to_dev(vd, "bf16"), g, beta, cu, s, h0=h0)
+    torch.cuda.synchronize()
+    assert ran == [variant], ran
+    assert torch.equal(o8.view(torch.int16), ob.view(torch.int16)), "o differs from the bf16 path"
+    assert torch.equal(ht8, htb), "ht differs from the bf16 path"
+    H = lambda a, h: a.reshape(T, h, cfg.d_k)
+    ro, rht = oracle.recurrence(H(qd, Hk), H(kd, Hk), H(vd, Hv), inp["g"], inp["beta"], inp["cu"], h0=inp["h0"])
+    assert_close(host(o8), ro, TOL["bf16"], "o")
+    assert_close(host(ht8), rht, TOL_F32_OUT["bf16"], "ht")
+
+
+def test_chunk_fwd_fp8_rejects():
+    """Non-power-of-two scales and shapes other than bf16, d = 128, chunk 64 are refused."""
+    cfg = small_cfg(dtype="bf16", d=128, chunk=64, Hk=1, Hv=1, lengths=(10,))
+    s = shape_of(cfg)
+    z8 = torch.zeros((10, 128), dtype=torch.uint8, device="cuda")
+    gz = torch.zeros((10, 1), dtype=torch.float32, device="cuda")
+    cu = torch.tensor([0, 10], dtype=torch.int32, device="cuda")
+    with pytest.raises(gdn.GdnError) as e:
+        gdn.chunk_fwd_fp8(z8, z8, z8, (0.75, 1.0, 1.0), gz, gz, cu, s)
+    assert e.value.code == -1
+    s2 = shape_of(small_cfg(dtype="bf16", d=64, chunk=64, Hk=1, Hv=1, lengths=(10,)))
+    z8b = torch.zeros((10, 64), dtype=torch.uint8, device="cuda")
+    with pytest.raises(gdn.GdnError) as e:
+        gdn.chunk_fwd_fp8(z8b, z8b, z8b, (1.0, 1.0, 1.0), gz, gz, cu, s2)
+    assert e.value.code == -2
+
+
 # ----------------------------------------------------------------------------- whole layer
 @pytest.mark.parametrize("norm,h0", [(False, False), (True, True)])
 def test_layer_tiny_full(norm, h0):
