@@ -1,10 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark the GatedDeltaNet layer on one MI355X.
 
-One step = the whole layer path over one packed row: conv1d+SiLU+L2, the
-chunked gated delta rule with its gates (g, beta computed inside the chunk
-kernels from a, b, A_log, dt_bias), RMSNormGated, and (for the training
-workload) the backward of all of them.  Default workload: the training step, 8 sequences x
+One step = the whole layer path over one packed row: the gates (g, beta from
+a, b, A_log, dt_bias), conv1d+SiLU+L2, the chunked gated delta rule,
+RMSNormGated, and (for the training workload) the backward of all of them
+(--fused-gates: the gates computed inside the chunk kernels instead).  Default workload: the training step, 8 sequences x
 8192 tokens packed in one row, 16 q/k heads, 32 v heads, d = 128, bf16.
 
 Prints ONE JSON line with the throughput (tokens/s), the roofline of the
@@ -157,12 +157,80 @@ def cpu_baseline(cfg, inp, kheads: int):
         oracle.gates_bwd(*gate_in, r["dg"], r["dbeta"])
     dt = time.perf_counter() - t0
     tokens_equiv = cfg.T * kheads / cfg.h_qk
+    single = single_thread_oracle()
     return {"value": tokens_equiv / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "single_thread": single,
             "sample": ("one-token sequences from the same states, conv from zero history: " if cfg.decode else "") +
                       f"all {cfg.N} sequences ({cfg.T} tokens) x {kheads} of {cfg.h_qk} q/k heads "
                       f"({hv} v-heads), gates + layer, fp64 {'fwd+bwd' if cfg.bwd else 'fwd'}; "
                       f"{dt:.1f} s scaled to whole-layer tokens/s",
             "seconds": dt}
+
+
+def single_thread_oracle() -> dict:
+    """The oracle on one thread, forward: the whole tiny workload, and the
+    dense 4 x 2048 workload on 1 of its 16 q/k heads (scaled to whole-layer
+    tokens/s)."""
+    import oracle
+    import synth
+    full = oracle.threads()
+    oracle.set_threads(1)
+    res = {}
+    try:
+        for name, kheads in (("tiny", None), ("dense", 1)):
+            cfg = synth.config(name)
+            inp = synth.make_inputs(cfg)
+            if kheads:
+                cfg, inp, _, _ = oracle.subset(cfg, inp, list(range(cfg.N)), list(range(kheads)))
+            t0 = time.perf_counter()
+            oracle.layer_fwd(cfg, inp)
+            dt = time.perf_counter() - t0
+            scale = synth.config(name).h_qk / cfg.h_qk
+            res[name] = {"tokens_per_s": round(cfg.T / scale / dt, 1), "seconds": round(dt, 3),
+                         "sample": f"{cfg.T} tokens x {cfg.h_qk} of {synth.config(name).h_qk} q/k heads, fwd"}
+    finally:
+        oracle.set_threads(full)
+    return res
+
+
+def achievable_peaks(gdn, torch) -> dict:
+    """What this chip reaches, beside the published peaks every kernel is
+    priced against: a 16-byte-per-lane streaming copy of 2 GiB (read + write
+    bytes / time) and a loop of independent bf16 matrix-core products on 16
+    waves per compute unit; each the best of 5 runs timed with HIP events."""
+    n = 2 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    out = torch.empty(1024 * 256, dtype=torch.float32, device="cuda:0")
+
+    def best(fn, reps=5):
+        fn()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return min(ts)
+
+    t_copy = best(lambda: gdn.probe_copy(src, dst))
+    t_tcopy = best(lambda: dst.copy_(src))
+    flops = 1024 * 4 * 8 * 20000 * 16384      # the same for both shapes (4 chains of twice the work)
+    t_16 = best(lambda: gdn.probe_mfma(out, 1024, 20000, 0))
+    t_32 = best(lambda: gdn.probe_mfma(out, 1024, 20000, 1))
+    del src, dst
+    gbs = 2 * n / min(t_copy, t_tcopy) / 1e9
+    tf16, tf32 = flops / t_16 / 1e12, flops / t_32 / 1e12
+    return {"copy_GBps": round(gbs, 1), "copy_frac_of_peak": round(gbs / HBM_PEAK_GBS, 3),
+            "copy_GBps_probe_kernel": round(2 * n / t_copy / 1e9, 1),
+            "copy_GBps_torch": round(2 * n / t_tcopy / 1e9, 1),
+            "mfma_bf16_16x16x32_TFLOPs": round(tf16, 1), "mfma_bf16_32x32x16_TFLOPs": round(tf32, 1),
+            "mfma_frac_of_peak": round(max(tf16, tf32) / MFMA_BF16_PEAK_TFLOPS, 3),
+            "method": "copy: gdn_probe_copy and torch copy_ of 2 GiB (read + write bytes); mfma: gdn_probe_mfma, "
+                      "1024 x 256 threads, 20000 rounds of independent v_mfma_f32_16x16x32_bf16 (8 chains) or "
+                      "v_mfma_f32_32x32x16_bf16 (4 chains); best of 5, HIP events"}
 
 
 def main():
@@ -172,6 +240,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="train", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-heads", type=int, default=8, help="q/k heads in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--peaks", type=int, default=1, help="also time the achievable-peak probes (0: skip)")
+    ap.add_argument("--fused-gates", action="store_true",
+                    help="compute the gates inside the chunk kernels (gdn_chunk_*_gated) instead of with "
+                         "gdn_gates / gdn_gates_bwd (measured slightly slower: the default is the separate kernels)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the reference for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters of rocprofv3) and exit")
@@ -229,7 +301,7 @@ def main():
             q, k, v = layer.split(yc)
             o, _ = gdn.recurrent_step(q, k, v, g, beta, shape, state_in=state, state_out=state)
             gdn.norm_gate(o, z, wn, shape)
-    else:
+    elif args.fused_gates:
         gates = (ga, gb, A_log, dt_bias)
 
         def step():
@@ -239,6 +311,14 @@ def main():
             f = layer.forward(x, w, None, None, cu, z, wn, h0, for_backward=cfg.bwd, gates=gates)
             if cfg.bwd:
                 layer.backward(dy, x, w, None, None, cu, f, z, wn, h0, gates=gates)
+    else:
+        def step():
+            g, beta = layer.gates(ga, gb, A_log, dt_bias)
+            # a training step keeps the forward's chunk products for the backward
+            f = layer.forward(x, w, g, beta, cu, z, wn, h0, for_backward=cfg.bwd)
+            if cfg.bwd:
+                r = layer.backward(dy, x, w, g, beta, cu, f, z, wn, h0)
+                layer.gates_backward(ga, gb, A_log, dt_bias, r["dg"], r["dbeta"])
 
     # Per-kernel durations come from HIP events that the library records around
     # each launch on the stream it launches on, during the timed steps
@@ -259,6 +339,8 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     value = cfg.T * args.steps / elapsed
 
+    peaks = achievable_peaks(gdn, torch) if args.peaks else None
+
     import oracle
     n_chunks = len(oracle.chunk_table(inp["cu"], cfg.chunk)[0])
     kb = kernel_bytes(cfg, n_chunks, cfg.h0)
@@ -270,9 +352,13 @@ def main():
         kernels[name] = {"launches": cnt, "avg_us": round(avg_ms * 1e3, 2),
                          "share": round(tot / sum(t for _, t in rep.values()), 4)}
         if base(name) in kb:
-            kernels[name]["GBps"] = round(kb[base(name)] / (avg_ms * 1e-3) / 1e9, 1)
+            gbs = kb[base(name)] / (avg_ms * 1e-3) / 1e9
+            kernels[name]["GBps"] = round(gbs, 1)
+            kernels[name]["hbm_frac"] = round(gbs / HBM_PEAK_GBS, 3)
         if base(name) in kf:
-            kernels[name]["TFLOPs"] = round(kf[base(name)] / (avg_ms * 1e-3) / 1e12, 2)
+            tfs = kf[base(name)] / (avg_ms * 1e-3) / 1e12
+            kernels[name]["TFLOPs"] = round(tfs, 2)
+            kernels[name]["mfma_frac"] = round(tfs / MFMA_BF16_PEAK_TFLOPS, 4)
     dom = max(rep, key=lambda k: rep[k][1])
     cnt, tot = rep[dom]
     avg_s = tot / cnt * 1e-3
@@ -315,13 +401,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {WORKLOADS[args.workload]}", "tokens": cfg.T,
                    "n_seqs": cfg.N, "h_qk": cfg.h_qk, "h_v": cfg.h_v, "d": cfg.d_k, "chunk": cfg.chunk,
-                   "gates": ("g, beta computed from a, b, A_log, dt_bias in the step" if cfg.decode else
-                             "g, beta computed from a, b, A_log, dt_bias inside the chunk kernels"),
+                   "gates": ("g, beta computed from a, b, A_log, dt_bias inside the chunk kernels"
+                             if args.fused_gates and not cfg.decode else
+                             "g, beta computed from a, b, A_log, dt_bias in the step (gate kernels)"),
                    "parallelism": "single GPU"},
         "roofline": roof,
         "step_fraction_of_fused_minimum": (round(step_bytes / (HBM_PEAK_GBS * 1e9) / (ms_per_step * 1e-3), 4)
                                            if step_bytes else None),
         "kernels": kernels,
+        "achievable_peaks": peaks,
         "cpu_baseline": cpu,
         "input_generation_s": round(t_gen, 2),
         "csrc_hash": csrc_hash(),

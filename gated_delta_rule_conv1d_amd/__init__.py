@@ -17,6 +17,6 @@ from ._binding import (  # noqa: F401
     norm_gate, norm_gate_bwd, norm_gate_bwd_workspace, norm_gate_bwd_noalloc,
     gates, gates_bwd, gates_bwd_workspace,
     recurrent_step, conv1d_step, conv1d_window, conv1d_prefill,
-    profile_enable, profile_report,
+    profile_enable, profile_report, probe_copy, probe_mfma,
 )
 from .layer import GatedDeltaNetLayer, layer_forward, layer_backward  # noqa: F401

@@ -18,10 +18,10 @@ SYMBOLS = ("gdn_status_string", "gdn_max_chunks", "gdn_chunk_index", "gdn_conv1d
            "gdn_conv1d_bwd", "gdn_chunk_fwd_workspace", "gdn_chunk_fwd", "gdn_chunk_bwd_workspace",
            "gdn_chunk_bwd", "gdn_chunk_fwd_save", "gdn_chunk_bwd_saved", "gdn_chunk_fwd_fp8", "gdn_chunk_fwd_gated",
            "gdn_chunk_fwd_save_gated", "gdn_chunk_bwd_gated", "gdn_chunk_bwd_saved_gated", "gdn_norm_gate",
-           "gdn_norm_gate_bwd_workspace", "gdn_norm_gate_bwd", "gdn_norm_gate_bwd_noalloc", "gdn_gates", "gdn_gates_bwd_workspace",
+           "gdn_norm_gate_bwd_workspace", "gdn_norm_gate_bwd", "gdn_norm_gate_bwd_noalloc", "gdn_gates",
+           "gdn_gates_bwd_workspace",
            "gdn_gates_bwd", "gdn_recurrent_step", "gdn_conv1d_step", "gdn_conv1d_window", "gdn_conv1d_prefill",
-           "gdn_profile_enable",
-           "gdn_profile_report")
+           "gdn_profile_enable", "gdn_profile_report", "gdn_probe_copy", "gdn_probe_mfma")
 
 
 class GdnError(RuntimeError):
@@ -121,6 +121,8 @@ def load() -> ctypes.CDLL:
             "gdn_conv1d_prefill": (I32, [S, P, P, I32, F, P, P, P, P, P]),
             "gdn_profile_enable": (None, [ctypes.c_int]),
             "gdn_profile_report": (SZ, [ctypes.c_char_p, SZ]),
+            "gdn_probe_copy": (I32, [P, P, SZ, P]),
+            "gdn_probe_mfma": (I32, [P, I32, I32, I32, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -577,3 +579,21 @@ def profile_report() -> dict:
         name, cnt, ms = line.split()
         out[name] = (int(cnt), float(ms))
     return out
+
+
+# ----------------------------------------------------------------------------- achievable-peak probes
+def probe_copy(src: torch.Tensor, dst: torch.Tensor) -> None:
+    """gdn_probe_copy of src's bytes into dst (contiguous GPU tensors)."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n or not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("dst must be contiguous and at least as large as src")
+    _check("gdn_probe_copy", load().gdn_probe_copy(_ptr(src), _ptr(dst), n, _stream(src.device)))
+
+
+def probe_mfma(out: torch.Tensor, blocks: int, iters: int, shape: int = 0) -> int:
+    """gdn_probe_mfma; out: float32 [blocks * 256]; shape 0: 16x16x32, 1: 32x32x16
+    bf16 products.  Returns the flops it performs."""
+    _need(out, "out", torch.float32, (blocks * 256,))
+    _check("gdn_probe_mfma", load().gdn_probe_mfma(_ptr(out), int(blocks), int(iters), int(shape),
+                                                   _stream(out.device)))
+    return blocks * 4 * iters * 8 * 16384

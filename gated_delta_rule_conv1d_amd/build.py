@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libgdn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["gdn_api.hip", "conv1d.hip", "norm_gate.hip", "gates.hip", "recurrent.hip", "chunk_fwd.hip", "chunk_bwd.hip", "state_wide.hip",
-           "profile.hip"]
+           "profile.hip", "probe.hip"]
 ARCH = "gfx950"
 
 

@@ -278,7 +278,7 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
     const int e = tid;
     const float g = a.gam[slot * C + e];
     const float gl = a.gam[slot * C + len - 1];
-    const float bt = chunk_beta(a, tok0 + min(e, len - 1), h);
+    const float bt = chunk_beta_fin(a, chunk_beta_raw(a, tok0 + min(e, len - 1), h));
     sm.bs[e] = e < len ? bt : 0.f;
     sm.gm[e] = __expf(g);
     sm.em[e] = e < len ? __expf(gl - g) : 0.f;
@@ -567,11 +567,21 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
     pTm.load(a.Tw + slot * C * C, C, C);
     rXu.load(a.dWt + slot * D * C, C, D);
     rXw.load(a.dWkt + slot * D * C, C, D);
+    // fused gates: this row's factors da / dg, db / dbeta and its g, kept for the row pass at the end
+    float fa_r = 0.f, fb_r = 0.f, g_r = 0.f;
     if (tid < C) {  // per-row gates; every load unconditional (clamped rows), so they issue together
       const int e = tid;
       const float gm = a.gam[slot * C + e];
       const float gl = a.gam[slot * C + len - 1];
-      const float bt = chunk_beta(a, tok0 + min(e, len - 1), h);
+      const float braw = chunk_beta_raw(a, tok0 + min(e, len - 1), h);
+      if (a.ga) {
+        // formed here, off the row pass's serial path (the expressions of gdn_gates_bwd)
+        const float ea = __expf(a.A_log[h]), xa = a.ga[(int64_t)(tok0 + min(e, len - 1)) * a.Hv + h] + a.dt_bias[h];
+        fa_r = -ea * gate_sigmoid(xa);
+        g_r = -ea * gate_softplus(xa);
+        fb_r = gate_sigmoid(braw) * gate_sigmoid(-braw);
+      }
+      const float bt = chunk_beta_fin(a, braw);
       const float hd = a.hdot[slot];  // used by the row pass at the end
       sm.gam[e] = gm;
       sm.Gm[e] = __expf(gm);
@@ -792,14 +802,12 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
         // fused gates: da = -exp(A_log) sigmoid(a + dt_bias) dg, db = beta (1 - beta) dbeta,
         // and this chunk's shares of dA_log = sum dg g and ddt_bias = sum da
         float sA = 0.f, sdt = 0.f;
-        if (r < len) {
+        if (r < len) {  // row r's factors: formed by this lane at the start of the v-head
           const int64_t e = (int64_t)(tok0 + r) * a.Hv + h;
-          const float ea = __expf(a.A_log[h]), xa = a.ga[e] + a.dt_bias[h];
-          const float dav = -ea * gate_sigmoid(xa) * x;
-          const float bb = a.gb[e];
+          const float dav = fa_r * x;
           a.da[e] = dav;
-          a.db[e] = gate_sigmoid(bb) * gate_sigmoid(-bb) * dbeta;
-          sA = x * (-ea * gate_softplus(xa));
+          a.db[e] = fb_r * dbeta;
+          sA = x * g_r;
           sdt = dav;
         }
         sA = wave_sum(sA);

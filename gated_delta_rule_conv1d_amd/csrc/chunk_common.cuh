@@ -85,14 +85,25 @@ struct ChunkArgs {
 
 
 // g and beta of token t, v-head h: the caller's arrays, or computed from the
-// raw gate inputs (the same functions as gdn_gates)
-__device__ __forceinline__ float chunk_g(const ChunkArgs& a, int64_t t, int h) {
-  if (a.ga) return -__expf(a.A_log[h]) * gate_softplus(a.ga[t * a.Hv + h] + a.dt_bias[h]);
-  return a.g[t * a.Hv + h];
+// raw gate inputs (the same functions as gdn_gates).  In two steps: *_raw
+// loads (the caller's value, or a / b) and *_fin finishes, at first use, so
+// that a prefetched gate does not force a wait for the loads issued with it
+// (the vector-memory counter retires in order).
+struct GateRaw {  // the caller's g (A, dt unused), or a with A_log[h] and dt_bias[h]
+  float x, A, dt;
+};
+__device__ __forceinline__ GateRaw chunk_g_raw(const ChunkArgs& a, int64_t t, int h) {
+  if (a.ga) return GateRaw{a.ga[t * a.Hv + h], a.A_log[h], a.dt_bias[h]};
+  return GateRaw{a.g[t * a.Hv + h], 0.f, 0.f};
 }
-__device__ __forceinline__ float chunk_beta(const ChunkArgs& a, int64_t t, int h) {
-  if (a.gb) return gate_sigmoid(a.gb[t * a.Hv + h]);
-  return a.beta[t * a.Hv + h];
+__device__ __forceinline__ float chunk_g_fin(const ChunkArgs& a, const GateRaw& r) {
+  return a.ga ? -__expf(r.A) * gate_softplus(r.x + r.dt) : r.x;
+}
+__device__ __forceinline__ float chunk_beta_raw(const ChunkArgs& a, int64_t t, int h) {
+  return a.gb ? a.gb[t * a.Hv + h] : a.beta[t * a.Hv + h];
+}
+__device__ __forceinline__ float chunk_beta_fin(const ChunkArgs& a, float raw) {
+  return a.gb ? gate_sigmoid(raw) : raw;
 }
 
 template <typename E> struct Pad {
@@ -346,16 +357,6 @@ struct StateSmem {
   float gam[C];
 };
 
-// Register staging of one [R][COLS] tile of T read from global memory (row
-// stride ld elements, rows past rows_valid read as zero) by all threads of a
-// workgroup with 16-byte loads; store() writes it to LDS afterwards.  Used to
-// issue the next chunk's loads before the current chunk's compute.
-// Piece e (16 bytes) is, by default, row e / PER_ROW, columns (e % PER_ROW) * V:
-// adjacent lanes take adjacent pieces of a row.  With RF (rows first), 16
-// adjacent lanes take the same columns of 16 adjacent rows: store_t then
-// writes 16 consecutive elements of a transposed row per lane group instead of
-// one element each of 16 rows a 16-byte piece apart (which fall in the same
-// LDS banks), at the price of 64-byte instead of 256-byte runs per global load.
 // fp8 inputs (OCP e4m3: 1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
 // exponent field 0 is subnormal, m 2^-9).  Decoded exactly: normal values are
 // (1 + m/8) 2^(e-7), i.e. float bits ((e + 120) << 23) | (m << 20).  Every
@@ -381,6 +382,16 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi, float
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Register staging of one [R][COLS] tile of T read from global memory (row
+// stride ld elements, rows past rows_valid read as zero) by all threads of a
+// workgroup with 16-byte loads; store() writes it to LDS afterwards.  Used to
+// issue the next chunk's loads before the current chunk's compute.
+// Piece e (16 bytes) is, by default, row e / PER_ROW, columns (e % PER_ROW) * V:
+// adjacent lanes take adjacent pieces of a row.  With RF (rows first), 16
+// adjacent lanes take the same columns of 16 adjacent rows: store_t then
+// writes 16 consecutive elements of a transposed row per lane group instead of
+// one element each of 16 rows a 16-byte piece apart (which fall in the same
+// LDS banks), at the price of 64-byte instead of 256-byte runs per global load.
 template <typename T, int R, int COLS, int NTH = kChunkThreads, bool RF = false, bool BUF = true>
 struct TileRegs {
   static constexpr int V = 16 / (int)sizeof(T);

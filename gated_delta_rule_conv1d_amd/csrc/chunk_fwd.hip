@@ -92,7 +92,8 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
   TileRegs<E, C, D, NTH, true> pV;  // a v-head's v rows; rows first: written transposed
   TileRegs<E, C, D, NTH> rQ;
   TileRegs<E, C, D, NTH, true> rK;  // rows first: also written transposed
-  float gv = 0.f, bv = 0.f;
+  GateRaw gv{0.f, 0.f, 0.f};  // this lane's gate inputs, finished where the v-head starts
+  float bv = 0.f;
   // F8: q, k, v arrive as e4m3 bytes and are decoded on load (exactly: the
   // registers then hold the bf16 tile of the dequantised inputs)
   auto load_head = [&](int tok, int n, int hh) {
@@ -101,8 +102,8 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
     else
       pV.load((const E*)a.v + (int64_t)tok * a.sv + (int64_t)hh * D, a.sv, n);
     if (w == 0 && lane < n) {
-      gv = chunk_g(a, tok + lane, hh);
-      bv = chunk_beta(a, tok + lane, hh);
+      gv = chunk_g_raw(a, tok + lane, hh);
+      bv = chunk_beta_raw(a, tok + lane, hh);
     }
   };
   auto load_item = [&](int4 e, int jj) {
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
       const int h = j * a.G + gi;
       const int64_t slot = (int64_t)ci * a.Hv + h;
       if (w == 0) {  // within-chunk cumulative gate
-        float x = gv;
+        float x = chunk_g_fin(a, gv);
 #pragma unroll
         for (int off = 1; off < kWave; off <<= 1) {
           const float y = __shfl_up(x, off, kWave);
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
         }
         if (lane < C) {
           sm.gam[lane] = x;
-          sm.beta[lane] = bv;
+          sm.beta[lane] = chunk_beta_fin(a, bv);
           a.gam[slot * C + lane] = x;
         }
       }

@@ -372,6 +372,19 @@ gdn_status gdn_conv1d_window(const gdn_shape* shape, const void* x, int32_t widt
 void gdn_profile_enable(int on);
 size_t gdn_profile_report(char* buf, size_t cap);
 
+/* Diagnostics: achievable-peak probes (not part of the layer).
+ * gdn_probe_copy: copies `bytes` (a multiple of 16; both pointers 16-byte
+ *   aligned, not overlapping) from src to dst with 16-byte loads and stores:
+ *   the HBM bandwidth a streaming kernel reaches.
+ * gdn_probe_mfma: `blocks` workgroups of 4 waves, each wave running
+ *   independent chains of `iters` bf16 matrix-core products: shape 0, 8
+ *   chains of 16x16x32 (blocks * 4 * 8 * iters * 16384 flops); shape 1, 4
+ *   chains of 32x32x16 (blocks * 4 * 4 * iters * 32768 flops); writes one
+ *   float per thread to out [blocks * 256]: the matrix-core rate a kernel
+ *   can reach with that instruction. */
+gdn_status gdn_probe_copy(const void* src, void* dst, size_t bytes, gdn_stream stream);
+gdn_status gdn_probe_mfma(float* out, int32_t blocks, int32_t iters, int32_t shape, gdn_stream stream);
+
 #ifdef __cplusplus
 }
 #endif
