@@ -627,7 +627,7 @@ void launch_chunk_fwd_core(const ChunkArgs& args, hipStream_t st, int mode) {
   }
   GDN_PROF(state_name[mode][variant], st);
   if constexpr (use_wide_state<E, D, C>()) {
-    if (nc == 16) launch_state_fwd_tiled<E, D, C, 16, true, F8>(a, st, mode);
+    if (nc == 16) launch_state_fwd_cols(a, st, mode, F8);
     else launch_state_fwd_wide(a, st, mode, nc < D, F8);
     return;
   }

@@ -513,6 +513,224 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Forward state pass over 16-column tiles of the state, for chains too few to
+// fill the chip (a single long sequence): eight 256-thread workgroups per
+// (sequence, v-head), each carrying 16 state columns through the whole
+// sequence.  Every operand that one wave reads alone goes straight from
+// global memory (L2) into matrix-core fragments: wave w's rows of Wk, q, U and
+// P (output row tile w) and of K^T (state row tiles w and w + 4); only H^T and
+// W^T, which all waves read, pass through LDS.  Each chunk's operands are
+// requested right after the previous chunk's last use of their registers.
+// Same arithmetic as the whole-state pass, per element.
+// ---------------------------------------------------------------------------
+struct ColsSmem {
+  E Ht[16][kLDQ];   // H^T: Ht[c][r] = H[r][c], this workgroup's 16 columns
+  E Htl[16][kLDQ];
+  E Wt[16][kLDC];   // W^T (with OUT, for P W), else (diag(e) W)^T
+  E Wtl[16][kLDC];
+  E Ws[16][kLDC];   // (diag(e) W)^T for the state update (OUT)
+  E Wsl[16][kLDC];
+  float gam[kC];
+};
+
+template <int MODE, bool F8>
+__global__ __launch_bounds__(256) void state_fwd_cols_kernel(ChunkArgs a) {
+  constexpr bool OUT = MODE & kFwdOut, STORE = MODE & kFwdStore;
+  constexpr int D = kD, C = kC, NT = 256;
+  __shared__ ColsSmem sm;
+  int n, h, vt;
+  if (!state_block(blockIdx.x, a.N, a.Hk, a.G, kD / 16, n, h, vt)) return;
+  const int j = h / a.G;
+  const int col0 = vt * 16;
+  const int tid = threadIdx.x, w = wave_id(), lane = lane_id();
+  const int r16 = lane & 15, kq = (lane >> 4) * 8;
+  const int rt1 = w;                    // W / O tile: row tile w
+  const int rtA = w, rtB = w + 4;       // state tiles: row tiles w and w + 4
+
+  f32x4 Hr[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rt = i ? rtB : rtA;
+    Hr[i] = zero4();
+    if (a.h0) {
+      const float* src = a.h0 + ((int64_t)n * a.Hv + h) * D * D;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Hr[i][e] = src[(rt * 16 + acc_row(e)) * D + col0 + acc_col()];
+    }
+  }
+  auto write_Ht = [&]() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = acc_col(), r = (i ? rtB : rtA) * 16 + acc_row(0);
+      st4_split<E>(&sm.Ht[c][r], &sm.Htl[c][r], Hr[i]);
+    }
+  };
+
+  // this wave's operands of the next chunk
+  float g_r = 0.f;
+  M::frag wkf[4], qf[4], ktf[2][2];
+  f32x4 uf;
+  float4 pf[2][2];
+  const int a_off = ((rt1 * 16 + r16) * D + kq) * 2;   // lane's A-fragment offset in a [C][D] bf16 tile
+  auto load_g = [&](int ci) {
+    g_r = Buf(a.gam + ((int64_t)ci * a.Hv + h) * C, C * 4).f1((tid & (C - 1)) * 4);
+  };
+  auto load_p1 = [&](int ci, int tok0, int len) {
+    const int64_t slot = (int64_t)ci * a.Hv + h;
+    const Buf wk((const E*)a.Wk + slot * C * D, C * D * 2);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) wkf[ks] = wk.fr(a_off + ks * 64);
+    if constexpr (OUT && F8) {  // e4m3 q rows, decoded exactly on load
+      const Buf qb((const uint8_t*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D, (int64_t)len * a.sqk);
+      const int q_off = (int)((int64_t)(rt1 * 16 + r16) * a.sqk + kq);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qf[ks] = qb.fr_f8(q_off + ks * 32, a.f8_scale[0]);
+    } else if constexpr (OUT) {  // rows past len fall outside the buffer and read zero
+      const Buf qb((const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D, (int64_t)len * a.sqk * 2);
+      const int q_off = (int)(((int64_t)(rt1 * 16 + r16) * a.sqk + kq) * 2);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qf[ks] = qb.fr(q_off + ks * 64);
+    }
+    const Buf ub(a.U + slot * C * D, C * D * 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) uf[e] = ub.f1(((rt1 * 16 + acc_row(e)) * D + col0 + acc_col()) * 4);
+  };
+  auto load_p2 = [&](int ci) {
+    const int64_t slot = (int64_t)ci * a.Hv + h;
+    const Buf kb((const E*)a.Kt + slot * D * C, D * C * 2);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) ktf[i][ks] = kb.fr((((i ? rtB : rtA) * 16 + r16) * C + kq + ks * 32) * 2);
+    if constexpr (OUT) {
+      const Buf pb(a.P + slot * C * C, C * C * 4);
+      const int p_off = ((rt1 * 16 + r16) * C + kq) * 4;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        pf[ks][0] = pb.f4(p_off + ks * 128);
+        pf[ks][1] = pb.f4(p_off + ks * 128 + 16);
+      }
+    }
+  };
+
+  // the sequence's chunks are consecutive table entries: (first token, length)
+  // follow from cu_seqlens
+  const int c0 = a.seq_chunk0[n], c1 = a.seq_chunk0[n + 1];
+  const int s0 = a.cu[n], s1 = a.cu[n + 1];
+  auto entry = [&](int ci) {
+    const int t = s0 + (ci - c0) * C;
+    return make_int4(n, t, min(C, s1 - t), 0);
+  };
+  int4 ent = make_int4(0, 0, 0, 0);
+  if (c0 < c1) {
+    ent = entry(c0);
+    load_g(c0);
+    load_p1(c0, ent.y, ent.z);
+    load_p2(c0);
+  }
+  write_Ht();
+  for (int ci = c0; ci < c1; ++ci) {
+    const int tok0 = ent.y, len = ent.z;
+    const int64_t slot = (int64_t)ci * a.Hv + h;
+    __syncthreads();  // the previous chunk is done with W^T, and H^T is written
+    if (tid < C) sm.gam[tid] = g_r;
+    __syncthreads();
+    const bool more = ci + 1 < c1;
+    int4 nent = ent;
+    if (more) {
+      nent = entry(ci + 1);
+      load_g(ci + 1);
+    }
+    // Stores go after the prefetch loads: the wait for a load also waits for
+    // every earlier vector-memory access of the wave.
+    if constexpr (STORE) {  // state entering this chunk, for the backward pass
+      float* Hg = a.Hc + slot * D * D;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) store_tile<float>(Hg, D, (i ? rtB : rtA) * 16, col0, Hr[i], D);
+    }
+
+    // phase 1: W = U - Wk H and diag(Gam) Q H on this wave's row tile
+    f32x4 x = zero4(), o = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const M::frag bh = fr(&sm.Ht[r16][ks * 32 + kq]);
+      const M::frag bl = fr(&sm.Htl[r16][ks * 32 + kq]);
+      x = M::mma(wkf[ks], bh, x);
+      x = M::mma(wkf[ks], bl, x);
+      if constexpr (OUT) {
+        o = M::mma(qf[ks], bh, o);
+        o = M::mma(qf[ks], bl, o);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = uf[e] - x[e];  // x <- W
+    if constexpr (OUT) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] *= __expf(sm.gam[rt1 * 16 + acc_row(e)]);
+    }
+    if (more) load_p1(ci + 1, nent.y, nent.z);  // Wk, q, U of the next chunk
+    {
+      const int c = acc_col(), r = rt1 * 16 + acc_row(0);
+      f32x4 xs;  // rows of W times e^{gamma_last - gamma_r}, 0 past len
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xs[e] = (r + e < len) ? x[e] * __expf(sm.gam[len - 1] - sm.gam[r + e]) : 0.f;
+      if constexpr (OUT) {
+        st4_split<E>(&sm.Wt[c][r], &sm.Wtl[c][r], x);
+        st4_split<E>(&sm.Ws[c][r], &sm.Wsl[c][r], xs);
+      } else {
+        st4_split<E>(&sm.Wt[c][r], &sm.Wtl[c][r], xs);
+      }
+      if constexpr (STORE) store_tile<float>(a.W + slot * C * D, D, rt1 * 16, col0, x, C);
+    }
+    __syncthreads();
+
+    // phase 2: H <- Gam_last H + K^T diag(e) W;  o = scale (diag(Gam) Q H + P W)
+    const float gl = __expf(sm.gam[len - 1]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Hr[i][e] *= gl;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const M::frag bh = fr(OUT ? &sm.Ws[r16][ks * 32 + kq] : &sm.Wt[r16][ks * 32 + kq]);
+        const M::frag bl = fr(OUT ? &sm.Wsl[r16][ks * 32 + kq] : &sm.Wtl[r16][ks * 32 + kq]);
+        Hr[i] = M::mma(ktf[i][ks], bh, Hr[i]);
+        Hr[i] = M::mma(ktf[i][ks], bl, Hr[i]);
+      }
+    }
+    if constexpr (OUT) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        M::frag ph, pl;
+        split8(pf[ks][0], pf[ks][1], ph, pl);
+        const M::frag bh = fr(&sm.Wt[r16][ks * 32 + kq]);
+        const M::frag bl = fr(&sm.Wtl[r16][ks * 32 + kq]);
+        o = M::mma(ph, bh, o);
+        o = M::mma(ph, bl, o);
+        o = M::mma(pl, bh, o);
+      }
+    }
+    if (more) load_p2(ci + 1);  // K^T and P of the next chunk
+    if constexpr (OUT) {
+      E* og = (E*)a.o + (int64_t)tok0 * a.Hv * D + (int64_t)h * D;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] *= a.scale;
+      store_tile<E>(og, (int64_t)a.Hv * D, rt1 * 16, col0, o, len);
+    }
+    write_Ht();  // phase 1 (the only reader of H^T) is over for every wave
+    ent = nent;
+  }
+  if (a.ht) {
+    float* dst = a.ht + ((int64_t)n * a.Hv + h) * D * D;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dst[((i ? rtB : rtA) * 16 + acc_row(e)) * D + col0 + acc_col()] = Hr[i][e];
+  }
+}
+
 template <int NC>
 static void launch_fwd_nc(const ChunkArgs& a, hipStream_t st, int mode, bool f8) {
   const dim3 grid(state_grid(a.N, a.Hk, a.G, kD / NC));
@@ -525,6 +743,14 @@ static void launch_fwd_nc(const ChunkArgs& a, hipStream_t st, int mode, bool f8)
 void launch_state_fwd_wide(const ChunkArgs& a, hipStream_t st, int mode, bool half, bool f8) {
   if (half) launch_fwd_nc<kD / 2>(a, st, mode, f8);
   else launch_fwd_nc<kD>(a, st, mode, f8);
+}
+
+void launch_state_fwd_cols(const ChunkArgs& a, hipStream_t st, int mode, bool f8) {
+  const dim3 grid(state_grid(a.N, a.Hk, a.G, kD / 16));
+  if (f8) state_fwd_cols_kernel<kFwdOut, true><<<grid, 256, 0, st>>>(a);  // fp8 inputs: inference only
+  else if (mode == kFwdOut) state_fwd_cols_kernel<kFwdOut, false><<<grid, 256, 0, st>>>(a);
+  else if (mode == kFwdStore) state_fwd_cols_kernel<kFwdStore, false><<<grid, 256, 0, st>>>(a);
+  else state_fwd_cols_kernel<kFwdBoth, false><<<grid, 256, 0, st>>>(a);
 }
 
 void launch_state_bwd_wide(const ChunkArgs& a, hipStream_t st) {
