@@ -50,7 +50,7 @@ struct ChunkArgs {
   // sizes
   int N, T, Hk, Hv, G, max_chunks;
   float scale;
-  int kt_plain;  // the preparation writes Kt = k_s^T unscaled (for the 16-column state pass)
+  int kt_plain;  // the preparation writes Kt = k_s^T unscaled (bf16, d = 128, chunk 64: the wide and 16-column passes)
   float f8_scale[3];  // fp8 inputs: power-of-two scales of q, k and v (q, k, v then point to e4m3 bytes)
   // workspace
   const int32_t* table;       // [max_chunks][4]
@@ -332,10 +332,7 @@ __device__ __forceinline__ void unit_lower_inverse(const float (*Am)[LDCF], floa
   }
 }
 
-// KP: Kt holds the plain k_s^T (exact in bf16, no lo part) and the decay
-// e^{gamma_last - gamma_s} is applied to the rows of W instead (Ws, Wsl); with
-// OUT the unscaled W^T stays in Wt / Wtl for the output's P W.
-template <typename E, int D, int C, int DVT, bool OUT, bool KP = false>
+template <typename E, int D, int C, int DVT, bool OUT>
 struct StateSmem {
   static constexpr int LDQ = D + Pad<E>::E16;
   static constexpr int LDCE = C + Pad<E>::E16;
@@ -344,15 +341,13 @@ struct StateSmem {
   E Wk[C][LDQ];
   E Q[OUT ? C : 1][LDQ];
   E Kt[D][LDCE];
-  E Ktl[LO && !KP ? D : 1][LDCE];
+  E Ktl[LO ? D : 1][LDCE];
   E P[OUT ? C : 1][LDCE];
   E Pl[OUT && LO ? C : 1][LDCE];
   E Ht[DVT][LDQ];
   E Htl[LO ? DVT : 1][LDQ];
   E Wt[DVT][LDCE];
   E Wtl[LO ? DVT : 1][LDCE];
-  E Ws[KP && OUT ? DVT : 1][LDCE];
-  E Wsl[KP && OUT && LO ? DVT : 1][LDCE];
   float U[C][LDU];
   float gam[C];
 };

@@ -331,13 +331,13 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
 //   OUT   = false: writes, per chunk, the entering state Hc and W (for the
 //                  backward pass), and the final state if asked
 // ---------------------------------------------------------------------------
-template <typename E, int D, int C, int DVT, int MODE, bool KP = false, bool F8 = false>
+template <typename E, int D, int C, int DVT, int MODE>
 __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
   constexpr bool OUT = MODE & kFwdOut, STORE = MODE & kFwdStore;
-  using S = StateSmem<E, D, C, DVT, OUT, KP>;
+  using S = StateSmem<E, D, C, DVT, OUT>;
   __shared__ S sm;
   constexpr bool LO = Split<E>::on;
-  constexpr bool KL = LO && !KP;  // Kt has a lo part
+  constexpr bool KL = LO;  // Kt has a lo part
   constexpr int NVT = D / DVT;
   constexpr int NCT = DVT / 16;                 // column tiles
   constexpr int NHT = (D / 16) * NCT;           // state tiles
@@ -397,10 +397,7 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
     pKt.load((const E*)a.Kt + slot * D * C, C, D);
     if constexpr (KL) pKtl.load((const E*)a.Ktl + slot * D * C, C, D);
     if constexpr (OUT) {
-      if constexpr (F8)
-        pQ.load_f8((const uint8_t*)a.q + (int64_t)ptok * a.sqk + (int64_t)j * D, a.sqk, plen, a.f8_scale[0]);
-      else
-        pQ.load((const E*)a.q + (int64_t)ptok * a.sqk + (int64_t)j * D, a.sqk, plen);
+      pQ.load((const E*)a.q + (int64_t)ptok * a.sqk + (int64_t)j * D, a.sqk, plen);
       pP.load(a.P + slot * C * C, C, C);
     }
     pU.load(a.U + slot * C * D + col0, D, C);
@@ -448,22 +445,7 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
         for (int e = 0; e < 4; ++e) wv[e] = sm.U[rt * 16 + acc_row(e)][ct * 16 + acc_col()] - x[e];
         {
           const int c = ct * 16 + acc_col(), r = rt * 16 + acc_row(0);
-          if constexpr (KP) {
-            // rows of W scaled by e^{gamma_last - gamma_r} (0 past len) for the
-            // state update K^T (diag(e) W); the output's P W keeps W itself
-            f32x4 ws;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              ws[e] = (r + e < len) ? wv[e] * __expf(sm.gam[len - 1] - sm.gam[r + e]) : 0.f;
-            if constexpr (OUT) {
-              st4_split<E>(&sm.Wt[c][r], &sm.Wtl[0][0] + c * S::LDCE + r, wv);
-              st4_split<E>(&sm.Ws[c][r], &sm.Wsl[0][0] + c * S::LDCE + r, ws);
-            } else {
-              st4_split<E>(&sm.Wt[c][r], &sm.Wtl[0][0] + c * S::LDCE + r, ws);
-            }
-          } else {
-            st4_split<E>(&sm.Wt[c][r], &sm.Wtl[0][0] + c * S::LDCE + r, wv);
-          }
+          st4_split<E>(&sm.Wt[c][r], &sm.Wtl[0][0] + c * S::LDCE + r, wv);
         }
         if constexpr (STORE) store_tile<float>(a.W + slot * C * D, D, rt * 16, col0 + ct * 16, wv, C);
         if constexpr (OUT) {
@@ -482,19 +464,10 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
       const int t = w + kChunkWaves * i;
       if (t < NHT) {
         const int rt = t / NCT, ct = t % NCT;
-        f32x4 y;
-        if constexpr (KP) {
-          // K exact in bf16: hi and lo parts of the scaled W
-          const E* wh = OUT ? &sm.Ws[ct * 16][0] : &sm.Wt[ct * 16][0];
-          const E* wl = OUT ? &sm.Wsl[0][0] + ct * 16 * S::LDCE : &sm.Wtl[0][0] + ct * 16 * S::LDCE;
-          y = mm_tile<E, C>(zero4(), &sm.Kt[rt * 16][0], S::LDCE, wh, S::LDCE);
-          if constexpr (LO) y = mm_tile<E, C>(y, &sm.Kt[rt * 16][0], S::LDCE, wl, S::LDCE);
-        } else {
-          y = mm_tile<E, C>(zero4(), &sm.Kt[rt * 16][0], S::LDCE, &sm.Wt[ct * 16][0], S::LDCE);
-          if constexpr (LO) {
-            y = mm_tile<E, C>(y, &sm.Kt[rt * 16][0], S::LDCE, &sm.Wtl[ct * 16][0], S::LDCE);
-            y = mm_tile<E, C>(y, &sm.Ktl[rt * 16][0], S::LDCE, &sm.Wt[ct * 16][0], S::LDCE);
-          }
+        f32x4 y = mm_tile<E, C>(zero4(), &sm.Kt[rt * 16][0], S::LDCE, &sm.Wt[ct * 16][0], S::LDCE);
+        if constexpr (LO) {
+          y = mm_tile<E, C>(y, &sm.Kt[rt * 16][0], S::LDCE, &sm.Wtl[ct * 16][0], S::LDCE);
+          y = mm_tile<E, C>(y, &sm.Ktl[rt * 16][0], S::LDCE, &sm.Wt[ct * 16][0], S::LDCE);
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) Hr[i][e] = gl * Hr[i][e] + y[e];
@@ -555,8 +528,10 @@ constexpr int state_dvt() { return D >= 32 ? 32 : D; }
 // chip idles (a single long sequence has only Hv of them).  The state's dv
 // columns are independent (the update multiplies it from the left only), so
 // it can be split:
-//  - at most 64 chains: 16-column tiles, eight workgroups per chain (the
-//    general tiled pass; one 65536-token sequence at d = 128: 8.0 -> 3.1 ms);
+//  - at most 64 chains: 16-column tiles, eight 256-thread workgroups per chain
+//    that read their operand rows straight into matrix-core fragments
+//    (state_wide.hip; one 65536-token sequence at d = 128: 8.0 ms with whole
+//    states, 2.8 ms with LDS-staged 16-column tiles, 2.15 ms now);
 //  - two workgroups per chain with 64 columns each (the whole-state pass
 //    halved, with the same arithmetic per element, so the same bits): when
 //    there are fewer chains than CUs, and for inference up to four chains per
@@ -575,16 +550,12 @@ inline int state_columns(const ChunkArgs& a, int D, int mode) {
   return chains < (mode == kFwdOut ? 4 * kNumCUs : kNumCUs) ? D / 2 : D;
 }
 
-template <typename E, int D, int C, int DVT, bool KP = false, bool F8 = false>
+template <typename E, int D, int C, int DVT>
 static void launch_state_fwd_tiled(const ChunkArgs& a, hipStream_t st, int mode) {
   const dim3 grid(state_grid(a.N, a.Hk, a.G, D / DVT));
-  if constexpr (F8) {  // fp8 inputs: inference only
-    state_fwd_kernel<E, D, C, DVT, kFwdOut, KP, true><<<grid, kChunkThreads, 0, st>>>(a);
-    return;
-  }
-  if (mode == kFwdOut) state_fwd_kernel<E, D, C, DVT, kFwdOut, KP><<<grid, kChunkThreads, 0, st>>>(a);
-  else if (mode == kFwdStore) state_fwd_kernel<E, D, C, DVT, kFwdStore, KP><<<grid, kChunkThreads, 0, st>>>(a);
-  else state_fwd_kernel<E, D, C, DVT, kFwdBoth, KP><<<grid, kChunkThreads, 0, st>>>(a);
+  if (mode == kFwdOut) state_fwd_kernel<E, D, C, DVT, kFwdOut><<<grid, kChunkThreads, 0, st>>>(a);
+  else if (mode == kFwdStore) state_fwd_kernel<E, D, C, DVT, kFwdStore><<<grid, kChunkThreads, 0, st>>>(a);
+  else state_fwd_kernel<E, D, C, DVT, kFwdBoth><<<grid, kChunkThreads, 0, st>>>(a);
 }
 
 template <typename E, int D, int C, bool F8>
@@ -629,9 +600,9 @@ void launch_chunk_fwd_core(const ChunkArgs& args, hipStream_t st, int mode) {
   if constexpr (use_wide_state<E, D, C>()) {
     if (nc == 16) launch_state_fwd_cols(a, st, mode, F8);
     else launch_state_fwd_wide(a, st, mode, nc < D, F8);
-    return;
+  } else {
+    launch_state_fwd_tiled<E, D, C, DVT>(a, st, mode);  // reads K~^T in hi + lo
   }
-  launch_state_fwd_tiled<E, D, C, DVT>(a, st, mode);
 }
 
 // explicit instantiation helpers used by the dispatcher in chunk_bwd.hip
