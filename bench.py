@@ -71,6 +71,16 @@ def kernel_bytes(cfg, n_chunks: int, has_h0: bool) -> dict:
     # there), else K~ in hi + lo parts
     kt = 1 if (cfg.dtype == "bf16" and D == 128 and C == 64) else lo
     prep_out = S * (tile_e + tile_f + cc_f + kt * tile_e + row_f)   # Wk, U, P, K^T, gamma
+    # what the preparation adds for the reverse pass: T and Wk^T (hi + lo); for the tiled
+    # reverse pass also P^T, the K rows and (Gamma q)^T (the whole-state pass, kt == 1,
+    # forms those from P, k and q)
+    prep_bwd_out = S * (cc_f + lo * tile_e) + (0 if kt == 1 else S * (cc_f + (kt + lo) * tile_e))
+    # the reverse pass: P (or P^T), K rows, Wk^T, (Gamma q)^T (or q), gamma, dO in; dH_n and
+    # dW^T out (the tiled pass also writes dW rows)
+    if kt == 1:
+        state_bwd = SK * 2 * tile_e + S * (cc_f + lo * tile_e + row_f + tile_e) + S * (dd_f + tile_f)
+    else:
+        state_bwd = S * (cc_f + (kt + 2 * lo) * tile_e + row_f + tile_e) + S * (dd_f + 2 * tile_f)
     return {
         # decode: the state is read and written once per (sequence, v-head)
         "recurrent_step": 2 * N * Hv * dd_f + N * (2 * Hk * D + 2 * Hv * D) * es + 2 * N * Hv * 4,
@@ -82,17 +92,17 @@ def kernel_bytes(cfg, n_chunks: int, has_h0: bool) -> dict:
         "norm_fwd": 3 * T * Hv * D * es + D * es,
         "norm_bwd": 5 * T * Hv * D * es + D * es,
         "chunk_prep": qk_in + v_in + gb_in + prep_out,
-        # + P^T, T, K rows (as the K^T above), Wk^T and (Gamma q)^T for the backward
-        "chunk_prep_bwd": qk_in + v_in + gb_in + prep_out + S * (2 * cc_f + (kt + 2 * lo) * tile_e),
+        # + what the reverse pass reads from the preparation (prep_bwd_out above)
+        "chunk_prep_bwd": qk_in + v_in + gb_in + prep_out + prep_bwd_out,
         "chunk_state_fwd": SK * tile_e + S * (tile_e + kt * tile_e + tile_f + cc_f + row_f)
                            + S * tile_e + (st if has_h0 else 0) + st,
         # forward that also keeps the backward's products: prep_bwd's outputs, and H_c, W per slot
-        "chunk_prep_save": qk_in + v_in + gb_in + prep_out + S * (2 * cc_f + (kt + 2 * lo) * tile_e),
+        "chunk_prep_save": qk_in + v_in + gb_in + prep_out + prep_bwd_out,
         "chunk_state_save": SK * tile_e + S * (tile_e + kt * tile_e + tile_f + cc_f + row_f)
                             + S * tile_e + (st if has_h0 else 0) + st + S * (dd_f + tile_f),
         "chunk_state_store": S * (tile_e + kt * tile_e + tile_f + row_f) + (st if has_h0 else 0)
                              + S * (dd_f + tile_f),
-        "chunk_state_bwd": S * (cc_f + (kt + 2 * lo) * tile_e + row_f + tile_e) + S * (dd_f + 2 * tile_f),
+        "chunk_state_bwd": state_bwd,
         "chunk_grad_a": SK * tile_e + S * (2 * dd_f + 2 * tile_f + 2 * tile_e + 2 * row_f)
                         + S * (3 * tile_f + 2 * cc_f + 4),
         "chunk_grad_b": qk_in + S * (4 * tile_f + 4 * cc_f + tile_e + 2 * row_f + 4)

@@ -263,15 +263,20 @@ __global__ __launch_bounds__(NTH) void grad_a_kernel(ChunkArgs a) {
     TileRegs<float, D, D, NTH> rH;
     TileRegs<E, C, D, NTH> rO, rV;
     TileRegs<float, C, D, NTH> rW;
+    // the whole-state reverse pass writes dW^T only: its rows are staged transposed here
+    constexpr bool DW_T = use_wide_state<E, D, C>();
+    TileRegs<float, D, C, NTH, true> rWt;
     rH.load(Hc, D, D);
     rO.load(dog, ldo, len);
-    rW.load(a.dW + slot * C * D, D, C);
+    if constexpr (DW_T) rWt.load(a.dWt + slot * D * C, C, D);
+    else rW.load(a.dW + slot * C * D, D, C);
     rV.load((const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)h * D, a.sv, len);
     rD.load(dHn, D, D);
     rK.load((const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D, a.sqk, len);
     rH.template store_split<E>(&sm.Hh[0][0], Hlo, S::LDQ);
     rO.store(&sm.Od[0][0], S::LDQ);
-    rW.template store_split<E>(&sm.Xh[0][0], Xlo, S::LDQ);
+    if constexpr (DW_T) rWt.template store_t<E>(&sm.Xh[0][0], S::LDQ, Xlo, S::LDQ);
+    else rW.template store_split<E>(&sm.Xh[0][0], Xlo, S::LDQ);
     rV.store(&sm.Vs[0][0], S::LDQ);
   }
   if (tid < C) {  // per-row gates; every load unconditional (clamped rows), so they issue together
@@ -861,18 +866,21 @@ static WsPlan plan(const gdn_shape* s) {
   p.Ktl = o; o = align256(o + (es == 2 && !plain_k ? M * Hv * D * C * es : 0));
   p.gam = o; o = align256(o + M * Hv * C * 4);
   p.end_fwd = o;
-  p.Ptr = o; o = align256(o + M * Hv * C * C * 4);
+  // the whole-state reverse pass (plain_k) forms P^T, the K rows and (Gam q)^T
+  // from P, k and q, and writes dW^T only
+  const size_t tr = plain_k ? 0 : 1;
+  p.Ptr = o; o = align256(o + tr * M * Hv * C * C * 4);
   p.Tw = o; o = align256(o + M * Hv * C * C * 4);
-  p.Krh = o; o = align256(o + M * Hv * C * D * es);
+  p.Krh = o; o = align256(o + tr * M * Hv * C * D * es);
   p.Krl = o; o = align256(o + (plain_k ? 0 : M * Hv * C * D * es));
   p.Wth = o; o = align256(o + M * Hv * D * C * es);
   p.Wtl = o; o = align256(o + M * Hv * D * C * es);
-  p.Qth = o; o = align256(o + M * Hv * D * C * es);
-  p.Qtl = o; o = align256(o + M * Hv * D * C * es);
+  p.Qth = o; o = align256(o + tr * M * Hv * D * C * es);
+  p.Qtl = o; o = align256(o + tr * M * Hv * D * C * es);
   p.Hc = o; o = align256(o + M * Hv * D * D * 4);
   p.W = o; o = align256(o + M * Hv * C * D * 4);
   p.dHn = o; o = align256(o + M * Hv * D * D * 4);
-  p.dW = o; o = align256(o + M * Hv * C * D * 4);
+  p.dW = o; o = align256(o + tr * M * Hv * C * D * 4);
   p.dWt = o; o = align256(o + M * Hv * D * C * 4);
   p.dT = o; o = align256(o + M * Hv * C * C * 4);
   p.dWkt = o; o = align256(o + M * Hv * D * C * 4);

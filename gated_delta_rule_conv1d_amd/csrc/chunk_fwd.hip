@@ -173,7 +173,8 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
               sm.Am[r][s] = (s < r) ? sm.beta[r] * dd * sm.Sk[r][s] : 0.f;
             }
             store_tile<float>(Pg, C, rt * 16, ct * 16, pv, C);
-            store_tile_t(a.Ptr + slot * C * C, C, rt * 16, ct * 16, pv);
+            // (the whole-state reverse pass, kt_plain, gathers P^T from P itself)
+            if (!a.kt_plain) store_tile_t(a.Ptr + slot * C * C, C, rt * 16, ct * 16, pv);
           } else {  // P^T = K Q^T tiles: a lane holds P[r][s..s+3] (one 16-byte store) and the same piece of A
             const f32x4 acc = mm_tile<E, D>(zero4(), &sm.Ks[ct * 16][0], S::LDQ, &sm.Qs[rt * 16][0], S::LDQ);
             const int r = rt * 16 + acc_col(), s0 = ct * 16 + acc_row(0);
@@ -215,12 +216,13 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
             if constexpr (Split<E>::on)
               if (!plain) Vec<E>::store((E*)a.Ktl + slot * D * C + d * C + s0, lo);
           }
-          if constexpr (LO_OUT) {
-            // rows e_s k_s [C][D] (with kt_plain the rows k_s, exact: no lo part)
-            // and (Gam_r q_r)^T [D][C], hi / lo, for the reverse state pass
+          // rows e_s k_s [C][D] and (Gam_r q_r)^T [D][C], hi / lo, for the
+          // reverse state pass (the whole-state pass, kt_plain, reads k and q
+          // and forms them itself)
+          if (LO_OUT && !plain) {
             for (int e = t0; e < C * (D / V); e += nt) {
               const int s = e / (D / V), c0 = (e % (D / V)) * V;
-              const float es = (s < len) ? (plain ? 1.f : __expf(glast - sm.gam[s])) : 0.f;
+              const float es = (s < len) ? __expf(glast - sm.gam[s]) : 0.f;
               float val[V], lo[V];
 #pragma unroll
               for (int i = 0; i < V; ++i) {
@@ -229,8 +231,7 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
               }
               const int64_t o = slot * C * D + (int64_t)s * D + c0;
               Vec<E>::store((E*)a.Krh + o, val);
-              if constexpr (Split<E>::on)
-                if (!plain) Vec<E>::store((E*)a.Krl + o, lo);
+              if constexpr (Split<E>::on) Vec<E>::store((E*)a.Krl + o, lo);
             }
             // Q^T through V x V register blocks: a thread reads V rows of V
             // consecutive d and writes V rows of Q^T; adjacent lanes take adjacent

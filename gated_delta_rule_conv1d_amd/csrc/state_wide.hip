@@ -58,6 +58,7 @@ struct BwdSmem {
   E dHtl[kD][kLDQ];
   E Kr[kC][kLDQ];    // rows of K (exact in bf16; the decay e_s goes onto K dH's rows)
   float gam[kC];
+  float Gm[kC];      // Gam_s = e^{gamma_s}
 };
 
 __device__ __forceinline__ M::frag fr(const E* p) { return M::load(p); }
@@ -361,40 +362,53 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
     }
   };
 
-  // staged operands of the next chunk (reverse order)
+  // staged operands of the next chunk (reverse order).  K, q and P come
+  // straight from the layer's k and q rows and the forward's P: the rows of K
+  // into LDS, q and P gathered column-wise into this wave's fragments of
+  // (Gam q)^T and P^T (a 2- or 4-byte load per element, rows past the chunk's
+  // end reading zero), Gam applied and the hi / lo parts split at use.
+  const int j = h / a.G;
   uint4 kr_h0, kr_h1;                // this thread's pieces of the K rows (named: registers)
   ColRegs<E, C, D, kThreads> pO;    // dO of the chunk, gathered column-wise
   float g_r = 0.f;
-  float4 ptf[2][2];                 // P^T rows of this wave's dW tiles
-  M::frag qth[2], qtl[2], wth[2], wtl[2];  // (Gam q)^T and Wk^T rows of its dH tiles
+  float ptf[2][8];                  // P^T rows of this wave's dW tiles
+  uint32_t qraw[2][4];              // q columns of its dH tiles (bf16 pairs), Gam not yet applied
+  M::frag wth[2], wtl[2];           // Wk^T rows of its dH tiles
+  const int64_t lq = a.sqk * 2;     // byte stride of q / k rows
   auto load_shared = [&](int ci, int tok0, int len) {
     const int64_t slot = (int64_t)ci * a.Hv + h;
-    const Buf kh((const E*)a.Krh + slot * C * D, C * D * 2);
-    kr_h0 = kh.u4(tid * 16);
-    kr_h1 = kh.u4((tid + kThreads) * 16);
+    // 16-byte piece e of the K rows: row e / 16, columns (e % 16) * 8 ..
+    const Buf kb((const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D, (int64_t)len * lq);
+    kr_h0 = kb.u4((int)((tid >> 4) * lq) + (tid & 15) * 16);
+    kr_h1 = kb.u4((int)(((tid + kThreads) >> 4) * lq) + (tid & 15) * 16);
     pO.load((const E*)a.d_o + (int64_t)tok0 * a.Hv * D + (int64_t)h * D, (int64_t)a.Hv * D, len);
     g_r = Buf(a.gam + slot * C, C * 4).f1((tid & (C - 1)) * 4);  // every thread loads; threads < C use it
   };
-  const int p_off = ((rt1 * 16 + r16) * C + kq) * 4;   // lane's fragment offset in a [C][C] fp32 tile
-  const int t_off = ((rt2 * 16 + r16) * C + kq) * 2;   // and in a [D][C] bf16 tile
+  // P^T[c][s] = P[s][c]: this lane's column c = rt1 * 16 + r16, rows s = ks * 32 + kq + u
   auto load_p1 = [&](int ci) {
-    const Buf pb(a.Ptr + ((int64_t)ci * a.Hv + h) * C * C, C * C * 4);
+    const Buf pb(a.P + ((int64_t)ci * a.Hv + h) * C * C, C * C * 4);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      ptf[ks][0] = pb.f4(p_off + ks * 128);
-      ptf[ks][1] = pb.f4(p_off + ks * 128 + 16);
-    }
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) ptf[ks][u] = pb.f1(((ks * 32 + kq + u) * C + rt1 * 16 + r16) * 4);
   };
-  auto load_p2 = [&](int ci) {
+  // (Gam q)^T[d][s]: this lane's d = rt2 * 16 + r16, positions s = ks * 32 + kq + u
+  auto load_p2 = [&](int ci, int tok0, int len) {
     const int64_t o = ((int64_t)ci * a.Hv + h) * D * C;
-    const Buf qh((const E*)a.Qth + o, D * C * 2), ql((const E*)a.Qtl + o, D * C * 2);
+    const int t_off = ((rt2 * 16 + r16) * C + kq) * 2;  // lane's fragment offset in a [D][C] bf16 tile
     const Buf wh((const E*)a.Wth + o, D * C * 2), wl((const E*)a.Wtl + o, D * C * 2);
+    const Buf qb((const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D, (int64_t)len * lq);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      qth[ks] = qh.fr(t_off + ks * 64);
-      qtl[ks] = ql.fr(t_off + ks * 64);
       wth[ks] = wh.fr(t_off + ks * 64);
       wtl[ks] = wl.fr(t_off + ks * 64);
+#pragma unroll
+      for (int u = 0; u < 8; u += 2) {
+        const int s = ks * 32 + kq + u, off = (rt2 * 16 + r16) * 2;
+        const uint32_t x0 = __builtin_amdgcn_raw_buffer_load_b16(qb.r, (int)(s * lq) + off, 0, 0);
+        const uint32_t x1 = __builtin_amdgcn_raw_buffer_load_b16(qb.r, (int)((s + 1) * lq) + off, 0, 0);
+        qraw[ks][u / 2] = (x0 & 0xFFFFu) | (x1 << 16);
+      }
     }
   };
 
@@ -409,7 +423,7 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
     ent = entry(c1 - 1);
     load_shared(c1 - 1, ent.y, ent.z);
     load_p1(c1 - 1);
-    load_p2(c1 - 1);
+    load_p2(c1 - 1, ent.y, ent.z);
   }
   write_dHt();
   for (int ci = c1 - 1; ci >= c0; --ci) {
@@ -422,7 +436,10 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
       *reinterpret_cast<uint4*>(&sm.Kr[e1 >> 4][(e1 & 15) * 8]) = kr_h1;
     }
     pO.store(&sm.OW[0][0], kLD2C);
-    if (tid < C) sm.gam[tid] = g_r;
+    if (tid < C) {
+      sm.gam[tid] = g_r;
+      sm.Gm[tid] = __expf(g_r);
+    }
     __syncthreads();
     const bool more = ci > c0;
     int4 nent = ent;
@@ -434,7 +451,9 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
     // phase 1: dW = scale P^T dO + diag(e) K dH on this wave's tiles, one tile at a time
     M::frag ph[2], pl[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) split8(ptf[ks][0], ptf[ks][1], ph[ks], pl[ks]);
+    for (int ks = 0; ks < 2; ++ks)
+      split8(make_float4(ptf[ks][0], ptf[ks][1], ptf[ks][2], ptf[ks][3]),
+             make_float4(ptf[ks][4], ptf[ks][5], ptf[ks][6], ptf[ks][7]), ph[ks], pl[ks]);
     if (more) load_p1(ci - 1);  // P^T of the next chunk
     // Stores go after this chunk's prefetch loads: the wait for a load also
     // waits for every earlier vector-memory access of the wave.
@@ -469,7 +488,6 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) kd[e] = dec[e] * kd[e] + a.scale * p[e];  // kd <- dW
-      store_tile<float>(a.dW + slot * C * D, D, rt1 * 16, (cb + i) * 16, kd, C);
       store_tile_t(a.dWt + slot * D * C, C, rt1 * 16, (cb + i) * 16, kd);
       const int cc = (cb + i) * 16 + acc_col(), r = rt1 * 16 + acc_row(0);
       st4_split<E>(&sm.OW[cc][C + r], &sm.dWl[cc][r], kd);
@@ -479,6 +497,20 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
 
     // phase 2: dH <- Gam_last dH + scale (diag(Gam) Q)^T dO - Wk^T dW
     const float gl = __expf(sm.gam[len - 1]);
+    M::frag qth[2], qtl[2];  // (Gam q)^T, hi / lo (the values the preparation would store)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const float4 g0 = *reinterpret_cast<const float4*>(&sm.Gm[ks * 32 + kq]);
+      const float4 g1 = *reinterpret_cast<const float4*>(&sm.Gm[ks * 32 + kq + 4]);
+      const float gs[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t b = (qraw[ks][u / 2] >> (16 * (u & 1))) & 0xFFFFu;
+        v[u] = gs[u] * bf2f((bf16)b);
+      }
+      split8(make_float4(v[0], v[1], v[2], v[3]), make_float4(v[4], v[5], v[6], v[7]), qth[ks], qtl[ks]);
+    }
 #pragma unroll
     for (int i = 0; i < kP2; ++i) {
       const int c = i * 16 + r16;
@@ -498,7 +530,7 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
       for (int e = 0; e < 4; ++e) dH[i][e] = gl * dH[i][e] + a.scale * y1[e] - y2[e];
       __builtin_amdgcn_sched_barrier(0);  // keep the next tile's fragment loads out of this one's registers
     }
-    if (more) load_p2(ci - 1);
+    if (more) load_p2(ci - 1, nent.y, nent.z);
     write_dHt();  // phase 1 (the only reader of dH^T) is over for every wave
     ent = nent;
   }
