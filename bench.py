@@ -254,6 +254,10 @@ def main():
     ap.add_argument("--fused-gates", action="store_true",
                     help="compute the gates inside the chunk kernels (gdn_chunk_*_gated) instead of with "
                          "gdn_gates / gdn_gates_bwd (measured slightly slower: the default is the separate kernels)")
+    ap.add_argument("--max-tokens", type=int, default=0, metavar="N",
+                    help="bounded-memory training step: the chunk calls run per token segment of at most N "
+                         "tokens and the backward recomputes the forward's chunk products (0: the whole row, "
+                         "the forward keeping its products for the backward)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the reference for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters of rocprofv3) and exit")
@@ -321,6 +325,13 @@ def main():
             f = layer.forward(x, w, None, None, cu, z, wn, h0, for_backward=cfg.bwd, gates=gates)
             if cfg.bwd:
                 layer.backward(dy, x, w, None, None, cu, f, z, wn, h0, gates=gates)
+    elif args.max_tokens:
+        def step():
+            g, beta = layer.gates(ga, gb, A_log, dt_bias)
+            f = layer.forward(x, w, g, beta, cu, z, wn, h0, max_tokens=args.max_tokens)
+            if cfg.bwd:
+                r = layer.backward(dy, x, w, g, beta, cu, f, z, wn, h0)
+                layer.gates_backward(ga, gb, A_log, dt_bias, r["dg"], r["dbeta"])
     else:
         def step():
             g, beta = layer.gates(ga, gb, A_log, dt_bias)
@@ -414,7 +425,9 @@ def main():
                    "gates": ("g, beta computed from a, b, A_log, dt_bias inside the chunk kernels"
                              if args.fused_gates and not cfg.decode else
                              "g, beta computed from a, b, A_log, dt_bias in the step (gate kernels)"),
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   "chunk_workspace_gib": round(sum(t.numel() for t in layer._ws.values()) / 2 ** 30, 3),
+                   "max_tokens": args.max_tokens or None},
         "roofline": roof,
         "step_fraction_of_fused_minimum": (round(step_bytes / (HBM_PEAK_GBS * 1e9) / (ms_per_step * 1e-3), 4)
                                            if step_bytes else None),

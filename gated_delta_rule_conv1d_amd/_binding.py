@@ -244,11 +244,13 @@ def _qkv_strides(q, k, v, shape: Shape):
 
 def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
               cu_seqlens: torch.Tensor, shape: Shape, h0: Optional[torch.Tensor] = None, want_ht: bool = True,
-              ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None, save: bool = False):
+              ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None, save: bool = False,
+              ht_out: Optional[torch.Tensor] = None):
     """q, k: [T, Hk*dk] views; v: [T, Hv*dv] view; g, beta: fp32 [T, Hv].
     Returns (o [T, Hv, dv], ht [N, Hv, dk, dv] fp32 or None).  With save=True
     (gdn_chunk_fwd_save) ws must be a backward-sized workspace, which then
-    holds what chunk_bwd(..., saved=True) reads."""
+    holds what chunk_bwd(..., saved=True) reads.  out / ht_out: contiguous
+    views of the caller's tensors to receive o / ht."""
     dt = shape.torch_dtype
     T, N, Hv, dk, dv = shape.total_tokens, shape.n_seqs, shape.h_v, shape.d_k, shape.d_v
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
@@ -259,8 +261,14 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
     if h0 is not None:
         _need(h0, "h0", torch.float32, (N, Hv, dk, dv))
-    o = torch.empty((T, Hv, dv), dtype=dt, device=q.device) if out is None else out
-    ht = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=q.device) if want_ht else None
+    if out is None:
+        out = torch.empty((T, Hv, dv), dtype=dt, device=q.device)
+    _need(out, "out", dt, (T, Hv, dv))
+    o = out
+    ht = None
+    if want_ht:
+        ht = torch.empty((N, Hv, dk, dv), dtype=torch.float32, device=q.device) if ht_out is None else ht_out
+        _need(ht, "ht", torch.float32, (N, Hv, dk, dv))
     if save and ws is None:
         raise ValueError("save=True needs the caller's backward workspace (it carries state to chunk_bwd)")
     ws = _workspace(chunk_bwd_workspace(shape) if save else chunk_fwd_workspace(shape), q.device, ws)
@@ -272,10 +280,13 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
 
 
 def chunk_bwd(q, k, v, g, beta, cu_seqlens, shape: Shape, d_o, h0=None, dht=None, dq=None, dk=None, dv=None,
-              want_dh0: bool = True, ws: Optional[torch.Tensor] = None, saved: bool = False):
+              want_dh0: bool = True, ws: Optional[torch.Tensor] = None, saved: bool = False,
+              dg: Optional[torch.Tensor] = None, dbeta: Optional[torch.Tensor] = None,
+              dh0: Optional[torch.Tensor] = None):
     """Returns dict dq, dk, dv (like q, k, v: [T, H*d]), dg, dbeta [T, Hv] fp32, dh0 (or None).
     saved=True (gdn_chunk_bwd_saved): ws is the workspace a chunk_fwd(..., save=True)
-    with the same inputs just filled."""
+    with the same inputs just filled.  dq, dk, dv, dg, dbeta, dh0 may be given
+    (contiguous views of the caller's tensors) to receive the results."""
     dt = shape.torch_dtype
     T, N, Hk, Hv, dkk, dvv = shape.total_tokens, shape.n_seqs, shape.h_qk, shape.h_v, shape.d_k, shape.d_v
     sqk, sv = _qkv_strides(q, k, v, shape)
@@ -291,9 +302,19 @@ def chunk_bwd(q, k, v, g, beta, cu_seqlens, shape: Shape, d_o, h0=None, dht=None
         raise ValueError("dq/dk/dv must use the token strides of q/k/v")
     if dht is not None:
         _need(dht, "dht", torch.float32, (N, Hv, dkk, dvv))
-    dg = torch.empty((T, Hv), dtype=torch.float32, device=q.device)
-    db = torch.empty((T, Hv), dtype=torch.float32, device=q.device)
-    dh0 = torch.empty((N, Hv, dkk, dvv), dtype=torch.float32, device=q.device) if want_dh0 else None
+    if dg is None:
+        dg = torch.empty((T, Hv), dtype=torch.float32, device=q.device)
+    if dbeta is None:
+        dbeta = torch.empty((T, Hv), dtype=torch.float32, device=q.device)
+    db = dbeta
+    _need(dg, "dg", torch.float32, (T, Hv))
+    _need(db, "dbeta", torch.float32, (T, Hv))
+    if not want_dh0:
+        dh0 = None
+    elif dh0 is None:
+        dh0 = torch.empty((N, Hv, dkk, dvv), dtype=torch.float32, device=q.device)
+    else:
+        _need(dh0, "dh0", torch.float32, (N, Hv, dkk, dvv))
     if saved and ws is None:
         raise ValueError("saved=True needs the workspace filled by chunk_fwd(..., save=True)")
     ws = _workspace(chunk_bwd_workspace(shape), q.device, ws)

@@ -201,10 +201,11 @@ def qkv_inputs(cfg: synth.Config, seed=11):
     return q, k, v
 
 
-def layer_gpu(cfg, inp, layer=None, for_backward=None):
+def layer_gpu(cfg, inp, layer=None, for_backward=None, max_tokens=None):
     """The whole layer through GatedDeltaNetLayer (the path bench.py times):
     forward, and backward when the workload has one (then, by default, the
-    forward keeps its chunk products for the backward, as bench.py does)."""
+    forward keeps its chunk products for the backward, as bench.py does).
+    max_tokens: the bounded-memory mode (chunk calls per token segment)."""
     s = shape_of(cfg)
     dt = cfg.dtype
     L = layer or gdn.GatedDeltaNetLayer(s, cfg.width, norm=cfg.norm)
@@ -212,8 +213,9 @@ def layer_gpu(cfg, inp, layer=None, for_backward=None):
              cu=torch.from_numpy(inp["cu"]).cuda(),
              z=to_dev(inp["z"], dt) if "z" in inp else None, wn=to_dev(inp["w_norm"], dt) if "w_norm" in inp else None,
              h0=f32(inp["h0"]) if "h0" in inp else None)
-    save = cfg.bwd if for_backward is None else for_backward
-    fwd = L.forward(t["x"], t["w"], t["g"], t["beta"], t["cu"], t["z"], t["wn"], t["h0"], for_backward=save)
+    save = (cfg.bwd if for_backward is None else for_backward) and max_tokens is None
+    fwd = L.forward(t["x"], t["w"], t["g"], t["beta"], t["cu"], t["z"], t["wn"], t["h0"], for_backward=save,
+                    max_tokens=max_tokens)
     bwd = None
     if cfg.bwd:
         bwd = L.backward(to_dev(inp["dy"], dt), t["x"], t["w"], t["g"], t["beta"], t["cu"], fwd, t["z"], t["wn"],

@@ -451,6 +451,47 @@ def test_layer_tiny_full(norm, h0):
         assert_close(host(bwd[key]), rb[key], tol, key)
 
 
+def test_layer_segmented_bf16():
+    """The bounded-memory mode (chunk calls per token segment of at most 192
+    tokens: long sequences cut into chunk-aligned pieces that carry the state
+    forward through h0 / ht and its gradient back through dht / dh0, short ones
+    grouped): the same oracle checks as the whole-row layer, a workspace that
+    is a fraction of the whole row's, and agreement with the whole-row run."""
+    cfg = small_cfg(dtype="bf16", d=128, chunk=64, Hk=2, Hv=4, lengths=(300, 1, 64, 65, 130, 0, 700))
+    _print_case("layer_segmented_bf16", lengths=cfg.lengths, max_tokens=192)
+    inp = synth.make_inputs(cfg)
+    segs = gdn.token_segments([int(c) for c in inp["cu"]], cfg.chunk, 192)
+    assert any(p is not None for *_, p in segs) and any(p is None for *_, p in segs)
+    s = shape_of(cfg)
+    seg_ws = max(gdn.chunk_bwd_workspace(gdn.Shape(n1 - n0, t1 - t0, s.h_qk, s.h_v, s.d_k, s.d_v, s.chunk, s.dtype,
+                                                   s.scale)) for t0, t1, n0, n1, _ in segs)
+    assert seg_ws * 3 < gdn.chunk_bwd_workspace(s), (seg_ws, gdn.chunk_bwd_workspace(s))
+    fwd, bwd = layer_gpu(cfg, inp, max_tokens=192)
+    toks, vheads = np.arange(cfg.T), np.arange(cfg.h_v)
+    check_chain(cfg, cfg, inp, fwd, bwd, toks, vheads, np.arange(cfg.channels), list(range(cfg.N)), True)
+    ref = oracle.layer_fwd(cfg, inp, storage="bf16")
+    r32 = oracle.layer_fwd(cfg, inp, storage="bf16", bits=32)
+    rb = oracle.layer_bwd(cfg, inp, ref, inp["dy"], storage="bf16")
+    rb32 = oracle.layer_bwd(cfg, inp, r32, inp["dy"], storage="bf16", bits=32)
+    tol, tol32 = TOL["bf16"], TOL_F32_OUT["bf16"]
+    assert_calibrated(host(fwd["y"]), ref["y"], r32["y"], tol, "y")
+    assert_calibrated(host(fwd["ht"]), ref["ht"], r32["ht"], tol32, "ht", stored=False)
+    for key in ("dx", "dz"):
+        assert_calibrated(host(bwd[key]), rb[key], rb32[key], tol, key, max_bar=False)
+    for key in ("dw_conv", "dg", "dbeta", "dw_norm", "dh0"):
+        assert_calibrated(host(bwd[key]), rb[key], rb32[key], tol32, key, stored=False, max_bar=False)
+    # the whole-row run: the same products, summed in another order where a
+    # segment has few enough chains for the 16-column state pass
+    fw, bw = layer_gpu(cfg, inp, for_backward=False)
+    for key, got, want in (("o", fwd["o"], fw["o"]), ("ht", fwd["ht"], fw["ht"]), ("dg", bwd["dg"], bw["dg"]),
+                           ("dbeta", bwd["dbeta"], bw["dbeta"]), ("dh0", bwd["dh0"], bw["dh0"]),
+                           ("dx", bwd["dx"], bw["dx"])):
+        a, b = host(got).astype(np.float64), host(want).astype(np.float64)
+        rel = np.abs(a - b).max() / max(np.sqrt(np.mean(b * b)), 1e-30)
+        print(f"  segmented vs whole row {key}: max|d|/rms={rel:.3e}", flush=True)
+        assert rel < (5e-2 if key in ("o", "dx") else 2 * tol32), key
+
+
 def test_layer_small_bf16_full():
     """The composed bf16 layer, forward and backward: each GPU stage against the
     oracle step fed the GPU's own upstream result, and every output against
