@@ -580,16 +580,16 @@ void launch_chunk_fwd_core(const ChunkArgs& args, hipStream_t st, int mode) {
       {"chunk_state_save:wide128", "chunk_state_save:wide64", "chunk_state_save:tiled16",
        "chunk_state_save:tiled32"}};
   const int variant = nc == 16 ? 2 : (use_wide_state<E, D, C>() ? (nc < D ? 1 : 0) : (DVT == 16 ? 2 : 3));
-  // Inference preparation runs persistent: as many workgroups as fit at once
-  // (its LDS use allows one per CU at d = 128, chunk 64), each walking its
-  // share of items with the next one's loads in flight (long 65536: 1.69 ->
-  // 1.60 ms; varlen: 0.87 -> 0.83 ms).  The variants that also write the
-  // backward's operands are write-bound and measured slower that way (2.18 ->
-  // 2.29 ms at the training workload): one item per workgroup there.
+  // The preparation runs persistent: as many workgroups as fit at once (its
+  // LDS use allows one per CU at d = 128, chunk 64), each walking its share of
+  // items with the next one's loads in flight (long 65536: 1.69 -> 1.60 ms;
+  // varlen: 0.87 -> 0.83 ms; the training workload's saving form 1.79 -> 1.68
+  // ms since the reverse pass forms its transposed operands itself; when that
+  // form still wrote them, one item per workgroup was faster).
   constexpr int per_cu = (160 * 1024) / (int)sizeof(PrepSmem<E, D, C>) >= 2 ? 2 : 1;
   const int64_t items = (int64_t)a.max_chunks * a.Hk;
   const int64_t resident = (int64_t)kNumCUs * per_cu;
-  dim3 gprep((unsigned)(mode == kFwdOut && items > resident ? resident : items));
+  dim3 gprep((unsigned)(items > resident ? resident : items));
   {
     GDN_PROF(prep_name[mode], st);
     constexpr int NTH = D >= 64 ? 512 : kChunkThreads;  // 8 waves for the wide heads
