@@ -942,11 +942,15 @@ static void launch_chunk_bwd_core(const ChunkArgs& a, hipStream_t st, bool recom
   constexpr int DVT = D >= 32 ? 32 : D;
   if (recompute) launch_chunk_fwd_core<E, D, C, false>(a, st, kFwdStore);  // operands, Hc, W per chunk
   {
+    // the whole-state reverse pass splits each chain's state into two 64-column
+    // halves when there are fewer chains than CUs (the same arithmetic per
+    // element, so the same bits)
     constexpr bool wide = use_wide_state<E, D, C>();
-    const char* name = wide ? "chunk_state_bwd:wide128"
+    const bool half = wide && a.N * a.Hv < kNumCUs;
+    const char* name = wide ? (half ? "chunk_state_bwd:wide64" : "chunk_state_bwd:wide128")
                             : (DVT == 16 ? "chunk_state_bwd:tiled16" : "chunk_state_bwd:tiled32");
     GDN_PROF(name, st);
-    if constexpr (use_wide_state<E, D, C>()) launch_state_bwd_wide(a, st);
+    if constexpr (use_wide_state<E, D, C>()) launch_state_bwd_wide(a, st, half);
     else state_bwd_kernel<E, D, C, DVT><<<dim3(state_grid(a.N, a.Hk, a.G, D / DVT)), kChunkThreads, 0, st>>>(a);
   }
   {

@@ -596,7 +596,8 @@ inline int state_grid(int N, int Hk, int G, int NVT) { return ((N * Hk + 7) / 8)
 void launch_state_fwd_wide(const ChunkArgs& a, hipStream_t st, int mode, bool half, bool f8 = false);
 // 16-column tiles, eight 256-thread workgroups per (sequence, v-head)
 void launch_state_fwd_cols(const ChunkArgs& a, hipStream_t st, int mode, bool f8);
-void launch_state_bwd_wide(const ChunkArgs& a, hipStream_t st);
+// half: two workgroups per (sequence, v-head), 64 state columns each
+void launch_state_bwd_wide(const ChunkArgs& a, hipStream_t st, bool half);
 template <typename E, int D, int C>
 constexpr bool use_wide_state() { return sizeof(E) == 2 && D == 128 && C == 64; }
 

@@ -29,8 +29,6 @@ namespace {
 
 constexpr int kD = 128, kC = 64;
 constexpr int kThreads = 512;
-constexpr int kP1 = 4;            // phase-1 tiles per wave: one row tile, 4 column tiles
-constexpr int kP2 = 8;            // state tiles per wave: one row tile, all 8 column tiles
 constexpr int kKR = kD * kC / 8 / kThreads;  // 16-byte pieces of a [D][C] tile per thread
 constexpr int kLDC = kC + 8;      // row stride of [.][C] tiles (elements), 16-byte pad
 constexpr int kLDQ = kD + 8;      // row stride of [.][D] tiles
@@ -51,11 +49,12 @@ struct FwdSmem {
   float gam[kC];
 };
 
+template <int NC>  // state columns this workgroup carries
 struct BwdSmem {
-  E OW[kD][kLD2C];   // [ dO^T | dW^T ]
-  E dWl[kD][kLDC];   // lo part of dW^T
-  E dHt[kD][kLDQ];   // dH^T
-  E dHtl[kD][kLDQ];
+  E OW[NC][kLD2C];   // [ dO^T | dW^T ]
+  E dWl[NC][kLDC];   // lo part of dW^T
+  E dHt[NC][kLDQ];   // dH^T
+  E dHtl[NC][kLDQ];
   E Kr[kC][kLDQ];    // rows of K (exact in bf16; the decay e_s goes onto K dH's rows)
   float gam[kC];
   float Gm[kC];      // Gam_s = e^{gamma_s}
@@ -334,29 +333,35 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
   }
 }
 
+// NC = 128: the whole state; NC = 64: half of its columns, two workgroups per
+// (sequence, v-head) (exact: dW's and dH's columns are computed independently)
+template <int NC>
 __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
   constexpr int D = kD, C = kC;
-  __shared__ BwdSmem sm;
+  constexpr int P1 = NC / 32;  // dW column tiles per wave
+  constexpr int P2 = NC / 16;  // dH column tiles per wave
+  __shared__ BwdSmem<NC> sm;
   int n, h, vt;
-  if (!state_block(blockIdx.x, a.N, a.Hk, a.G, 1, n, h, vt)) return;
+  if (!state_block(blockIdx.x, a.N, a.Hk, a.G, D / NC, n, h, vt)) return;
+  const int col0 = vt * NC;  // first state column of this workgroup
   const int tid = threadIdx.x, w = wave_id(), lane = lane_id();
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
-  const int rt1 = w & 3, cb = kP1 * (w >> 2);  // dW tiles
-  const int rt2 = w;                           // dH tiles: row tile rt2, every column tile
+  const int rt1 = w & 3, cb = P1 * (w >> 2);  // dW tiles
+  const int rt2 = w;                          // dH tiles: row tile rt2, every column tile
 
-  f32x4 dH[kP2];
+  f32x4 dH[P2];
 #pragma unroll
-  for (int i = 0; i < kP2; ++i) {
+  for (int i = 0; i < P2; ++i) {
     dH[i] = zero4();
     if (a.dht) {
       const float* src = a.dht + ((int64_t)n * a.Hv + h) * D * D;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dH[i][e] = src[(rt2 * 16 + acc_row(e)) * D + i * 16 + acc_col()];
+      for (int e = 0; e < 4; ++e) dH[i][e] = src[(rt2 * 16 + acc_row(e)) * D + col0 + i * 16 + acc_col()];
     }
   }
   auto write_dHt = [&]() {
 #pragma unroll
-    for (int i = 0; i < kP2; ++i) {
+    for (int i = 0; i < P2; ++i) {
       const int c = i * 16 + acc_col(), r = rt2 * 16 + acc_row(0);
       st4_split<E>(&sm.dHt[c][r], &sm.dHtl[c][r], dH[i]);
     }
@@ -369,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
   // end reading zero), Gam applied and the hi / lo parts split at use.
   const int j = h / a.G;
   uint4 kr_h0, kr_h1;                // this thread's pieces of the K rows (named: registers)
-  ColRegs<E, C, D, kThreads> pO;    // dO of the chunk, gathered column-wise
+  ColRegs<E, C, NC, kThreads> pO;   // dO of the chunk (this workgroup's columns), gathered column-wise
   float g_r = 0.f;
   float ptf[2][8];                  // P^T rows of this wave's dW tiles
   uint32_t qraw[2][4];              // q columns of its dH tiles (bf16 pairs), Gam not yet applied
@@ -381,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
     const Buf kb((const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D, (int64_t)len * lq);
     kr_h0 = kb.u4((int)((tid >> 4) * lq) + (tid & 15) * 16);
     kr_h1 = kb.u4((int)(((tid + kThreads) >> 4) * lq) + (tid & 15) * 16);
-    pO.load((const E*)a.d_o + (int64_t)tok0 * a.Hv * D + (int64_t)h * D, (int64_t)a.Hv * D, len);
+    pO.load((const E*)a.d_o + (int64_t)tok0 * a.Hv * D + (int64_t)h * D + col0, (int64_t)a.Hv * D, len);
     g_r = Buf(a.gam + slot * C, C * 4).f1((tid & (C - 1)) * 4);  // every thread loads; threads < C use it
   };
   // P^T[c][s] = P[s][c]: this lane's column c = rt1 * 16 + r16, rows s = ks * 32 + kq + u
@@ -460,7 +465,7 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
     {  // gradient w.r.t. the state leaving this chunk
       float* dst = a.dHn + slot * D * D;
 #pragma unroll
-      for (int i = 0; i < kP2; ++i) store_tile<float>(dst, D, rt2 * 16, i * 16, dH[i], D);
+      for (int i = 0; i < P2; ++i) store_tile<float>(dst, D, rt2 * 16, col0 + i * 16, dH[i], D);
     }
     float dec[4];  // e^{gamma_last - gamma_s} of this lane's rows s, 0 past len
 #pragma unroll
@@ -469,7 +474,7 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
       dec[e] = r < len ? __expf(sm.gam[len - 1] - sm.gam[r]) : 0.f;
     }
 #pragma unroll
-    for (int i = 0; i < kP1; ++i) {
+    for (int i = 0; i < P1; ++i) {
       const int c = (cb + i) * 16 + r16;
       f32x4 p = zero4(), kd = zero4();
 #pragma unroll
@@ -488,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) kd[e] = dec[e] * kd[e] + a.scale * p[e];  // kd <- dW
-      store_tile_t(a.dWt + slot * D * C, C, rt1 * 16, (cb + i) * 16, kd);
+      store_tile_t(a.dWt + slot * D * C, C, rt1 * 16, col0 + (cb + i) * 16, kd);
       const int cc = (cb + i) * 16 + acc_col(), r = rt1 * 16 + acc_row(0);
       st4_split<E>(&sm.OW[cc][C + r], &sm.dWl[cc][r], kd);
       __builtin_amdgcn_sched_barrier(0);
@@ -512,7 +517,7 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
       split8(make_float4(v[0], v[1], v[2], v[3]), make_float4(v[4], v[5], v[6], v[7]), qth[ks], qtl[ks]);
     }
 #pragma unroll
-    for (int i = 0; i < kP2; ++i) {
+    for (int i = 0; i < P2; ++i) {
       const int c = i * 16 + r16;
       f32x4 y1 = zero4(), y2 = zero4();
 #pragma unroll
@@ -537,9 +542,9 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
   if (a.dh0) {
     float* dst = a.dh0 + ((int64_t)n * a.Hv + h) * D * D;
 #pragma unroll
-    for (int i = 0; i < kP2; ++i)
+    for (int i = 0; i < P2; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[(rt2 * 16 + acc_row(e)) * D + i * 16 + acc_col()] = dH[i][e];
+      for (int e = 0; e < 4; ++e) dst[(rt2 * 16 + acc_row(e)) * D + col0 + i * 16 + acc_col()] = dH[i][e];
   }
 }
 
@@ -785,8 +790,9 @@ void launch_state_fwd_cols(const ChunkArgs& a, hipStream_t st, int mode, bool f8
   else state_fwd_cols_kernel<kFwdBoth, false><<<grid, 256, 0, st>>>(a);
 }
 
-void launch_state_bwd_wide(const ChunkArgs& a, hipStream_t st) {
-  state_bwd_wide_kernel<<<dim3(state_grid(a.N, a.Hk, a.G, 1)), kThreads, 0, st>>>(a);
+void launch_state_bwd_wide(const ChunkArgs& a, hipStream_t st, bool half) {
+  if (half) state_bwd_wide_kernel<64><<<dim3(state_grid(a.N, a.Hk, a.G, 2)), kThreads, 0, st>>>(a);
+  else state_bwd_wide_kernel<128><<<dim3(state_grid(a.N, a.Hk, a.G, 1)), kThreads, 0, st>>>(a);
 }
 
 }  // namespace gdn

@@ -271,10 +271,10 @@ def test_chunk_every_accepted_shape(dtype, d, chunk):
 LONG_RANGE_CASES = [
     ("bf16", 128, 64, 2, 4, (700, 390, 1),
      {"chunk_state_fwd": "tiled16", "chunk_state_store": "tiled16", "chunk_state_save": "tiled16",
-      "chunk_state_bwd": "wide128"}),
+      "chunk_state_bwd": "wide64"}),
     ("bf16", 128, 64, 8, 16, (330, 400, 64, 333, 129),
      {"chunk_state_fwd": "wide64", "chunk_state_store": "wide64", "chunk_state_save": "wide64",
-      "chunk_state_bwd": "wide128"}),
+      "chunk_state_bwd": "wide64"}),
     ("bf16", 128, 64, 16, 32, (330, 321, 64, 400, 350, 390, 329, 1),
      {"chunk_state_fwd": "wide64", "chunk_state_store": "wide128", "chunk_state_save": "wide128",
       "chunk_state_bwd": "wide128"}),
