@@ -271,9 +271,14 @@ struct PrepSmem {
 };
 
 // (I + A)^-1 for strictly lower A [C][C] (fp32 in LDS) into Tm and Tt = Tm^T.
-// While wave 0 solves the diagonal blocks, the other waves run
+// While wave 0 solves the 16 x 16 diagonal blocks, the other waves write the
+// zero blocks above the diagonal (of Tm; below it of Tt) and then run
 // other(first, count) (thread tid - 64 of NTH - 64); it must not touch Am, Tm,
-// Tt, Xs nor wait at a barrier.
+// Tt, Xs nor wait at a barrier.  The blocks below the diagonal follow by
+// doubling: the 32 x 32 diagonal blocks from their 16 x 16 halves
+// (L^-1 = [[L11^-1, 0], [-L22^-1 L21 L11^-1, L22^-1]]), then the 64 x 64 from
+// its 32 x 32 halves, each product on fp32 MFMA (4 barriers in all at C = 64).
+// The caller's barrier before and this function's last barrier bracket it.
 struct NoWork {
   __device__ void operator()(int, int) const {}
 };
@@ -281,14 +286,17 @@ template <int C, int LDCF, int NTH = kChunkThreads, typename F = NoWork>
 __device__ __forceinline__ void unit_lower_inverse(const float (*Am)[LDCF], float (*Tm)[LDCF], float (*Tt)[LDCF],
                                                    float (*Xs)[16][20], F&& other = F{}) {
   static_assert(C <= kWave && NTH > kWave, "diagonal solve in wave 0");
+  constexpr int NB = C / 16;
+  static_assert(NB == 1 || NB == 2 || NB == 4, "chunks of 16, 32 or 64");
   const int tid = threadIdx.x, w = wave_id();
-  for (int e = tid; e < C * C; e += NTH) {
-    Tm[e / C][e % C] = 0.f;
-    Tt[e / C][e % C] = 0.f;
-  }
-  __syncthreads();
-  if (tid >= kWave) other(tid - kWave, NTH - kWave);
-  else if (tid < C) {  // diagonal 16x16 blocks, one column per lane
+  if (tid >= kWave) {
+    for (int e = tid - kWave; e < C * C; e += NTH - kWave) {
+      const int r = e / C, c = e % C;
+      if (r / 16 < c / 16) Tm[r][c] = 0.f;
+      if (r / 16 > c / 16) Tt[r][c] = 0.f;
+    }
+    other(tid - kWave, NTH - kWave);
+  } else if (tid < C) {  // diagonal 16x16 blocks, one column per lane
     const int o = (tid >> 4) * 16, c = tid & 15;
     float x[16];
 #pragma unroll
@@ -305,28 +313,43 @@ __device__ __forceinline__ void unit_lower_inverse(const float (*Am)[LDCF], floa
     }
   }
   __syncthreads();
-  constexpr int NB = C / 16;
+  // T_rc = -T_rr X for the tile X in Xs[slot] (stored transposed), into Tm and Tt
+  auto finish = [&](int br, int bc, f32x4 acc) {
 #pragma unroll
-  for (int i = 1; i < NB; ++i) {
-    // T_{i,jb} = -T_ii sum_{k=jb}^{i-1} A_{i,k} T_{k,jb}; wave jb handles one block
-    if (w < i) {
-      const int jb = w;
-      f32x4 acc = zero4();
-      for (int kb = jb; kb < i; ++kb)
-        acc = mm_tile<float, 16>(acc, &Am[i * 16][kb * 16], LDCF, &Tt[jb * 16][kb * 16], LDCF);
+    for (int e = 0; e < 4; ++e) {
+      const int r = br * 16 + acc_row(e), c = bc * 16 + acc_col();
+      Tm[r][c] = -acc[e];
+      Tt[c][r] = -acc[e];
+    }
+  };
+  auto park = [&](int slot, f32x4 acc) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Xs[w][acc_col()][acc_row(e)] = acc[e];
+    for (int e = 0; e < 4; ++e) Xs[slot][acc_col()][acc_row(e)] = acc[e];
+  };
+  if constexpr (NB >= 2) {  // blocks (1, 0) and (3, 2): one wave each, X through its own Xs slot
+    if (w < NB / 2) {
+      const int b = 2 * w;
+      park(w, mm_tile<float, 16>(zero4(), &Am[(b + 1) * 16][b * 16], LDCF, &Tt[b * 16][b * 16], LDCF));
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // the wave's own parked tile
+      finish(b + 1, b, mm_tile<float, 16>(zero4(), &Tm[(b + 1) * 16][(b + 1) * 16], LDCF, &Xs[w][0][0], 20));
     }
     __syncthreads();
-    if (w < i) {
-      const int jb = w;
-      f32x4 acc = mm_tile<float, 16>(zero4(), &Tm[i * 16][i * 16], LDCF, &Xs[w][0][0], 20);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = i * 16 + acc_row(e), c = jb * 16 + acc_col();
-        Tm[r][c] = -acc[e];
-        Tt[c][r] = -acc[e];
-      }
+  }
+  if constexpr (NB == 4) {  // rows 2..3, columns 0..1: -T[2:4][2:4] (A[2:4][0:2] T[0:2][0:2])
+    if (w < 4) {  // X_ab = sum_{k = b}^{1} A_{2+a, k} T_{k, b}
+      const int ra = w >> 1, cb = w & 1;
+      f32x4 acc = zero4();
+      for (int k = cb; k < 2; ++k)
+        acc = mm_tile<float, 16>(acc, &Am[(2 + ra) * 16][k * 16], LDCF, &Tt[cb * 16][k * 16], LDCF);
+      park(w, acc);
+    }
+    __syncthreads();
+    if (w < 4) {  // T_{2+a, b} = -sum_{m = 0}^{a} T_{2+a, 2+m} X_mb
+      const int ra = w >> 1, cb = w & 1;
+      f32x4 acc = zero4();
+      for (int m = 0; m <= ra; ++m)
+        acc = mm_tile<float, 16>(acc, &Tm[(2 + ra) * 16][(2 + m) * 16], LDCF, &Xs[2 * m + cb][0][0], 20);
+      finish(2 + ra, cb, acc);
     }
     __syncthreads();
   }

@@ -262,7 +262,7 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
           }
         }
       };
-      unit_lower_inverse<C, S::LDCF, NTH>(sm.Am, sm.Tm, sm.Tt, sm.Xs, gate_outputs);  // starts and ends with a barrier
+      unit_lower_inverse<C, S::LDCF, NTH>(sm.Am, sm.Tm, sm.Tt, sm.Xs, gate_outputs);  // ends with a barrier
       if constexpr (LO_OUT) {  // T for the WY gradients
         for (int e = tid; e < C * (C / 4); e += NTH) {
           const int r = e / (C / 4), c = (e % (C / 4)) * 4;
