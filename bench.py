@@ -366,6 +366,14 @@ def main():
     n_chunks = len(oracle.chunk_table(inp["cu"], cfg.chunk)[0])
     kb = kernel_bytes(cfg, n_chunks, cfg.h0)
     kf = kernel_flops(cfg, n_chunks)
+    if args.max_tokens:
+        # the chunk kernels launch once per token segment: each launch covers that
+        # segment's share of the row (equal shares at the training workload)
+        nseg = len(gdn.token_segments([int(c) for c in inp["cu"]], cfg.chunk, args.max_tokens))
+        for d in (kb, kf):
+            for key in list(d):
+                if key.startswith("chunk_") and key != "chunk_index":
+                    d[key] = d[key] / nseg
     kernels = {}
     base = lambda name: name.split(":", 1)[0]   # state-pass records carry their variant after a colon
     for name, (cnt, tot) in rep.items():
