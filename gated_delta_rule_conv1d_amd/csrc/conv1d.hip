@@ -19,10 +19,11 @@
 
 namespace gdn {
 
-constexpr int kConvTB = 64;       // tokens per wave, forward
+constexpr int kConvTB = 64;       // tokens per wave, forward (at most; fewer on short rows)
 constexpr int kConvTBB = 128;     // tokens per wave, backward (its W-1 look-ahead
                                   // tokens and dw partials amortise over more)
 constexpr int kConvWaves = 4;     // waves (token blocks) per workgroup
+constexpr int kConvCUs = 256;     // MI355X compute units
 
 __device__ __forceinline__ int find_seq(const int32_t* cu, int N, int t) {
   // largest n with cu[n] <= t (so cu[n] <= t < cu[n+1] when t < T)
@@ -37,15 +38,15 @@ __device__ __forceinline__ int find_seq(const int32_t* cu, int N, int t) {
 template <typename E, int D, int W>
 __global__ __launch_bounds__(256) void conv_fwd_kernel(const E* __restrict__ x, const E* __restrict__ w,
                                                        const int32_t* __restrict__ cu, const E* __restrict__ win,
-                                                       int N, int T, int Cch, int n_qk, float eps,
+                                                       int N, int T, int Cch, int n_qk, float eps, int tpw,
                                                        E* __restrict__ y) {
   constexpr int V = Vec<E>::N;      // channels per lane
   constexpr int LPH = D / V;        // lanes per L2 group
   const int lane = lane_id();
   const int tb = blockIdx.x * kConvWaves + wave_id();
-  const int t0 = tb * kConvTB;
+  const int t0 = tb * tpw;          // tpw tokens per wave
   if (t0 >= T) return;
-  const int t1 = min(t0 + kConvTB, T);
+  const int t1 = min(t0 + tpw, T);
   const int ch = (blockIdx.y * kWave + lane) * V;
   const bool active = ch < Cch;
   const bool is_qk = ch < n_qk;
@@ -340,10 +341,17 @@ static void launch_conv_fwd(const gdn_shape* s, const void* x, const void* w, co
                             float eps, void* y, hipStream_t st) {
   constexpr int V = Vec<E>::N;
   const int Cch = 2 * s->h_qk * s->d_k + s->h_v * s->d_v;
-  dim3 grid(conv_grid_x(s->total_tokens, kConvTB), (Cch + kWave * V - 1) / (kWave * V));
+  // tokens per wave: 64, or fewer where that would leave under 16 waves per CU
+  // (each wave keeps one width of tokens in flight, so short rows need more
+  // waves to cover the memory latency; each extra wave re-reads W - 1 tokens of
+  // history)
+  const int cgroups = (Cch + kWave * V - 1) / (kWave * V);
+  int tpw = kConvTB;
+  while (tpw > 16 && (int64_t)((s->total_tokens + tpw - 1) / tpw) * cgroups < 16 * kConvCUs) tpw /= 2;
+  dim3 grid(conv_grid_x(s->total_tokens, tpw), cgroups);
   GDN_PROF("conv_fwd", st);
   conv_fwd_kernel<E, D, W><<<grid, 256, 0, st>>>((const E*)x, (const E*)w, cu, (const E*)win, s->n_seqs,
-                                                 s->total_tokens, Cch, 2 * s->h_qk * s->d_k, eps, (E*)y);
+                                                 s->total_tokens, Cch, 2 * s->h_qk * s->d_k, eps, tpw, (E*)y);
 }
 
 template <typename E, int D, int W>
