@@ -624,4 +624,26 @@ void launch_state_bwd_wide(const ChunkArgs& a, hipStream_t st, bool half);
 template <typename E, int D, int C>
 constexpr bool use_wide_state() { return sizeof(E) == 2 && D == 128 && C == 64; }
 
+// Workspace layouts of the preparation's outputs at those shapes, in the order
+// the state passes load them, so that every load instruction of a wave reads
+// 1 KB of consecutive bytes (a row-major tile read as matrix-core fragments
+// touches 16 rows per instruction, which the load path serves at about half
+// the rate).
+// A-operand order of a [M][K] bf16 tile: fragment (row tile, k step of 32),
+// lane 16 g + r holds row r, k = 8 g .. 8 g + 7 (Wk [C][D], K^T [D][C]).
+__device__ __forceinline__ int af_off(int row, int k, int K) {
+  return ((((row >> 4) * (K >> 5) + (k >> 5)) * 64 + ((k >> 3) & 3) * 16 + (row & 15)) << 3) + (k & 7);
+}
+// Accumulator order of a [M][N] fp32 tile: tile (row tile, column tile), lane
+// 16 g + c holds rows 4 g .. 4 g + 3 of column c (U [C][D]).
+__device__ __forceinline__ int acc_off(int row, int col, int N) {
+  return ((((row >> 4) * (N >> 4) + (col >> 4)) * 64 + ((row >> 2) & 3) * 16 + (col & 15)) << 2) + (row & 3);
+}
+// A-operand order of a [M][K] fp32 tile, each lane's 8 values as two 4-value
+// halves stored half by half (P [C][C] of the inference forward).
+__device__ __forceinline__ int pf_off(int row, int k, int K) {
+  return (((((row >> 4) * (K >> 5) + (k >> 5)) * 2 + ((k >> 2) & 1)) * 64 + ((k >> 3) & 3) * 16 + (row & 15)) << 2) +
+         (k & 3);
+}
+
 }  // namespace gdn

@@ -81,6 +81,9 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
   __shared__ S sm;
   constexpr int V = Vec<E>::N;
   constexpr int NT = C / 16, ND = D / 16;
+  // Wk, K^T, U (and P of the inference forward) in the state passes' load
+  // order at the shapes those passes serve
+  constexpr bool FRAG = use_wide_state<E, D, C>();
   const int tid = threadIdx.x, w = wave_id(), lane = lane_id();
   // Persistent: the workgroup walks items (chunk, k-head) = (it / Hk, it % Hk)
   // from blockIdx.x in steps of gridDim.x, and requests the next item's q, k
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
               av[e] = (s < r) ? sm.beta[r] * dd * sm.Sk[r][s] : 0.f;
             }
             *reinterpret_cast<float4*>(&sm.Am[r][s0]) = make_float4(av[0], av[1], av[2], av[3]);
-            st4<float>(Pg + (int64_t)r * C + s0, pv);
+            st4<float>(Pg + (FRAG ? pf_off(r, s0, C) : r * C + s0), pv);
           }
         }
       }
@@ -212,7 +215,7 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
               val[i] = (s < len) ? to_f<E>(sm.Kt[d][s]) * es : 0.f;
               lo[i] = val[i] - to_f<E>(from_f<E>(val[i]));
             }
-            Vec<E>::store(Kg + d * C + s0, val);
+            Vec<E>::store(Kg + (FRAG ? af_off(d, s0, C) : d * C + s0), val);
             if constexpr (Split<E>::on)
               if (!plain) Vec<E>::store((E*)a.Ktl + slot * D * C + d * C + s0, lo);
           }
@@ -276,7 +279,16 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
         split_store<E>(&sm.TB[r][s], &sm.TBl[0][0] + r * S::LDCE + s, sm.Tm[r][s] * sm.beta[s]);
       }
       __syncthreads();
-      {
+      if constexpr (FRAG) {  // U tiles, each lane's 4 values one 16-byte write in accumulator order
+        float* Ug = a.U + slot * C * D;
+        for (int t = w; t < NT * ND; t += NW) {
+          const int rt = t / ND, dt = t % ND;
+          f32x4 acc = mm_tile<E, C>(zero4(), &sm.TB[rt * 16][0], S::LDCE, &sm.Vt[dt * 16][0], S::LDCE);
+          if constexpr (Split<E>::on)
+            acc = mm_tile<E, C>(acc, &sm.TBl[rt * 16][0], S::LDCE, &sm.Vt[dt * 16][0], S::LDCE);
+          st4<float>(Ug + (t * 64 + lane) * 4, acc);
+        }
+      } else {
         // formed as U^T = V^T (T diag(beta))^T tiles: a lane then holds 4
         // consecutive d of one row of U, stored as one 16-byte write
         float* Ug = a.U + slot * C * D;
@@ -303,7 +315,12 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
             f32x4 acc = mm_tile<E, C>(zero4(), &sm.TB[rt * 16][0], S::LDCE, &sm.Kt[ct * 16][0], S::LDCE);
             if constexpr (Split<E>::on)
               acc = mm_tile<E, C>(acc, &sm.TBl[rt * 16][0], S::LDCE, &sm.Kt[ct * 16][0], S::LDCE);
-            store_tile<E>(Wg, D, rt * 16, ct * 16, acc, C);
+            if constexpr (FRAG) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) Wg[af_off(rt * 16 + acc_row(e), ct * 16 + acc_col(), D)] = from_f<E>(acc[e]);
+            } else {
+              store_tile<E>(Wg, D, rt * 16, ct * 16, acc, C);
+            }
             const int64_t o = slot * D * C + (int64_t)(ct * 16 + acc_col()) * C + rt * 16 + acc_row(0);
             st4_split<E>((E*)a.Wth + o, (E*)a.Wtl + o, acc);
           } else {  // Wk^T = K^T (T diag(beta Gam))^T tiles: 4 consecutive d of a Wk row per lane
@@ -311,7 +328,8 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
             f32x4 acc = mm_tile<E, C>(zero4(), &sm.Kt[dt * 16][0], S::LDCE, &sm.TB[rt * 16][0], S::LDCE);
             if constexpr (Split<E>::on)
               acc = mm_tile<E, C>(acc, &sm.Kt[dt * 16][0], S::LDCE, &sm.TBl[rt * 16][0], S::LDCE);
-            st4<E>(Wg + (int64_t)(rt * 16 + acc_col()) * D + dt * 16 + acc_row(0), acc);
+            const int r = rt * 16 + acc_col(), d0 = dt * 16 + acc_row(0);
+            st4<E>(Wg + (FRAG ? af_off(r, d0, D) : r * D + d0), acc);
           }
         }
       }

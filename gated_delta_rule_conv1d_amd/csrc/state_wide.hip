@@ -91,6 +91,13 @@ struct Buf {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
   }
   __device__ __forceinline__ M::frag fr(int off) const { return __builtin_bit_cast(M::frag, u4(off)); }
+  // stores: an offset at or past the end drops the store
+  __device__ __forceinline__ void st_f32(int off, float v) const {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+  }
+  __device__ __forceinline__ void st_b16(int off, bf16 v) const {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, v), r, off, 0, 0);
+  }
   // 8 e4m3 bytes at byte offset off, decoded exactly to a bf16 fragment
   __device__ __forceinline__ M::frag fr_f8(int off, float scale) const {
     const uint2 raw = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
@@ -150,12 +157,12 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
     kt_h1 = kh.u4((tid + kThreads) * 16);
     g_r = Buf(a.gam + slot * C, C * 4).f1((tid & (C - 1)) * 4);  // every thread loads; threads < C use it
   };
-  const int a_off = ((rt1 * 16 + r16) * D + kq) * 2;   // lane's A-fragment offset in a [C][D] bf16 tile
+  const int a_off = (rt1 * 4 * 64 + lane) * 16;   // lane's piece of Wk's fragment (rt1, 0), fragment order
   auto load_p1 = [&](int ci, int tok0, int len) {
     const int64_t slot = (int64_t)ci * a.Hv + h;
     const Buf wk((const E*)a.Wk + slot * C * D, C * D * 2);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) wkf[ks] = wk.fr(a_off + ks * 64);
+    for (int ks = 0; ks < 4; ++ks) wkf[ks] = wk.fr(a_off + ks * 1024);
     if constexpr (OUT && F8) {  // e4m3 q rows, decoded exactly on load
       const Buf qb((const uint8_t*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D, (int64_t)len * a.sqk);
       const int q_off = (int)((int64_t)(rt1 * 16 + r16) * a.sqk + kq);
@@ -167,20 +174,25 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) qf[ks] = qb.fr(q_off + ks * 64);
     }
-    const Buf ub(a.U + slot * C * D, C * D * 4);
+    const Buf ub(a.U + slot * C * D, C * D * 4);  // accumulator order
 #pragma unroll
-    for (int i = 0; i < P1; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        uf[i][e] = ub.f1(((rt1 * 16 + acc_row(e)) * D + col0 + (cb + i) * 16 + acc_col()) * 4);
+    for (int i = 0; i < P1; ++i) {
+      const float4 u = ub.f4(((rt1 * (D / 16) + col0 / 16 + cb + i) * 64 + lane) * 16);
+      uf[i] = f32x4{u.x, u.y, u.z, u.w};
+    }
   };
   auto load_p2 = [&](int ci) {
     const Buf pb(a.P + ((int64_t)ci * a.Hv + h) * C * C, C * C * 4);
-    const int p_off = ((rt1 * 16 + r16) * C + kq) * 4;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      pf[ks][0] = pb.f4(p_off + ks * 128);
-      pf[ks][1] = pb.f4(p_off + ks * 128 + 16);
+      if constexpr (MODE == kFwdOut) {  // fragment order (inference preparation)
+        pf[ks][0] = pb.f4((((rt1 * 2 + ks) * 2) * 64 + lane) * 16);
+        pf[ks][1] = pb.f4((((rt1 * 2 + ks) * 2 + 1) * 64 + lane) * 16);
+      } else {
+        const int p_off = ((rt1 * 16 + r16) * C + kq) * 4;
+        pf[ks][0] = pb.f4(p_off + ks * 128);
+        pf[ks][1] = pb.f4(p_off + ks * 128 + 16);
+      }
     }
   };
 
@@ -204,10 +216,13 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
     const int tok0 = ent.y, len = ent.z;
     const int64_t slot = (int64_t)ci * a.Hv + h;
     __syncthreads();  // the previous chunk is done with K^T and W^T, and H^T is written
-    {  // 16-byte piece e: row e / 8, columns (e % 8) * 8 ..
-      const int e0 = tid, e1 = tid + kThreads;
-      *reinterpret_cast<uint4*>(&sm.Kt[e0 >> 3][(e0 & 7) * 8]) = kt_h0;
-      *reinterpret_cast<uint4*>(&sm.Kt[e1 >> 3][(e1 & 7) * 8]) = kt_h1;
+    {  // 16-byte piece e of K^T in fragment order: fragment e / 64 (row tile, k step), lane e % 64
+      auto put = [&](int e, uint4 v) {
+        const int f = e >> 6, l = e & 63;
+        *reinterpret_cast<uint4*>(&sm.Kt[(f >> 1) * 16 + (l & 15)][(f & 1) * 32 + (l >> 4) * 8]) = v;
+      };
+      put(tid, kt_h0);
+      put(tid + kThreads, kt_h1);
     }
     if (tid < C) sm.gam[tid] = g_r;
     __syncthreads();
@@ -568,87 +583,48 @@ struct ColsSmem {
   E Wtl[16][kLDC];
   E Ws[16][kLDC];   // (diag(e) W)^T for the state update (OUT)
   E Wsl[16][kLDC];
-  float gam[kC];
+  // per chunk, double-buffered (written one chunk ahead by wave 0):
+  float eg[2][kC];  // e^{gamma_r}
+  float es[2][kC];  // e^{gamma_last - gamma_r}, 0 past the chunk's length
+  float gl[2];      // e^{gamma_last}
+};
+
+// one wave's operands of one chunk
+struct ColsOps {
+  M::frag af[4];    // rows of Wk (waves 0-3) or q (waves 4-7), row tile w & 3
+  f32x4 uf;         // U on the accumulator tile (waves 0-3)
+  float4 pf[2][2];  // P rows (waves 4-7)
+  M::frag ktf[2];   // K^T rows of state tile w
+  float g;          // gamma of row `lane`
 };
 
 template <int MODE, bool F8>
-__global__ __launch_bounds__(256) void state_fwd_cols_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(512) void state_fwd_cols_kernel(ChunkArgs a) {
   constexpr bool OUT = MODE & kFwdOut, STORE = MODE & kFwdStore;
-  constexpr int D = kD, C = kC, NT = 256;
+  constexpr int D = kD, C = kC;
+  constexpr int kOff = 0x40000000;  // a buffer offset past every buffer's end: the store is dropped
   __shared__ ColsSmem sm;
   int n, h, vt;
   if (!state_block(blockIdx.x, a.N, a.Hk, a.G, kD / 16, n, h, vt)) return;
   const int j = h / a.G;
   const int col0 = vt * 16;
-  const int tid = threadIdx.x, w = wave_id(), lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(wave_id()), lane = lane_id();
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
-  const int rt1 = w;                    // W / O tile: row tile w
-  const int rtA = w, rtB = w + 4;       // state tiles: row tiles w and w + 4
+  // waves 0-3 form W = U - Wk H on row tile w; waves 4-7 form
+  // diag(Gam) Q H + P W on row tile w - 4; wave w carries state row tile w
+  const bool xw = w < 4;
+  const int rt1 = w & 3;
+  const int rs = w;
 
-  f32x4 Hr[2];
+  f32x4 Hr = zero4();
+  if (a.h0) {
+    const float* src = a.h0 + ((int64_t)n * a.Hv + h) * D * D;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int rt = i ? rtB : rtA;
-    Hr[i] = zero4();
-    if (a.h0) {
-      const float* src = a.h0 + ((int64_t)n * a.Hv + h) * D * D;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Hr[i][e] = src[(rt * 16 + acc_row(e)) * D + col0 + acc_col()];
-    }
+    for (int e = 0; e < 4; ++e) Hr[e] = src[(rs * 16 + acc_row(e)) * D + col0 + acc_col()];
   }
   auto write_Ht = [&]() {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = acc_col(), r = (i ? rtB : rtA) * 16 + acc_row(0);
-      st4_split<E>(&sm.Ht[c][r], &sm.Htl[c][r], Hr[i]);
-    }
-  };
-
-  // this wave's operands of the next chunk
-  float g_r = 0.f;
-  M::frag wkf[4], qf[4], ktf[2][2];
-  f32x4 uf;
-  float4 pf[2][2];
-  const int a_off = ((rt1 * 16 + r16) * D + kq) * 2;   // lane's A-fragment offset in a [C][D] bf16 tile
-  auto load_g = [&](int ci) {
-    g_r = Buf(a.gam + ((int64_t)ci * a.Hv + h) * C, C * 4).f1((tid & (C - 1)) * 4);
-  };
-  auto load_p1 = [&](int ci, int tok0, int len) {
-    const int64_t slot = (int64_t)ci * a.Hv + h;
-    const Buf wk((const E*)a.Wk + slot * C * D, C * D * 2);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) wkf[ks] = wk.fr(a_off + ks * 64);
-    if constexpr (OUT && F8) {  // e4m3 q rows, decoded exactly on load
-      const Buf qb((const uint8_t*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D, (int64_t)len * a.sqk);
-      const int q_off = (int)((int64_t)(rt1 * 16 + r16) * a.sqk + kq);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qf[ks] = qb.fr_f8(q_off + ks * 32, a.f8_scale[0]);
-    } else if constexpr (OUT) {  // rows past len fall outside the buffer and read zero
-      const Buf qb((const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D, (int64_t)len * a.sqk * 2);
-      const int q_off = (int)(((int64_t)(rt1 * 16 + r16) * a.sqk + kq) * 2);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qf[ks] = qb.fr(q_off + ks * 64);
-    }
-    const Buf ub(a.U + slot * C * D, C * D * 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) uf[e] = ub.f1(((rt1 * 16 + acc_row(e)) * D + col0 + acc_col()) * 4);
-  };
-  auto load_p2 = [&](int ci) {
-    const int64_t slot = (int64_t)ci * a.Hv + h;
-    const Buf kb((const E*)a.Kt + slot * D * C, D * C * 2);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) ktf[i][ks] = kb.fr((((i ? rtB : rtA) * 16 + r16) * C + kq + ks * 32) * 2);
-    if constexpr (OUT) {
-      const Buf pb(a.P + slot * C * C, C * C * 4);
-      const int p_off = ((rt1 * 16 + r16) * C + kq) * 4;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        pf[ks][0] = pb.f4(p_off + ks * 128);
-        pf[ks][1] = pb.f4(p_off + ks * 128 + 16);
-      }
-    }
+    const int c = acc_col(), r = rs * 16 + acc_row(0);
+    st4_split<E>(&sm.Ht[c][r], &sm.Htl[c][r], Hr);
   };
 
   // the sequence's chunks are consecutive table entries: (first token, length)
@@ -657,114 +633,162 @@ __global__ __launch_bounds__(256) void state_fwd_cols_kernel(ChunkArgs a) {
   const int s0 = a.cu[n], s1 = a.cu[n + 1];
   auto entry = [&](int ci) {
     const int t = s0 + (ci - c0) * C;
-    return make_int4(n, t, min(C, s1 - t), 0);
+    return make_int2(t, min(C, s1 - t));
   };
-  int4 ent = make_int4(0, 0, 0, 0);
-  if (c0 < c1) {
-    ent = entry(c0);
-    load_g(c0);
-    load_p1(c0, ent.y, ent.z);
-    load_p2(c0);
-  }
-  write_Ht();
-  for (int ci = c0; ci < c1; ++ci) {
-    const int tok0 = ent.y, len = ent.z;
+
+  // Every wave issues the same number of vector-memory instructions, in the
+  // same order, on every path (loads of the last chunk repeat it; rows past a
+  // chunk's end and the other role's stores go to an offset past the buffer's
+  // end, which the hardware drops), so the compiler's wait counts are exact
+  // and the next chunk's loads stay in flight through the current one.
+  const int a_off = (rt1 * 4 * 64 + lane) * 16;   // lane's piece of Wk's fragment (rt1, 0), fragment order
+  auto load = [&](ColsOps& op, int ci) {
     const int64_t slot = (int64_t)ci * a.Hv + h;
-    __syncthreads();  // the previous chunk is done with W^T, and H^T is written
-    if (tid < C) sm.gam[tid] = g_r;
-    __syncthreads();
-    const bool more = ci + 1 < c1;
-    int4 nent = ent;
-    if (more) {
-      nent = entry(ci + 1);
-      load_g(ci + 1);
-    }
-    // Stores go after the prefetch loads: the wait for a load also waits for
-    // every earlier vector-memory access of the wave.
-    if constexpr (STORE) {  // state entering this chunk, for the backward pass
-      float* Hg = a.Hc + slot * D * D;
+    const int2 en = entry(ci);
+    op.g = Buf(a.gam + slot * C, C * 4).f1(lane * 4);
+    const int64_t q0 = (int64_t)en.x * a.sqk + (int64_t)j * D;   // q rows past the chunk's length read zero
+    const int q_row = (rt1 * 16 + r16) * (int)a.sqk + kq;        // element offset of the lane's q piece
+    if constexpr (F8) {  // e4m3 q rows, decoded exactly on load; waves 0-3 keep the Wk fragments
+      const Buf wk((const E*)a.Wk + slot * C * D, C * D * 2);
+      const Buf qb((const uint8_t*)a.q + q0, (int64_t)en.y * a.sqk);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) store_tile<float>(Hg, D, (i ? rtB : rtA) * 16, col0, Hr[i], D);
+      for (int ks = 0; ks < 4; ++ks) {
+        const M::frag fw = wk.fr(xw ? a_off + ks * 1024 : kOff);
+        const M::frag fq = qb.fr_f8(xw ? kOff : q_row + ks * 32, a.f8_scale[0]);
+        op.af[ks] = xw ? fw : fq;
+      }
+    } else {
+      const Buf ab(xw ? (const void*)((const E*)a.Wk + slot * C * D) : (const void*)((const E*)a.q + q0),
+                   xw ? (int64_t)C * D * 2 : (OUT ? (int64_t)en.y * a.sqk * 2 : 0));
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) op.af[ks] = ab.fr(xw ? a_off + ks * 1024 : q_row * 2 + ks * 64);
+    }
+    const Buf ub(a.U + slot * C * D, C * D * 4);  // accumulator order
+    const float4 u = ub.f4(xw ? ((rt1 * (D / 16) + vt) * 64 + lane) * 16 : kOff);
+    op.uf = f32x4{u.x, u.y, u.z, u.w};
+    const Buf pb(a.P + slot * C * C, OUT ? C * C * 4 : 0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if constexpr (MODE == kFwdOut) {  // fragment order (inference preparation)
+        op.pf[ks][0] = pb.f4(xw ? kOff : (((rt1 * 2 + ks) * 2) * 64 + lane) * 16);
+        op.pf[ks][1] = pb.f4(xw ? kOff : (((rt1 * 2 + ks) * 2 + 1) * 64 + lane) * 16);
+      } else {
+        const int p_off = xw ? kOff : ((rt1 * 16 + r16) * C + kq) * 4 + ks * 128;
+        op.pf[ks][0] = pb.f4(p_off);
+        op.pf[ks][1] = pb.f4(p_off + 16);
+      }
+    }
+    const Buf kb((const E*)a.Kt + slot * D * C, D * C * 2);  // fragment order
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) op.ktf[ks] = kb.fr(((rs * 2 + ks) * 64 + lane) * 16);
+  };
+  auto put_g = [&](const ColsOps& op, int b, int len) {  // wave 0: a chunk's decay factors into buffer b
+    const float g_last = __shfl(op.g, len - 1, kWave);
+    sm.eg[b][lane] = __expf(op.g);
+    sm.es[b][lane] = lane < len ? __expf(g_last - op.g) : 0.f;
+    if (lane == 0) sm.gl[b] = __expf(g_last);
+  };
+
+  auto step = [&](int ci, const ColsOps& cur, ColsOps& nxt) {
+    const int2 en = entry(ci);
+    const int tok0 = en.x, len = en.y;
+    const int b = (ci - c0) & 1;
+    const int64_t slot = (int64_t)ci * a.Hv + h;
+    const int cn = ci + 1 < c1 ? ci + 1 : ci;
+    __syncthreads();  // H^T and this chunk's decay factors are written, and W^T is free
+    load(nxt, cn);
+    if constexpr (STORE) {  // state entering this chunk, for the backward pass
+      const Buf hb(a.Hc + slot * D * D, D * D * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        hb.st_f32(((rs * 16 + acc_row(e)) * D + col0 + acc_col()) * 4, Hr[e]);
     }
 
-    // phase 1: W = U - Wk H and diag(Gam) Q H on this wave's row tile
-    f32x4 x = zero4(), o = zero4();
+    // phase 1: W = U - Wk H (waves 0-3) or diag(Gam) Q H (waves 4-7) on row tile rt1
+    f32x4 x = zero4();
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const M::frag bh = fr(&sm.Ht[r16][ks * 32 + kq]);
       const M::frag bl = fr(&sm.Htl[r16][ks * 32 + kq]);
-      x = M::mma(wkf[ks], bh, x);
-      x = M::mma(wkf[ks], bl, x);
-      if constexpr (OUT) {
-        o = M::mma(qf[ks], bh, o);
-        o = M::mma(qf[ks], bl, o);
-      }
+      x = M::mma(cur.af[ks], bh, x);
+      x = M::mma(cur.af[ks], bl, x);
     }
+    if (xw) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = uf[e] - x[e];  // x <- W
-    if constexpr (OUT) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] *= __expf(sm.gam[rt1 * 16 + acc_row(e)]);
-    }
-    if (more) load_p1(ci + 1, nent.y, nent.z);  // Wk, q, U of the next chunk
-    {
+      for (int e = 0; e < 4; ++e) x[e] = cur.uf[e] - x[e];  // x <- W
       const int c = acc_col(), r = rt1 * 16 + acc_row(0);
       f32x4 xs;  // rows of W times e^{gamma_last - gamma_r}, 0 past len
 #pragma unroll
-      for (int e = 0; e < 4; ++e) xs[e] = (r + e < len) ? x[e] * __expf(sm.gam[len - 1] - sm.gam[r + e]) : 0.f;
+      for (int e = 0; e < 4; ++e) xs[e] = x[e] * sm.es[b][r + e];
       if constexpr (OUT) {
         st4_split<E>(&sm.Wt[c][r], &sm.Wtl[c][r], x);
         st4_split<E>(&sm.Ws[c][r], &sm.Wsl[c][r], xs);
       } else {
         st4_split<E>(&sm.Wt[c][r], &sm.Wtl[c][r], xs);
       }
-      if constexpr (STORE) store_tile<float>(a.W + slot * C * D, D, rt1 * 16, col0, x, C);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] *= sm.eg[b][rt1 * 16 + acc_row(e)];
     }
     __syncthreads();
 
     // phase 2: H <- Gam_last H + K^T diag(e) W;  o = scale (diag(Gam) Q H + P W)
-    const float gl = __expf(sm.gam[len - 1]);
+    const float gl = sm.gl[b];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int e = 0; e < 4; ++e) Hr[e] *= gl;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Hr[i][e] *= gl;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const M::frag bh = fr(OUT ? &sm.Ws[r16][ks * 32 + kq] : &sm.Wt[r16][ks * 32 + kq]);
-        const M::frag bl = fr(OUT ? &sm.Wsl[r16][ks * 32 + kq] : &sm.Wtl[r16][ks * 32 + kq]);
-        Hr[i] = M::mma(ktf[i][ks], bh, Hr[i]);
-        Hr[i] = M::mma(ktf[i][ks], bl, Hr[i]);
-      }
+    for (int ks = 0; ks < 2; ++ks) {
+      const M::frag bh = fr(OUT ? &sm.Ws[r16][ks * 32 + kq] : &sm.Wt[r16][ks * 32 + kq]);
+      const M::frag bl = fr(OUT ? &sm.Wsl[r16][ks * 32 + kq] : &sm.Wtl[r16][ks * 32 + kq]);
+      Hr = M::mma(cur.ktf[ks], bh, Hr);
+      Hr = M::mma(cur.ktf[ks], bl, Hr);
     }
-    if constexpr (OUT) {
+    if (OUT && !xw) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         M::frag ph, pl;
-        split8(pf[ks][0], pf[ks][1], ph, pl);
+        split8(cur.pf[ks][0], cur.pf[ks][1], ph, pl);
         const M::frag bh = fr(&sm.Wt[r16][ks * 32 + kq]);
         const M::frag bl = fr(&sm.Wtl[r16][ks * 32 + kq]);
-        o = M::mma(ph, bh, o);
-        o = M::mma(ph, bl, o);
-        o = M::mma(pl, bh, o);
+        x = M::mma(ph, bh, x);
+        x = M::mma(ph, bl, x);
+        x = M::mma(pl, bh, x);
       }
     }
-    if (more) load_p2(ci + 1);  // K^T and P of the next chunk
-    if constexpr (OUT) {
-      E* og = (E*)a.o + (int64_t)tok0 * a.Hv * D + (int64_t)h * D;
+    // tile stores, issued by every wave: W (waves 0-3, STORE) and o (waves 4-7,
+    // OUT); the other role's, and rows past the chunk's end, go past the buffer
+    {
+      const Buf wb(a.W + slot * C * D, STORE ? C * D * 4 : 0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] *= a.scale;
-      store_tile<E>(og, (int64_t)a.Hv * D, rt1 * 16, col0, o, len);
+      for (int e = 0; e < 4; ++e)
+        wb.st_f32(xw ? ((rt1 * 16 + acc_row(e)) * D + col0 + acc_col()) * 4 : kOff, x[e]);
+      const int ld = a.Hv * D;
+      const Buf ob((E*)a.o + (int64_t)tok0 * ld + (int64_t)h * D, OUT ? ((int64_t)(len - 1) * ld + D) * 2 : 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = rt1 * 16 + acc_row(e);
+        ob.st_b16(!xw && r < len ? (r * ld + col0 + acc_col()) * 2 : kOff, f2bf(x[e] * a.scale));
+      }
     }
     write_Ht();  // phase 1 (the only reader of H^T) is over for every wave
-    ent = nent;
+    if (w == 0 && ci + 1 < c1) put_g(nxt, b ^ 1, entry(ci + 1).y);  // read after the next barrier
+  };
+
+  ColsOps A, B;
+  if (c0 < c1) {
+    load(A, c0);
+    if (w == 0) put_g(A, 0, entry(c0).y);
+  }
+  write_Ht();
+  for (int ci = c0; ci < c1; ci += 2) {
+    step(ci, A, B);
+    if (ci + 1 >= c1) break;
+    step(ci + 1, B, A);
   }
   if (a.ht) {
     float* dst = a.ht + ((int64_t)n * a.Hv + h) * D * D;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        dst[((i ? rtB : rtA) * 16 + acc_row(e)) * D + col0 + acc_col()] = Hr[i][e];
+    for (int e = 0; e < 4; ++e) dst[(rs * 16 + acc_row(e)) * D + col0 + acc_col()] = Hr[e];
   }
 }
 
@@ -784,10 +808,10 @@ void launch_state_fwd_wide(const ChunkArgs& a, hipStream_t st, int mode, bool ha
 
 void launch_state_fwd_cols(const ChunkArgs& a, hipStream_t st, int mode, bool f8) {
   const dim3 grid(state_grid(a.N, a.Hk, a.G, kD / 16));
-  if (f8) state_fwd_cols_kernel<kFwdOut, true><<<grid, 256, 0, st>>>(a);  // fp8 inputs: inference only
-  else if (mode == kFwdOut) state_fwd_cols_kernel<kFwdOut, false><<<grid, 256, 0, st>>>(a);
-  else if (mode == kFwdStore) state_fwd_cols_kernel<kFwdStore, false><<<grid, 256, 0, st>>>(a);
-  else state_fwd_cols_kernel<kFwdBoth, false><<<grid, 256, 0, st>>>(a);
+  if (f8) state_fwd_cols_kernel<kFwdOut, true><<<grid, 512, 0, st>>>(a);  // fp8 inputs: inference only
+  else if (mode == kFwdOut) state_fwd_cols_kernel<kFwdOut, false><<<grid, 512, 0, st>>>(a);
+  else if (mode == kFwdStore) state_fwd_cols_kernel<kFwdStore, false><<<grid, 512, 0, st>>>(a);
+  else state_fwd_cols_kernel<kFwdBoth, false><<<grid, 512, 0, st>>>(a);
 }
 
 void launch_state_bwd_wide(const ChunkArgs& a, hipStream_t st, bool half) {
