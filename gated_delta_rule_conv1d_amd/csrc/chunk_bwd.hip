@@ -846,7 +846,7 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsPlan {
-  size_t table, seq0, Wk, U, P, Kt, Ktl, gam, end_fwd;
+  size_t table, seq0, Wk, U, P, Kt, Ktl, gam, Qf, end_fwd;
   size_t Ptr, Tw, Krh, Krl, Wth, Wtl, Qth, Qtl, Hc, W, dHn, dW, dWt, dT, dWkt, dQs, dKh, dP, hdot, gpart, end_bwd;
 };
 
@@ -865,7 +865,10 @@ static WsPlan plan(const gdn_shape* s) {
   const bool plain_k = es == 2 && D == 128 && C == 64;
   p.Ktl = o; o = align256(o + (es == 2 && !plain_k ? M * Hv * D * C * es : 0));
   p.gam = o; o = align256(o + M * Hv * C * 4);
-  p.end_fwd = o;
+  // q rows in fragment order, written and read by the inference forward only:
+  // the backward's own buffers start at the same offset
+  p.Qf = o;
+  p.end_fwd = align256(o + (plain_k ? M * (size_t)s->h_qk * C * D * es : 0));
   // the whole-state reverse pass (plain_k) forms P^T, the K rows and (Gam q)^T
   // from P, k and q, and writes dW^T only
   const size_t tr = plain_k ? 0 : 1;
@@ -906,6 +909,7 @@ static void fill_ws(ChunkArgs& a, const gdn_shape* s, void* ws) {
   a.P = (float*)(b + p.P);
   a.Kt = b + p.Kt;
   a.Ktl = b + p.Ktl;
+  a.Qf = b + p.Qf;
   a.gam = (float*)(b + p.gam);
   a.Ptr = (float*)(b + p.Ptr);
   a.Tw = (float*)(b + p.Tw);

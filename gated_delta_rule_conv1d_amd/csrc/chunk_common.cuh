@@ -60,6 +60,8 @@ struct ChunkArgs {
   float* P;                   // [slot][C][C]
   void* Kt;                   // [slot][D][C]  (e_s k_s)^T, e_s = e^{gamma_last - gamma_s}; k_s^T with kt_plain
   void* Ktl;                  //               its lo part (bf16 only; not written with kt_plain)
+  void* Qf;                   // [chunk * Hk + k-head][C][D] q rows in fragment order (written when q_frag)
+  int q_frag;                 // the inference forward's 16-column state pass reads q from Qf
   // backward only: operands of the reverse state pass, transposed once per chunk
   float* Ptr;                 // [slot][C][C]  P^T
   float* Tw;                  // [slot][C][C]  T = (I + A)^-1 (for the WY gradients)

@@ -131,6 +131,14 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
     rK.store(&sm.Ks[0][0], S::LDQ);
     rK.template store_t<E>(&sm.Kt[0][0], S::LDCE);
     __syncthreads();
+    if (FRAG && !LO_OUT && !F8 && a.q_frag) {  // q rows in fragment order for the state pass (zero past len)
+      E* Qg = (E*)a.Qf + ((int64_t)ci * a.Hk + j) * C * D;
+      for (int e = tid; e < C * D / 8; e += NTH) {
+        const int f = e >> 6, l = e & 63;
+        *reinterpret_cast<uint4*>(Qg + e * 8) =
+            *reinterpret_cast<const uint4*>(&sm.Qs[(f / (D / 32)) * 16 + (l & 15)][(f % (D / 32)) * 32 + (l >> 4) * 8]);
+      }
+    }
     for (int t = w; t < NT * NT; t += NW) {
       const int rt = t / NT, ct = t % NT;
       const f32x4 acc = mm_tile<E, D>(zero4(), &sm.Ks[rt * 16][0], S::LDQ, &sm.Ks[ct * 16][0], S::LDQ);
@@ -587,6 +595,11 @@ void launch_chunk_fwd_core(const ChunkArgs& args, hipStream_t st, int mode) {
   const int nc = use_wide_state<E, D, C>() ? state_columns(args, D, mode) : DVT;
   ChunkArgs a = args;
   a.kt_plain = use_wide_state<E, D, C>();
+  // The 16-column pass (few chains) is bound by its operand loads, which are
+  // fastest as 1 KB of consecutive bytes per instruction: the preparation
+  // then also writes q in that order (long 65536: state pass 1.72 -> 1.53 ms
+  // for 0.05 ms more preparation; the whole-state passes read q themselves).
+  a.q_frag = use_wide_state<E, D, C>() && !F8 && mode == kFwdOut && nc == 16;
   static const char* prep_name[4] = {"", "chunk_prep", "chunk_prep_bwd", "chunk_prep_save"};
   // the timing record names the state-pass variant that ran (whole or half
   // state per workgroup, or the column tile of the tiled pass)

@@ -657,6 +657,11 @@ __global__ __launch_bounds__(512) void state_fwd_cols_kernel(ChunkArgs a) {
         const M::frag fq = qb.fr_f8(xw ? kOff : q_row + ks * 32, a.f8_scale[0]);
         op.af[ks] = xw ? fw : fq;
       }
+    } else if constexpr (MODE == kFwdOut) {  // q rows in fragment order, from the preparation (q_frag)
+      const Buf ab(xw ? (const void*)((const E*)a.Wk + slot * C * D)
+                      : (const void*)((const E*)a.Qf + ((int64_t)ci * a.Hk + j) * C * D), C * D * 2);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) op.af[ks] = ab.fr(a_off + ks * 1024);
     } else {
       const Buf ab(xw ? (const void*)((const E*)a.Wk + slot * C * D) : (const void*)((const E*)a.q + q0),
                    xw ? (int64_t)C * D * 2 : (OUT ? (int64_t)en.y * a.sqk * 2 : 0));
