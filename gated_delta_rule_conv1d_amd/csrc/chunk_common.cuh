@@ -94,6 +94,12 @@ struct ChunkArgs {
 struct GateRaw {  // the caller's g (A, dt unused), or a with A_log[h] and dt_bias[h]
   float x, A, dt;
 };
+// one float at byte offset off through a buffer over [base, base + bytes):
+// offsets past the end read zero (bytes = 0: no memory access at all)
+__device__ __forceinline__ float buf_load_f32(const float* base, int bytes, int off) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, bytes, 0x00020000);
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
 __device__ __forceinline__ GateRaw chunk_g_raw(const ChunkArgs& a, int64_t t, int h) {
   if (a.ga) return GateRaw{a.ga[t * a.Hv + h], a.A_log[h], a.dt_bias[h]};
   return GateRaw{a.g[t * a.Hv + h], 0.f, 0.f};

@@ -95,33 +95,42 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
   TileRegs<E, C, D, NTH, true> pV;  // a v-head's v rows; rows first: written transposed
   TileRegs<E, C, D, NTH> rQ;
   TileRegs<E, C, D, NTH, true> rK;  // rows first: also written transposed
-  GateRaw gv{0.f, 0.f, 0.f};  // this lane's gate inputs, finished where the v-head starts
-  float bv = 0.f;
-  // F8: q, k, v arrive as e4m3 bytes and are decoded on load (exactly: the
-  // registers then hold the bf16 tile of the dequantised inputs)
-  auto load_head = [&](int tok, int n, int hh) {
-    if constexpr (F8)
-      pV.load_f8((const uint8_t*)a.v + (int64_t)tok * a.sv + (int64_t)hh * D, a.sv, n, a.f8_scale[2]);
-    else
-      pV.load((const E*)a.v + (int64_t)tok * a.sv + (int64_t)hh * D, a.sv, n);
-    if (w == 0 && lane < n) {
-      gv = chunk_g_raw(a, tok + lane, hh);
-      bv = chunk_beta_raw(a, tok + lane, hh);
-    }
-  };
-  auto load_item = [&](int4 e, int jj) {
+  // wave 0: this lane's raw gate inputs (g or a; beta or b) and the head's
+  // A_log and dt_bias (fused gates), finished where the v-head starts
+  float gx = 0.f, bx = 0.f, gA = 0.f, gdt = 0.f;
+  // The next v-head's v rows and gate inputs, and at an item's last v-head
+  // the next item's q and k rows: every path issues the same loads, and what
+  // it does not need (q and k within an item, gates outside wave 0, anything
+  // past the last item) reads through a zero-size buffer (zeros, no memory
+  // access).  Loads issued on some paths only make the compiler join register
+  // copies that wait for them at once.  F8: q, k, v arrive as e4m3 bytes and
+  // are decoded on load (exactly: the registers then hold the bf16 tile of the
+  // dequantised inputs).
+  auto load_next = [&](bool item_start, int tok, int n, int jj, int hh) {
+    const int nqk = item_start ? n : 0;
     if constexpr (F8) {
-      rQ.load_f8((const uint8_t*)a.q + (int64_t)e.y * a.sqk + (int64_t)jj * D, a.sqk, e.z, a.f8_scale[0]);
-      rK.load_f8((const uint8_t*)a.k + (int64_t)e.y * a.sqk + (int64_t)jj * D, a.sqk, e.z, a.f8_scale[1]);
+      rQ.load_f8((const uint8_t*)a.q + (int64_t)tok * a.sqk + (int64_t)jj * D, a.sqk, nqk, a.f8_scale[0]);
+      rK.load_f8((const uint8_t*)a.k + (int64_t)tok * a.sqk + (int64_t)jj * D, a.sqk, nqk, a.f8_scale[1]);
+      pV.load_f8((const uint8_t*)a.v + (int64_t)tok * a.sv + (int64_t)hh * D, a.sv, n, a.f8_scale[2]);
     } else {
-      rQ.load((const E*)a.q + (int64_t)e.y * a.sqk + (int64_t)jj * D, a.sqk, e.z);
-      rK.load((const E*)a.k + (int64_t)e.y * a.sqk + (int64_t)jj * D, a.sqk, e.z);
+      rQ.load((const E*)a.q + (int64_t)tok * a.sqk + (int64_t)jj * D, a.sqk, nqk);
+      rK.load((const E*)a.k + (int64_t)tok * a.sqk + (int64_t)jj * D, a.sqk, nqk);
+      pV.load((const E*)a.v + (int64_t)tok * a.sv + (int64_t)hh * D, a.sv, n);
     }
-    load_head(e.y, e.z, jj * a.G);
+    // token tok + lane's value at lane * Hv floats; the wave index made
+    // visibly uniform, so the buffer's size stays a scalar
+    const int ng = __builtin_amdgcn_readfirstlane(w) == 0 ? n : 0;
+    const int gbytes = ng > 0 ? ((ng - 1) * a.Hv + 1) * 4 : 0;
+    const int64_t o = (int64_t)tok * a.Hv + hh;
+    gx = buf_load_f32((a.ga ? a.ga : a.g) + o, gbytes, lane * a.Hv * 4);
+    bx = buf_load_f32((a.gb ? a.gb : a.beta) + o, gbytes, lane * a.Hv * 4);
+    const int hbytes = a.ga && ng > 0 ? 4 : 0;
+    gA = buf_load_f32(a.ga ? a.A_log + hh : nullptr, hbytes, 0);
+    gdt = buf_load_f32(a.ga ? a.dt_bias + hh : nullptr, hbytes, 0);
   };
   int item = blockIdx.x;
   int4 ent = item_entry(item);
-  if (ent.x >= 0) load_item(ent, item % a.Hk);
+  load_next(true, ent.y, ent.x >= 0 ? ent.z : 0, item % a.Hk, (item % a.Hk) * a.G);
   while (ent.x >= 0) {
     const int ci = item / a.Hk, j = item % a.Hk;
     const int tok0 = ent.y, len = ent.z;
@@ -151,7 +160,7 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
       const int h = j * a.G + gi;
       const int64_t slot = (int64_t)ci * a.Hv + h;
       if (w == 0) {  // within-chunk cumulative gate
-        float x = chunk_g_fin(a, gv);
+        float x = chunk_g_fin(a, GateRaw{gx, gA, gdt});
 #pragma unroll
         for (int off = 1; off < kWave; off <<= 1) {
           const float y = __shfl_up(x, off, kWave);
@@ -159,13 +168,16 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
         }
         if (lane < C) {
           sm.gam[lane] = x;
-          sm.beta[lane] = chunk_beta_fin(a, bv);
+          sm.beta[lane] = chunk_beta_fin(a, bx);
           a.gam[slot * C + lane] = x;
         }
       }
       pV.template store_t<E>(&sm.Vt[0][0], S::LDCE);  // V^T
-      if (gi + 1 < a.G) load_head(tok0, len, h + 1);
-      else if (nent.x >= 0) load_item(nent, next % a.Hk);  // in flight during this v-head
+      {  // in flight during this v-head: its next v-head, or the next item
+        const bool last = gi + 1 == a.G;
+        const int nj = next % a.Hk;
+        load_next(last, last ? nent.y : tok0, last ? (nent.x >= 0 ? nent.z : 0) : len, nj, last ? nj * a.G : h + 1);
+      }
       __syncthreads();
 
       // P = lower_incl(D * Q K^T) (fp32 to workspace), A = strict_lower(beta_r D * K K^T)
