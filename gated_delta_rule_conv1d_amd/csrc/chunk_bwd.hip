@@ -102,8 +102,10 @@ __global__ __launch_bounds__(kChunkThreads) void state_bwd_kernel(ChunkArgs a) {
   ColRegs<E, C, DVT> pO;
   TileRegs<float, 1, C> pG;
   // (first token, length) of chunk ci from cu_seqlens: no table load in front of the dO load
-  const int c0 = a.seq_chunk0[n], c1 = a.seq_chunk0[n + 1];
-  const int s0 = a.cu[n], s1 = a.cu[n + 1];
+  // the sequence's bounds as scalars (buffer sizes formed from them stay uniform)
+  const int c0 = __builtin_amdgcn_readfirstlane(a.seq_chunk0[n]);
+  const int c1 = __builtin_amdgcn_readfirstlane(a.seq_chunk0[n + 1]);
+  const int s0 = __builtin_amdgcn_readfirstlane(a.cu[n]), s1 = __builtin_amdgcn_readfirstlane(a.cu[n + 1]);
   int plen = 0;
   auto prefetch = [&](int ci) {
     const int tok0 = s0 + (ci - c0) * C;

@@ -425,8 +425,10 @@ __global__ __launch_bounds__(kChunkThreads) void state_fwd_kernel(ChunkArgs a) {
   TileRegs<float, 1, C, TN, false, false> pG;
   // the sequence's chunks are consecutive table entries: (first token, length)
   // follow from cu_seqlens, so no table load sits in front of the Q load
-  const int c0 = a.seq_chunk0[n], c1 = a.seq_chunk0[n + 1];
-  const int s0 = a.cu[n], s1 = a.cu[n + 1];
+  // the sequence's bounds as scalars (buffer sizes formed from them stay uniform)
+  const int c0 = __builtin_amdgcn_readfirstlane(a.seq_chunk0[n]);
+  const int c1 = __builtin_amdgcn_readfirstlane(a.seq_chunk0[n + 1]);
+  const int s0 = __builtin_amdgcn_readfirstlane(a.cu[n]), s1 = __builtin_amdgcn_readfirstlane(a.cu[n + 1]);
   int ptok = 0, plen = 0;
   auto prefetch = [&](int ci) {
     ptok = s0 + (ci - c0) * C;

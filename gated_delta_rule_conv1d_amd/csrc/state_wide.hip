@@ -198,8 +198,10 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
 
   // the sequence's chunks are consecutive table entries: (first token, length)
   // follow from cu_seqlens, with no table load inside the serial loop
-  const int c0 = a.seq_chunk0[n], c1 = a.seq_chunk0[n + 1];
-  const int s0 = a.cu[n], s1 = a.cu[n + 1];
+  // the sequence's bounds as scalars (buffer sizes formed from them stay uniform)
+  const int c0 = __builtin_amdgcn_readfirstlane(a.seq_chunk0[n]);
+  const int c1 = __builtin_amdgcn_readfirstlane(a.seq_chunk0[n + 1]);
+  const int s0 = __builtin_amdgcn_readfirstlane(a.cu[n]), s1 = __builtin_amdgcn_readfirstlane(a.cu[n + 1]);
   auto entry = [&](int ci) {
     const int t = s0 + (ci - c0) * C;
     return make_int4(n, t, min(C, s1 - t), 0);
@@ -226,12 +228,11 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
     }
     if (tid < C) sm.gam[tid] = g_r;
     __syncthreads();
-    const bool more = ci + 1 < c1;
-    int4 nent = ent;
-    if (more) {
-      nent = entry(ci + 1);
-      load_shared(ci + 1);
-    }
+    // the next chunk's operands, or this chunk's again after the last: loads
+    // issued on every path keep the compiler's wait counts exact
+    const int cn = ci + 1 < c1 ? ci + 1 : ci;
+    const int4 nent = entry(cn);
+    load_shared(cn);
     // Stores go after the prefetch loads: the wait for a load also waits for
     // every earlier vector-memory access of the wave.
     if constexpr (STORE) {  // state entering this chunk, for the backward pass
@@ -271,7 +272,7 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
         for (int i = 0; i < P1; ++i) o[i][e] *= gm;
       }
     }
-    if (more) load_p1(ci + 1, nent.y, nent.z);  // Wk, q, U of the next chunk
+    load_p1(cn, nent.y, nent.z);  // Wk, q, U of the next chunk
     float dec[4];  // e^{gamma_last - gamma_r} of this lane's rows, 0 past len
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
           o[i] = M::mma(pl, bh, o[i]);
         }
       }
-      if (more) load_p2(ci + 1);
+      load_p2(cn);
       E* og = (E*)a.o + (int64_t)tok0 * a.Hv * D + (int64_t)h * D;
 #pragma unroll
       for (int i = 0; i < P1; ++i) {
@@ -432,8 +433,10 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
     }
   };
 
-  const int c0 = a.seq_chunk0[n], c1 = a.seq_chunk0[n + 1];
-  const int s0 = a.cu[n], s1 = a.cu[n + 1];
+  // the sequence's bounds as scalars (buffer sizes formed from them stay uniform)
+  const int c0 = __builtin_amdgcn_readfirstlane(a.seq_chunk0[n]);
+  const int c1 = __builtin_amdgcn_readfirstlane(a.seq_chunk0[n + 1]);
+  const int s0 = __builtin_amdgcn_readfirstlane(a.cu[n]), s1 = __builtin_amdgcn_readfirstlane(a.cu[n + 1]);
   auto entry = [&](int ci) {
     const int t = s0 + (ci - c0) * C;
     return make_int4(n, t, min(C, s1 - t), 0);
@@ -461,12 +464,11 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
       sm.Gm[tid] = __expf(g_r);
     }
     __syncthreads();
-    const bool more = ci > c0;
-    int4 nent = ent;
-    if (more) {
-      nent = entry(ci - 1);
-      load_shared(ci - 1, nent.y, nent.z);
-    }
+    // the next chunk's operands (the previous one), or this chunk's again
+    // after the first: loads issued on every path keep the wait counts exact
+    const int cn = ci > c0 ? ci - 1 : ci;
+    const int4 nent = entry(cn);
+    load_shared(cn, nent.y, nent.z);
 
     // phase 1: dW = scale P^T dO + diag(e) K dH on this wave's tiles, one tile at a time
     M::frag ph[2], pl[2];
@@ -474,7 +476,7 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
     for (int ks = 0; ks < 2; ++ks)
       split8(make_float4(ptf[ks][0], ptf[ks][1], ptf[ks][2], ptf[ks][3]),
              make_float4(ptf[ks][4], ptf[ks][5], ptf[ks][6], ptf[ks][7]), ph[ks], pl[ks]);
-    if (more) load_p1(ci - 1);  // P^T of the next chunk
+    load_p1(cn);  // P^T of the next chunk
     // Stores go after this chunk's prefetch loads: the wait for a load also
     // waits for every earlier vector-memory access of the wave.
     {  // gradient w.r.t. the state leaving this chunk
@@ -550,7 +552,7 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
       for (int e = 0; e < 4; ++e) dH[i][e] = gl * dH[i][e] + a.scale * y1[e] - y2[e];
       __builtin_amdgcn_sched_barrier(0);  // keep the next tile's fragment loads out of this one's registers
     }
-    if (more) load_p2(ci - 1, nent.y, nent.z);
+    load_p2(cn, nent.y, nent.z);
     write_dHt();  // phase 1 (the only reader of dH^T) is over for every wave
     ent = nent;
   }
@@ -629,8 +631,10 @@ __global__ __launch_bounds__(512) void state_fwd_cols_kernel(ChunkArgs a) {
 
   // the sequence's chunks are consecutive table entries: (first token, length)
   // follow from cu_seqlens
-  const int c0 = a.seq_chunk0[n], c1 = a.seq_chunk0[n + 1];
-  const int s0 = a.cu[n], s1 = a.cu[n + 1];
+  // the sequence's bounds as scalars (buffer sizes formed from them stay uniform)
+  const int c0 = __builtin_amdgcn_readfirstlane(a.seq_chunk0[n]);
+  const int c1 = __builtin_amdgcn_readfirstlane(a.seq_chunk0[n + 1]);
+  const int s0 = __builtin_amdgcn_readfirstlane(a.cu[n]), s1 = __builtin_amdgcn_readfirstlane(a.cu[n + 1]);
   auto entry = [&](int ci) {
     const int t = s0 + (ci - c0) * C;
     return make_int2(t, min(C, s1 - t));
