@@ -611,6 +611,21 @@ __device__ __forceinline__ bool state_block(int bid, int N, int Hk, int G, int N
 }
 
 
+// f(t) for t = first, first + STEP, ... below TOTAL (first < STEP): a fixed,
+// unrolled count per thread, so that the compiler's wait counts over the
+// stores inside stay exact (a loop whose trip count it cannot see makes it
+// assume the fewest stores, and later loads then wait for all of them)
+template <int TOTAL, int STEP, typename F>
+__device__ __forceinline__ void for_strided(int first, F&& f) {
+  constexpr int N = (TOTAL + STEP - 1) / STEP;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int t = first + i * STEP;
+    if constexpr (TOTAL % STEP == 0) f(t);
+    else if (t < TOTAL) f(t);
+  }
+}
+
 // visit the RT x CT blocks of an NR x NC tile grid owned by this wave
 template <int NR, int NC, int RT, int CT, int NW = kChunkWaves, typename F>
 __device__ __forceinline__ void for_blocks(F&& f) {

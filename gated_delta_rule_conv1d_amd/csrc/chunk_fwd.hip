@@ -140,13 +140,23 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
     rK.store(&sm.Ks[0][0], S::LDQ);
     rK.template store_t<E>(&sm.Kt[0][0], S::LDCE);
     __syncthreads();
+    if constexpr (FRAG) {
+      // K^T (plain: the same for every v-head of the k-head) once per item,
+      // in fragment order, for the state passes (zero past len)
+      E* Kg = (E*)a.Kt + ((int64_t)ci * a.Hk + j) * D * C;
+      for_strided<D * C / 8, NTH>(tid, [&](int e) {
+        const int f = e >> 6, l = e & 63;
+        *reinterpret_cast<uint4*>(Kg + e * 8) =
+            *reinterpret_cast<const uint4*>(&sm.Kt[(f / (C / 32)) * 16 + (l & 15)][(f % (C / 32)) * 32 + (l >> 4) * 8]);
+      });
+    }
     if (FRAG && !LO_OUT && !F8 && a.q_frag) {  // q rows in fragment order for the state pass (zero past len)
       E* Qg = (E*)a.Qf + ((int64_t)ci * a.Hk + j) * C * D;
-      for (int e = tid; e < C * D / 8; e += NTH) {
+      for_strided<C * D / 8, NTH>(tid, [&](int e) {
         const int f = e >> 6, l = e & 63;
         *reinterpret_cast<uint4*>(Qg + e * 8) =
             *reinterpret_cast<const uint4*>(&sm.Qs[(f / (D / 32)) * 16 + (l & 15)][(f % (D / 32)) * 32 + (l >> 4) * 8]);
-      }
+      });
     }
     for (int t = w; t < NT * NT; t += NW) {
       const int rt = t / NT, ct = t % NT;
@@ -183,7 +193,7 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
       // P = lower_incl(D * Q K^T) (fp32 to workspace), A = strict_lower(beta_r D * K K^T)
       {
         float* Pg = a.P + slot * C * C;
-        for (int t = w; t < NT * NT; t += NW) {
+        for_strided<NT * NT, NW>(w, [&](int t) {
           const int rt = t / NT, ct = t % NT;
           if constexpr (LO_OUT) {  // P tiles: P^T also leaves, as 4-element runs
             const f32x4 acc = mm_tile<E, D>(zero4(), &sm.Qs[rt * 16][0], S::LDQ, &sm.Ks[ct * 16][0], S::LDQ);
@@ -212,7 +222,7 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
             *reinterpret_cast<float4*>(&sm.Am[r][s0]) = make_float4(av[0], av[1], av[2], av[3]);
             st4<float>(Pg + (FRAG ? pf_off(r, s0, C) : r * C + s0), pv);
           }
-        }
+        });
       }
       __syncthreads();
       // Outputs that need only gamma, K and Q (K~^T hi / lo; for the backward
@@ -221,7 +231,7 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
       auto gate_outputs = [&](int t0, int nt) {
         // Kt_e[d][s] = e^{gamma_last - gamma_s} k_s[d]  (s < len), 0 past len;
         // with kt_plain the unscaled k_s[d] (exact: no lo part)
-        {
+        if (!FRAG) {  // (FRAG: written once per item above)
           E* Kg = (E*)a.Kt + slot * D * C;
           const float glast = sm.gam[len - 1];
           const bool plain = a.kt_plain;
@@ -235,7 +245,7 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
               val[i] = (s < len) ? to_f<E>(sm.Kt[d][s]) * es : 0.f;
               lo[i] = val[i] - to_f<E>(from_f<E>(val[i]));
             }
-            Vec<E>::store(Kg + (FRAG ? af_off(d, s0, C) : d * C + s0), val);
+            Vec<E>::store(Kg + d * C + s0, val);
             if constexpr (Split<E>::on)
               if (!plain) Vec<E>::store((E*)a.Ktl + slot * D * C + d * C + s0, lo);
           }
@@ -287,10 +297,10 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
       };
       unit_lower_inverse<C, S::LDCF, NTH>(sm.Am, sm.Tm, sm.Tt, sm.Xs, gate_outputs);  // ends with a barrier
       if constexpr (LO_OUT) {  // T for the WY gradients
-        for (int e = tid; e < C * (C / 4); e += NTH) {
+        for_strided<C * (C / 4), NTH>(tid, [&](int e) {
           const int r = e / (C / 4), c = (e % (C / 4)) * 4;
           *reinterpret_cast<float4*>(a.Tw + slot * C * C + r * C + c) = *reinterpret_cast<const float4*>(&sm.Tm[r][c]);
-        }
+        });
       }
 
       // U = (T diag(beta)) V, the left factor split into hi + lo bf16 parts; fp32 result
@@ -301,24 +311,24 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
       __syncthreads();
       if constexpr (FRAG) {  // U tiles, each lane's 4 values one 16-byte write in accumulator order
         float* Ug = a.U + slot * C * D;
-        for (int t = w; t < NT * ND; t += NW) {
+        for_strided<NT * ND, NW>(w, [&](int t) {
           const int rt = t / ND, dt = t % ND;
           f32x4 acc = mm_tile<E, C>(zero4(), &sm.TB[rt * 16][0], S::LDCE, &sm.Vt[dt * 16][0], S::LDCE);
           if constexpr (Split<E>::on)
             acc = mm_tile<E, C>(acc, &sm.TBl[rt * 16][0], S::LDCE, &sm.Vt[dt * 16][0], S::LDCE);
           st4<float>(Ug + (t * 64 + lane) * 4, acc);
-        }
+        });
       } else {
         // formed as U^T = V^T (T diag(beta))^T tiles: a lane then holds 4
         // consecutive d of one row of U, stored as one 16-byte write
         float* Ug = a.U + slot * C * D;
-        for (int t = w; t < NT * ND; t += NW) {
+        for_strided<NT * ND, NW>(w, [&](int t) {
           const int dt = t / NT, rt = t % NT;
           f32x4 acc = mm_tile<E, C>(zero4(), &sm.Vt[dt * 16][0], S::LDCE, &sm.TB[rt * 16][0], S::LDCE);
           if constexpr (Split<E>::on)
             acc = mm_tile<E, C>(acc, &sm.Vt[dt * 16][0], S::LDCE, &sm.TBl[rt * 16][0], S::LDCE);
           st4<float>(Ug + (int64_t)(rt * 16 + acc_col()) * D + dt * 16 + acc_row(0), acc);
-        }
+        });
       }
       __syncthreads();
       // Wk = (T diag(beta Gam)) K
@@ -329,7 +339,7 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
       __syncthreads();
       {
         E* Wg = (E*)a.Wk + slot * C * D;
-        for (int t = w; t < NT * ND; t += NW) {
+        for_strided<NT * ND, NW>(w, [&](int t) {
           if constexpr (LO_OUT) {  // Wk tiles: Wk^T [D][C] (hi / lo) leaves as 4-element runs
             const int rt = t / ND, ct = t % ND;
             f32x4 acc = mm_tile<E, C>(zero4(), &sm.TB[rt * 16][0], S::LDCE, &sm.Kt[ct * 16][0], S::LDCE);
@@ -351,7 +361,7 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
             const int r = rt * 16 + acc_col(), d0 = dt * 16 + acc_row(0);
             st4<E>(Wg + (FRAG ? af_off(r, d0, D) : r * D + d0), acc);
           }
-        }
+        });
       }
       __syncthreads();
     }

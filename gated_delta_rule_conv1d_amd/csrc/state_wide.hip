@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kThreads) void state_fwd_wide_kernel(ChunkArgs a) {
   float4 pf[2][2];
   auto load_shared = [&](int ci) {
     const int64_t slot = (int64_t)ci * a.Hv + h;
-    const Buf kh((const E*)a.Kt + slot * D * C, D * C * 2);
+    const Buf kh((const E*)a.Kt + ((int64_t)ci * a.Hk + j) * D * C, D * C * 2);  // one K^T per k-head
     kt_h0 = kh.u4(tid * 16);
     kt_h1 = kh.u4((tid + kThreads) * 16);
     g_r = Buf(a.gam + slot * C, C * 4).f1((tid & (C - 1)) * 4);  // every thread loads; threads < C use it
@@ -687,7 +687,7 @@ __global__ __launch_bounds__(512) void state_fwd_cols_kernel(ChunkArgs a) {
         op.pf[ks][1] = pb.f4(p_off + 16);
       }
     }
-    const Buf kb((const E*)a.Kt + slot * D * C, D * C * 2);  // fragment order
+    const Buf kb((const E*)a.Kt + ((int64_t)ci * a.Hk + j) * D * C, D * C * 2);  // fragment order, one per k-head
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) op.ktf[ks] = kb.fr(((rs * 2 + ks) * 64 + lane) * 16);
   };
