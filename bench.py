@@ -70,7 +70,12 @@ def kernel_bytes(cfg, n_chunks: int, has_h0: bool) -> dict:
     # bf16 K at d = 128, chunk 64 (the decay goes onto W's / K dH's rows
     # there), else K~ in hi + lo parts
     kt = 1 if (cfg.dtype == "bf16" and D == 128 and C == 64) else lo
-    prep_out = S * (tile_e + tile_f + cc_f + kt * tile_e + row_f)   # Wk, U, P, K^T, gamma
+    # the plain K^T is the same for the G v-heads of a k-head: written once per
+    # k-slot; the inference forward's 16-column state pass (at most 64 chains)
+    # also reads q from a copy the preparation writes in its load order
+    kt_out = SK * tile_e if kt == 1 else S * kt * tile_e
+    q_frag = kt == 1 and N * Hv * 4 <= 256
+    prep_out = S * (tile_e + tile_f + cc_f + row_f) + kt_out   # Wk, U, P, gamma; K^T
     # what the preparation adds for the reverse pass: T and Wk^T (hi + lo); for the tiled
     # reverse pass also P^T, the K rows and (Gamma q)^T (the whole-state pass, kt == 1,
     # forms those from P, k and q)
@@ -91,16 +96,16 @@ def kernel_bytes(cfg, n_chunks: int, has_h0: bool) -> dict:
         "conv_bwd": 3 * T * Cch * es + Cch * W * es,
         "norm_fwd": 3 * T * Hv * D * es + D * es,
         "norm_bwd": 5 * T * Hv * D * es + D * es,
-        "chunk_prep": qk_in + v_in + gb_in + prep_out,
+        "chunk_prep": qk_in + v_in + gb_in + prep_out + (SK * tile_e if q_frag else 0),
         # + what the reverse pass reads from the preparation (prep_bwd_out above)
         "chunk_prep_bwd": qk_in + v_in + gb_in + prep_out + prep_bwd_out,
-        "chunk_state_fwd": SK * tile_e + S * (tile_e + kt * tile_e + tile_f + cc_f + row_f)
+        "chunk_state_fwd": SK * tile_e + kt_out + S * (tile_e + tile_f + cc_f + row_f)
                            + S * tile_e + (st if has_h0 else 0) + st,
         # forward that also keeps the backward's products: prep_bwd's outputs, and H_c, W per slot
         "chunk_prep_save": qk_in + v_in + gb_in + prep_out + prep_bwd_out,
-        "chunk_state_save": SK * tile_e + S * (tile_e + kt * tile_e + tile_f + cc_f + row_f)
+        "chunk_state_save": SK * tile_e + kt_out + S * (tile_e + tile_f + cc_f + row_f)
                             + S * tile_e + (st if has_h0 else 0) + st + S * (dd_f + tile_f),
-        "chunk_state_store": S * (tile_e + kt * tile_e + tile_f + row_f) + (st if has_h0 else 0)
+        "chunk_state_store": kt_out + S * (tile_e + tile_f + row_f) + (st if has_h0 else 0)
                              + S * (dd_f + tile_f),
         "chunk_state_bwd": state_bwd,
         "chunk_grad_a": SK * tile_e + S * (2 * dd_f + 2 * tile_f + 2 * tile_e + 2 * row_f)

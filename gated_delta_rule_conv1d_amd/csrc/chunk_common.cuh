@@ -631,7 +631,7 @@ template <int NR, int NC, int RT, int CT, int NW = kChunkWaves, typename F>
 __device__ __forceinline__ void for_blocks(F&& f) {
   static_assert(NR % RT == 0 && NC % CT == 0, "block shape must divide the tile grid");
   constexpr int NBC = NC / CT, NB = (NR / RT) * NBC;
-  for (int b = wave_id(); b < NB; b += NW) f((b / NBC) * RT, (b % NBC) * CT);
+  for_strided<NB, NW>(wave_id(), [&](int b) { f((b / NBC) * RT, (b % NBC) * CT); });
 }
 
 inline int state_grid(int N, int Hk, int G, int NVT) { return ((N * Hk + 7) / 8) * 8 * G * NVT; }
