@@ -303,66 +303,64 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
         });
       }
 
-      // U = (T diag(beta)) V, the left factor split into hi + lo bf16 parts; fp32 result
-      for (int e = tid; e < C * C; e += NTH) {
+      // U = (T diag(beta)) V and Wk = (T diag(beta Gam)) K, their left factors
+      // split into hi + lo parts in one pass (the Wk factor in the LDS of A and
+      // T^T, which the inverse no longer needs), then both products' tiles in
+      // one phase; fp32 results
+      E (*const TB2)[S::LDCE] = reinterpret_cast<E (*)[S::LDCE]>(&sm.Am[0][0]);
+      E (*const TB2l)[S::LDCE] = reinterpret_cast<E (*)[S::LDCE]>(&sm.Tt[0][0]);
+      static_assert(sizeof(E) * S::LDCE <= sizeof(float) * S::LDCF, "the Wk factor fits A's rows");
+      for_strided<C * C, NTH>(tid, [&](int e) {
         const int r = e / C, s = e % C;
-        split_store<E>(&sm.TB[r][s], &sm.TBl[0][0] + r * S::LDCE + s, sm.Tm[r][s] * sm.beta[s]);
-      }
+        const float tb = sm.Tm[r][s] * sm.beta[s];
+        split_store<E>(&sm.TB[r][s], &sm.TBl[0][0] + r * S::LDCE + s, tb);
+        split_store<E>(&TB2[r][s], &TB2l[r][s], tb * __expf(sm.gam[s]));
+      });
       __syncthreads();
-      if constexpr (FRAG) {  // U tiles, each lane's 4 values one 16-byte write in accumulator order
+      auto u_tile = [&](int t) {
         float* Ug = a.U + slot * C * D;
-        for_strided<NT * ND, NW>(w, [&](int t) {
+        if constexpr (FRAG) {  // U tiles, each lane's 4 values one 16-byte write in accumulator order
           const int rt = t / ND, dt = t % ND;
           f32x4 acc = mm_tile<E, C>(zero4(), &sm.TB[rt * 16][0], S::LDCE, &sm.Vt[dt * 16][0], S::LDCE);
           if constexpr (Split<E>::on)
             acc = mm_tile<E, C>(acc, &sm.TBl[rt * 16][0], S::LDCE, &sm.Vt[dt * 16][0], S::LDCE);
           st4<float>(Ug + (t * 64 + lane) * 4, acc);
-        });
-      } else {
-        // formed as U^T = V^T (T diag(beta))^T tiles: a lane then holds 4
-        // consecutive d of one row of U, stored as one 16-byte write
-        float* Ug = a.U + slot * C * D;
-        for_strided<NT * ND, NW>(w, [&](int t) {
+        } else {
+          // formed as U^T = V^T (T diag(beta))^T tiles: a lane then holds 4
+          // consecutive d of one row of U, stored as one 16-byte write
           const int dt = t / NT, rt = t % NT;
           f32x4 acc = mm_tile<E, C>(zero4(), &sm.Vt[dt * 16][0], S::LDCE, &sm.TB[rt * 16][0], S::LDCE);
           if constexpr (Split<E>::on)
             acc = mm_tile<E, C>(acc, &sm.Vt[dt * 16][0], S::LDCE, &sm.TBl[rt * 16][0], S::LDCE);
           st4<float>(Ug + (int64_t)(rt * 16 + acc_col()) * D + dt * 16 + acc_row(0), acc);
-        });
-      }
-      __syncthreads();
-      // Wk = (T diag(beta Gam)) K
-      for (int e = tid; e < C * C; e += NTH) {
-        const int r = e / C, s = e % C;
-        split_store<E>(&sm.TB[r][s], &sm.TBl[0][0] + r * S::LDCE + s, sm.Tm[r][s] * sm.beta[s] * __expf(sm.gam[s]));
-      }
-      __syncthreads();
-      {
+        }
+      };
+      auto wk_tile = [&](int t) {
         E* Wg = (E*)a.Wk + slot * C * D;
-        for_strided<NT * ND, NW>(w, [&](int t) {
-          if constexpr (LO_OUT) {  // Wk tiles: Wk^T [D][C] (hi / lo) leaves as 4-element runs
-            const int rt = t / ND, ct = t % ND;
-            f32x4 acc = mm_tile<E, C>(zero4(), &sm.TB[rt * 16][0], S::LDCE, &sm.Kt[ct * 16][0], S::LDCE);
-            if constexpr (Split<E>::on)
-              acc = mm_tile<E, C>(acc, &sm.TBl[rt * 16][0], S::LDCE, &sm.Kt[ct * 16][0], S::LDCE);
-            if constexpr (FRAG) {
+        if constexpr (LO_OUT) {  // Wk tiles: Wk^T [D][C] (hi / lo) leaves as 4-element runs
+          const int rt = t / ND, ct = t % ND;
+          f32x4 acc = mm_tile<E, C>(zero4(), &TB2[rt * 16][0], S::LDCE, &sm.Kt[ct * 16][0], S::LDCE);
+          if constexpr (Split<E>::on)
+            acc = mm_tile<E, C>(acc, &TB2l[rt * 16][0], S::LDCE, &sm.Kt[ct * 16][0], S::LDCE);
+          if constexpr (FRAG) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) Wg[af_off(rt * 16 + acc_row(e), ct * 16 + acc_col(), D)] = from_f<E>(acc[e]);
-            } else {
-              store_tile<E>(Wg, D, rt * 16, ct * 16, acc, C);
-            }
-            const int64_t o = slot * D * C + (int64_t)(ct * 16 + acc_col()) * C + rt * 16 + acc_row(0);
-            st4_split<E>((E*)a.Wth + o, (E*)a.Wtl + o, acc);
-          } else {  // Wk^T = K^T (T diag(beta Gam))^T tiles: 4 consecutive d of a Wk row per lane
-            const int dt = t / NT, rt = t % NT;
-            f32x4 acc = mm_tile<E, C>(zero4(), &sm.Kt[dt * 16][0], S::LDCE, &sm.TB[rt * 16][0], S::LDCE);
-            if constexpr (Split<E>::on)
-              acc = mm_tile<E, C>(acc, &sm.Kt[dt * 16][0], S::LDCE, &sm.TBl[rt * 16][0], S::LDCE);
-            const int r = rt * 16 + acc_col(), d0 = dt * 16 + acc_row(0);
-            st4<E>(Wg + (FRAG ? af_off(r, d0, D) : r * D + d0), acc);
+            for (int e = 0; e < 4; ++e) Wg[af_off(rt * 16 + acc_row(e), ct * 16 + acc_col(), D)] = from_f<E>(acc[e]);
+          } else {
+            store_tile<E>(Wg, D, rt * 16, ct * 16, acc, C);
           }
-        });
-      }
+          const int64_t o = slot * D * C + (int64_t)(ct * 16 + acc_col()) * C + rt * 16 + acc_row(0);
+          st4_split<E>((E*)a.Wth + o, (E*)a.Wtl + o, acc);
+        } else {  // Wk^T = K^T (T diag(beta Gam))^T tiles: 4 consecutive d of a Wk row per lane
+          const int dt = t / NT, rt = t % NT;
+          f32x4 acc = mm_tile<E, C>(zero4(), &sm.Kt[dt * 16][0], S::LDCE, &TB2[rt * 16][0], S::LDCE);
+          if constexpr (Split<E>::on)
+            acc = mm_tile<E, C>(acc, &sm.Kt[dt * 16][0], S::LDCE, &TB2l[rt * 16][0], S::LDCE);
+          const int r = rt * 16 + acc_col(), d0 = dt * 16 + acc_row(0);
+          st4<E>(Wg + (FRAG ? af_off(r, d0, D) : r * D + d0), acc);
+        }
+      };
+      for_strided<NT * ND, NW>(w, u_tile);
+      for_strided<NT * ND, NW>(w, wk_tile);
       __syncthreads();
     }
     item = next;
