@@ -409,7 +409,9 @@ def main():
     roof["kernel"] = dom
     roof["avg_us"] = round(avg_s * 1e6, 2)
     roof["algorithmic_bytes"] = kb.get(base(dom))
-    roof["traffic"] = load_traffic(base(dom), args.workload, 1)
+    # the committed counters cover the whole-row launches of the standard step:
+    # not the per-segment launches of --max-tokens, nor the fused-gate kernels
+    roof["traffic"] = None if (args.max_tokens or args.fused_gates) else load_traffic(base(dom), args.workload, 1)
 
     # whole-step roofline of the path (fused algorithmic minimum)
     step_bytes = (33024 + (57856 if cfg.bwd else 0)) * cfg.T if args.workload != "tiny" else None
