@@ -600,8 +600,17 @@ struct ColsOps {
   float g;          // gamma of row `lane`
 };
 
+// A ninth wave per workgroup reads one dword of each 64 bytes of the chain's
+// operands kAhead chunks ahead, so the compute waves' own loads find them in L2
+// (their fragment loads missing to HBM cost ~12% of the pass).  The compute
+// waves could not do this themselves: the vector-memory counter retires in
+// order, so each of their own next-chunk loads would wait for those misses.
+// (Not with fp8 inputs: that form needs the registers a ninth wave would take.)
+constexpr int kColsWaves = 8, kAhead = 3;
+template <bool F8> constexpr int cols_threads() { return (kColsWaves + (F8 ? 0 : 1)) * kWave; }
+
 template <int MODE, bool F8>
-__global__ __launch_bounds__(512) void state_fwd_cols_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(cols_threads<F8>()) void state_fwd_cols_kernel(ChunkArgs a) {
   constexpr bool OUT = MODE & kFwdOut, STORE = MODE & kFwdStore;
   constexpr int D = kD, C = kC;
   constexpr int kOff = 0x40000000;  // a buffer offset past every buffer's end: the store is dropped
@@ -617,6 +626,51 @@ __global__ __launch_bounds__(512) void state_fwd_cols_kernel(ChunkArgs a) {
   const bool xw = w < 4;
   const int rt1 = w & 3;
   const int rs = w;
+
+  if (!F8 && w == kColsWaves) {  // the prefetch wave: the same barriers, no other work
+    const int pc0 = __builtin_amdgcn_readfirstlane(a.seq_chunk0[n]);
+    const int pc1 = __builtin_amdgcn_readfirstlane(a.seq_chunk0[n + 1]);
+    // the chain's lines of one chunk, 64 bytes each: Wk [0, 256), U [256, 768),
+    // P [768, 1024), K^T [1024, 1280), q in load order [1280, 1536); this
+    // workgroup takes 192 of them, 64 per instruction (one region each)
+    auto touch = [&](uint32_t (&t)[3], int cj) {
+      const bool ok = cj < pc1;
+      const int64_t slot = (int64_t)cj * a.Hv + h, kslot = (int64_t)cj * a.Hk + j;
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int L0 = vt * 192 + i * 64;  // a multiple of 64: one region per instruction
+        const void* base;
+        int bytes = 16384, r0;
+        if (L0 < 256) { base = (const E*)a.Wk + slot * C * D; r0 = 0; }
+        else if (L0 < 768) { base = a.U + slot * C * D; bytes = 32768; r0 = 256; }
+        else if (L0 < 1024) { base = a.P + slot * C * C; bytes = OUT ? 16384 : 0; r0 = 768; }
+        else if (L0 < 1280) { base = (const E*)a.Kt + kslot * D * C; r0 = 1024; }
+        else { base = (const E*)a.Qf + kslot * C * D; bytes = a.q_frag ? 16384 : 0; r0 = 1280; }
+        t[i] = __builtin_bit_cast(uint32_t, buf_load_f32((const float*)base, ok ? bytes : 0, (L0 - r0 + lane) * 64));
+      }
+    };
+    auto consume = [](const uint32_t (&t)[3]) { asm volatile("" ::"v"(t[0]), "v"(t[1]), "v"(t[2])); };
+    // chunk ci: the two barriers of the compute waves' chunk step, touches of
+    // chunk ci + kAhead, and the touches of two chunks ago taken (long returned)
+    auto pstep = [&](int ci, uint32_t (&issue)[3], const uint32_t (&old)[3]) {
+      __syncthreads();
+      touch(issue, ci + kAhead);
+      __syncthreads();
+      consume(old);
+    };
+    uint32_t g0[3] = {0u, 0u, 0u}, g1[3] = {0u, 0u, 0u}, g2[3] = {0u, 0u, 0u};
+    for (int ci = pc0; ci < pc1; ci += 3) {
+      pstep(ci, g0, g1);
+      if (ci + 1 >= pc1) break;
+      pstep(ci + 1, g1, g2);
+      if (ci + 2 >= pc1) break;
+      pstep(ci + 2, g2, g0);
+    }
+    consume(g0);
+    consume(g1);
+    consume(g2);
+    return;
+  }
 
   f32x4 Hr = zero4();
   if (a.h0) {
@@ -817,10 +871,10 @@ void launch_state_fwd_wide(const ChunkArgs& a, hipStream_t st, int mode, bool ha
 
 void launch_state_fwd_cols(const ChunkArgs& a, hipStream_t st, int mode, bool f8) {
   const dim3 grid(state_grid(a.N, a.Hk, a.G, kD / 16));
-  if (f8) state_fwd_cols_kernel<kFwdOut, true><<<grid, 512, 0, st>>>(a);  // fp8 inputs: inference only
-  else if (mode == kFwdOut) state_fwd_cols_kernel<kFwdOut, false><<<grid, 512, 0, st>>>(a);
-  else if (mode == kFwdStore) state_fwd_cols_kernel<kFwdStore, false><<<grid, 512, 0, st>>>(a);
-  else state_fwd_cols_kernel<kFwdBoth, false><<<grid, 512, 0, st>>>(a);
+  if (f8) state_fwd_cols_kernel<kFwdOut, true><<<grid, cols_threads<true>(), 0, st>>>(a);  // fp8 inputs: inference only
+  else if (mode == kFwdOut) state_fwd_cols_kernel<kFwdOut, false><<<grid, cols_threads<false>(), 0, st>>>(a);
+  else if (mode == kFwdStore) state_fwd_cols_kernel<kFwdStore, false><<<grid, cols_threads<false>(), 0, st>>>(a);
+  else state_fwd_cols_kernel<kFwdBoth, false><<<grid, cols_threads<false>(), 0, st>>>(a);
 }
 
 void launch_state_bwd_wide(const ChunkArgs& a, hipStream_t st, bool half) {
