@@ -55,10 +55,13 @@ struct ChunkArgs {
   // workspace
   const int32_t* table;       // [max_chunks][4]
   const int32_t* seq_chunk0;  // [N+1]
+  // (bf16, d = 128, chunk 64: Wk and K^T in A-fragment order, U in accumulator
+  // order and the inference P in split A-fragment order -- af_off, acc_off,
+  // pf_off below -- and the plain K^T once per (chunk, k-head))
   void* Wk;                   // [slot][C][D]
   float* U;                   // [slot][C][D]
   float* P;                   // [slot][C][C]
-  void* Kt;                   // [slot][D][C]  (e_s k_s)^T, e_s = e^{gamma_last - gamma_s}; k_s^T with kt_plain
+  void* Kt;                   // [slot][D][C]  (e_s k_s)^T, e_s = e^{gamma_last - gamma_s}; k_s^T with kt_plain ([chunk * Hk + k-head])
   void* Ktl;                  //               its lo part (bf16 only; not written with kt_plain)
   void* Qf;                   // [chunk * Hk + k-head][C][D] q rows in fragment order (written when q_frag)
   int q_frag;                 // the inference forward's 16-column state pass reads q from Qf

@@ -68,11 +68,12 @@ __global__ __launch_bounds__(1024) void chunk_index_kernel(const int32_t* __rest
 }
 
 // ---------------------------------------------------------------------------
-// WY preparation, one workgroup per (chunk, k-head), looping over the k-head's
-// v-heads.  K K^T and Q K^T on MFMA (operand type E), the unit-lower
-// triangular inverse in fp32 (16x16 diagonal blocks by per-lane forward
-// substitution, off-diagonal blocks by block substitution on fp32 MFMA),
-// U and Wk on MFMA.
+// WY preparation, persistent workgroups walking (chunk, k-head) items, each
+// looping over the k-head's v-heads.  K K^T and Q K^T on MFMA (operand type E),
+// the unit-lower triangular inverse in fp32 (16x16 diagonal blocks by per-lane
+// forward substitution, off-diagonal blocks by block substitution on fp32
+// MFMA), U and Wk on MFMA.  At bf16, d = 128, chunk 64 the outputs only the
+// state passes read leave in the order those passes load them.
 // ---------------------------------------------------------------------------
 template <typename E, int D, int C, bool LO_OUT, int NTH, bool F8 = false>
 __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {

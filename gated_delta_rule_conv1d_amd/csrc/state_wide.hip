@@ -9,10 +9,12 @@
 //
 // LDS holds only what several waves read: K^T, H^T and W^T (forward; H and W
 // as bf16 hi + lo); [dO^T | dW^T], dH^T and K~ rows (reverse, hi + lo).  Operands that
-// one row-tile of waves reads (Wk, q, U, P in the forward; P^T, (Gam q)^T,
-// Wk^T in the reverse) are loaded straight into MFMA fragments from global
-// memory (L2), and the next chunk's copies are requested right after the
-// current chunk's last use.
+// one row-tile of waves reads (Wk, q, U, P in the forward, Wk, U and the
+// inference P in the order the preparation wrote them; P^T and (Gam q)^T
+// gathered from P and q, and Wk^T, in the reverse) are loaded straight into
+// MFMA fragments from global memory (L2), and the next chunk's copies are
+// requested right after the current chunk's last use, on every path (the
+// last chunk loads itself again), so the compiler's wait counts stay exact.
 //
 // Forward, per chunk (H = state entering it):
 //   W = U - Wk H;   o = scale (diag(Gam) Q H + P W);   H <- Gam_last H + K^T diag(e) W
@@ -569,14 +571,16 @@ __global__ __launch_bounds__(kThreads) void state_bwd_wide_kernel(ChunkArgs a) {
 
 // ---------------------------------------------------------------------------
 // Forward state pass over 16-column tiles of the state, for chains too few to
-// fill the chip (a single long sequence): eight 256-thread workgroups per
-// (sequence, v-head), each carrying 16 state columns through the whole
-// sequence.  Every operand that one wave reads alone goes straight from
-// global memory (L2) into matrix-core fragments: wave w's rows of Wk, q, U and
-// P (output row tile w) and of K^T (state row tiles w and w + 4); only H^T and
-// W^T, which all waves read, pass through LDS.  Each chunk's operands are
-// requested right after the previous chunk's last use of their registers.
-// Same arithmetic as the whole-state pass, per element.
+// fill the chip (a single long sequence): eight workgroups per (sequence,
+// v-head), each carrying 16 state columns through the whole sequence with
+// eight compute waves (and, without fp8 inputs, a ninth that prefetches into
+// L2).  Every operand that one wave reads alone goes straight from global
+// memory (L2) into matrix-core fragments, in the order the preparation wrote it:
+// rows of Wk and the U tile (waves 0-3), rows of q and P (waves 4-7), K^T rows
+// of state row tile w (wave w); only H^T and W^T, which all waves read, pass
+// through LDS.  The next chunk's operands load into a second register set at
+// the start of each chunk.  Same arithmetic as the whole-state pass, per
+// element.
 // ---------------------------------------------------------------------------
 struct ColsSmem {
   E Ht[16][kLDQ];   // H^T: Ht[c][r] = H[r][c], this workgroup's 16 columns
