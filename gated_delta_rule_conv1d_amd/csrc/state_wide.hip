@@ -822,15 +822,18 @@ __global__ __launch_bounds__(cols_threads<F8>()) void state_fwd_cols_kernel(Chun
         x = M::mma(pl, bh, x);
       }
     }
-    // tile stores, issued by every wave: W (waves 0-3, STORE) and o (waves 4-7,
-    // OUT); the other role's, and rows past the chunk's end, go past the buffer
-    {
-      const Buf wb(a.W + slot * C * D, STORE ? C * D * 4 : 0);
+    // tile stores, issued by every wave in the modes that have them: W (waves
+    // 0-3, STORE) and o (waves 4-7, OUT); the other role's, and rows past the
+    // chunk's end, go past the buffer's end
+    if constexpr (STORE) {
+      const Buf wb(a.W + slot * C * D, C * D * 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         wb.st_f32(xw ? ((rt1 * 16 + acc_row(e)) * D + col0 + acc_col()) * 4 : kOff, x[e]);
+    }
+    if constexpr (OUT) {
       const int ld = a.Hv * D;
-      const Buf ob((E*)a.o + (int64_t)tok0 * ld + (int64_t)h * D, OUT ? ((int64_t)(len - 1) * ld + D) * 2 : 0);
+      const Buf ob((E*)a.o + (int64_t)tok0 * ld + (int64_t)h * D, ((int64_t)(len - 1) * ld + D) * 2);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = rt1 * 16 + acc_row(e);
