@@ -539,8 +539,14 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
   const E* qg = (const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D;
   const E* kg = (const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D;
 
-  rows2s_t<E, C, D, NTH>(&sm.QKt[0][0], S::LD2C, qg, a.sqk, len);
-  rows2s_t<E, C, D, NTH>(&sm.QKt[0][C], S::LD2C, kg, a.sqk, len);
+  {
+    // q and k rows, both requested before either is written (transposed) to LDS
+    TileRegs<E, C, D, NTH, true> rq, rk;
+    rq.load(qg, a.sqk, len);
+    rk.load(kg, a.sqk, len);
+    rq.store_t_raw(&sm.QKt[0][0], S::LD2C);
+    rk.store_t_raw(&sm.QKt[0][C], S::LD2C);
+  }
   __syncthreads();
   // K K^T (exact bf16 products, fp32 sums), shared by the k-head's v-heads
   for (int t = w; t < NT * NT; t += NW) {
@@ -567,6 +573,21 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
     const int h = j * a.G + gi;
     const int64_t slot = (int64_t)ci * a.Hv + h;
     const E* vg = (const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)h * D;
+    // Per-row gates, requested before the tiles so that wave 0, which writes
+    // them to LDS, waits for these loads only.  Every thread loads those of row
+    // tid % C (rows past len clamped): no load sits in a branch, where the
+    // compiler would issue it after the tiles' or on its own.
+    const int ge = tid & (C - 1), gr = min(ge, len - 1);
+    const float gm = a.gam[slot * C + ge];
+    const float gl = a.gam[slot * C + len - 1];
+    const float braw = chunk_beta_raw(a, tok0 + gr, h);
+    const float hd = a.hdot[slot];
+    // fused gates: this row's raw a, A_log and dt_bias (zero-size reads without
+    // them: a load under a branch is waited for in that branch)
+    const int fz = a.ga ? 4 : 0;
+    const float xa_raw = buf_load_f32(a.ga + (int64_t)tok0 * a.Hv + h, fz * len * a.Hv, gr * a.Hv * 4);
+    const float alog = buf_load_f32(a.A_log + h, fz, 0), dtb = buf_load_f32(a.dt_bias + h, fz, 0);
+    __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the tiles'
     TileRegs<E, C, D, NTH> pV;  // v rows and T (from the preparation pass)
     TileRegs<float, C, C, NTH, true> pTm;  // rows first: also written transposed
     TileRegs<float, D, C, NTH> rXu, rXw;  // dW^T, and dWk^T (in flight during the dXu products)
@@ -576,25 +597,20 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
     rXw.load(a.dWkt + slot * D * C, C, D);
     // fused gates: this row's factors da / dg, db / dbeta and its g, kept for the row pass at the end
     float fa_r = 0.f, fb_r = 0.f, g_r = 0.f;
-    if (tid < C) {  // per-row gates; every load unconditional (clamped rows), so they issue together
-      const int e = tid;
-      const float gm = a.gam[slot * C + e];
-      const float gl = a.gam[slot * C + len - 1];
-      const float braw = chunk_beta_raw(a, tok0 + min(e, len - 1), h);
+    if (tid < C) {
       if (a.ga) {
         // formed here, off the row pass's serial path (the expressions of gdn_gates_bwd)
-        const float ea = __expf(a.A_log[h]), xa = a.ga[(int64_t)(tok0 + min(e, len - 1)) * a.Hv + h] + a.dt_bias[h];
+        const float ea = __expf(alog), xa = xa_raw + dtb;
         fa_r = -ea * gate_sigmoid(xa);
         g_r = -ea * gate_softplus(xa);
         fb_r = gate_sigmoid(braw) * gate_sigmoid(-braw);
       }
       const float bt = chunk_beta_fin(a, braw);
-      const float hd = a.hdot[slot];  // used by the row pass at the end
-      sm.gam[e] = gm;
-      sm.Gm[e] = __expf(gm);
-      sm.beta[e] = e < len ? bt : 0.f;
-      sm.em[e] = e < len ? __expf(gl - gm) : 0.f;
-      if (e == 0) sm.hdot = hd;
+      sm.gam[ge] = gm;
+      sm.Gm[ge] = __expf(gm);
+      sm.beta[ge] = ge < len ? bt : 0.f;
+      sm.em[ge] = ge < len ? __expf(gl - gm) : 0.f;
+      sm.hdot = hd;  // the same value from every lane: no branch for the load to sink into
     }
     pTm.store(&sm.Tm[0][0], S::LDCF);
     // fp32 operands of the products below are split into their MFMA parts once
@@ -737,11 +753,14 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();
-    // this lane's dKh tiles: in flight during the transpose below
-    f32x4 khr[DT];
-    if (act) {
+    // this lane's dKh and dQs tiles: in flight during the transpose below
+    // (waves past the d-tiles load the last tile again and leave it unused)
+    f32x4 khr[DT], qsr[DT];
 #pragma unroll
-      for (int i = 0; i < DT; ++i) khr[i] = load_acc(a.dKh + slot * C * D, NT, dt0 + i, rt);
+    for (int i = 0; i < DT; ++i) {
+      const int dtl = min(dt0 + i, ND - 1);
+      khr[i] = load_acc(a.dKh + slot * C * D, NT, dtl, rt);
+      qsr[i] = load_acc(a.dQs + slot * C * D, NT, dtl, rt);
     }
     // [dS^T | A~ + A~^T] as rows (P and dP' are consumed)
     for (int e = tid; e < C * C; e += NTH) {
@@ -754,12 +773,11 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
     __syncthreads();
     // dQ += dQs + dS K;   dK += dKh + [dS^T | A~ + A~^T] [Q ; K]   (transposed)
     if (act) {
-      const float* dQsg = a.dQs + slot * C * D;
       float pq = 0.f, pk = 0.f;
 #pragma unroll
       for (int i = 0; i < DT; ++i) {
         const int d = (dt0 + i) * 16 + dl;
-        const f32x4 qs = load_acc(dQsg, NT, dt0 + i, rt);
+        const f32x4 qs = qsr[i];
         const f32x4 kh = khr[i];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {

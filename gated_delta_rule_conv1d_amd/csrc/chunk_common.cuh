@@ -208,53 +208,6 @@ __device__ __forceinline__ void st4_split(E* hi, E* lo, f32x4 v) {
   }
 }
 
-// copy a [R][Ccols] row-major E tile between global (dense, ld = Ccols) and LDS
-// (row stride lds), 16 bytes per thread step
-template <typename E, int R, int Ccols, int NTH = kChunkThreads>
-__device__ __forceinline__ void g2s(E* s, int lds, const E* g) {
-  constexpr int V = Vec<E>::N;
-  constexpr int PER_ROW = Ccols / V;
-  for (int e = threadIdx.x; e < R * PER_ROW; e += NTH) {
-    const int r = e / PER_ROW, c = (e % PER_ROW) * V;
-    *reinterpret_cast<uint4*>(s + r * lds + c) = *reinterpret_cast<const uint4*>(g + (int64_t)r * Ccols + c);
-  }
-}
-
-// rows [0, len) of a token-major input written transposed into LDS:
-// s[c * lds + r] = g[r * ld + c]; zero past len.  Rows first: 16 adjacent lanes
-// read the same columns of 16 adjacent rows, so each transposed write puts 16
-// consecutive elements of one LDS row down (no bank conflicts between them).
-// Buffer loads over rows [0, len) (zero past it), all issued before the
-// first write.
-template <typename E, int R, int Ccols, int NTH = kChunkThreads>
-__device__ __forceinline__ void rows2s_t(E* s, int lds, const E* g, int64_t ld, int len) {
-  constexpr int V = Vec<E>::N;
-  constexpr int PER_ROW = Ccols / V;
-  constexpr int NP = (R * PER_ROW + NTH - 1) / NTH;  // 16-byte pieces per thread
-  static_assert(R % 16 == 0, "rows in groups of 16");
-  const int64_t bytes = (int64_t)len * ld * (int64_t)sizeof(E);
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<E*>(g), 0, (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff), 0x00020000);
-  uint4 raw[NP];
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int e = threadIdx.x + i * NTH, grp = e >> 4;
-    const int r = (grp / PER_ROW) * 16 + (e & 15), c = (grp % PER_ROW) * V;
-    const int off = e < R * PER_ROW ? (int)(((int64_t)r * ld + c) * (int64_t)sizeof(E)) : 0x7fffffe0;
-    raw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-  }
-#pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int e = threadIdx.x + i * NTH, grp = e >> 4;
-    if (e < R * PER_ROW) {
-      const int r = (grp / PER_ROW) * 16 + (e & 15), c = (grp % PER_ROW) * V;
-      const E* v = reinterpret_cast<const E*>(&raw[i]);
-#pragma unroll
-      for (int u = 0; u < V; ++u) s[(c + u) * lds + r] = v[u];
-    }
-  }
-}
-
 __device__ __forceinline__ int4 chunk_entry(const int32_t* table, int ci) {
   return reinterpret_cast<const int4*>(table)[ci];
 }
@@ -427,6 +380,9 @@ struct TileRegs {
   static constexpr int PER_ROW = COLS / V;
   static constexpr int TOTAL = R * PER_ROW;
   static constexpr int N = (TOTAL + NTH - 1) / NTH;
+  // every thread holds N whole pieces: no per-piece guard (a guard the compiler
+  // cannot fold is a branch, and loads it sinks into it wait there one by one)
+  static constexpr bool FULL = TOTAL % NTH == 0;
   static_assert(!RF || R % 16 == 0, "rows-first pieces come in groups of 16 rows");
   uint4 r[N];
   __device__ __forceinline__ static void pos(int e, int& row, int& c) {
@@ -488,7 +444,7 @@ struct TileRegs {
     for (int i = 0; i < N; ++i) {
       const int e = threadIdx.x + i * NTH;
       r[i] = make_uint4(0, 0, 0, 0);
-      if (e < TOTAL) {
+      if (FULL || e < TOTAL) {
         int row, c;
         pos(e, row, c);
         if (row < rows_valid) r[i] = *reinterpret_cast<const uint4*>(g + (int64_t)row * ld + c);
@@ -499,7 +455,7 @@ struct TileRegs {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int e = threadIdx.x + i * NTH;
-      if (e < TOTAL) {
+      if (FULL || e < TOTAL) {
         int row, c;
         pos(e, row, c);
         *reinterpret_cast<uint4*>(s + row * lds + c) = r[i];
@@ -515,7 +471,7 @@ struct TileRegs {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int e = threadIdx.x + i * NTH;
-      if (e < TOTAL) {
+      if (FULL || e < TOTAL) {
         int row, c;
         pos(e, row, c);
         const T* f = reinterpret_cast<const T*>(&r[i]);
@@ -534,6 +490,20 @@ struct TileRegs {
     pos(threadIdx.x + i * NTH, row, c);
     return row;
   }
+  // tile written transposed as it is: s[c * lds + row]
+  __device__ __forceinline__ void store_t_raw(T* s, int lds) const {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int e = threadIdx.x + i * NTH;
+      if (FULL || e < TOTAL) {
+        int row, c;
+        pos(e, row, c);
+        const T* f = reinterpret_cast<const T*>(&r[i]);
+#pragma unroll
+        for (int u = 0; u < V; ++u) s[(c + u) * lds + row] = f[u];
+      }
+    }
+  }
   // float tile written as E hi (and lo) parts
   template <typename E>
   __device__ __forceinline__ void store_split(E* hi, E* lo, int lds) const {
@@ -541,7 +511,7 @@ struct TileRegs {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int e = threadIdx.x + i * NTH;
-      if (e < TOTAL) {
+      if (FULL || e < TOTAL) {
         int row, c;
         pos(e, row, c);
         const float* f = reinterpret_cast<const float*>(&r[i]);
@@ -560,6 +530,7 @@ struct ColRegs {
   static constexpr int V = 16 / (int)sizeof(T);
   static constexpr int TOTAL = COLS * (R / V);
   static constexpr int N = (TOTAL + NTH - 1) / NTH;
+  static constexpr bool FULL = TOTAL % NTH == 0;
   static_assert(sizeof(T) == 2 || sizeof(T) == 4, "16- or 32-bit elements");
   uint4 r[N];
   // Buffer loads through a resource that covers rows [0, rows_valid): rows
@@ -590,7 +561,7 @@ struct ColRegs {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const int e = threadIdx.x + i * NTH;
-      if (e < TOTAL) {
+      if (FULL || e < TOTAL) {
         const int c = e % COLS, r0 = (e / COLS) * V;
         *reinterpret_cast<uint4*>(s + c * lds + r0) = r[i];
       }

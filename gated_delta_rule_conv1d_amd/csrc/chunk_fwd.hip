@@ -151,13 +151,15 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
             *reinterpret_cast<const uint4*>(&sm.Kt[(f / (C / 32)) * 16 + (l & 15)][(f % (C / 32)) * 32 + (l >> 4) * 8]);
       });
     }
-    if (FRAG && !LO_OUT && !F8 && a.q_frag) {  // q rows in fragment order for the state pass (zero past len)
-      E* Qg = (E*)a.Qf + ((int64_t)ci * a.Hk + j) * C * D;
-      for_strided<C * D / 8, NTH>(tid, [&](int e) {
-        const int f = e >> 6, l = e & 63;
-        *reinterpret_cast<uint4*>(Qg + e * 8) =
-            *reinterpret_cast<const uint4*>(&sm.Qs[(f / (D / 32)) * 16 + (l & 15)][(f % (D / 32)) * 32 + (l >> 4) * 8]);
-      });
+    if constexpr (FRAG && !LO_OUT && !F8) {
+      if (a.q_frag) {  // q rows in fragment order for the state pass (zero past len)
+        E* Qg = (E*)a.Qf + ((int64_t)ci * a.Hk + j) * C * D;
+        for_strided<C * D / 8, NTH>(tid, [&](int e) {
+          const int f = e >> 6, l = e & 63;
+          *reinterpret_cast<uint4*>(Qg + e * 8) =
+              *reinterpret_cast<const uint4*>(&sm.Qs[(f / (D / 32)) * 16 + (l & 15)][(f % (D / 32)) * 32 + (l >> 4) * 8]);
+        });
+      }
     }
     for (int t = w; t < NT * NT; t += NW) {
       const int rt = t / NT, ct = t % NT;
