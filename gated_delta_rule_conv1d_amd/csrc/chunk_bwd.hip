@@ -680,7 +680,12 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
     __syncthreads();
     for (int t = w; t < NT * NT; t += NW) {
       const int rt = t / NT, ct = t % NT;
-      const f32x4 m = mm_tile<float, C>(zero4(), &sm.r.m.dT[rt * 16][0], S::LDCF, &sm.Tm[ct * 16][0], S::LDCF);
+      // fp32 operands fed as bf16 hi / lo parts (three products per k-step)
+      // rather than to the fp32 matrix instruction, which does a quarter of
+      // the work per cycle
+      const f32x4 m = mm_gen<E, C, true, true>(
+          zero4(), [&](int r, int k, float* o) { ld_row<float, KPL>(&sm.r.m.dT[rt * 16 + r][k], o); },
+          [&](int c, int k, float* o) { ld_row<float, KPL>(&sm.Tm[ct * 16 + c][k], o); });
       E* const M1L = LO ? &sm.r.m.M1l[0][0] : nullptr;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {

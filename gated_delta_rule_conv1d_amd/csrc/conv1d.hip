@@ -35,6 +35,39 @@ __device__ __forceinline__ int find_seq(const int32_t* cu, int N, int t) {
   return lo < N ? lo : N - 1;
 }
 
+// Prologue loads through buffer resources: a lane whose value does not exist
+// (channel past Cch, token outside its sequence) reads an out-of-range offset
+// and gets zeros, so every load is issued at once and waited for once (loads
+// under a per-lane branch were each waited for inside it).
+constexpr int kOob = 0x7fffff00;
+
+// this lane's V x W taps, w[(ch + c) * W + i]
+template <typename E, int V, int W>
+__device__ __forceinline__ void load_taps(const E* w, int Cch, int ch, float (&wr)[V][W]) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<E*>(w), 0, Cch * W * (int)sizeof(E), 0x00020000);
+  const int base = ch < Cch ? ch * W * (int)sizeof(E) : kOob;
+#pragma unroll
+  for (int c = 0; c < V; ++c)
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      const int k = (c * W + i) * (int)sizeof(E);
+      if constexpr (sizeof(E) == 2)
+        wr[c][i] = to_f<E>(__builtin_bit_cast(E, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs, base + k, 0, 0)));
+      else
+        wr[c][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, base + k, 0, 0));
+    }
+}
+
+// 16 bytes (V channels) at byte offset off of rs, as floats (zeros out of range)
+template <typename E>
+__device__ __forceinline__ void load_vec_buf(__amdgpu_buffer_rsrc_t rs, int off, float* out) {
+  const uint4 raw = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+  const E* e = reinterpret_cast<const E*>(&raw);
+#pragma unroll
+  for (int i = 0; i < Vec<E>::N; ++i) out[i] = to_f<E>(e[i]);
+}
+
 template <typename E, int D, int W>
 __global__ __launch_bounds__(256) void conv_fwd_kernel(const E* __restrict__ x, const E* __restrict__ w,
                                                        const int32_t* __restrict__ cu, const E* __restrict__ win,
@@ -43,7 +76,9 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(const E* __restrict__ x, 
   constexpr int V = Vec<E>::N;      // channels per lane
   constexpr int LPH = D / V;        // lanes per L2 group
   const int lane = lane_id();
-  const int tb = blockIdx.x * kConvWaves + wave_id();
+  // the wave index read as a scalar: the token range, the sequence search and
+  // its cu_seqlens reads are then scalar too
+  const int tb = blockIdx.x * kConvWaves + __builtin_amdgcn_readfirstlane(wave_id());
   const int t0 = tb * tpw;          // tpw tokens per wave
   if (t0 >= T) return;
   const int t1 = min(t0 + tpw, T);
@@ -52,10 +87,7 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(const E* __restrict__ x, 
   const bool is_qk = ch < n_qk;
 
   float wr[V][W];
-#pragma unroll
-  for (int c = 0; c < V; ++c)
-#pragma unroll
-    for (int i = 0; i < W; ++i) wr[c][i] = active ? to_f<E>(w[(size_t)(ch + c) * W + i]) : 0.f;
+  load_taps<E, V, W>(w, Cch, ch, wr);
 
   // ring[k] holds x of the token t with (t - t0) % W == k; the token loop is
   // unrolled by W so every slot index is a constant (no register shifting)
@@ -64,15 +96,25 @@ __global__ __launch_bounds__(256) void conv_fwd_kernel(const E* __restrict__ x, 
   int seq_start = cu[n], seq_end = cu[n + 1];
 #pragma unroll
   for (int c = 0; c < V; ++c) ring[0][c] = 0.f;
+  {
+    // history: token s = t0 - (W-1) + i from x inside the sequence, else its
+    // carried window (slot s - seq_start + W - 1), else zeros
+    const int b0 = max(t0 - (W - 1), 0);
+    const int es = (int)sizeof(E);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<E*>(x) + (size_t)b0 * Cch, 0, (t0 - b0) * Cch * es, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<E*>(win) + (win ? (size_t)n * (W - 1) * Cch : 0), 0, win ? (W - 1) * Cch * es : 0, 0x00020000);
 #pragma unroll
-  for (int i = 0; i < W - 1; ++i) {
-    const int s = t0 - (W - 1) + i;
-    if (active && s >= seq_start) Vec<E>::load(x + (size_t)s * Cch + ch, ring[i + 1]);
-    else if (active && win)  // before the sequence: its carried window, slot s - seq_start + W - 1
-      Vec<E>::load(win + ((size_t)n * (W - 1) + (s - seq_start + W - 1)) * Cch + ch, ring[i + 1]);
-    else
+    for (int i = 0; i < W - 1; ++i) {
+      const int s = t0 - (W - 1) + i;
+      const bool in_seq = s >= seq_start;
+      float fx[V], fw[V];
+      load_vec_buf<E>(rx, active && in_seq ? ((s - b0) * Cch + ch) * es : kOob, fx);
+      load_vec_buf<E>(rw, active && !in_seq ? ((s - seq_start + W - 1) * Cch + ch) * es : kOob, fw);
 #pragma unroll
-      for (int c = 0; c < V; ++c) ring[i + 1][c] = 0.f;
+      for (int c = 0; c < V; ++c) ring[i + 1][c] = in_seq ? fx[c] : fw[c];
+    }
   }
 
   // the next W tokens' x are loaded while the current W compute (W loads in
@@ -149,7 +191,7 @@ __global__ __launch_bounds__(256, 2) void conv_bwd_kernel(const E* __restrict__ 
   constexpr int LPH = D / V;
   __shared__ float red[kConvWaves][kWave * V * W];
   const int lane = lane_id();
-  const int wv = wave_id();
+  const int wv = __builtin_amdgcn_readfirstlane(wave_id());  // scalar: so are the token range and the cu_seqlens reads
   const int tb = blockIdx.x * kConvWaves + wv;
   const int t0 = tb * kConvTBB;
   const int ch = (blockIdx.y * kWave + lane) * V;
@@ -166,10 +208,7 @@ __global__ __launch_bounds__(256, 2) void conv_bwd_kernel(const E* __restrict__ 
     const int t1 = min(t0 + kConvTBB, T);
     const int tend = min(t1 + W - 1, T);
     float wr[V][W];
-#pragma unroll
-    for (int c = 0; c < V; ++c)
-#pragma unroll
-      for (int i = 0; i < W; ++i) wr[c][i] = active ? to_f<E>(w[(size_t)(ch + c) * W + i]) : 0.f;
+    load_taps<E, V, W>(w, Cch, ch, wr);
 
     int n = find_seq(cu, N, t0);
     int seq_start = cu[n], seq_end = cu[n + 1];
@@ -184,10 +223,16 @@ __global__ __launch_bounds__(256, 2) void conv_bwd_kernel(const E* __restrict__ 
 #pragma unroll
       for (int c = 0; c < V; ++c) xr[i][c] = dcr[i][c] = 0.f;
     }
+    {
+      const int b0 = max(t0 - (W - 1), 0);
+      const int es = (int)sizeof(E);
+      const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<E*>(x) + (size_t)b0 * Cch, 0, (t0 - b0) * Cch * es, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < W - 1; ++i) {
-      const int s = t0 - (W - 1) + i;
-      if (active && s >= seq_start) Vec<E>::load(x + (size_t)s * Cch + ch, xr[i + 1]);
+      for (int i = 0; i < W - 1; ++i) {
+        const int s = t0 - (W - 1) + i;
+        load_vec_buf<E>(rx, active && s >= seq_start ? ((s - b0) * Cch + ch) * es : kOob, xr[i + 1]);
+      }
     }
     // the next W tokens' x and dy are loaded while the current W compute
     uint4 cx[W], cg[W];
