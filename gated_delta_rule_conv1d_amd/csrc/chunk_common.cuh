@@ -1,6 +1,8 @@
 // Shared pieces of the chunked gated-delta-rule kernels (forward and backward).
 #pragma once
 
+#include <utility>
+
 #include "gdn_common.cuh"
 #include "gdn_internal.h"
 
@@ -246,6 +248,19 @@ struct PrepSmem {
 struct NoWork {
   __device__ void operator()(int, int) const {}
 };
+// the 16-byte pieces of a 16 x 16 strictly lower triangle, rows first: piece i
+// is row diag_piece_row(i), columns 4 diag_piece_col(i) ...
+constexpr int kDiagPieces = 36;  // sum over rows r of ceil(r / 4)
+constexpr int diag_piece_row(int i) {
+  int r = 1;
+  while (i >= (r + 3) / 4) i -= (r++ + 3) / 4;
+  return r;
+}
+constexpr int diag_piece_col(int i) {
+  int r = 1;
+  while (i >= (r + 3) / 4) i -= (r++ + 3) / 4;
+  return i;
+}
 template <int C, int LDCF, int NTH = kChunkThreads, typename F = NoWork>
 __device__ __forceinline__ void unit_lower_inverse(const float (*Am)[LDCF], float (*Tm)[LDCF], float (*Tt)[LDCF],
                                                    float (*Xs)[16][20], F&& other = F{}) {
@@ -262,14 +277,34 @@ __device__ __forceinline__ void unit_lower_inverse(const float (*Am)[LDCF], floa
     other(tid - kWave, NTH - kWave);
   } else if (tid < C) {  // diagonal 16x16 blocks, one column per lane
     const int o = (tid >> 4) * 16, c = tid & 15;
-    float x[16];
+    // Forward substitution over the block's lower-triangle entries, read as
+    // 16-byte pieces (row r, columns 4q .. 4q+3 for 4q < r) three pieces ahead
+    // of their use: read one at a time, each read was waited for at its
+    // multiply-add.  Same summation order as row by row.
+    float x[16], acc = 0.f;
+    float4 buf[4];
+    auto fetch = [&]<int I>() {
+      constexpr int r = diag_piece_row(I), q = diag_piece_col(I);
+      buf[I % 4] = *reinterpret_cast<const float4*>(&Am[o + r][o + 4 * q]);
+    };
+    auto solve_piece = [&]<int I>() {
+      if constexpr (I + 3 < kDiagPieces) fetch.template operator()<I + 3>();
+      constexpr int r = diag_piece_row(I), q = diag_piece_col(I);
+      if constexpr (q == 0) acc = (r == c) ? 1.f : 0.f;
+      const float4 v = buf[I % 4];
+      const float av[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float acc = (r == c) ? 1.f : 0.f;
-#pragma unroll
-      for (int s = 0; s < r; ++s) acc -= Am[o + r][o + s] * x[s];
-      x[r] = acc;
-    }
+      for (int u = 0; u < 4; ++u)
+        if (4 * q + u < r) acc -= av[u] * x[4 * q + u];
+      if constexpr (4 * q + 4 >= r) x[r] = acc;
+    };
+    fetch.template operator()<0>();
+    fetch.template operator()<1>();
+    fetch.template operator()<2>();
+    x[0] = (c == 0) ? 1.f : 0.f;
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (solve_piece.template operator()<I>(), ...);
+    }(std::make_integer_sequence<int, kDiagPieces>{});
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       Tm[o + r][o + c] = x[r];
