@@ -42,7 +42,7 @@ def test_chunk_index_bit_exact(lengths, chunk):
 @pytest.mark.parametrize("dtype,d,lengths", [("f32", 16, (64,)), ("f32", 32, (1, 2, 3, 70, 9)),
                                              ("bf16", 128, (1, 3, 64, 130, 2, 77)), ("bf16", 64, (200,)),
                                              ("bf16", 16, (5, 0, 40))])
-@pytest.mark.parametrize("width", [4, 3])
+@pytest.mark.parametrize("width", [4, 3, 2])
 def test_conv1d_fwd_bwd(dtype, d, lengths, width):
     _print_case("conv1d", dtype=dtype, d=d, lengths=lengths, width=width)
     cfg = small_cfg(dtype=dtype, lengths=lengths, d=d).replace(width=width)
