@@ -519,349 +519,371 @@ __global__ __launch_bounds__(NTH) void grad_b_kernel(ChunkArgs a) {
   static_assert(NT <= NW, "one r-tile per wave");
   constexpr int NWR = NT, NWD = NW / NWR;         // waves along r / along d
   constexpr int DT = ND >= NWD ? ND / NWD : 1;   // d-tiles per wave
-  const int ci = blockIdx.x, j = blockIdx.y;
-  const int4 ent = chunk_entry(a.table, ci);
-  if (ent.x < 0) {  // padding entry past the last chunk: its shares of the gate sums are zero
-    if (a.da)
-      for (int i = threadIdx.x; i < a.G; i += NTH) {
-        a.gpart[(int64_t)ci * a.Hv + j * a.G + i] = 0.f;
-        a.gpart[((int64_t)a.max_chunks + ci) * a.Hv + j * a.G + i] = 0.f;
-      }
-    return;
-  }
-  const int tok0 = ent.y, len = ent.z;
   const int w = wave_id(), lane = lane_id(), tid = threadIdx.x;
   const int rt = w % NWR, dt0 = (w / NWR) * DT;
   const bool act = dt0 < ND;
   const int pslot = (w / NWR) * 4 + (lane >> 4);  // this lane's row partial slot
   const int rrow = rt * 16 + (lane & 15);         // chunk row of this lane's accumulator column
   const int dl = 4 * (lane >> 4);                 // first of its 4 rows within a d-tile
-  const E* qg = (const E*)a.q + (int64_t)tok0 * a.sqk + (int64_t)j * D;
-  const E* kg = (const E*)a.k + (int64_t)tok0 * a.sqk + (int64_t)j * D;
-
-  {
-    // q and k rows, both requested before either is written (transposed) to LDS
-    TileRegs<E, C, D, NTH, true> rq, rk;
-    rq.load(qg, a.sqk, len);
-    rk.load(kg, a.sqk, len);
+  // Persistent: the workgroup walks items (chunk, k-head) = (it / Hk, it % Hk)
+  // from blockIdx.x in steps of gridDim.x and requests the next item's q and k
+  // rows before the current item's dq and dk leave, so that no item starts on
+  // a cold round trip.  Padding chunks past the last one only zero their
+  // shares of the gate sums.
+  const int n_items = a.max_chunks * a.Hk;
+  auto item_entry = [&](int it) {
+    int4 e = it < n_items ? chunk_entry(a.table, it / a.Hk) : make_int4(-1, 0, 0, 0);
+    // scalars: the buffer sizes formed from them stay scalar
+    e.x = __builtin_amdgcn_readfirstlane(e.x);
+    e.y = __builtin_amdgcn_readfirstlane(e.y);
+    e.z = __builtin_amdgcn_readfirstlane(e.z);
+    return e;
+  };
+  TileRegs<E, C, D, NTH, true> rq, rk;  // an item's q and k rows, requested one item ahead
+  auto load_qk = [&](int it, int4 e) {   // zero-size reads for padding chunks and past the last item
+    const int n = e.x >= 0 ? e.z : 0, tok = e.x >= 0 ? e.y : 0, jj = it % a.Hk;
+    rq.load((const E*)a.q + (int64_t)tok * a.sqk + (int64_t)jj * D, a.sqk, n);
+    rk.load((const E*)a.k + (int64_t)tok * a.sqk + (int64_t)jj * D, a.sqk, n);
+  };
+  int4 ent = item_entry(blockIdx.x);
+  load_qk(blockIdx.x, ent);
+  for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+    const int ci = it / a.Hk, j = it % a.Hk;
+    const int next = it + (int)gridDim.x;
+    const int4 nent = item_entry(next);
+    if (ent.x < 0) {  // padding entry past the last chunk: its shares of the gate sums are zero
+      if (a.da)
+        for (int i = threadIdx.x; i < a.G; i += NTH) {
+          a.gpart[(int64_t)ci * a.Hv + j * a.G + i] = 0.f;
+          a.gpart[((int64_t)a.max_chunks + ci) * a.Hv + j * a.G + i] = 0.f;
+        }
+      load_qk(next, nent);
+      ent = nent;
+      continue;
+    }
+    const int tok0 = ent.y, len = ent.z;
+    // q and k rows, written transposed to LDS (every wave passed the previous
+    // item's last barrier after its last read of them)
     rq.store_t_raw(&sm.QKt[0][0], S::LD2C);
     rk.store_t_raw(&sm.QKt[0][C], S::LD2C);
-  }
-  __syncthreads();
-  // K K^T (exact bf16 products, fp32 sums), shared by the k-head's v-heads
-  for (int t = w; t < NT * NT; t += NW) {
-    const int rt = t / NT, ct = t % NT;
-    const f32x4 skk = mm_gen<E, D, false, false>(
-        zero4(),
-        [&](int r, int k, float* o) {
+    __syncthreads();
+    // K K^T (exact bf16 products, fp32 sums), shared by the k-head's v-heads
+    for (int t = w; t < NT * NT; t += NW) {
+      const int rt = t / NT, ct = t % NT;
+      const f32x4 skk = mm_gen<E, D, false, false>(
+          zero4(),
+          [&](int r, int k, float* o) {
 #pragma unroll
-          for (int u = 0; u < KPL; ++u) o[u] = to_f<E>(sm.QKt[k + u][C + rt * 16 + r]);
-        },
-        [&](int c, int k, float* o) {
+            for (int u = 0; u < KPL; ++u) o[u] = to_f<E>(sm.QKt[k + u][C + rt * 16 + r]);
+          },
+          [&](int c, int k, float* o) {
 #pragma unroll
-          for (int u = 0; u < KPL; ++u) o[u] = to_f<E>(sm.QKt[k + u][C + ct * 16 + c]);
-        });
+            for (int u = 0; u < KPL; ++u) o[u] = to_f<E>(sm.QKt[k + u][C + ct * 16 + c]);
+          });
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sm.Skk[rt * 16 + acc_row(e)][ct * 16 + acc_col()] = skk[e];
-  }
+      for (int e = 0; e < 4; ++e) sm.Skk[rt * 16 + acc_row(e)][ct * 16 + acc_col()] = skk[e];
+    }
 
-  f32x4 dQ[DT][1], dK[DT][1];
-  zero_blk(dQ);
-  zero_blk(dK);
+    f32x4 dQ[DT][1], dK[DT][1];
+    zero_blk(dQ);
+    zero_blk(dK);
 
-  for (int gi = 0; gi < a.G; ++gi) {
-    const int h = j * a.G + gi;
-    const int64_t slot = (int64_t)ci * a.Hv + h;
-    const E* vg = (const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)h * D;
-    // Per-row gates, requested before the tiles so that wave 0, which writes
-    // them to LDS, waits for these loads only.  Every thread loads those of row
-    // tid % C (rows past len clamped): no load sits in a branch, where the
-    // compiler would issue it after the tiles' or on its own.
-    const int ge = tid & (C - 1), gr = min(ge, len - 1);
-    const float gm = a.gam[slot * C + ge];
-    const float gl = a.gam[slot * C + len - 1];
-    const float braw = chunk_beta_raw(a, tok0 + gr, h);
-    const float hd = a.hdot[slot];
-    // fused gates: this row's raw a, A_log and dt_bias (zero-size reads without
-    // them: a load under a branch is waited for in that branch)
-    const int fz = a.ga ? 4 : 0;
-    const float xa_raw = buf_load_f32(a.ga + (int64_t)tok0 * a.Hv + h, fz * len * a.Hv, gr * a.Hv * 4);
-    const float alog = buf_load_f32(a.A_log + h, fz, 0), dtb = buf_load_f32(a.dt_bias + h, fz, 0);
-    __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the tiles'
-    TileRegs<E, C, D, NTH> pV;  // v rows and T (from the preparation pass)
-    TileRegs<float, C, C, NTH, true> pTm;  // rows first: also written transposed
-    TileRegs<float, D, C, NTH> rXu, rXw;  // dW^T, and dWk^T (in flight during the dXu products)
-    pV.load(vg, a.sv, len);
-    pTm.load(a.Tw + slot * C * C, C, C);
-    rXu.load(a.dWt + slot * D * C, C, D);
-    rXw.load(a.dWkt + slot * D * C, C, D);
-    // fused gates: this row's factors da / dg, db / dbeta and its g, kept for the row pass at the end
-    float fa_r = 0.f, fb_r = 0.f, g_r = 0.f;
-    if (tid < C) {
-      if (a.ga) {
-        // formed here, off the row pass's serial path (the expressions of gdn_gates_bwd)
-        const float ea = __expf(alog), xa = xa_raw + dtb;
-        fa_r = -ea * gate_sigmoid(xa);
-        g_r = -ea * gate_softplus(xa);
-        fb_r = gate_sigmoid(braw) * gate_sigmoid(-braw);
+    for (int gi = 0; gi < a.G; ++gi) {
+      const int h = j * a.G + gi;
+      const int64_t slot = (int64_t)ci * a.Hv + h;
+      const E* vg = (const E*)a.v + (int64_t)tok0 * a.sv + (int64_t)h * D;
+      // Per-row gates, requested before the tiles so that wave 0, which writes
+      // them to LDS, waits for these loads only.  Every thread loads those of row
+      // tid % C (rows past len clamped): no load sits in a branch, where the
+      // compiler would issue it after the tiles' or on its own.
+      const int ge = tid & (C - 1), gr = min(ge, len - 1);
+      const float gm = a.gam[slot * C + ge];
+      const float gl = a.gam[slot * C + len - 1];
+      const float braw = chunk_beta_raw(a, tok0 + gr, h);
+      const float hd = a.hdot[slot];
+      // fused gates: this row's raw a, A_log and dt_bias (zero-size reads without
+      // them: a load under a branch is waited for in that branch)
+      const int fz = a.ga ? 4 : 0;
+      const float xa_raw = buf_load_f32(a.ga + (int64_t)tok0 * a.Hv + h, fz * len * a.Hv, gr * a.Hv * 4);
+      const float alog = buf_load_f32(a.A_log + h, fz, 0), dtb = buf_load_f32(a.dt_bias + h, fz, 0);
+      __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the tiles'
+      TileRegs<E, C, D, NTH> pV;  // v rows and T (from the preparation pass)
+      TileRegs<float, C, C, NTH, true> pTm;  // rows first: also written transposed
+      TileRegs<float, D, C, NTH> rXu, rXw;  // dW^T, and dWk^T (in flight during the dXu products)
+      pV.load(vg, a.sv, len);
+      pTm.load(a.Tw + slot * C * C, C, C);
+      rXu.load(a.dWt + slot * D * C, C, D);
+      rXw.load(a.dWkt + slot * D * C, C, D);
+      // fused gates: this row's factors da / dg, db / dbeta and its g, kept for the row pass at the end
+      float fa_r = 0.f, fb_r = 0.f, g_r = 0.f;
+      if (tid < C) {
+        if (a.ga) {
+          // formed here, off the row pass's serial path (the expressions of gdn_gates_bwd)
+          const float ea = __expf(alog), xa = xa_raw + dtb;
+          fa_r = -ea * gate_sigmoid(xa);
+          g_r = -ea * gate_softplus(xa);
+          fb_r = gate_sigmoid(braw) * gate_sigmoid(-braw);
+        }
+        const float bt = chunk_beta_fin(a, braw);
+        sm.gam[ge] = gm;
+        sm.Gm[ge] = __expf(gm);
+        sm.beta[ge] = ge < len ? bt : 0.f;
+        sm.em[ge] = ge < len ? __expf(gl - gm) : 0.f;
+        sm.hdot = hd;  // the same value from every lane: no branch for the load to sink into
       }
-      const float bt = chunk_beta_fin(a, braw);
-      sm.gam[ge] = gm;
-      sm.Gm[ge] = __expf(gm);
-      sm.beta[ge] = ge < len ? bt : 0.f;
-      sm.em[ge] = ge < len ? __expf(gl - gm) : 0.f;
-      sm.hdot = hd;  // the same value from every lane: no branch for the load to sink into
+      pTm.store(&sm.Tm[0][0], S::LDCF);
+      // fp32 operands of the products below are split into their MFMA parts once
+      // here, not per tile
+      E* const TtL = LO ? &sm.TtL[0][0] : nullptr;
+      E* const XL = LO ? &sm.r.x.l[0][0] : nullptr;
+      pTm.template store_t<E>(&sm.TtH[0][0], S::LDCE, TtL, S::LDCE);  // T^T, transposed here
+      // dXu = T^T dW -> dv and <dXu, v>
+      pV.store(&sm.av.Vs[0][0], S::LDV);
+      rXu.template store_split<E>(&sm.r.x.h[0][0], XL, S::LDCE);
+      __syncthreads();
+      // tile (dt, rt) of (T^T X)^T = X^T T (X = dW^T or dWk^T staged in r.x)
+      auto txt = [&](int dt) {
+        f32x4 acc[1][1];
+        zero_blk(acc);
+        mm_blk<E, C, 1, 1, LO, LO>(acc, &sm.r.x.h[dt * 16][0], LO ? XL + dt * 16 * S::LDCE : nullptr, S::LDCE,
+                                   &sm.TtH[rt * 16][0], LO ? TtL + rt * 16 * S::LDCE : nullptr, S::LDCE);
+        return acc[0][0];
+      };
+      E* dvg = (E*)a.dv + (int64_t)tok0 * a.sv + (int64_t)h * D;
+      if (act) {
+        const float br = sm.beta[rrow];
+        float pu = 0.f;
+#pragma unroll
+        for (int i = 0; i < DT; ++i) {
+          const int d = (dt0 + i) * 16 + dl;
+          const f32x4 xu = txt(dt0 + i);
+          float vv[4];
+          ld4<E>(&sm.av.Vs[rrow][d], vv);
+          f32x4 dvv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            dvv[e] = br * xu[e];
+            pu += xu[e] * vv[e];
+          }
+          if (rrow < len) st4<E>(dvg + (int64_t)rrow * a.sv + d, dvv);
+        }
+        sm.pCD[0][pslot][rrow] = pu;
+      }
+      __syncthreads();
+      // dXw = T^T dWk -> dK and <dXw, k>
+      rXw.template store_split<E>(&sm.r.x.h[0][0], XL, S::LDCE);
+      __syncthreads();
+      // dT, P and dP' of the C x C passes: in flight during the dXw products
+      TileRegs<float, C, C, NTH> rT, pP, pdP;
+      rT.load(a.dT + slot * C * C, C, C);
+      pP.load(a.P + slot * C * C, C, C);
+      pdP.load(a.dP + slot * C * C, C, C);
+      if (act) {
+        const float bg = sm.beta[rrow] * sm.Gm[rrow];
+        float pw = 0.f;
+#pragma unroll
+        for (int i = 0; i < DT; ++i) {
+          const int d = (dt0 + i) * 16 + dl;
+          const f32x4 xw = txt(dt0 + i);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pw += xw[e] * to_f<E>(sm.QKt[d + e][C + rrow]);
+            dK[i][0][e] += bg * xw[e];
+          }
+        }
+        sm.pCD[1][pslot][rrow] = pw;
+      }
+      __syncthreads();
+      // M1 = dT T^T (fp32 MFMA), stored transposed and split; dA = strict_lower(-T^T M1)
+      rT.store(&sm.r.m.dT[0][0], S::LDCF);
+      __syncthreads();
+      for (int t = w; t < NT * NT; t += NW) {
+        const int rt = t / NT, ct = t % NT;
+        // fp32 operands fed as bf16 hi / lo parts (three products per k-step)
+        // rather than to the fp32 matrix instruction, which does a quarter of
+        // the work per cycle
+        const f32x4 m = mm_gen<E, C, true, true>(
+            zero4(), [&](int r, int k, float* o) { ld_row<float, KPL>(&sm.r.m.dT[rt * 16 + r][k], o); },
+            [&](int c, int k, float* o) { ld_row<float, KPL>(&sm.Tm[ct * 16 + c][k], o); });
+        E* const M1L = LO ? &sm.r.m.M1l[0][0] : nullptr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = ct * 16 + acc_col(), r = rt * 16 + acc_row(e);
+          split_store<E>(&sm.r.m.M1h[c][r], LO ? M1L + c * S::LDCE + r : nullptr, m[e]);
+        }
+      }
+      __syncthreads();
+      for (int t = w; t < NT * NT; t += NW) {
+        const int rt = t / NT, ct = t % NT;
+        f32x4 mb[1][1];
+        zero_blk(mb);
+        mm_blk<E, C, 1, 1, LO, LO>(mb, &sm.TtH[rt * 16][0], LO ? TtL + rt * 16 * S::LDCE : nullptr, S::LDCE,
+                                   &sm.r.m.M1h[ct * 16][0], LO ? &sm.r.m.M1l[ct * 16][0] : nullptr, S::LDCE);
+        const f32x4 m = mb[0][0];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = rt * 16 + acc_row(e), s = ct * 16 + acc_col();
+          sm.av.Am[r][s] = (s < r && r < len) ? -m[e] : 0.f;
+        }
+      }
+      __syncthreads();
+      pP.store(&sm.Tm[0][0], S::LDCF);  // T is no longer needed
+      pdP.store(&sm.dPm[0][0], S::LDCF);  // T^T is no longer needed
+      __syncthreads();
+      // C x C pass: A~, dS, and the dgamma / dbeta terms of A and P
+      for (int t = w; t < NT * NT; t += NW) {
+        const int rt = t / NT, ct = t % NT;
+        float rb[4], ra[4], rp[4], ca = 0.f, cp = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = rt * 16 + acc_row(e), s = ct * 16 + acc_col();
+          const float skk = sm.Skk[r][s];
+          const float dd = (s <= r) ? __expf(sm.gam[r] - sm.gam[s]) : 0.f;
+          const float dA = sm.av.Am[r][s];
+          const float At = dA * sm.beta[r] * dd;
+          const float AdA = At * skk;
+          const float dP = sm.dPm[r][s];
+          const float PdP = dP * sm.Tm[r][s];
+          rb[e] = dA * dd * skk;
+          ra[e] = AdA;
+          rp[e] = PdP;
+          ca += AdA;
+          cp += PdP;
+          split_store<E>(&sm.r.s.dSh[r][s], &sm.r.s.dSl[0][0] + r * S::LDCE + s, dP * dd);
+          sm.r.s.At[r][s] = At;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          rb[e] = group_sum<16>(rb[e]);
+          ra[e] = group_sum<16>(ra[e]);
+          rp[e] = group_sum<16>(rp[e]);
+        }
+        ca += __shfl_xor(ca, 16, kWave);
+        ca += __shfl_xor(ca, 32, kWave);
+        cp += __shfl_xor(cp, 16, kWave);
+        cp += __shfl_xor(cp, 32, kWave);
+        if ((lane & 15) == 0) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = rt * 16 + acc_row(e);
+            sm.pCC[0][ct][r] = rb[e];
+            sm.pCC[1][ct][r] = ra[e];
+            sm.pCC[3][ct][r] = rp[e];
+          }
+        }
+        if (lane < 16) {
+          sm.pCC[2][rt][ct * 16 + lane] = ca;
+          sm.pCC[4][rt][ct * 16 + lane] = cp;
+        }
+      }
+      __syncthreads();
+      // this lane's dKh and dQs tiles: in flight during the transpose below
+      // (waves past the d-tiles load the last tile again and leave it unused)
+      f32x4 khr[DT], qsr[DT];
+#pragma unroll
+      for (int i = 0; i < DT; ++i) {
+        const int dtl = min(dt0 + i, ND - 1);
+        khr[i] = load_acc(a.dKh + slot * C * D, NT, dtl, rt);
+        qsr[i] = load_acc(a.dQs + slot * C * D, NT, dtl, rt);
+      }
+      // [dS^T | A~ + A~^T] as rows (P and dP' are consumed)
+      for (int e = tid; e < C * C; e += NTH) {
+        const int sr = e / C, r = e % C;
+        sm.TS.h[sr][r] = sm.r.s.dSh[r][sr];
+        if constexpr (LO) sm.TS.l[sr][r] = sm.r.s.dSl[r][sr];
+        split_store<E>(&sm.TS.h[sr][C + r], &sm.TS.l[0][0] + sr * S::LD2C + C + r,
+                       sm.r.s.At[sr][r] + sm.r.s.At[r][sr]);
+      }
+      __syncthreads();
+      // dQ += dQs + dS K;   dK += dKh + [dS^T | A~ + A~^T] [Q ; K]   (transposed)
+      if (act) {
+        float pq = 0.f, pk = 0.f;
+#pragma unroll
+        for (int i = 0; i < DT; ++i) {
+          const int d = (dt0 + i) * 16 + dl;
+          const f32x4 qs = qsr[i];
+          const f32x4 kh = khr[i];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            dQ[i][0][e] += qs[e];
+            dK[i][0][e] += kh[e];
+            pq += qs[e] * to_f<E>(sm.QKt[d + e][rrow]);
+            pk += kh[e] * to_f<E>(sm.QKt[d + e][C + rrow]);
+          }
+        }
+        sm.pCD[2][pslot][rrow] = pq;
+        sm.pCD[3][pslot][rrow] = pk;
+        mm_blk<E, C, DT, 1, false, LO>(dQ, &sm.QKt[dt0 * 16][C], nullptr, S::LD2C, &sm.r.s.dSh[rt * 16][0],
+                                       LO ? &sm.r.s.dSl[0][0] + rt * 16 * S::LDCE : nullptr, S::LDCE);
+        mm_blk<E, 2 * C, DT, 1, false, LO>(dK, &sm.QKt[dt0 * 16][0], nullptr, S::LD2C, &sm.TS.h[rt * 16][0],
+                                           LO ? &sm.TS.l[0][0] + rt * 16 * S::LD2C : nullptr, S::LD2C);
+      }
+      __syncthreads();
+      // per-row totals, then dg = reverse cumulative sum within the chunk
+      if (w == 0) {
+        const int r = lane;
+        float dbeta = 0.f, dgam = 0.f, tk = 0.f;
+        if (r < C) {
+          float su = 0.f, sw = 0.f, sq = 0.f;
+          for (int c = 0; c < S::NPD; ++c) {
+            su += sm.pCD[0][c][r];
+            sw += sm.pCD[1][c][r];
+            sq += sm.pCD[2][c][r];
+            tk += sm.pCD[3][c][r];
+          }
+          float rb = 0.f, ar = 0.f, ac = 0.f, pr = 0.f, pc = 0.f;
+          for (int c = 0; c < NT; ++c) {
+            rb += sm.pCC[0][c][r];
+            ar += sm.pCC[1][c][r];
+            ac += sm.pCC[2][c][r];
+            pr += sm.pCC[3][c][r];
+            pc += sm.pCC[4][c][r];
+          }
+          dbeta = su + sm.Gm[r] * sw + rb;
+          dgam = sq - tk + sm.beta[r] * sm.Gm[r] * sw + (ar - ac) + (pr - pc);
+          if (r >= len) dgam = tk = 0.f;
+        }
+        const float tks = wave_sum(tk);
+        if (r == len - 1) dgam += sm.Gm[len - 1] * sm.hdot + tks;
+        // reverse inclusive scan: dg_r = sum_{r' >= r} dgam_{r'}
+        const float x = wave_suffix_sum(dgam);
+        if (a.da) {
+          // fused gates: da = -exp(A_log) sigmoid(a + dt_bias) dg, db = beta (1 - beta) dbeta,
+          // and this chunk's shares of dA_log = sum dg g and ddt_bias = sum da
+          float sA = 0.f, sdt = 0.f;
+          if (r < len) {  // row r's factors: formed by this lane at the start of the v-head
+            const int64_t e = (int64_t)(tok0 + r) * a.Hv + h;
+            const float dav = fa_r * x;
+            a.da[e] = dav;
+            a.db[e] = fb_r * dbeta;
+            sA = x * g_r;
+            sdt = dav;
+          }
+          sA = wave_sum(sA);
+          sdt = wave_sum(sdt);
+          if (r == 0) {
+            a.gpart[(int64_t)ci * a.Hv + h] = sA;
+            a.gpart[((int64_t)a.max_chunks + ci) * a.Hv + h] = sdt;
+          }
+        } else if (r < len) {
+          a.dg[(int64_t)(tok0 + r) * a.Hv + h] = x;
+          a.dbeta[(int64_t)(tok0 + r) * a.Hv + h] = dbeta;
+        }
+      }
+      __syncthreads();
     }
-    pTm.store(&sm.Tm[0][0], S::LDCF);
-    // fp32 operands of the products below are split into their MFMA parts once
-    // here, not per tile
-    E* const TtL = LO ? &sm.TtL[0][0] : nullptr;
-    E* const XL = LO ? &sm.r.x.l[0][0] : nullptr;
-    pTm.template store_t<E>(&sm.TtH[0][0], S::LDCE, TtL, S::LDCE);  // T^T, transposed here
-    // dXu = T^T dW -> dv and <dXu, v>
-    pV.store(&sm.av.Vs[0][0], S::LDV);
-    rXu.template store_split<E>(&sm.r.x.h[0][0], XL, S::LDCE);
-    __syncthreads();
-    // tile (dt, rt) of (T^T X)^T = X^T T (X = dW^T or dWk^T staged in r.x)
-    auto txt = [&](int dt) {
-      f32x4 acc[1][1];
-      zero_blk(acc);
-      mm_blk<E, C, 1, 1, LO, LO>(acc, &sm.r.x.h[dt * 16][0], LO ? XL + dt * 16 * S::LDCE : nullptr, S::LDCE,
-                                 &sm.TtH[rt * 16][0], LO ? TtL + rt * 16 * S::LDCE : nullptr, S::LDCE);
-      return acc[0][0];
-    };
-    E* dvg = (E*)a.dv + (int64_t)tok0 * a.sv + (int64_t)h * D;
-    if (act) {
-      const float br = sm.beta[rrow];
-      float pu = 0.f;
+    load_qk(next, nent);  // in flight while this item's dq and dk leave
+    E* dqg = (E*)a.dq + (int64_t)tok0 * a.sqk + (int64_t)j * D;
+    E* dkg = (E*)a.dk + (int64_t)tok0 * a.sqk + (int64_t)j * D;
+    if (act && rrow < len) {
 #pragma unroll
       for (int i = 0; i < DT; ++i) {
         const int d = (dt0 + i) * 16 + dl;
-        const f32x4 xu = txt(dt0 + i);
-        float vv[4];
-        ld4<E>(&sm.av.Vs[rrow][d], vv);
-        f32x4 dvv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          dvv[e] = br * xu[e];
-          pu += xu[e] * vv[e];
-        }
-        if (rrow < len) st4<E>(dvg + (int64_t)rrow * a.sv + d, dvv);
-      }
-      sm.pCD[0][pslot][rrow] = pu;
-    }
-    __syncthreads();
-    // dXw = T^T dWk -> dK and <dXw, k>
-    rXw.template store_split<E>(&sm.r.x.h[0][0], XL, S::LDCE);
-    __syncthreads();
-    // dT, P and dP' of the C x C passes: in flight during the dXw products
-    TileRegs<float, C, C, NTH> rT, pP, pdP;
-    rT.load(a.dT + slot * C * C, C, C);
-    pP.load(a.P + slot * C * C, C, C);
-    pdP.load(a.dP + slot * C * C, C, C);
-    if (act) {
-      const float bg = sm.beta[rrow] * sm.Gm[rrow];
-      float pw = 0.f;
-#pragma unroll
-      for (int i = 0; i < DT; ++i) {
-        const int d = (dt0 + i) * 16 + dl;
-        const f32x4 xw = txt(dt0 + i);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pw += xw[e] * to_f<E>(sm.QKt[d + e][C + rrow]);
-          dK[i][0][e] += bg * xw[e];
-        }
-      }
-      sm.pCD[1][pslot][rrow] = pw;
-    }
-    __syncthreads();
-    // M1 = dT T^T (fp32 MFMA), stored transposed and split; dA = strict_lower(-T^T M1)
-    rT.store(&sm.r.m.dT[0][0], S::LDCF);
-    __syncthreads();
-    for (int t = w; t < NT * NT; t += NW) {
-      const int rt = t / NT, ct = t % NT;
-      // fp32 operands fed as bf16 hi / lo parts (three products per k-step)
-      // rather than to the fp32 matrix instruction, which does a quarter of
-      // the work per cycle
-      const f32x4 m = mm_gen<E, C, true, true>(
-          zero4(), [&](int r, int k, float* o) { ld_row<float, KPL>(&sm.r.m.dT[rt * 16 + r][k], o); },
-          [&](int c, int k, float* o) { ld_row<float, KPL>(&sm.Tm[ct * 16 + c][k], o); });
-      E* const M1L = LO ? &sm.r.m.M1l[0][0] : nullptr;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = ct * 16 + acc_col(), r = rt * 16 + acc_row(e);
-        split_store<E>(&sm.r.m.M1h[c][r], LO ? M1L + c * S::LDCE + r : nullptr, m[e]);
+        st4<E>(dqg + (int64_t)rrow * a.sqk + d, dQ[i][0]);
+        st4<E>(dkg + (int64_t)rrow * a.sqk + d, dK[i][0]);
       }
     }
-    __syncthreads();
-    for (int t = w; t < NT * NT; t += NW) {
-      const int rt = t / NT, ct = t % NT;
-      f32x4 mb[1][1];
-      zero_blk(mb);
-      mm_blk<E, C, 1, 1, LO, LO>(mb, &sm.TtH[rt * 16][0], LO ? TtL + rt * 16 * S::LDCE : nullptr, S::LDCE,
-                                 &sm.r.m.M1h[ct * 16][0], LO ? &sm.r.m.M1l[ct * 16][0] : nullptr, S::LDCE);
-      const f32x4 m = mb[0][0];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = rt * 16 + acc_row(e), s = ct * 16 + acc_col();
-        sm.av.Am[r][s] = (s < r && r < len) ? -m[e] : 0.f;
-      }
-    }
-    __syncthreads();
-    pP.store(&sm.Tm[0][0], S::LDCF);  // T is no longer needed
-    pdP.store(&sm.dPm[0][0], S::LDCF);  // T^T is no longer needed
-    __syncthreads();
-    // C x C pass: A~, dS, and the dgamma / dbeta terms of A and P
-    for (int t = w; t < NT * NT; t += NW) {
-      const int rt = t / NT, ct = t % NT;
-      float rb[4], ra[4], rp[4], ca = 0.f, cp = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = rt * 16 + acc_row(e), s = ct * 16 + acc_col();
-        const float skk = sm.Skk[r][s];
-        const float dd = (s <= r) ? __expf(sm.gam[r] - sm.gam[s]) : 0.f;
-        const float dA = sm.av.Am[r][s];
-        const float At = dA * sm.beta[r] * dd;
-        const float AdA = At * skk;
-        const float dP = sm.dPm[r][s];
-        const float PdP = dP * sm.Tm[r][s];
-        rb[e] = dA * dd * skk;
-        ra[e] = AdA;
-        rp[e] = PdP;
-        ca += AdA;
-        cp += PdP;
-        split_store<E>(&sm.r.s.dSh[r][s], &sm.r.s.dSl[0][0] + r * S::LDCE + s, dP * dd);
-        sm.r.s.At[r][s] = At;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        rb[e] = group_sum<16>(rb[e]);
-        ra[e] = group_sum<16>(ra[e]);
-        rp[e] = group_sum<16>(rp[e]);
-      }
-      ca += __shfl_xor(ca, 16, kWave);
-      ca += __shfl_xor(ca, 32, kWave);
-      cp += __shfl_xor(cp, 16, kWave);
-      cp += __shfl_xor(cp, 32, kWave);
-      if ((lane & 15) == 0) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = rt * 16 + acc_row(e);
-          sm.pCC[0][ct][r] = rb[e];
-          sm.pCC[1][ct][r] = ra[e];
-          sm.pCC[3][ct][r] = rp[e];
-        }
-      }
-      if (lane < 16) {
-        sm.pCC[2][rt][ct * 16 + lane] = ca;
-        sm.pCC[4][rt][ct * 16 + lane] = cp;
-      }
-    }
-    __syncthreads();
-    // this lane's dKh and dQs tiles: in flight during the transpose below
-    // (waves past the d-tiles load the last tile again and leave it unused)
-    f32x4 khr[DT], qsr[DT];
-#pragma unroll
-    for (int i = 0; i < DT; ++i) {
-      const int dtl = min(dt0 + i, ND - 1);
-      khr[i] = load_acc(a.dKh + slot * C * D, NT, dtl, rt);
-      qsr[i] = load_acc(a.dQs + slot * C * D, NT, dtl, rt);
-    }
-    // [dS^T | A~ + A~^T] as rows (P and dP' are consumed)
-    for (int e = tid; e < C * C; e += NTH) {
-      const int sr = e / C, r = e % C;
-      sm.TS.h[sr][r] = sm.r.s.dSh[r][sr];
-      if constexpr (LO) sm.TS.l[sr][r] = sm.r.s.dSl[r][sr];
-      split_store<E>(&sm.TS.h[sr][C + r], &sm.TS.l[0][0] + sr * S::LD2C + C + r,
-                     sm.r.s.At[sr][r] + sm.r.s.At[r][sr]);
-    }
-    __syncthreads();
-    // dQ += dQs + dS K;   dK += dKh + [dS^T | A~ + A~^T] [Q ; K]   (transposed)
-    if (act) {
-      float pq = 0.f, pk = 0.f;
-#pragma unroll
-      for (int i = 0; i < DT; ++i) {
-        const int d = (dt0 + i) * 16 + dl;
-        const f32x4 qs = qsr[i];
-        const f32x4 kh = khr[i];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          dQ[i][0][e] += qs[e];
-          dK[i][0][e] += kh[e];
-          pq += qs[e] * to_f<E>(sm.QKt[d + e][rrow]);
-          pk += kh[e] * to_f<E>(sm.QKt[d + e][C + rrow]);
-        }
-      }
-      sm.pCD[2][pslot][rrow] = pq;
-      sm.pCD[3][pslot][rrow] = pk;
-      mm_blk<E, C, DT, 1, false, LO>(dQ, &sm.QKt[dt0 * 16][C], nullptr, S::LD2C, &sm.r.s.dSh[rt * 16][0],
-                                     LO ? &sm.r.s.dSl[0][0] + rt * 16 * S::LDCE : nullptr, S::LDCE);
-      mm_blk<E, 2 * C, DT, 1, false, LO>(dK, &sm.QKt[dt0 * 16][0], nullptr, S::LD2C, &sm.TS.h[rt * 16][0],
-                                         LO ? &sm.TS.l[0][0] + rt * 16 * S::LD2C : nullptr, S::LD2C);
-    }
-    __syncthreads();
-    // per-row totals, then dg = reverse cumulative sum within the chunk
-    if (w == 0) {
-      const int r = lane;
-      float dbeta = 0.f, dgam = 0.f, tk = 0.f;
-      if (r < C) {
-        float su = 0.f, sw = 0.f, sq = 0.f;
-        for (int c = 0; c < S::NPD; ++c) {
-          su += sm.pCD[0][c][r];
-          sw += sm.pCD[1][c][r];
-          sq += sm.pCD[2][c][r];
-          tk += sm.pCD[3][c][r];
-        }
-        float rb = 0.f, ar = 0.f, ac = 0.f, pr = 0.f, pc = 0.f;
-        for (int c = 0; c < NT; ++c) {
-          rb += sm.pCC[0][c][r];
-          ar += sm.pCC[1][c][r];
-          ac += sm.pCC[2][c][r];
-          pr += sm.pCC[3][c][r];
-          pc += sm.pCC[4][c][r];
-        }
-        dbeta = su + sm.Gm[r] * sw + rb;
-        dgam = sq - tk + sm.beta[r] * sm.Gm[r] * sw + (ar - ac) + (pr - pc);
-        if (r >= len) dgam = tk = 0.f;
-      }
-      const float tks = wave_sum(tk);
-      if (r == len - 1) dgam += sm.Gm[len - 1] * sm.hdot + tks;
-      // reverse inclusive scan: dg_r = sum_{r' >= r} dgam_{r'}
-      const float x = wave_suffix_sum(dgam);
-      if (a.da) {
-        // fused gates: da = -exp(A_log) sigmoid(a + dt_bias) dg, db = beta (1 - beta) dbeta,
-        // and this chunk's shares of dA_log = sum dg g and ddt_bias = sum da
-        float sA = 0.f, sdt = 0.f;
-        if (r < len) {  // row r's factors: formed by this lane at the start of the v-head
-          const int64_t e = (int64_t)(tok0 + r) * a.Hv + h;
-          const float dav = fa_r * x;
-          a.da[e] = dav;
-          a.db[e] = fb_r * dbeta;
-          sA = x * g_r;
-          sdt = dav;
-        }
-        sA = wave_sum(sA);
-        sdt = wave_sum(sdt);
-        if (r == 0) {
-          a.gpart[(int64_t)ci * a.Hv + h] = sA;
-          a.gpart[((int64_t)a.max_chunks + ci) * a.Hv + h] = sdt;
-        }
-      } else if (r < len) {
-        a.dg[(int64_t)(tok0 + r) * a.Hv + h] = x;
-        a.dbeta[(int64_t)(tok0 + r) * a.Hv + h] = dbeta;
-      }
-    }
-    __syncthreads();
-  }
-  E* dqg = (E*)a.dq + (int64_t)tok0 * a.sqk + (int64_t)j * D;
-  E* dkg = (E*)a.dk + (int64_t)tok0 * a.sqk + (int64_t)j * D;
-  if (act && rrow < len) {
-#pragma unroll
-    for (int i = 0; i < DT; ++i) {
-      const int d = (dt0 + i) * 16 + dl;
-      st4<E>(dqg + (int64_t)rrow * a.sqk + d, dQ[i][0]);
-      st4<E>(dkg + (int64_t)rrow * a.sqk + d, dK[i][0]);
-    }
+    ent = nent;
   }
 }
 
@@ -990,7 +1012,11 @@ static void launch_chunk_bwd_core(const ChunkArgs& a, hipStream_t st, bool recom
   GDN_PROF("chunk_grad_b", st);
   // 8 waves where the [C][D] tiles give each one a column strip of its own
   constexpr int GB_THREADS = gb_threads<D, C>();
-  grad_b_kernel<E, D, C, GB_THREADS><<<dim3(a.max_chunks, a.Hk), GB_THREADS, 0, st>>>(a);
+  // persistent: as many workgroups as fit at once (one per CU at d = 128, chunk 64)
+  constexpr int gb_per_cu = (160 * 1024) / (int)sizeof(GradBSmem<E, D, C>) >= 2 ? 2 : 1;
+  const int64_t gb_items = (int64_t)a.max_chunks * a.Hk, gb_resident = (int64_t)kNumCUs * gb_per_cu;
+  grad_b_kernel<E, D, C, GB_THREADS>
+      <<<dim3((unsigned)(gb_items > gb_resident ? gb_resident : gb_items)), GB_THREADS, 0, st>>>(a);
 }
 
 // Calls f.template operator()<E, D, C>() for the runtime (dtype, d, chunk)
