@@ -15,6 +15,8 @@
 // which is the token recurrence re-associated exactly.  Only non-positive
 // differences gamma_r - gamma_s (r >= s) are ever exponentiated; the mask is
 // applied before the exponential.
+#include <cstddef>
+
 #include "chunk_common.cuh"
 #include "profile.h"
 
@@ -313,11 +315,16 @@ __global__ __launch_bounds__(NTH) void prep_kernel(ChunkArgs a) {
       E (*const TB2)[S::LDCE] = reinterpret_cast<E (*)[S::LDCE]>(&sm.Am[0][0]);
       E (*const TB2l)[S::LDCE] = reinterpret_cast<E (*)[S::LDCE]>(&sm.Tt[0][0]);
       static_assert(sizeof(E) * S::LDCE <= sizeof(float) * S::LDCF, "the Wk factor fits A's rows");
-      for_strided<C * C, NTH>(tid, [&](int e) {
-        const int r = e / C, s = e % C;
-        const float tb = sm.Tm[r][s] * sm.beta[s];
-        split_store<E>(&sm.TB[r][s], &sm.TBl[0][0] + r * S::LDCE + s, tb);
-        split_store<E>(&TB2[r][s], &TB2l[r][s], tb * __expf(sm.gam[s]));
+      static_assert(offsetof(S, gam) % 16 == 0 && offsetof(S, beta) % 16 == 0, "16-byte gate reads");
+      for_strided<C * C / 4, NTH>(tid, [&](int e) {  // 4 consecutive s per step: 16-byte reads, 8-byte writes
+        const int r = e / (C / 4), s = (e % (C / 4)) * 4;
+        const float4 t4 = *reinterpret_cast<const float4*>(&sm.Tm[r][s]);
+        const float4 b4 = *reinterpret_cast<const float4*>(&sm.beta[s]);
+        const float4 g4 = *reinterpret_cast<const float4*>(&sm.gam[s]);
+        const f32x4 tb = {t4.x * b4.x, t4.y * b4.y, t4.z * b4.z, t4.w * b4.w};
+        const f32x4 tb2 = {tb[0] * __expf(g4.x), tb[1] * __expf(g4.y), tb[2] * __expf(g4.z), tb[3] * __expf(g4.w)};
+        st4_split<E>(&sm.TB[r][s], &sm.TBl[0][0] + r * S::LDCE + s, tb);
+        st4_split<E>(&TB2[r][s], &TB2l[r][s], tb2);
       });
       __syncthreads();
       auto u_tile = [&](int t) {
