@@ -8,9 +8,13 @@ RMSNormGated, and (for the training workload) the backward of all of them
 8192 tokens packed in one row, 16 q/k heads, 32 v heads, d = 128, bf16.
 
 Prints ONE JSON line with the throughput (tokens/s), the roofline of the
-dominant kernel (per-kernel durations from HIP events that the library records
-on its stream during the timed steps), and the CPU oracle timed on a bounded
-sample of the same workload (all sequences, --cpu-heads of the q/k heads).
+dominant kernel, and the CPU oracle timed on a bounded sample of the same
+workload (all sequences, --cpu-heads of the q/k heads).  Two timed regions of
+--steps steps each, after --warmup untimed ones: the step launched eagerly with
+the library's per-kernel HIP events on (the per-kernel durations and the
+roofline; reported under "eager"), then the same step recorded once into a HIP
+graph and replayed (the throughput and ms_per_step; --graph 0 reports the eager
+figures instead).
 """
 from __future__ import annotations
 
@@ -259,6 +263,9 @@ def main():
     ap.add_argument("--fused-gates", action="store_true",
                     help="compute the gates inside the chunk kernels (gdn_chunk_*_gated) instead of with "
                          "gdn_gates / gdn_gates_bwd (measured slightly slower: the default is the separate kernels)")
+    ap.add_argument("--graph", type=int, default=1,
+                    help="1: the reported throughput times the step replayed from a HIP graph (per-kernel "
+                         "durations still come from the eager timed steps); 0: eager launches only")
     ap.add_argument("--max-tokens", type=int, default=0, metavar="N",
                     help="bounded-memory training step: the chunk calls run per token segment of at most N "
                          "tokens and the backward recomputes the forward's chunk products (0: the whole row, "
@@ -347,7 +354,7 @@ def main():
                 layer.gates_backward(ga, gb, A_log, dt_bias, r["dg"], r["dbeta"])
 
     # Per-kernel durations come from HIP events that the library records around
-    # each launch on the stream it launches on, during the timed steps
+    # each launch on the stream it launches on, during the eager timed steps
     # themselves.  Warm-up runs with recording on too, so that the timed steps
     # reuse pooled events instead of creating them.
     gdn.profile_enable(True)
@@ -362,6 +369,28 @@ def main():
     elapsed = time.perf_counter() - t0
     rep = gdn.profile_report()
     gdn.profile_enable(False)
+    eager = {"ms_per_step": round(elapsed * 1e3 / args.steps, 4), "value": round(cfg.T * args.steps / elapsed, 1)}
+
+    # The same step recorded once into a HIP graph and replayed: every kernel of
+    # the step runs on every replay, without the per-launch host work.  The
+    # bounded-memory mode reads cu_seqlens on the host and is not capturable.
+    graph_info = None
+    if args.graph and not args.max_tokens:
+        try:
+            graph, _ = gdn.capture(step)
+            for _ in range(args.warmup):
+                graph.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                graph.replay()
+            torch.cuda.synchronize()
+            elapsed = time.perf_counter() - t0
+            del graph
+            graph_info = "hip graph replay"
+        except Exception as e:  # report the eager figure rather than none
+            torch.cuda.synchronize()
+            graph_info = f"eager (graph capture failed: {type(e).__name__}: {e})"
     ms_per_step = elapsed * 1e3 / args.steps
     value = cfg.T * args.steps / elapsed
 
@@ -430,6 +459,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "launch": graph_info or "eager",
+        "eager": eager,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

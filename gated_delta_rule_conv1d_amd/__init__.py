@@ -19,4 +19,4 @@ from ._binding import (  # noqa: F401
     recurrent_step, conv1d_step, conv1d_window, conv1d_prefill,
     profile_enable, profile_report, probe_copy, probe_mfma,
 )
-from .layer import GatedDeltaNetLayer, layer_forward, layer_backward, token_segments  # noqa: F401
+from .layer import GatedDeltaNetLayer, capture, layer_forward, layer_backward, token_segments  # noqa: F401

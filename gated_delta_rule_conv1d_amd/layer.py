@@ -8,7 +8,7 @@ changes (varlen mode).
 """
 from __future__ import annotations
 
-from typing import Dict, List, Optional, Tuple
+from typing import Callable, Dict, List, Optional, Tuple, TypeVar
 
 import torch
 
@@ -224,6 +224,32 @@ class GatedDeltaNetLayer:
             carry = None if first else r["dh0"]
         self._segs = None
         return dict(dg=dg, dbeta=db, dh0=dh0)
+
+
+R = TypeVar("R")
+
+
+def capture(step: Callable[[], R]) -> Tuple["torch.cuda.CUDAGraph", R]:
+    """Record one call of `step` into a HIP graph; return (graph, what step
+    returned).  graph.replay() then re-issues every kernel of that call as one
+    graph launch, without the per-launch host work.
+
+    step() enqueues this library's calls on the current stream.  The entry
+    points it may use launch kernels only (no HIP allocation, memset, copy or
+    host synchronisation), so their launches record as plain kernel nodes.
+    Not capturable: the bounded-memory mode (forward(max_tokens=...)), which
+    reads cu_seqlens on the host, and per-kernel timing (profile_enable), whose
+    HIP events are not graph nodes: switch it off before capturing.  Run
+    step() once before capturing, so that the layers' workspaces already exist
+    (a workspace first allocated during capture comes from the graph's memory
+    pool and stays there).  Tensors that step allocates come from the graph's
+    private pool: each replay rewrites them in place, and reads whatever the
+    captured input tensors hold at that moment (copy new inputs into them)."""
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = step()
+    return graph, out
 
 
 def layer_forward(shape: B.Shape, x, w_conv, g, beta, cu_seqlens, z=None, w_norm=None, h0=None, norm=True):
