@@ -26,8 +26,13 @@
  *    buffer, including workspace (sized by the *_workspace queries).  The
  *    library allocates no device memory, never synchronises and never reads
  *    device memory from the host; its only mutable global state is the opt-in
- *    timing record of gdn_profile_enable (mutex-guarded).  All work is enqueued on `stream`
+ *    timing record of gdn_profile_enable (mutex-guarded) and the per-device
+ *    scratch array of gdn_norm_gate_bwd_noalloc.  All work is enqueued on `stream`
  *    (a hipStream_t; NULL means the default stream).
+ *  - The compute calls enqueue kernel launches only: no memset, copy, event
+ *    or wait (while gdn_profile_enable is off).  A sequence of them can be
+ *    recorded into a HIP graph by stream capture; each replay re-runs every
+ *    kernel on the captured pointers and reads their current contents.
  *  - Arguments are validated on the host before anything is enqueued; on any
  *    error nothing is launched.  Device-side contents that break a documented
  *    precondition (for example a cu_seqlens that is not non-decreasing or
