@@ -119,6 +119,28 @@ def kernel_bytes(cfg, n_chunks: int, has_h0: bool) -> dict:
     }
 
 
+def fused_minimum_bytes(cfg) -> int:
+    """What one step must move through HBM at the least, whatever the kernel
+    split: every input read once and every output written once, nothing in
+    between.  Per token, forward: the pre-conv q, k, v row, z, g and beta
+    (fp32), the norm output (o when there is no norm); backward adds the
+    re-read of those inputs, dy in and dq, dk, dv, dz, dg, dbeta out.  Per
+    sequence: its initial state read (when given) and its final state written
+    (fp32 [Hv][dk][dv]); a decode step also reads and writes its conv window."""
+    Hk, Hv, dk, dv = cfg.h_qk, cfg.h_v, cfg.d_k, cfg.d_v
+    es = 2 if cfg.dtype == "bf16" else 4
+    row = (2 * Hk * dk + Hv * dv) * es          # conv input, or its gradient
+    vh = Hv * dv * es                           # z, y, dy or dz
+    gb = 2 * Hv * 4                             # g and beta, or their gradients
+    fwd = row + gb + vh * (2 if cfg.norm else 1)
+    bwd = (row + gb + vh) + vh + (row + gb + vh) if cfg.bwd else 0   # re-read, dy, gradients
+    state = Hv * dk * dv * 4
+    per_seq = state * (2 if cfg.h0 else 1)
+    if cfg.decode:
+        per_seq += 2 * (cfg.width - 1) * (2 * Hk * dk + Hv * dv) * es
+    return (fwd + bwd) * cfg.T + per_seq * cfg.N
+
+
 def kernel_flops(cfg, n_chunks: int) -> dict:
     """Algorithmic flops per launch: the method's contractions, triangular
     factors counted once (no split-precision extra products)."""
@@ -443,7 +465,7 @@ def main():
     roof["traffic"] = None if (args.max_tokens or args.fused_gates) else load_traffic(base(dom), args.workload, 1)
 
     # whole-step roofline of the path (fused algorithmic minimum)
-    step_bytes = (33024 + (57856 if cfg.bwd else 0)) * cfg.T if args.workload != "tiny" else None
+    step_bytes = fused_minimum_bytes(cfg) if args.workload != "tiny" else None
 
     cpu = None
     if args.cpu_heads > 0:
